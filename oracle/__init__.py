@@ -1,0 +1,279 @@
+"""CPU oracle for lazily evaluated pairwise scores (test infrastructure only).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this package. The product library never does, and this
+package never imports the product: the two share no code.
+
+The arithmetic lives in ``oracle.cpp`` (a plain double loop over pairs,
+float32 inputs evaluated in double and float64 inputs in x87 long double);
+this module only builds it with g++ and marshals numpy arrays through ctypes.
+The definitions it follows are those of the torchpairwise guide "Using
+Torchpairwise in Models" (Task Map, Score Expressions and the Stein
+Variational Gradient Descent section); each function below names its part.
+
+Every function returns ``(result, mag)``: ``mag`` is the first-order error
+magnitude of each result (see the header of ``oracle.cpp``), which the
+parity tests use to scale the floating tolerance the guide's "What to Check"
+section says fused kernels agree within. Results are numpy float64 arrays for
+float32 inputs and numpy longdouble arrays for float64 inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Score-arithmetic op codes understood by oracle.cpp (its own numbering).
+OPS = {
+    "mul": 0,             # s <- c * s
+    "add": 1,             # s <- s + c
+    "add_rows": 2,        # s <- s + a_i
+    "add_columns": 3,     # s <- s + b_j
+    "weight_rows": 4,     # s <- w_i * s
+    "weight_columns": 5,  # s <- u_j * s
+    "exp": 6,             # s <- exp(s)
+}
+METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with g++ (OpenMP, no fast-math). Returns its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-Wall", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _CExpr(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("metric", ctypes.c_int),
+        ("gamma", ctypes.c_double),
+        ("X", ctypes.c_void_p),
+        ("N", ctypes.c_int64),
+        ("ldx", ctypes.c_int64),
+        ("Y", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("ldy", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("n_ops", ctypes.c_int),
+        ("op_kind", ctypes.POINTER(ctypes.c_int)),
+        ("op_scalar", ctypes.POINTER(ctypes.c_double)),
+        ("op_vec", ctypes.POINTER(ctypes.c_void_p)),
+    ]
+
+
+def _open(path: str):
+    """Open an oracle build at `path` and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    vp, i64, p64 = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)
+    pe = ctypes.POINTER(_CExpr)
+    lib.oracle_scores.argtypes = [pe, p64, i64, vp, vp]
+    lib.oracle_matmul.argtypes = [pe, vp, i64, i64, p64, i64, vp, vp]
+    lib.oracle_displacement.argtypes = [pe, p64, i64, vp, vp]
+    lib.oracle_logsumexp.argtypes = [pe, ctypes.c_int, p64, i64, vp, vp]
+    lib.oracle_softmax_matmul.argtypes = [pe, vp, i64, i64, p64, i64, vp, vp]
+    lib.oracle_topk.argtypes = [pe, ctypes.c_int, ctypes.c_int, p64, i64, vp, p64, vp]
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_real_size.argtypes = [ctypes.c_int]
+    lib.oracle_real_size.restype = ctypes.c_int
+    assert lib.oracle_real_size(1) == np.dtype(np.longdouble).itemsize, "long double layout mismatch"
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = _open(build())
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads every later oracle call uses."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _rows2d(a, dtype):
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError("expected %s array, got %s" % (dtype, a.dtype))
+    if a.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    if a.shape[0] > 0 and a.strides[1] != a.itemsize and a.shape[1] > 1:
+        a = np.ascontiguousarray(a)
+    if a.strides[0] % a.itemsize:
+        a = np.ascontiguousarray(a)
+    ld = a.strides[0] // a.itemsize if a.shape[0] > 1 else a.shape[1]
+    return a, max(int(ld), a.shape[1])
+
+
+class Expr:
+    """A bound pairwise score: metric on rows of X [N,D] and Y [M,D], then ops.
+
+    ``ops`` is a list of ``(name, arg)`` with name in ``OPS``: ``arg`` is a
+    float for "mul"/"add", a length-N array for "add_rows"/"weight_rows", a
+    length-M array for "add_columns"/"weight_columns" and ``None`` for "exp"
+    (Score Expressions section).
+    """
+
+    def __init__(self, X, Y, metric, gamma=1.0, ops=()):
+        X = np.asarray(X)
+        if X.dtype not in (np.float32, np.float64):
+            raise TypeError("oracle inputs are float32 or float64")
+        self.np_dtype = X.dtype
+        self.X, ldx = _rows2d(X, X.dtype)
+        self.Y, ldy = _rows2d(Y, X.dtype)
+        if self.X.shape[1] != self.Y.shape[1]:
+            raise ValueError("X and Y feature dims differ")
+        self.N, self.D = self.X.shape
+        self.M = self.Y.shape[0]
+        self.metric = metric
+        self.gamma = float(gamma)
+        self.real = np.float64 if X.dtype == np.float32 else np.longdouble
+        self._keep = []
+        kinds, scalars, vecs = [], [], []
+        for name, arg in ops:
+            kinds.append(OPS[name])
+            if name in ("mul", "add"):
+                scalars.append(float(arg))
+                vecs.append(None)
+            elif name == "exp":
+                scalars.append(0.0)
+                vecs.append(None)
+            else:
+                n = self.N if name.endswith("_rows") else self.M
+                v = np.ascontiguousarray(np.asarray(arg, dtype=X.dtype).reshape(-1))
+                if v.shape[0] != n:
+                    raise ValueError("%s needs %d values" % (name, n))
+                self._keep.append(v)
+                scalars.append(0.0)
+                vecs.append(v.ctypes.data)
+        nops = len(kinds)
+        self._kinds = (ctypes.c_int * max(nops, 1))(*kinds)
+        self._scalars = (ctypes.c_double * max(nops, 1))(*scalars)
+        self._vecs = (ctypes.c_void_p * max(nops, 1))(*vecs)
+        self._c = _CExpr(
+            0 if X.dtype == np.float32 else 1, METRICS[metric], self.gamma,
+            self.X.ctypes.data, self.N, ldx, self.Y.ctypes.data, self.M, ldy, self.D,
+            nops, self._kinds, self._scalars, self._vecs)
+
+    def _rows(self, rows):
+        if rows is None:
+            return None, self.N
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        if r.size and (r.min() < 0 or r.max() >= self.N):
+            raise IndexError("row index out of range")
+        return r, r.shape[0]
+
+    def _out(self, *shape):
+        return np.empty(shape, dtype=self.real), np.empty(shape, dtype=self.real)
+
+    def _V(self, V):
+        V, ldv = _rows2d(V, self.np_dtype)
+        if V.shape[0] != self.M:
+            raise ValueError("V needs M rows")
+        return V, ldv
+
+
+def _rp(r):
+    return None if r is None else r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def scores(e: Expr, rows=None):
+    """Dense scores s_ij for the listed rows (Score Expressions)."""
+    lib = _load()
+    r, n = e._rows(rows)
+    out, mag = e._out(n, e.M)
+    lib.oracle_scores(ctypes.byref(e._c), _rp(r), n, out.ctypes.data, mag.ctypes.data)
+    return out, mag
+
+
+def matmul(e: Expr, V, rows=None):
+    """Kernel product sum_j s_ij V[j,:] (Task Map, Nadaraya-Watson row)."""
+    lib = _load()
+    V, ldv = e._V(V)
+    r, n = e._rows(rows)
+    out, mag = e._out(n, V.shape[1])
+    lib.oracle_matmul(ctypes.byref(e._c), V.ctypes.data, V.shape[1], ldv, _rp(r), n, out.ctypes.data,
+                      mag.ctypes.data)
+    return out, mag
+
+
+def displacement(e: Expr, rows=None):
+    """sum_j s_ij (y_j - x_i) (Stein Variational Gradient Descent section)."""
+    lib = _load()
+    r, n = e._rows(rows)
+    out, mag = e._out(n, e.D)
+    lib.oracle_displacement(ctypes.byref(e._c), _rp(r), n, out.ctypes.data, mag.ctypes.data)
+    return out, mag
+
+
+def logsumexp(e: Expr, exclude_self=False, rows=None):
+    """Row log-sum-exp over j, optionally without j == i (Task Map, InfoNCE row)."""
+    lib = _load()
+    r, n = e._rows(rows)
+    out, mag = e._out(n)
+    lib.oracle_logsumexp(ctypes.byref(e._c), int(bool(exclude_self)), _rp(r), n, out.ctypes.data,
+                         mag.ctypes.data)
+    return out, mag
+
+
+def softmax_matmul(e: Expr, V, rows=None):
+    """softmax over j of s_ij, then @ V (Intro example; Task Map, Attention row)."""
+    lib = _load()
+    V, ldv = e._V(V)
+    r, n = e._rows(rows)
+    out, mag = e._out(n, V.shape[1])
+    lib.oracle_softmax_matmul(ctypes.byref(e._c), V.ctypes.data, V.shape[1], ldv, _rp(r), n,
+                              out.ctypes.data, mag.ctypes.data)
+    return out, mag
+
+
+def topk(e: Expr, k, largest=False, extra=0, rows=None):
+    """Row top-k by value, ties by lowest index (Task Map, k-NN and Chamfer rows).
+
+    Returns ``(values, indices, mag)`` with ``k + extra`` positions per row;
+    positions past M hold NaN / -1.
+    """
+    lib = _load()
+    r, n = e._rows(rows)
+    kk = int(k) + int(extra)
+    vals, mag = e._out(n, kk)
+    idx = np.empty((n, kk), dtype=np.int64)
+    lib.oracle_topk(ctypes.byref(e._c), kk, int(bool(largest)), _rp(r), n, vals.ctypes.data,
+                    idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), mag.ctypes.data)
+    return vals, idx, mag
+
+
+def svgd_direction(x, score, gamma, rows=None):
+    """SVGD direction (K@score - 2*gamma*K.displacement()) / n with K = rbf(x, x).
+
+    The host composition of two consumers, as in the SVGD section's
+    ``svgd_direction``; ``n`` is the number of particles.
+    """
+    e = Expr(x, x, "rbf", gamma=gamma)
+    km, km_mag = matmul(e, score, rows)
+    kd, kd_mag = displacement(e, rows)
+    n = e.N
+    g = e.real(gamma)
+    phi = (km - 2 * g * kd) / n
+    mag = (km_mag + 2 * g * kd_mag) / n
+    return phi, mag

@@ -1,0 +1,387 @@
+// CPU oracle for lazily evaluated pairwise scores.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing in the product path links, loads or calls
+// this file; only the test suite, the smoke check and the CPU-baseline leg of
+// the benchmark do. It shares no code, header or constant with the GPU library.
+//
+// What it computes (torchpairwise guide "Using Torchpairwise in Models"):
+//   * a pairwise score s_ij = f(x_i, y_j) for the built-in metrics "linear",
+//     "sqeuclidean" and "rbf" (Task Map table; Score Expressions; the SVGD
+//     section gives the rbf form exp(-gamma*|x-y|^2));
+//   * the per-pair score arithmetic applied left to right: scalar multiply
+//     and add, add_rows / add_columns, weight_rows / weight_columns and exp
+//     (Score Expressions section);
+//   * five consumers that reduce each row over j: the kernel product S@V and
+//     its row-mass column (Task Map, Nadaraya-Watson row), the displacement
+//     sum_j s_ij (y_j - x_i) (SVGD section), the row log-sum-exp with an
+//     optional exclusion of the self pair (Task Map, InfoNCE row), the
+//     softmax(S)@V product (Intro example, Attention row) and the row top-k
+//     with ties broken by lowest index (Task Map, k-NN row; argmin/min row).
+//
+// It is the plain definition written out: a double loop over pairs, the
+// metric in direct form (sum of squared differences, never the norm
+// expansion), each reduction two-pass over a per-row buffer of all M scores
+// (never online), in higher precision than the inputs: float32 inputs are
+// evaluated in double, float64 inputs in x87 80-bit long double. The pages
+// state that fused kernels agree with other evaluation orders only within a
+// floating tolerance (What to Check, "Precision"), so alongside every result
+// the oracle returns a first-order error magnitude `mag` that the tests use
+// to scale that tolerance.
+//
+// Parallelism: OpenMP over rows, nothing else. Build: g++ -O2 -fopenmp
+// (no -ffast-math).
+//
+// Error magnitudes (mu_ij is an upper bound on |s_ij| and on the first-order
+// sensitivity of s_ij to unit roundoff in any evaluation order):
+//   linear       mu = sum_d |x_d y_d|
+//   sqeuclidean  mu = sum_d (|x_d| + |y_d|)^2
+//   rbf          mu = k (1 + gamma * sum_d (|x_d| + |y_d|)^2)
+//   MUL c        mu <- |c| mu        (also MUL_ROWS / MUL_COLS with |w_i|, |u_j|)
+//   ADD c        mu <- mu + |s_new|  (also ADD_ROWS / ADD_COLS)
+//   EXP          mu <- exp(s_old) (1 + mu)
+// and per consumer:
+//   matmul        mag_c = sum_j (|s_ij| + mu_ij) |V_jc|
+//   displacement  mag_d = sum_j (|s_ij| + mu_ij) (|y_jd| + |x_id|)
+//   logsumexp     mag   = max_j mu_ij + log(l)   (l = sum_j exp(s_ij - m_i) >= 1)
+//   softmax@V     mag_c = sum_j p_ij (1 + mu_ij) |V_jc| + (sum_j p_ij mu_ij)(sum_j p_ij |V_jc|)
+//   top-k         mag   = mu of the selected pair
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <vector>
+#include <omp.h>
+
+extern "C" {
+
+// Mirrors the Python-side ctypes structure in oracle.py.
+typedef struct {
+  int dtype;                 // 0: float32 inputs, 1: float64 inputs
+  int metric;                // 0: linear, 1: sqeuclidean, 2: rbf
+  double gamma;              // rbf only
+  const void *X;             // [N, ldx] row-major, dtype
+  int64_t N, ldx;
+  const void *Y;             // [M, ldy] row-major, dtype
+  int64_t M, ldy;
+  int64_t D;
+  int n_ops;
+  const int *op_kind;        // n_ops entries, see OP_* below
+  const double *op_scalar;   // n_ops entries (MUL / ADD)
+  const void *const *op_vec; // n_ops entries, host vectors in dtype (ROWS: N, COLS: M)
+} oracle_expr;
+
+}  // extern "C"
+
+namespace {
+
+enum { OP_MUL = 0, OP_ADD = 1, OP_ADD_ROWS = 2, OP_ADD_COLS = 3, OP_MUL_ROWS = 4, OP_MUL_COLS = 5, OP_EXP = 6 };
+enum { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2 };
+
+inline double rexp(double v) { return std::exp(v); }
+inline long double rexp(long double v) { return expl(v); }
+inline double rlog(double v) { return std::log(v); }
+inline long double rlog(long double v) { return logl(v); }
+
+// One bound expression, inputs of type T, arithmetic in R.
+template <class T, class R>
+struct Expr {
+  const oracle_expr &e;
+  const T *X, *Y;
+  explicit Expr(const oracle_expr &ex)
+      : e(ex), X(static_cast<const T *>(ex.X)), Y(static_cast<const T *>(ex.Y)) {}
+
+  R x(int64_t i, int64_t d) const { return (R)X[i * e.ldx + d]; }
+  R y(int64_t j, int64_t d) const { return (R)Y[j * e.ldy + d]; }
+  R vec(int k, int64_t idx) const { return (R) static_cast<const T *>(e.op_vec[k])[idx]; }
+
+  // Score of pair (i, j) with its error magnitude.
+  R score(int64_t i, int64_t j, R *mu_out) const {
+    R s = 0, mu = 0;
+    if (e.metric == M_LINEAR) {
+      for (int64_t d = 0; d < e.D; ++d) {
+        R p = x(i, d) * y(j, d);
+        s += p;
+        mu += std::fabs(p);
+      }
+    } else {
+      R sum_sq = 0, spread = 0;
+      for (int64_t d = 0; d < e.D; ++d) {
+        R a = x(i, d), b = y(j, d);
+        R diff = a - b;
+        sum_sq += diff * diff;
+        R w = std::fabs(a) + std::fabs(b);
+        spread += w * w;
+      }
+      if (e.metric == M_SQEUCLIDEAN) {
+        s = sum_sq;
+        mu = spread;
+      } else {
+        s = rexp(-(R)e.gamma * sum_sq);
+        mu = s * (1 + (R)e.gamma * spread);
+      }
+    }
+    for (int k = 0; k < e.n_ops; ++k) {
+      switch (e.op_kind[k]) {
+        case OP_MUL: s = (R)e.op_scalar[k] * s; mu = std::fabs((R)e.op_scalar[k]) * mu; break;
+        case OP_ADD: s = s + (R)e.op_scalar[k]; mu = mu + std::fabs(s); break;
+        case OP_ADD_ROWS: s = s + vec(k, i); mu = mu + std::fabs(s); break;
+        case OP_ADD_COLS: s = s + vec(k, j); mu = mu + std::fabs(s); break;
+        case OP_MUL_ROWS: { R w = vec(k, i); s = w * s; mu = std::fabs(w) * mu; break; }
+        case OP_MUL_COLS: { R u = vec(k, j); s = u * s; mu = std::fabs(u) * mu; break; }
+        case OP_EXP: { R ex = rexp(s); mu = ex * (1 + mu); s = ex; break; }
+        default: break;
+      }
+    }
+    *mu_out = mu;
+    return s;
+  }
+};
+
+template <class T>
+using RealOf = typename std::conditional<std::is_same<T, float>::value, double, long double>::type;
+
+int64_t row_at(const int64_t *rows, int64_t r) { return rows ? rows[r] : r; }
+
+template <class T>
+void do_scores(const oracle_expr &ex, const int64_t *rows, int64_t n_rows, RealOf<T> *out, RealOf<T> *mag) {
+  using R = RealOf<T>;
+  Expr<T, R> E(ex);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int64_t i = row_at(rows, r);
+    for (int64_t j = 0; j < ex.M; ++j) {
+      R mu;
+      out[r * ex.M + j] = E.score(i, j, &mu);
+      mag[r * ex.M + j] = mu;
+    }
+  }
+}
+
+// Kernel product: out[i,c] = sum_j s_ij V[j,c].
+template <class T>
+void do_matmul(const oracle_expr &ex, const T *V, int64_t C, int64_t ldv, const int64_t *rows, int64_t n_rows,
+               RealOf<T> *out, RealOf<T> *mag) {
+  using R = RealOf<T>;
+  Expr<T, R> E(ex);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int64_t i = row_at(rows, r);
+    std::vector<R> acc(C, 0), m(C, 0);
+    for (int64_t j = 0; j < ex.M; ++j) {
+      R mu;
+      R s = E.score(i, j, &mu);
+      for (int64_t c = 0; c < C; ++c) {
+        R v = (R)V[j * ldv + c];
+        acc[c] += s * v;
+        m[c] += (std::fabs(s) + mu) * std::fabs(v);
+      }
+    }
+    for (int64_t c = 0; c < C; ++c) {
+      out[r * C + c] = acc[c];
+      mag[r * C + c] = m[c];
+    }
+  }
+}
+
+// Displacement: out[i,d] = sum_j s_ij (y_jd - x_id), evaluated directly.
+template <class T>
+void do_displacement(const oracle_expr &ex, const int64_t *rows, int64_t n_rows, RealOf<T> *out, RealOf<T> *mag) {
+  using R = RealOf<T>;
+  Expr<T, R> E(ex);
+  const int64_t D = ex.D;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int64_t i = row_at(rows, r);
+    std::vector<R> acc(D, 0), m(D, 0);
+    for (int64_t j = 0; j < ex.M; ++j) {
+      R mu;
+      R s = E.score(i, j, &mu);
+      for (int64_t d = 0; d < D; ++d) {
+        R yd = E.y(j, d), xd = E.x(i, d);
+        acc[d] += s * (yd - xd);
+        m[d] += (std::fabs(s) + mu) * (std::fabs(yd) + std::fabs(xd));
+      }
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      out[r * D + d] = acc[d];
+      mag[r * D + d] = m[d];
+    }
+  }
+}
+
+// Row log-sum-exp over j, two-pass over the row's buffer of scores.
+template <class T>
+void do_logsumexp(const oracle_expr &ex, int exclude_self, const int64_t *rows, int64_t n_rows, RealOf<T> *out,
+                  RealOf<T> *mag) {
+  using R = RealOf<T>;
+  Expr<T, R> E(ex);
+#pragma omp parallel
+  {
+    std::vector<R> s(ex.M), mu(ex.M);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t i = row_at(rows, r);
+      int64_t n = 0;
+      for (int64_t j = 0; j < ex.M; ++j) {
+        if (exclude_self && j == i) continue;
+        s[n] = E.score(i, j, &mu[n]);
+        ++n;
+      }
+      if (n == 0) {
+        out[r] = -std::numeric_limits<R>::infinity();
+        mag[r] = 0;
+        continue;
+      }
+      R m = s[0], mumax = mu[0];
+      for (int64_t t = 1; t < n; ++t) {
+        m = std::max(m, s[t]);
+        mumax = std::max(mumax, mu[t]);
+      }
+      R l = 0;
+      for (int64_t t = 0; t < n; ++t) l += rexp(s[t] - m);
+      out[r] = m + rlog(l);
+      mag[r] = mumax + rlog(l);
+    }
+  }
+}
+
+// softmax(S)@V over j, two-pass over the row's buffer of scores.
+template <class T>
+void do_softmax_matmul(const oracle_expr &ex, const T *V, int64_t C, int64_t ldv, const int64_t *rows,
+                       int64_t n_rows, RealOf<T> *out, RealOf<T> *mag) {
+  using R = RealOf<T>;
+  Expr<T, R> E(ex);
+#pragma omp parallel
+  {
+    std::vector<R> s(ex.M), mu(ex.M), acc(C), av(C), apv(C);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t i = row_at(rows, r);
+      if (ex.M == 0) {
+        for (int64_t c = 0; c < C; ++c) out[r * C + c] = mag[r * C + c] = 0;
+        continue;
+      }
+      for (int64_t j = 0; j < ex.M; ++j) s[j] = E.score(i, j, &mu[j]);
+      R m = s[0];
+      for (int64_t j = 1; j < ex.M; ++j) m = std::max(m, s[j]);
+      R l = 0;
+      for (int64_t j = 0; j < ex.M; ++j) l += rexp(s[j] - m);
+      std::fill(acc.begin(), acc.end(), (R)0);
+      std::fill(av.begin(), av.end(), (R)0);
+      std::fill(apv.begin(), apv.end(), (R)0);
+      R pmu = 0;
+      for (int64_t j = 0; j < ex.M; ++j) {
+        R p = rexp(s[j] - m) / l;
+        pmu += p * mu[j];
+        for (int64_t c = 0; c < C; ++c) {
+          R v = (R)V[j * ldv + c];
+          acc[c] += p * v;
+          av[c] += p * (1 + mu[j]) * std::fabs(v);
+          apv[c] += p * std::fabs(v);
+        }
+      }
+      for (int64_t c = 0; c < C; ++c) {
+        out[r * C + c] = acc[c];
+        mag[r * C + c] = av[c] + pmu * apv[c];
+      }
+    }
+  }
+}
+
+// Row top-k: the row's (s_ij, j) ordered by value (ascending, or descending
+// when `largest`), equal values by ascending j; the first kk = k + extra kept.
+template <class T>
+void do_topk(const oracle_expr &ex, int kk, int largest, const int64_t *rows, int64_t n_rows, RealOf<T> *values,
+             int64_t *indices, RealOf<T> *mag) {
+  using R = RealOf<T>;
+  Expr<T, R> E(ex);
+  struct Entry { R v; R mu; int64_t j; };
+  const int64_t keep = std::min<int64_t>(kk, ex.M);
+#pragma omp parallel
+  {
+    std::vector<Entry> buf(ex.M);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t i = row_at(rows, r);
+      for (int64_t j = 0; j < ex.M; ++j) {
+        buf[j].v = E.score(i, j, &buf[j].mu);
+        buf[j].j = j;
+      }
+      auto before = [largest](const Entry &a, const Entry &b) {
+        if (a.v != b.v) return largest ? (a.v > b.v) : (a.v < b.v);
+        return a.j < b.j;
+      };
+      std::partial_sort(buf.begin(), buf.begin() + keep, buf.end(), before);
+      for (int64_t p = 0; p < kk; ++p) {
+        if (p < keep) {
+          values[r * kk + p] = buf[p].v;
+          indices[r * kk + p] = buf[p].j;
+          mag[r * kk + p] = buf[p].mu;
+        } else {
+          values[r * kk + p] = std::numeric_limits<R>::quiet_NaN();
+          indices[r * kk + p] = -1;
+          mag[r * kk + p] = 0;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Threads used by every oracle call (0 leaves OpenMP's default).
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+
+// Size in bytes of the real type results are returned in (8 or sizeof(long double)).
+int oracle_real_size(int dtype) { return dtype == 0 ? (int)sizeof(double) : (int)sizeof(long double); }
+
+// For every call below: `rows` lists the global row indices to evaluate
+// (NULL means 0..N-1 and then n_rows must equal N); outputs are row-major over
+// that list, in double for float32 inputs and long double for float64 inputs.
+
+void oracle_scores(const oracle_expr *e, const int64_t *rows, int64_t n_rows, void *out, void *mag) {
+  if (e->dtype == 0) do_scores<float>(*e, rows, n_rows, (double *)out, (double *)mag);
+  else do_scores<double>(*e, rows, n_rows, (long double *)out, (long double *)mag);
+}
+
+void oracle_matmul(const oracle_expr *e, const void *V, int64_t C, int64_t ldv, const int64_t *rows,
+                   int64_t n_rows, void *out, void *mag) {
+  if (e->dtype == 0) do_matmul<float>(*e, (const float *)V, C, ldv, rows, n_rows, (double *)out, (double *)mag);
+  else do_matmul<double>(*e, (const double *)V, C, ldv, rows, n_rows, (long double *)out, (long double *)mag);
+}
+
+void oracle_displacement(const oracle_expr *e, const int64_t *rows, int64_t n_rows, void *out, void *mag) {
+  if (e->dtype == 0) do_displacement<float>(*e, rows, n_rows, (double *)out, (double *)mag);
+  else do_displacement<double>(*e, rows, n_rows, (long double *)out, (long double *)mag);
+}
+
+void oracle_logsumexp(const oracle_expr *e, int exclude_self, const int64_t *rows, int64_t n_rows, void *out,
+                      void *mag) {
+  if (e->dtype == 0) do_logsumexp<float>(*e, exclude_self, rows, n_rows, (double *)out, (double *)mag);
+  else do_logsumexp<double>(*e, exclude_self, rows, n_rows, (long double *)out, (long double *)mag);
+}
+
+void oracle_softmax_matmul(const oracle_expr *e, const void *V, int64_t C, int64_t ldv, const int64_t *rows,
+                           int64_t n_rows, void *out, void *mag) {
+  if (e->dtype == 0)
+    do_softmax_matmul<float>(*e, (const float *)V, C, ldv, rows, n_rows, (double *)out, (double *)mag);
+  else
+    do_softmax_matmul<double>(*e, (const double *)V, C, ldv, rows, n_rows, (long double *)out,
+                              (long double *)mag);
+}
+
+void oracle_topk(const oracle_expr *e, int kk, int largest, const int64_t *rows, int64_t n_rows, void *values,
+                 int64_t *indices, void *mag) {
+  if (e->dtype == 0)
+    do_topk<float>(*e, kk, largest, rows, n_rows, (double *)values, indices, (double *)mag);
+  else
+    do_topk<double>(*e, kk, largest, rows, n_rows, (long double *)values, indices, (long double *)mag);
+}
+
+}  // extern "C"

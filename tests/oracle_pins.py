@@ -1,0 +1,457 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each pin is a plain function that raises AssertionError on a mismatch. They
+are collected as tests by test_oracle_pins.py and also run against oracle
+builds with planted mistakes by test_oracle_mutants.py, which requires every
+planted mistake to trip at least one pin.
+
+Independent references used here: hand-derived closed forms
+(tests/golden/closed_forms.json), torch float64 library routines on dense
+tiny inputs (cdist, matmul, logsumexp, softmax, stable sort, argmin,
+autograd), exact integer arithmetic, and identities of the definitions.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_forms.json")
+_MATH = {"exp": math.exp, "log": math.log, "__builtins__": {}}
+DTYPES = (np.float32, np.float64)
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return {c["name"]: c for c in json.load(f)["cases"]}
+
+
+def _ev(expr):
+    return eval(expr, _MATH)  # expressions from the fixture: exp/log over literals only
+
+
+def _close(a, b, rtol=1e-13, atol=1e-13, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, "%s: shape %s vs %s" % (what, a.shape, b.shape)
+    ok = np.abs(a - b) <= atol + rtol * np.abs(b)
+    assert ok.all(), "%s: max abs diff %g" % (what, np.max(np.abs(a - b)))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- dense refs
+def dense_scores_torch(X, Y, metric, gamma=1.0, ops=()):
+    """Dense [N,M] scores in torch float64 from library routines."""
+    Xt = torch.as_tensor(np.asarray(X, np.float64))
+    Yt = torch.as_tensor(np.asarray(Y, np.float64))
+    if metric == "linear":
+        S = Xt @ Yt.T
+    else:
+        S = torch.cdist(Xt, Yt, compute_mode="donot_use_mm_for_euclid_dist") ** 2
+        if metric == "rbf":
+            S = torch.exp(-gamma * S)
+    for name, arg in ops:
+        if name == "mul":
+            S = S * arg
+        elif name == "add":
+            S = S + arg
+        elif name == "add_rows":
+            S = S + torch.as_tensor(np.asarray(arg, np.float64))[:, None]
+        elif name == "add_columns":
+            S = S + torch.as_tensor(np.asarray(arg, np.float64))[None, :]
+        elif name == "weight_rows":
+            S = S * torch.as_tensor(np.asarray(arg, np.float64))[:, None]
+        elif name == "weight_columns":
+            S = S * torch.as_tensor(np.asarray(arg, np.float64))[None, :]
+        elif name == "exp":
+            S = torch.exp(S)
+    return S
+
+
+def _inputs(seed, n, m, d, dtype, scale=1.0):
+    r = _rng(seed)
+    X = (scale * r.standard_normal((n, d))).astype(dtype)
+    Y = (scale * r.standard_normal((m, d))).astype(dtype)
+    return X, Y
+
+
+# ---------------------------------------------------------------- metric pins
+def pin_metric_closed_forms():
+    """Hand closed forms: x=(1,2), y=(3,5) (fixture metric_values)."""
+    c = _golden()["metric_values"]
+    for dt in DTYPES:
+        X = np.array(c["X"], dt)
+        Y = np.array(c["Y"], dt)
+        for metric, exp_rows in c["expect"].items():
+            out, _ = oracle.scores(oracle.Expr(X, Y, metric, gamma=c["gamma"]))
+            want = [[_ev(v) for v in row] for row in exp_rows]
+            _close(out, want, what="metric %s %s" % (metric, dt.__name__))
+
+
+def pin_grid_distances():
+    c = _golden()["grid_distances"]
+    for dt in DTYPES:
+        X = np.array(c["X"], dt)
+        Y = np.array(c["Y"], dt)
+        out, _ = oracle.scores(oracle.Expr(X, Y, "sqeuclidean"))
+        want = [[_ev(v) for v in row] for row in c["expect"]["sqeuclidean"]]
+        _close(out, want, rtol=0, atol=0, what="grid distances")
+
+
+def pin_rbf_self_is_one():
+    """rbf(x, x) = 1 exactly, for any x and gamma."""
+    for dt in DTYPES:
+        X, _ = _inputs(1, 13, 1, 7, dt, scale=3.0)
+        out, _ = oracle.scores(oracle.Expr(X, X, "rbf", gamma=0.37))
+        d = np.diag(np.asarray(out, np.float64))
+        assert np.all(d == 1.0), "rbf(x,x) != 1"
+
+
+def pin_metric_symmetry():
+    """f(x, y) = f(y, x) for all three metrics."""
+    for dt in DTYPES:
+        X, Y = _inputs(2, 9, 11, 5, dt)
+        for metric in ("linear", "sqeuclidean", "rbf"):
+            a, _ = oracle.scores(oracle.Expr(X, Y, metric, gamma=0.3))
+            b, _ = oracle.scores(oracle.Expr(Y, X, metric, gamma=0.3))
+            _close(a, np.asarray(b).T, what="symmetry %s" % metric)
+
+
+def pin_translation_invariance():
+    """sqeuclidean and rbf are unchanged by a common shift (exact on integers)."""
+    r = _rng(3)
+    for dt in DTYPES:
+        X = r.integers(-5, 6, (7, 4)).astype(dt)
+        Y = r.integers(-5, 6, (8, 4)).astype(dt)
+        t = np.array([3, -2, 7, 1], dt)
+        for metric in ("sqeuclidean", "rbf"):
+            a, _ = oracle.scores(oracle.Expr(X, Y, metric, gamma=0.25))
+            b, _ = oracle.scores(oracle.Expr(X + t, Y + t, metric, gamma=0.25))
+            _close(a, b, rtol=0, atol=0, what="translation %s" % metric)
+
+
+def pin_metrics_vs_dense():
+    """All metrics against torch float64 matmul / cdist on small random inputs."""
+    for dt in DTYPES:
+        for d in (1, 3, 16, 33, 64):
+            X, Y = _inputs(10 + d, 7, 9, d, dt)
+            for metric in ("linear", "sqeuclidean", "rbf"):
+                out, mag = oracle.scores(oracle.Expr(X, Y, metric, gamma=0.05))
+                ref = dense_scores_torch(X, Y, metric, 0.05).numpy()
+                _close(out, ref, rtol=1e-12, atol=1e-12, what="dense %s D=%d" % (metric, d))
+                assert np.all(np.asarray(mag, np.float64) >= np.abs(np.asarray(out, np.float64)) - 1e-12)
+
+
+# ---------------------------------------------------------------- op chain pins
+def pin_ops_each_vs_dense():
+    """Every score op, alone and in sequence, against dense torch float64."""
+    for dt in DTYPES:
+        X, Y = _inputs(20, 6, 8, 4, dt)
+        r = _rng(21)
+        a = r.standard_normal(6).astype(dt)
+        b = r.standard_normal(8).astype(dt)
+        w = r.standard_normal(6).astype(dt)
+        u = r.standard_normal(8).astype(dt)
+        chains = [
+            [("mul", 0.5)], [("add", 1.25)], [("add_rows", a)], [("add_columns", b)],
+            [("weight_rows", w)], [("weight_columns", u)], [("mul", 0.1), ("exp", None)],
+            [("mul", 2.0), ("add", 1.0)], [("add", 1.0), ("mul", 2.0)],
+            [("add_rows", a), ("weight_columns", u)], [("weight_columns", u), ("add_rows", a)],
+            [("mul", -0.5), ("add_rows", a), ("add_columns", b), ("exp", None), ("weight_rows", w)],
+        ]
+        for ops in chains:
+            for metric in ("linear", "sqeuclidean"):
+                out, _ = oracle.scores(oracle.Expr(X, Y, metric, ops=ops))
+                ref = dense_scores_torch(X, Y, metric, 1.0, ops).numpy()
+                _close(out, ref, rtol=1e-12, atol=1e-12,
+                       what="ops %s %s" % ([o[0] for o in ops], metric))
+
+
+def pin_op_order_matters():
+    """Left-to-right application: (s*2)+1 differs from (s+1)*2 by exactly 1."""
+    X, Y = _inputs(22, 3, 4, 2, np.float64)
+    a, _ = oracle.scores(oracle.Expr(X, Y, "linear", ops=[("mul", 2.0), ("add", 1.0)]))
+    b, _ = oracle.scores(oracle.Expr(X, Y, "linear", ops=[("add", 1.0), ("mul", 2.0)]))
+    _close(np.asarray(b, np.float64) - np.asarray(a, np.float64), np.ones((3, 4)), what="op order")
+
+
+# ---------------------------------------------------------------- matmul pins
+def pin_matmul_golden():
+    c = _golden()["grid_kernel_product"]
+    for dt in DTYPES:
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], gamma=c["gamma"])
+        out, _ = oracle.matmul(e, np.array(c["V"], dt))
+        _close(out, [[_ev(v) for v in row] for row in c["expect"]], what="kernel product golden")
+
+
+def pin_matmul_vs_dense():
+    for dt in DTYPES:
+        X, Y = _inputs(30, 9, 13, 5, dt)
+        V = _rng(31).standard_normal((13, 6)).astype(dt)
+        for metric in ("linear", "sqeuclidean", "rbf"):
+            ops = [("mul", 0.3), ("add_columns", _rng(32).standard_normal(13).astype(dt))]
+            out, mag = oracle.matmul(oracle.Expr(X, Y, metric, gamma=0.2, ops=ops), V)
+            S = dense_scores_torch(X, Y, metric, 0.2, ops)
+            ref = (S @ torch.as_tensor(V.astype(np.float64))).numpy()
+            _close(out, ref, rtol=1e-12, atol=1e-12, what="matmul %s" % metric)
+
+
+def pin_matmul_exact_integers():
+    """Integer inputs, linear metric: the product is exact."""
+    r = _rng(33)
+    for dt in DTYPES:
+        X = r.integers(-9, 10, (5, 3)).astype(dt)
+        Y = r.integers(-9, 10, (7, 3)).astype(dt)
+        V = r.integers(-9, 10, (7, 4)).astype(dt)
+        out, _ = oracle.matmul(oracle.Expr(X, Y, "linear"), V)
+        ref = X.astype(np.int64) @ Y.astype(np.int64).T @ V.astype(np.int64)
+        assert np.array_equal(np.asarray(out, np.float64), ref.astype(np.float64)), "integer product"
+
+
+def pin_row_mass_isolated_points():
+    """Ones column = row mass; for points 100 apart (gamma 1) only the self pair
+    survives, so the mass is exactly 1 and the product returns V_i."""
+    for dt in DTYPES:
+        X = (100.0 * np.arange(6, dtype=np.float64)[:, None] * np.array([[1.0, 0.5]])).astype(dt)
+        V = np.concatenate([_rng(34).standard_normal((6, 2)), np.ones((6, 1))], 1).astype(dt)
+        out, _ = oracle.matmul(oracle.Expr(X, X, "rbf", gamma=1.0), V)
+        _close(out, V.astype(np.float64), rtol=0, atol=0, what="isolated row mass")
+
+
+# ---------------------------------------------------------------- displacement pins
+def pin_displacement_golden():
+    c = _golden()["grid_displacement"]
+    for dt in DTYPES:
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], gamma=c["gamma"])
+        out, _ = oracle.displacement(e)
+        _close(out, [[_ev(v) for v in row] for row in c["expect"]], what="displacement golden")
+
+
+def pin_displacement_autograd():
+    """For rbf, d/dx_i sum_j k(x_i, y_j) = 2 gamma sum_j k_ij (y_j - x_i)."""
+    for dt in DTYPES:
+        X, Y = _inputs(40, 6, 9, 3, dt)
+        g = 0.7
+        out, _ = oracle.displacement(oracle.Expr(X, Y, "rbf", gamma=g))
+        Xt = torch.tensor(X.astype(np.float64), requires_grad=True)
+        Yt = torch.tensor(Y.astype(np.float64))
+        K = torch.exp(-g * ((Xt[:, None, :] - Yt[None, :, :]) ** 2).sum(-1))
+        (grad,) = torch.autograd.grad(K.sum(), Xt)
+        _close(out, grad.numpy() / (2 * g), rtol=1e-12, atol=1e-12, what="displacement autograd")
+
+
+def pin_displacement_identity():
+    """disp = S@Y - x_i * (S@1), via the oracle's own product on any expression."""
+    for dt in DTYPES:
+        X, Y = _inputs(41, 7, 10, 4, dt)
+        e = oracle.Expr(X, Y, "sqeuclidean", ops=[("mul", -0.1), ("exp", None)])
+        disp, _ = oracle.displacement(e)
+        V = np.concatenate([Y, np.ones((10, 1), dt)], 1)
+        prod, _ = oracle.matmul(e, V)
+        prod = np.asarray(prod, np.float64)
+        ref = prod[:, :4] - X.astype(np.float64) * prod[:, 4:5]
+        _close(disp, ref, rtol=1e-11, atol=1e-11, what="displacement identity")
+
+
+# ---------------------------------------------------------------- SVGD pin
+def pin_svgd_autograd():
+    """SVGD direction against the dense autograd form of the SVGD section:
+    phi(x_i) = 1/n sum_j [k(x_j,x_i) grad log p(x_j) + grad_{x_j} k(x_j,x_i)]."""
+    r = _rng(50)
+    n, d, g = 12, 3, 1.0 / 16.0
+    x = r.standard_normal((n, d))
+    score = -x
+    phi, _ = oracle.svgd_direction(x, score, g)
+    xt = torch.tensor(x)
+    xj = xt.clone().requires_grad_(True)
+    K = torch.exp(-g * ((xj[:, None, :] - xt[None, :, :]) ** 2).sum(-1))  # K[j, i] = k(x_j, x_i)
+    rep = torch.zeros(n, d, dtype=torch.float64)
+    for i in range(n):
+        (gi,) = torch.autograd.grad(K[:, i].sum(), xj, retain_graph=True)
+        rep[i] = gi.sum(0)  # row j of gi is grad_{x_j} k(x_j, x_i)
+    drive = K.detach().T @ torch.tensor(score)
+    ref = (drive + rep) / n
+    _close(phi, ref.numpy(), rtol=1e-12, atol=1e-12, what="svgd autograd")
+
+
+# ---------------------------------------------------------------- logsumexp pins
+def pin_lse_golden():
+    c = _golden()["grid_logsumexp"]
+    for dt in DTYPES:
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], ops=c["ops"])
+        out, _ = oracle.logsumexp(e)
+        _close(out, [_ev(v) for v in c["expect_logsumexp"]], what="lse golden")
+        out, _ = oracle.logsumexp(e, exclude_self=True)
+        _close(out, [_ev(v) for v in c["expect_logsumexp_exclude_self"]], what="lse golden exclude")
+
+
+def pin_lse_equal_scores():
+    """M equal scores s: lse = s + log M; excluding self, s + log(M - 1)."""
+    for dt in DTYPES:
+        M = 37
+        X = np.full((5, 2), 0.5, dt)
+        Y = np.tile(np.array([[1.0, 2.0]], dt), (M, 1))
+        s = 0.5 * 1.0 + 0.5 * 2.0
+        out, _ = oracle.logsumexp(oracle.Expr(X, Y, "linear"))
+        _close(out, np.full(5, s + math.log(M)), what="lse equal")
+        out, _ = oracle.logsumexp(oracle.Expr(X, Y, "linear"), exclude_self=True)
+        _close(out, np.full(5, s + math.log(M - 1)), what="lse equal exclude")
+
+
+def pin_lse_fully_excluded():
+    """A row whose only pair is excluded has lse = -inf."""
+    X = np.array([[1.0, 2.0]], np.float32)
+    out, _ = oracle.logsumexp(oracle.Expr(X, X, "linear"), exclude_self=True)
+    assert np.isneginf(np.asarray(out, np.float64)).all()
+
+
+def pin_lse_vs_torch():
+    for dt in DTYPES:
+        X, Y = _inputs(60, 8, 8, 6, dt)
+        b = _rng(61).standard_normal(8).astype(dt)
+        ops = [("mul", 1.0 / 0.07), ("add_rows", b)]
+        e = oracle.Expr(X, Y, "linear", ops=ops)
+        S = dense_scores_torch(X, Y, "linear", 1.0, ops)
+        out, _ = oracle.logsumexp(e)
+        _close(out, torch.logsumexp(S, -1).numpy(), rtol=1e-12, what="lse torch")
+        Sm = S.clone()
+        Sm.fill_diagonal_(-float("inf"))
+        out, _ = oracle.logsumexp(e, exclude_self=True)
+        _close(out, torch.logsumexp(Sm, -1).numpy(), rtol=1e-12, what="lse torch exclude")
+
+
+def pin_lse_row_shift():
+    """lse(s + b_i) = b_i + lse(s)."""
+    X, Y = _inputs(62, 6, 9, 3, np.float64)
+    b = _rng(63).standard_normal(6)
+    a, _ = oracle.logsumexp(oracle.Expr(X, Y, "sqeuclidean", ops=[("mul", -0.5)]))
+    c, _ = oracle.logsumexp(oracle.Expr(X, Y, "sqeuclidean", ops=[("mul", -0.5), ("add_rows", b)]))
+    _close(np.asarray(c, np.float64), np.asarray(a, np.float64) + b, rtol=1e-13, what="lse shift")
+
+
+# ---------------------------------------------------------------- softmax pins
+def pin_softmax_golden():
+    c = _golden()["grid_softmax_matmul"]
+    for dt in DTYPES:
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], ops=c["ops"])
+        out, _ = oracle.softmax_matmul(e, np.array(c["V"], dt))
+        _close(out, [[_ev(v) for v in row] for row in c["expect"]], what="softmax golden")
+
+
+def pin_softmax_rows_sum_to_one():
+    """V = ones gives 1; V = [V, 1] has last column 1."""
+    for dt in DTYPES:
+        X, Y = _inputs(70, 6, 11, 8, dt, scale=2.0)
+        V = np.concatenate([_rng(71).standard_normal((11, 3)), np.ones((11, 1))], 1).astype(dt)
+        out, _ = oracle.softmax_matmul(oracle.Expr(X, Y, "linear", ops=[("mul", 0.5)]), V)
+        _close(np.asarray(out, np.float64)[:, -1], np.ones(6), what="softmax rows sum")
+
+
+def pin_softmax_vs_torch():
+    for dt in DTYPES:
+        X, Y = _inputs(72, 7, 10, 5, dt)
+        V = _rng(73).standard_normal((10, 4)).astype(dt)
+        ops = [("mul", 1.0 / math.sqrt(5.0))]
+        out, _ = oracle.softmax_matmul(oracle.Expr(X, Y, "linear", ops=ops), V)
+        S = dense_scores_torch(X, Y, "linear", 1.0, ops)
+        ref = torch.softmax(S, -1) @ torch.as_tensor(V.astype(np.float64))
+        _close(out, ref.numpy(), rtol=1e-12, atol=1e-13, what="softmax torch")
+
+
+def pin_softmax_add_rows_invariant():
+    X, Y = _inputs(74, 5, 9, 3, np.float64)
+    V = _rng(75).standard_normal((9, 2))
+    b = 10 * _rng(76).standard_normal(5)
+    a, _ = oracle.softmax_matmul(oracle.Expr(X, Y, "linear"), V)
+    c, _ = oracle.softmax_matmul(oracle.Expr(X, Y, "linear", ops=[("add_rows", b)]), V)
+    _close(a, c, rtol=1e-13, atol=1e-14, what="softmax add_rows invariance")
+
+
+def pin_softmax_hard_limit():
+    """A large scale turns softmax into the row argmax: the output is V[argmax]."""
+    X, Y = _inputs(77, 6, 12, 4, np.float64)
+    V = _rng(78).standard_normal((12, 3))
+    out, _ = oracle.softmax_matmul(oracle.Expr(X, Y, "linear", ops=[("mul", 1e4)]), V)
+    am = np.argmax(X @ Y.T, axis=1)
+    _close(out, V[am], rtol=1e-9, atol=1e-9, what="softmax hard limit")
+
+
+# ---------------------------------------------------------------- top-k pins
+def pin_topk_golden():
+    c = _golden()["grid_distances"]
+    for dt in DTYPES:
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), "sqeuclidean")
+        v, i, _ = oracle.topk(e, 3)
+        assert np.array_equal(i, c["topk_smallest_3"]["indices"]), i
+        _close(v, c["topk_smallest_3"]["values"], rtol=0, atol=0, what="topk golden values")
+        v, i, _ = oracle.topk(e, 3, largest=True)
+        assert np.array_equal(i, c["topk_largest_3"]["indices"]), i
+        _close(v, c["topk_largest_3"]["values"], rtol=0, atol=0, what="topk largest golden")
+        v, i, _ = oracle.topk(e, 1)
+        assert np.array_equal(i[:, 0], c["min"]["indices"])
+        _close(v[:, 0], c["min"]["values"], rtol=0, atol=0, what="min golden")
+
+
+def _stable_ref(S, k, largest):
+    key = -S if largest else S
+    vals, idx = torch.sort(key, dim=-1, stable=True)
+    return idx[:, :k].numpy()
+
+
+def pin_topk_vs_stable_sort():
+    """Integer grids (many exact ties) and duplicated rows: indices equal a
+    stable sort's, lowest index first among equal values, both directions."""
+    r = _rng(80)
+    for dt in DTYPES:
+        X = r.integers(-2, 3, (9, 2)).astype(dt)
+        Y = r.integers(-2, 3, (23, 2)).astype(dt)
+        Y[7] = Y[3]
+        Y[15] = Y[3]
+        S = dense_scores_torch(X, Y, "sqeuclidean")
+        for k in (1, 5, 23):
+            for largest in (False, True):
+                v, i, _ = oracle.topk(oracle.Expr(X, Y, "sqeuclidean"), k, largest=largest)
+                assert np.array_equal(i, _stable_ref(S, k, largest)), (k, largest)
+                _close(v, torch.gather(S, 1, torch.as_tensor(i)).numpy(), rtol=1e-14, atol=0, what="topk vals")
+
+
+def pin_topk_argmin():
+    """k = 1 equals argmin (first occurrence), on random inputs."""
+    for dt in DTYPES:
+        X, Y = _inputs(81, 10, 30, 4, dt)
+        _, i, _ = oracle.topk(oracle.Expr(X, Y, "sqeuclidean"), 1)
+        S = dense_scores_torch(X, Y, "sqeuclidean")
+        assert np.array_equal(i[:, 0], torch.argmin(S, -1).numpy())
+
+
+def pin_topk_extra_positions():
+    """Positions past M are padded with NaN / -1."""
+    X, Y = _inputs(82, 2, 3, 2, np.float32)
+    v, i, _ = oracle.topk(oracle.Expr(X, Y, "linear"), 3, extra=2)
+    assert np.all(i[:, 3:] == -1) and np.all(np.isnan(np.asarray(v, np.float64)[:, 3:]))
+    assert sorted(i[0, :3].tolist()) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------- row subsets
+def pin_row_subset_matches_full():
+    X, Y = _inputs(90, 17, 12, 3, np.float32)
+    V = _rng(91).standard_normal((12, 2)).astype(np.float32)
+    e = oracle.Expr(X, Y, "rbf", gamma=0.3)
+    full, _ = oracle.matmul(e, V)
+    rows = np.array([16, 0, 5])
+    part, _ = oracle.matmul(e, V, rows=rows)
+    _close(part, np.asarray(full)[rows], rtol=0, atol=0, what="row subset")
+    lf, _ = oracle.logsumexp(e, exclude_self=True)
+    lp, _ = oracle.logsumexp(e, exclude_self=True, rows=rows)
+    _close(lp, np.asarray(lf)[rows], rtol=0, atol=0, what="row subset lse")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,75 @@
+"""Planted mistakes in the oracle must each trip at least one pin (CPU only).
+
+Each mutant is a one-line textual change to oracle.cpp -- a dropped term, a
+wrong sign, a wrong index, a mixed-up operand, a reversed order -- compiled to
+a temporary library. Every pin of oracle_pins.py is run against it; the test
+passes only if some pin fails. Mutations keep every access in bounds.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")
+
+MUTANTS = [
+    ("linear_drops_first_feature",
+     "for (int64_t d = 0; d < e.D; ++d) {\n        R p = x(i, d) * y(j, d);",
+     "for (int64_t d = 1; d < e.D; ++d) {\n        R p = x(i, d) * y(j, d);"),
+    ("difference_sign", "R diff = a - b;", "R diff = a + b;"),
+    ("rbf_half_exponent", "s = rexp(-(R)e.gamma * sum_sq);", "s = rexp(-(R)e.gamma * sum_sq / 2);"),
+    ("x_read_from_y", "R x(int64_t i, int64_t d) const { return (R)X[i * e.ldx + d]; }",
+     "R x(int64_t i, int64_t d) const { return (R)Y[(i % e.M) * e.ldy + d]; }"),
+    ("mul_divides", "case OP_MUL: s = (R)e.op_scalar[k] * s;", "case OP_MUL: s = s / (R)e.op_scalar[k];"),
+    ("add_rows_by_column", "case OP_ADD_ROWS: s = s + vec(k, i);", "case OP_ADD_ROWS: s = s + vec(k, j % e.N);"),
+    ("add_columns_by_row", "case OP_ADD_COLS: s = s + vec(k, j);", "case OP_ADD_COLS: s = s + vec(k, i % e.M);"),
+    ("weight_rows_by_column", "R w = vec(k, i);", "R w = vec(k, j % e.N);"),
+    ("weight_columns_by_row", "R u = vec(k, j);", "R u = vec(k, i % e.M);"),
+    ("exp_sign", "R ex = rexp(s);", "R ex = rexp(-s);"),
+    ("matmul_drops_score", "acc[c] += s * v;", "acc[c] += v;"),
+    ("displacement_sign", "acc[d] += s * (yd - xd);", "acc[d] += s * (xd - yd);"),
+    ("self_pair_misplaced", "if (exclude_self && j == i) continue;", "if (exclude_self && j == i + 1) continue;"),
+    ("lse_drops_max", "out[r] = m + rlog(l);", "out[r] = rlog(l);"),
+    ("softmax_unnormalised", "R p = rexp(s[j] - m) / l;", "R p = rexp(s[j] - m);"),
+    ("tie_order_reversed", "return a.j < b.j;", "return a.j > b.j;"),
+    ("largest_ignored", "return largest ? (a.v > b.v) : (a.v < b.v);", "return (a.v < b.v);"),
+]
+
+
+def _build_one(tmpdir, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation %s does not match exactly once" % name
+    path = os.path.join(tmpdir, name + ".cpp")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = os.path.join(tmpdir, "lib" + name + ".so")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-fopenmp", "-fPIC", "-shared", path, "-o", so], check=True)
+    return name, so
+
+
+@pytest.fixture(scope="module")
+def mutant_libs(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("mutants"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        return dict(ex.map(lambda m: _build_one(d, *m), MUTANTS))
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, mutant_libs):
+    lib = oracle._open(mutant_libs[name])
+    prev = oracle._load()
+    oracle._lib = lib
+    caught = []
+    try:
+        for pin in ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(pin.__name__)
+    finally:
+        oracle._lib = prev
+    assert caught, "no pin catches the planted mistake %s" % name

@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the pairwise-score workloads.
+
+This module only draws random inputs and states each workload's parameters;
+it holds none of the score arithmetic, so both the GPU library's tests and
+the CPU oracle can take their inputs from it. Every draw uses a CPU
+``torch.Generator`` seeded per workload, draws in float64 in the order
+listed, then casts to the workload's dtype. ``scale`` arguments shrink a
+workload (same distributions) for parity tests the oracle finishes quickly.
+
+The pages print no dataset or benchmark for these tasks; the shapes follow
+the uses the torchpairwise guide "Using Torchpairwise in Models" names in its
+Task Map (attention, Nadaraya-Watson kernel product, InfoNCE log-sum-exp,
+k-NN retrieval) and its Stein Variational Gradient Descent section.
+
+Ops are listed in the neutral vocabulary of that guide's Score Expressions
+section: ("mul", c), ("add", c), ("add_rows", name), ("add_columns", name),
+("weight_rows", name), ("weight_columns", name), ("exp", None); a vector
+argument names an array of the workload's dict.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator("cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(g, *shape):
+    return torch.randn(*shape, generator=g, dtype=torch.float64)
+
+
+@dataclass
+class Case:
+    """One consumer call on a workload."""
+    name: str
+    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk
+    x: str                   # array used as X
+    y: str                   # array used as Y
+    metric: str
+    gamma: float = 1.0
+    ops: list = field(default_factory=list)
+    v: str | None = None     # array used as V (matmul / softmax_matmul)
+    exclude_self: bool = False
+    k: int = 0
+    largest: bool = False
+
+
+def rbf_small(n: int = 1024, m: int | None = None, d: int = 3, seed: int = 1001):
+    """Nadaraya-Watson kernel product plus distance consumers, float32.
+
+    X, Y ~ N(0,1) [n,3]; V = [randn(m,3), ones] so the last product column is
+    the row mass. Consumers: rbf (gamma 0.5) product, log-sum-exp of -D/2 and
+    top-8 smallest of D = sqeuclidean(X, Y).
+    """
+    m = n if m is None else m
+    g = _gen(seed)
+    X = _randn(g, n, d)
+    Y = _randn(g, m, d)
+    V0 = _randn(g, m, 3)
+    V = torch.cat([V0, torch.ones(m, 1, dtype=torch.float64)], 1)
+    arrays = {k: t.to(torch.float32).numpy() for k, t in dict(X=X, Y=Y, V=V).items()}
+    cases = [
+        Case("rbf_matmul", "matmul", "X", "Y", "rbf", gamma=0.5, v="V"),
+        Case("sqeuclid_lse", "logsumexp", "X", "Y", "sqeuclidean", ops=[("mul", -0.5)]),
+        Case("sqeuclid_topk", "topk", "X", "Y", "sqeuclidean", k=8),
+    ]
+    return arrays, cases
+
+
+def rbf_large(n: int = 65536, seed: int = 1011):
+    """The rbf kernel product of ``rbf_small`` at n = m = 65536 (float32)."""
+    arrays, cases = rbf_small(n=n, seed=seed)
+    return arrays, cases[:1]
+
+
+def attention(n: int = 16384, m: int | None = None, d: int = 64, c: int = 64, seed: int = 1002):
+    """Softmax attention, float32: Q, K, V ~ N(0,1); scores linear(Q,K)/8."""
+    m = n if m is None else m
+    g = _gen(seed)
+    Q = _randn(g, n, d)
+    K = _randn(g, m, d)
+    V = _randn(g, m, c)
+    arrays = {k: t.to(torch.float32).numpy() for k, t in dict(Q=Q, K=K, V=V).items()}
+    scale = 1.0 / math.sqrt(64.0)
+    cases = [Case("attention", "softmax_matmul", "Q", "K", "linear", ops=[("mul", scale)], v="V")]
+    return arrays, cases
+
+
+def infonce(n: int = 65536, d: int = 64, seed: int = 1003):
+    """InfoNCE row log-sum-exp excluding self, float32.
+
+    z = rows of randn normalised to unit length (in float64, then cast);
+    scores z.z^T / 0.07 plus a per-row bias b ~ N(0, variance 0.1).
+    """
+    g = _gen(seed)
+    r = _randn(g, n, d)
+    z = r / r.norm(dim=1, keepdim=True)
+    b = math.sqrt(0.1) * _randn(g, n)
+    arrays = {"z": z.to(torch.float32).numpy(), "b": b.to(torch.float32).numpy()}
+    cases = [Case("infonce", "logsumexp", "z", "z", "linear", ops=[("mul", 1.0 / 0.07), ("add_rows", "b")],
+                  exclude_self=True)]
+    return arrays, cases
+
+
+def knn(n_query: int = 65536, n_ref: int = 1 << 20, d: int = 32, centres: int = 256, seed: int = 1004):
+    """k-NN retrieval, float32: top-10 smallest sqeuclidean distances.
+
+    256 centres with coordinates N(0, 4) (sd 2), equal weights; references
+    and queries are a uniformly drawn centre plus N(0, I) noise.
+    """
+    g = _gen(seed)
+    cen = 2.0 * _randn(g, centres, d)
+    lr = torch.randint(centres, (n_ref,), generator=g)
+    R = cen[lr] + _randn(g, n_ref, d)
+    lq = torch.randint(centres, (n_query,), generator=g)
+    Q = cen[lq] + _randn(g, n_query, d)
+    arrays = {"Q": Q.to(torch.float32).numpy(), "R": R.to(torch.float32).numpy()}
+    cases = [Case("knn", "topk", "Q", "R", "sqeuclidean", k=10)]
+    return arrays, cases
+
+
+def svgd(n: int = 131072, d: int = 16, seed: int = 1005):
+    """SVGD direction, float64: x ~ N(0, I), score = -x (standard normal
+    target), rbf gamma = 1/16; one kernel product and one displacement."""
+    g = _gen(seed)
+    x = _randn(g, n, d)
+    arrays = {"x": x.numpy(), "score": (-x).numpy()}
+    gamma = 1.0 / 16.0
+    cases = [
+        Case("svgd_matmul", "matmul", "x", "x", "rbf", gamma=gamma, v="score"),
+        Case("svgd_displacement", "displacement", "x", "x", "rbf", gamma=gamma),
+    ]
+    return arrays, cases
+
+
+# name -> (generator, full-size kwargs, reduced kwargs for quick parity runs)
+WORKLOADS = {
+    "rbf_small": (rbf_small, {}, {"n": 300, "m": 333}),
+    "rbf_large": (rbf_large, {}, {"n": 2000}),
+    "attention": (attention, {}, {"n": 700, "m": 650}),
+    "infonce": (infonce, {}, {"n": 900}),
+    "knn": (knn, {}, {"n_query": 500, "n_ref": 4099}),
+    "svgd": (svgd, {}, {"n": 1100}),
+}
+
+
+def make(name: str, reduced: bool = False, **override):
+    fn, full, small = WORKLOADS[name]
+    kw = dict(small if reduced else full)
+    kw.update(override)
+    return fn(**kw)
+
+
+def sample_rows(n: int, stride: int = 61, edge: int = 256) -> np.ndarray:
+    """A row subset touching every tile position and both ragged ends:
+    rows i with i % stride == 0, plus the first and last `edge` rows."""
+    rows = set(range(0, n, stride)) | set(range(min(edge, n))) | set(range(max(0, n - edge), n))
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,243 @@
+"""Benchmark of the fused pairwise-score consumers on one MI355X.
+
+A step is one full pass of the hot path over one synthetic workload: the
+consumer call(s) of that workload (epilogue pre-pass, tile kernel, split
+merge), with inputs, outputs and workspace already resident in HBM.
+Default workload: softmax attention, Q, K, V [16384, 64] float32, scores
+Q.K^T / 8 (the attention row of the torchpairwise guide's Task Map).
+
+Prints ONE JSON line: pair evaluations per second (Gpairs/s), the roofline
+of the dominant kernel, the CPU oracle timed on a bounded row sample on the
+host cores, and the parity of the timed outputs on that sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+import workloads  # noqa: E402
+
+# Algorithmic flops per pair (FMA = 2; add, mul, max, compare = 1; exp = 1;
+# row norms precomputed; distances through |x|^2 + |y|^2 - 2 x.y).
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}
+
+
+def flops_per_pair(case, D, C):
+    body = 0
+    if case.metric == "linear":
+        body = 2 * D
+    else:
+        body = 2 * D + 2
+        if case.metric == "rbf":
+            body += 2  # scale and exp
+    body += sum(1 for _ in case.ops)
+    if case.consumer == "matmul":
+        return body + 2 * C
+    if case.consumer == "displacement":
+        return body + 2 * (D + 1)
+    if case.consumer == "logsumexp":
+        return body + 4
+    if case.consumer == "softmax_matmul":
+        return body + 4 + 2 * C
+    if case.consumer == "topk":
+        return body + 1
+    raise ValueError(case.consumer)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="attention", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lazy_score_matrix_amd as pw
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    arrays, cases = workloads.make(args.workload)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in arrays.items()}
+
+    calls = []  # (case, expr, run_fn, outputs)
+    pairs_per_step = 0
+    flops_per_step = 0.0
+    for c in cases:
+        X = t[c.x]
+        Y = X if c.y == c.x else t[c.y]
+        ops = [(n, t[a] if isinstance(a, str) else a) for n, a in c.ops]
+        e = pw.lazy(X, Y, c.metric, gamma=c.gamma, ops=ops)
+        N, D = X.shape
+        M = Y.shape[0]
+        C = t[c.v].shape[1] if c.v else 0
+        if c.consumer in ("matmul", "softmax_matmul"):
+            out = torch.empty(N, C, dtype=X.dtype, device=dev)
+            ws = e.workspace(c.consumer, C)
+            V = t[c.v]
+            fn = (lambda e=e, V=V, out=out, ws=ws, m=c.consumer: getattr(e, m)(V, out=out, workspace=ws))
+            outs = (out,)
+        elif c.consumer == "displacement":
+            out = torch.empty(N, D, dtype=X.dtype, device=dev)
+            ws = e.workspace("displacement")
+            fn = (lambda e=e, out=out, ws=ws: e.displacement(out=out, workspace=ws))
+            outs = (out,)
+        elif c.consumer == "logsumexp":
+            out = torch.empty(N, dtype=X.dtype, device=dev)
+            ws = e.workspace("logsumexp")
+            fn = (lambda e=e, out=out, ws=ws, x=c.exclude_self: e.logsumexp(x, out=out, workspace=ws))
+            outs = (out,)
+        else:
+            vals = torch.empty(N, c.k, dtype=X.dtype, device=dev)
+            idx = torch.empty(N, c.k, dtype=torch.int64, device=dev)
+            ws = e.workspace("topk", 0, c.k)
+            fn = (lambda e=e, vals=vals, idx=idx, ws=ws, k=c.k, lg=c.largest:
+                  e.topk(k, lg, values=vals, indices=idx, workspace=ws))
+            outs = (vals, idx)
+        calls.append((c, e, fn, outs, C))
+        pairs_per_step += N * M
+        flops_per_step += float(N) * M * flops_per_pair(c, D, C)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for _, _, fn, _, _ in calls:
+            fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        for _, _, fn, _, _ in calls:
+            fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    gpairs = pairs_per_step / (ms * 1e-3) / 1e9
+
+    dtype = "f32" if calls[0][1].dtype == torch.float32 else "f64"
+    c0, e0 = calls[0][0], calls[0][1]
+    achieved = flops_per_step / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    contraction = c0.metric != "rbf" or e0.D >= 16
+    roofline = {
+        "bound": "mfma" if contraction else "alu",
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "flops_per_pair": [flops_per_pair(c, e.D, C) for c, e, _, _, C in calls],
+        "timed": "HIP events around the timed steps on the launch stream; a step is all calls of the workload",
+    }
+
+    result = {
+        "metric": "pair evaluations/sec (Gpairs/s) per consumer + % of gfx950 FP32/FP64 peak",
+        "value": round(gpairs, 3),
+        "unit": "Gpairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "consumers": [c.consumer for c, *_ in calls],
+            "N": int(e0.N), "M": int(e0.M), "D": int(e0.D),
+            "C": [C for *_, C in calls],
+            "pairs_per_step": pairs_per_step,
+            "plan": [e.plan(c.consumer, C, c.k) for c, e, _, _, C in calls],
+        },
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu:
+        result.update(cpu_leg(calls, arrays, args.cpu_seconds))
+    print(json.dumps(result), flush=True)
+
+
+def cpu_leg(calls, arrays, seconds):
+    """Time the oracle on a bounded row sample on the host cores, and check
+    the timed GPU outputs against it on the same rows."""
+    import oracle
+    from parity import topk_report, value_report
+
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    total_pairs, total_s, rows_desc, parity = 0, 0.0, [], []
+    budget = seconds / len(calls)
+    for c, e, _, outs, C in calls:
+        ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+        oe = oracle.Expr(arrays[c.x], arrays[c.y], c.metric, gamma=c.gamma, ops=ops)
+        V = arrays[c.v] if c.v else None
+
+        def run(rows):
+            if c.consumer == "matmul":
+                return oracle.matmul(oe, V, rows)
+            if c.consumer == "softmax_matmul":
+                return oracle.softmax_matmul(oe, V, rows)
+            if c.consumer == "displacement":
+                return oracle.displacement(oe, rows)
+            if c.consumer == "logsumexp":
+                return oracle.logsumexp(oe, c.exclude_self, rows)
+            return oracle.topk(oe, c.k, c.largest, extra=16, rows=rows)
+
+        # Probe on a few rows, then size the sample to the time budget.
+        probe = np.arange(0, oe.N, max(1, oe.N // (4 * threads)))[: 4 * threads]
+        t0 = time.perf_counter()
+        run(probe)
+        tp = max(time.perf_counter() - t0, 1e-6)
+        n_rows = int(min(oe.N, max(len(probe), len(probe) * budget / tp)))
+        rows = np.unique(np.linspace(0, oe.N - 1, n_rows).astype(np.int64))
+        t0 = time.perf_counter()
+        res = run(rows)
+        dt = time.perf_counter() - t0
+        total_pairs += len(rows) * oe.M
+        total_s += dt
+        rows_desc.append("%s: %d of %d rows evenly spaced (incl. first and last), all %d columns"
+                         % (c.name, len(rows), oe.N, oe.M))
+        dtype = np.dtype(oe.np_dtype)
+        if c.consumer == "topk":
+            gv = outs[0].cpu().numpy()[rows]
+            gi = outs[1].cpu().numpy()[rows]
+            fails = topk_report(gv, gi, res[0], res[1], res[2], c.k, c.largest, dtype)
+            parity.append({"call": c.name, "rows": len(rows), "pass": not fails, "failing_rows": len(fails)})
+        else:
+            g = outs[0].cpu().numpy()[rows]
+            vmax = float(np.max(np.abs(V))) if V is not None else float(np.max(np.abs(oe.Y)) + np.max(np.abs(oe.X)))
+            ok, ratio, rel = value_report(g, res[0], res[1], dtype, n_terms=oe.M, vmax=vmax)
+            parity.append({"call": c.name, "rows": len(rows), "pass": bool(ok), "worst_err_over_tol": ratio,
+                           "max_plain_rel_err": rel})
+    return {
+        "cpu_baseline": {
+            "value": round(total_pairs / total_s / 1e9, 6),
+            "unit": "Gpairs/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": "; ".join(rows_desc),
+        },
+        "parity": parity,
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * pw.h -- C ABI of libpw, lazy pairwise scores reduced on the fly on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A pairwise score s_ij = f(x_i, y_j) is bound once (pw_bind) over row-major
+ * feature matrices X [N, D] and Y [M, D], then consumed by one of five fused
+ * row reductions over j. The [N, M] score matrix is never stored: every call
+ * evaluates its pairs tile by tile in bounded device memory, so memory scales
+ * with (N + M) * (D + C) plus a caller-provided workspace (torchpairwise
+ * guide "Using Torchpairwise in Models", opening section).
+ *
+ * Conventions shared by every function:
+ *  - Return value: PW_OK (0) or a negative pw_status. All validation runs on
+ *    the host before any device work; on an error nothing is launched and no
+ *    output is written.
+ *  - Device pointers (X, Y, op vectors, V, outputs, workspace) are memory of
+ *    the current HIP device (e.g. from PyTorch), owned by the caller. A
+ *    pw_expr only borrows them: keep them alive and unmodified until the
+ *    stream work of every consumer call that uses them has completed.
+ *  - Consumers are asynchronous: they enqueue kernels on `stream` (a
+ *    hipStream_t; NULL is the null stream) and return. They never allocate
+ *    device memory and never synchronise.
+ *  - Element type of every floating array is the bound dtype (float or
+ *    double); top-k indices are int64_t. Matrices are row-major with the
+ *    given leading dimension (elements between consecutive rows).
+ *  - A pw_expr is immutable after pw_bind; concurrent consumer calls on one
+ *    handle are safe if each gets its own workspace and outputs.
+ *  - Results agree with other evaluation orders within floating tolerance,
+ *    not bitwise (guide, "What to Check", Precision); for a fixed handle,
+ *    consumer and argument set, repeated calls are bitwise identical.
+ */
+#ifndef PW_H
+#define PW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pw_expr pw_expr; /* opaque host-side handle */
+
+typedef enum {
+  PW_OK = 0,
+  PW_ERR_INVALID = -1,     /* null pointer, bad enum, bad size or stride, k > M, ... */
+  PW_ERR_UNSUPPORTED = -2, /* valid request outside the fused range (D not in 1..64, k > 64, > PW_MAX_OPS ops) */
+  PW_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pw_workspace_size reports */
+  PW_ERR_HIP = -4          /* a HIP runtime error was reported while enqueueing */
+} pw_status;
+
+typedef enum { PW_F32 = 0, PW_F64 = 1 } pw_dtype;
+
+/* Built-in metrics (guide, Task Map; rbf form from the SVGD section):
+ *   PW_LINEAR       f = sum_d x_d y_d
+ *   PW_SQEUCLIDEAN  f = sum_d (x_d - y_d)^2      (squared, no root)
+ *   PW_RBF          f = exp(-gamma * sum_d (x_d - y_d)^2), gamma >= 0 */
+typedef enum { PW_LINEAR = 0, PW_SQEUCLIDEAN = 1, PW_RBF = 2 } pw_metric;
+
+/* Score arithmetic applied to f left to right, in the order given
+ * (guide, "Score Expressions": scalar arithmetic, add_rows, add_columns,
+ * weight_rows, weight_columns, exp):
+ *   PW_OP_MUL             s <- scalar * s    (division by t is MUL 1/t)
+ *   PW_OP_ADD             s <- s + scalar
+ *   PW_OP_ADD_ROWS        s <- s + vec[i]    vec: N elements
+ *   PW_OP_ADD_COLUMNS     s <- s + vec[j]    vec: M elements
+ *   PW_OP_WEIGHT_ROWS     s <- vec[i] * s    vec: N elements
+ *   PW_OP_WEIGHT_COLUMNS  s <- vec[j] * s    vec: M elements
+ *   PW_OP_EXP             s <- exp(s)
+ * `vec` is a contiguous device array of the bound dtype (NULL for MUL, ADD,
+ * EXP); `scalar` is rounded to the bound dtype once. */
+typedef enum {
+  PW_OP_MUL = 0,
+  PW_OP_ADD = 1,
+  PW_OP_ADD_ROWS = 2,
+  PW_OP_ADD_COLUMNS = 3,
+  PW_OP_WEIGHT_ROWS = 4,
+  PW_OP_WEIGHT_COLUMNS = 5,
+  PW_OP_EXP = 6
+} pw_op_kind;
+
+#define PW_MAX_OPS 8
+#define PW_MAX_D 64
+#define PW_MAX_K 64
+
+typedef struct {
+  int kind;          /* pw_op_kind */
+  double scalar;     /* MUL, ADD */
+  const void *vec;   /* ROWS / COLUMNS ops: device vector, borrowed */
+} pw_op;
+
+typedef enum {
+  PW_C_MATMUL = 0,
+  PW_C_DISPLACEMENT = 1,
+  PW_C_LOGSUMEXP = 2,
+  PW_C_SOFTMAX_MATMUL = 3,
+  PW_C_TOPK = 4
+} pw_consumer;
+
+/* Bind a lazy score (the `tp.lazy(X, Y, metric, gamma=...)` call of the
+ * guide's Task Map, followed by its score arithmetic). Host-only: validates
+ * and records pointers, shapes and the op chain; launches nothing and
+ * evaluates no pair.
+ *   out     receives a new handle (set to NULL on error)
+ *   dtype   pw_dtype of X, Y and every op vector
+ *   metric  pw_metric; gamma used by PW_RBF only (finite, >= 0)
+ *   X       [N, ldx] device matrix, rows are x_i;   N >= 0, ldx >= D
+ *   Y       [M, ldy] device matrix, rows are y_j;   M >= 0, ldy >= D
+ *           X and Y may be the same pointer (scores of a set with itself)
+ *   D       features, 1..PW_MAX_D (PW_ERR_UNSUPPORTED outside that range)
+ *   ops     n_ops entries (0..PW_MAX_OPS), copied; op vectors are borrowed
+ * X and Y must be aligned to their element size. */
+int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
+            const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops);
+
+/* Free a handle (host memory only). NULL is ignored. */
+void pw_release(pw_expr *e);
+
+/* Bytes of device workspace `consumer` needs on this handle: C value
+ * columns for PW_C_MATMUL / PW_C_SOFTMAX_MATMUL (ignored otherwise) and k
+ * for PW_C_TOPK (ignored otherwise). The size depends on N, M, D, C, k and
+ * the op chain, never on N*M (the guide's "tile workspace"); it may be 0. */
+int pw_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes);
+
+/* Kernel product (guide, Task Map, "Kernel attention, Nadaraya-Watson" row:
+ * `lazy @ V`; with V = [V, ones] the last column is the row mass):
+ *   out[i, c] = sum_j s_ij V[j, c]
+ *   V    [M, ldv] device matrix, 1 <= C, ldv >= C
+ *   out  [N, ldo] device matrix, ldo >= C.  M == 0 writes zeros. */
+int pw_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *ws,
+              size_t ws_bytes, void *stream);
+
+/* Displacement (guide, Stein Variational Gradient Descent section: the
+ * kernel's displacement, sum_j k_ij (x_j - x_i) for an rbf kernel of a set
+ * with itself; for any bound score and Y it is):
+ *   out[i, d] = sum_j s_ij (Y[j, d] - X[i, d])
+ *   out  [N, ldo] device matrix, ldo >= D.  M == 0 writes zeros. */
+int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t ws_bytes, void *stream);
+
+/* Row log-sum-exp (guide, Task Map, InfoNCE row:
+ * `logsumexp(-1, exclude_self=True)`):
+ *   out[i] = log sum_{j in J_i} exp(s_ij),  J_i = {0..M-1} minus {i} when
+ *   exclude_self (the pair j == i, by index, whatever its value).
+ *   out  [N] device vector. An empty J_i gives -inf. */
+int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Attention-style product (guide, opening example and Task Map, Attention
+ * row: `softmax_matmul(V)`, softmax over the last axis j):
+ *   out[i, c] = sum_j softmax_j(s_i.)[j] V[j, c]
+ *   V    [M, ldv] device matrix, 1 <= C, ldv >= C
+ *   out  [N, ldo] device matrix, ldo >= C.  M == 0 writes zeros. */
+int pw_softmax_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Row top-k (guide, Task Map, k-NN row `topk(k, largest=False)` with exact
+ * tie order, and Chamfer row: min/argmin are k = 1):
+ * the k pairs of each row that come first when ordered by s_ij ascending
+ * (descending if `largest`), equal values by ascending j; written in that
+ * order.
+ *   k        0..min(M, PW_MAX_K); k > M is PW_ERR_INVALID, k > PW_MAX_K is
+ *            PW_ERR_UNSUPPORTED; k == 0 is a no-op
+ *   values   [N, k] device matrix (contiguous) of the bound dtype
+ *   indices  [N, k] device matrix (contiguous) of int64_t column indices j
+ * NaN scores are unsupported. */
+int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices, void *ws, size_t ws_bytes,
+            void *stream);
+
+/* Describe the launch plan `consumer` would use (kernel family, tile sizes,
+ * column splits) into buf as a NUL-terminated string. For logs and tuning. */
+int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf, size_t len);
+
+/* Static text for a pw_status code. */
+const char *pw_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PW_H */

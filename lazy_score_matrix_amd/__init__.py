@@ -1,0 +1,257 @@
+"""Lazy pairwise scores reduced on the fly on an AMD Instinct MI355X.
+
+Thin Python binding over the C ABI of ``libpw.so`` (include/pw.h): argument
+marshalling only. Tensors are PyTorch device tensors; every step of the
+computation runs in the library's HIP kernels on the current torch stream.
+There is no CPU fallback: if the library is missing, every call raises.
+
+    import lazy_score_matrix_amd as pw
+    e = pw.lazy(Q, K, "linear", ops=[("mul", Q.shape[-1] ** -0.5)])
+    out = e.softmax_matmul(V)                       # [N, C]
+
+Op names follow the guide's "Score Expressions" section: ("mul", c),
+("add", c), ("add_rows", a), ("add_columns", b), ("weight_rows", w),
+("weight_columns", u), ("exp", None).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpw.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "pw.h")
+
+PW_OK, PW_ERR_INVALID, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP = 0, -1, -2, -3, -4
+DTYPES = {torch.float32: 0, torch.float64: 1}
+METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2}
+OPS = {"mul": 0, "add": 1, "add_rows": 2, "add_columns": 3, "weight_rows": 4, "weight_columns": 5, "exp": 6}
+CONSUMERS = {"matmul": 0, "displacement": 1, "logsumexp": 2, "softmax_matmul": 3, "topk": 4}
+MAX_OPS, MAX_D, MAX_K = 8, 64, 64
+
+
+class PwError(RuntimeError):
+    """A libpw status other than PW_OK (HIP runtime or workspace errors)."""
+
+
+class _Op(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("scalar", ctypes.c_double), ("vec", ctypes.c_void_p)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Open libpw.so and declare its signatures. Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path == LIB_PATH:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "libpw.so is not built (%s); run `python -m lazy_score_matrix_amd.build` first" % path)
+        lib = ctypes.CDLL(path)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        c_int = ctypes.c_int
+        lib.pw_bind.argtypes = [ctypes.POINTER(vp), c_int, c_int, ctypes.c_double, vp, i64, i64, vp, i64, i64, i64,
+                                ctypes.POINTER(_Op), c_int]
+        lib.pw_release.argtypes = [vp]
+        lib.pw_release.restype = None
+        lib.pw_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
+        lib.pw_matmul.argtypes = [vp, vp, i64, i64, vp, i64, vp, sz, vp]
+        lib.pw_softmax_matmul.argtypes = [vp, vp, i64, i64, vp, i64, vp, sz, vp]
+        lib.pw_displacement.argtypes = [vp, vp, i64, vp, sz, vp]
+        lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
+        lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
+        lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
+        lib.pw_error_string.argtypes = [c_int]
+        lib.pw_error_string.restype = ctypes.c_char_p
+        if path == LIB_PATH:
+            _lib = lib
+        return lib
+
+
+def header_functions(header: str = HEADER):
+    """Names of the functions include/pw.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char \*)\s*(pw_\w+)\s*\(", text, flags=re.M)))
+
+
+def check(rc: int, what: str = "") -> None:
+    if rc == PW_OK:
+        return
+    msg = "%s: %s (%d)" % (what, load_library().pw_error_string(rc).decode(), rc)
+    if rc == PW_ERR_INVALID:
+        raise ValueError(msg)
+    if rc == PW_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise PwError(msg)
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows(t, name):
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.numel() == 0 or t.shape[0] == 1:
+        return max(t.shape[1], 1)
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError("%s must have unit column stride" % name)
+    return t.stride(0)
+
+
+class LazyScores:
+    """A bound lazy score matrix S[i, j] = ops(f(x_i, y_j)) (never stored)."""
+
+    def __init__(self, X: torch.Tensor, Y: torch.Tensor, metric: str = "linear", gamma: float = 1.0, ops=()):
+        lib = load_library()
+        if X.dtype not in DTYPES or Y.dtype != X.dtype:
+            raise TypeError("X and Y must both be float32 or both float64")
+        if not X.is_cuda or Y.device != X.device:
+            raise ValueError("X and Y must be on the same GPU")
+        if metric not in METRICS:
+            raise ValueError("unknown metric %r" % metric)
+        self.X, self.Y, self.metric, self.gamma = X, Y, metric, float(gamma)
+        self.N, self.D = X.shape
+        self.M = Y.shape[0]
+        self.dtype, self.device = X.dtype, X.device
+        if Y.shape[1] != self.D:
+            raise ValueError("X and Y feature dims differ")
+        ldx, ldy = _rows(X, "X"), _rows(Y, "Y")
+        self._keep = []
+        ops = list(ops)
+        arr = (_Op * max(len(ops), 1))()
+        for t, (name, arg) in enumerate(ops):
+            if name not in OPS:
+                raise ValueError("unknown op %r" % name)
+            arr[t].kind = OPS[name]
+            if name in ("mul", "add"):
+                arr[t].scalar = float(arg)
+            elif name != "exp":
+                v = arg
+                n = self.N if name.endswith("_rows") else self.M
+                if (not torch.is_tensor(v) or v.dtype != self.dtype or v.device != self.device
+                        or v.numel() != n or not v.is_contiguous()):
+                    raise ValueError("%s needs a contiguous %s vector of %d elements on %s"
+                                     % (name, self.dtype, n, self.device))
+                self._keep.append(v)
+                arr[t].vec = v.data_ptr()
+        self.ops = ops
+        h = ctypes.c_void_p()
+        check(lib.pw_bind(ctypes.byref(h), DTYPES[X.dtype], METRICS[metric], self.gamma, X.data_ptr(), self.N, ldx,
+                          Y.data_ptr(), self.M, ldy, self.D, arr, len(ops)), "pw_bind")
+        self._h = h
+        self._lib = lib
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pw_release(h)
+            self._h = None
+
+    # -- workspace -----------------------------------------------------
+    def workspace_size(self, consumer: str, C: int = 0, k: int = 0) -> int:
+        n = ctypes.c_size_t()
+        check(self._lib.pw_workspace_size(self._h, CONSUMERS[consumer], int(C), int(k), ctypes.byref(n)),
+              "pw_workspace_size")
+        return n.value
+
+    def workspace(self, consumer: str, C: int = 0, k: int = 0) -> torch.Tensor:
+        return torch.empty(max(self.workspace_size(consumer, C, k), 1), dtype=torch.uint8, device=self.device)
+
+    def plan(self, consumer: str, C: int = 0, k: int = 0) -> str:
+        buf = ctypes.create_string_buffer(512)
+        check(self._lib.pw_plan_describe(self._h, CONSUMERS[consumer], int(C), int(k), buf, 512), "pw_plan_describe")
+        return buf.value.decode()
+
+    def _ws(self, ws, consumer, C=0, k=0):
+        if ws is None:
+            ws = self.workspace(consumer, C, k)
+        return ws, ws.numel() * ws.element_size()
+
+    def _value(self, V, what):
+        if V.dtype != self.dtype or V.device != self.device or V.shape[0] != self.M:
+            raise ValueError("V must be [M, C] %s on %s" % (self.dtype, self.device))
+        return _rows(V, "V")
+
+    # -- consumers ------------------------------------------------------
+    def matmul(self, V: torch.Tensor, out=None, workspace=None) -> torch.Tensor:
+        """out[i, c] = sum_j S[i, j] V[j, c]."""
+        ldv = self._value(V, "matmul")
+        C = V.shape[1]
+        out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
+        ws, nb = self._ws(workspace, "matmul", C)
+        check(self._lib.pw_matmul(self._h, V.data_ptr(), C, ldv, out.data_ptr(), _rows(out, "out"), ws.data_ptr(),
+                                  nb, _stream(self.device)), "pw_matmul")
+        return out
+
+    __matmul__ = matmul
+
+    def softmax_matmul(self, V: torch.Tensor, out=None, workspace=None) -> torch.Tensor:
+        """out[i, c] = sum_j softmax_j(S[i, :])[j] V[j, c]."""
+        ldv = self._value(V, "softmax_matmul")
+        C = V.shape[1]
+        out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
+        ws, nb = self._ws(workspace, "softmax_matmul", C)
+        check(self._lib.pw_softmax_matmul(self._h, V.data_ptr(), C, ldv, out.data_ptr(), _rows(out, "out"),
+                                          ws.data_ptr(), nb, _stream(self.device)), "pw_softmax_matmul")
+        return out
+
+    def displacement(self, out=None, workspace=None) -> torch.Tensor:
+        """out[i, d] = sum_j S[i, j] (Y[j, d] - X[i, d])."""
+        out = torch.empty(self.N, self.D, dtype=self.dtype, device=self.device) if out is None else out
+        ws, nb = self._ws(workspace, "displacement")
+        check(self._lib.pw_displacement(self._h, out.data_ptr(), _rows(out, "out"), ws.data_ptr(), nb,
+                                        _stream(self.device)), "pw_displacement")
+        return out
+
+    def logsumexp(self, exclude_self: bool = False, out=None, workspace=None) -> torch.Tensor:
+        """out[i] = log sum_j exp(S[i, j]), optionally without j == i."""
+        out = torch.empty(self.N, dtype=self.dtype, device=self.device) if out is None else out
+        ws, nb = self._ws(workspace, "logsumexp")
+        check(self._lib.pw_logsumexp(self._h, int(bool(exclude_self)), out.data_ptr(), ws.data_ptr(), nb,
+                                     _stream(self.device)), "pw_logsumexp")
+        return out
+
+    def topk(self, k: int, largest: bool = False, values=None, indices=None, workspace=None):
+        """The k first pairs of each row by (value, index): values and int64 indices [N, k]."""
+        values = torch.empty(self.N, k, dtype=self.dtype, device=self.device) if values is None else values
+        indices = torch.empty(self.N, k, dtype=torch.int64, device=self.device) if indices is None else indices
+        ws, nb = self._ws(workspace, "topk", 0, k)
+        check(self._lib.pw_topk(self._h, int(k), int(bool(largest)), values.data_ptr(), indices.data_ptr(),
+                                ws.data_ptr(), nb, _stream(self.device)), "pw_topk")
+        return values, indices
+
+    def min(self):
+        """Row minimum and its (lowest) index: top-k with k = 1."""
+        v, i = self.topk(1)
+        return v[:, 0], i[:, 0]
+
+    def argmin(self):
+        return self.min()[1]
+
+
+def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()) -> LazyScores:
+    """Bind S[i, j] = ops(metric(X[i], Y[j])); Y defaults to X."""
+    return LazyScores(X, X if Y is None else Y, metric, gamma, ops)
+
+
+def svgd_direction(x: torch.Tensor, score: torch.Tensor, gamma: float, workspace=None) -> torch.Tensor:
+    """(K @ score - 2 gamma K.displacement()) / n for K = rbf(x, x): one
+    kernel product and one displacement, combined on the device."""
+    K = lazy(x, x, "rbf", gamma=gamma)
+    drive = K.matmul(score)
+    rep = K.displacement()
+    return (drive - 2.0 * gamma * rep) / x.shape[-2]

@@ -1,0 +1,196 @@
+// Auxiliary kernels of libpw: the epilogue-vector pre-pass, row norms,
+// output fills for empty reductions, and the merge of column-split partials.
+#include "device_common.h"
+
+namespace pw {
+
+// ---------------------------------------------------------------------------
+// Epilogue vectors: every program of the batch evaluated per element in
+// double, rounded once to the dtype.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void vec_prog_kernel(const VecProgBatch b) {
+  const int pi = blockIdx.y;
+  if (pi >= b.n_progs) return;
+  const VecProg &p = b.p[pi];
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.len) return;
+  double v = 0.0;
+  for (int k = 0; k < p.n; ++k) {
+    const VecInstr &in = p.ins[k];
+    switch (in.op) {
+      case VO_SET: v = in.c; break;
+      case VO_MULC: v *= in.c; break;
+      case VO_ADDC: v += in.c; break;
+      case VO_MULV: v *= (double)ldg<T>(in.v, e); break;
+      case VO_ADDV: v += (double)ldg<T>(in.v, e); break;
+    }
+  }
+  static_cast<T *>(p.out)[e] = (T)v;
+}
+
+hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s) {
+  int64_t len = 0;
+  for (int i = 0; i < b.n_progs; ++i) len = b.p[i].len > len ? b.p[i].len : len;
+  if (len == 0 || b.n_progs == 0) return hipSuccess;
+  dim3 grid((unsigned)((len + 255) / 256), (unsigned)b.n_progs), block(256);
+  if (dtype == 0) hipLaunchKernelGGL(vec_prog_kernel<float>, grid, block, 0, s, b);
+  else hipLaunchKernelGGL(vec_prog_kernel<double>, grid, block, 0, s, b);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fill a [rows, cols] block (leading dimension ld) with one value.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void fill_kernel(T *out, int64_t rows, int64_t cols, int64_t ld, T v) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * cols) return;
+  out[(t / cols) * ld + t % cols] = v;
+}
+
+hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == 0) hipLaunchKernelGGL(fill_kernel<float>, grid, block, 0, s, (float *)out, rows, cols, ld, (float)value);
+  else hipLaunchKernelGGL(fill_kernel<double>, grid, block, 0, s, (double *)out, rows, cols, ld, value);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row norms |x_i|^2 for the kernels that evaluate distances through the
+// expansion |x|^2 + |y|^2 - 2 x.y.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void row_norms_kernel(const T *X, int64_t n, int64_t ld, int D, T *out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  T s = 0;
+  for (int d = 0; d < D; ++d) {
+    T v = X[i * ld + d];
+    s = fma(v, v, s);
+  }
+  out[i] = s;
+}
+
+hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == 0) hipLaunchKernelGGL(row_norms_kernel<float>, grid, block, 0, s, (const float *)X, n, ld, D, (float *)out);
+  else hipLaunchKernelGGL(row_norms_kernel<double>, grid, block, 0, s, (const double *)X, n, ld, D, (double *)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Merge of n_split column-split partials, always in split order 0..S-1 so
+// results are deterministic for a fixed plan.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void merge_sum_kernel(const TileArgs a, int W) {
+  // matmul (W = C) and displacement (W = D): plain sums of the partials.
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.N * W) return;
+  const int64_t i = t / W;
+  const int c = (int)(t % W);
+  const T *part = static_cast<const T *>(a.partial);
+  T s = 0;
+  for (int sp = 0; sp < a.n_split; ++sp) s += part[((int64_t)sp * a.N + i) * W + c];
+  static_cast<T *>(a.out)[i * a.ldo + c] = s;
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void merge_lse_kernel(const TileArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.N) return;
+  const T *part = static_cast<const T *>(a.partial);
+  T m = neg_inf<T>();
+  for (int sp = 0; sp < a.n_split; ++sp) m = max(m, part[((int64_t)sp * a.N + i) * 2]);
+  T l = 0;
+  if (m != neg_inf<T>()) {
+    for (int sp = 0; sp < a.n_split; ++sp) {
+      const T *q = part + ((int64_t)sp * a.N + i) * 2;
+      if (q[1] > (T)0) l += q[1] * dexp(q[0] - m);
+    }
+  }
+  static_cast<T *>(a.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void merge_softmax_kernel(const TileArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.N * a.C) return;
+  const int64_t i = t / a.C;
+  const int c = (int)(t % a.C);
+  const int64_t W = a.C + 2;
+  const T *part = static_cast<const T *>(a.partial);
+  T m = neg_inf<T>();
+  for (int sp = 0; sp < a.n_split; ++sp) m = max(m, part[((int64_t)sp * a.N + i) * W]);
+  T l = 0, acc = 0;
+  if (m != neg_inf<T>()) {
+    for (int sp = 0; sp < a.n_split; ++sp) {
+      const T *q = part + ((int64_t)sp * a.N + i) * W;
+      if (q[1] > (T)0) {
+        const T f = dexp(q[0] - m);
+        l += q[1] * f;
+        acc += q[2 + c] * f;
+      }
+    }
+  }
+  static_cast<T *>(a.out)[i * a.ldo + c] = (l > (T)0) ? acc / l : (T)0;
+}
+
+template <class T, int KL>
+__global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.N) return;
+  Key<T> list[KL];
+#pragma unroll
+  for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const int64_t base = ((int64_t)sp * a.N + i) * a.k;
+    for (int p = 0; p < a.k; ++p) key_insert<T, KL>(list, Key<T>::load(a.partial, base + p));
+  }
+  T *v = static_cast<T *>(a.out) + i * a.k;
+  int64_t *ix = a.idx + i * a.k;
+#pragma unroll
+  for (int p = 0; p < KL; ++p)
+    if (p < a.k) {
+      v[p] = list[p].value(a.largest);
+      ix[p] = (int64_t)list[p].index();
+    }
+}
+
+template <class T>
+static hipError_t merge_t(int consumer, const TileArgs &a, hipStream_t s) {
+  dim3 block(256);
+  auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
+  if (a.N == 0) return hipSuccess;
+  switch (consumer) {
+    case C_MATMUL:
+      hipLaunchKernelGGL(merge_sum_kernel<T>, blocks(a.N * a.C), block, 0, s, a, a.C);
+      break;
+    case C_DISPLACEMENT:
+      hipLaunchKernelGGL(merge_sum_kernel<T>, blocks(a.N * a.D), block, 0, s, a, a.D);
+      break;
+    case C_LOGSUMEXP:
+      hipLaunchKernelGGL(merge_lse_kernel<T>, blocks(a.N), block, 0, s, a);
+      break;
+    case C_SOFTMAX:
+      hipLaunchKernelGGL(merge_softmax_kernel<T>, blocks(a.N * a.C), block, 0, s, a);
+      break;
+    case C_TOPK:
+      if (a.k <= 16) hipLaunchKernelGGL((merge_topk_kernel<T, 16>), blocks(a.N), block, 0, s, a);
+      else hipLaunchKernelGGL((merge_topk_kernel<T, 64>), blocks(a.N), block, 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int dtype, int consumer, const TileArgs &a, hipStream_t s) {
+  return dtype == 0 ? merge_t<float>(consumer, a, s) : merge_t<double>(consumer, a, s);
+}
+
+}  // namespace pw

@@ -1,0 +1,166 @@
+// Device helpers shared by the tile engines: exponentials, the score
+// epilogue, and order-preserving top-k keys.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pw_internal.h"
+
+namespace pw {
+
+constexpr float kLog2e_f = 1.4426950408889634f;
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr float kLn2_f = 0.69314718055994531f;
+constexpr double kLn2 = 0.69314718055994530942;
+
+// exp in the working precision. float: the hardware base-2 exponential
+// (v_exp_f32) of x*log2(e). double: the device library's exp.
+__device__ __forceinline__ float dexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e_f); }
+__device__ __forceinline__ double dexp(double x) { return exp(x); }
+__device__ __forceinline__ float dlog(float x) { return __builtin_amdgcn_logf(x) * kLn2_f; }
+__device__ __forceinline__ double dlog(double x) { return log(x); }
+
+template <class T>
+__device__ __forceinline__ T neg_inf() { return -__builtin_huge_valf(); }
+template <>
+__device__ __forceinline__ double neg_inf<double>() { return -__builtin_huge_val(); }
+
+template <class T>
+__device__ __forceinline__ T ldg(const void *p, int64_t i) { return static_cast<const T *>(p)[i]; }
+
+// Per-row part of the epilogue, loaded once per row.
+template <class T>
+struct RowEpi {
+  T r[kMaxStages];
+  T p[kMaxStages];
+};
+
+template <class T>
+__device__ __forceinline__ void load_row_epi(const Epi &e, int64_t i, bool valid, RowEpi<T> &re) {
+#pragma unroll
+  for (int s = 0; s < kMaxStages; ++s) {
+    T r = (T)1, p = (T)0;
+    if (s < e.n_stages && e.st[s].kind == ST_AFFINE) {
+      if (e.st[s].row_vec) {
+        if (valid) {
+          r = ldg<T>(e.st[s].r_vec, i);
+          p = ldg<T>(e.st[s].p_vec, i);
+        }
+      } else {
+        r = (T)e.st[s].r_scalar;
+        p = (T)e.st[s].p_scalar;
+      }
+    }
+    re.r[s] = r;
+    re.p[s] = p;
+  }
+}
+
+// Apply the stages to score s of column slot jj; colq/colo hold the staged
+// column vectors as [stage][tile width].
+template <class T, int BN>
+__device__ __forceinline__ T apply_epi(const Epi &e, const RowEpi<T> &re, T s, const T (*colq)[BN],
+                                       const T (*colo)[BN], int jj) {
+#pragma unroll
+  for (int st = 0; st < kMaxStages; ++st) {
+    if (st < e.n_stages) {
+      if (e.st[st].kind == ST_EXP) {
+        s = dexp(s);
+      } else if (e.st[st].col_vec) {
+        s = fma(s, re.r[st] * colq[st][jj], re.p[st] + colo[st][jj]);
+      } else {
+        s = fma(s, re.r[st], re.p[st]);
+      }
+    }
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k keys: total order (value, index), smaller first. For `largest` the
+// value is negated so the same "smaller first" order applies; -0 and +0 are
+// the same value. NaN is not supported.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_ord(float v) {
+  uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_ord(uint32_t o) {
+  uint32_t b = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(b);
+}
+__device__ __forceinline__ uint64_t f64_ord(double v) {
+  uint64_t b = (uint64_t)__double_as_longlong(v == 0.0 ? 0.0 : v);
+  return (b & 0x8000000000000000ull) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double f64_from_ord(uint64_t o) {
+  uint64_t b = (o & 0x8000000000000000ull) ? (o & 0x7fffffffffffffffull) : ~o;
+  return __longlong_as_double((long long)b);
+}
+
+template <class T>
+struct Key;
+
+template <>
+struct Key<float> {
+  uint64_t k;
+  __device__ __forceinline__ static Key make(float v, uint32_t j, int largest) {
+    return Key{((uint64_t)f32_ord(largest ? -v : v) << 32) | j};
+  }
+  __device__ __forceinline__ static Key sentinel() { return Key{~0ull}; }
+  __device__ __forceinline__ bool operator<(const Key &o) const { return k < o.k; }
+  __device__ __forceinline__ float value(int largest) const {
+    float v = f32_from_ord((uint32_t)(k >> 32));
+    return largest ? -v : v;
+  }
+  __device__ __forceinline__ uint32_t index() const { return (uint32_t)k; }
+  __device__ __forceinline__ void store(void *base, int64_t e) const { static_cast<uint64_t *>(base)[e] = k; }
+  __device__ __forceinline__ static Key load(const void *base, int64_t e) {
+    return Key{static_cast<const uint64_t *>(base)[e]};
+  }
+};
+
+template <>
+struct Key<double> {
+  uint64_t v;
+  uint32_t j;
+  __device__ __forceinline__ static Key make(double x, uint32_t j, int largest) {
+    return Key{f64_ord(largest ? -x : x), j};
+  }
+  __device__ __forceinline__ static Key sentinel() { return Key{~0ull, ~0u}; }
+  __device__ __forceinline__ bool operator<(const Key &o) const {
+    return v < o.v || (v == o.v && j < o.j);
+  }
+  __device__ __forceinline__ double value(int largest) const {
+    double x = f64_from_ord(v);
+    return largest ? -x : x;
+  }
+  __device__ __forceinline__ uint32_t index() const { return j; }
+  __device__ __forceinline__ void store(void *base, int64_t e) const {
+    uint64_t *b = static_cast<uint64_t *>(base);
+    b[2 * e] = v;
+    b[2 * e + 1] = j;
+  }
+  __device__ __forceinline__ static Key load(const void *base, int64_t e) {
+    const uint64_t *b = static_cast<const uint64_t *>(base);
+    return Key{b[2 * e], (uint32_t)b[2 * e + 1]};
+  }
+};
+
+// Insert `c` into the ascending list l[0..L); the largest key falls off.
+template <class T, int L>
+__device__ __forceinline__ void key_insert(Key<T> (&l)[L], Key<T> c) {
+  if (c < l[L - 1]) {
+#pragma unroll
+    for (int p = 0; p < L; ++p) {
+      bool lt = c < l[p];
+      Key<T> lo = lt ? c : l[p];
+      Key<T> hi = lt ? l[p] : c;
+      l[p] = lo;
+      c = hi;
+    }
+  }
+}
+
+}  // namespace pw

@@ -1,0 +1,537 @@
+// libpw C ABI: validation, op-chain compilation, launch planning, workspace
+// layout and dispatch. Declarations and semantics: include/pw.h.
+#include "../../include/pw.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pw_internal.h"
+
+using namespace pw;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Op-chain compilation into canonical stages (see pw_internal.h).
+// ---------------------------------------------------------------------------
+struct Prog {
+  std::vector<VecInstr> ins;
+  bool vec = false;   // depends on a vector
+  double cval = 0.0;  // value when !vec
+  void set(double c) {
+    ins.assign(1, VecInstr{VO_SET, c, nullptr});
+    vec = false;
+    cval = c;
+  }
+  void mulc(double c) {
+    ins.push_back(VecInstr{VO_MULC, c, nullptr});
+    if (!vec) cval *= c;
+  }
+  void addc(double c) {
+    ins.push_back(VecInstr{VO_ADDC, c, nullptr});
+    if (!vec) cval += c;
+  }
+  void mulv(const void *v) {
+    ins.push_back(VecInstr{VO_MULV, 0.0, v});
+    vec = true;
+  }
+  void addv(const void *v) {
+    ins.push_back(VecInstr{VO_ADDV, 0.0, v});
+    vec = true;
+  }
+  bool is_const(double c) const { return !vec && cval == c; }
+};
+
+struct HostStage {
+  int kind = ST_AFFINE;
+  bool row_vec = false, col_vec = false;
+  double r_scalar = 1.0, p_scalar = 0.0;
+  Prog r, p, q, o;
+};
+
+struct StageBuilder {
+  std::vector<HostStage> out;
+  Prog ar, br, ac, bc;
+  StageBuilder() { start(); }
+  void start() {
+    ar.set(1.0);
+    br.set(0.0);
+    ac.set(1.0);
+    bc.set(0.0);
+  }
+  void close() {
+    const bool row_vec = ar.vec || br.vec, col_vec = ac.vec || bc.vec;
+    if (!row_vec && !col_vec && ar.cval == 1.0 && br.cval == 0.0) {
+      start();
+      return;  // identity
+    }
+    HostStage s;
+    s.kind = ST_AFFINE;
+    s.row_vec = row_vec;
+    s.col_vec = col_vec;
+    s.r_scalar = ar.cval;
+    s.p_scalar = br.cval;
+    s.r = ar;
+    s.p = br;
+    s.q = ac;
+    s.o = bc;
+    out.push_back(s);
+    start();
+  }
+  void op(const pw_op &o) {
+    switch (o.kind) {
+      case PW_OP_EXP: {
+        close();
+        HostStage s;
+        s.kind = ST_EXP;
+        out.push_back(s);
+        break;
+      }
+      case PW_OP_MUL:
+        ar.mulc(o.scalar);
+        br.mulc(o.scalar);
+        bc.mulc(o.scalar);
+        break;
+      case PW_OP_ADD: br.addc(o.scalar); break;
+      case PW_OP_ADD_ROWS: br.addv(o.vec); break;
+      case PW_OP_ADD_COLUMNS: bc.addv(o.vec); break;
+      case PW_OP_WEIGHT_ROWS:
+        if (bc.vec) close();  // w_i * o_j is not separable: new stage
+        ar.mulv(o.vec);
+        br.mulv(o.vec);
+        break;
+      case PW_OP_WEIGHT_COLUMNS:
+        if (br.vec) close();  // u_j * p_i is not separable: new stage
+        if (!br.is_const(0.0)) {  // a scalar offset moves to the column side
+          bc.addc(br.cval);
+          br.set(0.0);
+        }
+        ac.mulv(o.vec);
+        bc.mulv(o.vec);
+        break;
+    }
+  }
+};
+
+}  // namespace
+
+struct pw_expr {
+  int dtype, metric;
+  double gamma;
+  const void *X;
+  int64_t N, ldx;
+  const void *Y;
+  int64_t M, ldy;
+  int64_t D;
+  std::vector<pw_op> ops;
+  std::vector<HostStage> stages;
+};
+
+namespace {
+
+constexpr int kTargetCUs = 256;            // MI355X compute units
+constexpr int64_t kTargetWGs = 4 * kTargetCUs;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t esize(int dtype) { return dtype == PW_F32 ? 4 : 8; }
+
+struct Plan {
+  int family = 0;  // 0: generic VALU engine
+  ValuConfig vcfg{4, 0};
+  int bm = kValuBM, bn = kValuBN;
+  int n_rb = 0, n_split = 1;
+  int64_t split_cols = 0;
+  int chunk = 0;  // value columns per launch (matmul, softmax)
+  size_t off_epi = 0, off_part = 0, part_bytes = 0, total = 0;
+  std::vector<size_t> stage_off;  // per stage: offset of its vectors
+};
+
+int valu_dtile(int64_t D) { return D <= 4 ? 4 : (D <= 16 ? 16 : 64); }
+int valu_vtile(int64_t C) { return C <= 4 ? 4 : (C <= 16 ? 16 : 64); }
+
+Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
+  Plan p;
+  const size_t es = esize(e.dtype);
+  // Epilogue vectors.
+  size_t off = 0;
+  for (const HostStage &s : e.stages) {
+    p.stage_off.push_back(off);
+    if (s.kind == ST_AFFINE) {
+      if (s.row_vec) off += align_up(2 * (size_t)e.N * es);
+      if (s.col_vec) off += align_up(2 * (size_t)e.M * es);
+    }
+  }
+  p.off_epi = 0;
+  p.off_part = off;
+  // Tile grid.
+  p.vcfg.dtile = valu_dtile(e.D);
+  if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {
+    p.vcfg.vtile = valu_vtile(C);
+    p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
+  } else if (consumer == PW_C_TOPK) {
+    p.vcfg.vtile = k <= 16 ? 16 : 64;
+  } else {
+    p.vcfg.vtile = 0;
+  }
+  p.n_rb = (int)((e.N + p.bm - 1) / p.bm);
+  const int64_t tiles = std::max<int64_t>(1, (e.M + p.bn - 1) / p.bn);
+  int64_t want = std::max<int64_t>(1, (kTargetWGs + p.n_rb - 1) / std::max(p.n_rb, 1));
+  want = std::min(want, tiles);
+  const int64_t tiles_per_split = (tiles + want - 1) / want;
+  p.split_cols = tiles_per_split * p.bn;
+  p.n_split = (int)std::max<int64_t>(1, (e.M + p.split_cols - 1) / p.split_cols);
+  // Partials.
+  if (p.n_split > 1) {
+    size_t per_row = 0;
+    switch (consumer) {
+      case PW_C_MATMUL: per_row = (size_t)p.chunk * es; break;
+      case PW_C_DISPLACEMENT: per_row = (size_t)e.D * es; break;
+      case PW_C_LOGSUMEXP: per_row = 2 * es; break;
+      case PW_C_SOFTMAX_MATMUL: per_row = (size_t)(p.chunk + 2) * es; break;
+      case PW_C_TOPK: per_row = (size_t)k * (e.dtype == PW_F32 ? 8 : 16); break;
+    }
+    p.part_bytes = align_up((size_t)p.n_split * (size_t)e.N * per_row);
+  }
+  p.total = p.off_part + p.part_bytes;
+  if (p.total) p.total += kAlign;  // room to align the caller's pointer
+  return p;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_expr(const pw_expr *e) { return e ? PW_OK : PW_ERR_INVALID; }
+
+// Validate a consumer call's common arguments and its workspace.
+int check_ws(const Plan &p, void *ws, size_t ws_bytes, char **base) {
+  *base = nullptr;
+  if (p.total == 0) return PW_OK;
+  if (!ws || ws_bytes < p.total) return PW_ERR_WORKSPACE;
+  uintptr_t b = ((uintptr_t)ws + kAlign - 1) / kAlign * kAlign;
+  *base = reinterpret_cast<char *>(b);
+  return PW_OK;
+}
+
+int hip_status(hipError_t err) { return err == hipSuccess ? PW_OK : PW_ERR_HIP; }
+
+// Fill the device epilogue and launch the vector programs into the workspace.
+int prepare_epilogue(const pw_expr &e, const Plan &p, char *base, Epi *epi, hipStream_t s) {
+  std::memset(epi, 0, sizeof(*epi));
+  epi->n_stages = (int)e.stages.size();
+  VecProgBatch batch;
+  std::memset(&batch, 0, sizeof(batch));
+  const size_t es = esize(e.dtype);
+  auto add_prog = [&](const Prog &pr, void *out, int64_t len) -> int {
+    if (len == 0) return PW_OK;
+    if (pr.ins.size() > (size_t)kMaxVecInstr) return PW_ERR_UNSUPPORTED;
+    VecProg &vp = batch.p[batch.n_progs++];
+    vp.n = (int)pr.ins.size();
+    vp.len = len;
+    vp.out = out;
+    for (size_t t = 0; t < pr.ins.size(); ++t) vp.ins[t] = pr.ins[t];
+    if (batch.n_progs == kProgsPerLaunch) {
+      int rc = hip_status(launch_vec_progs(e.dtype, batch, s));
+      std::memset(&batch, 0, sizeof(batch));
+      return rc;
+    }
+    return PW_OK;
+  };
+  for (size_t si = 0; si < e.stages.size(); ++si) {
+    const HostStage &hs = e.stages[si];
+    Stage &d = epi->st[si];
+    d.kind = hs.kind;
+    d.row_vec = hs.row_vec;
+    d.col_vec = hs.col_vec;
+    d.r_scalar = hs.r_scalar;
+    d.p_scalar = hs.p_scalar;
+    if (hs.kind != ST_AFFINE) continue;
+    char *ptr = base + p.off_epi + p.stage_off[si];
+    int rc = PW_OK;
+    if (hs.row_vec) {
+      d.r_vec = ptr;
+      d.p_vec = ptr + (size_t)e.N * es;
+      rc = add_prog(hs.r, ptr, e.N);
+      if (rc == PW_OK) rc = add_prog(hs.p, ptr + (size_t)e.N * es, e.N);
+      ptr += align_up(2 * (size_t)e.N * es);
+    }
+    if (rc == PW_OK && hs.col_vec) {
+      epi->any_col = 1;
+      d.q_vec = ptr;
+      d.o_vec = ptr + (size_t)e.M * es;
+      rc = add_prog(hs.q, ptr, e.M);
+      if (rc == PW_OK) rc = add_prog(hs.o, ptr + (size_t)e.M * es, e.M);
+    }
+    if (rc != PW_OK) return rc;
+  }
+  if (batch.n_progs) return hip_status(launch_vec_progs(e.dtype, batch, s));
+  return PW_OK;
+}
+
+TileArgs base_args(const pw_expr &e, const Plan &p, char *base) {
+  TileArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = e.X;
+  a.ldx = e.ldx;
+  a.Y = e.Y;
+  a.ldy = e.ldy;
+  a.N = e.N;
+  a.M = e.M;
+  a.D = (int)e.D;
+  a.gamma = e.metric == PW_RBF ? e.gamma : 0.0;
+  a.n_rb = p.n_rb;
+  a.n_split = p.n_split;
+  a.split_cols = p.split_cols;
+  a.partial = p.n_split > 1 ? base + p.off_part : nullptr;
+  return a;
+}
+
+hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const TileArgs &a, hipStream_t s) {
+  if (e.dtype == PW_F32) {
+    switch (e.metric) {
+      case PW_LINEAR: return valu_launch_metric<float, M_LINEAR>(consumer, p.vcfg, a, s);
+      case PW_SQEUCLIDEAN: return valu_launch_metric<float, M_SQEUCLIDEAN>(consumer, p.vcfg, a, s);
+      default: return valu_launch_metric<float, M_RBF>(consumer, p.vcfg, a, s);
+    }
+  }
+  switch (e.metric) {
+    case PW_LINEAR: return valu_launch_metric<double, M_LINEAR>(consumer, p.vcfg, a, s);
+    case PW_SQEUCLIDEAN: return valu_launch_metric<double, M_SQEUCLIDEAN>(consumer, p.vcfg, a, s);
+    default: return valu_launch_metric<double, M_RBF>(consumer, p.vcfg, a, s);
+  }
+}
+
+// One tile launch plus, when the columns are split, the merge.
+int run_tiles(const pw_expr &e, int consumer, const Plan &p, TileArgs &a, hipStream_t s) {
+  int rc = hip_status(launch_tile(e, consumer, p, a, s));
+  if (rc == PW_OK && p.n_split > 1) rc = hip_status(launch_merge(e.dtype, consumer, a, s));
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pw_error_string(int code) {
+  switch (code) {
+    case PW_OK: return "ok";
+    case PW_ERR_INVALID: return "invalid argument";
+    case PW_ERR_UNSUPPORTED: return "unsupported: outside the fused range";
+    case PW_ERR_WORKSPACE: return "workspace missing or too small";
+    case PW_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
+            const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops) {
+  if (!out) return PW_ERR_INVALID;
+  *out = nullptr;
+  if (dtype != PW_F32 && dtype != PW_F64) return PW_ERR_INVALID;
+  if (metric < PW_LINEAR || metric > PW_RBF) return PW_ERR_INVALID;
+  if (metric == PW_RBF && !(std::isfinite(gamma) && gamma >= 0.0)) return PW_ERR_INVALID;
+  if (N < 0 || M < 0 || n_ops < 0) return PW_ERR_INVALID;
+  if (D < 1 || D > PW_MAX_D) return PW_ERR_UNSUPPORTED;
+  if (N > INT32_MAX || M > INT32_MAX) return PW_ERR_UNSUPPORTED;
+  if (ldx < D || ldy < D) return PW_ERR_INVALID;
+  const size_t es = esize(dtype);
+  if ((N > 0 && !X) || (M > 0 && !Y)) return PW_ERR_INVALID;
+  if (!aligned(X, es) || !aligned(Y, es)) return PW_ERR_INVALID;
+  if (n_ops > PW_MAX_OPS) return PW_ERR_UNSUPPORTED;
+  if (n_ops > 0 && !ops) return PW_ERR_INVALID;
+  for (int t = 0; t < n_ops; ++t) {
+    const pw_op &o = ops[t];
+    switch (o.kind) {
+      case PW_OP_MUL:
+      case PW_OP_ADD:
+        if (!std::isfinite(o.scalar)) return PW_ERR_INVALID;
+        break;
+      case PW_OP_ADD_ROWS:
+      case PW_OP_WEIGHT_ROWS:
+        if ((N > 0 && !o.vec) || !aligned(o.vec, es)) return PW_ERR_INVALID;
+        break;
+      case PW_OP_ADD_COLUMNS:
+      case PW_OP_WEIGHT_COLUMNS:
+        if ((M > 0 && !o.vec) || !aligned(o.vec, es)) return PW_ERR_INVALID;
+        break;
+      case PW_OP_EXP: break;
+      default: return PW_ERR_INVALID;
+    }
+  }
+  pw_expr *e = new (std::nothrow) pw_expr();
+  if (!e) return PW_ERR_INVALID;
+  e->dtype = dtype;
+  e->metric = metric;
+  e->gamma = gamma;
+  e->X = X;
+  e->N = N;
+  e->ldx = ldx;
+  e->Y = Y;
+  e->M = M;
+  e->ldy = ldy;
+  e->D = D;
+  e->ops.assign(ops, ops + n_ops);
+  StageBuilder b;
+  for (const pw_op &o : e->ops) b.op(o);
+  b.close();
+  e->stages = b.out;
+  if (e->stages.size() > (size_t)kMaxStages) {
+    delete e;
+    return PW_ERR_UNSUPPORTED;
+  }
+  *out = e;
+  return PW_OK;
+}
+
+void pw_release(pw_expr *e) { delete e; }
+
+static int check_consumer_args(const pw_expr *e, int consumer, int64_t C, int k) {
+  if (!e) return PW_ERR_INVALID;
+  switch (consumer) {
+    case PW_C_MATMUL:
+    case PW_C_SOFTMAX_MATMUL:
+      if (C < 1) return PW_ERR_INVALID;
+      return PW_OK;
+    case PW_C_DISPLACEMENT:
+    case PW_C_LOGSUMEXP:
+      return PW_OK;
+    case PW_C_TOPK:
+      if (k < 0 || k > e->M) return PW_ERR_INVALID;
+      if (k > PW_MAX_K) return PW_ERR_UNSUPPORTED;
+      return PW_OK;
+  }
+  return PW_ERR_INVALID;
+}
+
+int pw_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes) {
+  if (!bytes) return PW_ERR_INVALID;
+  *bytes = 0;
+  int rc = check_consumer_args(e, consumer, C, k);
+  if (rc != PW_OK) return rc;
+  if (e->N == 0 || e->M == 0 || (consumer == PW_C_TOPK && k == 0)) return PW_OK;
+  *bytes = make_plan(*e, consumer, C, k).total;
+  return PW_OK;
+}
+
+int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf, size_t len) {
+  if (!buf || len == 0) return PW_ERR_INVALID;
+  int rc = check_consumer_args(e, consumer, C, k);
+  if (rc != PW_OK) return rc;
+  Plan p = make_plan(*e, consumer, C, k);
+  std::snprintf(buf, len,
+                "family=valu dtile=%d vtile=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
+                "workspace=%zu",
+                p.vcfg.dtile, p.vcfg.vtile, p.bm, p.bn, p.n_rb, p.n_split, (long long)p.split_cols,
+                (int)e->stages.size(), p.total);
+  return PW_OK;
+}
+
+// Shared body of the value-matrix consumers (matmul, softmax).
+static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t C, int64_t ldv, void *out,
+                          int64_t ldo, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_consumer_args(e, consumer, C, 0);
+  if (rc != PW_OK) return rc;
+  const size_t es = esize(e->dtype);
+  if (ldv < C || ldo < C) return PW_ERR_INVALID;
+  if ((e->M > 0 && !V) || (e->N > 0 && !out)) return PW_ERR_INVALID;
+  if (!aligned(V, es) || !aligned(out, es)) return PW_ERR_INVALID;
+  if (e->N == 0) return PW_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->N, C, ldo, 0.0, s));
+  Plan p = make_plan(*e, consumer, C, 0);
+  char *base;
+  rc = check_ws(p, ws, ws_bytes, &base);
+  if (rc != PW_OK) return rc;
+  TileArgs a = base_args(*e, p, base);
+  rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc != PW_OK) return rc;
+  a.ldv = ldv;
+  a.ldo = ldo;
+  const int cons = consumer == PW_C_MATMUL ? C_MATMUL : C_SOFTMAX;
+  for (int64_t c0 = 0; c0 < C && rc == PW_OK; c0 += p.chunk) {
+    a.C = (int)std::min<int64_t>(p.chunk, C - c0);
+    a.V = static_cast<const char *>(V) + c0 * es;
+    a.out = static_cast<char *>(out) + c0 * es;
+    rc = run_tiles(*e, cons, p, a, s);
+  }
+  return rc;
+}
+
+int pw_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *ws,
+              size_t ws_bytes, void *stream) {
+  return value_consumer(e, PW_C_MATMUL, V, C, ldv, out, ldo, ws, ws_bytes, stream);
+}
+
+int pw_softmax_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *ws,
+                      size_t ws_bytes, void *stream) {
+  return value_consumer(e, PW_C_SOFTMAX_MATMUL, V, C, ldv, out, ldo, ws, ws_bytes, stream);
+}
+
+int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_consumer_args(e, PW_C_DISPLACEMENT, 0, 0);
+  if (rc != PW_OK) return rc;
+  if (ldo < e->D || (e->N > 0 && !out) || !aligned(out, esize(e->dtype))) return PW_ERR_INVALID;
+  if (e->N == 0) return PW_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->N, e->D, ldo, 0.0, s));
+  Plan p = make_plan(*e, PW_C_DISPLACEMENT, 0, 0);
+  char *base;
+  rc = check_ws(p, ws, ws_bytes, &base);
+  if (rc != PW_OK) return rc;
+  TileArgs a = base_args(*e, p, base);
+  rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc != PW_OK) return rc;
+  a.out = out;
+  a.ldo = ldo;
+  return run_tiles(*e, C_DISPLACEMENT, p, a, s);
+}
+
+int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_consumer_args(e, PW_C_LOGSUMEXP, 0, 0);
+  if (rc != PW_OK) return rc;
+  if (exclude_self != 0 && exclude_self != 1) return PW_ERR_INVALID;
+  if ((e->N > 0 && !out) || !aligned(out, esize(e->dtype))) return PW_ERR_INVALID;
+  if (e->N == 0) return PW_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->N, 1, 1, -HUGE_VAL, s));
+  Plan p = make_plan(*e, PW_C_LOGSUMEXP, 0, 0);
+  char *base;
+  rc = check_ws(p, ws, ws_bytes, &base);
+  if (rc != PW_OK) return rc;
+  TileArgs a = base_args(*e, p, base);
+  rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc != PW_OK) return rc;
+  a.out = out;
+  a.exclude_self = exclude_self;
+  return run_tiles(*e, C_LOGSUMEXP, p, a, s);
+}
+
+int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices, void *ws, size_t ws_bytes,
+            void *stream) {
+  int rc = check_consumer_args(e, PW_C_TOPK, 0, k);
+  if (rc != PW_OK) return rc;
+  if (largest != 0 && largest != 1) return PW_ERR_INVALID;
+  if (e->N == 0 || k == 0) return PW_OK;
+  if (!values || !indices || !aligned(values, esize(e->dtype)) || !aligned(indices, 8)) return PW_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  Plan p = make_plan(*e, PW_C_TOPK, 0, k);
+  char *base;
+  rc = check_ws(p, ws, ws_bytes, &base);
+  if (rc != PW_OK) return rc;
+  TileArgs a = base_args(*e, p, base);
+  rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc != PW_OK) return rc;
+  a.out = values;
+  a.idx = indices;
+  a.k = k;
+  a.largest = largest;
+  return run_tiles(*e, C_TOPK, p, a, s);
+}
+
+}  // extern "C"

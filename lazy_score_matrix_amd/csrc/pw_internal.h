@@ -1,0 +1,131 @@
+// Internal structures shared by the libpw host code and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pw {
+
+// ---------------------------------------------------------------------------
+// Canonical score epilogue.
+//
+// The score arithmetic of the guide's "Score Expressions" section (scalar
+// multiply/add, add_rows, add_columns, weight_rows, weight_columns, exp) is
+// compiled at bind time into at most kMaxStages stages, applied in order:
+//   affine:  s <- s * (r_i * q_j) + (p_i + o_j)
+//   exp:     s <- exp(s)
+// Consecutive ops fold into one affine stage while the result stays of this
+// separable form; an op that would break it (a column weight after a row
+// offset, a row weight after a column offset) starts a new stage. r_i, p_i
+// are uniform scalars or per-row vectors, q_j, o_j per-column vectors; the
+// vectors are evaluated once per consumer call into the workspace by a
+// pre-pass (vector programs below), in double, then rounded to the dtype.
+// ---------------------------------------------------------------------------
+constexpr int kMaxStages = 8;
+enum StageKind : int { ST_AFFINE = 0, ST_EXP = 1 };
+
+struct Stage {
+  int kind;         // StageKind
+  int row_vec;      // r_i, p_i read from r_vec / p_vec (else r_scalar / p_scalar)
+  int col_vec;      // q_j, o_j read from q_vec / o_vec (else 1 and 0)
+  double r_scalar;
+  double p_scalar;
+  const void *r_vec, *p_vec;  // N elements of the dtype, in the workspace
+  const void *q_vec, *o_vec;  // M elements of the dtype, in the workspace
+};
+
+struct Epi {
+  int n_stages;
+  int any_col;  // some stage has column vectors
+  Stage st[kMaxStages];
+};
+
+// Vector program: out[e] = evaluation of `ins` at element e, in double.
+enum VecOp : int { VO_SET = 0, VO_MULC = 1, VO_ADDC = 2, VO_MULV = 3, VO_ADDV = 4 };
+constexpr int kMaxVecInstr = 12;
+struct VecInstr {
+  int op;
+  double c;
+  const void *v;  // dtype vector for VO_MULV / VO_ADDV
+};
+struct VecProg {
+  int n;
+  int64_t len;
+  void *out;  // dtype vector of `len` elements
+  VecInstr ins[kMaxVecInstr];
+};
+constexpr int kProgsPerLaunch = 6;
+struct VecProgBatch {
+  int n_progs;
+  VecProg p[kProgsPerLaunch];
+};
+
+enum Consumer : int { C_MATMUL = 0, C_DISPLACEMENT = 1, C_LOGSUMEXP = 2, C_SOFTMAX = 3, C_TOPK = 4 };
+enum Metric : int { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2 };
+
+// ---------------------------------------------------------------------------
+// Arguments of one tile-engine launch.
+//
+// The grid covers (row block) x (column split). Each workgroup reduces its
+// rows over one contiguous column range; with n_split > 1 it writes a
+// partial (per-row sums, (max, sum[, acc]) pairs or sorted top-k keys) to
+// the workspace and a merge kernel combines the splits in a fixed order.
+// ---------------------------------------------------------------------------
+struct TileArgs {
+  const void *X;
+  int64_t ldx;
+  const void *Y;
+  int64_t ldy;
+  int64_t N, M;
+  int D;
+  double gamma;
+  const void *V;  // value matrix (matmul / softmax), already offset to the column chunk
+  int64_t ldv;
+  int C;          // value columns in this launch
+  void *out;      // final output (n_split == 1), already offset to the column chunk
+  int64_t ldo;
+  int64_t *idx;   // top-k indices
+  int k;
+  int largest;
+  int exclude_self;
+  int n_rb;              // row blocks
+  int n_split;           // column splits
+  int64_t split_cols;    // columns per split (multiple of the tile width)
+  void *partial;         // workspace partials when n_split > 1
+  const void *nx;        // row norms (kernels using the norm expansion)
+  const void *ny;        // column norms
+  Epi epi;
+};
+
+// Top-k partial key layouts in the workspace.
+//   float:  one uint64 per entry: orderable(value) << 32 | j
+//   double: two uint64 per entry: orderable(value), j
+template <class T>
+struct TopkKeyBytes;
+template <>
+struct TopkKeyBytes<float> { static constexpr int value = 8; };
+template <>
+struct TopkKeyBytes<double> { static constexpr int value = 16; };
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files). All return hipError_t of the launch.
+// ---------------------------------------------------------------------------
+// Generic VALU tile engine: any D <= 64, any metric, consumer and op chain.
+//   dtile: feature tile 4 / 16 / 64 (D zero-padded up to it)
+//   vtile: value tile 4 / 16 / 64 (matmul, softmax), top-k list 16 / 64, else 0
+struct ValuConfig {
+  int dtile;
+  int vtile;
+};
+template <class T, int METRIC>
+hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s);
+constexpr int kValuBM = 256;  // rows per workgroup (one per thread)
+constexpr int kValuBN = 64;   // columns per staged tile
+
+// Auxiliary kernels.
+hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s);
+hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);
+hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s);
+hipError_t launch_merge(int dtype, int consumer, const TileArgs &a, hipStream_t s);
+
+}  // namespace pw

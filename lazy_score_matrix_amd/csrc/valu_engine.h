@@ -1,0 +1,267 @@
+// Generic VALU tile engine.
+//
+// One thread owns one row x_i (kept in registers) and streams the columns of
+// its workgroup's column range through LDS tiles of kValuBN rows of Y (and V
+// and the staged column epilogue vectors). Every lane of a wave reads the
+// same LDS address for a column, so the reads are broadcasts. Each score is
+// evaluated in direct form (the sum of squared differences for the distance
+// metrics), run through the epilogue, and folded into the row's reduction:
+//   matmul        acc[c] += s * V[j, c]
+//   displacement  acc[d] += s * y_jd, mass += s; out = acc - x * mass
+//   logsumexp     online (max m, sum l) per group of 8 columns
+//   softmax@V     online (m, l, acc[c]) per group of 8 columns
+//   top-k         sorted register list of (value, index) keys
+// This engine covers every D in 1..64, every op chain and both dtypes; the
+// planner prefers it for small D and small value widths, where there is no
+// real contraction to hand to the matrix cores.
+#pragma once
+
+#include "device_common.h"
+
+namespace pw {
+
+template <int METRIC, class T, int DT>
+__device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gamma) {
+  if constexpr (METRIC == M_LINEAR) {
+    T s0 = 0, s1 = 0;
+#pragma unroll
+    for (int d = 0; d < DT; d += 2) {
+      s0 = fma(x[d], y[d], s0);
+      if (d + 1 < DT) s1 = fma(x[d + 1], y[d + 1], s1);
+    }
+    return s0 + s1;
+  } else {
+    T s0 = 0, s1 = 0;
+#pragma unroll
+    for (int d = 0; d < DT; d += 2) {
+      T t0 = x[d] - y[d];
+      s0 = fma(t0, t0, s0);
+      if (d + 1 < DT) {
+        T t1 = x[d + 1] - y[d + 1];
+        s1 = fma(t1, t1, s1);
+      }
+    }
+    T d2 = s0 + s1;
+    if constexpr (METRIC == M_RBF) return dexp(neg_gamma * d2);
+    return d2;
+  }
+}
+
+template <class T, int METRIC, int CONS, int DT, int VT>
+__global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
+  constexpr int BM = kValuBM, BN = kValuBN;
+  constexpr bool HAS_V = (CONS == C_MATMUL || CONS == C_SOFTMAX);
+  constexpr int VW = HAS_V ? VT : 1;
+  constexpr int ACCN = HAS_V ? VT : (CONS == C_DISPLACEMENT ? DT : 1);
+  constexpr int KL = (CONS == C_TOPK) ? VT : 1;
+  constexpr int G = 8;  // columns per online-softmax group
+
+  __shared__ T sY[BN][DT];
+  __shared__ T sV[BN][VW];
+  __shared__ T sQ[kMaxStages][BN];
+  __shared__ T sO[kMaxStages][BN];
+
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x % a.n_rb;
+  const int sp = blockIdx.x / a.n_rb;
+  const int64_t i = (int64_t)rb * BM + tid;
+  const bool rv = i < a.N;
+  const int64_t jb = (int64_t)sp * a.split_cols;
+  const int64_t je = min(a.M, jb + a.split_cols);
+
+  T x[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) x[d] = (rv && d < a.D) ? ldg<T>(a.X, i * a.ldx + d) : (T)0;
+  RowEpi<T> re;
+  load_row_epi<T>(a.epi, i, rv, re);
+  const T neg_gamma = (T)(-a.gamma);
+
+  T acc[ACCN];
+#pragma unroll
+  for (int c = 0; c < ACCN; ++c) acc[c] = 0;
+  T mass = 0;
+  T m = neg_inf<T>(), l = 0;
+  Key<T> list[KL];
+#pragma unroll
+  for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
+
+  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+    const int nb = (int)min((int64_t)BN, je - j0);
+    __syncthreads();
+    for (int e = tid; e < BN * DT; e += BM) {
+      int jj = e / DT, d = e % DT;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<T>(a.Y, (j0 + jj) * a.ldy + d) : (T)0;
+    }
+    if constexpr (HAS_V) {
+      for (int e = tid; e < BN * VW; e += BM) {
+        int jj = e / VW, c = e % VW;
+        sV[jj][c] = (jj < nb && c < a.C) ? ldg<T>(a.V, (j0 + jj) * a.ldv + c) : (T)0;
+      }
+    }
+    if (a.epi.any_col) {
+      for (int e = tid; e < kMaxStages * BN; e += BM) {
+        int st = e / BN, jj = e % BN;
+        if (st < a.epi.n_stages && a.epi.st[st].col_vec) {
+          bool ok = jj < nb;
+          sQ[st][jj] = ok ? ldg<T>(a.epi.st[st].q_vec, j0 + jj) : (T)1;
+          sO[st][jj] = ok ? ldg<T>(a.epi.st[st].o_vec, j0 + jj) : (T)0;
+        }
+      }
+    }
+    __syncthreads();
+    if (!rv) continue;
+
+    if constexpr (CONS == C_LOGSUMEXP || CONS == C_SOFTMAX) {
+      for (int g = 0; g < nb; g += G) {
+        T sv[G];
+        T gm = neg_inf<T>();
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          const int jj = g + u;
+          T s = neg_inf<T>();
+          if (jj < nb) {
+            s = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
+            s = apply_epi<T, BN>(a.epi, re, s, sQ, sO, jj);
+            if (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) s = neg_inf<T>();
+          }
+          sv[u] = s;
+          gm = max(gm, s);
+        }
+        if (gm > m) {
+          const T alpha = dexp(m - gm);
+          l *= alpha;
+          if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+            for (int c = 0; c < ACCN; ++c) acc[c] *= alpha;
+          }
+          m = gm;
+        }
+        if (m != neg_inf<T>()) {
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            const T p = dexp(sv[u] - m);
+            l += p;
+            if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+              for (int c = 0; c < ACCN; ++c) acc[c] = fma(p, sV[g + u][c], acc[c]);
+            }
+          }
+        }
+      }
+    } else {
+      for (int jj = 0; jj < nb; ++jj) {
+        T s = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
+        s = apply_epi<T, BN>(a.epi, re, s, sQ, sO, jj);
+        if constexpr (CONS == C_MATMUL) {
+#pragma unroll
+          for (int c = 0; c < ACCN; ++c) acc[c] = fma(s, sV[jj][c], acc[c]);
+        } else if constexpr (CONS == C_DISPLACEMENT) {
+#pragma unroll
+          for (int d = 0; d < ACCN; ++d) acc[d] = fma(s, sY[jj][d], acc[d]);
+          mass += s;
+        } else if constexpr (CONS == C_TOPK) {
+          key_insert<T, KL>(list, Key<T>::make(s, (uint32_t)(j0 + jj), a.largest));
+        }
+      }
+    }
+  }
+  if (!rv) return;
+
+  const bool fin = a.n_split == 1;
+  const int64_t prow = (int64_t)sp * a.N + i;  // partial row
+  if constexpr (CONS == C_MATMUL) {
+    T *o = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.C;
+#pragma unroll
+    for (int c = 0; c < ACCN; ++c)
+      if (c < a.C) o[c] = acc[c];
+  } else if constexpr (CONS == C_DISPLACEMENT) {
+    T *o = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.D;
+#pragma unroll
+    for (int d = 0; d < ACCN; ++d)
+      if (d < a.D) o[d] = acc[d] - x[d] * mass;
+  } else if constexpr (CONS == C_LOGSUMEXP) {
+    if (fin) {
+      static_cast<T *>(a.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
+    } else {
+      T *o = static_cast<T *>(a.partial) + prow * 2;
+      o[0] = m;
+      o[1] = l;
+    }
+  } else if constexpr (CONS == C_SOFTMAX) {
+    if (fin) {
+      T *o = static_cast<T *>(a.out) + i * a.ldo;
+      const T inv = (l > (T)0) ? (T)1 / l : (T)0;
+#pragma unroll
+      for (int c = 0; c < ACCN; ++c)
+        if (c < a.C) o[c] = acc[c] * inv;
+    } else {
+      T *o = static_cast<T *>(a.partial) + prow * (a.C + 2);
+      o[0] = m;
+      o[1] = l;
+#pragma unroll
+      for (int c = 0; c < ACCN; ++c)
+        if (c < a.C) o[2 + c] = acc[c];
+    }
+  } else if constexpr (CONS == C_TOPK) {
+    if (fin) {
+      T *v = static_cast<T *>(a.out) + i * a.k;
+      int64_t *ix = a.idx + i * a.k;
+#pragma unroll
+      for (int p = 0; p < KL; ++p)
+        if (p < a.k) {
+          v[p] = list[p].value(a.largest);
+          ix[p] = (int64_t)list[p].index();
+        }
+    } else {
+#pragma unroll
+      for (int p = 0; p < KL; ++p)
+        if (p < a.k) list[p].store(a.partial, prow * a.k + p);
+    }
+  }
+}
+
+template <class T, int METRIC, int CONS, int DT, int VT>
+hipError_t launch_valu_kernel(const TileArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
+  hipLaunchKernelGGL((valu_tile<T, METRIC, CONS, DT, VT>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, int METRIC, int CONS, int DT>
+hipError_t valu_by_vt(int vt, const TileArgs &a, hipStream_t s) {
+  if constexpr (CONS == C_MATMUL || CONS == C_SOFTMAX) {
+    if (vt == 4) return launch_valu_kernel<T, METRIC, CONS, DT, 4>(a, s);
+    if (vt == 16) return launch_valu_kernel<T, METRIC, CONS, DT, 16>(a, s);
+    if (vt == 64) return launch_valu_kernel<T, METRIC, CONS, DT, 64>(a, s);
+  } else if constexpr (CONS == C_TOPK) {
+    if (vt == 16) return launch_valu_kernel<T, METRIC, CONS, DT, 16>(a, s);
+    if (vt == 64) return launch_valu_kernel<T, METRIC, CONS, DT, 64>(a, s);
+  } else {
+    return launch_valu_kernel<T, METRIC, CONS, DT, 1>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T, int METRIC, int DT>
+hipError_t valu_by_consumer(int consumer, int vt, const TileArgs &a, hipStream_t s) {
+  switch (consumer) {
+    case C_MATMUL: return valu_by_vt<T, METRIC, C_MATMUL, DT>(vt, a, s);
+    case C_DISPLACEMENT: return valu_by_vt<T, METRIC, C_DISPLACEMENT, DT>(vt, a, s);
+    case C_LOGSUMEXP: return valu_by_vt<T, METRIC, C_LOGSUMEXP, DT>(vt, a, s);
+    case C_SOFTMAX: return valu_by_vt<T, METRIC, C_SOFTMAX, DT>(vt, a, s);
+    case C_TOPK: return valu_by_vt<T, METRIC, C_TOPK, DT>(vt, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T, int METRIC>
+hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s) {
+  switch (cfg.dtile) {
+    case 4: return valu_by_consumer<T, METRIC, 4>(consumer, cfg.vtile, a, s);
+    case 16: return valu_by_consumer<T, METRIC, 16>(consumer, cfg.vtile, a, s);
+    case 64: return valu_by_consumer<T, METRIC, 64>(consumer, cfg.vtile, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pw

@@ -1,0 +1,180 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and validates arguments on the host before any device work.
+
+No call here reaches a HIP launch: pointers are fake (never dereferenced by
+host validation), and each call fails validation, or has N == 0 / k == 0,
+before the library would enqueue anything.
+"""
+import ctypes
+
+import pytest
+
+import lazy_score_matrix_amd as pw
+
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pw.load_library()
+
+
+def test_exports_every_header_function(lib):
+    names = pw.header_functions()
+    assert {"pw_bind", "pw_release", "pw_workspace_size", "pw_matmul", "pw_displacement", "pw_logsumexp",
+            "pw_softmax_matmul", "pw_topk", "pw_error_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def bind(lib, dtype=0, metric=0, gamma=1.0, X=FAKE, N=10, ldx=None, Y=FAKE, M=12, ldy=None, D=4, ops=()):
+    h = ctypes.c_void_p()
+    arr = (pw._Op * max(len(ops), 1))()
+    for t, (kind, scalar, vec) in enumerate(ops):
+        arr[t].kind, arr[t].scalar, arr[t].vec = kind, scalar, vec
+    rc = lib.pw_bind(ctypes.byref(h), dtype, metric, gamma, X, N, D if ldx is None else ldx, Y, M,
+                     D if ldy is None else ldy, D, arr, len(ops))
+    return rc, h
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.pw_error_string(code)
+    assert lib.pw_error_string(0) == b"ok"
+
+
+def test_bind_validation(lib):
+    ok, h = bind(lib)
+    assert ok == pw.PW_OK and h.value
+    lib.pw_release(h)
+    lib.pw_release(None)
+    cases = [
+        (dict(dtype=2), pw.PW_ERR_INVALID),
+        (dict(metric=3), pw.PW_ERR_INVALID),
+        (dict(metric=2, gamma=-1.0), pw.PW_ERR_INVALID),
+        (dict(metric=2, gamma=float("nan")), pw.PW_ERR_INVALID),
+        (dict(metric=2, gamma=float("inf")), pw.PW_ERR_INVALID),
+        (dict(D=0), pw.PW_ERR_UNSUPPORTED),
+        (dict(D=65), pw.PW_ERR_UNSUPPORTED),
+        (dict(N=-1), pw.PW_ERR_INVALID),
+        (dict(ldx=3), pw.PW_ERR_INVALID),
+        (dict(ldy=2), pw.PW_ERR_INVALID),
+        (dict(X=0), pw.PW_ERR_INVALID),
+        (dict(Y=0), pw.PW_ERR_INVALID),
+        (dict(X=FAKE + 2), pw.PW_ERR_INVALID),                       # misaligned
+        (dict(N=2 ** 31), pw.PW_ERR_UNSUPPORTED),
+        (dict(ops=[(0, float("nan"), None)]), pw.PW_ERR_INVALID),
+        (dict(ops=[(2, 0.0, None)]), pw.PW_ERR_INVALID),             # add_rows without vector
+        (dict(ops=[(5, 0.0, None)]), pw.PW_ERR_INVALID),             # weight_columns without vector
+        (dict(ops=[(9, 0.0, None)]), pw.PW_ERR_INVALID),             # bad kind
+        (dict(ops=[(0, 2.0, None)] * 9), pw.PW_ERR_UNSUPPORTED),     # > PW_MAX_OPS
+    ]
+    for kw, want in cases:
+        rc, h = bind(lib, **kw)
+        assert rc == want, (kw, rc)
+        assert not h.value
+    # Boundary values accepted: D = 1 and 64, gamma = 0, X aliasing Y, empty sets.
+    for kw in (dict(D=1), dict(D=64), dict(metric=2, gamma=0.0), dict(N=0, X=0), dict(M=0, Y=0),
+               dict(ops=[(0, 0.5, None), (2, 0, FAKE), (3, 0, FAKE), (6, 0, None), (4, 0, FAKE), (5, 0, FAKE)])):
+        rc, h = bind(lib, **kw)
+        assert rc == pw.PW_OK, kw
+        lib.pw_release(h)
+
+
+def ws_size(lib, h, consumer, C=0, k=0):
+    n = ctypes.c_size_t()
+    rc = lib.pw_workspace_size(h, consumer, C, k, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_bounded(lib):
+    """The workspace never grows with N*M: at fixed N it is constant in M
+    (the guide's 'tile workspace'), and it scales with N (C + k)."""
+    for cons, C, k in ((0, 4, 0), (1, 0, 0), (2, 0, 0), (3, 64, 0), (4, 0, 10)):
+        sizes = []
+        for M in (4096, 65536, 1 << 20, 1 << 24):
+            rc, h = bind(lib, N=65536, M=M, D=32)
+            assert rc == 0
+            rc, n = ws_size(lib, h, cons, C, k)
+            assert rc == 0
+            sizes.append(n)
+            lib.pw_release(h)
+        assert max(sizes) <= sizes[0] * 1.01 + 4096, (cons, sizes)
+        assert max(sizes) < 65536 * 64 * (C + k + 3) * 8 + (1 << 20)
+
+
+def test_workspace_includes_epilogue_vectors(lib):
+    rc, h = bind(lib, N=1000, M=3000, ops=[(2, 0, FAKE), (3, 0, FAKE)])
+    assert rc == 0
+    _, n = ws_size(lib, h, 2)
+    assert n >= 2 * 1000 * 4 + 2 * 3000 * 4
+    lib.pw_release(h)
+
+
+def test_consumer_validation(lib):
+    rc, h = bind(lib, N=10, M=12, D=4)
+    assert rc == 0
+    V = FAKE
+    # matmul / softmax
+    assert lib.pw_matmul(h, V, 0, 4, FAKE, 4, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID      # C = 0
+    assert lib.pw_matmul(h, V, 4, 3, FAKE, 4, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID      # ldv < C
+    assert lib.pw_matmul(h, V, 4, 4, FAKE, 3, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID      # ldo < C
+    assert lib.pw_matmul(h, 0, 4, 4, FAKE, 4, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID      # V null
+    assert lib.pw_matmul(h, V, 4, 4, 0, 4, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID         # out null
+    assert lib.pw_softmax_matmul(h, V, 4, 4, FAKE + 1, 4, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    assert lib.pw_matmul(None, V, 4, 4, FAKE, 4, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    # displacement / logsumexp
+    assert lib.pw_displacement(h, FAKE, 3, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID          # ldo < D
+    assert lib.pw_logsumexp(h, 2, FAKE, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID            # bad flag
+    assert lib.pw_logsumexp(h, 0, 0, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    # top-k
+    assert lib.pw_topk(h, 13, 0, FAKE, FAKE, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID       # k > M
+    assert lib.pw_topk(h, -1, 0, FAKE, FAKE, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    assert lib.pw_topk(h, 3, 2, FAKE, FAKE, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID        # bad largest
+    assert lib.pw_topk(h, 0, 0, 0, 0, 0, 0, None) == pw.PW_OK                               # k = 0: no-op
+    lib.pw_release(h)
+    # workspace too small / missing: reported before any launch
+    rc, h = bind(lib, N=10, M=100000, D=4)
+    rc, need = ws_size(lib, h, 0, 4)
+    assert rc == 0 and need > 0
+    assert lib.pw_matmul(h, V, 4, 4, FAKE, 4, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert lib.pw_matmul(h, V, 4, 4, FAKE, 4, 0, need, None) == pw.PW_ERR_WORKSPACE
+    lib.pw_release(h)
+    # k above the fused list size
+    rc, h = bind(lib, N=10, M=100)
+    assert lib.pw_topk(h, 65, 0, FAKE, FAKE, FAKE, 1 << 20, None) == pw.PW_ERR_UNSUPPORTED
+    lib.pw_release(h)
+
+
+def test_empty_rows_are_noops(lib):
+    rc, h = bind(lib, N=0, X=0, M=12)
+    assert rc == 0
+    assert lib.pw_matmul(h, FAKE, 4, 4, 0, 4, 0, 0, None) == pw.PW_OK
+    assert lib.pw_displacement(h, 0, 4, 0, 0, None) == pw.PW_OK
+    assert lib.pw_logsumexp(h, 1, 0, 0, 0, None) == pw.PW_OK
+    assert lib.pw_softmax_matmul(h, FAKE, 4, 4, 0, 4, 0, 0, None) == pw.PW_OK
+    assert lib.pw_topk(h, 3, 0, 0, 0, 0, 0, None) == pw.PW_OK
+    _, n = ws_size(lib, h, 3, 4)
+    assert n == 0
+    lib.pw_release(h)
+
+
+def test_plan_describe(lib):
+    rc, h = bind(lib, N=65536, M=65536, D=3)
+    buf = ctypes.create_string_buffer(256)
+    assert lib.pw_plan_describe(h, 0, 4, 0, buf, 256) == 0
+    assert b"splits=" in buf.value
+    lib.pw_release(h)
+
+
+def test_product_has_no_oracle_dependency():
+    """The product package neither imports nor links the oracle."""
+    import os
+    import re
+    root = os.path.dirname(pw.__file__)
+    for dirpath, _, files in os.walk(root):
+        for f in files:
+            if f.endswith((".py", ".h", ".hip", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text, f

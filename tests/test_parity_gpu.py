@@ -1,0 +1,234 @@
+"""GPU parity against the CPU oracle on seeded inputs small enough for the
+oracle, spanning several row blocks and column tiles with ragged tails,
+every metric, consumer, dtype and op-chain shape, and the edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_cases import bind_both, check_consumer, to_dev
+
+pytestmark = pytest.mark.gpu
+
+METRICS = ("linear", "sqeuclidean", "rbf")
+CONSUMERS = ("matmul", "displacement", "logsumexp", "softmax_matmul", "topk")
+DTYPES = (np.float32, np.float64)
+
+
+def _data(seed, n, m, d, dtype, scale=1.0):
+    r = np.random.default_rng(seed)
+    X = (scale * r.standard_normal((n, d))).astype(dtype)
+    Y = (scale * r.standard_normal((m, d))).astype(dtype)
+    return X, Y, r
+
+
+def _gamma(metric, d):
+    return 0.5 / d if metric == "rbf" else 1.0
+
+
+def _linear_scale(metric, d):
+    # keep linear scores O(1) so exp-based consumers stay in range
+    return [("mul", 1.0 / np.sqrt(d))] if metric == "linear" else []
+
+
+GRID = [(dt, m, c, d) for dt in DTYPES for m in METRICS for c in CONSUMERS for d in (3, 33)]
+
+
+@pytest.mark.parametrize("dtype,metric,consumer,D", GRID,
+                         ids=["%s-%s-%s-D%d" % (np.dtype(a).name, b, c, d) for a, b, c, d in GRID])
+def test_grid_ragged(dtype, metric, consumer, D):
+    """N=300 (two row blocks, ragged), M=333 (six column tiles, ragged)."""
+    X, Y, r = _data(7 + D, 300, 333, D, dtype)
+    V = r.standard_normal((333, 5)).astype(dtype)
+    ops = _linear_scale(metric, D)
+    if metric == "sqeuclidean" and consumer in ("logsumexp", "softmax_matmul"):
+        ops = [("mul", -0.5)]
+    e, oe = bind_both(X, Y, metric, _gamma(metric, D), ops)
+    check_consumer(e, oe, consumer, V=V, k=10, exclude_self=True, what=consumer)
+
+
+@pytest.mark.parametrize("D", [1, 2, 4, 5, 15, 16, 17, 31, 32, 63, 64])
+def test_feature_dims(D):
+    X, Y, r = _data(100 + D, 70, 130, D, np.float32)
+    V = r.standard_normal((130, 4)).astype(np.float32)
+    e, oe = bind_both(X, Y, "rbf", 0.5 / D)
+    check_consumer(e, oe, "matmul", V=V, what="matmul D=%d" % D)
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    check_consumer(e, oe, "topk", k=8, what="topk D=%d" % D)
+
+
+@pytest.mark.parametrize("C", [1, 3, 4, 5, 16, 17, 64, 65, 130])
+@pytest.mark.parametrize("consumer", ["matmul", "softmax_matmul"])
+def test_value_widths(C, consumer):
+    X, Y, r = _data(200 + C, 90, 150, 8, np.float32)
+    V = r.standard_normal((150, C)).astype(np.float32)
+    e, oe = bind_both(X, Y, "linear", ops=[("mul", 0.3)])
+    check_consumer(e, oe, consumer, V=V, what="%s C=%d" % (consumer, C))
+
+
+def _op_chains(N, M, dtype, r):
+    a = r.standard_normal(N).astype(dtype)
+    b = r.standard_normal(M).astype(dtype)
+    w = (0.5 + r.random(N)).astype(dtype)
+    u = (0.5 + r.random(M)).astype(dtype)
+    return {
+        "mul": [("mul", -0.7)],
+        "add": [("add", 1.5)],
+        "add_rows": [("mul", 0.5), ("add_rows", a)],
+        "add_columns": [("add_columns", b)],
+        "weight_rows": [("weight_rows", w)],
+        "weight_columns": [("weight_columns", u)],
+        "offsets_both": [("mul", -0.5), ("add_rows", a), ("add_columns", b)],
+        "exp_then_weights": [("mul", -0.2), ("exp", None), ("weight_rows", w), ("weight_columns", u)],
+        "nonseparable_rows_then_colweight": [("add_rows", a), ("weight_columns", u)],
+        "nonseparable_cols_then_rowweight": [("add_columns", b), ("weight_rows", w)],
+        "scalar_moves_to_columns": [("add", 0.75), ("weight_columns", u), ("add_rows", a)],
+        "two_exps": [("mul", -0.1), ("exp", None), ("mul", -1.0), ("exp", None)],
+        "eight_ops": [("mul", 0.5), ("add_rows", a), ("weight_columns", u), ("add", -0.25), ("add_columns", b),
+                      ("weight_rows", w), ("mul", 0.5), ("add", 0.1)],
+    }
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("chain", list(_op_chains(1, 1, np.float32, np.random.default_rng(0)).keys()))
+@pytest.mark.parametrize("consumer", ["matmul", "logsumexp", "softmax_matmul", "topk", "displacement"])
+def test_op_chains(dtype, chain, consumer):
+    X, Y, r = _data(300, 260, 200, 6, dtype, scale=0.5)
+    ops = _op_chains(260, 200, dtype, r)[chain]
+    V = r.standard_normal((200, 3)).astype(dtype)
+    e, oe = bind_both(X, Y, "sqeuclidean", ops=ops)
+    check_consumer(e, oe, consumer, V=V, k=5, largest=True, what="%s %s" % (chain, consumer))
+
+
+@pytest.mark.parametrize("N,M", [(1, 1), (1, 500), (500, 1), (3, 2), (257, 65), (64, 4097)])
+@pytest.mark.parametrize("consumer", CONSUMERS)
+def test_small_and_ragged_sizes(N, M, consumer):
+    X, Y, r = _data(N * 1000 + M, N, M, 3, np.float64)
+    V = r.standard_normal((M, 2))
+    e, oe = bind_both(X, Y, "rbf", 0.3)
+    check_consumer(e, oe, consumer, V=V, k=min(M, 4), exclude_self=True, what="%s N=%d M=%d" % (consumer, N, M))
+
+
+@pytest.mark.parametrize("N,M", [(300, 200), (200, 300), (129, 129)])
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+def test_exclude_self(N, M, dtype):
+    """The pair j == i is dropped by index; rows i >= M exclude nothing."""
+    X, Y, r = _data(400 + N, N, M, 4, dtype)
+    for exclude in (False, True):
+        e, oe = bind_both(X, Y, "linear", ops=[("mul", 2.0)])
+        check_consumer(e, oe, "logsumexp", exclude_self=exclude, what="exclude=%s" % exclude)
+
+
+def test_exclude_self_aliased_identical_rows():
+    """X = Y with all rows equal: lse = s + log(M - 1) everywhere; one row -> -inf."""
+    X = np.tile(np.array([[0.25, -0.5, 1.0]], np.float32), (1000, 1))
+    e, oe = bind_both(X, X, "linear", same=True)
+    check_consumer(e, oe, "logsumexp", exclude_self=True, what="identical rows")
+    X1 = X[:1]
+    e, oe = bind_both(X1, X1, "linear", same=True)
+    out = e.logsumexp(exclude_self=True).cpu().numpy()
+    assert np.isneginf(out).all()
+
+
+@pytest.mark.parametrize("k", [1, 2, 10, 16, 17, 40, 64])
+@pytest.mark.parametrize("largest", [False, True])
+def test_topk_exact_ties(k, largest):
+    """Integer grid with duplicated reference rows: every score is exact, so
+    values and indices must match the oracle bit for bit, lowest index first."""
+    r = np.random.default_rng(500 + k)
+    X = r.integers(-3, 4, (300, 3)).astype(np.float32)
+    Y = r.integers(-3, 4, (700, 3)).astype(np.float32)
+    Y[100:200] = Y[:100]
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    check_consumer(e, oe, "topk", k=k, largest=largest, exact=True, what="exact k=%d" % k)
+    e, oe = bind_both(X, Y, "linear")
+    check_consumer(e, oe, "topk", k=k, largest=largest, exact=True, what="exact linear k=%d" % k)
+
+
+def test_topk_full_permutation():
+    """k = M returns the whole stable order."""
+    r = np.random.default_rng(9)
+    X = r.integers(-2, 3, (50, 2)).astype(np.float64)
+    Y = r.integers(-2, 3, (64, 2)).astype(np.float64)
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    check_consumer(e, oe, "topk", k=64, exact=True, what="k=M")
+
+
+def test_matmul_exact_integers():
+    """Integer inputs with the linear metric: every partial sum is exact."""
+    r = np.random.default_rng(11)
+    X = r.integers(-5, 6, (300, 7)).astype(np.float64)
+    Y = r.integers(-5, 6, (900, 7)).astype(np.float64)
+    V = r.integers(-5, 6, (900, 3)).astype(np.float64)
+    e, _ = bind_both(X, Y, "linear")
+    g = e.matmul(to_dev(V)).cpu().numpy()
+    ref = X.astype(np.int64) @ Y.astype(np.int64).T @ V.astype(np.int64)
+    assert np.array_equal(g, ref.astype(np.float64))
+
+
+def test_rbf_self_pairs_are_one():
+    """rbf(x, x) = 1: isolated points (100 apart) give the row mass exactly 1."""
+    X = (100.0 * np.arange(600, dtype=np.float64)[:, None] * np.array([[1.0, 0.5]])).astype(np.float32)
+    V = np.ones((600, 1), np.float32)
+    e, _ = bind_both(X, X, "rbf", 1.0, same=True)
+    g = e.matmul(to_dev(V)).cpu().numpy()
+    assert np.array_equal(g, np.ones((600, 1), np.float32))
+
+
+def test_softmax_rows_sum_to_one():
+    X, Y, r = _data(12, 400, 700, 16, np.float32)
+    V = np.ones((700, 1), np.float32)
+    e, _ = bind_both(X, Y, "linear", ops=[("mul", 0.25)])
+    g = e.softmax_matmul(to_dev(V)).cpu().numpy()
+    assert np.max(np.abs(g - 1.0)) < 1e-5
+
+
+@pytest.mark.parametrize("consumer", CONSUMERS)
+def test_empty_columns(consumer):
+    """M = 0: sums are zero, log-sum-exp is -inf; N = 0 is a no-op."""
+    X = np.ones((5, 3), np.float32)
+    Y = np.zeros((0, 3), np.float32)
+    e, _ = bind_both(X, Y, "linear")
+    V = to_dev(np.zeros((0, 2), np.float32))
+    if consumer == "matmul":
+        assert (e.matmul(V).cpu().numpy() == 0).all()
+    elif consumer == "softmax_matmul":
+        assert (e.softmax_matmul(V).cpu().numpy() == 0).all()
+    elif consumer == "displacement":
+        assert (e.displacement().cpu().numpy() == 0).all()
+    elif consumer == "logsumexp":
+        assert np.isneginf(e.logsumexp().cpu().numpy()).all()
+    else:
+        with pytest.raises(ValueError):
+            e.topk(1)
+    e0, _ = bind_both(np.zeros((0, 3), np.float32), np.ones((4, 3), np.float32), "linear")
+    assert e0.matmul(to_dev(np.ones((4, 2), np.float32))).shape == (0, 2)
+
+
+def test_determinism():
+    """Two calls with the same plan give bitwise-identical results."""
+    X, Y, r = _data(13, 2000, 3000, 32, np.float32)
+    V = r.standard_normal((3000, 8)).astype(np.float32)
+    e, _ = bind_both(X, Y, "rbf", 0.05)
+    a = e.matmul(to_dev(V)).cpu().numpy()
+    b = e.matmul(to_dev(V)).cpu().numpy()
+    assert np.array_equal(a, b)
+    d, _ = bind_both(X, Y, "sqeuclidean")
+    va, ia = d.topk(10)
+    vb, ib = d.topk(10)
+    assert torch.equal(va, vb) and torch.equal(ia, ib)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS.keys()))
+def test_reduced_workloads(name):
+    """Every workload's distributions and op chains at a size the oracle
+    finishes in seconds."""
+    arrays, cases = workloads.make(name, reduced=True)
+    for c in cases:
+        ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+        same = c.x == c.y
+        e, oe = bind_both(arrays[c.x], arrays[c.y], c.metric, c.gamma, ops, same=same)
+        V = arrays[c.v] if c.v else None
+        check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k, largest=c.largest,
+                       what="%s/%s" % (name, c.name))

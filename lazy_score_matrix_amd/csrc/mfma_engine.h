@@ -1,0 +1,493 @@
+// Matrix-core (MFMA) tile engine for gfx950.
+//
+// Used when the feature dimension makes X.Y^T a real contraction (D >= 16).
+// A workgroup of 4 waves owns BM query rows; every wave owns QB blocks of TM
+// queries and streams the workgroup's column range through LDS tiles of 64
+// keys. Per TM-key sub-block a wave computes the TRANSPOSED score block
+// S^T = K . Q^T on the matrix cores:
+//   float:  v_mfma_f32_32x32x2f32  (TM = 32; lane l holds query l%32 and the
+//           16 keys 8*(r/4) + 4*(l/32) + r%4, r = 0..15)
+//   double: v_mfma_f64_16x16x4f64  (TM = 16; lane l holds query l%16 and the
+//           4 keys 4*r + l/16, r = 0..3)
+// so each lane holds one query's scores and a row reduction needs only a
+// register fold plus one or two cross-lane exchanges. The same registers are
+// directly the B operand of the second contraction O^T += V^T . P (matmul,
+// softmax@V, displacement), whose accumulator again keeps one query per lane.
+//
+// Distances use |x|^2 + |y|^2 - 2 x.y: the query operand is pre-scaled by -2
+// (exact) and the accumulator starts at |x_i|^2 + |y_j|^2, so the matrix
+// cores return the squared distance directly; it is clamped at 0.
+//
+// Epilogue: this engine takes chains that reduce to one affine stage with
+// row terms only (s <- r_i s + p_i, scalars or per-row vectors); any other
+// chain runs on the VALU engine. For logsumexp and softmax the scores are
+// kept in base 2 (log2(e) folded into r_i), p_i is added once at the end
+// for logsumexp and drops out of softmax.
+#pragma once
+
+#include "device_common.h"
+
+namespace pw {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <class T>
+struct Mfma;
+
+template <>
+struct Mfma<float> {
+  static constexpr int TM = 32, G = 2, NREG = 16;
+  typedef f32x16 acc_t;
+  __device__ __forceinline__ static int key_of(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+  __device__ __forceinline__ static acc_t mma(float a, float b, const acc_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static float gmax(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+  __device__ __forceinline__ static float gsum(float v) { return v + __shfl_xor(v, 32); }
+  __device__ __forceinline__ static float exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+  __device__ __forceinline__ static float log(float x) { return __builtin_amdgcn_logf(x) * kLn2_f; }
+};
+
+template <>
+struct Mfma<double> {
+  static constexpr int TM = 16, G = 4, NREG = 4;
+  typedef f64x4 acc_t;
+  __device__ __forceinline__ static int key_of(int r, int g) { return 4 * r + g; }
+  __device__ __forceinline__ static acc_t mma(double a, double b, const acc_t &c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static double gmax(double v) {
+    v = fmax(v, __shfl_xor(v, 16));
+    return fmax(v, __shfl_xor(v, 32));
+  }
+  __device__ __forceinline__ static double gsum(double v) {
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+  }
+  __device__ __forceinline__ static double exp2(double x) { return ::exp2(x); }
+  __device__ __forceinline__ static double log(double x) { return ::log(x); }
+};
+
+// Top-k filter threshold: the signed value (negated for `largest`) of the
+// list's last key, +inf while that slot is empty. Within one lane keys
+// arrive in increasing column order, so a candidate whose value equals the
+// threshold loses the index tie-break and is rightly skipped by a strict <.
+__device__ __forceinline__ float key_threshold(const Key<float> &last) {
+  const uint32_t hi = (uint32_t)(last.k >> 32);
+  return hi == 0xffffffffu ? __builtin_huge_valf() : f32_from_ord(hi);
+}
+__device__ __forceinline__ double key_threshold(const Key<double> &last) {
+  return last.v == ~0ull ? __builtin_huge_val() : f64_from_ord(last.v);
+}
+__device__ __forceinline__ Key<float> key_placeholder(Key<float>) { return Key<float>{0ull}; }
+__device__ __forceinline__ Key<double> key_placeholder(Key<double>) { return Key<double>{0ull, 0u}; }
+// Cooperative loader of a [ROWS, COLS] tile (COLS padded, zero beyond the
+// valid columns and rows) through registers: load() issues the global reads
+// for the next tile before the current one is computed, store() writes them
+// to LDS after it. Reads are 16-byte vectors when the source allows.
+template <class T, int ROWS, int COLS>
+struct TileLoader {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int VPR = COLS / VEC;  // vectors per row
+  static constexpr int NV = (ROWS * VPR + 255) / 256;
+  typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  vec_t buf[NV];
+
+  __device__ __forceinline__ void load(const T *__restrict__ src, int64_t ld, int64_t row0, int nrows, int ncols,
+                                       bool vec_ok, int tid) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int idx = tid + v * 256;
+      const int r = idx / VPR, c = (idx % VPR) * VEC;
+      vec_t x;
+      if (idx < ROWS * VPR && r < nrows && vec_ok && c + VEC <= ncols) {
+        x = *reinterpret_cast<const vec_t *>(src + (row0 + r) * ld + c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          x[e] = (idx < ROWS * VPR && r < nrows && c + e < ncols) ? src[(row0 + r) * ld + c + e] : (T)0;
+      }
+      buf[v] = x;
+    }
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(T (*dst)[LD], int tid) const {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int idx = tid + v * 256;
+      if (idx < ROWS * VPR) {
+        const int r = idx / VPR, c = (idx % VPR) * VEC;
+        *reinterpret_cast<vec_t *>(&dst[r][c]) = buf[v];
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ bool vec_ok(const void *p, int64_t ld, int vec) {
+  return ((uintptr_t)p % 16 == 0) && (ld % vec == 0);
+}
+
+template <class T, int CONS>
+struct MfmaShape {
+  static constexpr int QB = (sizeof(T) == 8 && CONS != C_TOPK) ? 2 : 1;
+  static constexpr int BM = kMfmaWaves * QB * Mfma<T>::TM;
+  static_assert(BM == mfma_bm(sizeof(T) == 4 ? 0 : 1, CONS), "host and device row-block sizes differ");
+};
+
+template <class T, int METRIC, int CONS, int DP, int CP, int KL>
+__global__ __launch_bounds__(256, 2) void mfma_tile(const TileArgs a) {
+  using F = Mfma<T>;
+  using acc_t = typename F::acc_t;
+  constexpr int TM = F::TM, G = F::G, NREG = F::NREG;
+  constexpr int QB = MfmaShape<T, CONS>::QB;
+  constexpr int BM = MfmaShape<T, CONS>::BM;
+  constexpr int BN = kMfmaBN;
+  constexpr int SB = BN / TM;
+  constexpr int DG = DP / G;
+  constexpr bool DIST = METRIC != M_LINEAR;
+  constexpr bool HAS_V = CONS == C_MATMUL || CONS == C_SOFTMAX;
+  constexpr bool ONLINE = CONS == C_LOGSUMEXP || CONS == C_SOFTMAX;
+  constexpr int NCB = HAS_V ? CP / TM : (CONS == C_DISPLACEMENT ? (DP + TM - 1) / TM : 1);
+  constexpr bool PV = HAS_V || CONS == C_DISPLACEMENT;
+  constexpr int KPAD = sizeof(T) == 4 ? 4 : 2;
+  constexpr int VW = HAS_V ? CP : 1;
+  constexpr int KLQ = CONS == C_TOPK ? KL : 1;
+  constexpr T kNegInf = -__builtin_huge_valf();
+
+  __shared__ __attribute__((aligned(16))) T sK[BN][DP + KPAD];
+  __shared__ __attribute__((aligned(16))) T sN[BN];
+  __shared__ __attribute__((aligned(16))) T sV[HAS_V ? BN : 1][VW];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l / TM, q = l % TM;
+  const int rb = blockIdx.x % a.n_rb;
+  const int sp = blockIdx.x / a.n_rb;
+  const int64_t row0 = (int64_t)rb * BM;
+  const int64_t jb = (int64_t)sp * a.split_cols;
+  const int64_t je = min(a.M, jb + a.split_cols);
+  const T* __restrict__ Xp = static_cast<const T *>(a.X);
+  const T* __restrict__ Yp = static_cast<const T *>(a.Y);
+
+  int64_t qi[QB];
+  bool qv[QB];
+  T qr[QB][DG];
+  T nx[QB];
+  T er[QB], ep[QB];  // row epilogue: s <- er * s + ep
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    qi[b] = row0 + (int64_t)(w * QB + b) * TM + q;
+    qv[b] = qi[b] < a.N;
+    T part = 0;
+#pragma unroll
+    for (int s = 0; s < DG; ++s) {
+      const int d = g * DG + s;
+      T v = (qv[b] && d < a.D) ? Xp[qi[b] * a.ldx + d] : (T)0;
+      part = fma(v, v, part);
+      qr[b][s] = DIST ? (T)-2 * v : v;
+    }
+    nx[b] = F::gsum(part);
+    T r = (T)1, p = (T)0;
+    if (a.epi.n_stages == 1) {
+      const Stage &st = a.epi.st[0];
+      if (st.row_vec) {
+        if (qv[b]) {
+          r = ldg<T>(st.r_vec, qi[b]);
+          p = ldg<T>(st.p_vec, qi[b]);
+        }
+      } else {
+        r = (T)st.r_scalar;
+        p = (T)st.p_scalar;
+      }
+    }
+    if constexpr (ONLINE) r *= (T)kLog2e;  // base-2 scores
+    er[b] = r;
+    ep[b] = p;
+  }
+  const T ngl2 = (T)(-a.gamma * kLog2e);
+
+  acc_t o[QB][NCB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int r = 0; r < NREG; ++r) o[b][c][r] = 0;
+  T m[QB], lsum[QB], mass[QB];
+  Key<T> list[QB][KLQ];
+  T thr[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    thr[b] = __builtin_huge_valf();
+    m[b] = kNegInf;
+    lsum[b] = 0;
+    mass[b] = 0;
+#pragma unroll
+    for (int p = 0; p < KLQ; ++p)
+      list[b][p] = (p < KLQ - a.k) ? key_placeholder(Key<T>()) : Key<T>::sentinel();
+  }
+
+  // Register-prefetched tiles: the global reads of tile t+1 are in flight
+  // while tile t is computed from LDS.
+  TileLoader<T, BN, DP> ldK;
+  TileLoader<T, BN, HAS_V ? CP : 16 / (int)sizeof(T)> ldV;
+  T nyv = 0;
+  const bool kvec = vec_ok(a.Y, a.ldy, 16 / (int)sizeof(T));
+  const bool vvec = HAS_V && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
+  auto prefetch = [&](int64_t t0) {
+    const int nbt = (int)min((int64_t)BN, je - t0);
+    ldK.load(Yp, a.ldy, t0, nbt, a.D, kvec, tid);
+    if constexpr (HAS_V) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, vvec, tid);
+    if constexpr (DIST) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
+  };
+  if (jb < je) prefetch(jb);
+
+  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+    const int nb = (int)min((int64_t)BN, je - j0);
+    __syncthreads();
+    ldK.store(sK, tid);
+    if constexpr (HAS_V) ldV.store(sV, tid);
+    if constexpr (DIST) {
+      if (tid < BN) sN[tid] = nyv;
+    }
+    __syncthreads();
+    if (j0 + BN < je) prefetch(j0 + BN);
+    const bool diag = CONS == C_LOGSUMEXP && a.exclude_self && j0 < row0 + BM && j0 + BN > row0;
+
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      const int kb = sb * TM;
+      if (kb >= nb) break;
+      const bool tail = kb + TM > nb;
+      acc_t s[QB];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) s[b][r] = DIST ? nx[b] + sN[kb + F::key_of(r, g)] : (T)0;
+#pragma unroll
+      for (int st = 0; st < DG; ++st) {
+        const T av = sK[kb + q][g * DG + st];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b] = F::mma(av, qr[b][st], s[b]);
+      }
+
+      // Epilogue: finished score per register (base 2 for the online consumers).
+      T v[QB][NREG];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          T x = s[b][r];
+          if constexpr (DIST) x = max(x, (T)0);
+          if constexpr (METRIC == M_RBF) x = F::exp2(x * ngl2);
+          if constexpr (ONLINE) {
+            x = x * er[b];
+          } else {
+            x = fma(x, er[b], ep[b]);
+          }
+          v[b][r] = x;
+        }
+        if (tail) {
+#pragma unroll
+          for (int r = 0; r < NREG; ++r)
+            if (kb + F::key_of(r, g) >= nb) v[b][r] = ONLINE ? kNegInf : (T)0;
+        }
+        if (CONS == C_LOGSUMEXP && diag) {
+#pragma unroll
+          for (int r = 0; r < NREG; ++r)
+            if (j0 + kb + F::key_of(r, g) == qi[b]) v[b][r] = kNegInf;
+        }
+      }
+
+      if constexpr (ONLINE) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          T bm = v[b][0];
+#pragma unroll
+          for (int r = 1; r < NREG; ++r) bm = max(bm, v[b][r]);
+          bm = F::gmax(bm);
+          const T mn = max(m[b], bm);
+          const bool live = mn != kNegInf;
+          const T alpha = live ? F::exp2(m[b] - mn) : (T)1;
+          T acc = 0;
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const T p = live ? F::exp2(v[b][r] - mn) : (T)0;
+            v[b][r] = p;
+            acc += p;
+          }
+          lsum[b] = fma(lsum[b], alpha, acc);
+          m[b] = mn;
+          if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) o[b][c] *= alpha;
+          }
+        }
+      }
+
+      if constexpr (PV) {
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const int key = kb + F::key_of(r, g);
+            T av;
+            if constexpr (HAS_V) {
+              av = sV[key][c * TM + q];
+            } else {
+              const int ch = c * TM + q;
+              av = ch < DP ? sK[key][ch] : (T)0;
+            }
+#pragma unroll
+            for (int b = 0; b < QB; ++b) o[b][c] = F::mma(av, v[b][r], o[b][c]);
+          }
+        }
+        if constexpr (CONS == C_DISPLACEMENT) {
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int r = 0; r < NREG; ++r) mass[b] += v[b][r];
+        }
+      }
+
+      if constexpr (CONS == C_TOPK) {
+        // Filter on the value alone against the list's last real key (as a
+        // signed value, +inf while the list is not full).
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const int key = kb + F::key_of(r, g);
+            const T sv = a.largest ? -v[b][r] : v[b][r];
+            if (key < nb && sv < thr[b]) {
+              key_insert<T, KLQ>(list[b], Key<T>::make(v[b][r], (uint32_t)(j0 + key), a.largest));
+              thr[b] = key_threshold(list[b][KLQ - 1]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- finalize
+  const bool fin = a.n_split == 1;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int64_t i = qi[b];
+    const int64_t prow = (int64_t)sp * a.N + i;
+    if constexpr (CONS == C_LOGSUMEXP) {
+      const T lt = F::gsum(lsum[b]);
+      if (g == 0 && qv[b]) {
+        const T mnat = m[b] * (T)kLn2 + ep[b];
+        if (fin) {
+          static_cast<T *>(a.out)[i] = lt > (T)0 ? mnat + F::log(lt) : kNegInf;
+        } else {
+          T *pp = static_cast<T *>(a.partial) + prow * 2;
+          pp[0] = lt > (T)0 ? mnat : kNegInf;
+          pp[1] = lt;
+        }
+      }
+    } else if constexpr (CONS == C_SOFTMAX) {
+      const T lt = F::gsum(lsum[b]);
+      if (qv[b]) {
+        const T inv = lt > (T)0 ? (T)1 / lt : (T)0;
+        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * (a.C + 2) + 2;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const int ch = c * TM + F::key_of(r, g);
+            if (ch < a.C) dst[ch] = fin ? o[b][c][r] * inv : o[b][c][r];
+          }
+        if (!fin && g == 0) {
+          T *pp = static_cast<T *>(a.partial) + prow * (a.C + 2);
+          pp[0] = lt > (T)0 ? m[b] * (T)kLn2 : kNegInf;
+          pp[1] = lt;
+        }
+      }
+    } else if constexpr (CONS == C_MATMUL) {
+      if (qv[b]) {
+        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.C;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const int ch = c * TM + F::key_of(r, g);
+            if (ch < a.C) dst[ch] = o[b][c][r];
+          }
+      }
+    } else if constexpr (CONS == C_DISPLACEMENT) {
+      const T mt = F::gsum(mass[b]);
+      if (qv[b]) {
+        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.D;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const int ch = c * TM + F::key_of(r, g);
+            if (ch < a.D) dst[ch] = o[b][c][r] - Xp[i * a.ldx + ch] * mt;
+          }
+      }
+    } else if constexpr (CONS == C_TOPK) {
+      // Every lane group's list is its own partial (split sp, group g); the
+      // merge kernel combines the n_split * G sorted lists of each row.
+      if (qv[b]) {
+        const int off = KLQ - a.k;
+        const int64_t prow_g = ((int64_t)sp * G + g) * a.N + i;
+#pragma unroll
+        for (int p = 0; p < KLQ; ++p)
+          if (p >= off) list[b][p].store(a.partial, prow_g * a.k + (p - off));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <class T, int METRIC, int CONS, int DP, int CP, int KL>
+hipError_t launch_mfma_kernel(const TileArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(256);
+  hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, int METRIC, int CONS, int DP>
+hipError_t mfma_by_tile(const MfmaConfig &c, const TileArgs &a, hipStream_t s) {
+  if constexpr (CONS == C_MATMUL || CONS == C_SOFTMAX) {
+    if constexpr (sizeof(T) == 8) {
+      if (c.cp == 16) return launch_mfma_kernel<T, METRIC, CONS, DP, 16, 1>(a, s);
+    }
+    if (c.cp == 32) return launch_mfma_kernel<T, METRIC, CONS, DP, 32, 1>(a, s);
+    if (c.cp == 64) return launch_mfma_kernel<T, METRIC, CONS, DP, 64, 1>(a, s);
+  } else if constexpr (CONS == C_TOPK) {
+    if (c.kl == 16) return launch_mfma_kernel<T, METRIC, CONS, DP, 1, 16>(a, s);
+    if (c.kl == 64) return launch_mfma_kernel<T, METRIC, CONS, DP, 1, 64>(a, s);
+  } else {
+    return launch_mfma_kernel<T, METRIC, CONS, DP, 1, 1>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T, int METRIC, int DP>
+hipError_t mfma_by_consumer(int consumer, const MfmaConfig &c, const TileArgs &a, hipStream_t s) {
+  switch (consumer) {
+    case C_MATMUL: return mfma_by_tile<T, METRIC, C_MATMUL, DP>(c, a, s);
+    case C_DISPLACEMENT: return mfma_by_tile<T, METRIC, C_DISPLACEMENT, DP>(c, a, s);
+    case C_LOGSUMEXP: return mfma_by_tile<T, METRIC, C_LOGSUMEXP, DP>(c, a, s);
+    case C_SOFTMAX: return mfma_by_tile<T, METRIC, C_SOFTMAX, DP>(c, a, s);
+    case C_TOPK: return mfma_by_tile<T, METRIC, C_TOPK, DP>(c, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T, int METRIC>
+hipError_t mfma_launch_metric(int consumer, const MfmaConfig &c, const TileArgs &a, hipStream_t s) {
+  switch (c.dp) {
+    case 16: return mfma_by_consumer<T, METRIC, 16>(consumer, c, a, s);
+    case 32: return mfma_by_consumer<T, METRIC, 32>(consumer, c, a, s);
+    case 64: return mfma_by_consumer<T, METRIC, 64>(consumer, c, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pw

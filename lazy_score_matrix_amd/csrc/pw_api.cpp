@@ -144,18 +144,32 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 size_t esize(int dtype) { return dtype == PW_F32 ? 4 : 8; }
 
 struct Plan {
-  int family = 0;  // 0: generic VALU engine
+  int family = 0;  // 0: generic VALU engine, 1: MFMA engine
   ValuConfig vcfg{4, 0};
+  MfmaConfig mcfg{16, 32, 16};
   int bm = kValuBM, bn = kValuBN;
   int n_rb = 0, n_split = 1;
+  int n_part = 1;  // partial lists or sums per row the merge reads (0: none)
   int64_t split_cols = 0;
   int chunk = 0;  // value columns per launch (matmul, softmax)
-  size_t off_epi = 0, off_part = 0, part_bytes = 0, total = 0;
+  bool col_norms = false;
+  size_t off_epi = 0, off_ny = 0, off_part = 0, part_bytes = 0, total = 0;
   std::vector<size_t> stage_off;  // per stage: offset of its vectors
 };
 
 int valu_dtile(int64_t D) { return D <= 4 ? 4 : (D <= 16 ? 16 : 64); }
 int valu_vtile(int64_t C) { return C <= 4 ? 4 : (C <= 16 ? 16 : 64); }
+
+// The MFMA engine takes D >= 16 (a real contraction), chains that reduce to
+// at most one affine stage with row terms only, and for the value consumers
+// at least 16 value columns (narrower products stay on the VALU engine).
+bool mfma_eligible(const pw_expr &e, int consumer, int64_t C) {
+  if (e.D < 16) return false;
+  if (e.stages.size() > 1) return false;
+  if (e.stages.size() == 1 && (e.stages[0].kind != ST_AFFINE || e.stages[0].col_vec)) return false;
+  if ((consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) && C < 16) return false;
+  return true;
+}
 
 Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   Plan p;
@@ -170,26 +184,46 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     }
   }
   p.off_epi = 0;
-  p.off_part = off;
-  // Tile grid.
-  p.vcfg.dtile = valu_dtile(e.D);
-  if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {
-    p.vcfg.vtile = valu_vtile(C);
-    p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
-  } else if (consumer == PW_C_TOPK) {
-    p.vcfg.vtile = k <= 16 ? 16 : 64;
+  int64_t target_wgs = kTargetWGs;
+  if (mfma_eligible(e, consumer, C)) {
+    p.family = 1;
+    p.bm = mfma_bm(e.dtype, consumer);
+    p.bn = kMfmaBN;
+    p.mcfg.dp = e.D <= 16 ? 16 : (e.D <= 32 ? 32 : 64);
+    if (e.dtype == PW_F32) p.mcfg.cp = C <= 32 ? 32 : 64;
+    else p.mcfg.cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
+    p.mcfg.kl = k <= 16 ? 16 : 64;
+    p.chunk = (int)std::min<int64_t>(C, p.mcfg.cp);
+    p.col_norms = e.metric != PW_LINEAR;
+    target_wgs = 2 * kTargetCUs;
   } else {
-    p.vcfg.vtile = 0;
+    p.vcfg.dtile = valu_dtile(e.D);
+    if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {
+      p.vcfg.vtile = valu_vtile(C);
+      p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
+    } else if (consumer == PW_C_TOPK) {
+      p.vcfg.vtile = k <= 16 ? 16 : 64;
+    } else {
+      p.vcfg.vtile = 0;
+    }
   }
+  p.off_ny = off;
+  if (p.col_norms) off += align_up((size_t)e.M * es);
+  p.off_part = off;
+  // Tile grid: enough workgroups to fill the chip, splitting the columns
+  // when there are too few row blocks.
   p.n_rb = (int)((e.N + p.bm - 1) / p.bm);
   const int64_t tiles = std::max<int64_t>(1, (e.M + p.bn - 1) / p.bn);
-  int64_t want = std::max<int64_t>(1, (kTargetWGs + p.n_rb - 1) / std::max(p.n_rb, 1));
+  int64_t want = std::max<int64_t>(1, (target_wgs + p.n_rb - 1) / std::max(p.n_rb, 1));
   want = std::min(want, tiles);
   const int64_t tiles_per_split = (tiles + want - 1) / want;
   p.split_cols = tiles_per_split * p.bn;
   p.n_split = (int)std::max<int64_t>(1, (e.M + p.split_cols - 1) / p.split_cols);
-  // Partials.
-  if (p.n_split > 1) {
+  // Partials: one per column split, and for MFMA top-k one per split and
+  // lane group.
+  p.n_part = p.n_split;
+  if (p.family == 1 && consumer == PW_C_TOPK) p.n_part = p.n_split * mfma_groups(e.dtype);
+  if (p.n_part > 1) {
     size_t per_row = 0;
     switch (consumer) {
       case PW_C_MATMUL: per_row = (size_t)p.chunk * es; break;
@@ -198,7 +232,7 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       case PW_C_SOFTMAX_MATMUL: per_row = (size_t)(p.chunk + 2) * es; break;
       case PW_C_TOPK: per_row = (size_t)k * (e.dtype == PW_F32 ? 8 : 16); break;
     }
-    p.part_bytes = align_up((size_t)p.n_split * (size_t)e.N * per_row);
+    p.part_bytes = align_up((size_t)p.n_part * (size_t)e.N * per_row);
   }
   p.total = p.off_part + p.part_bytes;
   if (p.total) p.total += kAlign;  // room to align the caller's pointer
@@ -288,11 +322,26 @@ TileArgs base_args(const pw_expr &e, const Plan &p, char *base) {
   a.n_rb = p.n_rb;
   a.n_split = p.n_split;
   a.split_cols = p.split_cols;
-  a.partial = p.n_split > 1 ? base + p.off_part : nullptr;
+  a.partial = p.n_part > 1 ? base + p.off_part : nullptr;
+  a.ny = p.col_norms ? base + p.off_ny : nullptr;
   return a;
 }
 
 hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const TileArgs &a, hipStream_t s) {
+  if (p.family == 1) {
+    if (e.dtype == PW_F32) {
+      switch (e.metric) {
+        case PW_LINEAR: return mfma_launch_metric<float, M_LINEAR>(consumer, p.mcfg, a, s);
+        case PW_SQEUCLIDEAN: return mfma_launch_metric<float, M_SQEUCLIDEAN>(consumer, p.mcfg, a, s);
+        default: return mfma_launch_metric<float, M_RBF>(consumer, p.mcfg, a, s);
+      }
+    }
+    switch (e.metric) {
+      case PW_LINEAR: return mfma_launch_metric<double, M_LINEAR>(consumer, p.mcfg, a, s);
+      case PW_SQEUCLIDEAN: return mfma_launch_metric<double, M_SQEUCLIDEAN>(consumer, p.mcfg, a, s);
+      default: return mfma_launch_metric<double, M_RBF>(consumer, p.mcfg, a, s);
+    }
+  }
   if (e.dtype == PW_F32) {
     switch (e.metric) {
       case PW_LINEAR: return valu_launch_metric<float, M_LINEAR>(consumer, p.vcfg, a, s);
@@ -307,10 +356,20 @@ hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const Tile
   }
 }
 
+// Column norms |y_j|^2 for the MFMA engine's distance expansion.
+int prepare_norms(const pw_expr &e, const Plan &p, const TileArgs &a, hipStream_t s) {
+  if (!p.col_norms) return PW_OK;
+  return hip_status(launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s));
+}
+
 // One tile launch plus, when the columns are split, the merge.
 int run_tiles(const pw_expr &e, int consumer, const Plan &p, TileArgs &a, hipStream_t s) {
   int rc = hip_status(launch_tile(e, consumer, p, a, s));
-  if (rc == PW_OK && p.n_split > 1) rc = hip_status(launch_merge(e.dtype, consumer, a, s));
+  if (rc == PW_OK && p.n_part > 1) {
+    TileArgs m = a;
+    m.n_split = p.n_part;
+    rc = hip_status(launch_merge(e.dtype, consumer, m, s));
+  }
   return rc;
 }
 
@@ -424,11 +483,18 @@ int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf
   int rc = check_consumer_args(e, consumer, C, k);
   if (rc != PW_OK) return rc;
   Plan p = make_plan(*e, consumer, C, k);
-  std::snprintf(buf, len,
-                "family=valu dtile=%d vtile=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
-                "workspace=%zu",
-                p.vcfg.dtile, p.vcfg.vtile, p.bm, p.bn, p.n_rb, p.n_split, (long long)p.split_cols,
-                (int)e->stages.size(), p.total);
+  if (p.family == 1)
+    std::snprintf(buf, len,
+                  "family=mfma dp=%d cp=%d kl=%d bm=%d bn=%d row_blocks=%d splits=%d partials=%d split_cols=%lld "
+                  "stages=%d workspace=%zu",
+                  p.mcfg.dp, p.mcfg.cp, p.mcfg.kl, p.bm, p.bn, p.n_rb, p.n_split, p.n_part, (long long)p.split_cols,
+                  (int)e->stages.size(), p.total);
+  else
+    std::snprintf(buf, len,
+                  "family=valu dtile=%d vtile=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
+                  "workspace=%zu",
+                  p.vcfg.dtile, p.vcfg.vtile, p.bm, p.bn, p.n_rb, p.n_split, (long long)p.split_cols,
+                  (int)e->stages.size(), p.total);
   return PW_OK;
 }
 
@@ -450,6 +516,7 @@ static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
   rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
   if (rc != PW_OK) return rc;
   a.ldv = ldv;
   a.ldo = ldo;
@@ -486,6 +553,7 @@ int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t w
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
   rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
   if (rc != PW_OK) return rc;
   a.out = out;
   a.ldo = ldo;
@@ -506,6 +574,7 @@ int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
   rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
   if (rc != PW_OK) return rc;
   a.out = out;
   a.exclude_self = exclude_self;
@@ -526,6 +595,7 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
   rc = prepare_epilogue(*e, p, base, &a.epi, s);
+  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
   if (rc != PW_OK) return rc;
   a.out = values;
   a.idx = indices;

@@ -122,6 +122,25 @@ hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArg
 constexpr int kValuBM = 256;  // rows per workgroup (one per thread)
 constexpr int kValuBN = 64;   // columns per staged tile
 
+// MFMA tile engine: D >= 16, op chains of at most one row-affine stage.
+//   dp: feature tile 16 / 32 / 64; cp: value tile (float 32 / 64, double
+//   16 / 32 / 64); kl: top-k list 16 / 64.
+struct MfmaConfig {
+  int dp;
+  int cp;
+  int kl;
+};
+constexpr int kMfmaWaves = 4;   // waves per workgroup
+constexpr int kMfmaBN = 64;     // keys per staged tile
+// Query rows per workgroup: 4 waves x QB blocks x (32 float / 16 double)
+// queries; double uses QB = 2 except for top-k.
+constexpr int mfma_bm(int dtype, int consumer) { return dtype == 0 ? 128 : (consumer == C_TOPK ? 64 : 128); }
+// Lane groups per query in the MFMA layouts (float 2, double 4); each keeps
+// its own top-k list, written as a separate partial.
+constexpr int mfma_groups(int dtype) { return dtype == 0 ? 2 : 4; }
+template <class T, int METRIC>
+hipError_t mfma_launch_metric(int consumer, const MfmaConfig &cfg, const TileArgs &a, hipStream_t s);
+
 // Auxiliary kernels.
 hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s);
 hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);

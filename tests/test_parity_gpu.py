@@ -232,3 +232,87 @@ def test_reduced_workloads(name):
         V = arrays[c.v] if c.v else None
         check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k, largest=c.largest,
                        what="%s/%s" % (name, c.name))
+
+
+# ---------------------------------------------------------------- MFMA engine
+MFMA_GRID = [(dt, m, c, d, ch) for dt in DTYPES for m in METRICS for c in CONSUMERS for d in (16, 32, 64)
+             for ch in ("none", "row_affine")]
+
+
+def _assert_family(e, consumer, family, C=0, k=0):
+    plan = e.plan(consumer, C, k)
+    assert ("family=%s" % family) in plan, plan
+
+
+@pytest.mark.parametrize("dtype,metric,consumer,D,chain", MFMA_GRID,
+                         ids=["%s-%s-%s-D%d-%s" % (np.dtype(a).name, b, c, d, ch) for a, b, c, d, ch in MFMA_GRID])
+def test_mfma_grid(dtype, metric, consumer, D, chain):
+    """MFMA engine: N=300 (ragged row blocks), M=333 (ragged 64-key tiles)."""
+    X, Y, r = _data(900 + D, 300, 333, D, dtype)
+    V = r.standard_normal((333, 20)).astype(dtype)
+    ops = _linear_scale(metric, D)
+    if metric == "sqeuclidean" and consumer in ("logsumexp", "softmax_matmul"):
+        ops = [("mul", -0.5 / D)]
+    if chain == "row_affine":
+        ops = ops + [("add_rows", r.standard_normal(300).astype(dtype)), ("weight_rows", (0.5 + r.random(300)).astype(dtype))]
+    e, oe = bind_both(X, Y, metric, _gamma(metric, D), ops)
+    _assert_family(e, consumer, "mfma", C=20, k=10)
+    check_consumer(e, oe, consumer, V=V, k=10, exclude_self=True, what="mfma %s" % consumer)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("C", [16, 17, 32, 33, 64, 65, 130])
+@pytest.mark.parametrize("consumer", ["matmul", "softmax_matmul"])
+def test_mfma_value_widths(dtype, C, consumer):
+    X, Y, r = _data(1000 + C, 150, 500, 32, dtype)
+    V = r.standard_normal((500, C)).astype(dtype)
+    e, oe = bind_both(X, Y, "linear", ops=[("mul", 0.2)])
+    _assert_family(e, consumer, "mfma", C=C)
+    check_consumer(e, oe, consumer, V=V, what="%s C=%d" % (consumer, C))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("k", [1, 10, 16, 17, 64])
+@pytest.mark.parametrize("largest", [False, True])
+def test_mfma_topk(dtype, k, largest):
+    X, Y, r = _data(1100 + k, 260, 1500, 32, dtype)
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    _assert_family(e, "topk", "mfma", k=k)
+    check_consumer(e, oe, "topk", k=k, largest=largest, what="mfma topk k=%d" % k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("k", [1, 5, 16, 40])
+def test_mfma_topk_exact_ties(dtype, k):
+    """Integer grid in 16 dimensions with duplicated references: the norm
+    expansion is exact, so indices and values must match bit for bit."""
+    r = np.random.default_rng(1200 + k)
+    X = r.integers(-2, 3, (200, 16)).astype(dtype)
+    Y = r.integers(-2, 3, (900, 16)).astype(dtype)
+    Y[300:600] = Y[:300]
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    _assert_family(e, "topk", "mfma", k=k)
+    check_consumer(e, oe, "topk", k=k, exact=True, what="mfma exact k=%d" % k)
+    e, oe = bind_both(X, Y, "linear")
+    check_consumer(e, oe, "topk", k=k, largest=True, exact=True, what="mfma exact linear k=%d" % k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("N", [129, 300, 1000])
+def test_mfma_exclude_self(dtype, N):
+    X, _, r = _data(1300 + N, N, 1, 64, dtype)
+    X /= np.linalg.norm(X, axis=1, keepdims=True)
+    b = r.standard_normal(N).astype(dtype)
+    e, oe = bind_both(X, X, "linear", ops=[("mul", 1 / 0.07), ("add_rows", b)], same=True)
+    _assert_family(e, "logsumexp", "mfma")
+    check_consumer(e, oe, "logsumexp", exclude_self=True, what="mfma infonce N=%d" % N)
+
+
+def test_mfma_determinism():
+    X, Y, r = _data(14, 3000, 5000, 64, np.float32)
+    V = r.standard_normal((5000, 64)).astype(np.float32)
+    e, _ = bind_both(X, Y, "linear", ops=[("mul", 0.125)])
+    _assert_family(e, "softmax_matmul", "mfma", C=64)
+    a = e.softmax_matmul(to_dev(V)).cpu().numpy()
+    b = e.softmax_matmul(to_dev(V)).cpu().numpy()
+    assert np.array_equal(a, b)

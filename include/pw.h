@@ -169,6 +169,14 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
  * column splits) into buf as a NUL-terminated string. For logs and tuning. */
 int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf, size_t len);
 
+/* Profiling hook for benchmarks: after this call, every consumer call made
+ * by the calling thread records the hipEvent_t `start` on its stream just
+ * before its main tile-kernel launch and `stop` just after it (for value
+ * widths above one launch's chunk, around all of the call's tile launches).
+ * The events are created and owned by the caller; NULL, NULL disables the
+ * hook. Thread-local: other threads are unaffected. Never fails. */
+int pw_set_tile_events(void *start, void *stop);
+
 /* Static text for a pw_status code. */
 const char *pw_error_string(int code);
 

@@ -69,6 +69,7 @@ def load_library(path: str = LIB_PATH):
         lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
+        lib.pw_set_tile_events.argtypes = [vp, vp]
         lib.pw_error_string.argtypes = [c_int]
         lib.pw_error_string.restype = ctypes.c_char_p
         if path == LIB_PATH:

@@ -60,26 +60,42 @@ hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t
 
 // ---------------------------------------------------------------------------
 // Row norms |x_i|^2 for the kernels that evaluate distances through the
-// expansion |x|^2 + |y|^2 - 2 x.y.
+// expansion |x|^2 + |y|^2 - 2 x.y. L consecutive lanes share a row and read
+// consecutive features, so a wave reads whole rows contiguously; the L
+// partial sums are folded with lane exchanges inside the group.
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(256) void row_norms_kernel(const T *X, int64_t n, int64_t ld, int D, T *out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+template <class T, int L>
+__global__ __launch_bounds__(256) void row_norms_kernel(const T *__restrict__ X, int64_t n, int64_t ld, int D,
+                                                        T *__restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / L;
+  const int lane = (int)(t % L);
   T s = 0;
-  for (int d = 0; d < D; ++d) {
-    T v = X[i * ld + d];
-    s = fma(v, v, s);
+  if (row < n) {
+    for (int d = lane; d < D; d += L) {
+      const T v = X[row * ld + d];
+      s = fma(v, v, s);
+    }
   }
-  out[i] = s;
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (row < n && lane == 0) out[row] = s;
+}
+
+template <class T>
+static hipError_t row_norms_t(const T *X, int64_t n, int64_t ld, int D, T *out, hipStream_t s) {
+  dim3 block(256);
+  auto grid = [&](int L) { return dim3((unsigned)((n * L + 255) / 256)); };
+  if (D <= 4) hipLaunchKernelGGL((row_norms_kernel<T, 4>), grid(4), block, 0, s, X, n, ld, D, out);
+  else if (D <= 8) hipLaunchKernelGGL((row_norms_kernel<T, 8>), grid(8), block, 0, s, X, n, ld, D, out);
+  else hipLaunchKernelGGL((row_norms_kernel<T, 16>), grid(16), block, 0, s, X, n, ld, D, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  if (dtype == 0) hipLaunchKernelGGL(row_norms_kernel<float>, grid, block, 0, s, (const float *)X, n, ld, D, (float *)out);
-  else hipLaunchKernelGGL(row_norms_kernel<double>, grid, block, 0, s, (const double *)X, n, ld, D, (double *)out);
-  return hipGetLastError();
+  if (dtype == 0) return row_norms_t<float>((const float *)X, n, ld, D, (float *)out, s);
+  return row_norms_t<double>((const double *)X, n, ld, D, (double *)out, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -362,9 +362,15 @@ int prepare_norms(const pw_expr &e, const Plan &p, const TileArgs &a, hipStream_
   return hip_status(launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s));
 }
 
+// Caller-owned events recorded around tile launches (pw_set_tile_events).
+thread_local hipEvent_t tile_ev_start = nullptr, tile_ev_stop = nullptr;
+
 // One tile launch plus, when the columns are split, the merge.
-int run_tiles(const pw_expr &e, int consumer, const Plan &p, TileArgs &a, hipStream_t s) {
+int run_tiles(const pw_expr &e, int consumer, const Plan &p, TileArgs &a, hipStream_t s, bool first = true,
+              bool last = true) {
+  if (first && tile_ev_start) hipEventRecord(tile_ev_start, s);
   int rc = hip_status(launch_tile(e, consumer, p, a, s));
+  if (last && tile_ev_stop) hipEventRecord(tile_ev_stop, s);
   if (rc == PW_OK && p.n_part > 1) {
     TileArgs m = a;
     m.n_split = p.n_part;
@@ -376,6 +382,12 @@ int run_tiles(const pw_expr &e, int consumer, const Plan &p, TileArgs &a, hipStr
 }  // namespace
 
 extern "C" {
+
+int pw_set_tile_events(void *start, void *stop) {
+  tile_ev_start = (hipEvent_t)start;
+  tile_ev_stop = (hipEvent_t)stop;
+  return PW_OK;
+}
 
 const char *pw_error_string(int code) {
   switch (code) {
@@ -525,7 +537,7 @@ static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t
     a.C = (int)std::min<int64_t>(p.chunk, C - c0);
     a.V = static_cast<const char *>(V) + c0 * es;
     a.out = static_cast<char *>(out) + c0 * es;
-    rc = run_tiles(*e, cons, p, a, s);
+    rc = run_tiles(*e, cons, p, a, s, c0 == 0, c0 + p.chunk >= C);
   }
   return rc;
 }

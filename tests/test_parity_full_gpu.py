@@ -1,0 +1,31 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times, checked against the oracle on a row sample: every 61st row (or a
+coarser stride for the largest sweeps) plus the first and last 256 rows, so
+every tile position and both ragged ends are covered."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_cases import bind_both, check_consumer
+
+pytestmark = pytest.mark.gpu
+
+STRIDE = {"knn": 257, "svgd": 151}
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS.keys()))
+def test_full_size_workload(name):
+    import oracle
+    import os
+    oracle.set_threads(len(os.sched_getaffinity(0)))
+    arrays, cases = workloads.make(name)
+    for c in cases:
+        ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+        e, oe = bind_both(arrays[c.x], arrays[c.y], c.metric, c.gamma, ops, same=c.x == c.y)
+        rows = workloads.sample_rows(oe.N, stride=STRIDE.get(name, 61))
+        V = arrays[c.v] if c.v else None
+        ratio, rel = check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k,
+                                    largest=c.largest, rows=rows, what="%s/%s" % (name, c.name))
+        print("%s/%s: %d rows, worst err/tol %.3g, plan %s" % (name, c.name, len(rows), ratio,
+                                                              e.plan(c.consumer, V.shape[1] if V is not None else 0,
+                                                                     c.k)))

@@ -69,6 +69,24 @@ struct Mfma<double> {
   __device__ __forceinline__ static double log(double x) { return ::log(x); }
 };
 
+// Table-driven 2^x in double (Tang's method): with t = 256 x (exact),
+// n = round(t) and f = t - n (exact, |f| <= 1/2),
+//   2^x = 2^floor(n/256) * 2^((n mod 256)/256) * e^(a f),  a = ln2/256,
+// where the middle factor comes from a 256-entry table in LDS and
+// e^(a f) - 1 from its Taylor polynomial to degree 4 (|a f| <= 1.36e-3, so
+// the first omitted term is below 4e-17). The scale by 2^floor(n/256) is an
+// ldexp, which also flushes far-underflowing results to zero; t is clamped
+// at -2^30 so that x = -inf gives 0.
+__device__ __forceinline__ double exp2_table(double x, const double *__restrict__ tab, const double (&c)[4]) {
+  const double t = fmax(x * 256.0, -1073741824.0);
+  const double nd = rint(t);
+  const double f = t - nd;
+  const int n = (int)nd;
+  const double p = f * fma(f, fma(f, fma(f, c[3], c[2]), c[1]), c[0]);
+  const double T = tab[n & 255];
+  return ldexp(fma(T, p, T), n >> 8);
+}
+
 // Top-k filter threshold: the signed value (negated for `largest`) of the
 // list's last key, +inf while that slot is empty. Within one lane keys
 // arrive in increasing column order, so a candidate whose value equals the
@@ -135,14 +153,22 @@ struct MfmaShape {
   static_assert(BM == mfma_bm(sizeof(T) == 4 ? 0 : 1, CONS), "host and device row-block sizes differ");
 };
 
+// Workgroups per CU the register budget is sized for: two (256 registers per
+// lane) for the common shapes, one (512) for 64-slot top-k lists and for
+// double precision with wide feature or value tiles.
+template <class T, int DP, int CP, int KL>
+struct MfmaOcc {
+  static constexpr int value = (KL > 16 || (sizeof(T) == 8 && (DP > 16 || CP > 16))) ? 1 : 2;
+};
+
 template <class T, int METRIC, int CONS, int DP, int CP, int KL>
-__global__ __launch_bounds__(256, 2) void mfma_tile(const TileArgs a) {
+__global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_tile(const TileArgs a) {
   using F = Mfma<T>;
   using acc_t = typename F::acc_t;
   constexpr int TM = F::TM, G = F::G, NREG = F::NREG;
   constexpr int QB = MfmaShape<T, CONS>::QB;
   constexpr int BM = MfmaShape<T, CONS>::BM;
-  constexpr int BN = kMfmaBN;
+  constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS);
   constexpr int SB = BN / TM;
   constexpr int DG = DP / G;
   constexpr bool DIST = METRIC != M_LINEAR;
@@ -158,22 +184,38 @@ __global__ __launch_bounds__(256, 2) void mfma_tile(const TileArgs a) {
   __shared__ __attribute__((aligned(16))) T sK[BN][DP + KPAD];
   __shared__ __attribute__((aligned(16))) T sN[BN];
   __shared__ __attribute__((aligned(16))) T sV[HAS_V ? BN : 1][VW];
+  constexpr bool TABLE_EXP = sizeof(T) == 8 && (ONLINE || METRIC == M_RBF);
+  __shared__ double sE[TABLE_EXP ? 256 : 1];
 
   const int tid = threadIdx.x;
+  // 2^x: the hardware exponential for float, the LDS table for double (the
+  // table is complete after the first barrier of the main loop).
+  double ec[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ec[k] = a.exp2_c[k];
+  if constexpr (TABLE_EXP) {
+    for (int j = tid; j < 256; j += 256) sE[j] = ::exp2((double)j / 256.0);
+  }
+  auto ex2 = [&](T x) -> T {
+    if constexpr (TABLE_EXP) return exp2_table(x, sE, ec);
+    else return F::exp2(x);
+  };
   const int w = tid >> 6, l = tid & 63, g = l / TM, q = l % TM;
   const int rb = blockIdx.x % a.n_rb;
   const int sp = blockIdx.x / a.n_rb;
   const int64_t row0 = (int64_t)rb * BM;
   const int64_t jb = (int64_t)sp * a.split_cols;
   const int64_t je = min(a.M, jb + a.split_cols);
-  const T* __restrict__ Xp = static_cast<const T *>(a.X);
-  const T* __restrict__ Yp = static_cast<const T *>(a.Y);
+  const T *__restrict__ Xp = static_cast<const T *>(a.X);
+  const T *__restrict__ Yp = static_cast<const T *>(a.Y);
 
+  // ------------------------------------------------------------ row state
   int64_t qi[QB];
   bool qv[QB];
   T qr[QB][DG];
   T nx[QB];
   T er[QB], ep[QB];  // row epilogue: s <- er * s + ep
+  const bool has_epi = a.epi.n_stages == 1;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     qi[b] = row0 + (int64_t)(w * QB + b) * TM + q;
@@ -188,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void mfma_tile(const TileArgs a) {
     }
     nx[b] = F::gsum(part);
     T r = (T)1, p = (T)0;
-    if (a.epi.n_stages == 1) {
+    if (has_epi) {
       const Stage &st = a.epi.st[0];
       if (st.row_vec) {
         if (qv[b]) {
@@ -227,8 +269,150 @@ __global__ __launch_bounds__(256, 2) void mfma_tile(const TileArgs a) {
       list[b][p] = (p < KLQ - a.k) ? key_placeholder(Key<T>()) : Key<T>::sentinel();
   }
 
+  // ----------------------------------------------------------- sub-blocks
+  // S^T for the TM keys at offset kb of the staged tile, all QB query blocks.
+  auto qk = [&](int kb, acc_t (&s)[QB]) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int r = 0; r < NREG; ++r) s[b][r] = DIST ? nx[b] + sN[kb + F::key_of(r, g)] : (T)0;
+#pragma unroll
+    for (int st = 0; st < DG; ++st) {
+      const T av = sK[kb + q][g * DG + st];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) s[b] = F::mma(av, qr[b][st], s[b]);
+    }
+  };
+
+  // Fold one sub-block of scores into the row reductions.
+  auto consume = [&](int kb, int nb, int64_t j0, bool diag, acc_t (&s)[QB]) {
+    const bool tail = kb + TM > nb;
+    if constexpr (CONS == C_TOPK) {
+      // Cheap filter first, one wave vote for the whole sub-block. For a
+      // plain smallest-distance search the clamp at 0 is deferred to the
+      // candidates: max(x, 0) < thr implies x < thr, so the raw value is a
+      // safe filter and the exact value is recomputed before insertion.
+      const bool defer = METRIC == M_SQEUCLIDEAN && !has_epi && !a.largest;
+      bool any = false;
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          T x = s[b][r];
+          if constexpr (DIST) {
+            if (!defer) x = max(x, (T)0);
+          }
+          if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
+          if (has_epi) x = fma(x, er[b], ep[b]);
+          s[b][r] = x;
+          const T sv = a.largest ? -x : x;
+          any |= sv < thr[b];
+        }
+      if (__any(any)) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            const int key = kb + F::key_of(r, g);
+            T x = s[b][r];
+            if (defer) x = max(x, (T)0);
+            const T sv = a.largest ? -x : x;
+            if (key < nb && sv < thr[b]) {
+              key_insert<T, KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), a.largest));
+              thr[b] = key_threshold(list[b][KLQ - 1]);
+            }
+          }
+      }
+      return;
+    }
+
+    // Finished score per register (base 2 for the online consumers).
+    T v[QB][NREG];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+#pragma unroll
+      for (int r = 0; r < NREG; ++r) {
+        T x = s[b][r];
+        if constexpr (DIST) x = max(x, (T)0);
+        if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
+        if constexpr (ONLINE) x = x * er[b];
+        v[b][r] = x;
+      }
+      if constexpr (!ONLINE) {
+        if (has_epi) {
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) v[b][r] = fma(v[b][r], er[b], ep[b]);
+        }
+      }
+      if (tail) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r)
+          if (kb + F::key_of(r, g) >= nb) v[b][r] = ONLINE ? kNegInf : (T)0;
+      }
+      if (CONS == C_LOGSUMEXP && diag) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r)
+          if (j0 + kb + F::key_of(r, g) == qi[b]) v[b][r] = kNegInf;
+      }
+    }
+
+    if constexpr (ONLINE) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        T bm = v[b][0];
+#pragma unroll
+        for (int r = 1; r < NREG; ++r) bm = max(bm, v[b][r]);
+        bm = F::gmax(bm);
+        const T mn = max(m[b], bm);
+        const bool live = mn != kNegInf;
+        const T alpha = live ? ex2(m[b] - mn) : (T)1;
+        T acc = 0;
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          const T p = live ? ex2(v[b][r] - mn) : (T)0;
+          v[b][r] = p;
+          acc += p;
+        }
+        lsum[b] = fma(lsum[b], alpha, acc);
+        m[b] = mn;
+        if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+          for (int c = 0; c < NCB; ++c) o[b][c] *= alpha;
+        }
+      }
+    }
+
+    if constexpr (PV) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          const int key = kb + F::key_of(r, g);
+          T av;
+          if constexpr (HAS_V) {
+            av = sV[key][c * TM + q];
+          } else {
+            const int ch = c * TM + q;
+            av = ch < DP ? sK[key][ch] : (T)0;
+          }
+#pragma unroll
+          for (int b = 0; b < QB; ++b) o[b][c] = F::mma(av, v[b][r], o[b][c]);
+        }
+      }
+      if constexpr (CONS == C_DISPLACEMENT) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) mass[b] += v[b][r];
+      }
+    }
+  };
+
+  // ------------------------------------------------------------ main loop
   // Register-prefetched tiles: the global reads of tile t+1 are in flight
-  // while tile t is computed from LDS.
+  // while tile t is computed from LDS. Within a tile the scores of
+  // sub-block sb+1 are issued to the matrix cores before sub-block sb is
+  // consumed, so its vector work overlaps them.
   TileLoader<T, BN, DP> ldK;
   TileLoader<T, BN, HAS_V ? CP : 16 / (int)sizeof(T)> ldV;
   T nyv = 0;
@@ -254,117 +438,18 @@ __global__ __launch_bounds__(256, 2) void mfma_tile(const TileArgs a) {
     if (j0 + BN < je) prefetch(j0 + BN);
     const bool diag = CONS == C_LOGSUMEXP && a.exclude_self && j0 < row0 + BM && j0 + BN > row0;
 
+    acc_t s0[QB], s1[QB];
+    qk(0, s0);
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
-      const int kb = sb * TM;
-      if (kb >= nb) break;
-      const bool tail = kb + TM > nb;
-      acc_t s[QB];
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int r = 0; r < NREG; ++r) s[b][r] = DIST ? nx[b] + sN[kb + F::key_of(r, g)] : (T)0;
-#pragma unroll
-      for (int st = 0; st < DG; ++st) {
-        const T av = sK[kb + q][g * DG + st];
-#pragma unroll
-        for (int b = 0; b < QB; ++b) s[b] = F::mma(av, qr[b][st], s[b]);
-      }
-
-      // Epilogue: finished score per register (base 2 for the online consumers).
-      T v[QB][NREG];
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-#pragma unroll
-        for (int r = 0; r < NREG; ++r) {
-          T x = s[b][r];
-          if constexpr (DIST) x = max(x, (T)0);
-          if constexpr (METRIC == M_RBF) x = F::exp2(x * ngl2);
-          if constexpr (ONLINE) {
-            x = x * er[b];
-          } else {
-            x = fma(x, er[b], ep[b]);
-          }
-          v[b][r] = x;
-        }
-        if (tail) {
-#pragma unroll
-          for (int r = 0; r < NREG; ++r)
-            if (kb + F::key_of(r, g) >= nb) v[b][r] = ONLINE ? kNegInf : (T)0;
-        }
-        if (CONS == C_LOGSUMEXP && diag) {
-#pragma unroll
-          for (int r = 0; r < NREG; ++r)
-            if (j0 + kb + F::key_of(r, g) == qi[b]) v[b][r] = kNegInf;
-        }
-      }
-
-      if constexpr (ONLINE) {
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-          T bm = v[b][0];
-#pragma unroll
-          for (int r = 1; r < NREG; ++r) bm = max(bm, v[b][r]);
-          bm = F::gmax(bm);
-          const T mn = max(m[b], bm);
-          const bool live = mn != kNegInf;
-          const T alpha = live ? F::exp2(m[b] - mn) : (T)1;
-          T acc = 0;
-#pragma unroll
-          for (int r = 0; r < NREG; ++r) {
-            const T p = live ? F::exp2(v[b][r] - mn) : (T)0;
-            v[b][r] = p;
-            acc += p;
-          }
-          lsum[b] = fma(lsum[b], alpha, acc);
-          m[b] = mn;
-          if constexpr (CONS == C_SOFTMAX) {
-#pragma unroll
-            for (int c = 0; c < NCB; ++c) o[b][c] *= alpha;
-          }
-        }
-      }
-
-      if constexpr (PV) {
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-#pragma unroll
-          for (int r = 0; r < NREG; ++r) {
-            const int key = kb + F::key_of(r, g);
-            T av;
-            if constexpr (HAS_V) {
-              av = sV[key][c * TM + q];
-            } else {
-              const int ch = c * TM + q;
-              av = ch < DP ? sK[key][ch] : (T)0;
-            }
-#pragma unroll
-            for (int b = 0; b < QB; ++b) o[b][c] = F::mma(av, v[b][r], o[b][c]);
-          }
-        }
-        if constexpr (CONS == C_DISPLACEMENT) {
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-#pragma unroll
-            for (int r = 0; r < NREG; ++r) mass[b] += v[b][r];
-        }
-      }
-
-      if constexpr (CONS == C_TOPK) {
-        // Filter on the value alone against the list's last real key (as a
-        // signed value, +inf while the list is not full).
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-#pragma unroll
-          for (int r = 0; r < NREG; ++r) {
-            const int key = kb + F::key_of(r, g);
-            const T sv = a.largest ? -v[b][r] : v[b][r];
-            if (key < nb && sv < thr[b]) {
-              key_insert<T, KLQ>(list[b], Key<T>::make(v[b][r], (uint32_t)(j0 + key), a.largest));
-              thr[b] = key_threshold(list[b][KLQ - 1]);
-            }
-          }
-        }
+      if (sb * TM >= nb) break;
+      const bool more = sb + 1 < SB && (sb + 1) * TM < nb;
+      if (sb & 1) {
+        if (more) qk((sb + 1) * TM, s0);
+        consume(sb * TM, nb, j0, diag, s1);
+      } else {
+        if (more) qk((sb + 1) * TM, s1);
+        consume(sb * TM, nb, j0, diag, s0);
       }
     }
   }

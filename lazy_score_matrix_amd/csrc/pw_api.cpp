@@ -188,7 +188,7 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   if (mfma_eligible(e, consumer, C)) {
     p.family = 1;
     p.bm = mfma_bm(e.dtype, consumer);
-    p.bn = kMfmaBN;
+    p.bn = mfma_bn(e.dtype, consumer);
     p.mcfg.dp = e.D <= 16 ? 16 : (e.D <= 32 ? 32 : 64);
     if (e.dtype == PW_F32) p.mcfg.cp = C <= 32 ? 32 : 64;
     else p.mcfg.cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
@@ -324,6 +324,13 @@ TileArgs base_args(const pw_expr &e, const Plan &p, char *base) {
   a.split_cols = p.split_cols;
   a.partial = p.n_part > 1 ? base + p.off_part : nullptr;
   a.ny = p.col_norms ? base + p.off_ny : nullptr;
+  // Taylor coefficients of e^(a f) - 1, a = ln2/256, for the double exp2.
+  const long double ak = logl(2.0L) / 256.0L;
+  long double c = 1.0L;
+  for (int k = 1; k <= 4; ++k) {
+    c *= ak / (long double)k;
+    a.exp2_c[k - 1] = (double)c;
+  }
   return a;
 }
 

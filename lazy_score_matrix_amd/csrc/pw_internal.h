@@ -94,6 +94,7 @@ struct TileArgs {
   void *partial;         // workspace partials when n_split > 1
   const void *nx;        // row norms (kernels using the norm expansion)
   const void *ny;        // column norms
+  double exp2_c[4];      // (ln2/256)^k / k!, k = 1..4, for the table-driven double exp2
   Epi epi;
 };
 
@@ -131,7 +132,11 @@ struct MfmaConfig {
   int kl;
 };
 constexpr int kMfmaWaves = 4;   // waves per workgroup
-constexpr int kMfmaBN = 64;     // keys per staged tile
+// Keys per staged tile: float 128 (4 sub-blocks of 32) except for the value
+// consumers, whose prefetched V tile needs the registers (64); double 64.
+constexpr int mfma_bn(int dtype, int consumer) {
+  return (dtype == 0 && consumer != C_MATMUL && consumer != C_SOFTMAX) ? 128 : 64;
+}
 // Query rows per workgroup: 4 waves x QB blocks x (32 float / 16 double)
 // queries; double uses QB = 2 except for top-k.
 constexpr int mfma_bm(int dtype, int consumer) { return dtype == 0 ? 128 : (consumer == C_TOPK ? 64 : 128); }

@@ -30,6 +30,12 @@ FLAGS = [
 ]
 
 
+# Device code: NaN scores are unsupported (include/pw.h), so kernels are built
+# without NaN semantics and without IEEE mode; min/max then need no operand
+# canonicalisation. Host validation (pw_api.cpp) keeps full NaN handling.
+KERNEL_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
@@ -41,12 +47,13 @@ def _headers_digest():
             if f.endswith(".h"):
                 with open(os.path.join(d, f), "rb") as fh:
                     h.update(f.encode() + fh.read())
-    h.update(" ".join(FLAGS).encode())
+    h.update(" ".join(FLAGS + KERNEL_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
 def _compile(src, obj, verbose):
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    cmd = [HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -43,8 +43,16 @@ struct Mfma<float> {
   __device__ __forceinline__ static acc_t mma(float a, float b, const acc_t &c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static float gmax(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
-  __device__ __forceinline__ static float gsum(float v) { return v + __shfl_xor(v, 32); }
+  // Lanes l and l^32 hold the same query: one cross-half lane swap leaves
+  // {v[l], v[l^32]} in the two result registers of every lane.
+  __device__ __forceinline__ static float gmax(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  __device__ __forceinline__ static float gsum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   __device__ __forceinline__ static float exp2(float x) { return __builtin_amdgcn_exp2f(x); }
   __device__ __forceinline__ static float log(float x) { return __builtin_amdgcn_logf(x) * kLn2_f; }
 };
@@ -57,13 +65,29 @@ struct Mfma<double> {
   __device__ __forceinline__ static acc_t mma(double a, double b, const acc_t &c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
   }
+  // Lanes l, l^16, l^32, l^48 hold the same query: two lane swaps (16 and
+  // 32 apart), each leaving {v[l], v[l^d]} in the two result registers.
+  template <int D>
+  __device__ __forceinline__ static void swap2(double v, double &a, double &b) {
+    const uint32_t lo = (uint32_t)__double_as_longlong(v), hi = (uint32_t)(__double_as_longlong(v) >> 32);
+    auto rl = D == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                      : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    auto rh = D == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                      : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    a = __longlong_as_double((long long)(((uint64_t)rh[0] << 32) | rl[0]));
+    b = __longlong_as_double((long long)(((uint64_t)rh[1] << 32) | rl[1]));
+  }
   __device__ __forceinline__ static double gmax(double v) {
-    v = fmax(v, __shfl_xor(v, 16));
-    return fmax(v, __shfl_xor(v, 32));
+    double a, b;
+    swap2<16>(v, a, b);
+    swap2<32>(fmax(a, b), a, b);
+    return fmax(a, b);
   }
   __device__ __forceinline__ static double gsum(double v) {
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
+    double a, b;
+    swap2<16>(v, a, b);
+    swap2<32>(a + b, a, b);
+    return a + b;
   }
   __device__ __forceinline__ static double exp2(double x) { return ::exp2(x); }
   __device__ __forceinline__ static double log(double x) { return ::log(x); }
@@ -103,7 +127,9 @@ __device__ __forceinline__ Key<double> key_placeholder(Key<double>) { return Key
 // Cooperative loader of a [ROWS, COLS] tile (COLS padded, zero beyond the
 // valid columns and rows) through registers: load() issues the global reads
 // for the next tile before the current one is computed, store() writes them
-// to LDS after it. Reads are 16-byte vectors when the source allows.
+// to LDS after it. A full, unpadded, 16-byte aligned tile takes the fast
+// path: one vector read per slot from a uniform tile base plus a per-thread
+// offset computed once. Other tiles read element by element with bounds.
 template <class T, int ROWS, int COLS>
 struct TileLoader {
   static constexpr int VEC = 16 / sizeof(T);
@@ -111,21 +137,35 @@ struct TileLoader {
   static constexpr int NV = (ROWS * VPR + 255) / 256;
   typedef T vec_t __attribute__((ext_vector_type(VEC)));
   vec_t buf[NV];
+  uint32_t off[NV];  // element offset of each slot inside a full tile
+  bool fast;         // offsets fit 32 bits and rows are vector aligned
 
+  __device__ __forceinline__ void init(int64_t ld, bool vec_ok, int tid) {
+    fast = vec_ok && (int64_t)ROWS * ld < (int64_t)1 << 31;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int idx = tid + v * 256;
+      off[v] = (uint32_t)((idx / VPR) * ld + (idx % VPR) * VEC);
+    }
+  }
   __device__ __forceinline__ void load(const T *__restrict__ src, int64_t ld, int64_t row0, int nrows, int ncols,
-                                       bool vec_ok, int tid) {
+                                       int tid) {
+    if (fast && nrows == ROWS && ncols == COLS) {
+      const T *__restrict__ base = src + row0 * ld;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if (ROWS * VPR % 256 == 0 || tid + v * 256 < ROWS * VPR)
+          buf[v] = *reinterpret_cast<const vec_t *>(base + off[v]);
+      return;
+    }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int idx = tid + v * 256;
       const int r = idx / VPR, c = (idx % VPR) * VEC;
       vec_t x;
-      if (idx < ROWS * VPR && r < nrows && vec_ok && c + VEC <= ncols) {
-        x = *reinterpret_cast<const vec_t *>(src + (row0 + r) * ld + c);
-      } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          x[e] = (idx < ROWS * VPR && r < nrows && c + e < ncols) ? src[(row0 + r) * ld + c + e] : (T)0;
-      }
+      for (int e = 0; e < VEC; ++e)
+        x[e] = (idx < ROWS * VPR && r < nrows && c + e < ncols) ? src[(row0 + r) * ld + c + e] : (T)0;
       buf[v] = x;
     }
   }
@@ -134,7 +174,7 @@ struct TileLoader {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int idx = tid + v * 256;
-      if (idx < ROWS * VPR) {
+      if (ROWS * VPR % 256 == 0 || idx < ROWS * VPR) {
         const int r = idx / VPR, c = (idx % VPR) * VEC;
         *reinterpret_cast<vec_t *>(&dst[r][c]) = buf[v];
       }
@@ -245,6 +285,13 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
     if constexpr (ONLINE) r *= (T)kLog2e;  // base-2 scores
     er[b] = r;
     ep[b] = p;
+    // Online consumers of a dot product: fold the row scale into the query
+    // operand, so the matrix cores return the base-2 score directly.
+    if constexpr (ONLINE && !DIST) {
+#pragma unroll
+      for (int s = 0; s < DG; ++s) qr[b][s] *= r;
+      er[b] = (T)1;
+    }
   }
   const T ngl2 = (T)(-a.gamma * kLog2e);
 
@@ -288,26 +335,36 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
   auto consume = [&](int kb, int nb, int64_t j0, bool diag, acc_t (&s)[QB]) {
     const bool tail = kb + TM > nb;
     if constexpr (CONS == C_TOPK) {
-      // Cheap filter first, one wave vote for the whole sub-block. For a
-      // plain smallest-distance search the clamp at 0 is deferred to the
-      // candidates: max(x, 0) < thr implies x < thr, so the raw value is a
-      // safe filter and the exact value is recomputed before insertion.
-      const bool defer = METRIC == M_SQEUCLIDEAN && !has_epi && !a.largest;
+      // Filter a whole sub-block with one wave vote before any insertion.
+      // Plain searches (no epilogue, smallest first, dot product or squared
+      // distance) filter on the raw accumulator: for distances the clamp at
+      // 0 is deferred to the candidates, as max(x, 0) < thr implies x < thr.
+      const bool plain = METRIC != M_RBF && !has_epi && !a.largest;
       bool any = false;
+      if (plain) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
+        for (int b = 0; b < QB; ++b) {
+          T mn = s[b][0];
 #pragma unroll
-        for (int r = 0; r < NREG; ++r) {
-          T x = s[b][r];
-          if constexpr (DIST) {
-            if (!defer) x = max(x, (T)0);
-          }
-          if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
-          if (has_epi) x = fma(x, er[b], ep[b]);
-          s[b][r] = x;
-          const T sv = a.largest ? -x : x;
-          any |= sv < thr[b];
+          for (int r = 1; r < NREG; ++r) mn = min(mn, s[b][r]);
+          any |= mn < thr[b];
         }
+      } else {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          T mn = __builtin_huge_valf();
+#pragma unroll
+          for (int r = 0; r < NREG; ++r) {
+            T x = s[b][r];
+            if constexpr (DIST) x = max(x, (T)0);
+            if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
+            x = fma(x, er[b], ep[b]);
+            s[b][r] = x;
+            mn = min(mn, a.largest ? -x : x);
+          }
+          any |= mn < thr[b];
+        }
+      }
       if (__any(any)) {
 #pragma unroll
         for (int b = 0; b < QB; ++b)
@@ -315,7 +372,7 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
           for (int r = 0; r < NREG; ++r) {
             const int key = kb + F::key_of(r, g);
             T x = s[b][r];
-            if (defer) x = max(x, (T)0);
+            if (DIST && plain) x = max(x, (T)0);
             const T sv = a.largest ? -x : x;
             if (key < nb && sv < thr[b]) {
               key_insert<T, KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), a.largest));
@@ -335,7 +392,7 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
         T x = s[b][r];
         if constexpr (DIST) x = max(x, (T)0);
         if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
-        if constexpr (ONLINE) x = x * er[b];
+        if constexpr (ONLINE && DIST) x = x * er[b];
         v[b][r] = x;
       }
       if constexpr (!ONLINE) {
@@ -357,28 +414,45 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
     }
 
     if constexpr (ONLINE) {
+      // Online max/sum in base 2 with a lazily moved reference m: it only
+      // moves when a block's maximum exceeds it by more than 8, so every
+      // weight 2^(v - m) stays <= 256 and most blocks skip the rescale of
+      // the running sums. The result divides by the sum taken with the same
+      // reference, so the reference's value never enters it.
+      bool need_any = false;
+      T bmax[QB];
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
         T bm = v[b][0];
 #pragma unroll
         for (int r = 1; r < NREG; ++r) bm = max(bm, v[b][r]);
-        bm = F::gmax(bm);
-        const T mn = max(m[b], bm);
-        const bool live = mn != kNegInf;
-        const T alpha = live ? ex2(m[b] - mn) : (T)1;
+        bmax[b] = F::gmax(bm);
+        need_any |= bmax[b] > m[b] + (T)8;
+      }
+      if (__any(need_any)) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          const bool need = bmax[b] > m[b] + (T)8;
+          const T alpha = need ? ex2(m[b] - bmax[b]) : (T)1;
+          m[b] = need ? bmax[b] : m[b];
+          lsum[b] *= alpha;
+          if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) o[b][c] *= alpha;
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const T mu = m[b] == kNegInf ? (T)0 : m[b];  // no valid key yet: weights are 2^-inf = 0
         T acc = 0;
 #pragma unroll
         for (int r = 0; r < NREG; ++r) {
-          const T p = live ? ex2(v[b][r] - mn) : (T)0;
+          const T p = ex2(v[b][r] - mu);
           v[b][r] = p;
           acc += p;
         }
-        lsum[b] = fma(lsum[b], alpha, acc);
-        m[b] = mn;
-        if constexpr (CONS == C_SOFTMAX) {
-#pragma unroll
-          for (int c = 0; c < NCB; ++c) o[b][c] *= alpha;
-        }
+        lsum[b] += acc;
       }
     }
 
@@ -418,10 +492,12 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
   T nyv = 0;
   const bool kvec = vec_ok(a.Y, a.ldy, 16 / (int)sizeof(T));
   const bool vvec = HAS_V && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
+  ldK.init(a.ldy, kvec, tid);
+  if constexpr (HAS_V) ldV.init(a.ldv, vvec, tid);
   auto prefetch = [&](int64_t t0) {
     const int nbt = (int)min((int64_t)BN, je - t0);
-    ldK.load(Yp, a.ldy, t0, nbt, a.D, kvec, tid);
-    if constexpr (HAS_V) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, vvec, tid);
+    ldK.load(Yp, a.ldy, t0, nbt, a.D, tid);
+    if constexpr (HAS_V) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
     if constexpr (DIST) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
   };
   if (jb < je) prefetch(jb);

@@ -130,11 +130,11 @@ __device__ __forceinline__ Key<double> key_placeholder(Key<double>) { return Key
 // to LDS after it. A full, unpadded, 16-byte aligned tile takes the fast
 // path: one vector read per slot from a uniform tile base plus a per-thread
 // offset computed once. Other tiles read element by element with bounds.
-template <class T, int ROWS, int COLS>
+template <class T, int ROWS, int COLS, int NT>
 struct TileLoader {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int VPR = COLS / VEC;  // vectors per row
-  static constexpr int NV = (ROWS * VPR + 255) / 256;
+  static constexpr int NV = (ROWS * VPR + NT - 1) / NT;
   typedef T vec_t __attribute__((ext_vector_type(VEC)));
   vec_t buf[NV];
   uint32_t off[NV];  // element offset of each slot inside a full tile
@@ -144,7 +144,7 @@ struct TileLoader {
     fast = vec_ok && (int64_t)ROWS * ld < (int64_t)1 << 31;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int idx = tid + v * 256;
+      const int idx = tid + v * NT;
       off[v] = (uint32_t)((idx / VPR) * ld + (idx % VPR) * VEC);
     }
   }
@@ -154,13 +154,13 @@ struct TileLoader {
       const T *__restrict__ base = src + row0 * ld;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
-        if (ROWS * VPR % 256 == 0 || tid + v * 256 < ROWS * VPR)
+        if (ROWS * VPR % NT == 0 || tid + v * NT < ROWS * VPR)
           buf[v] = *reinterpret_cast<const vec_t *>(base + off[v]);
       return;
     }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int idx = tid + v * 256;
+      const int idx = tid + v * NT;
       const int r = idx / VPR, c = (idx % VPR) * VEC;
       vec_t x;
 #pragma unroll
@@ -173,8 +173,8 @@ struct TileLoader {
   __device__ __forceinline__ void store(T (*dst)[LD], int tid) const {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int idx = tid + v * 256;
-      if (ROWS * VPR % 256 == 0 || idx < ROWS * VPR) {
+      const int idx = tid + v * NT;
+      if (ROWS * VPR % NT == 0 || idx < ROWS * VPR) {
         const int r = idx / VPR, c = (idx % VPR) * VEC;
         *reinterpret_cast<vec_t *>(&dst[r][c]) = buf[v];
       }
@@ -186,28 +186,26 @@ __device__ __forceinline__ bool vec_ok(const void *p, int64_t ld, int vec) {
   return ((uintptr_t)p % 16 == 0) && (ld % vec == 0);
 }
 
-template <class T, int CONS>
+template <class T, int CONS, int DP, int CP, int KL>
 struct MfmaShape {
+  static constexpr int DT = sizeof(T) == 4 ? 0 : 1;
+  static constexpr int WAVES = mfma_waves(DT, DP, CP, KL);
+  static constexpr int NT = WAVES * 64;
   static constexpr int QB = (sizeof(T) == 8 && CONS != C_TOPK) ? 2 : 1;
-  static constexpr int BM = kMfmaWaves * QB * Mfma<T>::TM;
-  static_assert(BM == mfma_bm(sizeof(T) == 4 ? 0 : 1, CONS), "host and device row-block sizes differ");
-};
-
-// Workgroups per CU the register budget is sized for: two (256 registers per
-// lane) for the common shapes, one (512) for 64-slot top-k lists and for
-// double precision with wide feature or value tiles.
-template <class T, int DP, int CP, int KL>
-struct MfmaOcc {
-  static constexpr int value = (KL > 16 || (sizeof(T) == 8 && (DP > 16 || CP > 16))) ? 1 : 2;
+  static constexpr int BM = WAVES * QB * Mfma<T>::TM;
+  static_assert(BM == mfma_bm(DT, CONS, DP, CP, KL), "host and device row-block sizes differ");
 };
 
 template <class T, int METRIC, int CONS, int DP, int CP, int KL>
-__global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_tile(const TileArgs a) {
+__global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
+                             (mfma_wgs_per_cu(sizeof(T) == 4 ? 0 : 1, DP, CP, KL))) void mfma_tile(const TileArgs a) {
   using F = Mfma<T>;
   using acc_t = typename F::acc_t;
   constexpr int TM = F::TM, G = F::G, NREG = F::NREG;
-  constexpr int QB = MfmaShape<T, CONS>::QB;
-  constexpr int BM = MfmaShape<T, CONS>::BM;
+  using Shape = MfmaShape<T, CONS, DP, CP, KL>;
+  constexpr int QB = Shape::QB;
+  constexpr int BM = Shape::BM;
+  constexpr int NT = Shape::NT;
   constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS);
   constexpr int SB = BN / TM;
   constexpr int DG = DP / G;
@@ -221,9 +219,14 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
   constexpr int KLQ = CONS == C_TOPK ? KL : 1;
   constexpr T kNegInf = -__builtin_huge_valf();
 
-  __shared__ __attribute__((aligned(16))) T sK[BN][DP + KPAD];
-  __shared__ __attribute__((aligned(16))) T sN[BN];
-  __shared__ __attribute__((aligned(16))) T sV[HAS_V ? BN : 1][VW];
+  // Two LDS buffers per tile array: tile t+1 is written into one while
+  // tile t is read from the other, so each tile costs a single barrier.
+  __shared__ __attribute__((aligned(16))) T sKb[2][BN][DP + KPAD];
+  __shared__ __attribute__((aligned(16))) T sNb[2][BN];
+  __shared__ __attribute__((aligned(16))) T sVb[2][HAS_V ? BN : 1][VW];
+  T(*sK)[DP + KPAD] = sKb[0];
+  T *sN = sNb[0];
+  T(*sV)[VW] = sVb[0];
   constexpr bool TABLE_EXP = sizeof(T) == 8 && (ONLINE || METRIC == M_RBF);
   __shared__ double sE[TABLE_EXP ? 256 : 1];
 
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
 #pragma unroll
   for (int k = 0; k < 4; ++k) ec[k] = a.exp2_c[k];
   if constexpr (TABLE_EXP) {
-    for (int j = tid; j < 256; j += 256) sE[j] = ::exp2((double)j / 256.0);
+    for (int j = tid; j < 256; j += NT) sE[j] = ::exp2((double)j / 256.0);
   }
   auto ex2 = [&](T x) -> T {
     if constexpr (TABLE_EXP) return exp2_table(x, sE, ec);
@@ -487,8 +490,8 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
   // while tile t is computed from LDS. Within a tile the scores of
   // sub-block sb+1 are issued to the matrix cores before sub-block sb is
   // consumed, so its vector work overlaps them.
-  TileLoader<T, BN, DP> ldK;
-  TileLoader<T, BN, HAS_V ? CP : 16 / (int)sizeof(T)> ldV;
+  TileLoader<T, BN, DP, NT> ldK;
+  TileLoader<T, BN, HAS_V ? CP : 16 / (int)sizeof(T), NT> ldV;
   T nyv = 0;
   const bool kvec = vec_ok(a.Y, a.ldy, 16 / (int)sizeof(T));
   const bool vvec = HAS_V && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
@@ -500,18 +503,27 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
     if constexpr (HAS_V) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
     if constexpr (DIST) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
   };
-  if (jb < je) prefetch(jb);
+  auto stage = [&](int buf) {
+    ldK.store(sKb[buf], tid);
+    if constexpr (HAS_V) ldV.store(sVb[buf], tid);
+    if constexpr (DIST) {
+      if (tid < BN) sNb[buf][tid] = nyv;
+    }
+  };
+  int buf = 0;
+  if (jb < je) {
+    prefetch(jb);
+    stage(0);
+  }
+  __syncthreads();
 
   for (int64_t j0 = jb; j0 < je; j0 += BN) {
     const int nb = (int)min((int64_t)BN, je - j0);
-    __syncthreads();
-    ldK.store(sK, tid);
-    if constexpr (HAS_V) ldV.store(sV, tid);
-    if constexpr (DIST) {
-      if (tid < BN) sN[tid] = nyv;
-    }
-    __syncthreads();
-    if (j0 + BN < je) prefetch(j0 + BN);
+    const bool next = j0 + BN < je;
+    if (next) prefetch(j0 + BN);
+    sK = sKb[buf];
+    sN = sNb[buf];
+    sV = sVb[buf];
     const bool diag = CONS == C_LOGSUMEXP && a.exclude_self && j0 < row0 + BM && j0 + BN > row0;
 
     acc_t s0[QB], s1[QB];
@@ -528,6 +540,9 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
         consume(sb * TM, nb, j0, diag, s0);
       }
     }
+    if (next) stage(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
 
   // ---------------------------------------------------------------- finalize
@@ -607,7 +622,7 @@ __global__ __launch_bounds__(256, (MfmaOcc<T, DP, CP, KL>::value)) void mfma_til
 
 template <class T, int METRIC, int CONS, int DP, int CP, int KL>
 hipError_t launch_mfma_kernel(const TileArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(256);
+  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(MfmaShape<T, CONS, DP, CP, KL>::NT);
   hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL>), grid, block, 0, s, a);
   return hipGetLastError();
 }

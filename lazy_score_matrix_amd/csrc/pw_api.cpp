@@ -157,7 +157,7 @@ struct Plan {
   std::vector<size_t> stage_off;  // per stage: offset of its vectors
 };
 
-int valu_dtile(int64_t D) { return D <= 4 ? 4 : (D <= 16 ? 16 : 64); }
+int valu_dtile(int64_t D) { return D <= 3 ? 3 : (D <= 4 ? 4 : (D <= 16 ? 16 : 64)); }
 int valu_vtile(int64_t C) { return C <= 4 ? 4 : (C <= 16 ? 16 : 64); }
 
 // The MFMA engine takes D >= 16 (a real contraction), chains that reduce to
@@ -187,15 +187,17 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   int64_t target_wgs = kTargetWGs;
   if (mfma_eligible(e, consumer, C)) {
     p.family = 1;
-    p.bm = mfma_bm(e.dtype, consumer);
-    p.bn = mfma_bn(e.dtype, consumer);
     p.mcfg.dp = e.D <= 16 ? 16 : (e.D <= 32 ? 32 : 64);
-    if (e.dtype == PW_F32) p.mcfg.cp = C <= 32 ? 32 : 64;
+    const bool value = consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL;
+    if (!value) p.mcfg.cp = 1;
+    else if (e.dtype == PW_F32) p.mcfg.cp = C <= 32 ? 32 : 64;
     else p.mcfg.cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
-    p.mcfg.kl = k <= 16 ? 16 : 64;
+    p.mcfg.kl = consumer == PW_C_TOPK ? (k <= 16 ? 16 : 64) : 1;
+    p.bm = mfma_bm(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
+    p.bn = mfma_bn(e.dtype, consumer);
     p.chunk = (int)std::min<int64_t>(C, p.mcfg.cp);
     p.col_norms = e.metric != PW_LINEAR;
-    target_wgs = 2 * kTargetCUs;
+    target_wgs = (int64_t)kTargetCUs * mfma_wgs_per_cu(e.dtype, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
   } else {
     p.vcfg.dtile = valu_dtile(e.D);
     if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {

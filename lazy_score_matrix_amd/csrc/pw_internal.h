@@ -112,7 +112,7 @@ struct TopkKeyBytes<double> { static constexpr int value = 16; };
 // Launchers (defined in the .hip files). All return hipError_t of the launch.
 // ---------------------------------------------------------------------------
 // Generic VALU tile engine: any D <= 64, any metric, consumer and op chain.
-//   dtile: feature tile 4 / 16 / 64 (D zero-padded up to it)
+//   dtile: feature tile 3 / 4 / 16 / 64 (D zero-padded up to it)
 //   vtile: value tile 4 / 16 / 64 (matmul, softmax), top-k list 16 / 64, else 0
 struct ValuConfig {
   int dtile;
@@ -131,15 +131,24 @@ struct MfmaConfig {
   int cp;
   int kl;
 };
-constexpr int kMfmaWaves = 4;   // waves per workgroup
+// Wide variants (64-slot top-k lists; double with a feature or value tile
+// above 16) need the whole 512-register budget: one 4-wave workgroup per CU,
+// one wave per SIMD. The others run two 4-wave workgroups per CU (two waves
+// per SIMD, 256 registers each). Measured on gfx950, sharing each staged
+// tile among 8 waves instead did not pay.
+constexpr bool mfma_wide(int dtype, int dp, int cp, int kl) { return kl > 16 || (dtype == 1 && (dp > 16 || cp > 16)); }
+constexpr int mfma_waves(int, int, int, int) { return 4; }
+constexpr int mfma_wgs_per_cu(int dtype, int dp, int cp, int kl) { return mfma_wide(dtype, dp, cp, kl) ? 1 : 2; }
+// Query rows per workgroup: waves x QB blocks x (32 float / 16 double)
+// queries; double uses QB = 2 except for top-k.
+constexpr int mfma_bm(int dtype, int consumer, int dp, int cp, int kl) {
+  return mfma_waves(dtype, dp, cp, kl) * ((dtype == 1 && consumer != C_TOPK) ? 2 : 1) * (dtype == 0 ? 32 : 16);
+}
 // Keys per staged tile: float 128 (4 sub-blocks of 32) except for the value
 // consumers, whose prefetched V tile needs the registers (64); double 64.
 constexpr int mfma_bn(int dtype, int consumer) {
   return (dtype == 0 && consumer != C_MATMUL && consumer != C_SOFTMAX) ? 128 : 64;
 }
-// Query rows per workgroup: 4 waves x QB blocks x (32 float / 16 double)
-// queries; double uses QB = 2 except for top-k.
-constexpr int mfma_bm(int dtype, int consumer) { return dtype == 0 ? 128 : (consumer == C_TOPK ? 64 : 128); }
 // Lane groups per query in the MFMA layouts (float 2, double 4); each keeps
 // its own top-k list, written as a separate partial.
 constexpr int mfma_groups(int dtype) { return dtype == 0 ? 2 : 4; }

@@ -20,6 +20,8 @@
 
 namespace pw {
 
+// neg_gamma = -gamma for double (device exp); -gamma * log2(e) for float
+// (the hardware base-2 exponential).
 template <int METRIC, class T, int DT>
 __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gamma) {
   if constexpr (METRIC == M_LINEAR) {
@@ -42,7 +44,10 @@ __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gam
       }
     }
     T d2 = s0 + s1;
-    if constexpr (METRIC == M_RBF) return dexp(neg_gamma * d2);
+    if constexpr (METRIC == M_RBF) {
+      if constexpr (sizeof(T) == 4) return __builtin_amdgcn_exp2f(neg_gamma * d2);
+      else return dexp(neg_gamma * d2);
+    }
     return d2;
   }
 }
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   for (int d = 0; d < DT; ++d) x[d] = (rv && d < a.D) ? ldg<T>(a.X, i * a.ldx + d) : (T)0;
   RowEpi<T> re;
   load_row_epi<T>(a.epi, i, rv, re);
-  const T neg_gamma = (T)(-a.gamma);
+  const T neg_gamma = sizeof(T) == 4 ? (T)(-a.gamma * kLog2e) : (T)(-a.gamma);
 
   T acc[ACCN];
 #pragma unroll
@@ -149,9 +154,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
         }
       }
     } else {
-      for (int jj = 0; jj < nb; ++jj) {
-        T s = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
-        s = apply_epi<T, BN>(a.epi, re, s, sQ, sO, jj);
+      auto fold = [&](int jj, T s) {
         if constexpr (CONS == C_MATMUL) {
 #pragma unroll
           for (int c = 0; c < ACCN; ++c) acc[c] = fma(s, sV[jj][c], acc[c]);
@@ -162,6 +165,14 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
         } else if constexpr (CONS == C_TOPK) {
           key_insert<T, KL>(list, Key<T>::make(s, (uint32_t)(j0 + jj), a.largest));
         }
+      };
+      // The stage loop runs only when the expression has score arithmetic;
+      // a bare metric takes a loop without it (a uniform branch).
+      if (a.epi.n_stages == 0) {
+        for (int jj = 0; jj < nb; ++jj) fold(jj, valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma));
+      } else {
+        for (int jj = 0; jj < nb; ++jj)
+          fold(jj, apply_epi<T, BN>(a.epi, re, valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma), sQ, sO, jj));
       }
     }
   }
@@ -257,6 +268,7 @@ hipError_t valu_by_consumer(int consumer, int vt, const TileArgs &a, hipStream_t
 template <class T, int METRIC>
 hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s) {
   switch (cfg.dtile) {
+    case 3: return valu_by_consumer<T, METRIC, 3>(consumer, cfg.vtile, a, s);
     case 4: return valu_by_consumer<T, METRIC, 4>(consumer, cfg.vtile, a, s);
     case 16: return valu_by_consumer<T, METRIC, 16>(consumer, cfg.vtile, a, s);
     case 64: return valu_by_consumer<T, METRIC, 64>(consumer, cfg.vtile, a, s);

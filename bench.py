@@ -96,7 +96,31 @@ def flops_per_pair(case, D, C):
         return body + 4 + 2 * C
     if case.consumer == "topk":
         return body + 1
+    if case.consumer == "mean":
+        return body + 1 + 2  # the 1/M scale, then a product with a ones column
     raise ValueError(case.consumer)
+
+
+SWAP = {"add_rows": "add_columns", "add_columns": "add_rows", "weight_rows": "weight_columns",
+        "weight_columns": "weight_rows"}
+
+
+def lib_consumer(c):
+    """The library call behind a case (a mean is a product with ones)."""
+    return "matmul" if c.consumer == "mean" else c.consumer
+
+
+def case_operands(c, arrays):
+    """(X, Y, ops) of a case; a transposed case reduces over the rows, so it
+    binds (Y, X) with row and column ops swapped."""
+    X, Y = arrays[c.x], arrays[c.y]
+    ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+    if c.transpose:
+        X, Y = Y, X
+        ops = [(SWAP.get(n, n), a) for n, a in ops]
+    if c.consumer == "mean":
+        ops = ops + [("mul", 1.0 / Y.shape[0])]
+    return X, Y, ops
 
 
 def main():
@@ -129,14 +153,20 @@ def main():
     calls = []  # (case, expr, run_fn, outputs)
     pairs_per_step = 0
     for c in cases:
-        X = t[c.x]
-        Y = X if c.y == c.x else t[c.y]
-        ops = [(n, t[a] if isinstance(a, str) else a) for n, a in c.ops]
+        X, Y, ops = case_operands(c, t)
         e = pw.lazy(X, Y, c.metric, gamma=c.gamma, ops=ops)
         N, D = X.shape
         M = Y.shape[0]
-        C = t[c.v].shape[1] if c.v else 0
-        if c.consumer in ("matmul", "softmax_matmul"):
+        C = t[c.v].shape[1] if c.v else (1 if c.consumer == "mean" else 0)
+        if c.consumer == "mean":
+            # The row mean: the scores scaled by 1/M (an extra op bound
+            # above) times a ones column, as LazyScores.mean computes it.
+            ones = torch.ones(M, 1, dtype=X.dtype, device=dev)
+            out = torch.empty(N, 1, dtype=X.dtype, device=dev)
+            ws = e.workspace("matmul", 1)
+            fn = (lambda e=e, V=ones, out=out, ws=ws: e.matmul(V, out=out, workspace=ws))
+            outs = (out,)
+        elif c.consumer in ("matmul", "softmax_matmul"):
             out = torch.empty(N, C, dtype=X.dtype, device=dev)
             ws = e.workspace(c.consumer, C)
             V = t[c.v]
@@ -206,13 +236,15 @@ def main():
             hip.hipEventDestroy(b_)
 
     dtype = "f32" if calls[0][1].dtype == torch.float32 else "f64"
-    contraction = calls[0][1].D >= 16
+    dom0 = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
+    c_, e_, _, _, C_ = calls[dom0]
+    contraction = e_.plan(lib_consumer(c_), C_, c_.k).startswith("family=mfma")
     peak = PEAK_TFLOPS[dtype] if contraction else ALU_PEAK_TFLOPS[dtype]
     kernels = []
     for (c, e, _, _, C), kms in zip(calls, kernel_ms):
         fl = float(e.N) * e.M * flops_per_pair(c, e.D, C)
         tf = fl / (kms * 1e-3) / 1e12
-        kernels.append({"call": c.name, "plan": e.plan(c.consumer, C, c.k), "avg_ms": round(kms, 4),
+        kernels.append({"call": c.name, "plan": e.plan(lib_consumer(c), C, c.k), "avg_ms": round(kms, 4),
                         "flops_per_pair": flops_per_pair(c, e.D, C), "tflops": round(tf, 3),
                         "frac": round(tf / peak, 4)})
     dom = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
@@ -270,12 +302,12 @@ def cpu_leg(calls, arrays, seconds):
     total_pairs, total_s, rows_desc, parity = 0, 0.0, [], []
     budget = seconds / len(calls)
     for c, e, _, outs, C in calls:
-        ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
-        oe = oracle.Expr(arrays[c.x], arrays[c.y], c.metric, gamma=c.gamma, ops=ops)
-        V = arrays[c.v] if c.v else None
+        X, Y, ops = case_operands(c, arrays)
+        oe = oracle.Expr(X, Y, c.metric, gamma=c.gamma, ops=ops)
+        V = arrays[c.v] if c.v else (np.ones((Y.shape[0], 1), dtype=Y.dtype) if c.consumer == "mean" else None)
 
         def run(rows):
-            if c.consumer == "matmul":
+            if c.consumer in ("matmul", "mean"):
                 return oracle.matmul(oe, V, rows)
             if c.consumer == "softmax_matmul":
                 return oracle.softmax_matmul(oe, V, rows)

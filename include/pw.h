@@ -51,11 +51,14 @@ typedef enum {
 
 typedef enum { PW_F32 = 0, PW_F64 = 1 } pw_dtype;
 
-/* Built-in metrics (guide, Task Map; rbf form from the SVGD section):
+/* Built-in metrics (guide, Task Map; rbf form from the SVGD section; cosine
+ * from the Custom Comparisons / Encoded Feature Reuse page, "Prepare Once,
+ * Use Several Consumers"):
  *   PW_LINEAR       f = sum_d x_d y_d
  *   PW_SQEUCLIDEAN  f = sum_d (x_d - y_d)^2      (squared, no root)
- *   PW_RBF          f = exp(-gamma * sum_d (x_d - y_d)^2), gamma >= 0 */
-typedef enum { PW_LINEAR = 0, PW_SQEUCLIDEAN = 1, PW_RBF = 2 } pw_metric;
+ *   PW_RBF          f = exp(-gamma * sum_d (x_d - y_d)^2), gamma >= 0
+ *   PW_COSINE       f = 1 - x.y / (|x| |y|), and 1 when x or y is zero */
+typedef enum { PW_LINEAR = 0, PW_SQEUCLIDEAN = 1, PW_RBF = 2, PW_COSINE = 3 } pw_metric;
 
 /* Score arithmetic applied to f left to right, in the order given
  * (guide, "Score Expressions": scalar arithmetic, add_rows, add_columns,

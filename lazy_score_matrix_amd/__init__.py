@@ -28,7 +28,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "pw.h")
 
 PW_OK, PW_ERR_INVALID, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP = 0, -1, -2, -3, -4
 DTYPES = {torch.float32: 0, torch.float64: 1}
-METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2}
+METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2, "cosine_distances": 3, "cosine": 3}
 OPS = {"mul": 0, "add": 1, "add_rows": 2, "add_columns": 3, "weight_rows": 4, "weight_columns": 5, "exp": 6}
 CONSUMERS = {"matmul": 0, "displacement": 1, "logsumexp": 2, "softmax_matmul": 3, "topk": 4}
 MAX_OPS, MAX_D, MAX_K = 8, 64, 64
@@ -235,13 +235,50 @@ class LazyScores:
                                 ws.data_ptr(), nb, _stream(self.device)), "pw_topk")
         return values, indices
 
-    def min(self):
-        """Row minimum and its (lowest) index: top-k with k = 1."""
+    # -- views and derived reductions ----------------------------------
+    @property
+    def T(self) -> "LazyScores":
+        """The transposed score S^T[j, i] = S[i, j] (Y and X swapped, row and
+        column ops swapped; every built-in metric is symmetric). Column
+        reductions such as min(-2) are row reductions of this view."""
+        swap = {"add_rows": "add_columns", "add_columns": "add_rows",
+                "weight_rows": "weight_columns", "weight_columns": "weight_rows"}
+        ops = [(swap.get(n, n), a) for n, a in self.ops]
+        return LazyScores(self.Y, self.X, self.metric, self.gamma, ops)
+
+    def min(self, dim: int = -1):
+        """Minimum over `dim` and its (lowest) index: top-k with k = 1 (Task
+        Map, Chamfer row: D.min(-1) and D.min(-2))."""
+        if dim in (-2, 0):
+            return self.T.min(-1)
         v, i = self.topk(1)
         return v[:, 0], i[:, 0]
 
-    def argmin(self):
-        return self.min()[1]
+    def argmin(self, dim: int = -1):
+        return self.min(dim)[1]
+
+    def max(self, dim: int = -1):
+        if dim in (-2, 0):
+            return self.T.max(-1)
+        v, i = self.topk(1, largest=True)
+        return v[:, 0], i[:, 0]
+
+    def sum(self, dim: int = -1) -> torch.Tensor:
+        """Sum over `dim`: the kernel product with a column of ones."""
+        if dim in (-2, 0):
+            return self.T.sum(-1)
+        ones = torch.ones(self.M, 1, dtype=self.dtype, device=self.device)
+        return self.matmul(ones)[:, 0]
+
+    def mean(self, dim: int = -1) -> torch.Tensor:
+        """Mean over `dim` (Features page, Native Deployment: reduce("mean",
+        -1)): the sum of the scores scaled by 1/count, as one more op."""
+        if dim in (-2, 0):
+            return self.T.mean(-1)
+        if self.M == 0:
+            return torch.full((self.N,), float("nan"), dtype=self.dtype, device=self.device)
+        scaled = LazyScores(self.X, self.Y, self.metric, self.gamma, list(self.ops) + [("mul", 1.0 / self.M)])
+        return scaled.sum(-1)
 
 
 def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()) -> LazyScores:

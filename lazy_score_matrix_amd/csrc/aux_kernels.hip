@@ -66,7 +66,7 @@ hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t
 // ---------------------------------------------------------------------------
 template <class T, int L>
 __global__ __launch_bounds__(256) void row_norms_kernel(const T *__restrict__ X, int64_t n, int64_t ld, int D,
-                                                        T *__restrict__ out) {
+                                                        T *__restrict__ out, bool inverse) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = t / L;
   const int lane = (int)(t % L);
@@ -79,23 +79,24 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const T *__restrict__ X,
   }
 #pragma unroll
   for (int m = L / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (row < n && lane == 0) out[row] = s;
+  if (row < n && lane == 0) out[row] = inverse ? (s > (T)0 ? (T)1 / sqrt(s) : (T)0) : s;
 }
 
 template <class T>
-static hipError_t row_norms_t(const T *X, int64_t n, int64_t ld, int D, T *out, hipStream_t s) {
+static hipError_t row_norms_t(const T *X, int64_t n, int64_t ld, int D, T *out, hipStream_t s, bool inv) {
   dim3 block(256);
   auto grid = [&](int L) { return dim3((unsigned)((n * L + 255) / 256)); };
-  if (D <= 4) hipLaunchKernelGGL((row_norms_kernel<T, 4>), grid(4), block, 0, s, X, n, ld, D, out);
-  else if (D <= 8) hipLaunchKernelGGL((row_norms_kernel<T, 8>), grid(8), block, 0, s, X, n, ld, D, out);
-  else hipLaunchKernelGGL((row_norms_kernel<T, 16>), grid(16), block, 0, s, X, n, ld, D, out);
+  if (D <= 4) hipLaunchKernelGGL((row_norms_kernel<T, 4>), grid(4), block, 0, s, X, n, ld, D, out, inv);
+  else if (D <= 8) hipLaunchKernelGGL((row_norms_kernel<T, 8>), grid(8), block, 0, s, X, n, ld, D, out, inv);
+  else hipLaunchKernelGGL((row_norms_kernel<T, 16>), grid(16), block, 0, s, X, n, ld, D, out, inv);
   return hipGetLastError();
 }
 
-hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s) {
+hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s,
+                            bool inverse) {
   if (n == 0) return hipSuccess;
-  if (dtype == 0) return row_norms_t<float>((const float *)X, n, ld, D, (float *)out, s);
-  return row_norms_t<double>((const double *)X, n, ld, D, (double *)out, s);
+  if (dtype == 0) return row_norms_t<float>((const float *)X, n, ld, D, (float *)out, s, inverse);
+  return row_norms_t<double>((const double *)X, n, ld, D, (double *)out, s, inverse);
 }
 
 // ---------------------------------------------------------------------------

@@ -163,4 +163,17 @@ __device__ __forceinline__ void key_insert(Key<T> (&l)[L], Key<T> c) {
   }
 }
 
+// Top-k filter threshold: the signed value (negated for `largest`) of the
+// list's last key, +inf while that slot is empty. Within one lane (or one
+// thread) keys arrive in increasing column order, so a candidate whose value
+// equals the threshold loses the index tie-break and is rightly skipped by a
+// strict <.
+__device__ __forceinline__ float key_threshold(const Key<float> &last) {
+  const uint32_t hi = (uint32_t)(last.k >> 32);
+  return hi == 0xffffffffu ? __builtin_huge_valf() : f32_from_ord(hi);
+}
+__device__ __forceinline__ double key_threshold(const Key<double> &last) {
+  return last.v == ~0ull ? __builtin_huge_val() : f64_from_ord(last.v);
+}
+
 }  // namespace pw

@@ -16,7 +16,9 @@
 //
 // Distances use |x|^2 + |y|^2 - 2 x.y: the query operand is pre-scaled by -2
 // (exact) and the accumulator starts at |x_i|^2 + |y_j|^2, so the matrix
-// cores return the squared distance directly; it is clamped at 0.
+// cores return the squared distance directly; it is clamped at 0. Cosine
+// distance is 1 - (x.y) (1/|x_i|) (1/|y_j|) with the inverse norms from a
+// pre-pass (columns) and from the query operand (rows).
 //
 // Epilogue: this engine takes chains that reduce to one affine stage with
 // row terms only (s <- r_i s + p_i, scalars or per-row vectors); any other
@@ -111,17 +113,6 @@ __device__ __forceinline__ double exp2_table(double x, const double *__restrict_
   return ldexp(fma(T, p, T), n >> 8);
 }
 
-// Top-k filter threshold: the signed value (negated for `largest`) of the
-// list's last key, +inf while that slot is empty. Within one lane keys
-// arrive in increasing column order, so a candidate whose value equals the
-// threshold loses the index tie-break and is rightly skipped by a strict <.
-__device__ __forceinline__ float key_threshold(const Key<float> &last) {
-  const uint32_t hi = (uint32_t)(last.k >> 32);
-  return hi == 0xffffffffu ? __builtin_huge_valf() : f32_from_ord(hi);
-}
-__device__ __forceinline__ double key_threshold(const Key<double> &last) {
-  return last.v == ~0ull ? __builtin_huge_val() : f64_from_ord(last.v);
-}
 __device__ __forceinline__ Key<float> key_placeholder(Key<float>) { return Key<float>{0ull}; }
 __device__ __forceinline__ Key<double> key_placeholder(Key<double>) { return Key<double>{0ull, 0u}; }
 // Cooperative loader of a [ROWS, COLS] tile (COLS padded, zero beyond the
@@ -209,7 +200,9 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS);
   constexpr int SB = BN / TM;
   constexpr int DG = DP / G;
-  constexpr bool DIST = METRIC != M_LINEAR;
+  constexpr bool DIST = METRIC == M_SQEUCLIDEAN || METRIC == M_RBF;  // norm expansion
+  constexpr bool COS = METRIC == M_COSINE;
+  constexpr bool NEEDN = DIST || COS;  // a per-key norm term staged in sN
   constexpr bool HAS_V = CONS == C_MATMUL || CONS == C_SOFTMAX;
   constexpr bool ONLINE = CONS == C_LOGSUMEXP || CONS == C_SOFTMAX;
   constexpr int NCB = HAS_V ? CP / TM : (CONS == C_DISPLACEMENT ? (DP + TM - 1) / TM : 1);
@@ -272,6 +265,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       qr[b][s] = DIST ? (T)-2 * v : v;
     }
     nx[b] = F::gsum(part);
+    if constexpr (COS) nx[b] = nx[b] > (T)0 ? (T)1 / sqrt(nx[b]) : (T)0;  // cosine keeps 1/|x_i| here
     T r = (T)1, p = (T)0;
     if (has_epi) {
       const Stage &st = a.epi.st[0];
@@ -290,7 +284,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     ep[b] = p;
     // Online consumers of a dot product: fold the row scale into the query
     // operand, so the matrix cores return the base-2 score directly.
-    if constexpr (ONLINE && !DIST) {
+    if constexpr (ONLINE && METRIC == M_LINEAR) {
 #pragma unroll
       for (int s = 0; s < DG; ++s) qr[b][s] *= r;
       er[b] = (T)1;
@@ -342,7 +336,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       // Plain searches (no epilogue, smallest first, dot product or squared
       // distance) filter on the raw accumulator: for distances the clamp at
       // 0 is deferred to the candidates, as max(x, 0) < thr implies x < thr.
-      const bool plain = METRIC != M_RBF && !has_epi && !a.largest;
+      const bool plain = (METRIC == M_LINEAR || METRIC == M_SQEUCLIDEAN) && !has_epi && !a.largest;
       bool any = false;
       if (plain) {
 #pragma unroll
@@ -361,6 +355,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
             T x = s[b][r];
             if constexpr (DIST) x = max(x, (T)0);
             if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
+            if constexpr (COS) x = fma(-x * sN[kb + F::key_of(r, g)], nx[b], (T)1);
             x = fma(x, er[b], ep[b]);
             s[b][r] = x;
             mn = min(mn, a.largest ? -x : x);
@@ -395,7 +390,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         T x = s[b][r];
         if constexpr (DIST) x = max(x, (T)0);
         if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
-        if constexpr (ONLINE && DIST) x = x * er[b];
+        if constexpr (COS) x = fma(-x * sN[kb + F::key_of(r, g)], nx[b], (T)1);
+        if constexpr (ONLINE && METRIC != M_LINEAR) x = x * er[b];
         v[b][r] = x;
       }
       if constexpr (!ONLINE) {
@@ -501,12 +497,12 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     const int nbt = (int)min((int64_t)BN, je - t0);
     ldK.load(Yp, a.ldy, t0, nbt, a.D, tid);
     if constexpr (HAS_V) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
-    if constexpr (DIST) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
+    if constexpr (NEEDN) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
   };
   auto stage = [&](int buf) {
     ldK.store(sKb[buf], tid);
     if constexpr (HAS_V) ldV.store(sVb[buf], tid);
-    if constexpr (DIST) {
+    if constexpr (NEEDN) {
       if (tid < BN) sNb[buf][tid] = nyv;
     }
   };

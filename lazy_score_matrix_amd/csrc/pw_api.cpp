@@ -160,14 +160,15 @@ struct Plan {
 int valu_dtile(int64_t D) { return D <= 3 ? 3 : (D <= 4 ? 4 : (D <= 16 ? 16 : 64)); }
 int valu_vtile(int64_t C) { return C <= 4 ? 4 : (C <= 16 ? 16 : 64); }
 
-// The MFMA engine takes D >= 16 (a real contraction), chains that reduce to
-// at most one affine stage with row terms only, and for the value consumers
-// at least 16 value columns (narrower products stay on the VALU engine).
+// The MFMA engine takes D >= 16 (a real contraction) and chains that reduce
+// to at most one affine stage with row terms only. For the value consumers
+// a narrow V (C < 16) pads the second contraction to 32 (float) or 16
+// (double) columns, which only pays once D >= 32.
 bool mfma_eligible(const pw_expr &e, int consumer, int64_t C) {
   if (e.D < 16) return false;
   if (e.stages.size() > 1) return false;
   if (e.stages.size() == 1 && (e.stages[0].kind != ST_AFFINE || e.stages[0].col_vec)) return false;
-  if ((consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) && C < 16) return false;
+  if ((consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) && C < 16 && e.D < 32) return false;
   return true;
 }
 
@@ -196,7 +197,6 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     p.bm = mfma_bm(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
     p.bn = mfma_bn(e.dtype, consumer);
     p.chunk = (int)std::min<int64_t>(C, p.mcfg.cp);
-    p.col_norms = e.metric != PW_LINEAR;
     target_wgs = (int64_t)kTargetCUs * mfma_wgs_per_cu(e.dtype, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
   } else {
     p.vcfg.dtile = valu_dtile(e.D);
@@ -204,11 +204,14 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       p.vcfg.vtile = valu_vtile(C);
       p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
     } else if (consumer == PW_C_TOPK) {
-      p.vcfg.vtile = k <= 16 ? 16 : 64;
+      p.vcfg.vtile = k == 1 ? 1 : (k <= 16 ? 16 : 64);
     } else {
       p.vcfg.vtile = 0;
     }
   }
+  // Column norms: |y_j|^2 for the MFMA engine's distance expansion, 1/|y_j|
+  // for cosine on either engine.
+  p.col_norms = (p.family == 1 && e.metric != PW_LINEAR) || e.metric == PW_COSINE;
   p.off_ny = off;
   if (p.col_norms) off += align_up((size_t)e.M * es);
   p.off_part = off;
@@ -342,12 +345,14 @@ hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const Tile
       switch (e.metric) {
         case PW_LINEAR: return mfma_launch_metric<float, M_LINEAR>(consumer, p.mcfg, a, s);
         case PW_SQEUCLIDEAN: return mfma_launch_metric<float, M_SQEUCLIDEAN>(consumer, p.mcfg, a, s);
+        case PW_COSINE: return mfma_launch_metric<float, M_COSINE>(consumer, p.mcfg, a, s);
         default: return mfma_launch_metric<float, M_RBF>(consumer, p.mcfg, a, s);
       }
     }
     switch (e.metric) {
       case PW_LINEAR: return mfma_launch_metric<double, M_LINEAR>(consumer, p.mcfg, a, s);
       case PW_SQEUCLIDEAN: return mfma_launch_metric<double, M_SQEUCLIDEAN>(consumer, p.mcfg, a, s);
+      case PW_COSINE: return mfma_launch_metric<double, M_COSINE>(consumer, p.mcfg, a, s);
       default: return mfma_launch_metric<double, M_RBF>(consumer, p.mcfg, a, s);
     }
   }
@@ -355,12 +360,14 @@ hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const Tile
     switch (e.metric) {
       case PW_LINEAR: return valu_launch_metric<float, M_LINEAR>(consumer, p.vcfg, a, s);
       case PW_SQEUCLIDEAN: return valu_launch_metric<float, M_SQEUCLIDEAN>(consumer, p.vcfg, a, s);
+      case PW_COSINE: return valu_launch_metric<float, M_COSINE>(consumer, p.vcfg, a, s);
       default: return valu_launch_metric<float, M_RBF>(consumer, p.vcfg, a, s);
     }
   }
   switch (e.metric) {
     case PW_LINEAR: return valu_launch_metric<double, M_LINEAR>(consumer, p.vcfg, a, s);
     case PW_SQEUCLIDEAN: return valu_launch_metric<double, M_SQEUCLIDEAN>(consumer, p.vcfg, a, s);
+    case PW_COSINE: return valu_launch_metric<double, M_COSINE>(consumer, p.vcfg, a, s);
     default: return valu_launch_metric<double, M_RBF>(consumer, p.vcfg, a, s);
   }
 }
@@ -368,7 +375,8 @@ hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const Tile
 // Column norms |y_j|^2 for the MFMA engine's distance expansion.
 int prepare_norms(const pw_expr &e, const Plan &p, const TileArgs &a, hipStream_t s) {
   if (!p.col_norms) return PW_OK;
-  return hip_status(launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s));
+  return hip_status(
+      launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s, e.metric == PW_COSINE));
 }
 
 // Caller-owned events recorded around tile launches (pw_set_tile_events).
@@ -414,7 +422,7 @@ int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, i
   if (!out) return PW_ERR_INVALID;
   *out = nullptr;
   if (dtype != PW_F32 && dtype != PW_F64) return PW_ERR_INVALID;
-  if (metric < PW_LINEAR || metric > PW_RBF) return PW_ERR_INVALID;
+  if (metric < PW_LINEAR || metric > PW_COSINE) return PW_ERR_INVALID;
   if (metric == PW_RBF && !(std::isfinite(gamma) && gamma >= 0.0)) return PW_ERR_INVALID;
   if (N < 0 || M < 0 || n_ops < 0) return PW_ERR_INVALID;
   if (D < 1 || D > PW_MAX_D) return PW_ERR_UNSUPPORTED;

@@ -61,7 +61,7 @@ struct VecProgBatch {
 };
 
 enum Consumer : int { C_MATMUL = 0, C_DISPLACEMENT = 1, C_LOGSUMEXP = 2, C_SOFTMAX = 3, C_TOPK = 4 };
-enum Metric : int { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2 };
+enum Metric : int { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2, M_COSINE = 3 };
 
 // ---------------------------------------------------------------------------
 // Arguments of one tile-engine launch.
@@ -92,8 +92,8 @@ struct TileArgs {
   int n_split;           // column splits
   int64_t split_cols;    // columns per split (multiple of the tile width)
   void *partial;         // workspace partials when n_split > 1
-  const void *nx;        // row norms (kernels using the norm expansion)
-  const void *ny;        // column norms
+  const void *nx;        // unused (row norms are formed in-kernel)
+  const void *ny;        // column norms |y_j|^2 (distances) or 1/|y_j| (cosine, 0 for y_j = 0)
   double exp2_c[4];      // (ln2/256)^k / k!, k = 1..4, for the table-driven double exp2
   Epi epi;
 };
@@ -158,7 +158,9 @@ hipError_t mfma_launch_metric(int consumer, const MfmaConfig &cfg, const TileArg
 // Auxiliary kernels.
 hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s);
 hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);
-hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s);
+// Row norms |x_i|^2, or with `inverse` 1/|x_i| (0 for a zero row).
+hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s,
+                            bool inverse = false);
 hipError_t launch_merge(int dtype, int consumer, const TileArgs &a, hipStream_t s);
 
 }  // namespace pw

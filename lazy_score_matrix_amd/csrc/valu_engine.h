@@ -5,12 +5,14 @@
 // and the staged column epilogue vectors). Every lane of a wave reads the
 // same LDS address for a column, so the reads are broadcasts. Each score is
 // evaluated in direct form (the sum of squared differences for the distance
-// metrics), run through the epilogue, and folded into the row's reduction:
+// metrics; the dot product scaled by 1/|x_i| and a staged 1/|y_j| for
+// cosine), run through the epilogue, and folded into the row's reduction:
 //   matmul        acc[c] += s * V[j, c]
 //   displacement  acc[d] += s * y_jd, mass += s; out = acc - x * mass
 //   logsumexp     online (max m, sum l) per group of 8 columns
 //   softmax@V     online (m, l, acc[c]) per group of 8 columns
-//   top-k         sorted register list of (value, index) keys
+//   top-k         sorted register list of (value, index) keys behind a
+//                 value threshold; k = 1 keeps one (value, index) pair
 // This engine covers every D in 1..64, every op chain and both dtypes; the
 // planner prefers it for small D and small value widths, where there is no
 // real contraction to hand to the matrix cores.
@@ -24,7 +26,13 @@ namespace pw {
 // (the hardware base-2 exponential).
 template <int METRIC, class T, int DT>
 __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gamma) {
-  if constexpr (METRIC == M_LINEAR) {
+  if constexpr (METRIC == M_LINEAR || METRIC == M_COSINE) {
+    if constexpr (DT <= 4) {
+      T s = x[0] * y[0];
+#pragma unroll
+      for (int d = 1; d < DT; ++d) s = fma(x[d], y[d], s);
+      return s;
+    }
     T s0 = 0, s1 = 0;
 #pragma unroll
     for (int d = 0; d < DT; d += 2) {
@@ -33,17 +41,29 @@ __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gam
     }
     return s0 + s1;
   } else {
-    T s0 = 0, s1 = 0;
+    T d2;
+    if constexpr (DT <= 4) {
+      // One chain: the columns of a tile already give the ILP.
+      T t = x[0] - y[0];
+      d2 = t * t;
 #pragma unroll
-    for (int d = 0; d < DT; d += 2) {
-      T t0 = x[d] - y[d];
-      s0 = fma(t0, t0, s0);
-      if (d + 1 < DT) {
-        T t1 = x[d + 1] - y[d + 1];
-        s1 = fma(t1, t1, s1);
+      for (int d = 1; d < DT; ++d) {
+        t = x[d] - y[d];
+        d2 = fma(t, t, d2);
       }
+    } else {
+      T s0 = 0, s1 = 0;
+#pragma unroll
+      for (int d = 0; d < DT; d += 2) {
+        T t0 = x[d] - y[d];
+        s0 = fma(t0, t0, s0);
+        if (d + 1 < DT) {
+          T t1 = x[d + 1] - y[d + 1];
+          s1 = fma(t1, t1, s1);
+        }
+      }
+      d2 = s0 + s1;
     }
-    T d2 = s0 + s1;
     if constexpr (METRIC == M_RBF) {
       if constexpr (sizeof(T) == 4) return __builtin_amdgcn_exp2f(neg_gamma * d2);
       else return dexp(neg_gamma * d2);
@@ -60,11 +80,14 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   constexpr int ACCN = HAS_V ? VT : (CONS == C_DISPLACEMENT ? DT : 1);
   constexpr int KL = (CONS == C_TOPK) ? VT : 1;
   constexpr int G = 8;  // columns per online-softmax group
+  // Three features are padded to four so a column is one aligned LDS read.
+  constexpr int DTS = DT == 3 ? 4 : DT;
 
-  __shared__ T sY[BN][DT];
+  __shared__ T sY[BN][DTS];
   __shared__ T sV[BN][VW];
   __shared__ T sQ[kMaxStages][BN];
   __shared__ T sO[kMaxStages][BN];
+  __shared__ T sR[METRIC == M_COSINE ? BN : 1];  // 1/|y_j| for cosine
 
   const int tid = threadIdx.x;
   const int rb = blockIdx.x % a.n_rb;
@@ -80,6 +103,19 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   RowEpi<T> re;
   load_row_epi<T>(a.epi, i, rv, re);
   const T neg_gamma = sizeof(T) == 4 ? (T)(-a.gamma * kLog2e) : (T)(-a.gamma);
+  T rx = 0;  // 1/|x_i| for cosine (0 for a zero row)
+  if constexpr (METRIC == M_COSINE) {
+    T n2 = 0;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) n2 = fma(x[d], x[d], n2);
+    rx = n2 > (T)0 ? (T)1 / sqrt(n2) : (T)0;
+  }
+  // Score of column slot jj (the metric; cosine scales the dot product).
+  auto metric = [&](int jj) -> T {
+    T v = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
+    if constexpr (METRIC == M_COSINE) v = fma(-v * sR[jj], rx, (T)1);
+    return v;
+  };
 
   T acc[ACCN];
 #pragma unroll
@@ -89,6 +125,10 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   Key<T> list[KL];
 #pragma unroll
   for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
+  // Top-k threshold in the signed orientation (negated for `largest`); with
+  // k = 1 the best signed value and its column are kept directly.
+  T thr = __builtin_huge_val();
+  uint32_t best_j = ~0u;
 
   for (int64_t j0 = jb; j0 < je; j0 += BN) {
     const int nb = (int)min((int64_t)BN, je - j0);
@@ -102,6 +142,9 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
         int jj = e / VW, c = e % VW;
         sV[jj][c] = (jj < nb && c < a.C) ? ldg<T>(a.V, (j0 + jj) * a.ldv + c) : (T)0;
       }
+    }
+    if constexpr (METRIC == M_COSINE) {
+      for (int e = tid; e < BN; e += BM) sR[e] = e < nb ? ldg<T>(a.ny, j0 + e) : (T)0;
     }
     if (a.epi.any_col) {
       for (int e = tid; e < kMaxStages * BN; e += BM) {
@@ -125,8 +168,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
           const int jj = g + u;
           T s = neg_inf<T>();
           if (jj < nb) {
-            s = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
-            s = apply_epi<T, BN>(a.epi, re, s, sQ, sO, jj);
+            s = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
             if (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) s = neg_inf<T>();
           }
           sv[u] = s;
@@ -162,17 +204,40 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
 #pragma unroll
           for (int d = 0; d < ACCN; ++d) acc[d] = fma(s, sY[jj][d], acc[d]);
           mass += s;
-        } else if constexpr (CONS == C_TOPK) {
-          key_insert<T, KL>(list, Key<T>::make(s, (uint32_t)(j0 + jj), a.largest));
+        }
+      };
+      // Top-k: columns reach a thread in increasing order, so a candidate
+      // enters only when its signed value is strictly below the threshold.
+      auto fold_topk = [&](int jj, T sv) {
+        if constexpr (KL == 1) {
+          const bool lt = sv < thr;
+          thr = lt ? sv : thr;
+          best_j = lt ? (uint32_t)(j0 + jj) : best_j;
+        } else {
+          if (sv < thr) {
+            key_insert<T, KL>(list, Key<T>::make(a.largest ? -sv : sv, (uint32_t)(j0 + jj), a.largest));
+            thr = key_threshold(list[KL - 1]);
+          }
         }
       };
       // The stage loop runs only when the expression has score arithmetic;
       // a bare metric takes a loop without it (a uniform branch).
-      if (a.epi.n_stages == 0) {
-        for (int jj = 0; jj < nb; ++jj) fold(jj, valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma));
+      if constexpr (CONS == C_TOPK) {
+        if (a.epi.n_stages == 0) {
+          if (a.largest) {
+            for (int jj = 0; jj < nb; ++jj) fold_topk(jj, -metric(jj));
+          } else {
+            for (int jj = 0; jj < nb; ++jj) fold_topk(jj, metric(jj));
+          }
+        } else {
+          const T sg = a.largest ? (T)-1 : (T)1;
+          for (int jj = 0; jj < nb; ++jj) fold_topk(jj, sg * apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj));
+        }
+      } else if (a.epi.n_stages == 0) {
+        for (int jj = 0; jj < nb; ++jj) fold(jj, metric(jj));
       } else {
         for (int jj = 0; jj < nb; ++jj)
-          fold(jj, apply_epi<T, BN>(a.epi, re, valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma), sQ, sO, jj));
+          fold(jj, apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj));
       }
     }
   }
@@ -214,6 +279,9 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
         if (c < a.C) o[2 + c] = acc[c];
     }
   } else if constexpr (CONS == C_TOPK) {
+    if constexpr (KL == 1) {
+      if (best_j != ~0u) list[0] = Key<T>::make(a.largest ? -thr : thr, best_j, a.largest);
+    }
     if (fin) {
       T *v = static_cast<T *>(a.out) + i * a.k;
       int64_t *ix = a.idx + i * a.k;
@@ -245,6 +313,7 @@ hipError_t valu_by_vt(int vt, const TileArgs &a, hipStream_t s) {
     if (vt == 16) return launch_valu_kernel<T, METRIC, CONS, DT, 16>(a, s);
     if (vt == 64) return launch_valu_kernel<T, METRIC, CONS, DT, 64>(a, s);
   } else if constexpr (CONS == C_TOPK) {
+    if (vt == 1) return launch_valu_kernel<T, METRIC, CONS, DT, 1>(a, s);
     if (vt == 16) return launch_valu_kernel<T, METRIC, CONS, DT, 16>(a, s);
     if (vt == 64) return launch_valu_kernel<T, METRIC, CONS, DT, 64>(a, s);
   } else {

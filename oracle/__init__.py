@@ -40,7 +40,7 @@ OPS = {
     "weight_columns": 5,  # s <- u_j * s
     "exp": 6,             # s <- exp(s)
 }
-METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2}
+METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2, "cosine_distances": 3}
 
 _lock = threading.Lock()
 _lib = None

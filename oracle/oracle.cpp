@@ -7,7 +7,10 @@
 // What it computes (torchpairwise guide "Using Torchpairwise in Models"):
 //   * a pairwise score s_ij = f(x_i, y_j) for the built-in metrics "linear",
 //     "sqeuclidean" and "rbf" (Task Map table; Score Expressions; the SVGD
-//     section gives the rbf form exp(-gamma*|x-y|^2));
+//     section gives the rbf form exp(-gamma*|x-y|^2)), and "cosine_distances"
+//     (Custom Comparisons / Encoded Feature Reuse page, "Prepare Once, Use
+//     Several Consumers": 1 - x.y / (|x| |y|), taken as 1 when either vector
+//     is zero);
 //   * the per-pair score arithmetic applied left to right: scalar multiply
 //     and add, add_rows / add_columns, weight_rows / weight_columns and exp
 //     (Score Expressions section);
@@ -36,6 +39,7 @@
 //   linear       mu = sum_d |x_d y_d|
 //   sqeuclidean  mu = sum_d (|x_d| + |y_d|)^2
 //   rbf          mu = k (1 + gamma * sum_d (|x_d| + |y_d|)^2)
+//   cosine       mu = 1 + 3 sum_d |x_d y_d| / (|x| |y|)   (1 for a zero vector)
 //   MUL c        mu <- |c| mu        (also MUL_ROWS / MUL_COLS with |w_i|, |u_j|)
 //   ADD c        mu <- mu + |s_new|  (also ADD_ROWS / ADD_COLS)
 //   EXP          mu <- exp(s_old) (1 + mu)
@@ -58,7 +62,7 @@ extern "C" {
 // Mirrors the Python-side ctypes structure in oracle.py.
 typedef struct {
   int dtype;                 // 0: float32 inputs, 1: float64 inputs
-  int metric;                // 0: linear, 1: sqeuclidean, 2: rbf
+  int metric;                // 0: linear, 1: sqeuclidean, 2: rbf, 3: cosine_distances
   double gamma;              // rbf only
   const void *X;             // [N, ldx] row-major, dtype
   int64_t N, ldx;
@@ -76,7 +80,7 @@ typedef struct {
 namespace {
 
 enum { OP_MUL = 0, OP_ADD = 1, OP_ADD_ROWS = 2, OP_ADD_COLS = 3, OP_MUL_ROWS = 4, OP_MUL_COLS = 5, OP_EXP = 6 };
-enum { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2 };
+enum { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2, M_COSINE = 3 };
 
 inline double rexp(double v) { return std::exp(v); }
 inline long double rexp(long double v) { return expl(v); }
@@ -103,6 +107,23 @@ struct Expr {
         R p = x(i, d) * y(j, d);
         s += p;
         mu += std::fabs(p);
+      }
+    } else if (e.metric == M_COSINE) {
+      R dot = 0, nx = 0, ny = 0, adot = 0;
+      for (int64_t d = 0; d < e.D; ++d) {
+        R a = x(i, d), b = y(j, d);
+        dot += a * b;
+        adot += std::fabs(a * b);
+        nx += a * a;
+        ny += b * b;
+      }
+      if (nx > 0 && ny > 0) {
+        R den = std::sqrt(nx) * std::sqrt(ny);
+        s = 1 - dot / den;
+        mu = 1 + 3 * adot / den;
+      } else {
+        s = 1;
+        mu = 1;
       }
     } else {
       R sum_sq = 0, spread = 0;

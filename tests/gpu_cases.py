@@ -18,6 +18,21 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
 
 
+SWAP = {"add_rows": "add_columns", "add_columns": "add_rows", "weight_rows": "weight_columns",
+        "weight_columns": "weight_rows"}
+
+
+def bind_case(arrays, c):
+    """Both expressions of a workload case; a transposed case reduces over
+    the rows, i.e. binds (Y, X) with row and column ops swapped."""
+    ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+    X, Y = arrays[c.x], arrays[c.y]
+    if getattr(c, "transpose", False):
+        X, Y = Y, X
+        ops = [(SWAP.get(n, n), a) for n, a in ops]
+    return bind_both(X, Y, c.metric, c.gamma, ops, same=c.x == c.y)
+
+
 def bind_both(X, Y, metric, gamma=1.0, ops=(), same=False):
     """The GPU expression and the oracle expression of one score."""
     tX = to_dev(X)
@@ -48,6 +63,10 @@ def check_consumer(e, oe, consumer, V=None, exclude_self=False, k=0, largest=Fal
     elif consumer == "logsumexp":
         g = e.logsumexp(exclude_self=exclude_self)[sel]
         o, mag = oracle.logsumexp(oe, exclude_self=exclude_self, rows=rows)
+    elif consumer == "mean":
+        g = e.mean()[sel][:, None]
+        o, mag = oracle.matmul(oe, np.ones((oe.M, 1), dtype=oe.np_dtype), rows)
+        o, mag = o / oe.M, mag / oe.M
     elif consumer == "topk":
         gv, gi = e.topk(k, largest=largest)
         gv, gi = gv[sel].cpu().numpy(), gi[sel].cpu().numpy()

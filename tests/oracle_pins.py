@@ -54,6 +54,8 @@ def dense_scores_torch(X, Y, metric, gamma=1.0, ops=()):
     Yt = torch.as_tensor(np.asarray(Y, np.float64))
     if metric == "linear":
         S = Xt @ Yt.T
+    elif metric == "cosine_distances":
+        S = 1 - torch.nn.functional.cosine_similarity(Xt[:, None, :], Yt[None, :, :], dim=-1, eps=1e-300)
     else:
         S = torch.cdist(Xt, Yt, compute_mode="donot_use_mm_for_euclid_dist") ** 2
         if metric == "rbf":
@@ -116,13 +118,28 @@ def pin_rbf_self_is_one():
 
 
 def pin_metric_symmetry():
-    """f(x, y) = f(y, x) for all three metrics."""
+    """f(x, y) = f(y, x) for all four metrics."""
     for dt in DTYPES:
         X, Y = _inputs(2, 9, 11, 5, dt)
-        for metric in ("linear", "sqeuclidean", "rbf"):
+        for metric in ("linear", "sqeuclidean", "rbf", "cosine_distances"):
             a, _ = oracle.scores(oracle.Expr(X, Y, metric, gamma=0.3))
             b, _ = oracle.scores(oracle.Expr(Y, X, metric, gamma=0.3))
             _close(a, np.asarray(b).T, what="symmetry %s" % metric)
+
+
+def pin_cosine_special_cases():
+    """cosine distance: 0 for parallel, 1 for orthogonal or zero, 2 for
+    antipodal vectors; unchanged by positive scaling of either side."""
+    for dt in DTYPES:
+        X = np.array([[1, 2, 2], [0, 0, 0], [3, 0, 0]], dt)
+        Y = np.array([[2, 4, 4], [-1, -2, -2], [0, 5, 0]], dt)
+        out, _ = oracle.scores(oracle.Expr(X, Y, "cosine_distances"))
+        want = [[0, 2, 1 - 2 / 3.0], [1, 1, 1], [1 - 1 / 3.0, 1 + 1 / 3.0, 1]]
+        _close(out, want, rtol=1e-14, atol=1e-14, what="cosine special cases")
+        X2, Y2 = _inputs(4, 6, 8, 5, dt)
+        a, _ = oracle.scores(oracle.Expr(X2, Y2, "cosine_distances"))
+        b, _ = oracle.scores(oracle.Expr((4 * X2).astype(dt), (0.5 * Y2).astype(dt), "cosine_distances"))
+        _close(a, b, rtol=1e-12, atol=1e-13, what="cosine scale invariance")
 
 
 def pin_translation_invariance():
@@ -139,11 +156,11 @@ def pin_translation_invariance():
 
 
 def pin_metrics_vs_dense():
-    """All metrics against torch float64 matmul / cdist on small random inputs."""
+    """All metrics against torch float64 matmul / cdist / cosine_similarity on small random inputs."""
     for dt in DTYPES:
         for d in (1, 3, 16, 33, 64):
             X, Y = _inputs(10 + d, 7, 9, d, dt)
-            for metric in ("linear", "sqeuclidean", "rbf"):
+            for metric in ("linear", "sqeuclidean", "rbf", "cosine_distances"):
                 out, mag = oracle.scores(oracle.Expr(X, Y, metric, gamma=0.05))
                 ref = dense_scores_torch(X, Y, metric, 0.05).numpy()
                 _close(out, ref, rtol=1e-12, atol=1e-12, what="dense %s D=%d" % (metric, d))

@@ -50,7 +50,7 @@ def test_bind_validation(lib):
     lib.pw_release(None)
     cases = [
         (dict(dtype=2), pw.PW_ERR_INVALID),
-        (dict(metric=3), pw.PW_ERR_INVALID),
+        (dict(metric=4), pw.PW_ERR_INVALID),
         (dict(metric=2, gamma=-1.0), pw.PW_ERR_INVALID),
         (dict(metric=2, gamma=float("nan")), pw.PW_ERR_INVALID),
         (dict(metric=2, gamma=float("inf")), pw.PW_ERR_INVALID),

@@ -21,6 +21,7 @@ MUTANTS = [
      "for (int64_t d = 0; d < e.D; ++d) {\n        R p = x(i, d) * y(j, d);",
      "for (int64_t d = 1; d < e.D; ++d) {\n        R p = x(i, d) * y(j, d);"),
     ("difference_sign", "R diff = a - b;", "R diff = a + b;"),
+    ("cosine_norm_not_rooted", "R den = std::sqrt(nx) * std::sqrt(ny);", "R den = nx * std::sqrt(ny);"),
     ("rbf_half_exponent", "s = rexp(-(R)e.gamma * sum_sq);", "s = rexp(-(R)e.gamma * sum_sq / 2);"),
     ("x_read_from_y", "R x(int64_t i, int64_t d) const { return (R)X[i * e.ldx + d]; }",
      "R x(int64_t i, int64_t d) const { return (R)Y[(i % e.M) * e.ldy + d]; }"),

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_cases import bind_both, check_consumer
+from gpu_cases import bind_both, bind_case, check_consumer
 
 pytestmark = pytest.mark.gpu
 
@@ -20,12 +20,16 @@ def test_full_size_workload(name):
     oracle.set_threads(len(os.sched_getaffinity(0)))
     arrays, cases = workloads.make(name)
     for c in cases:
-        ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
-        e, oe = bind_both(arrays[c.x], arrays[c.y], c.metric, c.gamma, ops, same=c.x == c.y)
+        e, oe = bind_case(arrays, c)
         rows = workloads.sample_rows(oe.N, stride=STRIDE.get(name, 61))
         V = arrays[c.v] if c.v else None
         ratio, rel = check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k,
                                     largest=c.largest, rows=rows, what="%s/%s" % (name, c.name))
         print("%s/%s: %d rows, worst err/tol %.3g, plan %s" % (name, c.name, len(rows), ratio,
-                                                              e.plan(c.consumer, V.shape[1] if V is not None else 0,
-                                                                     c.k)))
+                                                              e.plan(*_plan_args(c, V))))
+
+
+def _plan_args(c, V):
+    if c.consumer == "mean":
+        return "matmul", 1, 0
+    return c.consumer, V.shape[1] if V is not None else 0, c.k

@@ -7,11 +7,11 @@ import pytest
 import torch
 
 import workloads
-from gpu_cases import bind_both, check_consumer, to_dev
+from gpu_cases import bind_both, bind_case, check_consumer, to_dev
 
 pytestmark = pytest.mark.gpu
 
-METRICS = ("linear", "sqeuclidean", "rbf")
+METRICS = ("linear", "sqeuclidean", "rbf", "cosine_distances")
 CONSUMERS = ("matmul", "displacement", "logsumexp", "softmax_matmul", "topk")
 DTYPES = (np.float32, np.float64)
 
@@ -226,9 +226,7 @@ def test_reduced_workloads(name):
     finishes in seconds."""
     arrays, cases = workloads.make(name, reduced=True)
     for c in cases:
-        ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
-        same = c.x == c.y
-        e, oe = bind_both(arrays[c.x], arrays[c.y], c.metric, c.gamma, ops, same=same)
+        e, oe = bind_case(arrays, c)
         V = arrays[c.v] if c.v else None
         check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k, largest=c.largest,
                        what="%s/%s" % (name, c.name))

@@ -40,7 +40,7 @@ def _randn(g, *shape):
 class Case:
     """One consumer call on a workload."""
     name: str
-    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk
+    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk | mean
     x: str                   # array used as X
     y: str                   # array used as Y
     metric: str
@@ -50,6 +50,7 @@ class Case:
     exclude_self: bool = False
     k: int = 0
     largest: bool = False
+    transpose: bool = False  # reduce over rows instead (the transposed score)
 
 
 def rbf_small(n: int = 1024, m: int | None = None, d: int = 3, seed: int = 1001):
@@ -140,6 +141,41 @@ def svgd(n: int = 131072, d: int = 16, seed: int = 1005):
     return arrays, cases
 
 
+def chamfer(n: int = 65536, m: int = 65536, d: int = 3, seed: int = 1006):
+    """Chamfer-style nearest neighbours in both directions, float32: D.min(-1)
+    and D.min(-2) on D = sqeuclidean(X, Y) for two N(0, I) point clouds
+    (Task Map, Chamfer row)."""
+    g = _gen(seed)
+    X = _randn(g, n, d)
+    Y = _randn(g, m, d)
+    arrays = {"X": X.to(torch.float32).numpy(), "Y": Y.to(torch.float32).numpy()}
+    cases = [Case("chamfer_x_to_y", "topk", "X", "Y", "sqeuclidean", k=1),
+             Case("chamfer_y_to_x", "topk", "X", "Y", "sqeuclidean", k=1, transpose=True)]
+    return arrays, cases
+
+
+def cosine_knn(n_query: int = 32768, n_ref: int = 524288, d: int = 64, seed: int = 1007):
+    """Retrieval by cosine distance on encoded features, float32: top-10
+    smallest cosine distances (Features page, "Prepare Once, Use Several
+    Consumers": a cosine_distances head on extracted features)."""
+    g = _gen(seed)
+    R = _randn(g, n_ref, d)
+    Q = _randn(g, n_query, d)
+    arrays = {"Q": Q.to(torch.float32).numpy(), "R": R.to(torch.float32).numpy()}
+    return arrays, [Case("cosine_knn", "topk", "Q", "R", "cosine_distances", k=10)]
+
+
+def feature_mean(n: int = 65536, m: int = 65536, d: int = 16, seed: int = 1008):
+    """Row mean of squared distances between two feature sets, float32 (Features
+    page, Native Deployment: pairwise_expression(features, other,
+    "sqeuclidean") then reduce("mean", -1))."""
+    g = _gen(seed)
+    F = _randn(g, n, d)
+    G = _randn(g, m, d)
+    arrays = {"F": F.to(torch.float32).numpy(), "G": G.to(torch.float32).numpy()}
+    return arrays, [Case("feature_mean", "mean", "F", "G", "sqeuclidean")]
+
+
 # name -> (generator, full-size kwargs, reduced kwargs for quick parity runs)
 WORKLOADS = {
     "rbf_small": (rbf_small, {}, {"n": 300, "m": 333}),
@@ -148,6 +184,9 @@ WORKLOADS = {
     "infonce": (infonce, {}, {"n": 900}),
     "knn": (knn, {}, {"n_query": 500, "n_ref": 4099}),
     "svgd": (svgd, {}, {"n": 1100}),
+    "chamfer": (chamfer, {}, {"n": 700, "m": 900}),
+    "cosine_knn": (cosine_knn, {}, {"n_query": 300, "n_ref": 3000}),
+    "feature_mean": (feature_mean, {}, {"n": 800, "m": 1000}),
 }
 
 

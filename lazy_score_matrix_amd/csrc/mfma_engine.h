@@ -189,7 +189,7 @@ struct MfmaShape {
 
 template <class T, int METRIC, int CONS, int DP, int CP, int KL>
 __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
-                             (mfma_wgs_per_cu(sizeof(T) == 4 ? 0 : 1, DP, CP, KL))) void mfma_tile(const TileArgs a) {
+                             (mfma_wgs_per_cu(sizeof(T) == 4 ? 0 : 1, CONS, DP, CP, KL))) void mfma_tile(const TileArgs a) {
   using F = Mfma<T>;
   using acc_t = typename F::acc_t;
   constexpr int TM = F::TM, G = F::G, NREG = F::NREG;
@@ -197,16 +197,21 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   constexpr int QB = Shape::QB;
   constexpr int BM = Shape::BM;
   constexpr int NT = Shape::NT;
-  constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS);
+  constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS, CP);
   constexpr int SB = BN / TM;
   constexpr int DG = DP / G;
   constexpr bool DIST = METRIC == M_SQEUCLIDEAN || METRIC == M_RBF;  // norm expansion
   constexpr bool COS = METRIC == M_COSINE;
   constexpr bool NEEDN = DIST || COS;  // a per-key norm term staged in sN
   constexpr bool HAS_V = CONS == C_MATMUL || CONS == C_SOFTMAX;
+  // A single value column (a weighted row sum): V is staged as one LDS
+  // column and folded with vector FMAs; the matrix cores compute the scores.
+  constexpr bool NARROW = CONS == C_MATMUL && CP == 1;
+  constexpr bool VTILE = HAS_V && !NARROW;
   constexpr bool ONLINE = CONS == C_LOGSUMEXP || CONS == C_SOFTMAX;
-  constexpr int NCB = HAS_V ? CP / TM : (CONS == C_DISPLACEMENT ? (DP + TM - 1) / TM : 1);
-  constexpr bool PV = HAS_V || CONS == C_DISPLACEMENT;
+  constexpr int NCB = VTILE ? CP / TM : (CONS == C_DISPLACEMENT ? (DP + TM - 1) / TM : 1);
+  constexpr bool PV = VTILE || CONS == C_DISPLACEMENT;
+  static_assert(BN <= NT, "one thread stages each key's norm and value");
   constexpr int KPAD = sizeof(T) == 4 ? 4 : 2;
   constexpr int VW = HAS_V ? CP : 1;
   constexpr int KLQ = CONS == C_TOPK ? KL : 1;
@@ -300,6 +305,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 #pragma unroll
       for (int r = 0; r < NREG; ++r) o[b][c][r] = 0;
   T m[QB], lsum[QB], mass[QB];
+  T wsum[QB][4];  // NARROW: four partial sums per row
   Key<T> list[QB][KLQ];
   T thr[QB];
 #pragma unroll
@@ -308,6 +314,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     m[b] = kNegInf;
     lsum[b] = 0;
     mass[b] = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wsum[b][u] = 0;
 #pragma unroll
     for (int p = 0; p < KLQ; ++p)
       list[b][p] = (p < KLQ - a.k) ? key_placeholder(Key<T>()) : Key<T>::sentinel();
@@ -455,6 +463,13 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       }
     }
 
+    if constexpr (NARROW) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) wsum[b][r % 4] = fma(v[b][r], sV[kb + F::key_of(r, g)][0], wsum[b][r % 4]);
+    }
+
     if constexpr (PV) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
@@ -487,21 +502,25 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   // sub-block sb+1 are issued to the matrix cores before sub-block sb is
   // consumed, so its vector work overlaps them.
   TileLoader<T, BN, DP, NT> ldK;
-  TileLoader<T, BN, HAS_V ? CP : 16 / (int)sizeof(T), NT> ldV;
-  T nyv = 0;
+  TileLoader<T, BN, VTILE ? CP : 16 / (int)sizeof(T), NT> ldV;
+  T nyv = 0, vcol = 0;
   const bool kvec = vec_ok(a.Y, a.ldy, 16 / (int)sizeof(T));
-  const bool vvec = HAS_V && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
+  const bool vvec = VTILE && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
   ldK.init(a.ldy, kvec, tid);
-  if constexpr (HAS_V) ldV.init(a.ldv, vvec, tid);
+  if constexpr (VTILE) ldV.init(a.ldv, vvec, tid);
   auto prefetch = [&](int64_t t0) {
     const int nbt = (int)min((int64_t)BN, je - t0);
     ldK.load(Yp, a.ldy, t0, nbt, a.D, tid);
-    if constexpr (HAS_V) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
+    if constexpr (VTILE) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
+    if constexpr (NARROW) vcol = (tid < nbt) ? ldg<T>(a.V, (t0 + tid) * a.ldv) : (T)0;
     if constexpr (NEEDN) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
   };
   auto stage = [&](int buf) {
     ldK.store(sKb[buf], tid);
-    if constexpr (HAS_V) ldV.store(sVb[buf], tid);
+    if constexpr (VTILE) ldV.store(sVb[buf], tid);
+    if constexpr (NARROW) {
+      if (tid < BN) sVb[buf][tid][0] = vcol;
+    }
     if constexpr (NEEDN) {
       if (tid < BN) sNb[buf][tid] = nyv;
     }
@@ -577,6 +596,12 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
           pp[1] = lt;
         }
       }
+    } else if constexpr (NARROW) {
+      const T t = F::gsum((wsum[b][0] + wsum[b][1]) + (wsum[b][2] + wsum[b][3]));
+      if (g == 0 && qv[b]) {
+        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow;
+        dst[0] = t;
+      }
     } else if constexpr (CONS == C_MATMUL) {
       if (qv[b]) {
         T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.C;
@@ -626,6 +651,9 @@ hipError_t launch_mfma_kernel(const TileArgs &a, hipStream_t s) {
 template <class T, int METRIC, int CONS, int DP>
 hipError_t mfma_by_tile(const MfmaConfig &c, const TileArgs &a, hipStream_t s) {
   if constexpr (CONS == C_MATMUL || CONS == C_SOFTMAX) {
+    if constexpr (CONS == C_MATMUL) {
+      if (c.cp == 1) return launch_mfma_kernel<T, METRIC, CONS, DP, 1, 1>(a, s);
+    }
     if constexpr (sizeof(T) == 8) {
       if (c.cp == 16) return launch_mfma_kernel<T, METRIC, CONS, DP, 16, 1>(a, s);
     }

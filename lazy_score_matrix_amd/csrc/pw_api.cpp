@@ -168,6 +168,10 @@ bool mfma_eligible(const pw_expr &e, int consumer, int64_t C) {
   if (e.D < 16) return false;
   if (e.stages.size() > 1) return false;
   if (e.stages.size() == 1 && (e.stages[0].kind != ST_AFFINE || e.stages[0].col_vec)) return false;
+  // Value consumers: the matrix cores take V in columns of 16 or 32, so a
+  // narrow V is left to the vector engine unless D is large; a single
+  // column (a weighted row sum) is folded with vector FMAs instead.
+  if (consumer == PW_C_MATMUL && C == 1) return true;
   if ((consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) && C < 16 && e.D < 32) return false;
   return true;
 }
@@ -190,14 +194,14 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     p.family = 1;
     p.mcfg.dp = e.D <= 16 ? 16 : (e.D <= 32 ? 32 : 64);
     const bool value = consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL;
-    if (!value) p.mcfg.cp = 1;
+    if (!value || (consumer == PW_C_MATMUL && C == 1)) p.mcfg.cp = 1;
     else if (e.dtype == PW_F32) p.mcfg.cp = C <= 32 ? 32 : 64;
     else p.mcfg.cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
     p.mcfg.kl = consumer == PW_C_TOPK ? (k <= 16 ? 16 : 64) : 1;
     p.bm = mfma_bm(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
-    p.bn = mfma_bn(e.dtype, consumer);
+    p.bn = mfma_bn(e.dtype, consumer, p.mcfg.cp);
     p.chunk = (int)std::min<int64_t>(C, p.mcfg.cp);
-    target_wgs = (int64_t)kTargetCUs * mfma_wgs_per_cu(e.dtype, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
+    target_wgs = (int64_t)kTargetCUs * mfma_wgs_per_cu(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
   } else {
     p.vcfg.dtile = valu_dtile(e.D);
     if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {

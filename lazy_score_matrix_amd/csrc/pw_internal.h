@@ -138,16 +138,21 @@ struct MfmaConfig {
 // tile among 8 waves instead did not pay.
 constexpr bool mfma_wide(int dtype, int dp, int cp, int kl) { return kl > 16 || (dtype == 1 && (dp > 16 || cp > 16)); }
 constexpr int mfma_waves(int, int, int, int) { return 4; }
-constexpr int mfma_wgs_per_cu(int dtype, int dp, int cp, int kl) { return mfma_wide(dtype, dp, cp, kl) ? 1 : 2; }
+// Workgroups per CU (the launch bound): wide register states run one, the
+// rest two (three measured no faster for the single-column product).
+constexpr int mfma_wgs_per_cu(int dtype, int consumer, int dp, int cp, int kl) {
+  return (void)consumer, mfma_wide(dtype, dp, cp, kl) ? 1 : 2;
+}
 // Query rows per workgroup: waves x QB blocks x (32 float / 16 double)
 // queries; double uses QB = 2 except for top-k.
 constexpr int mfma_bm(int dtype, int consumer, int dp, int cp, int kl) {
   return mfma_waves(dtype, dp, cp, kl) * ((dtype == 1 && consumer != C_TOPK) ? 2 : 1) * (dtype == 0 ? 32 : 16);
 }
 // Keys per staged tile: float 128 (4 sub-blocks of 32) except for the value
-// consumers, whose prefetched V tile needs the registers (64); double 64.
-constexpr int mfma_bn(int dtype, int consumer) {
-  return (dtype == 0 && consumer != C_MATMUL && consumer != C_SOFTMAX) ? 128 : 64;
+// consumers with a V tile (cp > 1), whose prefetched tile needs the
+// registers (64); double 64.
+constexpr int mfma_bn(int dtype, int consumer, int cp) {
+  return (dtype == 0 && ((consumer != C_MATMUL && consumer != C_SOFTMAX) || cp == 1)) ? 128 : 64;
 }
 // Lane groups per query in the MFMA layouts (float 2, double 4); each keeps
 // its own top-k list, written as a separate partial.

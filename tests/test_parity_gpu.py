@@ -270,6 +270,35 @@ def test_mfma_value_widths(dtype, C, consumer):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("metric", METRICS)
+@pytest.mark.parametrize("D", [16, 17, 64])
+@pytest.mark.parametrize("chain", ["none", "row_affine"])
+def test_mfma_single_column(dtype, metric, D, chain):
+    """A kernel product with one value column (a weighted row sum) runs on
+    the matrix-core engine with the column folded by vector FMAs; N = 300
+    and M = 333 leave ragged row blocks and tiles."""
+    X, Y, r = _data(1300 + D, 300, 333, D, dtype)
+    w = r.standard_normal((333, 1)).astype(dtype)
+    ops = _linear_scale(metric, D)
+    if chain == "row_affine":
+        ops = ops + [("add_rows", r.standard_normal(300).astype(dtype)), ("weight_rows", (0.5 + r.random(300)).astype(dtype))]
+    e, oe = bind_both(X, Y, metric, _gamma(metric, D), ops)
+    _assert_family(e, "matmul", "mfma", C=1)
+    check_consumer(e, oe, "matmul", V=w, what="mfma single column %s D=%d" % (metric, D))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("M", [1, 127, 128, 129, 5000])
+def test_mfma_single_column_sizes(dtype, M):
+    """Column counts around the 128-key tile and a column split."""
+    X, Y, r = _data(1400 + M, 200, M, 32, dtype)
+    w = r.standard_normal((M, 1)).astype(dtype)
+    e, oe = bind_both(X, Y, "rbf", 1.0 / 32)
+    _assert_family(e, "matmul", "mfma", C=1)
+    check_consumer(e, oe, "matmul", V=w, what="mfma single column M=%d" % M)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
 @pytest.mark.parametrize("k", [1, 10, 16, 17, 64])
 @pytest.mark.parametrize("largest", [False, True])
 def test_mfma_topk(dtype, k, largest):

@@ -41,6 +41,14 @@ OPS = {
     "exp": 6,             # s <- exp(s)
 }
 METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2, "cosine_distances": 3}
+# Masks, given in the same op list (Score Expressions: boolean row/column
+# masks; Task Map, Attention row: causal, band, same_group). A mask drops
+# pairs from every consumer wherever it stands in the list:
+#   ("mask_rows", bool[N]), ("mask_columns", bool[M])
+#   ("causal", d)          keep j - i <= d (d = 0: j <= i)
+#   ("band", (lo, hi))     keep -lo <= j - i <= hi
+#   ("same_group", (g_rows[N], g_cols[M]))   keep g_rows[i] == g_cols[j]
+MASKS = ("mask_rows", "mask_columns", "causal", "band", "same_group")
 
 _lock = threading.Lock()
 _lib = None
@@ -72,6 +80,14 @@ class _CExpr(ctypes.Structure):
         ("op_kind", ctypes.POINTER(ctypes.c_int)),
         ("op_scalar", ctypes.POINTER(ctypes.c_double)),
         ("op_vec", ctypes.POINTER(ctypes.c_void_p)),
+        ("row_mask", ctypes.c_void_p),
+        ("col_mask", ctypes.c_void_p),
+        ("has_upper", ctypes.c_int),
+        ("upper", ctypes.c_int64),
+        ("has_lower", ctypes.c_int),
+        ("lower", ctypes.c_int64),
+        ("group_rows", ctypes.c_void_p),
+        ("group_cols", ctypes.c_void_p),
     ]
 
 
@@ -131,7 +147,7 @@ class Expr:
     ``ops`` is a list of ``(name, arg)`` with name in ``OPS``: ``arg`` is a
     float for "mul"/"add", a length-N array for "add_rows"/"weight_rows", a
     length-M array for "add_columns"/"weight_columns" and ``None`` for "exp"
-    (Score Expressions section).
+    (Score Expressions section), or a mask of ``MASKS``.
     """
 
     def __init__(self, X, Y, metric, gamma=1.0, ops=()):
@@ -150,7 +166,36 @@ class Expr:
         self.real = np.float64 if X.dtype == np.float32 else np.longdouble
         self._keep = []
         kinds, scalars, vecs = [], [], []
+        row_mask = col_mask = groups = None
+        upper = lower = None
         for name, arg in ops:
+            if name in MASKS:
+                if name == "mask_rows":
+                    m = np.asarray(arg, dtype=bool).reshape(-1)
+                    if m.shape[0] != self.N:
+                        raise ValueError("mask_rows needs %d values" % self.N)
+                    row_mask = m if row_mask is None else (row_mask & m)
+                elif name == "mask_columns":
+                    m = np.asarray(arg, dtype=bool).reshape(-1)
+                    if m.shape[0] != self.M:
+                        raise ValueError("mask_columns needs %d values" % self.M)
+                    col_mask = m if col_mask is None else (col_mask & m)
+                elif name == "causal":
+                    d = 0 if arg is None else int(arg)
+                    upper = d if upper is None else min(upper, d)
+                elif name == "band":
+                    lo, hi = int(arg[0]), int(arg[1])
+                    upper = hi if upper is None else min(upper, hi)
+                    lower = lo if lower is None else min(lower, lo)
+                else:
+                    if groups is not None:
+                        raise ValueError("one same_group mask per expression")
+                    gr = np.ascontiguousarray(np.asarray(arg[0], dtype=np.int64).reshape(-1))
+                    gc = np.ascontiguousarray(np.asarray(arg[1], dtype=np.int64).reshape(-1))
+                    if gr.shape[0] != self.N or gc.shape[0] != self.M:
+                        raise ValueError("same_group needs %d row and %d column groups" % (self.N, self.M))
+                    groups = (gr, gc)
+                continue
             kinds.append(OPS[name])
             if name in ("mul", "add"):
                 scalars.append(float(arg))
@@ -170,10 +215,25 @@ class Expr:
         self._kinds = (ctypes.c_int * max(nops, 1))(*kinds)
         self._scalars = (ctypes.c_double * max(nops, 1))(*scalars)
         self._vecs = (ctypes.c_void_p * max(nops, 1))(*vecs)
+        masks = []
+        for m in (row_mask, col_mask):
+            m = None if m is None else np.ascontiguousarray(m.astype(np.uint8))
+            masks.append(m)
+            self._keep.append(m)
+        if groups is not None:
+            self._keep.extend(groups)
+        self.masked = any(m is not None for m in masks) or upper is not None or lower is not None or \
+            groups is not None
         self._c = _CExpr(
             0 if X.dtype == np.float32 else 1, METRICS[metric], self.gamma,
             self.X.ctypes.data, self.N, ldx, self.Y.ctypes.data, self.M, ldy, self.D,
-            nops, self._kinds, self._scalars, self._vecs)
+            nops, self._kinds, self._scalars, self._vecs,
+            None if masks[0] is None else masks[0].ctypes.data,
+            None if masks[1] is None else masks[1].ctypes.data,
+            int(upper is not None), 0 if upper is None else upper,
+            int(lower is not None), 0 if lower is None else lower,
+            None if groups is None else groups[0].ctypes.data,
+            None if groups is None else groups[1].ctypes.data)
 
     def _rows(self, rows):
         if rows is None:
@@ -198,7 +258,8 @@ def _rp(r):
 
 
 def scores(e: Expr, rows=None):
-    """Dense scores s_ij for the listed rows (Score Expressions)."""
+    """Dense scores s_ij for the listed rows (Score Expressions); masks are
+    not applied here (they act in the consumers)."""
     lib = _load()
     r, n = e._rows(rows)
     out, mag = e._out(n, e.M)
@@ -251,7 +312,7 @@ def topk(e: Expr, k, largest=False, extra=0, rows=None):
     """Row top-k by value, ties by lowest index (Task Map, k-NN and Chamfer rows).
 
     Returns ``(values, indices, mag)`` with ``k + extra`` positions per row;
-    positions past M hold NaN / -1.
+    positions past the row's kept pairs hold NaN / -1.
     """
     lib = _load()
     r, n = e._rows(rows)

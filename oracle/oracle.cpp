@@ -14,6 +14,11 @@
 //   * the per-pair score arithmetic applied left to right: scalar multiply
 //     and add, add_rows / add_columns, weight_rows / weight_columns and exp
 //     (Score Expressions section);
+//   * masks that drop pairs from every consumer (Score Expressions: boolean
+//     row and column masks; Task Map, Attention row and the note below the
+//     Score Expressions example: the pair masks causal, band and
+//     same_group). A dropped pair takes no part in the reduction, wherever
+//     the mask stands in the op list;
 //   * five consumers that reduce each row over j: the kernel product S@V and
 //     its row-mass column (Task Map, Nadaraya-Watson row), the displacement
 //     sum_j s_ij (y_j - x_i) (SVGD section), the row log-sum-exp with an
@@ -73,6 +78,15 @@ typedef struct {
   const int *op_kind;        // n_ops entries, see OP_* below
   const double *op_scalar;   // n_ops entries (MUL / ADD)
   const void *const *op_vec; // n_ops entries, host vectors in dtype (ROWS: N, COLS: M)
+  // Masks (all optional). A pair (i, j) is kept iff every present mask keeps it.
+  const unsigned char *row_mask;  // N entries: row i kept iff nonzero
+  const unsigned char *col_mask;  // M entries: column j kept iff nonzero
+  int has_upper;                  // kept iff j - i <= upper (causal: upper = 0)
+  int64_t upper;
+  int has_lower;                  // kept iff i - j <= lower
+  int64_t lower;
+  const int64_t *group_rows;      // N entries; with group_cols: kept iff
+  const int64_t *group_cols;      // group_rows[i] == group_cols[j] (M entries)
 } oracle_expr;
 
 }  // extern "C"
@@ -98,6 +112,16 @@ struct Expr {
   R x(int64_t i, int64_t d) const { return (R)X[i * e.ldx + d]; }
   R y(int64_t j, int64_t d) const { return (R)Y[j * e.ldy + d]; }
   R vec(int k, int64_t idx) const { return (R) static_cast<const T *>(e.op_vec[k])[idx]; }
+
+  // Whether pair (i, j) survives the masks.
+  bool keep(int64_t i, int64_t j) const {
+    if (e.row_mask && !e.row_mask[i]) return false;
+    if (e.col_mask && !e.col_mask[j]) return false;
+    if (e.has_upper && j - i > e.upper) return false;
+    if (e.has_lower && i - j > e.lower) return false;
+    if (e.group_rows && e.group_rows[i] != e.group_cols[j]) return false;
+    return true;
+  }
 
   // Score of pair (i, j) with its error magnitude.
   R score(int64_t i, int64_t j, R *mu_out) const {
@@ -164,6 +188,7 @@ using RealOf = typename std::conditional<std::is_same<T, float>::value, double, 
 
 int64_t row_at(const int64_t *rows, int64_t r) { return rows ? rows[r] : r; }
 
+// Dense scores (masks are not applied: they act in the consumers).
 template <class T>
 void do_scores(const oracle_expr &ex, const int64_t *rows, int64_t n_rows, RealOf<T> *out, RealOf<T> *mag) {
   using R = RealOf<T>;
@@ -190,6 +215,7 @@ void do_matmul(const oracle_expr &ex, const T *V, int64_t C, int64_t ldv, const 
     int64_t i = row_at(rows, r);
     std::vector<R> acc(C, 0), m(C, 0);
     for (int64_t j = 0; j < ex.M; ++j) {
+      if (!E.keep(i, j)) continue;
       R mu;
       R s = E.score(i, j, &mu);
       for (int64_t c = 0; c < C; ++c) {
@@ -216,6 +242,7 @@ void do_displacement(const oracle_expr &ex, const int64_t *rows, int64_t n_rows,
     int64_t i = row_at(rows, r);
     std::vector<R> acc(D, 0), m(D, 0);
     for (int64_t j = 0; j < ex.M; ++j) {
+      if (!E.keep(i, j)) continue;
       R mu;
       R s = E.score(i, j, &mu);
       for (int64_t d = 0; d < D; ++d) {
@@ -246,6 +273,7 @@ void do_logsumexp(const oracle_expr &ex, int exclude_self, const int64_t *rows, 
       int64_t n = 0;
       for (int64_t j = 0; j < ex.M; ++j) {
         if (exclude_self && j == i) continue;
+        if (!E.keep(i, j)) continue;
         s[n] = E.score(i, j, &mu[n]);
         ++n;
       }
@@ -276,29 +304,38 @@ void do_softmax_matmul(const oracle_expr &ex, const T *V, int64_t C, int64_t ldv
 #pragma omp parallel
   {
     std::vector<R> s(ex.M), mu(ex.M), acc(C), av(C), apv(C);
+    std::vector<int64_t> jx(ex.M);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < n_rows; ++r) {
       int64_t i = row_at(rows, r);
-      if (ex.M == 0) {
+      // The row's kept columns (all of them without masks).
+      int64_t n = 0;
+      for (int64_t j = 0; j < ex.M; ++j) {
+        if (!E.keep(i, j)) continue;
+        s[n] = E.score(i, j, &mu[n]);
+        jx[n] = j;
+        ++n;
+      }
+      if (n == 0) {
         for (int64_t c = 0; c < C; ++c) out[r * C + c] = mag[r * C + c] = 0;
         continue;
       }
-      for (int64_t j = 0; j < ex.M; ++j) s[j] = E.score(i, j, &mu[j]);
       R m = s[0];
-      for (int64_t j = 1; j < ex.M; ++j) m = std::max(m, s[j]);
+      for (int64_t t = 1; t < n; ++t) m = std::max(m, s[t]);
       R l = 0;
-      for (int64_t j = 0; j < ex.M; ++j) l += rexp(s[j] - m);
+      for (int64_t t = 0; t < n; ++t) l += rexp(s[t] - m);
       std::fill(acc.begin(), acc.end(), (R)0);
       std::fill(av.begin(), av.end(), (R)0);
       std::fill(apv.begin(), apv.end(), (R)0);
       R pmu = 0;
-      for (int64_t j = 0; j < ex.M; ++j) {
-        R p = rexp(s[j] - m) / l;
-        pmu += p * mu[j];
+      for (int64_t t = 0; t < n; ++t) {
+        const int64_t j = jx[t];
+        R p = rexp(s[t] - m) / l;
+        pmu += p * mu[t];
         for (int64_t c = 0; c < C; ++c) {
           R v = (R)V[j * ldv + c];
           acc[c] += p * v;
-          av[c] += p * (1 + mu[j]) * std::fabs(v);
+          av[c] += p * (1 + mu[t]) * std::fabs(v);
           apv[c] += p * std::fabs(v);
         }
       }
@@ -310,30 +347,34 @@ void do_softmax_matmul(const oracle_expr &ex, const T *V, int64_t C, int64_t ldv
   }
 }
 
-// Row top-k: the row's (s_ij, j) ordered by value (ascending, or descending
-// when `largest`), equal values by ascending j; the first kk = k + extra kept.
+// Row top-k: the row's kept (s_ij, j) ordered by value (ascending, or
+// descending when `largest`), equal values by ascending j; the first
+// kk = k + extra are returned, positions past the kept count as NaN / -1.
 template <class T>
 void do_topk(const oracle_expr &ex, int kk, int largest, const int64_t *rows, int64_t n_rows, RealOf<T> *values,
              int64_t *indices, RealOf<T> *mag) {
   using R = RealOf<T>;
   Expr<T, R> E(ex);
   struct Entry { R v; R mu; int64_t j; };
-  const int64_t keep = std::min<int64_t>(kk, ex.M);
 #pragma omp parallel
   {
     std::vector<Entry> buf(ex.M);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < n_rows; ++r) {
       int64_t i = row_at(rows, r);
+      int64_t n = 0;
       for (int64_t j = 0; j < ex.M; ++j) {
-        buf[j].v = E.score(i, j, &buf[j].mu);
-        buf[j].j = j;
+        if (!E.keep(i, j)) continue;
+        buf[n].v = E.score(i, j, &buf[n].mu);
+        buf[n].j = j;
+        ++n;
       }
+      const int64_t keep = std::min<int64_t>(kk, n);
       auto before = [largest](const Entry &a, const Entry &b) {
         if (a.v != b.v) return largest ? (a.v > b.v) : (a.v < b.v);
         return a.j < b.j;
       };
-      std::partial_sort(buf.begin(), buf.begin() + keep, buf.end(), before);
+      std::partial_sort(buf.begin(), buf.begin() + keep, buf.begin() + n, before);
       for (int64_t p = 0; p < kk; ++p) {
         if (p < keep) {
           values[r * kk + p] = buf[p].v;

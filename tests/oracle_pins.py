@@ -471,4 +471,141 @@ def pin_row_subset_matches_full():
     _close(lp, np.asarray(lf)[rows], rtol=0, atol=0, what="row subset lse")
 
 
+# ---------------------------------------------------------------- masks
+# A mask drops pairs from the reduction (Score Expressions: boolean row and
+# column masks; Task Map, Attention row: causal, band, same_group). The pins
+# derive each masked result from unmasked oracle calls on the surviving
+# columns, or from torch's own triangular routines, never from the mask
+# predicate itself.
+
+def _consumers(e, V, rows=None):
+    """Every consumer's result on expression e (top-k: 3 smallest, 2 extra)."""
+    return {
+        "matmul": np.asarray(oracle.matmul(e, V, rows)[0], np.float64),
+        "displacement": np.asarray(oracle.displacement(e, rows)[0], np.float64),
+        "logsumexp": np.asarray(oracle.logsumexp(e, rows=rows)[0], np.float64),
+        "softmax_matmul": np.asarray(oracle.softmax_matmul(e, V, rows)[0], np.float64),
+        "topk": oracle.topk(e, 3, extra=2, rows=rows),
+    }
+
+
+def _check_row_against_subset(got, i, ref, cols):
+    """Row i of a masked result equals the unmasked result over the kept
+    columns `cols` (ref evaluated on Y[cols], V[cols]); top-k indices map
+    back through cols."""
+    for name in ("matmul", "displacement", "logsumexp", "softmax_matmul"):
+        _close(got[name][i], ref[name][0], rtol=1e-12, atol=1e-12, what="%s row %d" % (name, i))
+    gv, gi, _ = got["topk"]
+    rv, ri, _ = ref["topk"]
+    mapped = np.where(ri[0] >= 0, np.asarray(cols)[np.maximum(ri[0], 0)], -1)
+    assert np.array_equal(gi[i], mapped), ("topk row", i, gi[i], mapped)
+    _close(np.nan_to_num(np.asarray(gv[i], np.float64), nan=7.0), np.nan_to_num(np.asarray(rv[0], np.float64), nan=7.0),
+           rtol=1e-14, atol=0, what="topk values row %d" % i)
+
+
+def _subset_ref(X, Y, V, metric, gamma, ops, i, cols):
+    e = oracle.Expr(X[i:i + 1], Y[cols], metric, gamma=gamma, ops=ops)
+    return _consumers(e, V[cols])
+
+
+def pin_mask_columns_is_column_subset():
+    """A column mask equals evaluating on the kept columns only."""
+    for dt in DTYPES:
+        X, Y = _inputs(100, 6, 11, 3, dt)
+        V = _rng(101).standard_normal((11, 2)).astype(dt)
+        keep = np.array([1, 0, 1, 1, 0, 0, 1, 1, 0, 1, 1], bool)
+        cols = np.nonzero(keep)[0]
+        got = _consumers(oracle.Expr(X, Y, "rbf", 0.4, [("mask_columns", keep)]), V)
+        for i in range(6):
+            _check_row_against_subset(got, i, _subset_ref(X, Y, V, "rbf", 0.4, [], i, cols), cols)
+
+
+def pin_mask_rows_empty_rows():
+    """A row mask leaves kept rows unchanged and gives masked rows the
+    empty-row results: zero sums, -inf log-sum-exp, zero softmax product and
+    top-k positions NaN / -1."""
+    X, Y = _inputs(102, 5, 7, 2, np.float64)
+    V = _rng(103).standard_normal((7, 2))
+    keep = np.array([1, 0, 1, 0, 1], bool)
+    ops = [("mul", -1.0)]
+    got = _consumers(oracle.Expr(X, Y, "sqeuclidean", ops=ops + [("mask_rows", keep)]), V)
+    ref = _consumers(oracle.Expr(X, Y, "sqeuclidean", ops=ops), V)
+    for i in range(5):
+        if keep[i]:
+            for name in ("matmul", "displacement", "logsumexp", "softmax_matmul"):
+                _close(got[name][i], ref[name][i], rtol=0, atol=0, what=name)
+            assert np.array_equal(got["topk"][1][i], ref["topk"][1][i])
+        else:
+            assert np.all(got["matmul"][i] == 0) and np.all(got["displacement"][i] == 0)
+            assert np.all(got["softmax_matmul"][i] == 0) and np.isneginf(got["logsumexp"][i])
+            assert np.all(got["topk"][1][i] == -1) and np.all(np.isnan(np.asarray(got["topk"][0][i], np.float64)))
+
+
+def pin_causal_is_prefix():
+    """causal(d): row i reduces over the prefix of columns j <= i + d
+    (the rows whose prefix is empty get the empty-row results)."""
+    X, Y = _inputs(104, 9, 9, 3, np.float32)
+    V = _rng(105).standard_normal((9, 3)).astype(np.float32)
+    for d in (0, 2, -3):
+        got = _consumers(oracle.Expr(X, Y, "linear", ops=[("mul", 0.5), ("causal", d)]), V)
+        for i in range(9):
+            cols = np.arange(0, min(9, i + d + 1))
+            if cols.size == 0:
+                assert np.isneginf(got["logsumexp"][i]) and np.all(got["topk"][1][i] == -1)
+                continue
+            _check_row_against_subset(got, i, _subset_ref(X, Y, V, "linear", 1.0, [("mul", 0.5)], i, cols), cols)
+
+
+def pin_band_is_window():
+    """band(lo, hi): row i reduces over the window i - lo <= j <= i + hi."""
+    X, Y = _inputs(106, 8, 12, 2, np.float64)
+    V = _rng(107).standard_normal((12, 2))
+    for lo, hi in ((1, 2), (0, 0), (3, -1)):
+        got = _consumers(oracle.Expr(X, Y, "sqeuclidean", ops=[("band", (lo, hi)), ("mul", -1.0)]), V)
+        for i in range(8):
+            cols = np.arange(max(0, i - lo), min(12, i + hi + 1))
+            if cols.size == 0:
+                continue
+            _check_row_against_subset(got, i, _subset_ref(X, Y, V, "sqeuclidean", 1.0, [("mul", -1.0)], i, cols),
+                                      cols)
+
+
+def pin_same_group_is_block():
+    """same_group: row i reduces over the columns of its own group."""
+    X, Y = _inputs(108, 10, 13, 3, np.float32)
+    V = _rng(109).standard_normal((13, 2)).astype(np.float32)
+    gr = np.array([0, 2, 1, 0, 5, 2, 2, 1, 0, 3])
+    gc = np.array([1, 0, 0, 2, 1, 2, 0, 4, 2, 1, 0, 3, 3])
+    got = _consumers(oracle.Expr(X, Y, "rbf", 0.2, [("same_group", (gr, gc))]), V)
+    for i in range(10):
+        cols = np.nonzero(gc == gr[i])[0]
+        if cols.size == 0:
+            assert np.all(got["matmul"][i] == 0) and np.isneginf(got["logsumexp"][i])
+            continue
+        _check_row_against_subset(got, i, _subset_ref(X, Y, V, "rbf", 0.2, [], i, cols), cols)
+
+
+def pin_masks_vs_torch_triangles():
+    """causal and band against torch.tril / torch.triu applied to dense
+    scores: masked log-sum-exp and softmax(S)@V, several masks combined."""
+    X, Y = _inputs(110, 12, 10, 4, np.float64)
+    V = _rng(111).standard_normal((10, 3))
+    S = dense_scores_torch(X, Y, "linear", ops=[("mul", 0.3)])
+    ones = torch.ones(12, 10, dtype=torch.bool)
+    rows = torch.as_tensor(np.array([1, 1, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1], bool))
+    for masks, K in (
+            ([("causal", 0)], ones.tril(0)),
+            ([("causal", 1), ("band", (2, 5))], ones.tril(1) & ones.triu(-2)),
+            ([("band", (4, 1)), ("mask_rows", rows.numpy())], ones.tril(1) & ones.triu(-4) & rows[:, None])):
+        e = oracle.Expr(X, Y, "linear", ops=[("mul", 0.3)] + masks)
+        Sm = S.masked_fill(~K, float("-inf"))
+        got, want = np.asarray(oracle.logsumexp(e)[0], np.float64), torch.logsumexp(Sm, -1).numpy()
+        assert np.array_equal(np.isneginf(got), np.isneginf(want))
+        fin = np.isfinite(want)
+        _close(got[fin], want[fin], rtol=1e-13, atol=1e-13, what="lse")
+        P = torch.softmax(Sm, -1).nan_to_num(0.0)
+        _close(oracle.softmax_matmul(e, V)[0], (P @ torch.as_tensor(V)).numpy(), rtol=1e-12, atol=1e-13, what="smx")
+        _close(oracle.matmul(e, V)[0], ((S * K) @ torch.as_tensor(V)).numpy(), rtol=1e-12, atol=1e-13, what="mm")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

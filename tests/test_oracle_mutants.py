@@ -35,9 +35,18 @@ MUTANTS = [
     ("displacement_sign", "acc[d] += s * (yd - xd);", "acc[d] += s * (xd - yd);"),
     ("self_pair_misplaced", "if (exclude_self && j == i) continue;", "if (exclude_self && j == i + 1) continue;"),
     ("lse_drops_max", "out[r] = m + rlog(l);", "out[r] = rlog(l);"),
-    ("softmax_unnormalised", "R p = rexp(s[j] - m) / l;", "R p = rexp(s[j] - m);"),
+    ("softmax_unnormalised", "R p = rexp(s[t] - m) / l;", "R p = rexp(s[t] - m);"),
     ("tie_order_reversed", "return a.j < b.j;", "return a.j > b.j;"),
     ("largest_ignored", "return largest ? (a.v > b.v) : (a.v < b.v);", "return (a.v < b.v);"),
+    ("row_mask_ignored", "if (e.row_mask && !e.row_mask[i]) return false;", ""),
+    ("column_mask_by_row", "if (e.col_mask && !e.col_mask[j]) return false;",
+     "if (e.col_mask && !e.col_mask[i % e.M]) return false;"),
+    ("causal_strict", "if (e.has_upper && j - i > e.upper) return false;",
+     "if (e.has_upper && j - i >= e.upper) return false;"),
+    ("band_lower_sign", "if (e.has_lower && i - j > e.lower) return false;",
+     "if (e.has_lower && j - i > e.lower) return false;"),
+    ("group_of_row_index", "e.group_rows[i] != e.group_cols[j]", "e.group_rows[i] != e.group_cols[i % e.M]"),
+    ("softmax_v_by_position", "const int64_t j = jx[t];", "const int64_t j = t;"),
 ]
 
 

@@ -114,7 +114,7 @@ def case_operands(c, arrays):
     """(X, Y, ops) of a case; a transposed case reduces over the rows, so it
     binds (Y, X) with row and column ops swapped."""
     X, Y = arrays[c.x], arrays[c.y]
-    ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+    ops = [(n, workloads.resolve(a, arrays)) for n, a in c.ops]
     if c.transpose:
         X, Y = Y, X
         ops = [(SWAP.get(n, n), a) for n, a in ops]
@@ -190,7 +190,7 @@ def main():
                   e.topk(k, lg, values=vals, indices=idx, workspace=ws))
             outs = (vals, idx)
         calls.append((c, e, fn, outs, C))
-        pairs_per_step += N * M
+        pairs_per_step += c.pairs if c.pairs is not None else N * M
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -242,7 +242,7 @@ def main():
     peak = PEAK_TFLOPS[dtype] if contraction else ALU_PEAK_TFLOPS[dtype]
     kernels = []
     for (c, e, _, _, C), kms in zip(calls, kernel_ms):
-        fl = float(e.N) * e.M * flops_per_pair(c, e.D, C)
+        fl = float(c.pairs if c.pairs is not None else e.N * e.M) * flops_per_pair(c, e.D, C)
         tf = fl / (kms * 1e-3) / 1e12
         kernels.append({"call": c.name, "plan": e.plan(lib_consumer(c), C, c.k), "avg_ms": round(kms, 4),
                         "flops_per_pair": flops_per_pair(c, e.D, C), "tflops": round(tf, 3),
@@ -327,10 +327,13 @@ def cpu_leg(calls, arrays, seconds):
         t0 = time.perf_counter()
         res = run(rows)
         dt = time.perf_counter() - t0
-        total_pairs += len(rows) * oe.M
+        # Masked workloads count the kept pairs (the rows' average share).
+        per_row = (c.pairs / oe.N) if c.pairs is not None else oe.M
+        total_pairs += len(rows) * per_row
         total_s += dt
-        rows_desc.append("%s: %d of %d rows evenly spaced (incl. first and last), all %d columns"
-                         % (c.name, len(rows), oe.N, oe.M))
+        rows_desc.append("%s: %d of %d rows evenly spaced (incl. first and last), %s"
+                         % (c.name, len(rows), oe.N, "all %d columns" % oe.M if c.pairs is None
+                            else "their kept pairs (%.0f per row on average)" % per_row))
         dtype = np.dtype(oe.np_dtype)
         if c.consumer == "topk":
             gv = outs[0].cpu().numpy()[rows]

@@ -72,6 +72,25 @@ typedef enum { PW_LINEAR = 0, PW_SQEUCLIDEAN = 1, PW_RBF = 2, PW_COSINE = 3 } pw
  *   PW_OP_EXP             s <- exp(s)
  * `vec` is a contiguous device array of the bound dtype (NULL for MUL, ADD,
  * EXP); `scalar` is rounded to the bound dtype once. */
+/* Masks drop pairs (i, j) from every consumer, wherever they stand in the
+ * op list (guide, "Score Expressions": boolean row and column masks; Task
+ * Map, Attention row, and the note after the Score Expressions example:
+ * the pair masks causal, band and same_group). A dropped pair takes no part
+ * in the reduction:
+ *   PW_OP_MASK_ROWS       keep row i iff vec[i] != 0     vec: N bytes (uint8)
+ *   PW_OP_MASK_COLUMNS    keep column j iff vec[j] != 0  vec: M bytes (uint8)
+ *   PW_OP_BAND_UPPER      keep iff j - i <= scalar   (causal: scalar = 0)
+ *   PW_OP_BAND_LOWER      keep iff i - j <= scalar   (band(lo, hi) is
+ *                         BAND_LOWER lo and BAND_UPPER hi)
+ *   PW_OP_GROUP_ROWS      row group ids,    vec: N int64_t
+ *   PW_OP_GROUP_COLUMNS   column group ids, vec: M int64_t; with GROUP_ROWS
+ *                         (both or neither): keep iff g_rows[i] == g_cols[j]
+ * Band scalars are integers (|scalar| <= 2^53). At most one mask of each
+ * vector kind; several band bounds of one kind keep the tightest. A row whose
+ * pairs are all dropped gets the empty-row result of its consumer (zeros,
+ * -inf log-sum-exp, zero softmax product, top-k positions NaN / -1). Whole
+ * tiles outside a band, or whose row and column group ranges are disjoint,
+ * are skipped. */
 typedef enum {
   PW_OP_MUL = 0,
   PW_OP_ADD = 1,
@@ -79,17 +98,23 @@ typedef enum {
   PW_OP_ADD_COLUMNS = 3,
   PW_OP_WEIGHT_ROWS = 4,
   PW_OP_WEIGHT_COLUMNS = 5,
-  PW_OP_EXP = 6
+  PW_OP_EXP = 6,
+  PW_OP_MASK_ROWS = 7,
+  PW_OP_MASK_COLUMNS = 8,
+  PW_OP_BAND_UPPER = 9,
+  PW_OP_BAND_LOWER = 10,
+  PW_OP_GROUP_ROWS = 11,
+  PW_OP_GROUP_COLUMNS = 12
 } pw_op_kind;
 
-#define PW_MAX_OPS 8
+#define PW_MAX_OPS 16
 #define PW_MAX_D 64
 #define PW_MAX_K 64
 
 typedef struct {
   int kind;          /* pw_op_kind */
-  double scalar;     /* MUL, ADD */
-  const void *vec;   /* ROWS / COLUMNS ops: device vector, borrowed */
+  double scalar;     /* MUL, ADD, BAND_UPPER, BAND_LOWER */
+  const void *vec;   /* ROWS / COLUMNS ops and masks: device vector, borrowed */
 } pw_op;
 
 typedef enum {
@@ -111,7 +136,10 @@ typedef enum {
  *   Y       [M, ldy] device matrix, rows are y_j;   M >= 0, ldy >= D
  *           X and Y may be the same pointer (scores of a set with itself)
  *   D       features, 1..PW_MAX_D (PW_ERR_UNSUPPORTED outside that range)
- *   ops     n_ops entries (0..PW_MAX_OPS), copied; op vectors are borrowed
+ *   ops     n_ops entries (0..PW_MAX_OPS), copied; op vectors are borrowed.
+ *           PW_ERR_UNSUPPORTED when the score arithmetic needs more than 8
+ *           fused stages; PW_ERR_INVALID for a second mask of one vector
+ *           kind or group ids on one side only
  * X and Y must be aligned to their element size. */
 int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
             const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops);

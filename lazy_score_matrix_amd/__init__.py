@@ -11,7 +11,11 @@ There is no CPU fallback: if the library is missing, every call raises.
 
 Op names follow the guide's "Score Expressions" section: ("mul", c),
 ("add", c), ("add_rows", a), ("add_columns", b), ("weight_rows", w),
-("weight_columns", u), ("exp", None).
+("weight_columns", u), ("exp", None). Masks (``masks`` module) drop pairs
+from every consumer: ("mask_rows", keep[N]), ("mask_columns", keep[M]),
+("band_upper", d), ("band_lower", d), ("group_rows", g[N]),
+("group_columns", g[M]), and the shorthands ("causal", d), ("band", (lo, hi))
+and ("same_group", (g_rows, g_cols)).
 """
 from __future__ import annotations
 
@@ -29,9 +33,16 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "pw.h")
 PW_OK, PW_ERR_INVALID, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP = 0, -1, -2, -3, -4
 DTYPES = {torch.float32: 0, torch.float64: 1}
 METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2, "cosine_distances": 3, "cosine": 3}
-OPS = {"mul": 0, "add": 1, "add_rows": 2, "add_columns": 3, "weight_rows": 4, "weight_columns": 5, "exp": 6}
+OPS = {"mul": 0, "add": 1, "add_rows": 2, "add_columns": 3, "weight_rows": 4, "weight_columns": 5, "exp": 6,
+       "mask_rows": 7, "mask_columns": 8, "band_upper": 9, "band_lower": 10, "group_rows": 11, "group_columns": 12}
+MASK_OPS = ("mask_rows", "mask_columns", "band_upper", "band_lower", "group_rows", "group_columns")
+# Row and column roles of every op, swapped by the transposed view.
+_SWAP = {"add_rows": "add_columns", "add_columns": "add_rows", "weight_rows": "weight_columns",
+         "weight_columns": "weight_rows", "mask_rows": "mask_columns", "mask_columns": "mask_rows",
+         "band_upper": "band_lower", "band_lower": "band_upper", "group_rows": "group_columns",
+         "group_columns": "group_rows"}
 CONSUMERS = {"matmul": 0, "displacement": 1, "logsumexp": 2, "softmax_matmul": 3, "topk": 4}
-MAX_OPS, MAX_D, MAX_K = 8, 64, 64
+MAX_OPS, MAX_D, MAX_K = 16, 64, 64
 
 
 class PwError(RuntimeError):
@@ -103,6 +114,22 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def expand_ops(ops):
+    """Op list with the mask shorthands causal / band / same_group expanded."""
+    out = []
+    for op in ops:
+        name, arg = op
+        if name == "causal":
+            out.append(("band_upper", 0 if arg is None else int(arg)))
+        elif name == "band":
+            out += [("band_lower", int(arg[0])), ("band_upper", int(arg[1]))]
+        elif name == "same_group":
+            out += [("group_rows", arg[0]), ("group_columns", arg[1])]
+        else:
+            out.append((name, arg))
+    return out
+
+
 def _rows(t, name):
     if t.dim() != 2:
         raise ValueError("%s must be 2-D" % name)
@@ -132,14 +159,24 @@ class LazyScores:
             raise ValueError("X and Y feature dims differ")
         ldx, ldy = _rows(X, "X"), _rows(Y, "Y")
         self._keep = []
-        ops = list(ops)
+        ops = expand_ops(ops)
         arr = (_Op * max(len(ops), 1))()
         for t, (name, arg) in enumerate(ops):
             if name not in OPS:
                 raise ValueError("unknown op %r" % name)
             arr[t].kind = OPS[name]
-            if name in ("mul", "add"):
+            if name in ("mul", "add", "band_upper", "band_lower"):
                 arr[t].scalar = float(arg)
+            elif name in ("mask_rows", "mask_columns", "group_rows", "group_columns"):
+                v = arg
+                n = self.N if name.endswith("_rows") else self.M
+                want = (torch.bool, torch.uint8) if name.startswith("mask") else (torch.int64,)
+                if (not torch.is_tensor(v) or v.dtype not in want or v.device != self.device or v.numel() != n
+                        or not v.is_contiguous()):
+                    raise ValueError("%s needs a contiguous %s vector of %d elements on %s"
+                                     % (name, " or ".join(str(w) for w in want), n, self.device))
+                self._keep.append(v)
+                arr[t].vec = v.data_ptr()
             elif name != "exp":
                 v = arg
                 n = self.N if name.endswith("_rows") else self.M
@@ -188,8 +225,10 @@ class LazyScores:
         return _rows(V, "V")
 
     # -- consumers ------------------------------------------------------
-    def matmul(self, V: torch.Tensor, out=None, workspace=None) -> torch.Tensor:
-        """out[i, c] = sum_j S[i, j] V[j, c]."""
+    def matmul(self, V: torch.Tensor, out=None, workspace=None, mask=None) -> torch.Tensor:
+        """out[i, c] = sum_j S[i, j] V[j, c] over the kept pairs."""
+        if mask is not None:
+            return self.masked(mask).matmul(V, out, workspace)
         ldv = self._value(V, "matmul")
         C = V.shape[1]
         out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
@@ -200,8 +239,11 @@ class LazyScores:
 
     __matmul__ = matmul
 
-    def softmax_matmul(self, V: torch.Tensor, out=None, workspace=None) -> torch.Tensor:
-        """out[i, c] = sum_j softmax_j(S[i, :])[j] V[j, c]."""
+    def softmax_matmul(self, V: torch.Tensor, out=None, workspace=None, mask=None) -> torch.Tensor:
+        """out[i, c] = sum_j softmax_j(S[i, :])[j] V[j, c], over the pairs
+        `mask` (op entries, e.g. masks.causal()) and the bound masks keep."""
+        if mask is not None:
+            return self.masked(mask).softmax_matmul(V, out, workspace)
         ldv = self._value(V, "softmax_matmul")
         C = V.shape[1]
         out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
@@ -210,24 +252,32 @@ class LazyScores:
                                           ws.data_ptr(), nb, _stream(self.device)), "pw_softmax_matmul")
         return out
 
-    def displacement(self, out=None, workspace=None) -> torch.Tensor:
-        """out[i, d] = sum_j S[i, j] (Y[j, d] - X[i, d])."""
+    def displacement(self, out=None, workspace=None, mask=None) -> torch.Tensor:
+        """out[i, d] = sum_j S[i, j] (Y[j, d] - X[i, d]) over the kept pairs."""
+        if mask is not None:
+            return self.masked(mask).displacement(out, workspace)
         out = torch.empty(self.N, self.D, dtype=self.dtype, device=self.device) if out is None else out
         ws, nb = self._ws(workspace, "displacement")
         check(self._lib.pw_displacement(self._h, out.data_ptr(), _rows(out, "out"), ws.data_ptr(), nb,
                                         _stream(self.device)), "pw_displacement")
         return out
 
-    def logsumexp(self, exclude_self: bool = False, out=None, workspace=None) -> torch.Tensor:
-        """out[i] = log sum_j exp(S[i, j]), optionally without j == i."""
+    def logsumexp(self, exclude_self: bool = False, out=None, workspace=None, mask=None) -> torch.Tensor:
+        """out[i] = log sum_j exp(S[i, j]) over the kept pairs, optionally
+        without j == i (-inf for a row with none)."""
+        if mask is not None:
+            return self.masked(mask).logsumexp(exclude_self, out, workspace)
         out = torch.empty(self.N, dtype=self.dtype, device=self.device) if out is None else out
         ws, nb = self._ws(workspace, "logsumexp")
         check(self._lib.pw_logsumexp(self._h, int(bool(exclude_self)), out.data_ptr(), ws.data_ptr(), nb,
                                      _stream(self.device)), "pw_logsumexp")
         return out
 
-    def topk(self, k: int, largest: bool = False, values=None, indices=None, workspace=None):
-        """The k first pairs of each row by (value, index): values and int64 indices [N, k]."""
+    def topk(self, k: int, largest: bool = False, values=None, indices=None, workspace=None, mask=None):
+        """The k first kept pairs of each row by (value, index): values and
+        int64 indices [N, k]; positions past a row's kept pairs hold NaN / -1."""
+        if mask is not None:
+            return self.masked(mask).topk(k, largest, values, indices, workspace)
         values = torch.empty(self.N, k, dtype=self.dtype, device=self.device) if values is None else values
         indices = torch.empty(self.N, k, dtype=torch.int64, device=self.device) if indices is None else indices
         ws, nb = self._ws(workspace, "topk", 0, k)
@@ -236,14 +286,23 @@ class LazyScores:
         return values, indices
 
     # -- views and derived reductions ----------------------------------
+    def masked(self, mask) -> "LazyScores":
+        """This score with more masks (op entries from the masks module)."""
+        mask = [mask] if isinstance(mask, tuple) else list(mask)
+        return LazyScores(self.X, self.Y, self.metric, self.gamma, list(self.ops) + mask)
+
+    def mask_rows(self, keep) -> "LazyScores":
+        return self.masked([("mask_rows", keep)])
+
+    def mask_columns(self, keep) -> "LazyScores":
+        return self.masked([("mask_columns", keep)])
+
     @property
     def T(self) -> "LazyScores":
         """The transposed score S^T[j, i] = S[i, j] (Y and X swapped, row and
-        column ops swapped; every built-in metric is symmetric). Column
-        reductions such as min(-2) are row reductions of this view."""
-        swap = {"add_rows": "add_columns", "add_columns": "add_rows",
-                "weight_rows": "weight_columns", "weight_columns": "weight_rows"}
-        ops = [(swap.get(n, n), a) for n, a in self.ops]
+        column ops and masks swapped; every built-in metric is symmetric).
+        Column reductions such as min(-2) are row reductions of this view."""
+        ops = [(_SWAP.get(n, n), a) for n, a in self.ops]
         return LazyScores(self.Y, self.X, self.metric, self.gamma, ops)
 
     def min(self, dim: int = -1):
@@ -277,8 +336,16 @@ class LazyScores:
             return self.T.mean(-1)
         if self.M == 0:
             return torch.full((self.N,), float("nan"), dtype=self.dtype, device=self.device)
+        masks = [(n, a) for n, a in self.ops if n in MASK_OPS]
+        if masks:
+            # Divide by each row's kept count: a second product whose score is 1.
+            ones = LazyScores(self.X, self.Y, "linear", 1.0, [("mul", 0.0), ("add", 1.0)] + masks)
+            return self.sum(-1) / ones.sum(-1)
         scaled = LazyScores(self.X, self.Y, self.metric, self.gamma, list(self.ops) + [("mul", 1.0 / self.M)])
         return scaled.sum(-1)
+
+
+from . import masks  # noqa: E402  (pair-mask helpers)
 
 
 def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()) -> LazyScores:

@@ -59,6 +59,86 @@ hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// Group ranges for the same_group mask: min and max id of each block of
+// `block` consecutive entries (a row block, or a key tile), so the tile
+// kernels can skip pairs of blocks whose ranges are disjoint. One wave per
+// block: lanes read consecutive entries, then a butterfly reduction.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void group_ranges_kernel(const int64_t *__restrict__ g, int64_t n, int block,
+                                                           int64_t *__restrict__ out, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= nblocks) return;  // whole waves leave together
+  const int64_t e0 = b * block, e1 = min(n, e0 + block);
+  long long lo = g[e0], hi = g[e0];
+  for (int64_t e = e0 + lane; e < e1; e += 64) {
+    const long long v = g[e];
+    lo = min(lo, v);
+    hi = max(hi, v);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    lo = min(lo, (long long)__shfl_xor(lo, sh, 64));
+    hi = max(hi, (long long)__shfl_xor(hi, sh, 64));
+  }
+  if (lane == 0) {
+    out[2 * b] = lo;
+    out[2 * b + 1] = hi;
+  }
+}
+
+hipError_t launch_group_ranges(const int64_t *g, int64_t n, int block, int64_t *out, hipStream_t s) {
+  const int64_t nb = (n + block - 1) / block;
+  if (nb == 0) return hipSuccess;
+  dim3 grid((unsigned)((nb + 3) / 4)), block_dim(256);
+  hipLaunchKernelGGL(group_ranges_kernel, grid, block_dim, 0, s, g, n, block, out, nb);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Spans of kept tiles: one workgroup per row block; its threads classify
+// the key tiles with the tile kernels' own rule and reduce the first and the
+// end column of the tiles not skipped. Runs after the group ranges it reads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tile_spans_kernel(const MaskArgs m, int64_t N, int64_t M, int bm, int bn,
+                                                         int64_t *__restrict__ out) {
+  __shared__ unsigned long long s_first, s_end;
+  const int rb = blockIdx.x;
+  if (threadIdx.x == 0) {
+    s_first = ~0ull;
+    s_end = 0;
+  }
+  __syncthreads();
+  const int64_t r0 = (int64_t)rb * bm, r1 = min(N, r0 + bm) - 1;
+  const int64_t tiles = (M + bn - 1) / bn;
+  unsigned long long first = ~0ull, end = 0;
+  for (int64_t t = threadIdx.x; t < tiles; t += 256) {
+    const int64_t j0 = t * bn, j1 = min(M, j0 + bn) - 1;
+    if (tile_class(m, r0, r1, j0, j1, rb, t) == TILE_SKIP) continue;
+    first = min(first, (unsigned long long)j0);
+    end = max(end, (unsigned long long)(j1 + 1));
+  }
+  if (first != ~0ull) {
+    atomicMin(&s_first, first);
+    atomicMax(&s_end, end);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const bool none = s_first == ~0ull;
+    out[2 * rb] = none ? 0 : (int64_t)s_first;
+    out[2 * rb + 1] = none ? 0 : (int64_t)s_end;
+  }
+}
+
+hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, int bn, int n_rb, int64_t *out,
+                             hipStream_t s) {
+  if (n_rb == 0) return hipSuccess;
+  dim3 grid((unsigned)n_rb), block(256);
+  hipLaunchKernelGGL(tile_spans_kernel, grid, block, 0, s, m, N, M, bm, bn, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Row norms |x_i|^2 for the kernels that evaluate distances through the
 // expansion |x|^2 + |y|^2 - 2 x.y. L consecutive lanes share a row and read
 // consecutive features, so a wave reads whole rows contiguously; the L
@@ -174,7 +254,7 @@ __global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
   for (int p = 0; p < KL; ++p)
     if (p < a.k) {
       v[p] = list[p].value(a.largest);
-      ix[p] = (int64_t)list[p].index();
+      ix[p] = list[p].out_index();
     }
 }
 

@@ -115,6 +115,8 @@ struct Key<float> {
     return largest ? -v : v;
   }
   __device__ __forceinline__ uint32_t index() const { return (uint32_t)k; }
+  // Output index: -1 for an empty slot (fewer kept pairs than k).
+  __device__ __forceinline__ int64_t out_index() const { return (uint32_t)k == ~0u ? -1 : (int64_t)(uint32_t)k; }
   __device__ __forceinline__ void store(void *base, int64_t e) const { static_cast<uint64_t *>(base)[e] = k; }
   __device__ __forceinline__ static Key load(const void *base, int64_t e) {
     return Key{static_cast<const uint64_t *>(base)[e]};
@@ -137,6 +139,7 @@ struct Key<double> {
     return largest ? -x : x;
   }
   __device__ __forceinline__ uint32_t index() const { return j; }
+  __device__ __forceinline__ int64_t out_index() const { return j == ~0u ? -1 : (int64_t)j; }
   __device__ __forceinline__ void store(void *base, int64_t e) const {
     uint64_t *b = static_cast<uint64_t *>(base);
     b[2 * e] = v;
@@ -161,6 +164,56 @@ __device__ __forceinline__ void key_insert(Key<T> (&l)[L], Key<T> c) {
       c = hi;
     }
   }
+}
+
+// ------------------------------------------------------------------ masks
+// Tile classes under the pair masks, for the rows r0..r1 of a row block and
+// the keys j0..j1 of a tile (both inclusive, non-empty).
+enum TileClass : int { TILE_SKIP = 0, TILE_CHECK = 1, TILE_FULL = 2 };
+
+__device__ __forceinline__ int tile_class(const MaskArgs &m, int64_t r0, int64_t r1, int64_t j0, int64_t j1,
+                                          int rb, int64_t tile) {
+  int c = TILE_FULL;
+  if (m.band) {
+    // j - i spans [j0 - r1, j1 - r0] over the tile.
+    if (j1 - r0 < m.lo || j0 - r1 > m.hi) return TILE_SKIP;
+    if (j0 - r1 < m.lo || j1 - r0 > m.hi) c = TILE_CHECK;
+  }
+  if (m.grow) {
+    const int64_t a0 = m.grow_rng[2 * rb], a1 = m.grow_rng[2 * rb + 1];
+    const int64_t b0 = m.gcol_rng[2 * tile], b1 = m.gcol_rng[2 * tile + 1];
+    if (b1 < a0 || b0 > a1) return TILE_SKIP;
+    if (!(a0 == a1 && b0 == b1 && a0 == b0)) c = TILE_CHECK;
+  }
+  if (m.col) c = TILE_CHECK;
+  return c;
+}
+
+// The key range [first, last) row block rb (rows r0..r1) visits inside the
+// column split [jb, je): the band's reach, cut to the block's span of kept
+// tiles when one was computed, with `first` on a tile boundary.
+__device__ __forceinline__ void band_range(const MaskArgs &m, int rb, int64_t r0, int64_t r1, int64_t jb, int64_t je,
+                                           int bn, int64_t *first, int64_t *last) {
+  int64_t f = jb, l = je;
+  if (m.band) {
+    const int64_t lo = r0 + m.lo, hi = r1 + m.hi + 1;
+    if (lo > jb) f = jb + (lo - jb) / bn * bn;
+    l = min(l, hi);
+  }
+  if (m.span) {
+    const int64_t s0 = m.span[2 * rb], s1 = m.span[2 * rb + 1];
+    if (s0 > f) f = jb + (s0 - jb) / bn * bn;
+    l = min(l, s1);
+  }
+  *first = f;
+  *last = l;
+}
+
+// Whether pair (i, j) survives the band and the group mask (the column mask
+// is staged per key by the engines).
+__device__ __forceinline__ bool pair_kept(const MaskArgs &m, int64_t i, int64_t j, int64_t gi, int64_t gj) {
+  const int64_t d = j - i;
+  return (!m.band || (d >= m.lo && d <= m.hi)) && (!m.grow || gi == gj);
 }
 
 // Top-k filter threshold: the signed value (negated for `largest`) of the

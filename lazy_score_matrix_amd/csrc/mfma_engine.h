@@ -187,7 +187,10 @@ struct MfmaShape {
   static_assert(BM == mfma_bm(DT, CONS, DP, CP, KL), "host and device row-block sizes differ");
 };
 
-template <class T, int METRIC, int CONS, int DP, int CP, int KL>
+// MASKED instantiations carry the mask logic (row flags, per-key flags and
+// group ids in LDS, tile classes, keep bits); the others compile without it
+// and keep their register budget.
+template <class T, int METRIC, int CONS, int DP, int CP, int KL, bool MASKED>
 __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
                              (mfma_wgs_per_cu(sizeof(T) == 4 ? 0 : 1, CONS, DP, CP, KL))) void mfma_tile(const TileArgs a) {
   using F = Mfma<T>;
@@ -222,9 +225,14 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   __shared__ __attribute__((aligned(16))) T sKb[2][BN][DP + KPAD];
   __shared__ __attribute__((aligned(16))) T sNb[2][BN];
   __shared__ __attribute__((aligned(16))) T sVb[2][HAS_V ? BN : 1][VW];
+  constexpr int MBN = MASKED ? BN : 1;
+  __shared__ int sCb[2][MBN];      // column mask flags
+  __shared__ int64_t sGb[2][MBN];  // column group ids
   T(*sK)[DP + KPAD] = sKb[0];
   T *sN = sNb[0];
   T(*sV)[VW] = sVb[0];
+  int *sC = sCb[0];
+  int64_t *sG = sGb[0];
   constexpr bool TABLE_EXP = sizeof(T) == 8 && (ONLINE || METRIC == M_RBF);
   __shared__ double sE[TABLE_EXP ? 256 : 1];
 
@@ -242,13 +250,40 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     else return F::exp2(x);
   };
   const int w = tid >> 6, l = tid & 63, g = l / TM, q = l % TM;
-  const int rb = blockIdx.x % a.n_rb;
-  const int sp = blockIdx.x / a.n_rb;
+  // Row blocks of this workgroup: one, or with rb_pairs (masked launches
+  // with a band) the pair r, n_rb - 1 - r, so the light rows at one end of
+  // a causal band and the heavy rows at the other share a workgroup.
+  const int rb_slots = (MASKED && a.rb_pairs) ? a.rb_pairs : a.n_rb;
+  const int rb_first = blockIdx.x % rb_slots;
+  const int sp = blockIdx.x / rb_slots;
+  const bool paired = MASKED && a.rb_pairs;
+  const int npass = (paired && a.n_rb - 1 - rb_first != rb_first) ? 2 : 1;
+  // Paired launches deal the pair's tiles (those of the first row block,
+  // then those of the second, each within its band reach) out to the
+  // splits in equal runs, so every workgroup gets the same number of tiles.
+  int64_t pf[2] = {0, 0}, pl[2] = {0, 0}, pt[2] = {0, 0}, v0 = 0, v1 = 0;
+  if (paired) {
+    for (int p = 0; p < npass; ++p) {
+      const int64_t q0 = (int64_t)(p ? a.n_rb - 1 - rb_first : rb_first) * BM;
+      band_range(a.mask, p ? a.n_rb - 1 - rb_first : rb_first, q0, min(a.N, q0 + BM) - 1, 0, a.M, BN, &pf[p],
+                 &pl[p]);
+      pt[p] = pl[p] > pf[p] ? (pl[p] - pf[p] + BN - 1) / BN : 0;
+    }
+    const int64_t tt = pt[0] + pt[1];
+    v0 = tt * sp / a.n_split;
+    v1 = tt * (sp + 1) / a.n_split;
+  }
+  for (int pass = 0; pass < npass; ++pass) {
+  if (pass) __syncthreads();  // the previous row block's last LDS reads
+  const int rb = pass ? a.n_rb - 1 - rb_first : rb_first;
   const int64_t row0 = (int64_t)rb * BM;
-  const int64_t jb = (int64_t)sp * a.split_cols;
-  const int64_t je = min(a.M, jb + a.split_cols);
+  const int64_t jb = paired ? 0 : (int64_t)sp * a.split_cols;
+  const int64_t je = paired ? a.M : min(a.M, jb + a.split_cols);
   const T *__restrict__ Xp = static_cast<const T *>(a.X);
   const T *__restrict__ Yp = static_cast<const T *>(a.Y);
+  const MaskArgs &mk = a.mask;
+  const bool keyflags = MASKED && (mk.col || mk.grow);  // per-key mask data is staged
+  const int64_t r1 = min(a.N, row0 + BM) - 1;
 
   // ------------------------------------------------------------ row state
   int64_t qi[QB];
@@ -256,11 +291,15 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   T qr[QB][DG];
   T nx[QB];
   T er[QB], ep[QB];  // row epilogue: s <- er * s + ep
+  bool rkeep[QB];    // row survives the row mask
+  int64_t gq[QB];    // row group id
   const bool has_epi = a.epi.n_stages == 1;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     qi[b] = row0 + (int64_t)(w * QB + b) * TM + q;
     qv[b] = qi[b] < a.N;
+    rkeep[b] = qv[b] && (!MASKED || !mk.row || mk.row[qi[b]]);
+    gq[b] = (MASKED && qv[b] && mk.grow) ? mk.grow[qi[b]] : 0;
     T part = 0;
 #pragma unroll
     for (int s = 0; s < DG; ++s) {
@@ -337,8 +376,35 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   };
 
   // Fold one sub-block of scores into the row reductions.
-  auto consume = [&](int kb, int nb, int64_t j0, bool diag, acc_t (&s)[QB]) {
+  // Keep bits of a checked sub-block: bit r of km[b] tells whether the pair
+  // of query block b and register r survives the masks.
+  auto keep_bits = [&](int kb, int64_t j0, uint32_t (&km)[QB]) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int64_t dbase = j0 + kb - qi[b];
+      uint32_t bits = 0;
+#pragma unroll
+      for (int r = 0; r < NREG; ++r) {
+        const int key = kb + F::key_of(r, g);
+        bool kp = (!mk.col || sC[key]) && (!mk.grow || sG[key] == gq[b]);
+        const int64_t d = dbase + F::key_of(r, g);
+        kp = kp && (!mk.band || (d >= mk.lo && d <= mk.hi));
+        bits |= (uint32_t)kp << r;
+      }
+      km[b] = bits;
+    }
+  };
+  // Keep bits of every sub-block of a checked tile, formed once when the
+  // tile starts (few registers are live there) and read back per sub-block.
+  __shared__ uint32_t sKm[MASKED ? SB : 1][QB][MASKED ? NT : 1];
+  auto consume = [&](int kb, int nb, int64_t j0, bool diag, bool check_, acc_t (&s)[QB]) {
+    const bool check = MASKED && check_;
     const bool tail = kb + TM > nb;
+    uint32_t km[QB];
+    if (check) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) km[b] = sKm[MASKED ? kb / TM : 0][b][MASKED ? tid : 0];
+    }
     if constexpr (CONS == C_TOPK) {
       // Filter a whole sub-block with one wave vote before any insertion.
       // Plain searches (no epilogue, smallest first, dot product or squared
@@ -349,6 +415,11 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       if (plain) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
+          if (check) {
+#pragma unroll
+            for (int r = 0; r < NREG; ++r)
+              if (!((km[b] >> r) & 1u)) s[b][r] = __builtin_huge_valf();
+          }
           T mn = s[b][0];
 #pragma unroll
           for (int r = 1; r < NREG; ++r) mn = min(mn, s[b][r]);
@@ -365,6 +436,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
             if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
             if constexpr (COS) x = fma(-x * sN[kb + F::key_of(r, g)], nx[b], (T)1);
             x = fma(x, er[b], ep[b]);
+            if (check && !((km[b] >> r) & 1u)) x = a.largest ? -__builtin_huge_valf() : __builtin_huge_valf();
             s[b][r] = x;
             mn = min(mn, a.largest ? -x : x);
           }
@@ -417,6 +489,11 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 #pragma unroll
         for (int r = 0; r < NREG; ++r)
           if (j0 + kb + F::key_of(r, g) == qi[b]) v[b][r] = kNegInf;
+      }
+      if (check) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r)
+          if (!((km[b] >> r) & 1u)) v[b][r] = ONLINE ? kNegInf : (T)0;
       }
     }
 
@@ -504,6 +581,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   TileLoader<T, BN, DP, NT> ldK;
   TileLoader<T, BN, VTILE ? CP : 16 / (int)sizeof(T), NT> ldV;
   T nyv = 0, vcol = 0;
+  int ckv = 0;
+  int64_t gkv = 0;
   const bool kvec = vec_ok(a.Y, a.ldy, 16 / (int)sizeof(T));
   const bool vvec = VTILE && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
   ldK.init(a.ldy, kvec, tid);
@@ -514,6 +593,10 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     if constexpr (VTILE) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
     if constexpr (NARROW) vcol = (tid < nbt) ? ldg<T>(a.V, (t0 + tid) * a.ldv) : (T)0;
     if constexpr (NEEDN) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
+    if (keyflags) {
+      ckv = (tid < nbt && (!mk.col || mk.col[t0 + tid])) ? 1 : 0;
+      gkv = (tid < nbt && mk.grow) ? mk.gcol[t0 + tid] : 0;
+    }
   };
   auto stage = [&](int buf) {
     ldK.store(sKb[buf], tid);
@@ -524,23 +607,64 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     if constexpr (NEEDN) {
       if (tid < BN) sNb[buf][tid] = nyv;
     }
+    if (keyflags && tid < BN) {
+      sCb[buf][tid] = ckv;
+      sGb[buf][tid] = gkv;
+    }
+  };
+  // Tiles this row block visits: the band's reach inside the split, minus
+  // tiles the masks drop whole.
+  int64_t jfirst = jb, jlast = je;
+  if constexpr (MASKED) {
+    if (paired) {
+      const int64_t off = pass ? pt[0] : 0;
+      const int64_t t0 = max(v0 - off, (int64_t)0), t1 = min(v1 - off, pt[pass]);
+      jfirst = pf[pass] + t0 * BN;
+      jlast = t1 > t0 ? min(pl[pass], pf[pass] + t1 * BN) : jfirst;
+    } else {
+      band_range(mk, rb, row0, r1, jb, je, BN, &jfirst, &jlast);
+    }
+  }
+  auto tile_cls = [&](int64_t t0) -> int {
+    if constexpr (MASKED) return tile_class(mk, row0, r1, t0, min(t0 + BN, je) - 1, rb, t0 / BN);
+    return TILE_FULL;
+  };
+  auto next_tile = [&](int64_t t0) {
+    if constexpr (MASKED) {
+      while (t0 < jlast && tile_cls(t0) == TILE_SKIP) t0 += BN;
+    }
+    return t0;
   };
   int buf = 0;
-  if (jb < je) {
-    prefetch(jb);
+  int64_t j0 = next_tile(jfirst);
+  if (j0 < jlast) {
+    prefetch(j0);
     stage(0);
   }
   __syncthreads();
 
-  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+  while (j0 < jlast) {
     const int nb = (int)min((int64_t)BN, je - j0);
-    const bool next = j0 + BN < je;
-    if (next) prefetch(j0 + BN);
+    const int64_t jn = next_tile(j0 + BN);
+    const bool next = jn < jlast;
+    if (next) prefetch(jn);
     sK = sKb[buf];
     sN = sNb[buf];
     sV = sVb[buf];
+    sC = sCb[buf];
+    sG = sGb[buf];
     const bool diag = CONS == C_LOGSUMEXP && a.exclude_self && j0 < row0 + BM && j0 + BN > row0;
+    const bool check = tile_cls(j0) == TILE_CHECK;
 
+    if (MASKED && check) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        uint32_t km[QB];
+        keep_bits(sb * TM, j0, km);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) sKm[MASKED ? sb : 0][b][MASKED ? tid : 0] = km[b];
+      }
+    }
     acc_t s0[QB], s1[QB];
     qk(0, s0);
 #pragma unroll
@@ -549,15 +673,34 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       const bool more = sb + 1 < SB && (sb + 1) * TM < nb;
       if (sb & 1) {
         if (more) qk((sb + 1) * TM, s0);
-        consume(sb * TM, nb, j0, diag, s1);
+        consume(sb * TM, nb, j0, diag, check, s1);
       } else {
         if (more) qk((sb + 1) * TM, s1);
-        consume(sb * TM, nb, j0, diag, s0);
+        consume(sb * TM, nb, j0, diag, check, s0);
       }
     }
     if (next) stage(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+    j0 = jn;
+  }
+
+  // Rows dropped by the row mask take the empty-row result.
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    if (MASKED && !rkeep[b]) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) o[b][c][r] = 0;
+      m[b] = kNegInf;
+      lsum[b] = 0;
+      mass[b] = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) wsum[b][u] = 0;
+#pragma unroll
+      for (int p = 0; p < KLQ; ++p) list[b][p] = Key<T>::sentinel();
+    }
   }
 
   // ---------------------------------------------------------------- finalize
@@ -637,14 +780,17 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       }
     }
   }
+  }  // pass
 }
 
 // ------------------------------------------------------------------ dispatch
 
 template <class T, int METRIC, int CONS, int DP, int CP, int KL>
 hipError_t launch_mfma_kernel(const TileArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(MfmaShape<T, CONS, DP, CP, KL>::NT);
-  hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL>), grid, block, 0, s, a);
+  const int slots = (a.mask.any && a.rb_pairs) ? a.rb_pairs : a.n_rb;
+  dim3 grid((unsigned)(slots * a.n_split)), block(MfmaShape<T, CONS, DP, CP, KL>::NT);
+  if (a.mask.any) hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

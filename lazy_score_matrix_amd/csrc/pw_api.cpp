@@ -132,6 +132,11 @@ struct pw_expr {
   int64_t D;
   std::vector<pw_op> ops;
   std::vector<HostStage> stages;
+  // Masks collected from the op list.
+  const uint8_t *row_mask = nullptr, *col_mask = nullptr;
+  bool band = false;
+  int64_t lo = -kBandNone, hi = kBandNone;
+  const int64_t *grow = nullptr, *gcol = nullptr;
 };
 
 namespace {
@@ -148,6 +153,9 @@ struct Plan {
   ValuConfig vcfg{4, 0};
   MfmaConfig mcfg{16, 32, 16};
   int bm = kValuBM, bn = kValuBN;
+  int rb_pairs = 0;
+  size_t off_grp = 0;  // group ranges: rows [n_rb][2], then key tiles [ceil(M / bn)][2]
+  size_t off_span = 0;  // kept-tile spans per row block [n_rb][2]
   int n_rb = 0, n_split = 1;
   int n_part = 1;  // partial lists or sums per row the merge reads (0: none)
   int64_t split_cols = 0;
@@ -218,18 +226,37 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   p.col_norms = (p.family == 1 && e.metric != PW_LINEAR) || e.metric == PW_COSINE;
   p.off_ny = off;
   if (p.col_norms) off += align_up((size_t)e.M * es);
-  p.off_part = off;
   // Tile grid: enough workgroups to fill the chip, splitting the columns
   // when there are too few row blocks.
   p.n_rb = (int)((e.N + p.bm - 1) / p.bm);
+  // Pair masks make the work per row block uneven (causal: linear in the
+  // block); the MFMA engine then pairs the row blocks r and n_rb - 1 - r and
+  // deals each pair's kept tiles evenly to the splits.
+  p.rb_pairs = (p.family == 1 && (e.band || e.grow)) ? (p.n_rb + 1) / 2 : 0;
+  const int rb_slots = p.rb_pairs ? p.rb_pairs : p.n_rb;
   const int64_t tiles = std::max<int64_t>(1, (e.M + p.bn - 1) / p.bn);
-  int64_t want = std::max<int64_t>(1, (target_wgs + p.n_rb - 1) / std::max(p.n_rb, 1));
+  int64_t want = std::max<int64_t>(1, (target_wgs + rb_slots - 1) / std::max(rb_slots, 1));
   want = std::min(want, tiles);
   const int64_t tiles_per_split = (tiles + want - 1) / want;
   p.split_cols = tiles_per_split * p.bn;
   p.n_split = (int)std::max<int64_t>(1, (e.M + p.split_cols - 1) / p.split_cols);
+  // Paired launches deal each pair's tiles to the splits (not column
+  // ranges): `want` splits, as long as each gets a few tiles.
+  if (p.rb_pairs) p.n_split = (int)std::max<int64_t>(1, std::min<int64_t>(want, 2 * tiles / 4));
+  // Group ranges of a same_group mask, and per row block the span of tiles
+  // the pair masks keep (with groups: a band alone needs no table).
+  if (e.grow) {
+    p.off_grp = off;
+    const int64_t key_tiles = (e.M + p.bn - 1) / p.bn;
+    off += align_up((size_t)(p.n_rb + key_tiles) * 2 * sizeof(int64_t));
+  }
+  if (e.grow) {
+    p.off_span = off;
+    off += align_up((size_t)p.n_rb * 2 * sizeof(int64_t));
+  }
   // Partials: one per column split, and for MFMA top-k one per split and
   // lane group.
+  p.off_part = off;
   p.n_part = p.n_split;
   if (p.family == 1 && consumer == PW_C_TOPK) p.n_part = p.n_split * mfma_groups(e.dtype);
   if (p.n_part > 1) {
@@ -329,6 +356,7 @@ TileArgs base_args(const pw_expr &e, const Plan &p, char *base) {
   a.D = (int)e.D;
   a.gamma = e.metric == PW_RBF ? e.gamma : 0.0;
   a.n_rb = p.n_rb;
+  a.rb_pairs = p.rb_pairs;
   a.n_split = p.n_split;
   a.split_cols = p.split_cols;
   a.partial = p.n_part > 1 ? base + p.off_part : nullptr;
@@ -381,6 +409,41 @@ int prepare_norms(const pw_expr &e, const Plan &p, const TileArgs &a, hipStream_
   if (!p.col_norms) return PW_OK;
   return hip_status(
       launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s, e.metric == PW_COSINE));
+}
+
+// Mask arguments, and the group ranges per row block and key tile.
+int prepare_masks(const pw_expr &e, const Plan &p, char *base, TileArgs &a, hipStream_t s) {
+  MaskArgs &m = a.mask;
+  m.row = e.row_mask;
+  m.col = e.col_mask;
+  m.band = e.band ? 1 : 0;
+  m.lo = e.lo;
+  m.hi = e.hi;
+  m.grow = e.grow;
+  m.gcol = e.gcol;
+  m.any = (m.row || m.col || m.band || m.grow) ? 1 : 0;
+  int rc = PW_OK;
+  if (e.grow) {
+    int64_t *rng = reinterpret_cast<int64_t *>(base + p.off_grp);
+    m.grow_rng = rng;
+    m.gcol_rng = rng + 2 * (size_t)p.n_rb;
+    rc = hip_status(launch_group_ranges(e.grow, e.N, p.bm, rng, s));
+    if (rc == PW_OK) rc = hip_status(launch_group_ranges(e.gcol, e.M, p.bn, rng + 2 * (size_t)p.n_rb, s));
+  }
+  if (rc == PW_OK && e.grow) {  // a band alone gives the range in closed form
+    int64_t *span = reinterpret_cast<int64_t *>(base + p.off_span);
+    rc = hip_status(launch_tile_spans(m, e.N, e.M, p.bm, p.bn, p.n_rb, span, s));
+    m.span = span;  // the spans pass itself runs without them
+  }
+  return rc;
+}
+
+// Everything a tile launch reads besides the caller's arrays.
+int prepare(const pw_expr &e, const Plan &p, char *base, TileArgs &a, hipStream_t s) {
+  int rc = prepare_epilogue(e, p, base, &a.epi, s);
+  if (rc == PW_OK) rc = prepare_norms(e, p, a, s);
+  if (rc == PW_OK) rc = prepare_masks(e, p, base, a, s);
+  return rc;
 }
 
 // Caller-owned events recorded around tile launches (pw_set_tile_events).
@@ -453,9 +516,29 @@ int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, i
         if ((M > 0 && !o.vec) || !aligned(o.vec, es)) return PW_ERR_INVALID;
         break;
       case PW_OP_EXP: break;
+      case PW_OP_MASK_ROWS:
+      case PW_OP_GROUP_ROWS:
+        if (N > 0 && !o.vec) return PW_ERR_INVALID;
+        if (o.kind == PW_OP_GROUP_ROWS && !aligned(o.vec, 8)) return PW_ERR_INVALID;
+        break;
+      case PW_OP_MASK_COLUMNS:
+      case PW_OP_GROUP_COLUMNS:
+        if (M > 0 && !o.vec) return PW_ERR_INVALID;
+        if (o.kind == PW_OP_GROUP_COLUMNS && !aligned(o.vec, 8)) return PW_ERR_INVALID;
+        break;
+      case PW_OP_BAND_UPPER:
+      case PW_OP_BAND_LOWER:
+        if (!(std::fabs(o.scalar) <= 9007199254740992.0) || o.scalar != std::floor(o.scalar))
+          return PW_ERR_INVALID;
+        break;
       default: return PW_ERR_INVALID;
     }
   }
+  int n_kind[16] = {0};
+  for (int t = 0; t < n_ops; ++t) n_kind[ops[t].kind]++;
+  if (n_kind[PW_OP_MASK_ROWS] > 1 || n_kind[PW_OP_MASK_COLUMNS] > 1 || n_kind[PW_OP_GROUP_ROWS] > 1 ||
+      n_kind[PW_OP_GROUP_COLUMNS] > 1 || n_kind[PW_OP_GROUP_ROWS] != n_kind[PW_OP_GROUP_COLUMNS])
+    return PW_ERR_INVALID;
   pw_expr *e = new (std::nothrow) pw_expr();
   if (!e) return PW_ERR_INVALID;
   e->dtype = dtype;
@@ -469,6 +552,26 @@ int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, i
   e->ldy = ldy;
   e->D = D;
   e->ops.assign(ops, ops + n_ops);
+  for (const pw_op &o : e->ops) {
+    switch (o.kind) {
+      case PW_OP_MASK_ROWS: e->row_mask = static_cast<const uint8_t *>(o.vec); break;
+      case PW_OP_MASK_COLUMNS: e->col_mask = static_cast<const uint8_t *>(o.vec); break;
+      case PW_OP_GROUP_ROWS: e->grow = static_cast<const int64_t *>(o.vec); break;
+      case PW_OP_GROUP_COLUMNS: e->gcol = static_cast<const int64_t *>(o.vec); break;
+      case PW_OP_BAND_UPPER:
+        e->band = true;
+        e->hi = std::min(e->hi, (int64_t)o.scalar);
+        break;
+      case PW_OP_BAND_LOWER:
+        e->band = true;
+        e->lo = std::max(e->lo, -(int64_t)o.scalar);
+        break;
+    }
+  }
+  // Bounds beyond the matrix mean the same as none, and keep the device
+  // arithmetic on them free of overflow.
+  e->hi = std::max(std::min(e->hi, kBandNone), -kBandNone);
+  e->lo = std::max(std::min(e->lo, kBandNone), -kBandNone);
   StageBuilder b;
   for (const pw_op &o : e->ops) b.op(o);
   b.close();
@@ -518,10 +621,10 @@ int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf
   Plan p = make_plan(*e, consumer, C, k);
   if (p.family == 1)
     std::snprintf(buf, len,
-                  "family=mfma dp=%d cp=%d kl=%d bm=%d bn=%d row_blocks=%d splits=%d partials=%d split_cols=%lld "
-                  "stages=%d workspace=%zu",
-                  p.mcfg.dp, p.mcfg.cp, p.mcfg.kl, p.bm, p.bn, p.n_rb, p.n_split, p.n_part, (long long)p.split_cols,
-                  (int)e->stages.size(), p.total);
+                  "family=mfma dp=%d cp=%d kl=%d bm=%d bn=%d row_blocks=%d row_block_pairs=%d splits=%d partials=%d "
+                  "split_cols=%lld stages=%d workspace=%zu",
+                  p.mcfg.dp, p.mcfg.cp, p.mcfg.kl, p.bm, p.bn, p.n_rb, p.rb_pairs, p.n_split, p.n_part,
+                  (long long)p.split_cols, (int)e->stages.size(), p.total);
   else
     std::snprintf(buf, len,
                   "family=valu dtile=%d vtile=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
@@ -548,8 +651,7 @@ static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t
   rc = check_ws(p, ws, ws_bytes, &base);
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
-  rc = prepare_epilogue(*e, p, base, &a.epi, s);
-  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
+  rc = prepare(*e, p, base, a, s);
   if (rc != PW_OK) return rc;
   a.ldv = ldv;
   a.ldo = ldo;
@@ -585,8 +687,7 @@ int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t w
   rc = check_ws(p, ws, ws_bytes, &base);
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
-  rc = prepare_epilogue(*e, p, base, &a.epi, s);
-  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
+  rc = prepare(*e, p, base, a, s);
   if (rc != PW_OK) return rc;
   a.out = out;
   a.ldo = ldo;
@@ -606,8 +707,7 @@ int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t
   rc = check_ws(p, ws, ws_bytes, &base);
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
-  rc = prepare_epilogue(*e, p, base, &a.epi, s);
-  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
+  rc = prepare(*e, p, base, a, s);
   if (rc != PW_OK) return rc;
   a.out = out;
   a.exclude_self = exclude_self;
@@ -627,8 +727,7 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
   rc = check_ws(p, ws, ws_bytes, &base);
   if (rc != PW_OK) return rc;
   TileArgs a = base_args(*e, p, base);
-  rc = prepare_epilogue(*e, p, base, &a.epi, s);
-  if (rc == PW_OK) rc = prepare_norms(*e, p, a, s);
+  rc = prepare(*e, p, base, a, s);
   if (rc != PW_OK) return rc;
   a.out = values;
   a.idx = indices;

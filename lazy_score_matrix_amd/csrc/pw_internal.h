@@ -71,6 +71,23 @@ enum Metric : int { M_LINEAR = 0, M_SQEUCLIDEAN = 1, M_RBF = 2, M_COSINE = 3 };
 // partial (per-row sums, (max, sum[, acc]) pairs or sorted top-k keys) to
 // the workspace and a merge kernel combines the splits in a fixed order.
 // ---------------------------------------------------------------------------
+// Masks: pairs dropped from every consumer. Tiles are classified per row
+// block and key tile: skipped, checked pair by pair, or kept whole.
+struct MaskArgs {
+  const uint8_t *row;       // N bytes: row i kept iff nonzero (null: all)
+  const uint8_t *col;       // M bytes: column j kept iff nonzero (null: all)
+  int band;                 // lo/hi bounds present
+  int64_t lo, hi;           // kept iff lo <= j - i <= hi
+  const int64_t *grow;      // row group ids (null: no group mask)
+  const int64_t *gcol;      // column group ids: kept iff grow[i] == gcol[j]
+  const int64_t *grow_rng;  // [n_rb][2] min and max row group per row block
+  const int64_t *gcol_rng;  // [ceil(M / bn)][2] min and max per key tile
+  const int64_t *span;      // [n_rb][2] first and end column of the tiles a row
+                            // block keeps under the pair masks (null: no span)
+  int any;                  // any mask present
+};
+constexpr int64_t kBandNone = (int64_t)1 << 62;
+
 struct TileArgs {
   const void *X;
   int64_t ldx;
@@ -89,6 +106,8 @@ struct TileArgs {
   int largest;
   int exclude_self;
   int n_rb;              // row blocks
+  int rb_pairs;          // MFMA masked launches: workgroups per split that each take
+                         // row blocks r and n_rb - 1 - r (0: one row block each)
   int n_split;           // column splits
   int64_t split_cols;    // columns per split (multiple of the tile width)
   void *partial;         // workspace partials when n_split > 1
@@ -96,6 +115,7 @@ struct TileArgs {
   const void *ny;        // column norms |y_j|^2 (distances) or 1/|y_j| (cosine, 0 for y_j = 0)
   double exp2_c[4];      // (ln2/256)^k / k!, k = 1..4, for the table-driven double exp2
   Epi epi;
+  MaskArgs mask;
 };
 
 // Top-k partial key layouts in the workspace.
@@ -162,6 +182,12 @@ hipError_t mfma_launch_metric(int consumer, const MfmaConfig &cfg, const TileArg
 
 // Auxiliary kernels.
 hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s);
+// Per block of `block` entries of g[0..n): min and max, written as pairs.
+hipError_t launch_group_ranges(const int64_t *g, int64_t n, int block, int64_t *out, hipStream_t s);
+// Per row block of bm rows: the column span [first, end) of the key tiles of
+// bn columns that the pair masks do not skip ([0, 0) when none).
+hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, int bn, int n_rb, int64_t *out,
+                             hipStream_t s);
 hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);
 // Row norms |x_i|^2, or with `inverse` 1/|x_i| (0 for a zero row).
 hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s,

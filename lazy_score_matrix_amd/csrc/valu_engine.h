@@ -88,6 +88,8 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   __shared__ T sQ[kMaxStages][BN];
   __shared__ T sO[kMaxStages][BN];
   __shared__ T sR[METRIC == M_COSINE ? BN : 1];  // 1/|y_j| for cosine
+  __shared__ int sC[BN];                          // column mask flags
+  __shared__ int64_t sG[BN];                      // column group ids
 
   const int tid = threadIdx.x;
   const int rb = blockIdx.x % a.n_rb;
@@ -96,6 +98,12 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   const bool rv = i < a.N;
   const int64_t jb = (int64_t)sp * a.split_cols;
   const int64_t je = min(a.M, jb + a.split_cols);
+  const MaskArgs &mk = a.mask;
+  const int64_t r0 = (int64_t)rb * BM, r1 = min(a.N, r0 + BM) - 1;
+  const bool rkeep = rv && (!mk.row || mk.row[i]);
+  const int64_t gi = (rv && mk.grow) ? mk.grow[i] : 0;
+  int64_t jfirst, jlast;
+  band_range(mk, rb, r0, r1, jb, je, BN, &jfirst, &jlast);
 
   T x[DT];
 #pragma unroll
@@ -110,6 +118,10 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     for (int d = 0; d < DT; ++d) n2 = fma(x[d], x[d], n2);
     rx = n2 > (T)0 ? (T)1 / sqrt(n2) : (T)0;
   }
+  // Whether column slot jj of the tile at j0 (a checked tile) survives the
+  // masks.
+  int64_t j0c = 0;
+  auto kept = [&](int jj) -> bool { return sC[jj] && pair_kept(a.mask, i, j0c + jj, gi, sG[jj]); };
   // Score of column slot jj (the metric; cosine scales the dot product).
   auto metric = [&](int jj) -> T {
     T v = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
@@ -130,8 +142,12 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   T thr = __builtin_huge_val();
   uint32_t best_j = ~0u;
 
-  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+  for (int64_t j0 = jfirst; j0 < jlast; j0 += BN) {
     const int nb = (int)min((int64_t)BN, je - j0);
+    const int cls = tile_class(mk, r0, r1, j0, j0 + nb - 1, rb, j0 / BN);
+    if (cls == TILE_SKIP) continue;  // uniform over the workgroup
+    const bool check = cls == TILE_CHECK;
+    j0c = j0;
     __syncthreads();
     for (int e = tid; e < BN * DT; e += BM) {
       int jj = e / DT, d = e % DT;
@@ -145,6 +161,12 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     }
     if constexpr (METRIC == M_COSINE) {
       for (int e = tid; e < BN; e += BM) sR[e] = e < nb ? ldg<T>(a.ny, j0 + e) : (T)0;
+    }
+    if (check) {
+      for (int e = tid; e < BN; e += BM) {
+        sC[e] = (e < nb && (!mk.col || mk.col[j0 + e])) ? 1 : 0;
+        sG[e] = (e < nb && mk.grow) ? mk.gcol[j0 + e] : 0;
+      }
     }
     if (a.epi.any_col) {
       for (int e = tid; e < kMaxStages * BN; e += BM) {
@@ -170,6 +192,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
           if (jj < nb) {
             s = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
             if (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) s = neg_inf<T>();
+            if (check && !kept(jj)) s = neg_inf<T>();
           }
           sv[u] = s;
           gm = max(gm, s);
@@ -222,7 +245,17 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
       };
       // The stage loop runs only when the expression has score arithmetic;
       // a bare metric takes a loop without it (a uniform branch).
-      if constexpr (CONS == C_TOPK) {
+      // Checked tiles drop masked pairs: no weight in a sum, +inf (never a
+      // candidate) in the signed top-k orientation.
+      if (check) {
+        const T sg = a.largest ? (T)-1 : (T)1;
+        for (int jj = 0; jj < nb; ++jj) {
+          const T sc = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
+          const bool kp = kept(jj);
+          if constexpr (CONS == C_TOPK) fold_topk(jj, kp ? sg * sc : (T)__builtin_huge_val());
+          else fold(jj, kp ? sc : (T)0);
+        }
+      } else if constexpr (CONS == C_TOPK) {
         if (a.epi.n_stages == 0) {
           if (a.largest) {
             for (int jj = 0; jj < nb; ++jj) fold_topk(jj, -metric(jj));
@@ -242,6 +275,16 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     }
   }
   if (!rv) return;
+  if (!rkeep) {  // a masked row: the empty-row result
+#pragma unroll
+    for (int c = 0; c < ACCN; ++c) acc[c] = 0;
+    mass = 0;
+    m = neg_inf<T>();
+    l = 0;
+#pragma unroll
+    for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
+    best_j = ~0u;
+  }
 
   const bool fin = a.n_split == 1;
   const int64_t prow = (int64_t)sp * a.N + i;  // partial row
@@ -289,7 +332,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
       for (int p = 0; p < KL; ++p)
         if (p < a.k) {
           v[p] = list[p].value(a.largest);
-          ix[p] = (int64_t)list[p].index();
+          ix[p] = list[p].out_index();
         }
     } else {
 #pragma unroll

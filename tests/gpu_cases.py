@@ -25,7 +25,8 @@ SWAP = {"add_rows": "add_columns", "add_columns": "add_rows", "weight_rows": "we
 def bind_case(arrays, c):
     """Both expressions of a workload case; a transposed case reduces over
     the rows, i.e. binds (Y, X) with row and column ops swapped."""
-    ops = [(n, arrays[a] if isinstance(a, str) else a) for n, a in c.ops]
+    import workloads
+    ops = [(n, workloads.resolve(a, arrays)) for n, a in c.ops]
     X, Y = arrays[c.x], arrays[c.y]
     if getattr(c, "transpose", False):
         X, Y = Y, X
@@ -37,7 +38,13 @@ def bind_both(X, Y, metric, gamma=1.0, ops=(), same=False):
     """The GPU expression and the oracle expression of one score."""
     tX = to_dev(X)
     tY = tX if same else to_dev(Y)
-    gops = [(n, to_dev(a) if isinstance(a, np.ndarray) else a) for n, a in ops]
+    def dev_arg(a):
+        if isinstance(a, np.ndarray):
+            return to_dev(a)
+        if isinstance(a, tuple):
+            return tuple(dev_arg(x) for x in a)
+        return a
+    gops = [(n, dev_arg(a)) for n, a in ops]
     e = pw.lazy(tX, tY, metric, gamma=gamma, ops=gops)
     oe = oracle.Expr(X, X if same else Y, metric, gamma=gamma, ops=list(ops))
     return e, oe

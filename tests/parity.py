@@ -71,23 +71,30 @@ def topk_report(gv, gi, ov, oi, omag, k, largest, dtype, exact=False):
     fails = []
     R = gv.shape[0]
     for r in range(R):
+        # Rows with fewer kept pairs than k (masks): the oracle pads with
+        # index -1 / NaN, and so must the GPU, past the same count.
+        nv = int(np.sum(oi[r, :k] >= 0))
         if exact:
-            if not np.array_equal(gi[r], oi[r, :k]) or not np.array_equal(gv[r], ov[r, :k]):
+            if not np.array_equal(gi[r], oi[r, :k]) or not np.array_equal(gv[r], ov[r, :k], equal_nan=True):
                 fails.append("row %d: exact mismatch gpu %s vs oracle %s" % (r, gi[r].tolist(), oi[r, :k].tolist()))
             continue
-        idx = gi[r]
-        if len(set(idx.tolist())) != k or idx.min() < 0:
+        if np.any(gi[r, nv:] != -1) or not np.all(np.isnan(gv[r, nv:])):
+            fails.append("row %d: %d kept pairs, but positions past them are %s / %s"
+                         % (r, nv, gi[r, nv:].tolist(), gv[r, nv:].tolist()))
+            continue
+        idx = gi[r, :nv]
+        if len(set(idx.tolist())) != nv or (nv and idx.min() < 0):
             fails.append("row %d: indices not distinct / negative %s" % (r, idx.tolist()))
             continue
         v = gv[r]
-        for p in range(k - 1):
+        for p in range(nv - 1):
             before = v[p] > v[p + 1] if largest else v[p] < v[p + 1]
             if not (before or (v[p] == v[p + 1] and idx[p] < idx[p + 1])):
                 fails.append("row %d: order broken at %d (%r,%d) (%r,%d)" % (r, p, v[p], idx[p], v[p + 1], idx[p + 1]))
                 break
         pos = {j: q for q, j in enumerate(oi[r].tolist()) if j >= 0}
         tol = rtol * np.maximum(np.abs(ov[r]), omag[r])
-        for p in range(k):
+        for p in range(nv):
             q = pos.get(int(idx[p]))
             if q is None:
                 fails.append("row %d pos %d: index %d not among the oracle's first %d" % (r, p, idx[p], ov.shape[1]))

@@ -66,8 +66,15 @@ def test_bind_validation(lib):
         (dict(ops=[(0, float("nan"), None)]), pw.PW_ERR_INVALID),
         (dict(ops=[(2, 0.0, None)]), pw.PW_ERR_INVALID),             # add_rows without vector
         (dict(ops=[(5, 0.0, None)]), pw.PW_ERR_INVALID),             # weight_columns without vector
-        (dict(ops=[(9, 0.0, None)]), pw.PW_ERR_INVALID),             # bad kind
-        (dict(ops=[(0, 2.0, None)] * 9), pw.PW_ERR_UNSUPPORTED),     # > PW_MAX_OPS
+        (dict(ops=[(13, 0.0, None)]), pw.PW_ERR_INVALID),            # bad kind
+        (dict(ops=[(0, 2.0, None)] * 17), pw.PW_ERR_UNSUPPORTED),    # > PW_MAX_OPS
+        (dict(ops=[(0, 2.0, None), (6, 0, None)] * 5), pw.PW_ERR_UNSUPPORTED),  # > 8 fused stages
+        (dict(ops=[(7, 0.0, None)]), pw.PW_ERR_INVALID),             # mask_rows without vector
+        (dict(ops=[(8, 0.0, FAKE), (8, 0.0, FAKE)]), pw.PW_ERR_INVALID),  # two column masks
+        (dict(ops=[(9, 0.5, None)]), pw.PW_ERR_INVALID),             # band bound not an integer
+        (dict(ops=[(10, float("inf"), None)]), pw.PW_ERR_INVALID),   # band bound not finite
+        (dict(ops=[(11, 0.0, FAKE)]), pw.PW_ERR_INVALID),            # row groups without column groups
+        (dict(ops=[(11, 0.0, FAKE + 4), (12, 0.0, FAKE)]), pw.PW_ERR_INVALID),  # misaligned group ids
     ]
     for kw, want in cases:
         rc, h = bind(lib, **kw)
@@ -75,7 +82,10 @@ def test_bind_validation(lib):
         assert not h.value
     # Boundary values accepted: D = 1 and 64, gamma = 0, X aliasing Y, empty sets.
     for kw in (dict(D=1), dict(D=64), dict(metric=2, gamma=0.0), dict(N=0, X=0), dict(M=0, Y=0),
-               dict(ops=[(0, 0.5, None), (2, 0, FAKE), (3, 0, FAKE), (6, 0, None), (4, 0, FAKE), (5, 0, FAKE)])):
+               dict(ops=[(0, 0.5, None), (2, 0, FAKE), (3, 0, FAKE), (6, 0, None), (4, 0, FAKE), (5, 0, FAKE)]),
+               dict(ops=[(7, 0, FAKE), (8, 0, FAKE + 1), (9, -3.0, None), (10, 2.0, None), (9, 5.0, None),
+                         (11, 0, FAKE), (12, 0, FAKE), (0, 2.0, None)] * 1),
+               dict(ops=[(0, 2.0, None)] * 16)):
         rc, h = bind(lib, **kw)
         assert rc == pw.PW_OK, kw
         lib.pw_release(h)

@@ -14,8 +14,9 @@ k-NN retrieval) and its Stein Variational Gradient Descent section.
 
 Ops are listed in the neutral vocabulary of that guide's Score Expressions
 section: ("mul", c), ("add", c), ("add_rows", name), ("add_columns", name),
-("weight_rows", name), ("weight_columns", name), ("exp", None); a vector
-argument names an array of the workload's dict.
+("weight_rows", name), ("weight_columns", name), ("exp", None), and the
+masks ("causal", d) and ("same_group", (rows, columns)); a vector argument
+names an array of the workload's dict.
 """
 from __future__ import annotations
 
@@ -51,6 +52,7 @@ class Case:
     k: int = 0
     largest: bool = False
     transpose: bool = False  # reduce over rows instead (the transposed score)
+    pairs: int | None = None  # pairs the masks keep (None: all N * M)
 
 
 def rbf_small(n: int = 1024, m: int | None = None, d: int = 3, seed: int = 1001):
@@ -176,6 +178,51 @@ def feature_mean(n: int = 65536, m: int = 65536, d: int = 16, seed: int = 1008):
     return arrays, [Case("feature_mean", "mean", "F", "G", "sqeuclidean")]
 
 
+def attention_causal(n: int = 16384, d: int = 64, c: int = 64, seed: int = 1009):
+    """Causal softmax attention, float32: Q, K, V ~ N(0,1), scores
+    linear(Q,K)/8, pairs j <= i only (Task Map, Attention row:
+    masks.causal()). Kept pairs n (n + 1) / 2."""
+    arrays, cases = attention(n=n, d=d, c=c, seed=seed)
+    c0 = cases[0]
+    c0.name = "attention_causal"
+    c0.ops = c0.ops + [("causal", 0)]
+    c0.pairs = n * (n + 1) // 2
+    return arrays, cases
+
+
+def attention_packed(n: int = 16384, d: int = 64, c: int = 64, min_len: int = 256, max_len: int = 4096,
+                     seed: int = 1010):
+    """Packed causal attention, float32: sequences of lengths uniform in
+    [min_len, max_len) laid end to end up to n rows (the last one cut), each
+    attending causally within itself (masks.same_group on the sequence ids
+    plus masks.causal())."""
+    g = _gen(seed)
+    lengths = []
+    while sum(lengths) < n:
+        lengths.append(int(torch.randint(min_len, max_len, (1,), generator=g)))
+    lengths[-1] -= sum(lengths) - n
+    seg = np.repeat(np.arange(len(lengths), dtype=np.int64), lengths)
+    Q = _randn(g, n, d)
+    K = _randn(g, n, d)
+    V = _randn(g, n, c)
+    arrays = {k: t.to(torch.float32).numpy() for k, t in dict(Q=Q, K=K, V=V).items()}
+    arrays["seg"] = seg
+    scale = 1.0 / math.sqrt(float(d))
+    cases = [Case("attention_packed", "softmax_matmul", "Q", "K", "linear", v="V",
+                  ops=[("mul", scale), ("same_group", ("seg", "seg")), ("causal", 0)],
+                  pairs=sum(L * (L + 1) // 2 for L in lengths))]
+    return arrays, cases
+
+
+def resolve(arg, arrays):
+    """An op argument with array names replaced by the arrays."""
+    if isinstance(arg, str):
+        return arrays[arg]
+    if isinstance(arg, tuple):
+        return tuple(resolve(a, arrays) for a in arg)
+    return arg
+
+
 # name -> (generator, full-size kwargs, reduced kwargs for quick parity runs)
 WORKLOADS = {
     "rbf_small": (rbf_small, {}, {"n": 300, "m": 333}),
@@ -187,6 +234,8 @@ WORKLOADS = {
     "chamfer": (chamfer, {}, {"n": 700, "m": 900}),
     "cosine_knn": (cosine_knn, {}, {"n_query": 300, "n_ref": 3000}),
     "feature_mean": (feature_mean, {}, {"n": 800, "m": 1000}),
+    "attention_causal": (attention_causal, {}, {"n": 700}),
+    "attention_packed": (attention_packed, {}, {"n": 900, "min_len": 40, "max_len": 300}),
 }
 
 

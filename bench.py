@@ -98,6 +98,8 @@ def flops_per_pair(case, D, C):
         return body + 1
     if case.consumer == "mean":
         return body + 1 + 2  # the 1/M scale, then a product with a ones column
+    if case.consumer == "cg_solve":
+        return body + 2 * C  # one kernel product per iteration
     raise ValueError(case.consumer)
 
 
@@ -106,8 +108,9 @@ SWAP = {"add_rows": "add_columns", "add_columns": "add_rows", "weight_rows": "we
 
 
 def lib_consumer(c):
-    """The library call behind a case (a mean is a product with ones)."""
-    return "matmul" if c.consumer == "mean" else c.consumer
+    """The tile-kernel consumer behind a case (a mean is a product with
+    ones; a CG solve runs one product per iteration)."""
+    return "matmul" if c.consumer in ("mean", "cg_solve") else c.consumer
 
 
 def case_operands(c, arrays):
@@ -152,13 +155,28 @@ def main():
 
     calls = []  # (case, expr, run_fn, outputs)
     pairs_per_step = 0
+    solve_infos = []
     for c in cases:
         X, Y, ops = case_operands(c, t)
         e = pw.lazy(X, Y, c.metric, gamma=c.gamma, ops=ops)
         N, D = X.shape
         M = Y.shape[0]
         C = t[c.v].shape[1] if c.v else (1 if c.consumer == "mean" else 0)
-        if c.consumer == "mean":
+        if c.consumer == "cg_solve":
+            # One step is one whole solve; its pairs are iterations * N * M,
+            # counted from the solver's own iteration count.
+            B = t[c.v]
+            C = B.shape[1]
+            A = torch.empty(N, C, dtype=X.dtype, device=dev)
+            n = ctypes.c_size_t()
+            pw.check(e._lib.pw_cg_workspace_size(e._h, C, ctypes.byref(n)))
+            ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+            solve_infos.append([])
+            fn = (lambda e=e, B=B, A=A, ws=ws, p=c.params, log=solve_infos[-1]:
+                  log.append(e.solve(B, p["shift"], rtol=p["rtol"], max_iter=p["max_iter"], out=A,
+                                     workspace=ws)[1]))
+            outs = (A,)
+        elif c.consumer == "mean":
             # The row mean: the scores scaled by 1/M (an extra op bound
             # above) times a ones column, as LazyScores.mean computes it.
             ones = torch.ones(M, 1, dtype=X.dtype, device=dev)
@@ -190,7 +208,8 @@ def main():
                   e.topk(k, lg, values=vals, indices=idx, workspace=ws))
             outs = (vals, idx)
         calls.append((c, e, fn, outs, C))
-        pairs_per_step += c.pairs if c.pairs is not None else N * M
+        if c.consumer != "cg_solve":
+            pairs_per_step += c.pairs if c.pairs is not None else N * M
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -221,6 +240,15 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
+    solve_summary = None
+    if solve_infos:
+        # Timed solves: the last args.steps entries of each solve's log.
+        timed = [log[-args.steps:] for log in solve_infos]
+        its = [sum(i["iterations"] for i in log) / len(log) for log in timed]
+        cg_calls = [(c, e) for c, e, *_ in calls if c.consumer == "cg_solve"]
+        pairs_per_step += sum(it * e.N * e.M for it, (c, e) in zip(its, cg_calls))
+        solve_summary = [{"call": c.name, "iterations_per_solve": it, "info": log[-1]}
+                         for it, (c, e), log in zip(its, cg_calls, timed)]
     gpairs = pairs_per_step / (ms * 1e-3) / 1e9
     kernel_ms = []
     for ci in range(len(calls)):
@@ -285,6 +313,8 @@ def main():
         },
         "roofline": roofline,
     }
+    if solve_summary:
+        result["config"]["solves"] = solve_summary
 
     if not args.no_cpu:
         result.update(cpu_leg(calls, arrays, args.cpu_seconds))
@@ -305,10 +335,17 @@ def cpu_leg(calls, arrays, seconds):
         X, Y, ops = case_operands(c, arrays)
         oe = oracle.Expr(X, Y, c.metric, gamma=c.gamma, ops=ops)
         V = arrays[c.v] if c.v else (np.ones((Y.shape[0], 1), dtype=Y.dtype) if c.consumer == "mean" else None)
+        if c.consumer == "cg_solve":
+            # The oracle's unit of work is the product inside every
+            # iteration: timed as S @ A on the sampled rows, which is also
+            # the true residual's product for the parity check.
+            A_gpu = outs[0].cpu().numpy()
 
         def run(rows):
             if c.consumer in ("matmul", "mean"):
                 return oracle.matmul(oe, V, rows)
+            if c.consumer == "cg_solve":
+                return oracle.matmul(oe, A_gpu, rows)
             if c.consumer == "softmax_matmul":
                 return oracle.softmax_matmul(oe, V, rows)
             if c.consumer == "displacement":
@@ -335,7 +372,11 @@ def cpu_leg(calls, arrays, seconds):
                          % (c.name, len(rows), oe.N, "all %d columns" % oe.M if c.pairs is None
                             else "their kept pairs (%.0f per row on average)" % per_row))
         dtype = np.dtype(oe.np_dtype)
-        if c.consumer == "topk":
+        if c.consumer == "cg_solve":
+            from gpu_cases import solve_report
+            ok, ratio = solve_report(oe, A_gpu, V, c.params["shift"], c.params["rtol"], rows)
+            parity.append({"call": c.name, "rows": len(rows), "pass": ok, "residual_over_bound": ratio})
+        elif c.consumer == "topk":
             gv = outs[0].cpu().numpy()[rows]
             gi = outs[1].cpu().numpy()[rows]
             fails = topk_report(gv, gi, res[0], res[1], res[2], c.k, c.largest, dtype)

@@ -196,6 +196,46 @@ int pw_softmax_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, v
 int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices, void *ws, size_t ws_bytes,
             void *stream);
 
+/* ------------------------------------------------------------------------
+ * Conjugate-gradient solve (guide, Task Map, "Kernel ridge, GP mean" row:
+ * solve(K + a * eye_like(K), Y, method="cg"); "What to Check", Solvers:
+ * results carry converged and status, to be checked before the solution is
+ * used). The product with K in every iteration is pw_matmul's fused tile
+ * path; the vector steps are small reduction kernels of this library.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  PW_SOLVE_CONVERGED = 0, /* every column reached |r_c| <= rtol |b_c| */
+  PW_SOLVE_MAX_ITER = 1,  /* max_iter iterations without reaching it */
+  PW_SOLVE_BREAKDOWN = 2  /* p.(S + shift I)p <= 0 in some column: not positive definite */
+} pw_solve_status;
+
+typedef struct {
+  int converged;           /* 1 iff status == PW_SOLVE_CONVERGED */
+  int status;              /* pw_solve_status */
+  int iterations;          /* iterations run (the last check's count) */
+  double max_rel_residual; /* max over columns of |r_c| / |b_c| from the CG recurrence */
+} pw_solve_info;
+
+/* Bytes of device workspace pw_cg_solve needs for C right-hand sides. */
+int pw_cg_workspace_size(const pw_expr *e, int64_t C, size_t *bytes);
+
+/* Solve (S + shift I) A = B by conjugate gradients from A = 0, for a square
+ * bound score S (N == M) that is symmetric positive semi-definite (e.g. an
+ * rbf kernel of a set with itself), column by column:
+ *   shift       > 0 (finite)
+ *   B           [N, ldb] device matrix, C right-hand sides, 1 <= C, ldb >= C
+ *   A           [N, lda] device matrix, the solution (overwritten)
+ *   max_iter    >= 1; rtol >= 0 per column: stop when |r_c| <= rtol |b_c|
+ *   check_every >= 1: iterations between the host's convergence checks
+ *   info        host struct, filled on PW_OK
+ * Columns that converge are frozen; a zero column of B gives a zero column
+ * of A. Unlike the consumers, this call synchronises `stream` at every
+ * convergence check (a small device-to-host copy) and on return. The
+ * workspace must not be used by other work until the call returns. */
+int pw_cg_solve(const pw_expr *e, double shift, const void *B, int64_t C, int64_t ldb, void *A, int64_t lda,
+                int max_iter, double rtol, int check_every, void *ws, size_t ws_bytes, void *stream,
+                pw_solve_info *info);
+
 /* Describe the launch plan `consumer` would use (kernel family, tile sizes,
  * column splits) into buf as a NUL-terminated string. For logs and tuning. */
 int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf, size_t len);

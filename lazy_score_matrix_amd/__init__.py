@@ -53,6 +53,13 @@ class _Op(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("scalar", ctypes.c_double), ("vec", ctypes.c_void_p)]
 
 
+class _SolveInfo(ctypes.Structure):
+    _fields_ = [("converged", ctypes.c_int), ("status", ctypes.c_int), ("iterations", ctypes.c_int),
+                ("max_rel_residual", ctypes.c_double)]
+
+
+SOLVE_STATUS = {0: "converged", 1: "max_iter", 2: "breakdown"}
+
 _lock = threading.Lock()
 _lib = None
 
@@ -80,6 +87,9 @@ def load_library(path: str = LIB_PATH):
         lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
+        lib.pw_cg_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
+        lib.pw_cg_solve.argtypes = [vp, ctypes.c_double, vp, i64, i64, vp, i64, c_int, ctypes.c_double, c_int, vp, sz,
+                                    vp, ctypes.POINTER(_SolveInfo)]
         lib.pw_set_tile_events.argtypes = [vp, vp]
         lib.pw_error_string.argtypes = [c_int]
         lib.pw_error_string.restype = ctypes.c_char_p
@@ -284,6 +294,31 @@ class LazyScores:
         check(self._lib.pw_topk(self._h, int(k), int(bool(largest)), values.data_ptr(), indices.data_ptr(),
                                 ws.data_ptr(), nb, _stream(self.device)), "pw_topk")
         return values, indices
+
+    # -- solver ---------------------------------------------------------
+    def solve(self, B: torch.Tensor, shift: float, rtol: float = 1e-6, max_iter: int = 1000, check_every: int = 8,
+              out=None, workspace=None):
+        """Conjugate-gradient solution A of (S + shift I) A = B for a square,
+        symmetric positive semi-definite score (Task Map, Kernel ridge / GP
+        mean row). Returns (A, info) with info's converged, status
+        ("converged", "max_iter" or "breakdown"), iterations and
+        max_rel_residual; check them before using A."""
+        vec = B.dim() == 1
+        B2 = B[:, None] if vec else B
+        ldb = self._value(B2, "solve")
+        C = B2.shape[1]
+        A = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
+        if workspace is None:
+            n = ctypes.c_size_t()
+            check(self._lib.pw_cg_workspace_size(self._h, C, ctypes.byref(n)), "pw_cg_workspace_size")
+            workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=self.device)
+        info = _SolveInfo()
+        check(self._lib.pw_cg_solve(self._h, float(shift), B2.data_ptr(), C, ldb, A.data_ptr(), _rows(A, "out"),
+                                    int(max_iter), float(rtol), int(check_every), workspace.data_ptr(),
+                                    workspace.numel(), _stream(self.device), ctypes.byref(info)), "pw_cg_solve")
+        res = {"converged": bool(info.converged), "status": SOLVE_STATUS[info.status],
+               "iterations": int(info.iterations), "max_rel_residual": float(info.max_rel_residual)}
+        return (A[:, 0] if vec and out is None else A), res
 
     # -- views and derived reductions ----------------------------------
     def masked(self, mask) -> "LazyScores":

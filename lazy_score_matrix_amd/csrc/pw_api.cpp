@@ -737,3 +737,120 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ CG solve
+
+namespace {
+
+// Workspace of a CG solve: the kernel product's own workspace, the iterates
+// R, P, Q [N, C], the column partials and the per-column state.
+struct CgLayout {
+  size_t mm = 0, r = 0, p = 0, q = 0, part = 0, st = 0, total = 0;
+};
+
+CgLayout cg_layout(const pw_expr &e, int64_t C) {
+  CgLayout L;
+  const size_t es = esize(e.dtype);
+  const Plan mp = make_plan(e, PW_C_MATMUL, C, 0);
+  size_t off = align_up(mp.total);
+  const size_t vec = align_up((size_t)e.N * (size_t)C * es);
+  L.r = off;
+  off += vec;
+  L.p = off;
+  off += vec;
+  L.q = off;
+  off += vec;
+  L.part = off;
+  off += align_up((size_t)cg_blocks(e.N) * (size_t)C * sizeof(double));
+  L.st = off;
+  off += align_up((size_t)C * (4 * sizeof(double) + sizeof(int)));
+  L.total = off + kAlign;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pw_cg_workspace_size(const pw_expr *e, int64_t C, size_t *bytes) {
+  if (!e || !bytes || C < 1) return PW_ERR_INVALID;
+  *bytes = cg_layout(*e, C).total;
+  return PW_OK;
+}
+
+int pw_cg_solve(const pw_expr *e, double shift, const void *B, int64_t C, int64_t ldb, void *A, int64_t lda,
+                int max_iter, double rtol, int check_every, void *ws, size_t ws_bytes, void *stream,
+                pw_solve_info *info) {
+  if (!e || !info || e->N != e->M || C < 1 || ldb < C || lda < C) return PW_ERR_INVALID;
+  if (!(std::isfinite(shift) && shift > 0) || !(std::isfinite(rtol) && rtol >= 0)) return PW_ERR_INVALID;
+  if (max_iter < 1 || check_every < 1) return PW_ERR_INVALID;
+  const size_t es = esize(e->dtype);
+  if (e->N > 0 && (!B || !A)) return PW_ERR_INVALID;
+  if (!aligned(B, es) || !aligned(A, es)) return PW_ERR_INVALID;
+  if (C > INT32_MAX) return PW_ERR_UNSUPPORTED;
+  info->converged = 1;
+  info->status = PW_SOLVE_CONVERGED;
+  info->iterations = 0;
+  info->max_rel_residual = 0.0;
+  if (e->N == 0) return PW_OK;
+  const CgLayout L = cg_layout(*e, C);
+  if (!ws || ws_bytes < L.total) return PW_ERR_WORKSPACE;
+  char *base = reinterpret_cast<char *>(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+  hipStream_t s = (hipStream_t)stream;
+  const int nC = (int)C;
+  void *R = base + L.r, *P = base + L.p, *Q = base + L.q;
+  double *part = reinterpret_cast<double *>(base + L.part);
+  CgState st;
+  double *sd = reinterpret_cast<double *>(base + L.st);
+  st.rr = sd;
+  st.bb = sd + C;
+  st.alpha = sd + 2 * C;
+  st.beta = sd + 3 * C;
+  st.flag = reinterpret_cast<int *>(sd + 4 * C);
+  const int nblk = cg_blocks(e->N);
+  const double tol2 = rtol * rtol;
+  const size_t mm_bytes = L.r;  // the product's workspace sits first
+
+  int rc = hip_status(launch_cg_init(e->dtype, B, ldb, A, lda, R, P, e->N, nC, part, s));
+  if (rc == PW_OK) rc = hip_status(launch_cg_scalars(0, part, nblk, nC, st, tol2, s));
+  std::vector<int> flag(C);
+  auto running = [&](int *any_running, int *any_breakdown) -> int {
+    int r = hip_status(hipMemcpyAsync(flag.data(), st.flag, C * sizeof(int), hipMemcpyDeviceToHost, s));
+    if (r == PW_OK) r = hip_status(hipStreamSynchronize(s));
+    *any_running = *any_breakdown = 0;
+    for (int c = 0; c < nC; ++c) {
+      *any_running |= flag[c] == 1;
+      *any_breakdown |= flag[c] == 2;
+    }
+    return r;
+  };
+  int any_run = 1, any_brk = 0, it = 0;
+  if (rc == PW_OK) rc = running(&any_run, &any_brk);
+  while (rc == PW_OK && any_run && it < max_iter) {
+    rc = value_consumer(e, PW_C_MATMUL, P, C, C, Q, C, base, mm_bytes, stream);
+    if (rc == PW_OK) rc = hip_status(launch_cg_pq(e->dtype, P, Q, e->N, nC, shift, part, s));
+    if (rc == PW_OK) rc = hip_status(launch_cg_scalars(1, part, nblk, nC, st, tol2, s));
+    if (rc == PW_OK) rc = hip_status(launch_cg_update(e->dtype, P, Q, A, lda, R, e->N, nC, st, part, s));
+    if (rc == PW_OK) rc = hip_status(launch_cg_scalars(2, part, nblk, nC, st, tol2, s));
+    if (rc == PW_OK) rc = hip_status(launch_cg_direction(e->dtype, R, P, e->N, nC, st, s));
+    ++it;
+    if (rc == PW_OK && (it % check_every == 0 || it == max_iter)) rc = running(&any_run, &any_brk);
+  }
+  if (rc != PW_OK) return rc;
+  std::vector<double> rr(C), bb(C);
+  rc = hip_status(hipMemcpyAsync(rr.data(), st.rr, C * sizeof(double), hipMemcpyDeviceToHost, s));
+  if (rc == PW_OK) rc = hip_status(hipMemcpyAsync(bb.data(), st.bb, C * sizeof(double), hipMemcpyDeviceToHost, s));
+  if (rc == PW_OK) rc = hip_status(hipStreamSynchronize(s));
+  if (rc != PW_OK) return rc;
+  double worst = 0.0;
+  for (int c = 0; c < nC; ++c)
+    if (bb[c] > 0) worst = std::max(worst, std::sqrt(rr[c] / bb[c]));
+  info->iterations = it;
+  info->max_rel_residual = worst;
+  info->status = any_brk ? PW_SOLVE_BREAKDOWN : (any_run ? PW_SOLVE_MAX_ITER : PW_SOLVE_CONVERGED);
+  info->converged = info->status == PW_SOLVE_CONVERGED;
+  return PW_OK;
+}
+
+}  // extern "C"
+

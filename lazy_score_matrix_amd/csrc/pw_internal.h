@@ -180,6 +180,25 @@ constexpr int mfma_groups(int dtype) { return dtype == 0 ? 2 : 4; }
 template <class T, int METRIC>
 hipError_t mfma_launch_metric(int consumer, const MfmaConfig &cfg, const TileArgs &a, hipStream_t s);
 
+// Conjugate-gradient vector steps (cg_kernels.hip). Iterates are [N, C]
+// row-major with ld C; column partial sums are doubles [cg_blocks(N)][C].
+struct CgState {
+  double *rr, *bb, *alpha, *beta;  // per column: |r|^2, |b|^2, step sizes
+  int *flag;                       // per column: 1 running, 0 converged, 2 breakdown
+};
+constexpr int kCgRows = 1024;  // rows per reduction block
+int cg_blocks(int64_t N);
+hipError_t launch_cg_init(int dtype, const void *B, int64_t ldb, void *A, int64_t lda, void *R, void *P, int64_t N,
+                          int C, double *part, hipStream_t s);
+hipError_t launch_cg_pq(int dtype, const void *P, void *Q, int64_t N, int C, double shift, double *part,
+                        hipStream_t s);
+hipError_t launch_cg_update(int dtype, const void *P, const void *Q, void *A, int64_t lda, void *R, int64_t N, int C,
+                            CgState st, double *part, hipStream_t s);
+hipError_t launch_cg_direction(int dtype, const void *R, void *P, int64_t N, int C, CgState st, hipStream_t s);
+// phase 0: after init, 1: step sizes alpha, 2: betas and convergence.
+hipError_t launch_cg_scalars(int phase, const double *part, int nblk, int C, CgState st, double tol2,
+                             hipStream_t s);
+
 // Auxiliary kernels.
 hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s);
 // Per block of `block` entries of g[0..n): min and max, written as pairs.

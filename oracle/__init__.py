@@ -324,6 +324,21 @@ def topk(e: Expr, k, largest=False, extra=0, rows=None):
     return vals, idx, mag
 
 
+def solve(e: Expr, shift, B):
+    """The exact solution of (S + shift * I) A = B for a square score S
+    (Task Map, Kernel ridge / GP mean row: solve(K + a * eye_like(K), Y)):
+    dense oracle scores, then a dense LU solve in float64 (numpy). Returns
+    (A, cond) with cond the 2-norm condition number of S + shift * I, which
+    bounds how far an iterative solution with a small residual may sit from A.
+    """
+    if e.N != e.M:
+        raise ValueError("solve needs a square score")
+    S, _ = scores(e)
+    Kd = np.asarray(S, np.float64) + float(shift) * np.eye(e.N)
+    Bd = np.asarray(B, np.float64).reshape(e.N, -1)
+    return np.linalg.solve(Kd, Bd), float(np.linalg.cond(Kd))
+
+
 def svgd_direction(x, score, gamma, rows=None):
     """SVGD direction (K@score - 2*gamma*K.displacement()) / n with K = rbf(x, x).
 

@@ -50,11 +50,53 @@ def bind_both(X, Y, metric, gamma=1.0, ops=(), same=False):
     return e, oe
 
 
+EPS = {np.dtype(np.float32): 2.0 ** -24, np.dtype(np.float64): 2.0 ** -53}
+
+
+def solve_report(oe, A, B, shift, rtol, rows=None):
+    """Check a CG solution of (S + shift I) A = B against the oracle: the
+    true residual r = B - (S + shift I) A (oracle product, higher precision)
+    within rtol of |B| up to the recurrence's rounding drift, and, on a full
+    system, |A - A*| <= |r| / shift per column (the smallest eigenvalue of
+    S + shift I is at least shift for S positive semi-definite), A* the
+    dense solve. On a row sample the residual is compared with |B| scaled
+    to the sample's share of the rows (3x slack). Returns (ok, worst
+    residual / bound)."""
+    dtype = np.dtype(oe.np_dtype)
+    A = np.asarray(A, np.float64).reshape(oe.N, -1)
+    B64 = np.asarray(B, np.float64).reshape(oe.N, -1)
+    KA, mag = oracle.matmul(oe, A.astype(dtype), rows)
+    sel = slice(None) if rows is None else rows
+    res = B64[sel] - (np.asarray(KA, np.float64) + shift * A[sel])
+    rn = np.linalg.norm(res, axis=0)
+    drift = 8 * oe.N * EPS[dtype] * (np.linalg.norm(np.asarray(mag, np.float64), axis=0)
+                                     + shift * np.linalg.norm(A[sel], axis=0))
+    if rows is None:
+        bound = 1.05 * rtol * np.linalg.norm(B64, axis=0) + drift
+    else:
+        bound = 3 * rtol * np.sqrt(len(rows) / oe.N) * np.linalg.norm(B64, axis=0) + drift
+    ok = bool(np.all(rn <= bound + 1e-300))
+    if rows is None and ok:
+        Astar, _ = oracle.solve(oe, shift, B64.astype(dtype))
+        err = np.linalg.norm(A - Astar, axis=0)
+        ok = bool(np.all(err <= (rn + drift) / shift * 1.01 + 1e-300))
+    return ok, float(np.max(rn / np.maximum(bound, 1e-300)))
+
+
 def check_consumer(e, oe, consumer, V=None, exclude_self=False, k=0, largest=False, rows=None, exact=False,
-                   what="", report=False):
+                   what="", report=False, params=None):
     """Run `consumer` on the GPU and the oracle (optionally on a row subset of
     the oracle side) and assert parity. Returns (worst err/tol, plain rel)."""
     dtype = np.dtype(oe.np_dtype)
+    if consumer == "cg_solve":
+        p = dict(params or {})
+        A, info = e.solve(to_dev(V), p["shift"], rtol=p["rtol"], max_iter=p.get("max_iter", 1000))
+        ok, ratio = solve_report(oe, A.cpu().numpy(), V, p["shift"], p["rtol"], rows)
+        if report:
+            return ok and info["converged"], ratio, info
+        assert info["converged"], (what, info)
+        assert ok, (what, "residual / bound", ratio, info)
+        return ratio, info["max_rel_residual"]
     sel = slice(None) if rows is None else torch.as_tensor(rows, device=dev())
     vmax = float(np.max(np.abs(V))) if V is not None and V.size else 1.0
     if consumer == "matmul":

@@ -608,4 +608,27 @@ def pin_masks_vs_torch_triangles():
         _close(oracle.matmul(e, V)[0], ((S * K) @ torch.as_tensor(V)).numpy(), rtol=1e-12, atol=1e-13, what="mm")
 
 
+# ---------------------------------------------------------------- solve
+def pin_solve_two_points_closed_form():
+    """Two points at distance 1, rbf gamma: K + aI = [[1+a, e], [e, 1+a]]
+    with e = exp(-gamma); its inverse applied to b = (1, 2) is written out
+    from the 2x2 inverse formula."""
+    g, a = 0.7, 0.25
+    X = np.array([[0.0], [1.0]])
+    A, cond = oracle.solve(oracle.Expr(X, X, "rbf", gamma=g), a, np.array([[1.0], [2.0]]))
+    e, d = math.exp(-g), 1 + a
+    det = d * d - e * e
+    want = np.array([[(d * 1 - e * 2) / det], [(-e * 1 + d * 2) / det]])
+    _close(A, want, rtol=1e-14, atol=1e-15, what="2x2 solve")
+    assert abs(cond - (d + e) / (d - e)) < 1e-12 * cond
+
+
+def pin_solve_shift_only():
+    """With X far apart (rbf ~ identity), (K + aI) A = B gives A = B / (1 + a)."""
+    X = (100.0 * np.arange(5, dtype=np.float64))[:, None]
+    B = _rng(120).standard_normal((5, 3))
+    A, _ = oracle.solve(oracle.Expr(X, X, "rbf", gamma=1.0), 3.0, B)
+    _close(A, B / 4.0, rtol=1e-14, atol=1e-15, what="shift only")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -188,3 +188,40 @@ def test_product_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "liboracle" not in text, f
+
+
+def test_cg_solve_validation(lib):
+    """pw_cg_solve rejects bad arguments on the host before any launch."""
+    ok, h = bind(lib, N=12, M=12)
+    assert ok == pw.PW_OK
+    info = pw._SolveInfo()
+    n = ctypes.c_size_t()
+    assert lib.pw_cg_workspace_size(h, 3, ctypes.byref(n)) == pw.PW_OK and n.value > 0
+    assert lib.pw_cg_workspace_size(h, 0, ctypes.byref(n)) == pw.PW_ERR_INVALID
+
+    def call(shift=1.0, B=FAKE, C=3, ldb=3, A=FAKE, lda=3, max_iter=10, rtol=1e-6, check_every=4, ws=FAKE,
+             ws_bytes=1 << 30, inf=True, handle=h):
+        return lib.pw_cg_solve(handle, shift, B, C, ldb, A, lda, max_iter, rtol, check_every, ws, ws_bytes, None,
+                               ctypes.byref(info) if inf else None)
+
+    assert call(shift=0.0) == pw.PW_ERR_INVALID
+    assert call(shift=-1.0) == pw.PW_ERR_INVALID
+    assert call(shift=float("inf")) == pw.PW_ERR_INVALID
+    assert call(C=0) == pw.PW_ERR_INVALID
+    assert call(ldb=2) == pw.PW_ERR_INVALID
+    assert call(lda=2) == pw.PW_ERR_INVALID
+    assert call(max_iter=0) == pw.PW_ERR_INVALID
+    assert call(check_every=0) == pw.PW_ERR_INVALID
+    assert call(rtol=-1.0) == pw.PW_ERR_INVALID
+    assert call(B=0) == pw.PW_ERR_INVALID
+    assert call(A=FAKE + 2) == pw.PW_ERR_INVALID
+    assert call(inf=False) == pw.PW_ERR_INVALID
+    assert call(ws=0) == pw.PW_ERR_WORKSPACE
+    assert call(ws_bytes=n.value - 1) == pw.PW_ERR_WORKSPACE
+    lib.pw_release(h)
+    ok, h2 = bind(lib, N=12, M=13)          # not square
+    assert call(handle=h2) == pw.PW_ERR_INVALID
+    lib.pw_release(h2)
+    ok, h3 = bind(lib, N=0, M=0, X=0, Y=0)  # empty system: converged, nothing launched
+    assert call(handle=h3, B=0, A=0) == pw.PW_OK and info.converged == 1 and info.iterations == 0
+    lib.pw_release(h3)

@@ -24,12 +24,13 @@ def test_full_size_workload(name):
         rows = workloads.sample_rows(oe.N, stride=STRIDE.get(name, 61))
         V = arrays[c.v] if c.v else None
         ratio, rel = check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k,
-                                    largest=c.largest, rows=rows, what="%s/%s" % (name, c.name))
+                                    largest=c.largest, rows=rows, what="%s/%s" % (name, c.name),
+                                    params=c.params)
         print("%s/%s: %d rows, worst err/tol %.3g, plan %s" % (name, c.name, len(rows), ratio,
                                                               e.plan(*_plan_args(c, V))))
 
 
 def _plan_args(c, V):
-    if c.consumer == "mean":
+    if c.consumer in ("mean", "cg_solve"):
         return "matmul", 1, 0
     return c.consumer, V.shape[1] if V is not None else 0, c.k

@@ -41,7 +41,7 @@ def _randn(g, *shape):
 class Case:
     """One consumer call on a workload."""
     name: str
-    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk | mean
+    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk | mean | cg_solve
     x: str                   # array used as X
     y: str                   # array used as Y
     metric: str
@@ -53,6 +53,7 @@ class Case:
     largest: bool = False
     transpose: bool = False  # reduce over rows instead (the transposed score)
     pairs: int | None = None  # pairs the masks keep (None: all N * M)
+    params: dict = field(default_factory=dict)  # consumer settings (cg_solve: shift, rtol, max_iter)
 
 
 def rbf_small(n: int = 1024, m: int | None = None, d: int = 3, seed: int = 1001):
@@ -214,6 +215,21 @@ def attention_packed(n: int = 16384, d: int = 64, c: int = 64, min_len: int = 25
     return arrays, cases
 
 
+def kernel_ridge(n: int = 65536, d: int = 16, seed: int = 1012):
+    """Kernel ridge regression / GP mean, float32 (Task Map, Kernel ridge row:
+    solve(K + a * eye_like(K), Y, method="cg")): x ~ N(0, I) [n, 16], rbf
+    gamma = 1/32, targets y = sin(x . w) + 0.1 noise with w ~ N(0, I/16),
+    a = 10, relative residual 1e-3."""
+    g = _gen(seed)
+    X = _randn(g, n, d)
+    w = _randn(g, d) / 4.0
+    y = torch.sin(X @ w)[:, None] + 0.1 * _randn(g, n, 1)
+    arrays = {"x": X.to(torch.float32).numpy(), "y": y.to(torch.float32).numpy()}
+    cases = [Case("kernel_ridge", "cg_solve", "x", "x", "rbf", gamma=1.0 / 32, v="y",
+                  params={"shift": 10.0, "rtol": 1e-3, "max_iter": 1000})]
+    return arrays, cases
+
+
 def resolve(arg, arrays):
     """An op argument with array names replaced by the arrays."""
     if isinstance(arg, str):
@@ -236,6 +252,7 @@ WORKLOADS = {
     "feature_mean": (feature_mean, {}, {"n": 800, "m": 1000}),
     "attention_causal": (attention_causal, {}, {"n": 700}),
     "attention_packed": (attention_packed, {}, {"n": 900, "min_len": 40, "max_len": 300}),
+    "kernel_ridge": (kernel_ridge, {}, {"n": 900}),
 }
 
 

@@ -102,6 +102,8 @@ def _open(path: str):
     lib.oracle_logsumexp.argtypes = [pe, ctypes.c_int, p64, i64, vp, vp]
     lib.oracle_softmax_matmul.argtypes = [pe, vp, i64, i64, p64, i64, vp, vp]
     lib.oracle_topk.argtypes = [pe, ctypes.c_int, ctypes.c_int, p64, i64, vp, p64, vp]
+    lib.oracle_backward.argtypes = [pe, ctypes.c_int, vp, i64, vp, i64, i64, ctypes.c_int, p64, ctypes.c_int,
+                                    p64, i64, p64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_real_size.argtypes = [ctypes.c_int]
@@ -168,6 +170,7 @@ class Expr:
         kinds, scalars, vecs = [], [], []
         row_mask = col_mask = groups = None
         upper = lower = None
+        self.op_list = []  # the score arithmetic ops, masks left out
         for name, arg in ops:
             if name in MASKS:
                 if name == "mask_rows":
@@ -197,6 +200,7 @@ class Expr:
                     groups = (gr, gc)
                 continue
             kinds.append(OPS[name])
+            self.op_list.append((name, arg))
             if name in ("mul", "add"):
                 scalars.append(float(arg))
                 vecs.append(None)
@@ -322,6 +326,63 @@ def topk(e: Expr, k, largest=False, extra=0, rows=None):
     lib.oracle_topk(ctypes.byref(e._c), kk, int(bool(largest)), _rp(r), n, vals.ctypes.data,
                     idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), mag.ctypes.data)
     return vals, idx, mag
+
+
+CONSUMER_CODES = {"matmul": 0, "displacement": 1, "logsumexp": 2, "softmax_matmul": 3, "topk": 4}
+
+
+def backward(e: Expr, consumer, G, V=None, exclude_self=False, indices=None, rows=None, cols=None):
+    """First-order gradients of a consumer's output contracted with the
+    upstream gradient G (guide: backward by replay; selections route
+    gradients through the selected pairs only), per pair from the chain rule
+    (see oracle.cpp). Row-side results (dX, row-op grads) for `rows`,
+    column-side results (dY, dV, column-op grads) for `cols` (all by
+    default). Returns a dict of arrays and their absolute-term scales:
+    dX, dY, dV, and "ops": per op its grad (rows or columns, None for a
+    scalar op), each as (value, mag)."""
+    lib = _load()
+    code = CONSUMER_CODES[consumer]
+    G = np.ascontiguousarray(np.asarray(G, dtype=e.np_dtype))
+    if G.ndim == 1:
+        G = G[:, None]
+    if G.shape[0] != e.N:
+        raise ValueError("G needs N rows")
+    if V is not None:
+        V, ldv = e._V(V)
+        C = V.shape[1]
+    else:
+        V, ldv, C = None, 0, 0
+    idx = None
+    k = 0
+    if indices is not None:
+        idx = np.ascontiguousarray(np.asarray(indices, dtype=np.int64))
+        k = idx.shape[1]
+    r = np.arange(e.N, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, np.int64))
+    c = np.arange(e.M, dtype=np.int64) if cols is None else np.ascontiguousarray(np.asarray(cols, np.int64))
+    nr, nc = r.shape[0], c.shape[0]
+    n_ops = len(e._kinds) if e._c.n_ops else 0
+    buf = {}
+    for name, shape in (("dX", (nr, e.D)), ("dY", (nc, e.D)), ("dV", (nc, max(C, 1))),
+                        ("dOr", (max(n_ops, 1), nr)), ("dOc", (max(n_ops, 1), nc))):
+        buf[name] = np.zeros(shape, dtype=e.real)
+        buf[name + "m"] = np.zeros(shape, dtype=e.real)
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_backward(ctypes.byref(e._c), code, G.ctypes.data, G.shape[1], None if V is None else V.ctypes.data, C,
+                        ldv, int(bool(exclude_self)), None if idx is None else idx.ctypes.data_as(p64), k,
+                        r.ctypes.data_as(p64), nr, c.ctypes.data_as(p64), nc,
+                        *[buf[n].ctypes.data for n in ("dX", "dXm", "dY", "dYm", "dV", "dVm", "dOr", "dOrm", "dOc",
+                                                       "dOcm")])
+    ops = []
+    names = [n for n, _ in e.op_list]
+    for t, name in enumerate(names):
+        if name in ("add_rows", "weight_rows"):
+            ops.append((buf["dOr"][t], buf["dOrm"][t]))
+        elif name in ("add_columns", "weight_columns"):
+            ops.append((buf["dOc"][t], buf["dOcm"][t]))
+        else:
+            ops.append(None)
+    return {"dX": (buf["dX"], buf["dXm"]), "dY": (buf["dY"], buf["dYm"]),
+            "dV": (buf["dV"][:, :C], buf["dVm"][:, :C]), "ops": ops}
 
 
 def solve(e: Expr, shift, B):

@@ -390,6 +390,292 @@ void do_topk(const oracle_expr &ex, int kk, int largest, const int64_t *rows, in
   }
 }
 
+// ------------------------------------------------------------------ backward
+// First-order gradients of each consumer's output, contracted with an
+// upstream gradient G, with respect to X, Y, V and every op vector (guide,
+// opening section: backward replays the pairs instead of storing them;
+// "What to Check", Gradients: selections route gradients through the
+// selected pairs only). Written per pair from the chain rule:
+//   forward   t_0 = f(x_i, y_j), t_k = op_k(t_{k-1}), s = t_n
+//   dS        matmul        G_i . V_j
+//             displacement  G_i . (y_j - x_i)
+//             logsumexp     g_i exp(s - lse_i)
+//             softmax@V     P_ij (G_i . V_j - sum_j' P_ij' G_i . V_j'),  P = exp(s - lse_i)
+//             top-k         G_ip at the selected pairs (i, idx_ip), else 0
+//   ops       back through the list: MUL c: c d; ADD_ROWS a: grad a_i += d;
+//             MUL_ROWS w: grad w_i += d t_{k-1}, d <- w_i d; EXP: d <- d t_k
+//             (and the column forms)
+//   metric    dX_i += d_0 df/dx_i, dY_j += d_0 df/dy_j with
+//             linear df/dx = y; sqeuclidean 2(x - y); rbf -2 gamma f (x - y);
+//             cosine -(y/(|x||y|) - (x.y) x/(|x|^3 |y|)) (0 for a zero vector)
+//   direct    matmul dV_j += s G_i; softmax dV_j += P_ij G_i;
+//             displacement dX_i -= s G_i, dY_j += s G_i
+// Masked and excluded pairs contribute nothing. Row-side outputs (dX, row
+// op vectors) are returned for a list of rows, column-side outputs (dY,
+// dV, column op vectors) for a list of columns; each is computed over all
+// pairs it depends on. `mag` arrays hold the same sums taken over absolute
+// values of every term (the scale of their rounding).
+template <class T>
+struct Backward {
+  using R = RealOf<T>;
+  const oracle_expr &ex;
+  Expr<T, R> E;
+  int consumer;
+  const T *G;
+  int64_t ldg;
+  const T *V;
+  int64_t C, ldv;
+  int exclude_self;
+  const int64_t *idx;
+  int k;
+  std::vector<R> lse, delta;  // per row, for logsumexp / softmax
+
+  Backward(const oracle_expr &e_, int cons, const T *G_, int64_t ldg_, const T *V_, int64_t C_, int64_t ldv_,
+           int excl, const int64_t *idx_, int k_)
+      : ex(e_), E(e_), consumer(cons), G(G_), ldg(ldg_), V(V_), C(C_), ldv(ldv_), exclude_self(excl), idx(idx_),
+        k(k_) {}
+
+  bool kept(int64_t i, int64_t j) const {
+    if (consumer == 2 && exclude_self && i == j) return false;
+    return E.keep(i, j);
+  }
+  R g(int64_t i, int64_t c) const { return (R)G[i * ldg + c]; }
+  R v(int64_t j, int64_t c) const { return (R)V[j * ldv + c]; }
+  R gv(int64_t i, int64_t j) const {
+    R a = 0;
+    for (int64_t c = 0; c < C; ++c) a += g(i, c) * v(j, c);
+    return a;
+  }
+  R gv_abs(int64_t i, int64_t j) const {
+    R a = 0;
+    for (int64_t c = 0; c < C; ++c) a += std::fabs(g(i, c) * v(j, c));
+    return a;
+  }
+
+  // Per-row log-sum-exp and, for softmax, Delta_i = sum_j P_ij G_i.V_j
+  // (two passes over the row, as the forward oracle does).
+  void row_stats(int64_t i) {
+    R m = -std::numeric_limits<R>::infinity();
+    for (int64_t j = 0; j < ex.M; ++j) {
+      if (!kept(i, j)) continue;
+      R mu;
+      m = std::max(m, E.score(i, j, &mu));
+    }
+    R l = 0, d = 0;
+    if (m != -std::numeric_limits<R>::infinity()) {
+      for (int64_t j = 0; j < ex.M; ++j) {
+        if (!kept(i, j)) continue;
+        R mu;
+        R p = rexp(E.score(i, j, &mu) - m);
+        l += p;
+        if (consumer == 3) d += p * gv(i, j);
+      }
+    }
+    lse[i] = l > 0 ? m + rlog(l) : -std::numeric_limits<R>::infinity();
+    delta[i] = l > 0 ? d / l : 0;
+  }
+  void all_row_stats() {
+    if (consumer != 2 && consumer != 3) return;
+    lse.assign(ex.N, 0);
+    delta.assign(ex.N, 0);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < ex.N; ++i) row_stats(i);
+  }
+
+  // Forward values t_0..t_n of pair (i, j).
+  void forward(int64_t i, int64_t j, R *t) const {
+    R mu;
+    // The metric alone: score() with the ops applied is replayed below.
+    oracle_expr bare = ex;
+    bare.n_ops = 0;
+    Expr<T, R> B(bare);
+    t[0] = B.score(i, j, &mu);
+    for (int op = 0; op < ex.n_ops; ++op) {
+      R x = t[op];
+      switch (ex.op_kind[op]) {
+        case OP_MUL: x = (R)ex.op_scalar[op] * x; break;
+        case OP_ADD: x = x + (R)ex.op_scalar[op]; break;
+        case OP_ADD_ROWS: x = x + E.vec(op, i); break;
+        case OP_ADD_COLS: x = x + E.vec(op, j); break;
+        case OP_MUL_ROWS: x = E.vec(op, i) * x; break;
+        case OP_MUL_COLS: x = E.vec(op, j) * x; break;
+        case OP_EXP: x = rexp(x); break;
+      }
+      t[op + 1] = x;
+    }
+  }
+
+  // Upstream dS of pair (i, j) (and its absolute-term scale), given s.
+  R dS(int64_t i, int64_t j, R s, R *scale) const {
+    switch (consumer) {
+      case 0: *scale = gv_abs(i, j); return gv(i, j);
+      case 1: {
+        R a = 0, b = 0;
+        for (int64_t d = 0; d < ex.D; ++d) {
+          R t = g(i, d) * (E.y(j, d) - E.x(i, d));
+          a += t;
+          b += std::fabs(g(i, d)) * (std::fabs(E.y(j, d)) + std::fabs(E.x(i, d)));
+        }
+        *scale = b;
+        return a;
+      }
+      case 2: {
+        R p = rexp(s - lse[i]);
+        *scale = std::fabs((R)G[i * ldg]) * p;
+        return (R)G[i * ldg] * p;
+      }
+      case 3: {
+        R p = rexp(s - lse[i]);
+        *scale = p * (gv_abs(i, j) + std::fabs(delta[i]));
+        return p * (gv(i, j) - delta[i]);
+      }
+      default: {  // top-k: the selected positions of row i equal to j
+        R a = 0;
+        for (int p = 0; p < k; ++p)
+          if (idx[i * k + p] == j) a += (R)G[i * ldg + p];
+        *scale = std::fabs(a);
+        return a;
+      }
+    }
+  }
+
+  // df/dx_i (side 0) or df/dy_j (side 1) in out[D], given f = t[0].
+  void metric_grad(int64_t i, int64_t j, R f, int side, R *out) const {
+    const int64_t D = ex.D;
+    if (ex.metric == M_LINEAR) {
+      for (int64_t d = 0; d < D; ++d) out[d] = side == 0 ? E.y(j, d) : E.x(i, d);
+    } else if (ex.metric == M_SQEUCLIDEAN || ex.metric == M_RBF) {
+      R c = ex.metric == M_SQEUCLIDEAN ? (R)2 : (R)-2 * (R)ex.gamma * f;
+      if (side == 1) c = -c;
+      for (int64_t d = 0; d < D; ++d) out[d] = c * (E.x(i, d) - E.y(j, d));
+    } else {
+      R dot = 0, nx = 0, ny = 0;
+      for (int64_t d = 0; d < D; ++d) {
+        dot += E.x(i, d) * E.y(j, d);
+        nx += E.x(i, d) * E.x(i, d);
+        ny += E.y(j, d) * E.y(j, d);
+      }
+      if (!(nx > 0 && ny > 0)) {
+        for (int64_t d = 0; d < D; ++d) out[d] = 0;
+        return;
+      }
+      R a = std::sqrt(nx), b = std::sqrt(ny);
+      for (int64_t d = 0; d < D; ++d) {
+        if (side == 0) out[d] = -(E.y(j, d) / (a * b) - dot * E.x(i, d) / (a * a * a * b));
+        else out[d] = -(E.x(i, d) / (a * b) - dot * E.y(j, d) / (b * b * b * a));
+      }
+    }
+  }
+
+  // Accumulate pair (i, j) into the side's outputs (row i for side 0,
+  // column j for side 1).
+  void pair(int64_t i, int64_t j, int side, R *gx, R *gxm, R *gvout, R *gvm, R *gops, R *gopsm) const {
+    if (!kept(i, j)) return;
+    R t[17];
+    forward(i, j, t);
+    const int n = ex.n_ops;
+    R sc;
+    R d = dS(i, j, t[n], &sc);
+    R dm = sc;
+    // direct terms
+    if (side == 1 && consumer == 0)
+      for (int64_t c = 0; c < C; ++c) {
+        gvout[c] += t[n] * g(i, c);
+        gvm[c] += std::fabs(t[n] * g(i, c));
+      }
+    if (side == 1 && consumer == 3) {
+      R p = rexp(t[n] - lse[i]);
+      for (int64_t c = 0; c < C; ++c) {
+        gvout[c] += p * g(i, c);
+        gvm[c] += std::fabs(p * g(i, c));
+      }
+    }
+    if (consumer == 1)
+      for (int64_t dd = 0; dd < ex.D; ++dd) {
+        R w = t[n] * g(i, dd);
+        gx[dd] += side == 0 ? -w : w;
+        gxm[dd] += std::fabs(w);
+      }
+    // back through the ops
+    for (int op = n - 1; op >= 0; --op) {
+      const int kind = ex.op_kind[op];
+      switch (kind) {
+        case OP_MUL: d = (R)ex.op_scalar[op] * d; dm = std::fabs((R)ex.op_scalar[op]) * dm; break;
+        case OP_ADD: break;
+        case OP_ADD_ROWS:
+          if (side == 0) { gops[op] += d; gopsm[op] += dm; }
+          break;
+        case OP_ADD_COLS:
+          if (side == 1) { gops[op] += d; gopsm[op] += dm; }
+          break;
+        case OP_MUL_ROWS:
+          if (side == 0) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]); }
+          d = E.vec(op, i) * d;
+          dm = std::fabs(E.vec(op, i)) * dm;
+          break;
+        case OP_MUL_COLS:
+          if (side == 1) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]); }
+          d = E.vec(op, j) * d;
+          dm = std::fabs(E.vec(op, j)) * dm;
+          break;
+        case OP_EXP: d = d * t[op + 1]; dm = dm * t[op + 1]; break;
+      }
+    }
+    R mg[64];
+    metric_grad(i, j, t[0], side, mg);
+    for (int64_t dd = 0; dd < ex.D; ++dd) {
+      gx[dd] += d * mg[dd];
+      gxm[dd] += std::fabs(dm * mg[dd]);
+    }
+  }
+};
+
+template <class T>
+void do_backward(const oracle_expr &ex, int consumer, const T *G, int64_t ldg, const T *V, int64_t C, int64_t ldv,
+                 int exclude_self, const int64_t *idx, int k, const int64_t *rows, int64_t n_rows,
+                 const int64_t *cols, int64_t n_cols, RealOf<T> *dX, RealOf<T> *dXm, RealOf<T> *dY, RealOf<T> *dYm,
+                 RealOf<T> *dV, RealOf<T> *dVm, RealOf<T> *dOr, RealOf<T> *dOrm, RealOf<T> *dOc, RealOf<T> *dOcm) {
+  using R = RealOf<T>;
+  Backward<T> B(ex, consumer, G, ldg, V, C, ldv, exclude_self, idx, k);
+  B.all_row_stats();
+  const int64_t D = ex.D;
+  const int no = ex.n_ops;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t i = rows[r];
+    std::vector<R> gx(D, 0), gxm(D, 0), gops(no + 1, 0), gopsm(no + 1, 0);
+    for (int64_t j = 0; j < ex.M; ++j) B.pair(i, j, 0, gx.data(), gxm.data(), nullptr, nullptr, gops.data(), gopsm.data());
+    for (int64_t d = 0; d < D; ++d) {
+      dX[r * D + d] = gx[d];
+      dXm[r * D + d] = gxm[d];
+    }
+    for (int op = 0; op < no; ++op) {
+      dOr[op * n_rows + r] = gops[op];
+      dOrm[op * n_rows + r] = gopsm[op];
+    }
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t q = 0; q < n_cols; ++q) {
+    const int64_t j = cols[q];
+    std::vector<R> gy(D, 0), gym(D, 0), gv(std::max<int64_t>(C, 1), 0), gvm(std::max<int64_t>(C, 1), 0),
+        gops(no + 1, 0), gopsm(no + 1, 0);
+    for (int64_t i = 0; i < ex.N; ++i)
+      B.pair(i, j, 1, gy.data(), gym.data(), gv.data(), gvm.data(), gops.data(), gopsm.data());
+    for (int64_t d = 0; d < D; ++d) {
+      dY[q * D + d] = gy[d];
+      dYm[q * D + d] = gym[d];
+    }
+    for (int64_t c = 0; c < C; ++c) {
+      dV[q * C + c] = gv[c];
+      dVm[q * C + c] = gvm[c];
+    }
+    for (int op = 0; op < no; ++op) {
+      dOc[op * n_cols + q] = gops[op];
+      dOcm[op * n_cols + q] = gopsm[op];
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -444,6 +730,28 @@ void oracle_topk(const oracle_expr *e, int kk, int largest, const int64_t *rows,
     do_topk<float>(*e, kk, largest, rows, n_rows, (double *)values, indices, (double *)mag);
   else
     do_topk<double>(*e, kk, largest, rows, n_rows, (long double *)values, indices, (long double *)mag);
+}
+
+// Backward of `consumer` (0 matmul, 1 displacement, 2 logsumexp, 3 softmax
+// matmul, 4 top-k) contracted with G: row-side outputs for `rows`
+// (dX [n_rows, D], row-op grads [n_ops, n_rows]) and column-side outputs for
+// `cols` (dY [n_cols, D], dV [n_cols, C], column-op grads [n_ops, n_cols]);
+// each with its absolute-term scale (the *_mag arrays). G is [N, ldg]: C
+// columns (matmul, softmax), D (displacement), 1 (logsumexp), k (top-k,
+// with the forward's indices idx [N, k]).
+void oracle_backward(const oracle_expr *e, int consumer, const void *G, int64_t ldg, const void *V, int64_t C,
+                     int64_t ldv, int exclude_self, const int64_t *idx, int k, const int64_t *rows, int64_t n_rows,
+                     const int64_t *cols, int64_t n_cols, void *dX, void *dXm, void *dY, void *dYm, void *dV,
+                     void *dVm, void *dOr, void *dOrm, void *dOc, void *dOcm) {
+  if (e->dtype == 0)
+    do_backward<float>(*e, consumer, (const float *)G, ldg, (const float *)V, C, ldv, exclude_self, idx, k, rows,
+                       n_rows, cols, n_cols, (double *)dX, (double *)dXm, (double *)dY, (double *)dYm, (double *)dV,
+                       (double *)dVm, (double *)dOr, (double *)dOrm, (double *)dOc, (double *)dOcm);
+  else
+    do_backward<double>(*e, consumer, (const double *)G, ldg, (const double *)V, C, ldv, exclude_self, idx, k, rows,
+                        n_rows, cols, n_cols, (long double *)dX, (long double *)dXm, (long double *)dY,
+                        (long double *)dYm, (long double *)dV, (long double *)dVm, (long double *)dOr,
+                        (long double *)dOrm, (long double *)dOc, (long double *)dOcm);
 }
 
 }  // extern "C"

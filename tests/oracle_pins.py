@@ -631,4 +631,175 @@ def pin_solve_shift_only():
     _close(A, B / 4.0, rtol=1e-14, atol=1e-15, what="shift only")
 
 
+# ---------------------------------------------------------------- backward
+def _autograd_reference(X, Y, metric, gamma, ops, consumer, G, V=None, exclude_self=False, masks=(), indices=None):
+    """Gradients of sum(out * G) by torch autograd on the dense float64
+    computation: library routines only (cdist, cosine_similarity,
+    logsumexp, softmax, matmul, gather)."""
+    Xt = torch.tensor(np.asarray(X, np.float64), requires_grad=True)
+    Yt = torch.tensor(np.asarray(Y, np.float64), requires_grad=True)
+    leaves = [Xt, Yt]
+    Vt = None
+    if V is not None:
+        Vt = torch.tensor(np.asarray(V, np.float64), requires_grad=True)
+        leaves.append(Vt)
+    if metric == "linear":
+        S = Xt @ Yt.T
+    elif metric == "cosine_distances":
+        S = 1 - torch.nn.functional.cosine_similarity(Xt[:, None, :], Yt[None, :, :], dim=-1, eps=1e-300)
+    else:
+        diff = Xt[:, None, :] - Yt[None, :, :]
+        S = (diff * diff).sum(-1)
+        if metric == "rbf":
+            S = torch.exp(-gamma * S)
+    vec_leaves = []
+    for name, arg in ops:
+        if name in ("mul", "add"):
+            S = S * arg if name == "mul" else S + arg
+            vec_leaves.append(None)
+        elif name == "exp":
+            S = torch.exp(S)
+            vec_leaves.append(None)
+        else:
+            a = torch.tensor(np.asarray(arg, np.float64), requires_grad=True)
+            vec_leaves.append(a)
+            if name == "add_rows":
+                S = S + a[:, None]
+            elif name == "add_columns":
+                S = S + a[None, :]
+            elif name == "weight_rows":
+                S = S * a[:, None]
+            else:
+                S = S * a[None, :]
+    N, M = S.shape
+    keep = torch.ones(N, M, dtype=torch.bool)
+    for name, arg in masks:
+        if name == "causal":
+            keep &= torch.ones(N, M, dtype=torch.bool).tril(arg)
+        elif name == "mask_columns":
+            keep &= torch.as_tensor(np.asarray(arg, bool))[None, :]
+    if consumer == "logsumexp" and exclude_self:
+        keep &= ~torch.eye(N, M, dtype=torch.bool)
+    Gt = torch.as_tensor(np.asarray(G, np.float64))
+    if consumer == "matmul":
+        out = torch.where(keep, S, torch.zeros_like(S)) @ Vt
+    elif consumer == "displacement":
+        Sk = torch.where(keep, S, torch.zeros_like(S))
+        out = Sk @ Yt - Sk.sum(1, keepdim=True) * Xt
+    elif consumer == "logsumexp":
+        out = torch.logsumexp(S.masked_fill(~keep, float("-inf")), -1)[:, None]
+    elif consumer == "softmax_matmul":
+        out = torch.softmax(S.masked_fill(~keep, float("-inf")), -1) @ Vt
+    else:
+        out = torch.gather(S, 1, torch.as_tensor(indices))
+    loss = (out * Gt.reshape(out.shape)).sum()
+    wanted = leaves + [a for a in vec_leaves if a is not None]
+    grads = torch.autograd.grad(loss, wanted, allow_unused=True)
+    res = {"dX": grads[0], "dY": grads[1]}
+    if Vt is not None:
+        res["dV"] = grads[2]
+    it = iter(grads[len(leaves):])
+    res["ops"] = [None if a is None else next(it) for a in vec_leaves]
+    return res
+
+
+def _compare_backward(got, ref, what, rtol=1e-10):
+    def z(t):
+        return np.zeros(1) if t is None else np.asarray(t.detach().numpy() if torch.is_tensor(t) else t, np.float64)
+    for key in ("dX", "dY") + (("dV",) if "dV" in ref else ()):
+        val, mag = got[key]
+        want = z(ref[key])
+        tol = rtol * (np.asarray(mag, np.float64) + np.abs(want)) + 1e-300
+        assert np.all(np.abs(np.asarray(val, np.float64) - want) <= tol), (what, key, np.max(np.abs(val - want)))
+    for t, (g, r) in enumerate(zip(got["ops"], ref["ops"])):
+        if r is None:
+            continue
+        val, mag = g
+        want = z(r)
+        tol = rtol * (np.asarray(mag, np.float64) + np.abs(want)) + 1e-300
+        assert np.all(np.abs(np.asarray(val, np.float64) - want) <= tol), (what, "op %d" % t)
+
+
+def pin_backward_vs_autograd():
+    """Every consumer and metric, an op chain with every vector kind and an
+    exp, against torch autograd of the dense float64 computation."""
+    r = _rng(130)
+    N, M, D, C = 7, 9, 3, 2
+    X = r.standard_normal((N, D))
+    Y = r.standard_normal((M, D))
+    V = r.standard_normal((M, C))
+    chains = {
+        "plain": [("mul", 0.7)],
+        "rows_cols": [("mul", -0.5), ("add_rows", r.standard_normal(N)), ("add_columns", r.standard_normal(M)),
+                      ("weight_rows", 0.5 + r.random(N)), ("weight_columns", 0.5 + r.random(M)), ("add", 0.1)],
+        "exp": [("mul", -0.3), ("exp", None), ("weight_columns", r.random(M) + 0.2), ("add_rows", r.standard_normal(N))],
+    }
+    for metric in ("linear", "sqeuclidean", "rbf", "cosine_distances"):
+        for cname, ops in chains.items():
+            for consumer in ("matmul", "displacement", "logsumexp", "softmax_matmul"):
+                G = r.standard_normal((N, {"matmul": C, "softmax_matmul": C, "displacement": D}.get(consumer, 1)))
+                Vc = V if consumer in ("matmul", "softmax_matmul") else None
+                e = oracle.Expr(X, Y, metric, gamma=0.4, ops=ops)
+                got = oracle.backward(e, consumer, G, Vc)
+                ref = _autograd_reference(X, Y, metric, 0.4, ops, consumer, G, Vc)
+                _compare_backward(got, ref, "%s/%s/%s" % (metric, cname, consumer))
+
+
+def pin_backward_masks_and_selection():
+    """Masked pairs (causal, column mask), the excluded self pair, and
+    top-k gradients routed through the selected pairs only."""
+    r = _rng(131)
+    N = M = 8
+    X = r.standard_normal((N, 4))
+    V = r.standard_normal((M, 3))
+    keep = r.random(M) < 0.7
+    for consumer in ("matmul", "logsumexp", "softmax_matmul"):
+        G = r.standard_normal((N, 3 if consumer != "logsumexp" else 1))
+        Vc = V if consumer != "logsumexp" else None
+        masks = [("causal", 1), ("mask_columns", keep)]
+        e = oracle.Expr(X, X, "linear", ops=[("mul", 0.5)] + masks)
+        got = oracle.backward(e, consumer, G, Vc)
+        ref = _autograd_reference(X, X, "linear", 1.0, [("mul", 0.5)], consumer, G, Vc, masks=masks)
+        # X is both operands here: the torch leaves are separate copies, so
+        # the gradient of X is the sum of the two sides.
+        _compare_backward(got, ref, "masked %s" % consumer)
+    G = r.standard_normal((N, 1))
+    e = oracle.Expr(X, X, "sqeuclidean", ops=[("mul", -1.0)])
+    got = oracle.backward(e, "logsumexp", G, exclude_self=True)
+    ref = _autograd_reference(X, X, "sqeuclidean", 1.0, [("mul", -1.0)], "logsumexp", G, exclude_self=True)
+    _compare_backward(got, ref, "exclude_self")
+    v, idx, _ = oracle.topk(oracle.Expr(X, X, "sqeuclidean"), 3)
+    G = r.standard_normal((N, 3))
+    e = oracle.Expr(X, X, "sqeuclidean")
+    got = oracle.backward(e, "topk", G, indices=idx)
+    ref = _autograd_reference(X, X, "sqeuclidean", 1.0, [], "topk", G, indices=idx)
+    _compare_backward(got, ref, "topk")
+
+
+def pin_backward_finite_differences():
+    """Central differences of the oracle's own forward (no autograd): dX
+    of an rbf kernel product and of a log-sum-exp with a column bias."""
+    r = _rng(132)
+    X = r.standard_normal((4, 2))
+    Y = r.standard_normal((5, 2))
+    V = r.standard_normal((5, 2))
+    G = r.standard_normal((4, 2))
+    b = r.standard_normal(5)
+    h = 1e-6
+    for consumer, ops, Gc in (("matmul", [], G), ("logsumexp", [("mul", -0.5), ("add_columns", b)], G[:, :1])):
+        got = oracle.backward(oracle.Expr(X, Y, "rbf", 0.6, ops), consumer, Gc, V if consumer == "matmul" else None)
+        fd = np.zeros_like(X)
+        for i in range(4):
+            for d in range(2):
+                vals = []
+                for sgn in (1, -1):
+                    Xp = X.copy()
+                    Xp[i, d] += sgn * h
+                    e = oracle.Expr(Xp, Y, "rbf", 0.6, ops)
+                    out = oracle.matmul(e, V)[0] if consumer == "matmul" else oracle.logsumexp(e)[0][:, None]
+                    vals.append(float(np.sum(np.asarray(out, np.float64) * Gc)))
+                fd[i, d] = (vals[0] - vals[1]) / (2 * h)
+        _close(np.asarray(got["dX"][0], np.float64), fd, rtol=1e-6, atol=1e-7, what="finite differences %s" % consumer)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

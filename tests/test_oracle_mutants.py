@@ -47,6 +47,14 @@ MUTANTS = [
      "if (e.has_lower && j - i > e.lower) return false;"),
     ("group_of_row_index", "e.group_rows[i] != e.group_cols[j]", "e.group_rows[i] != e.group_cols[i % e.M]"),
     ("softmax_v_by_position", "const int64_t j = jx[t];", "const int64_t j = t;"),
+    ("backward_exp_derivative", "case OP_EXP: d = d * t[op + 1];", "case OP_EXP: d = d * t[op];"),
+    ("backward_weight_rows_grad", "if (side == 0) { gops[op] += d * t[op];", "if (side == 0) { gops[op] += d;"),
+    ("backward_softmax_delta", "return p * (gv(i, j) - delta[i]);", "return p * gv(i, j);"),
+    ("backward_distance_side_sign", "if (side == 1) c = -c;", ""),
+    ("backward_displacement_direct", "gx[dd] += side == 0 ? -w : w;", "gx[dd] += w;"),
+    ("backward_matmul_dv", "gvout[c] += t[n] * g(i, c);", "gvout[c] += g(i, c);"),
+    ("backward_topk_position", "if (idx[i * k + p] == j) a += (R)G[i * ldg + p];",
+     "if (idx[i * k + p] == j) a += (R)G[i * ldg];"),
 ]
 
 

@@ -100,6 +100,11 @@ def flops_per_pair(case, D, C):
         return body + 1 + 2  # the 1/M scale, then a product with a ones column
     if case.consumer == "cg_solve":
         return body + 2 * C  # one kernel product per iteration
+    if case.consumer == "backward_softmax_matmul":
+        # Both sides replay the pair: metric and ops, the upstream dot
+        # product (2C) and exp, the gradient sums (2D); the column side
+        # also sums dV (2C).
+        return 2 * (body + 2 * C + 4) + 4 * D + 2 * C
     raise ValueError(case.consumer)
 
 
@@ -109,7 +114,10 @@ SWAP = {"add_rows": "add_columns", "add_columns": "add_rows", "weight_rows": "we
 
 def lib_consumer(c):
     """The tile-kernel consumer behind a case (a mean is a product with
-    ones; a CG solve runs one product per iteration)."""
+    ones; a CG solve runs one product per iteration; a backward is planned
+    as its forward consumer)."""
+    if c.consumer.startswith("backward_"):
+        return c.consumer[len("backward_"):]
     return "matmul" if c.consumer in ("mean", "cg_solve") else c.consumer
 
 
@@ -162,7 +170,20 @@ def main():
         N, D = X.shape
         M = Y.shape[0]
         C = t[c.v].shape[1] if c.v else (1 if c.consumer == "mean" else 0)
-        if c.consumer == "cg_solve":
+        if c.consumer == "backward_softmax_matmul":
+            # One step is the backward given dO and the forward output (the
+            # forward itself runs once, before the timed region).
+            V = t[c.v]
+            C = V.shape[1]
+            O = e.softmax_matmul(V)
+            G = t[c.params["G"]]
+            grads = {"X": torch.empty(N, D, dtype=X.dtype, device=dev), "Y": torch.empty(M, D, dtype=X.dtype, device=dev),
+                     "V": torch.empty(M, C, dtype=X.dtype, device=dev)}
+            ws = e.backward_workspace("softmax_matmul", C)
+            fn = (lambda e=e, G=G, V=V, O=O, grads=grads, ws=ws:
+                  e.backward("softmax_matmul", G, V=V, out=O, grads=grads, workspace=ws))
+            outs = (grads["X"], grads["Y"], grads["V"])
+        elif c.consumer == "cg_solve":
             # One step is one whole solve; its pairs are iterations * N * M,
             # counted from the solver's own iteration count.
             B = t[c.v]
@@ -266,13 +287,17 @@ def main():
     dtype = "f32" if calls[0][1].dtype == torch.float32 else "f64"
     dom0 = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
     c_, e_, _, _, C_ = calls[dom0]
-    contraction = e_.plan(lib_consumer(c_), C_, c_.k).startswith("family=mfma")
+    # The backward runs on the vector engine whatever the forward's plan.
+    contraction = (not c_.consumer.startswith("backward_")
+                   and e_.plan(lib_consumer(c_), C_, c_.k).startswith("family=mfma"))
     peak = PEAK_TFLOPS[dtype] if contraction else ALU_PEAK_TFLOPS[dtype]
     kernels = []
     for (c, e, _, _, C), kms in zip(calls, kernel_ms):
         fl = float(c.pairs if c.pairs is not None else e.N * e.M) * flops_per_pair(c, e.D, C)
         tf = fl / (kms * 1e-3) / 1e12
-        kernels.append({"call": c.name, "plan": e.plan(lib_consumer(c), C, c.k), "avg_ms": round(kms, 4),
+        plan = ("vector backward engine (row side, column side)" if c.consumer.startswith("backward_")
+                else e.plan(lib_consumer(c), C, c.k))
+        kernels.append({"call": c.name, "plan": plan, "avg_ms": round(kms, 4),
                         "flops_per_pair": flops_per_pair(c, e.D, C), "tflops": round(tf, 3),
                         "frac": round(tf / peak, 4)})
     dom = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
@@ -321,6 +346,41 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def backward_cpu_leg(c, oe, arrays, outs, budget, threads):
+    """The oracle's backward on sampled rows (dX) and the same number of
+    sampled columns (dY, dV). Its pair count is the
+    rows' and columns' pairs plus, for the softmax backward, the full pass
+    over all pairs that its per-row log-sum-exp and delta take."""
+    import oracle
+    from gpu_cases import grad_report
+    base = c.consumer[len("backward_"):]
+    G = arrays[c.params["G"]]
+    V = arrays[c.v] if c.v else None
+
+    def run(rows):
+        return oracle.backward(oe, base, G, V, rows=rows, cols=rows)
+
+    # One call (its full row-statistics pass is a fixed cost): a sample of
+    # 4 rows and columns per host thread.
+    rows = np.unique(np.linspace(0, oe.N - 1, min(oe.N, 4 * threads)).astype(np.int64))
+    t0 = time.perf_counter()
+    ref = run(rows)
+    dt = time.perf_counter() - t0
+    pairs = 2 * len(rows) * oe.M + (oe.N * oe.M if base in ("softmax_matmul", "logsumexp") else 0)
+    import torch
+    sel = torch.as_tensor(rows, device=outs[0].device)
+    dtype = np.dtype(oe.np_dtype)
+    worst, ok = 0.0, True
+    for g, r, terms in ((outs[0][sel], ref["dX"], oe.M), (outs[1][sel], ref["dY"], oe.N),
+                        (outs[2][sel], ref["dV"], oe.N)):
+        good, ratio = grad_report(g, r, dtype, terms)
+        ok &= good
+        worst = max(worst, ratio)
+    desc = ("%s: oracle backward on %d evenly spaced rows (dX) and the same %d columns (dY, dV), plus its full "
+            "per-row log-sum-exp and delta pass" % (c.name, len(rows), len(rows)))
+    return pairs, dt, desc, {"call": c.name, "rows": len(rows), "pass": bool(ok), "worst_err_over_tol": worst}
+
+
 def cpu_leg(calls, arrays, seconds):
     """Time the oracle on a bounded row sample on the host cores, and check
     the timed GPU outputs against it on the same rows."""
@@ -340,6 +400,13 @@ def cpu_leg(calls, arrays, seconds):
             # iteration: timed as S @ A on the sampled rows, which is also
             # the true residual's product for the parity check.
             A_gpu = outs[0].cpu().numpy()
+        if c.consumer.startswith("backward_"):
+            total_pairs_b, dt_b, desc_b, par_b = backward_cpu_leg(c, oe, arrays, outs, budget, threads)
+            total_pairs += total_pairs_b
+            total_s += dt_b
+            rows_desc.append(desc_b)
+            parity.append(par_b)
+            continue
 
         def run(rows):
             if c.consumer in ("matmul", "mean"):

@@ -197,6 +197,51 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
             void *stream);
 
 /* ------------------------------------------------------------------------
+ * Backward by replay (guide, opening section: the consumer's backward
+ * re-evaluates the pairs instead of keeping the [N, M] matrix; "What to
+ * Check", Gradients: selections route gradients through the selected pairs
+ * only). Given the upstream gradient G of a consumer's output, returns the
+ * gradients of sum(output * G) with respect to X, Y, V and the vector of
+ * every op, each pair's contribution formed from the chain rule on the fly.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *G;           /* [N, ldg] upstream gradient: C columns (matmul, softmax),
+                              D (displacement), 1 (logsumexp), k (top-k) */
+  int64_t ldg;
+  const void *V;           /* matmul, softmax: the forward call's V [M, ldv], C columns */
+  int64_t C, ldv;
+  const void *out;         /* softmax: the forward output [N, ldo] (required);
+                              logsumexp: the forward output [N] (NULL: recomputed) */
+  int64_t ldo;
+  const int64_t *indices;  /* top-k: the forward call's indices [N, k] (-1 entries skipped) */
+  int k;
+  int exclude_self;        /* logsumexp: as in the forward call */
+} pw_grad_in;
+
+typedef struct {
+  void *dX;                /* [N, lddx] gradient of X, or NULL */
+  int64_t lddx;
+  void *dY;                /* [M, lddy] gradient of Y, or NULL */
+  int64_t lddy;
+  void *dV;                /* [M, lddv] gradient of V (matmul, softmax), or NULL */
+  int64_t lddv;
+  void *dops[PW_MAX_OPS];  /* entry t: gradient of op t's vector (N or M elements) for
+                              ADD/WEIGHT_ROWS/COLUMNS ops, else ignored; NULL: not wanted */
+} pw_grad_out;
+
+/* Workspace bytes of pw_backward for `consumer`, C value columns, k. */
+int pw_backward_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes);
+
+/* Gradients of sum(consumer output * G): every requested output is
+ * overwritten. Masks and the excluded self pair contribute nothing. For
+ * X aliasing Y (one set with itself) dX and dY are the two sides' parts;
+ * the set's gradient is their sum. Supported: every metric, op and mask;
+ * D <= 64; C <= 64 (PW_ERR_UNSUPPORTED above). Top-k column gradients
+ * (dY, column ops) are summed with atomics: not bitwise repeatable. */
+int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_grad_out *out, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Conjugate-gradient solve (guide, Task Map, "Kernel ridge, GP mean" row:
  * solve(K + a * eye_like(K), Y, method="cg"); "What to Check", Solvers:
  * results carry converged and status, to be checked before the solution is
@@ -245,7 +290,9 @@ int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf
  * before its main tile-kernel launch and `stop` just after it (for value
  * widths above one launch's chunk, around all of the call's tile launches).
  * The events are created and owned by the caller; NULL, NULL disables the
- * hook. Thread-local: other threads are unaffected. Never fails. */
+ * hook. Thread-local: other threads are unaffected. Never fails.
+ * pw_backward records the pair around all of its tile launches (both
+ * sides, with the small merges between them). */
 int pw_set_tile_events(void *start, void *stop);
 
 /* Static text for a pw_status code. */

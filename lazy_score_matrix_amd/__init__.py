@@ -60,6 +60,17 @@ class _SolveInfo(ctypes.Structure):
 
 SOLVE_STATUS = {0: "converged", 1: "max_iter", 2: "breakdown"}
 
+
+class _GradIn(ctypes.Structure):
+    _fields_ = [("G", ctypes.c_void_p), ("ldg", ctypes.c_int64), ("V", ctypes.c_void_p), ("C", ctypes.c_int64),
+                ("ldv", ctypes.c_int64), ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64),
+                ("indices", ctypes.c_void_p), ("k", ctypes.c_int), ("exclude_self", ctypes.c_int)]
+
+
+class _GradOut(ctypes.Structure):
+    _fields_ = [("dX", ctypes.c_void_p), ("lddx", ctypes.c_int64), ("dY", ctypes.c_void_p), ("lddy", ctypes.c_int64),
+                ("dV", ctypes.c_void_p), ("lddv", ctypes.c_int64), ("dops", ctypes.c_void_p * 16)]
+
 _lock = threading.Lock()
 _lib = None
 
@@ -87,6 +98,8 @@ def load_library(path: str = LIB_PATH):
         lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
+        lib.pw_backward_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
+        lib.pw_backward.argtypes = [vp, c_int, ctypes.POINTER(_GradIn), ctypes.POINTER(_GradOut), vp, sz, vp]
         lib.pw_cg_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         lib.pw_cg_solve.argtypes = [vp, ctypes.c_double, vp, i64, i64, vp, i64, c_int, ctypes.c_double, c_int, vp, sz,
                                     vp, ctypes.POINTER(_SolveInfo)]
@@ -239,6 +252,8 @@ class LazyScores:
         """out[i, c] = sum_j S[i, j] V[j, c] over the kept pairs."""
         if mask is not None:
             return self.masked(mask).matmul(V, out, workspace)
+        if out is None and _needs_grad(self, V):
+            return _replay(self, "matmul", V)
         ldv = self._value(V, "matmul")
         C = V.shape[1]
         out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
@@ -254,6 +269,8 @@ class LazyScores:
         `mask` (op entries, e.g. masks.causal()) and the bound masks keep."""
         if mask is not None:
             return self.masked(mask).softmax_matmul(V, out, workspace)
+        if out is None and _needs_grad(self, V):
+            return _replay(self, "softmax_matmul", V)
         ldv = self._value(V, "softmax_matmul")
         C = V.shape[1]
         out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
@@ -266,6 +283,8 @@ class LazyScores:
         """out[i, d] = sum_j S[i, j] (Y[j, d] - X[i, d]) over the kept pairs."""
         if mask is not None:
             return self.masked(mask).displacement(out, workspace)
+        if out is None and _needs_grad(self):
+            return _replay(self, "displacement")
         out = torch.empty(self.N, self.D, dtype=self.dtype, device=self.device) if out is None else out
         ws, nb = self._ws(workspace, "displacement")
         check(self._lib.pw_displacement(self._h, out.data_ptr(), _rows(out, "out"), ws.data_ptr(), nb,
@@ -277,6 +296,8 @@ class LazyScores:
         without j == i (-inf for a row with none)."""
         if mask is not None:
             return self.masked(mask).logsumexp(exclude_self, out, workspace)
+        if out is None and _needs_grad(self):
+            return _replay(self, "logsumexp", exclude_self=bool(exclude_self))
         out = torch.empty(self.N, dtype=self.dtype, device=self.device) if out is None else out
         ws, nb = self._ws(workspace, "logsumexp")
         check(self._lib.pw_logsumexp(self._h, int(bool(exclude_self)), out.data_ptr(), ws.data_ptr(), nb,
@@ -288,12 +309,80 @@ class LazyScores:
         int64 indices [N, k]; positions past a row's kept pairs hold NaN / -1."""
         if mask is not None:
             return self.masked(mask).topk(k, largest, values, indices, workspace)
+        if values is None and _needs_grad(self):
+            return _replay(self, "topk", k=int(k), largest=bool(largest))
         values = torch.empty(self.N, k, dtype=self.dtype, device=self.device) if values is None else values
         indices = torch.empty(self.N, k, dtype=torch.int64, device=self.device) if indices is None else indices
         ws, nb = self._ws(workspace, "topk", 0, k)
         check(self._lib.pw_topk(self._h, int(k), int(bool(largest)), values.data_ptr(), indices.data_ptr(),
                                 ws.data_ptr(), nb, _stream(self.device)), "pw_topk")
         return values, indices
+
+    # -- backward -------------------------------------------------------
+    def backward(self, consumer: str, G: torch.Tensor, V=None, out=None, indices=None, exclude_self=False,
+                 want=("X", "Y", "V", "ops"), grads=None, workspace=None):
+        """Gradients of sum(consumer output * G) by replay (guide: backward
+        re-evaluates the pairs; selections route gradients through the
+        selected pairs only). Returns {"X": dX, "Y": dY, "V": dV, "ops": [per
+        op: gradient of its vector or None]}; only the entries in `want` are
+        computed. `out` is the forward output (softmax_matmul: required;
+        logsumexp: optional), `indices` the top-k indices."""
+        G2 = G[:, None] if G.dim() == 1 else G
+        if G2.dtype != self.dtype or G2.device != self.device or G2.shape[0] != self.N:
+            raise ValueError("G must be [N, *] %s on %s" % (self.dtype, self.device))
+        gin = _GradIn()
+        gin.G, gin.ldg = G2.data_ptr(), _rows(G2, "G")
+        keep = [G2]
+        if V is not None:
+            gin.V, gin.C, gin.ldv = V.data_ptr(), V.shape[1], self._value(V, "backward")
+        if out is not None:
+            o2 = out[:, None] if out.dim() == 1 else out
+            gin.out, gin.ldo = o2.data_ptr(), _rows(o2, "out")
+            keep.append(o2)
+        if indices is not None:
+            idx = indices.contiguous()
+            keep.append(idx)
+            gin.indices, gin.k = idx.data_ptr(), idx.shape[1]
+        gin.exclude_self = int(bool(exclude_self))
+        res = {"X": None, "Y": None, "V": None, "ops": [None] * len(self.ops)}
+        gout = _GradOut()
+        given = grads or {}
+
+        def new(*shape, key=None):
+            if key in given:
+                return given[key]
+            return torch.empty(*shape, dtype=self.dtype, device=self.device)
+        if "X" in want:
+            res["X"] = new(self.N, self.D, key="X")
+            gout.dX, gout.lddx = res["X"].data_ptr(), max(self.D, 1)
+        if "Y" in want:
+            res["Y"] = new(self.M, self.D, key="Y")
+            gout.dY, gout.lddy = res["Y"].data_ptr(), max(self.D, 1)
+        if "V" in want and V is not None:
+            res["V"] = new(self.M, V.shape[1], key="V")
+            gout.dV, gout.lddv = res["V"].data_ptr(), V.shape[1]
+        if "ops" in want:
+            for t, (name, arg) in enumerate(self.ops):
+                if name in ("add_rows", "weight_rows", "add_columns", "weight_columns"):
+                    res["ops"][t] = new(self.N if name.endswith("_rows") else self.M)
+                    gout.dops[t] = res["ops"][t].data_ptr()
+        C = V.shape[1] if V is not None else 0
+        n = ctypes.c_size_t()
+        check(self._lib.pw_backward_workspace_size(self._h, CONSUMERS[consumer], C, gin.k, ctypes.byref(n)),
+              "pw_backward_workspace_size")
+        ws = workspace if workspace is not None else torch.empty(max(n.value, 1), dtype=torch.uint8,
+                                                                 device=self.device)
+        if ws.numel() < n.value:
+            raise ValueError("workspace needs %d bytes" % n.value)
+        check(self._lib.pw_backward(self._h, CONSUMERS[consumer], ctypes.byref(gin), ctypes.byref(gout),
+                                    ws.data_ptr(), ws.numel(), _stream(self.device)), "pw_backward")
+        return res
+
+    def backward_workspace(self, consumer: str, C: int = 0, k: int = 0) -> torch.Tensor:
+        n = ctypes.c_size_t()
+        check(self._lib.pw_backward_workspace_size(self._h, CONSUMERS[consumer], int(C), int(k), ctypes.byref(n)),
+              "pw_backward_workspace_size")
+        return torch.empty(max(n.value, 1), dtype=torch.uint8, device=self.device)
 
     # -- solver ---------------------------------------------------------
     def solve(self, B: torch.Tensor, shift: float, rtol: float = 1e-6, max_iter: int = 1000, check_every: int = 8,
@@ -381,6 +470,78 @@ class LazyScores:
 
 
 from . import masks  # noqa: E402  (pair-mask helpers)
+
+_VEC_OPS = ("add_rows", "weight_rows", "add_columns", "weight_columns")
+
+
+class _Replay(torch.autograd.Function):
+    """A consumer call whose backward replays the pairs with pw_backward.
+    Inputs: a spec tuple, then X, Y, V (or None) and every op argument that
+    is a tensor (op vectors, masks, group ids), in op order."""
+
+    @staticmethod
+    def forward(ctx, spec, X, Y, V, *tensors):
+        metric, gamma, ops_spec, consumer, kw = spec
+        it = iter(tensors)
+        ops = [(n, next(it) if is_t else a) for n, a, is_t in ops_spec]
+        e = LazyScores(X, Y, metric, gamma, ops)
+        if consumer in ("matmul", "softmax_matmul"):
+            out = getattr(e, consumer)(V)
+            outs = (out,)
+        elif consumer == "displacement":
+            out = e.displacement()
+            outs = (out,)
+        elif consumer == "logsumexp":
+            out = e.logsumexp(kw.get("exclude_self", False))
+            outs = (out,)
+        else:
+            vals, idx = e.topk(kw["k"], kw.get("largest", False))
+            ctx.mark_non_differentiable(idx)
+            outs = (vals, idx)
+            out = vals
+        ctx.spec = spec
+        ctx.save_for_backward(X, Y, V if V is not None else torch.empty(0), out, outs[-1], *tensors)
+        ctx.has_v = V is not None
+        return outs if len(outs) > 1 else outs[0]
+
+    @staticmethod
+    def backward(ctx, *grads):
+        metric, gamma, ops_spec, consumer, kw = ctx.spec
+        X, Y, V, out, last, *tensors = ctx.saved_tensors
+        V = V if ctx.has_v else None
+        it = iter(tensors)
+        ops = [(n, next(it) if is_t else a) for n, a, is_t in ops_spec]
+        e = LazyScores(X, Y, metric, gamma, ops)
+        G = grads[0].contiguous()
+        want = ["ops"]
+        if ctx.needs_input_grad[1]:
+            want.append("X")
+        if ctx.needs_input_grad[2]:
+            want.append("Y")
+        if ctx.needs_input_grad[3]:
+            want.append("V")
+        r = e.backward(consumer, G, V=V, out=out if consumer in ("softmax_matmul", "logsumexp") else None,
+                       indices=last if consumer == "topk" else None, exclude_self=kw.get("exclude_self", False),
+                       want=tuple(want))
+        op_grads = []
+        for t, (n, a, is_t) in enumerate(ops_spec):
+            if is_t:
+                op_grads.append(r["ops"][t] if n in _VEC_OPS else None)
+        return (None, r["X"], r["Y"], r["V"], *op_grads)
+
+
+def _needs_grad(e, V=None):
+    if not torch.is_grad_enabled():
+        return False
+    ts = [e.X, e.Y] + ([V] if V is not None else []) + [a for n, a in e.ops if torch.is_tensor(a)]
+    return any(t.requires_grad for t in ts)
+
+
+def _replay(e, consumer, V=None, **kw):
+    ops_spec = tuple((n, None if torch.is_tensor(a) else a, torch.is_tensor(a)) for n, a in e.ops)
+    tensors = [a for n, a in e.ops if torch.is_tensor(a)]
+    spec = (e.metric, e.gamma, ops_spec, consumer, kw)
+    return _Replay.apply(spec, e.X, e.Y, V, *tensors)
 
 
 def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()) -> LazyScores:

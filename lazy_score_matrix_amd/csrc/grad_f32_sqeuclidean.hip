@@ -1,0 +1,11 @@
+// Backward tile kernels: float, sqeuclidean metric.
+#include "grad_engine.h"
+
+namespace pw {
+hipError_t grad_launch_f32_sqeuclidean(int consumer, int side, int dt, int ct, const GradArgs &a, hipStream_t s) {
+  return grad_launch_metric<float, M_SQEUCLIDEAN>(consumer, side, dt, ct, a, s);
+}
+hipError_t grad_topk_f32_sqeuclidean(int dt, const GradArgs &a, hipStream_t s) {
+  return grad_topk_metric<float, M_SQEUCLIDEAN>(dt, a, s);
+}
+}  // namespace pw

@@ -738,6 +738,262 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
 
 }  // extern "C"
 
+// ------------------------------------------------------------------ backward
+
+namespace {
+
+constexpr int kGradRows = 256, kGradCols = 64;  // grad_tile workgroup rows and tile
+
+int grad_dtile(int64_t D) { return D <= 4 ? 4 : (D <= 16 ? 16 : 64); }
+bool is_vec_op(int kind) {
+  return kind == PW_OP_ADD_ROWS || kind == PW_OP_ADD_COLUMNS || kind == PW_OP_WEIGHT_ROWS ||
+         kind == PW_OP_WEIGHT_COLUMNS;
+}
+bool is_arith_op(int kind) { return kind >= PW_OP_MUL && kind <= PW_OP_EXP; }
+
+struct GradPlan {
+  int dt = 4, ct = 16, n_arith = 0;
+  int n_rb[2] = {0, 0}, n_split[2] = {1, 1}, W[2] = {0, 0};
+  int64_t split[2] = {0, 0};
+  size_t off_lse = 0, off_delta = 0, off_invx = 0, off_invy = 0, off_part = 0, off_fwd = 0, off_epi = 0, total = 0;
+};
+
+GradPlan grad_plan(const pw_expr &e, int consumer, int64_t C) {
+  GradPlan g;
+  const size_t es = esize(e.dtype);
+  g.dt = grad_dtile(e.D);
+  g.ct = C <= 16 ? 16 : 64;
+  for (const pw_op &o : e.ops) g.n_arith += is_arith_op(o.kind);
+  const bool value = consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL;
+  size_t part = 0;
+  for (int side = 0; side < 2; ++side) {
+    const int64_t n_own = side == 0 ? e.N : e.M, n_oth = side == 0 ? e.M : e.N;
+    g.n_rb[side] = (int)std::max<int64_t>(1, (n_own + kGradRows - 1) / kGradRows);
+    const int64_t tiles = std::max<int64_t>(1, (n_oth + kGradCols - 1) / kGradCols);
+    int64_t want = std::max<int64_t>(1, (kTargetWGs + g.n_rb[side] - 1) / g.n_rb[side]);
+    want = std::min(want, tiles);
+    g.split[side] = (tiles + want - 1) / want * kGradCols;
+    g.n_split[side] = (int)std::max<int64_t>(1, (n_oth + g.split[side] - 1) / g.split[side]);
+    g.W[side] = (int)e.D + ((side == 1 && value) ? (int)C : 0) + g.n_arith;
+    part = std::max(part, (size_t)g.n_split[side] * (size_t)n_own * (size_t)g.W[side] * es);
+  }
+  size_t off = 0;
+  g.off_lse = off;
+  off += align_up((size_t)e.N * es);
+  g.off_delta = off;
+  off += align_up((size_t)e.N * es);
+  g.off_invx = off;
+  off += align_up((size_t)e.N * es);
+  g.off_invy = off;
+  off += align_up((size_t)e.M * es);
+  g.off_part = off;
+  off += align_up(part);
+  g.off_fwd = off;
+  if (consumer == PW_C_LOGSUMEXP || consumer == PW_C_SOFTMAX_MATMUL) off += align_up(make_plan(e, PW_C_LOGSUMEXP, 0, 0).total);
+  // The canonical stage's vectors for the fast path (the forward's layout).
+  g.off_epi = off;
+  off += align_up(make_plan(e, PW_C_MATMUL, 1, 0).off_ny);
+  g.total = off + kAlign;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pw_backward_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes) {
+  (void)k;
+  if (!e || !bytes || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
+  *bytes = grad_plan(*e, consumer, std::max<int64_t>(C, 1)).total;
+  return PW_OK;
+}
+
+int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_grad_out *out, void *ws,
+                size_t ws_bytes, void *stream) {
+  if (!e || !in || !out || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
+  const size_t es = esize(e->dtype);
+  const bool value = consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL;
+  const int64_t C = value ? in->C : 0;
+  if (value) {
+    if (C < 1) return PW_ERR_INVALID;
+    if (C > 64) return PW_ERR_UNSUPPORTED;
+    if ((e->M > 0 && !in->V) || in->ldv < C || in->ldg < C || !aligned(in->V, es)) return PW_ERR_INVALID;
+  }
+  if (consumer == PW_C_SOFTMAX_MATMUL && ((e->N > 0 && !in->out) || in->ldo < C || !aligned(in->out, es)))
+    return PW_ERR_INVALID;
+  if (consumer == PW_C_DISPLACEMENT && in->ldg < e->D) return PW_ERR_INVALID;
+  if (consumer == PW_C_LOGSUMEXP && (in->ldg < 1 || (in->exclude_self != 0 && in->exclude_self != 1) ||
+                                     !aligned(in->out, es)))
+    return PW_ERR_INVALID;
+  if (consumer == PW_C_TOPK) {
+    if (in->k < 1 || in->k > e->M || in->ldg < in->k || (e->N > 0 && !in->indices) || !aligned(in->indices, 8))
+      return PW_ERR_INVALID;
+    if (in->k > PW_MAX_K) return PW_ERR_UNSUPPORTED;
+  }
+  if ((e->N > 0 && !in->G) || !aligned(in->G, es)) return PW_ERR_INVALID;
+  if ((out->dX && (out->lddx < e->D || !aligned(out->dX, es))) ||
+      (out->dY && (out->lddy < e->D || !aligned(out->dY, es))) ||
+      (out->dV && (!value || out->lddv < C || !aligned(out->dV, es))))
+    return PW_ERR_INVALID;
+  for (size_t t = 0; t < e->ops.size(); ++t)
+    if (out->dops[t] && !aligned(out->dops[t], es)) return PW_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+
+  // Arithmetic ops in order, and for each the caller's output slot.
+  GradArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int bound_of[kGradOps];
+  for (size_t t = 0; t < e->ops.size(); ++t) {
+    const pw_op &o = e->ops[t];
+    if (!is_arith_op(o.kind)) continue;
+    GradOp &g = a.ops[a.n_ops];
+    g.kind = o.kind;
+    g.scalar = o.scalar;
+    g.vec = o.vec;
+    g.where = (o.kind == PW_OP_ADD_ROWS || o.kind == PW_OP_WEIGHT_ROWS) ? 1
+              : (o.kind == PW_OP_ADD_COLUMNS || o.kind == PW_OP_WEIGHT_COLUMNS) ? 2 : 0;
+    bound_of[a.n_ops++] = (int)t;
+  }
+  auto want_side = [&](int side) {
+    if (side == 0 ? out->dX != nullptr : (out->dY != nullptr || out->dV != nullptr)) return true;
+    for (int t = 0; t < a.n_ops; ++t)
+      if (a.ops[t].where == side + 1 && out->dops[bound_of[t]]) return true;
+    return false;
+  };
+
+  // Empty sets: every requested gradient is zero.
+  if (e->N == 0 || e->M == 0) {
+    int rc = PW_OK;
+    if (out->dX && rc == PW_OK) rc = hip_status(launch_fill(e->dtype, out->dX, e->N, e->D, out->lddx, 0.0, s));
+    if (out->dY && rc == PW_OK) rc = hip_status(launch_fill(e->dtype, out->dY, e->M, e->D, out->lddy, 0.0, s));
+    if (out->dV && rc == PW_OK) rc = hip_status(launch_fill(e->dtype, out->dV, e->M, C, out->lddv, 0.0, s));
+    for (int t = 0; t < a.n_ops && rc == PW_OK; ++t)
+      if (a.ops[t].where && out->dops[bound_of[t]])
+        rc = hip_status(launch_fill(e->dtype, out->dops[bound_of[t]], a.ops[t].where == 1 ? e->N : e->M, 1, 1,
+                                    0.0, s));
+    return rc;
+  }
+
+  const GradPlan g = grad_plan(*e, consumer, std::max<int64_t>(C, 1));
+  if (!ws || ws_bytes < g.total) return PW_ERR_WORKSPACE;
+  char *base = reinterpret_cast<char *>(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+  a.X = e->X;
+  a.Y = e->Y;
+  a.ldx = e->ldx;
+  a.ldy = e->ldy;
+  a.N = e->N;
+  a.M = e->M;
+  a.D = (int)e->D;
+  a.gamma = e->metric == PW_RBF ? e->gamma : 0.0;
+  a.G = in->G;
+  a.ldg = in->ldg;
+  a.V = in->V;
+  a.ldv = in->ldv;
+  a.C = (int)C;
+  a.exclude_self = consumer == PW_C_LOGSUMEXP ? in->exclude_self : 0;
+  a.mask.row = e->row_mask;
+  a.mask.col = e->col_mask;
+  a.mask.band = e->band ? 1 : 0;
+  a.mask.lo = e->lo;
+  a.mask.hi = e->hi;
+  a.mask.grow = e->grow;
+  a.mask.gcol = e->gcol;
+  a.mask.any = (a.mask.row || a.mask.col || a.mask.band || a.mask.grow) ? 1 : 0;
+  int rc = PW_OK;
+  if (e->metric == PW_COSINE) {
+    a.inv_x = base + g.off_invx;
+    a.inv_y = base + g.off_invy;
+    rc = hip_status(launch_row_norms(e->dtype, e->X, e->N, e->ldx, (int)e->D, base + g.off_invx, s, true));
+    if (rc == PW_OK)
+      rc = hip_status(launch_row_norms(e->dtype, e->Y, e->M, e->ldy, (int)e->D, base + g.off_invy, s, true));
+  }
+  if (rc == PW_OK && (consumer == PW_C_LOGSUMEXP || consumer == PW_C_SOFTMAX_MATMUL)) {
+    if (consumer == PW_C_LOGSUMEXP && in->out) {
+      a.lse = in->out;
+    } else {
+      // The row log-sum-exp of the forward scores: one more forward pass.
+      a.lse = base + g.off_lse;
+      const size_t fwd = make_plan(*e, PW_C_LOGSUMEXP, 0, 0).total;
+      rc = pw_logsumexp(e, a.exclude_self, base + g.off_lse, base + g.off_fwd, fwd, stream);
+    }
+    if (rc == PW_OK && consumer == PW_C_SOFTMAX_MATMUL) {
+      a.delta = base + g.off_delta;
+      rc = hip_status(launch_grad_delta(e->dtype, in->G, in->ldg, in->out, in->ldo, e->N, (int)C,
+                                        base + g.off_delta, s));
+    }
+  }
+  if (rc != PW_OK) return rc;
+
+  if (consumer == PW_C_TOPK) {
+    a.idx = in->indices;
+    a.k = in->k;
+    a.dX = out->dX;
+    a.dY = out->dY;
+    a.lddx = out->lddx;
+    a.lddy = out->lddy;
+    for (int t = 0; t < a.n_ops; ++t) a.dop[t] = out->dops[bound_of[t]];
+    // Column-side results are summed atomically into cleared outputs.
+    if (out->dY) rc = hip_status(launch_fill(e->dtype, out->dY, e->M, e->D, out->lddy, 0.0, s));
+    for (int t = 0; t < a.n_ops && rc == PW_OK; ++t)
+      if (a.ops[t].where == 2 && a.dop[t]) rc = hip_status(launch_fill(e->dtype, a.dop[t], e->M, 1, 1, 0.0, s));
+    if (rc == PW_OK) rc = hip_status(grad_topk_launch(e->dtype, e->metric, g.dt, a, s));
+    return rc;
+  }
+
+  // Fast path: the ops fold into at most one affine stage and no op-vector
+  // gradient is wanted; the stage's vectors come from the forward's own
+  // pre-pass.
+  bool want_ops = false;
+  for (int t = 0; t < a.n_ops; ++t) want_ops |= a.ops[t].where && out->dops[bound_of[t]] != nullptr;
+  if (!want_ops && e->stages.size() <= 1 && (e->stages.empty() || e->stages[0].kind == ST_AFFINE)) {
+    a.fast = 1;
+    Epi epi;
+    Plan ep = make_plan(*e, PW_C_MATMUL, 1, 0);
+    rc = prepare_epilogue(*e, ep, base + g.off_epi, &epi, s);
+    if (rc != PW_OK) return rc;
+    if (epi.n_stages == 1) {
+      a.stage = epi.st[0];
+    } else {
+      std::memset(&a.stage, 0, sizeof(a.stage));
+      a.stage.kind = ST_AFFINE;
+      a.stage.r_scalar = 1.0;
+    }
+  }
+  const int cons = consumer == PW_C_MATMUL ? C_MATMUL
+                   : consumer == PW_C_DISPLACEMENT ? C_DISPLACEMENT
+                   : consumer == PW_C_LOGSUMEXP ? C_LOGSUMEXP : C_SOFTMAX;
+  const int last_side = want_side(1) ? 1 : 0;
+  bool started = false;
+  for (int side = 0; side < 2 && rc == PW_OK; ++side) {
+    if (!want_side(side)) continue;
+    if (!started && tile_ev_start) hipEventRecord(tile_ev_start, s);
+    started = true;
+    a.n_rb = g.n_rb[side];
+    a.n_split = g.n_split[side];
+    a.split = g.split[side];
+    a.W = g.W[side];
+    a.partial = base + g.off_part;
+    rc = hip_status(grad_launch(e->dtype, e->metric, cons, side, g.dt, g.ct, a, s));
+    if (rc != PW_OK) break;
+    GradOut o;
+    std::memset(&o, 0, sizeof(o));
+    o.own = side == 0 ? out->dX : out->dY;
+    o.ld_own = side == 0 ? out->lddx : out->lddy;
+    if (side == 1) {
+      o.dV = out->dV;
+      o.lddv = out->lddv;
+    }
+    for (int t = 0; t < a.n_ops; ++t)
+      if (a.ops[t].where == side + 1) o.dop[t] = out->dops[bound_of[t]];
+    rc = hip_status(launch_grad_merge(e->dtype, a, side, side == 0 ? e->N : e->M, (side == 1 && value) ? (int)C : 0,
+                                      o, s));
+    if (side == last_side && tile_ev_stop) hipEventRecord(tile_ev_stop, s);
+  }
+  return rc;
+}
+
+}  // extern "C"
+
 // ------------------------------------------------------------------ CG solve
 
 namespace {

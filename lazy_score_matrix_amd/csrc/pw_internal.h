@@ -180,6 +180,65 @@ constexpr int mfma_groups(int dtype) { return dtype == 0 ? 2 : 4; }
 template <class T, int METRIC>
 hipError_t mfma_launch_metric(int consumer, const MfmaConfig &cfg, const TileArgs &a, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Backward by replay (grad_engine.h). The raw arithmetic ops, in order (the
+// masks are in MaskArgs); `where` 0 scalar / none, 1 row vector, 2 column.
+// ---------------------------------------------------------------------------
+constexpr int kGradOps = 16;
+struct GradOp {
+  int kind;       // PW_OP_* arithmetic kind
+  int where;
+  double scalar;
+  const void *vec;
+};
+struct GradArgs {
+  const void *X, *Y;
+  int64_t ldx, ldy, N, M;
+  int D;
+  double gamma;
+  int n_ops;
+  GradOp ops[kGradOps];
+  int fast;            // ops folded into `stage` (one affine stage), no op grads
+  Stage stage;
+  const void *G;       // upstream gradient [N, ldg]
+  int64_t ldg;
+  const void *V;       // forward V [M, ldv] (matmul, softmax)
+  int64_t ldv;
+  int C;
+  const void *lse;     // [N] row log-sum-exp (logsumexp, softmax)
+  const void *delta;   // [N] sum_c G_ic O_ic (softmax)
+  const void *inv_x;   // [N] 1/|x_i| (cosine)
+  const void *inv_y;   // [M] 1/|y_j| (cosine)
+  int exclude_self;
+  MaskArgs mask;
+  const int64_t *idx;  // top-k indices [N, k]
+  int k;
+  // Partial outputs [n_split][own rows][W]: gradient of the own point (D),
+  // then dV (C, column side of value consumers), then one slot per op.
+  int n_rb, n_split;
+  int64_t split;
+  void *partial;
+  int W;
+  // Top-k writes its outputs directly (row side plain, column side atomic).
+  void *dX, *dY;
+  int64_t lddx, lddy;
+  void *dop[kGradOps];
+};
+struct GradOut {
+  void *own;  // dX (side 0) or dY (side 1)
+  int64_t ld_own;
+  void *dV;
+  int64_t lddv;
+  void *dop[kGradOps];  // only the ops on this side are written
+};
+hipError_t grad_launch(int dtype, int metric, int consumer, int side, int dt, int ct, const GradArgs &a,
+                       hipStream_t s);
+hipError_t grad_topk_launch(int dtype, int metric, int dt, const GradArgs &a, hipStream_t s);
+hipError_t launch_grad_merge(int dtype, const GradArgs &a, int side, int64_t n_own, int C1, const GradOut &o,
+                             hipStream_t s);
+hipError_t launch_grad_delta(int dtype, const void *G, int64_t ldg, const void *O, int64_t ldo, int64_t N, int C,
+                             void *delta, hipStream_t s);
+
 // Conjugate-gradient vector steps (cg_kernels.hip). Iterates are [N, C]
 // row-major with ld C; column partial sums are doubles [cg_blocks(N)][C].
 struct CgState {

@@ -83,11 +83,68 @@ def solve_report(oe, A, B, shift, rtol, rows=None):
     return ok, float(np.max(rn / np.maximum(bound, 1e-300)))
 
 
+GRAD_RTOL = {np.dtype(np.float32): 5e-5, np.dtype(np.float64): 1e-11}
+
+
+def grad_report(g, ref, dtype, terms):
+    """(ok, worst |gpu - oracle| / tol) for one gradient: tol = rtol *
+    sqrt(max(1, terms / 256)) * (mag + |oracle|), mag the oracle's sum of
+    the absolute terms (their rounding scale)."""
+    val, mag = ref
+    o = np.asarray(val, np.float64)
+    m = np.asarray(mag, np.float64)
+    g = g.detach().cpu().numpy().astype(np.float64).reshape(o.shape)
+    tol = GRAD_RTOL[np.dtype(dtype)] * max(1.0, np.sqrt(terms / 256.0)) * (m + np.abs(o)) + 1e-300
+    ratio = float(np.max(np.abs(g - o) / tol)) if o.size else 0.0
+    return ratio <= 1.0, ratio
+
+
+def check_backward(e, oe, consumer, G, V=None, k=0, exclude_self=False, rows=None, cols=None, report=False,
+                   what="", want=("X", "Y", "V", "ops")):
+    """GPU backward of `consumer` against the oracle's chain rule: dX and
+    row-op grads on `rows`, dY, dV and column-op grads on `cols` (all by
+    default). Returns (ok, worst ratio) with report=True, else asserts."""
+    dtype = np.dtype(oe.np_dtype)
+    out = idx = None
+    Vd = None if V is None else to_dev(V)
+    if consumer == "softmax_matmul":
+        out = e.softmax_matmul(Vd)
+    elif consumer == "topk":
+        _, idx = e.topk(k)
+    got = e.backward(consumer, to_dev(G), V=Vd, out=out, indices=idx, exclude_self=exclude_self, want=want)
+    ref = oracle.backward(oe, consumer, G, V, exclude_self=exclude_self,
+                          indices=None if idx is None else idx.cpu().numpy(), rows=rows, cols=cols)
+    sel_r = slice(None) if rows is None else torch.as_tensor(rows, device=dev())
+    sel_c = slice(None) if cols is None else torch.as_tensor(cols, device=dev())
+    checks = [("dX", got["X"][sel_r], ref["dX"], oe.M), ("dY", got["Y"][sel_c], ref["dY"], oe.N)]
+    if V is not None:
+        checks.append(("dV", got["V"][sel_c], ref["dV"], oe.N))
+    for t, (name, _) in enumerate(oe.op_list):
+        if ref["ops"][t] is not None and "ops" in want:
+            rowop = name.endswith("_rows")
+            checks.append(("op %d %s" % (t, name), got["ops"][t][sel_r if rowop else sel_c], ref["ops"][t],
+                           oe.M if rowop else oe.N))
+    worst, ok = 0.0, True
+    for name, g, r, terms in checks:
+        good, ratio = grad_report(g, r, dtype, terms)
+        worst = max(worst, ratio)
+        if not report:
+            assert good, "%s %s: worst |gpu - oracle| / tol = %.3g" % (what, name, ratio)
+        ok &= good
+    return ok, worst
+
+
 def check_consumer(e, oe, consumer, V=None, exclude_self=False, k=0, largest=False, rows=None, exact=False,
                    what="", report=False, params=None):
     """Run `consumer` on the GPU and the oracle (optionally on a row subset of
     the oracle side) and assert parity. Returns (worst err/tol, plain rel)."""
     dtype = np.dtype(oe.np_dtype)
+    if consumer.startswith("backward_"):
+        p = dict(params or {})
+        ok, ratio = check_backward(e, oe, consumer[len("backward_"):], p["G"], V=V, k=k, exclude_self=exclude_self,
+                                   rows=rows, cols=None if rows is None else p.get("cols", rows), report=report,
+                                   what=what)
+        return (ok, ratio) if report else (ratio, 0.0)
     if consumer == "cg_solve":
         p = dict(params or {})
         A, info = e.solve(to_dev(V), p["shift"], rtol=p["rtol"], max_iter=p.get("max_iter", 1000))

@@ -25,7 +25,7 @@ def test_full_size_workload(name):
         V = arrays[c.v] if c.v else None
         ratio, rel = check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k,
                                     largest=c.largest, rows=rows, what="%s/%s" % (name, c.name),
-                                    params=c.params)
+                                    params={k: workloads.resolve(v, arrays) for k, v in c.params.items()})
         print("%s/%s: %d rows, worst err/tol %.3g, plan %s" % (name, c.name, len(rows), ratio,
                                                               e.plan(*_plan_args(c, V))))
 
@@ -33,4 +33,6 @@ def test_full_size_workload(name):
 def _plan_args(c, V):
     if c.consumer in ("mean", "cg_solve"):
         return "matmul", 1, 0
+    if c.consumer.startswith("backward_"):
+        return c.consumer[len("backward_"):], V.shape[1] if V is not None else 0, c.k
     return c.consumer, V.shape[1] if V is not None else 0, c.k

@@ -229,7 +229,8 @@ def test_reduced_workloads(name):
         e, oe = bind_case(arrays, c)
         V = arrays[c.v] if c.v else None
         check_consumer(e, oe, c.consumer, V=V, exclude_self=c.exclude_self, k=c.k, largest=c.largest,
-                       what="%s/%s" % (name, c.name), params=c.params)
+                       what="%s/%s" % (name, c.name),
+                       params={k: workloads.resolve(v, arrays) for k, v in c.params.items()})
 
 
 # ---------------------------------------------------------------- MFMA engine

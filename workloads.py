@@ -42,6 +42,7 @@ class Case:
     """One consumer call on a workload."""
     name: str
     consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk | mean | cg_solve
+    #                          | backward_<consumer>
     x: str                   # array used as X
     y: str                   # array used as Y
     metric: str
@@ -215,6 +216,20 @@ def attention_packed(n: int = 16384, d: int = 64, c: int = 64, min_len: int = 25
     return arrays, cases
 
 
+def attention_backward(n: int = 16384, d: int = 64, c: int = 64, seed: int = 1013):
+    """Backward of the softmax attention workload, float32: the arrays of
+    `attention` plus an upstream gradient dO ~ N(0, 1) [n, c]; gradients of
+    Q, K and V (guide: backward by replay)."""
+    arrays, cases = attention(n=n, d=d, c=c, seed=seed)
+    g = _gen(seed + 1)
+    arrays["dO"] = _randn(g, n, c).to(torch.float32).numpy()
+    c0 = cases[0]
+    c0.name = "attention_backward"
+    c0.consumer = "backward_softmax_matmul"
+    c0.params = {"G": "dO"}
+    return arrays, cases
+
+
 def kernel_ridge(n: int = 65536, d: int = 16, seed: int = 1012):
     """Kernel ridge regression / GP mean, float32 (Task Map, Kernel ridge row:
     solve(K + a * eye_like(K), Y, method="cg")): x ~ N(0, I) [n, 16], rbf
@@ -253,6 +268,7 @@ WORKLOADS = {
     "attention_causal": (attention_causal, {}, {"n": 700}),
     "attention_packed": (attention_packed, {}, {"n": 900, "min_len": 40, "max_len": 300}),
     "kernel_ridge": (kernel_ridge, {}, {"n": 900}),
+    "attention_backward": (attention_backward, {}, {"n": 700}),
 }
 
 

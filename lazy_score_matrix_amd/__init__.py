@@ -544,9 +544,94 @@ def _replay(e, consumer, V=None, **kw):
     return _Replay.apply(spec, e.X, e.Y, V, *tensors)
 
 
-def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()) -> LazyScores:
-    """Bind S[i, j] = ops(metric(X[i], Y[j])); Y defaults to X."""
-    return LazyScores(X, X if Y is None else Y, metric, gamma, ops)
+class BatchedLazyScores:
+    """Lazy scores over leading batch dimensions (Task Map, MMD row: one
+    feature set per batch element; the Features page: a [1, N, *] input
+    compares against every element of a [B, M, *] input). X is [B or 1,
+    N, D], Y is [B or 1, M, D]; op vectors are either shared ([N] / [M]) or
+    per element ([B, N] / [B, M]). Each element binds its own LazyScores
+    and runs the same fused kernels; outputs stack along a leading B axis.
+    Differentiable like LazyScores (the slices carry autograd)."""
+
+    def __init__(self, X, Y, metric="linear", gamma=1.0, ops=()):
+        if X.dim() != 3 or Y.dim() != 3:
+            raise ValueError("batched scores need [B, N, D] and [B, M, D] inputs")
+        bx, by = X.shape[0], Y.shape[0]
+        if bx != by and 1 not in (bx, by):
+            raise ValueError("batch sizes %d and %d do not broadcast" % (bx, by))
+        self.B = max(bx, by)
+        self.X, self.Y, self.metric, self.gamma = X, Y, metric, float(gamma)
+        self.ops = expand_ops(ops)
+        self.N, self.M, self.D = X.shape[1], Y.shape[1], X.shape[2]
+
+    def element(self, b: int) -> LazyScores:
+        X = self.X[b if self.X.shape[0] > 1 else 0]
+        Y = self.Y[b if self.Y.shape[0] > 1 else 0]
+        ops = []
+        for n, a in self.ops:
+            if torch.is_tensor(a) and a.dim() == 2:  # per-element vector [B, len]
+                a = a[b]
+            ops.append((n, a))
+        return LazyScores(X, Y, self.metric, self.gamma, ops)
+
+    def _each(self, fn):
+        outs = [fn(self.element(b)) for b in range(self.B)]
+        if isinstance(outs[0], tuple):
+            return tuple(torch.stack(parts) for parts in zip(*outs))
+        return torch.stack(outs)
+
+    def _V(self, V, b):
+        return V[b if V.shape[0] > 1 else 0] if V.dim() == 3 else V
+
+    def matmul(self, V, mask=None):
+        return torch.stack([self.element(b).matmul(self._V(V, b), mask=mask) for b in range(self.B)])
+
+    __matmul__ = matmul
+
+    def softmax_matmul(self, V, mask=None):
+        return torch.stack([self.element(b).softmax_matmul(self._V(V, b), mask=mask) for b in range(self.B)])
+
+    def displacement(self, mask=None):
+        return self._each(lambda e: e.displacement(mask=mask))
+
+    def logsumexp(self, exclude_self=False, mask=None):
+        return self._each(lambda e: e.logsumexp(exclude_self, mask=mask))
+
+    def topk(self, k, largest=False, mask=None):
+        return self._each(lambda e: e.topk(k, largest, mask=mask))
+
+    def min(self, dim=-1):
+        return self._each(lambda e: e.min(dim))
+
+    def max(self, dim=-1):
+        return self._each(lambda e: e.max(dim))
+
+    def argmin(self, dim=-1):
+        return self._each(lambda e: e.argmin(dim))
+
+    def sum(self, dim=-1):
+        return self._each(lambda e: e.sum(dim))
+
+    def mean(self, dim=-1):
+        return self._each(lambda e: e.mean(dim))
+
+    def masked(self, mask):
+        mask = [mask] if isinstance(mask, tuple) else list(mask)
+        return BatchedLazyScores(self.X, self.Y, self.metric, self.gamma, list(self.ops) + mask)
+
+    @property
+    def T(self):
+        ops = [(_SWAP.get(n, n), a) for n, a in self.ops]
+        return BatchedLazyScores(self.Y, self.X, self.metric, self.gamma, ops)
+
+
+def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()):
+    """Bind S[i, j] = ops(metric(X[i], Y[j])); Y defaults to X. Inputs with
+    a leading batch axis ([B, N, D]) give a BatchedLazyScores."""
+    Y = X if Y is None else Y
+    if X.dim() == 3 or Y.dim() == 3:
+        return BatchedLazyScores(X if X.dim() == 3 else X[None], Y if Y.dim() == 3 else Y[None], metric, gamma, ops)
+    return LazyScores(X, Y, metric, gamma, ops)
 
 
 def svgd_direction(x: torch.Tensor, score: torch.Tensor, gamma: float, workspace=None) -> torch.Tensor:

@@ -287,15 +287,16 @@ def main():
     dtype = "f32" if calls[0][1].dtype == torch.float32 else "f64"
     dom0 = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
     c_, e_, _, _, C_ = calls[dom0]
-    # The backward runs on the vector engine whatever the forward's plan.
-    contraction = (not c_.consumer.startswith("backward_")
-                   and e_.plan(lib_consumer(c_), C_, c_.k).startswith("family=mfma"))
+    if c_.consumer.startswith("backward_"):
+        contraction = e_.backward_plan(lib_consumer(c_), C_).startswith("family=mfma")
+    else:
+        contraction = e_.plan(lib_consumer(c_), C_, c_.k).startswith("family=mfma")
     peak = PEAK_TFLOPS[dtype] if contraction else ALU_PEAK_TFLOPS[dtype]
     kernels = []
     for (c, e, _, _, C), kms in zip(calls, kernel_ms):
         fl = float(c.pairs if c.pairs is not None else e.N * e.M) * flops_per_pair(c, e.D, C)
         tf = fl / (kms * 1e-3) / 1e12
-        plan = ("vector backward engine (row side, column side)" if c.consumer.startswith("backward_")
+        plan = (e.backward_plan(lib_consumer(c), C) if c.consumer.startswith("backward_")
                 else e.plan(lib_consumer(c), C, c.k))
         kernels.append({"call": c.name, "plan": plan, "avg_ms": round(kms, 4),
                         "flops_per_pair": flops_per_pair(c, e.D, C), "tflops": round(tf, 3),

@@ -229,6 +229,11 @@ typedef struct {
                               ADD/WEIGHT_ROWS/COLUMNS ops, else ignored; NULL: not wanted */
 } pw_grad_out;
 
+/* Describe the kernels pw_backward would run for `consumer` and C value
+ * columns when no op-vector gradient is asked (want_ops = 0) or some is
+ * (want_ops = 1): the matrix-core backward or the vector backward engine. */
+int pw_backward_plan_describe(const pw_expr *e, int consumer, int64_t C, int want_ops, char *buf, size_t len);
+
 /* Workspace bytes of pw_backward for `consumer`, C value columns, k. */
 int pw_backward_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes);
 

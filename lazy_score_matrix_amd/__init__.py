@@ -99,6 +99,7 @@ def load_library(path: str = LIB_PATH):
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
         lib.pw_backward_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
+        lib.pw_backward_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
         lib.pw_backward.argtypes = [vp, c_int, ctypes.POINTER(_GradIn), ctypes.POINTER(_GradOut), vp, sz, vp]
         lib.pw_cg_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
         lib.pw_cg_solve.argtypes = [vp, ctypes.c_double, vp, i64, i64, vp, i64, c_int, ctypes.c_double, c_int, vp, sz,
@@ -377,6 +378,12 @@ class LazyScores:
         check(self._lib.pw_backward(self._h, CONSUMERS[consumer], ctypes.byref(gin), ctypes.byref(gout),
                                     ws.data_ptr(), ws.numel(), _stream(self.device)), "pw_backward")
         return res
+
+    def backward_plan(self, consumer: str, C: int = 0, want_ops: bool = False) -> str:
+        buf = ctypes.create_string_buffer(256)
+        check(self._lib.pw_backward_plan_describe(self._h, CONSUMERS[consumer], int(C), int(bool(want_ops)), buf, 256),
+              "pw_backward_plan_describe")
+        return buf.value.decode()
 
     def backward_workspace(self, consumer: str, C: int = 0, k: int = 0) -> torch.Tensor:
         n = ctypes.c_size_t()

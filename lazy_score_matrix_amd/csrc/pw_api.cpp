@@ -755,6 +755,9 @@ struct GradPlan {
   int dt = 4, ct = 16, n_arith = 0;
   int n_rb[2] = {0, 0}, n_split[2] = {1, 1}, W[2] = {0, 0};
   int64_t split[2] = {0, 0};
+  // The matrix-core backward (128-row workgroups, two per CU).
+  int m_n_rb[2] = {0, 0}, m_n_split[2] = {1, 1};
+  int64_t m_split[2] = {0, 0};
   size_t off_lse = 0, off_delta = 0, off_invx = 0, off_invy = 0, off_part = 0, off_fwd = 0, off_epi = 0, total = 0;
 };
 
@@ -776,6 +779,13 @@ GradPlan grad_plan(const pw_expr &e, int consumer, int64_t C) {
     g.n_split[side] = (int)std::max<int64_t>(1, (n_oth + g.split[side] - 1) / g.split[side]);
     g.W[side] = (int)e.D + ((side == 1 && value) ? (int)C : 0) + g.n_arith;
     part = std::max(part, (size_t)g.n_split[side] * (size_t)n_own * (size_t)g.W[side] * es);
+    const int mrows = mfma_grad_rows();
+    g.m_n_rb[side] = (int)std::max<int64_t>(1, (n_own + mrows - 1) / mrows);
+    int64_t mwant = std::max<int64_t>(1, (2 * kTargetCUs + g.m_n_rb[side] - 1) / g.m_n_rb[side]);
+    mwant = std::min(mwant, tiles);
+    g.m_split[side] = (tiles + mwant - 1) / mwant * kGradCols;
+    g.m_n_split[side] = (int)std::max<int64_t>(1, (n_oth + g.m_split[side] - 1) / g.m_split[side]);
+    part = std::max(part, (size_t)g.m_n_split[side] * (size_t)n_own * (size_t)g.W[side] * es);
   }
   size_t off = 0;
   g.off_lse = off;
@@ -800,6 +810,25 @@ GradPlan grad_plan(const pw_expr &e, int consumer, int64_t C) {
 }  // namespace
 
 extern "C" {
+
+int pw_backward_plan_describe(const pw_expr *e, int consumer, int64_t C, int want_ops, char *buf, size_t len) {
+  if (!e || !buf || len == 0 || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
+  const GradPlan g = grad_plan(*e, consumer, std::max<int64_t>(C, 1));
+  const bool fast = !want_ops && e->stages.size() <= 1 && (e->stages.empty() || e->stages[0].kind == ST_AFFINE);
+  const bool masked = e->row_mask || e->col_mask || e->band || e->grow;
+  const bool col_stage = !e->stages.empty() && e->stages[0].col_vec;
+  const bool mfma = e->dtype == PW_F32 && e->metric == PW_LINEAR && fast && !col_stage && !masked && e->D >= 16 &&
+                    (consumer == PW_C_SOFTMAX_MATMUL || consumer == PW_C_LOGSUMEXP);
+  if (consumer == PW_C_TOPK)
+    std::snprintf(buf, len, "family=grad_topk dtile=%d", g.dt);
+  else if (mfma)
+    std::snprintf(buf, len, "family=mfma_grad dp=%d cp=%d rows_per_wg=%d splits=%d/%d", e->D <= 16 ? 16 : (e->D <= 32 ? 32 : 64),
+                  C <= 32 ? 32 : 64, mfma_grad_rows(), g.m_n_split[0], g.m_n_split[1]);
+  else
+    std::snprintf(buf, len, "family=valu_grad dtile=%d ctile=%d fast=%d splits=%d/%d", g.dt, g.ct, fast ? 1 : 0,
+                  g.n_split[0], g.n_split[1]);
+  return PW_OK;
+}
 
 int pw_backward_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes) {
   (void)k;
@@ -964,6 +993,67 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
                    : consumer == PW_C_LOGSUMEXP ? C_LOGSUMEXP : C_SOFTMAX;
   const int last_side = want_side(1) ? 1 : 0;
   bool started = false;
+
+  // Dot-product scores with one row-only affine stage, float32, no masks:
+  // the matrix-core backward (softmax@V and logsumexp).
+  const bool mfma = e->dtype == PW_F32 && e->metric == PW_LINEAR && a.fast && !a.stage.col_vec && !a.mask.any &&
+                    e->D >= 16 && (cons == C_SOFTMAX || cons == C_LOGSUMEXP);
+  if (mfma) {
+    MfmaGradArgs m;
+    std::memset(&m, 0, sizeof(m));
+    m.X = static_cast<const float *>(e->X);
+    m.Y = static_cast<const float *>(e->Y);
+    m.V = static_cast<const float *>(in->V);
+    m.G = static_cast<const float *>(in->G);
+    m.ldx = e->ldx;
+    m.ldy = e->ldy;
+    m.ldv = in->ldv;
+    m.ldg = in->ldg;
+    m.N = e->N;
+    m.M = e->M;
+    m.D = (int)e->D;
+    m.C = (int)C;
+    m.lse = static_cast<const float *>(a.lse);
+    m.delta = static_cast<const float *>(a.delta);
+    m.row_vec = a.stage.row_vec;
+    m.r_s = (float)a.stage.r_scalar;
+    m.p_s = (float)a.stage.p_scalar;
+    m.r_vec = static_cast<const float *>(a.stage.r_vec);
+    m.p_vec = static_cast<const float *>(a.stage.p_vec);
+    m.exclude_self = a.exclude_self;
+    m.partial = reinterpret_cast<float *>(base + g.off_part);
+    const int dp = e->D <= 16 ? 16 : (e->D <= 32 ? 32 : 64);
+    const int cp = C <= 32 ? 32 : 64;
+    for (int side = 0; side < 2 && rc == PW_OK; ++side) {
+      if (!want_side(side)) continue;
+      if (!started && tile_ev_start) hipEventRecord(tile_ev_start, s);
+      started = true;
+      m.n_rb = g.m_n_rb[side];
+      m.n_split = g.m_n_split[side];
+      m.split = g.m_split[side];
+      m.W = (int)e->D + ((side == 1 && cons == C_SOFTMAX) ? (int)C : 0);
+      rc = hip_status(mfma_grad_launch(cons, side, dp, cp, m, s));
+      if (rc != PW_OK) break;
+      GradArgs ma;
+      std::memset(&ma, 0, sizeof(ma));
+      ma.partial = m.partial;
+      ma.n_split = m.n_split;
+      ma.W = m.W;
+      ma.D = m.D;
+      GradOut o;
+      std::memset(&o, 0, sizeof(o));
+      o.own = side == 0 ? out->dX : out->dY;
+      o.ld_own = side == 0 ? out->lddx : out->lddy;
+      if (side == 1) {
+        o.dV = out->dV;
+        o.lddv = out->lddv;
+      }
+      rc = hip_status(launch_grad_merge(e->dtype, ma, side, side == 0 ? e->N : e->M,
+                                        (side == 1 && cons == C_SOFTMAX) ? (int)C : 0, o, s));
+      if (side == last_side && tile_ev_stop) hipEventRecord(tile_ev_stop, s);
+    }
+    return rc;
+  }
   for (int side = 0; side < 2 && rc == PW_OK; ++side) {
     if (!want_side(side)) continue;
     if (!started && tile_ev_start) hipEventRecord(tile_ev_start, s);

@@ -231,6 +231,26 @@ struct GradOut {
   int64_t lddv;
   void *dop[kGradOps];  // only the ops on this side are written
 };
+// Matrix-core backward of dot-product scores s_ij = r_i (x_i . y_j) + p_i
+// for softmax@V and logsumexp, float32 (mfma_grad.hip).
+struct MfmaGradArgs {
+  const float *X, *Y, *V, *G;
+  int64_t ldx, ldy, ldv, ldg;
+  int64_t N, M;
+  int D, C;
+  const float *lse;    // [N] row log-sum-exp
+  const float *delta;  // [N] G_i . O_i (softmax)
+  int row_vec;         // r_i, p_i from r_vec / p_vec, else r_s, p_s
+  float r_s, p_s;
+  const float *r_vec, *p_vec;
+  int exclude_self;
+  int n_rb, n_split;
+  int64_t split;
+  float *partial;      // [n_split][own rows][W]: own gradient (D), then dV (C, side 1)
+  int W;
+};
+hipError_t mfma_grad_launch(int consumer, int side, int dp, int cp, const MfmaGradArgs &a, hipStream_t s);
+int mfma_grad_rows();  // rows per workgroup of the matrix-core backward
 hipError_t grad_launch(int dtype, int metric, int consumer, int side, int dt, int ct, const GradArgs &a,
                        hipStream_t s);
 hipError_t grad_topk_launch(int dtype, int metric, int dt, const GradArgs &a, hipStream_t s);

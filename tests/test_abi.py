@@ -190,6 +190,37 @@ def test_product_has_no_oracle_dependency():
                 assert "liboracle" not in text, f
 
 
+def test_backward_validation(lib):
+    """pw_backward rejects bad arguments on the host before any launch."""
+    ok, h = bind(lib, N=12, M=12, D=16)
+    gin, gout = pw._GradIn(), pw._GradOut()
+    gin.G, gin.ldg = FAKE, 4
+    gin.V, gin.C, gin.ldv = FAKE, 4, 4
+    gin.out, gin.ldo = FAKE, 4
+    assert lib.pw_backward(h, 5, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_INVALID
+    assert lib.pw_backward(h, 0, None, ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_INVALID
+    gin.C = 65
+    gin.ldv = gin.ldg = gin.ldo = 65
+    assert lib.pw_backward(h, 3, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_UNSUPPORTED
+    gin.C, gin.ldv, gin.ldg, gin.ldo = 4, 4, 3, 4                        # ldg < C
+    assert lib.pw_backward(h, 0, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_INVALID
+    gin.ldg = 4
+    gin.out = 0                                                          # softmax needs its forward output
+    assert lib.pw_backward(h, 3, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_INVALID
+    gin.out = FAKE
+    gin.indices, gin.k = FAKE, 13                                        # k > M
+    assert lib.pw_backward(h, 4, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_INVALID
+    gout.dX, gout.lddx = FAKE, 15                                        # lddx < D
+    assert lib.pw_backward(h, 0, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 30, None) == pw.PW_ERR_INVALID
+    gout.lddx = 16
+    n = ctypes.c_size_t()
+    assert lib.pw_backward_workspace_size(h, 0, 4, 0, ctypes.byref(n)) == pw.PW_OK
+    assert lib.pw_backward(h, 0, ctypes.byref(gin), ctypes.byref(gout), FAKE, n.value - 1, None) == pw.PW_ERR_WORKSPACE
+    buf = ctypes.create_string_buffer(256)
+    assert lib.pw_backward_plan_describe(h, 3, 4, 0, buf, 256) == pw.PW_OK and b"family=" in buf.value
+    lib.pw_release(h)
+
+
 def test_cg_solve_validation(lib):
     """pw_cg_solve rejects bad arguments on the host before any launch."""
     ok, h = bind(lib, N=12, M=12)

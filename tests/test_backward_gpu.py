@@ -140,3 +140,39 @@ def test_autograd_through_consumers(consumer):
     _compare(grads[2], ref["ops"][0], dtype, 110, "d bias")
     if consumer in ("matmul", "softmax_matmul"):
         _compare(grads[3], ref["dV"], dtype, 90, "dV")
+
+
+MFMA_BWD = [(c, D, C, chain) for c in ("softmax_matmul", "logsumexp") for D in (16, 20, 48, 64)
+            for C in ((16, 33, 64) if c == "softmax_matmul" else (0,)) for chain in ("scale", "row_affine")]
+
+
+@pytest.mark.parametrize("consumer,D,C,chain", MFMA_BWD, ids=["%s-D%d-C%d-%s" % t for t in MFMA_BWD])
+def test_backward_matrix_cores(consumer, D, C, chain):
+    """Dot-product scores with one row-only affine stage in float32: the
+    matrix-core backward (no op grads asked). N = 300, M = 333: ragged row
+    blocks, sub-blocks and key tiles on both sides."""
+    r = np.random.default_rng(3600 + D + C)
+    n, m = 300, 333
+    X = r.standard_normal((n, D)).astype(np.float32)
+    Y = r.standard_normal((m, D)).astype(np.float32)
+    ops = [("mul", 1.0 / np.sqrt(D))]
+    if chain == "row_affine":
+        ops += [("add_rows", r.standard_normal(n).astype(np.float32)),
+                ("weight_rows", (0.5 + r.random(n)).astype(np.float32))]
+    e, oe = bind_both(X, Y, "linear", 1.0, ops)
+    assert e.backward_plan(consumer, C).startswith("family=mfma_grad"), e.backward_plan(consumer, C)
+    V = r.standard_normal((m, C)).astype(np.float32) if C else None
+    G = r.standard_normal((n, C if C else 1)).astype(np.float32)
+    check_backward(e, oe, consumer, G, V=V, want=("X", "Y", "V"), what="mfma bwd %s D=%d C=%d" % (consumer, D, C))
+
+
+@pytest.mark.parametrize("n", [1, 31, 1000])
+def test_backward_matrix_cores_infonce(n):
+    """InfoNCE shape: X with itself, a row bias, the self pair excluded."""
+    r = np.random.default_rng(3700 + n)
+    z = r.standard_normal((n, 32)).astype(np.float32)
+    z /= np.linalg.norm(z, axis=1, keepdims=True)
+    e, oe = bind_both(z, z, "linear", 1.0, [("mul", 1 / 0.07), ("add_rows", r.standard_normal(n).astype(np.float32))],
+                      same=True)
+    G = r.standard_normal((n, 1)).astype(np.float32)
+    check_backward(e, oe, "logsumexp", G, exclude_self=True, want=("X", "Y"), what="infonce bwd n=%d" % n)

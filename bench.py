@@ -175,13 +175,14 @@ def main():
             # forward itself runs once, before the timed region).
             V = t[c.v]
             C = V.shape[1]
-            O = e.softmax_matmul(V)
+            lse = torch.empty(N, dtype=X.dtype, device=dev)
+            O = e.softmax_matmul(V, lse=lse)  # the forward keeps its row statistics
             G = t[c.params["G"]]
             grads = {"X": torch.empty(N, D, dtype=X.dtype, device=dev), "Y": torch.empty(M, D, dtype=X.dtype, device=dev),
                      "V": torch.empty(M, C, dtype=X.dtype, device=dev)}
             ws = e.backward_workspace("softmax_matmul", C)
-            fn = (lambda e=e, G=G, V=V, O=O, grads=grads, ws=ws:
-                  e.backward("softmax_matmul", G, V=V, out=O, grads=grads, workspace=ws))
+            fn = (lambda e=e, G=G, V=V, O=O, grads=grads, ws=ws, lse=lse:
+                  e.backward("softmax_matmul", G, V=V, out=O, grads=grads, workspace=ws, lse=lse))
             outs = (grads["X"], grads["Y"], grads["V"])
         elif c.consumer == "cg_solve":
             # One step is one whole solve; its pairs are iterations * N * M,

@@ -183,6 +183,13 @@ int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t
 int pw_softmax_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *ws,
                       size_t ws_bytes, void *stream);
 
+/* softmax@V as pw_softmax_matmul, also writing each row's log-sum-exp of the
+ * scores, lse[i] = log sum_j exp(s_ij) (-inf for a row with no kept pair),
+ * the per-row statistic the backward replays with (guide, opening section:
+ * backward by replay; pw_grad_in.lse). lse: N elements of the bound dtype. */
+int pw_softmax_matmul_lse(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *lse,
+                          void *ws, size_t ws_bytes, void *stream);
+
 /* Row top-k (guide, Task Map, k-NN row `topk(k, largest=False)` with exact
  * tie order, and Chamfer row: min/argmin are k = 1):
  * the k pairs of each row that come first when ordered by s_ij ascending
@@ -216,6 +223,8 @@ typedef struct {
   const int64_t *indices;  /* top-k: the forward call's indices [N, k] (-1 entries skipped) */
   int k;
   int exclude_self;        /* logsumexp: as in the forward call */
+  const void *lse;         /* softmax: the forward's row log-sum-exp [N] from
+                              pw_softmax_matmul_lse, or NULL (recomputed) */
 } pw_grad_in;
 
 typedef struct {

@@ -64,7 +64,8 @@ SOLVE_STATUS = {0: "converged", 1: "max_iter", 2: "breakdown"}
 class _GradIn(ctypes.Structure):
     _fields_ = [("G", ctypes.c_void_p), ("ldg", ctypes.c_int64), ("V", ctypes.c_void_p), ("C", ctypes.c_int64),
                 ("ldv", ctypes.c_int64), ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64),
-                ("indices", ctypes.c_void_p), ("k", ctypes.c_int), ("exclude_self", ctypes.c_int)]
+                ("indices", ctypes.c_void_p), ("k", ctypes.c_int), ("exclude_self", ctypes.c_int),
+                ("lse", ctypes.c_void_p)]
 
 
 class _GradOut(ctypes.Structure):
@@ -94,6 +95,7 @@ def load_library(path: str = LIB_PATH):
         lib.pw_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
         lib.pw_matmul.argtypes = [vp, vp, i64, i64, vp, i64, vp, sz, vp]
         lib.pw_softmax_matmul.argtypes = [vp, vp, i64, i64, vp, i64, vp, sz, vp]
+        lib.pw_softmax_matmul_lse.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, sz, vp]
         lib.pw_displacement.argtypes = [vp, vp, i64, vp, sz, vp]
         lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
@@ -265,19 +267,27 @@ class LazyScores:
 
     __matmul__ = matmul
 
-    def softmax_matmul(self, V: torch.Tensor, out=None, workspace=None, mask=None) -> torch.Tensor:
+    def softmax_matmul(self, V: torch.Tensor, out=None, workspace=None, mask=None, lse=None) -> torch.Tensor:
         """out[i, c] = sum_j softmax_j(S[i, :])[j] V[j, c], over the pairs
-        `mask` (op entries, e.g. masks.causal()) and the bound masks keep."""
+        `mask` (op entries, e.g. masks.causal()) and the bound masks keep.
+        With `lse` (an [N] tensor) each row's log-sum-exp is written too."""
         if mask is not None:
-            return self.masked(mask).softmax_matmul(V, out, workspace)
-        if out is None and _needs_grad(self, V):
+            return self.masked(mask).softmax_matmul(V, out, workspace, lse=lse)
+        if out is None and lse is None and _needs_grad(self, V):
             return _replay(self, "softmax_matmul", V)
         ldv = self._value(V, "softmax_matmul")
         C = V.shape[1]
         out = torch.empty(self.N, C, dtype=self.dtype, device=self.device) if out is None else out
         ws, nb = self._ws(workspace, "softmax_matmul", C)
-        check(self._lib.pw_softmax_matmul(self._h, V.data_ptr(), C, ldv, out.data_ptr(), _rows(out, "out"),
-                                          ws.data_ptr(), nb, _stream(self.device)), "pw_softmax_matmul")
+        if lse is None:
+            check(self._lib.pw_softmax_matmul(self._h, V.data_ptr(), C, ldv, out.data_ptr(), _rows(out, "out"),
+                                              ws.data_ptr(), nb, _stream(self.device)), "pw_softmax_matmul")
+        else:
+            if lse.dtype != self.dtype or lse.device != self.device or lse.numel() != self.N or not lse.is_contiguous():
+                raise ValueError("lse must be a contiguous [N] %s tensor on %s" % (self.dtype, self.device))
+            check(self._lib.pw_softmax_matmul_lse(self._h, V.data_ptr(), C, ldv, out.data_ptr(), _rows(out, "out"),
+                                                  lse.data_ptr(), ws.data_ptr(), nb, _stream(self.device)),
+                  "pw_softmax_matmul_lse")
         return out
 
     def displacement(self, out=None, workspace=None, mask=None) -> torch.Tensor:
@@ -321,7 +331,7 @@ class LazyScores:
 
     # -- backward -------------------------------------------------------
     def backward(self, consumer: str, G: torch.Tensor, V=None, out=None, indices=None, exclude_self=False,
-                 want=("X", "Y", "V", "ops"), grads=None, workspace=None):
+                 want=("X", "Y", "V", "ops"), grads=None, workspace=None, lse=None):
         """Gradients of sum(consumer output * G) by replay (guide: backward
         re-evaluates the pairs; selections route gradients through the
         selected pairs only). Returns {"X": dX, "Y": dY, "V": dV, "ops": [per
@@ -345,6 +355,9 @@ class LazyScores:
             keep.append(idx)
             gin.indices, gin.k = idx.data_ptr(), idx.shape[1]
         gin.exclude_self = int(bool(exclude_self))
+        if lse is not None:
+            gin.lse = lse.data_ptr()
+            keep.append(lse)
         res = {"X": None, "Y": None, "V": None, "ops": [None] * len(self.ops)}
         gout = _GradOut()
         given = grads or {}
@@ -492,8 +505,13 @@ class _Replay(torch.autograd.Function):
         it = iter(tensors)
         ops = [(n, next(it) if is_t else a) for n, a, is_t in ops_spec]
         e = LazyScores(X, Y, metric, gamma, ops)
-        if consumer in ("matmul", "softmax_matmul"):
-            out = getattr(e, consumer)(V)
+        lse = torch.empty(0)
+        if consumer == "softmax_matmul":
+            lse = torch.empty(e.N, dtype=e.dtype, device=e.device)
+            out = e.softmax_matmul(V, lse=lse)
+            outs = (out,)
+        elif consumer == "matmul":
+            out = e.matmul(V)
             outs = (out,)
         elif consumer == "displacement":
             out = e.displacement()
@@ -507,14 +525,14 @@ class _Replay(torch.autograd.Function):
             outs = (vals, idx)
             out = vals
         ctx.spec = spec
-        ctx.save_for_backward(X, Y, V if V is not None else torch.empty(0), out, outs[-1], *tensors)
+        ctx.save_for_backward(X, Y, V if V is not None else torch.empty(0), out, outs[-1], lse, *tensors)
         ctx.has_v = V is not None
         return outs if len(outs) > 1 else outs[0]
 
     @staticmethod
     def backward(ctx, *grads):
         metric, gamma, ops_spec, consumer, kw = ctx.spec
-        X, Y, V, out, last, *tensors = ctx.saved_tensors
+        X, Y, V, out, last, lse, *tensors = ctx.saved_tensors
         V = V if ctx.has_v else None
         it = iter(tensors)
         ops = [(n, next(it) if is_t else a) for n, a, is_t in ops_spec]
@@ -529,7 +547,7 @@ class _Replay(torch.autograd.Function):
             want.append("V")
         r = e.backward(consumer, G, V=V, out=out if consumer in ("softmax_matmul", "logsumexp") else None,
                        indices=last if consumer == "topk" else None, exclude_self=kw.get("exclude_self", False),
-                       want=tuple(want))
+                       want=tuple(want), lse=lse if consumer == "softmax_matmul" else None)
         op_grads = []
         for t, (n, a, is_t) in enumerate(ops_spec):
             if is_t:

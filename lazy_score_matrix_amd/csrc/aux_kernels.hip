@@ -235,6 +235,8 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const TileArgs a) {
     }
   }
   static_cast<T *>(a.out)[i * a.ldo + c] = (l > (T)0) ? acc / l : (T)0;
+  // The split maxima carry the row offset, so m + log l is the row's lse.
+  if (c == 0 && a.lse_out) static_cast<T *>(a.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
 }
 
 template <class T, int KL>

@@ -733,11 +733,16 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
             const int ch = c * TM + F::key_of(r, g);
             if (ch < a.C) dst[ch] = fin ? o[b][c][r] * inv : o[b][c][r];
           }
+        // The row offset p_i drops out of the softmax but belongs to the
+        // row's log-sum-exp: it rides on the partial maximum (the merge's
+        // rescale is unchanged by a common shift).
         if (!fin && g == 0) {
           T *pp = static_cast<T *>(a.partial) + prow * (a.C + 2);
-          pp[0] = lt > (T)0 ? m[b] * (T)kLn2 : kNegInf;
+          pp[0] = lt > (T)0 ? m[b] * (T)kLn2 + ep[b] : kNegInf;
           pp[1] = lt;
         }
+        if (fin && g == 0 && a.lse_out)
+          static_cast<T *>(a.lse_out)[i] = lt > (T)0 ? m[b] * (T)kLn2 + ep[b] + F::log(lt) : kNegInf;
       }
     } else if constexpr (NARROW) {
       const T t = F::gsum((wsum[b][0] + wsum[b][1]) + (wsum[b][2] + wsum[b][3]));

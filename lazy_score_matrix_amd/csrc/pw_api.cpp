@@ -636,16 +636,21 @@ int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf
 
 // Shared body of the value-matrix consumers (matmul, softmax).
 static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t C, int64_t ldv, void *out,
-                          int64_t ldo, void *ws, size_t ws_bytes, void *stream) {
+                          int64_t ldo, void *ws, size_t ws_bytes, void *stream, void *lse_out = nullptr) {
   int rc = check_consumer_args(e, consumer, C, 0);
   if (rc != PW_OK) return rc;
   const size_t es = esize(e->dtype);
   if (ldv < C || ldo < C) return PW_ERR_INVALID;
   if ((e->M > 0 && !V) || (e->N > 0 && !out)) return PW_ERR_INVALID;
   if (!aligned(V, es) || !aligned(out, es)) return PW_ERR_INVALID;
+  if (lse_out && !aligned(lse_out, es)) return PW_ERR_INVALID;
   if (e->N == 0) return PW_OK;
   hipStream_t s = (hipStream_t)stream;
-  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->N, C, ldo, 0.0, s));
+  if (e->M == 0) {
+    rc = hip_status(launch_fill(e->dtype, out, e->N, C, ldo, 0.0, s));
+    if (rc == PW_OK && lse_out) rc = hip_status(launch_fill(e->dtype, lse_out, e->N, 1, 1, -HUGE_VAL, s));
+    return rc;
+  }
   Plan p = make_plan(*e, consumer, C, 0);
   char *base;
   rc = check_ws(p, ws, ws_bytes, &base);
@@ -655,6 +660,7 @@ static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t
   if (rc != PW_OK) return rc;
   a.ldv = ldv;
   a.ldo = ldo;
+  a.lse_out = consumer == PW_C_SOFTMAX_MATMUL ? lse_out : nullptr;
   const int cons = consumer == PW_C_MATMUL ? C_MATMUL : C_SOFTMAX;
   for (int64_t c0 = 0; c0 < C && rc == PW_OK; c0 += p.chunk) {
     a.C = (int)std::min<int64_t>(p.chunk, C - c0);
@@ -673,6 +679,12 @@ int pw_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out
 int pw_softmax_matmul(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *ws,
                       size_t ws_bytes, void *stream) {
   return value_consumer(e, PW_C_SOFTMAX_MATMUL, V, C, ldv, out, ldo, ws, ws_bytes, stream);
+}
+
+int pw_softmax_matmul_lse(const pw_expr *e, const void *V, int64_t C, int64_t ldv, void *out, int64_t ldo, void *lse,
+                          void *ws, size_t ws_bytes, void *stream) {
+  if (e && e->N > 0 && !lse) return PW_ERR_INVALID;
+  return value_consumer(e, PW_C_SOFTMAX_MATMUL, V, C, ldv, out, ldo, ws, ws_bytes, stream, lse);
 }
 
 int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t ws_bytes, void *stream) {
@@ -848,7 +860,8 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
     if (C > 64) return PW_ERR_UNSUPPORTED;
     if ((e->M > 0 && !in->V) || in->ldv < C || in->ldg < C || !aligned(in->V, es)) return PW_ERR_INVALID;
   }
-  if (consumer == PW_C_SOFTMAX_MATMUL && ((e->N > 0 && !in->out) || in->ldo < C || !aligned(in->out, es)))
+  if (consumer == PW_C_SOFTMAX_MATMUL &&
+      ((e->N > 0 && !in->out) || in->ldo < C || !aligned(in->out, es) || !aligned(in->lse, es)))
     return PW_ERR_INVALID;
   if (consumer == PW_C_DISPLACEMENT && in->ldg < e->D) return PW_ERR_INVALID;
   if (consumer == PW_C_LOGSUMEXP && (in->ldg < 1 || (in->exclude_self != 0 && in->exclude_self != 1) ||
@@ -939,6 +952,8 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
   if (rc == PW_OK && (consumer == PW_C_LOGSUMEXP || consumer == PW_C_SOFTMAX_MATMUL)) {
     if (consumer == PW_C_LOGSUMEXP && in->out) {
       a.lse = in->out;
+    } else if (consumer == PW_C_SOFTMAX_MATMUL && in->lse) {
+      a.lse = in->lse;
     } else {
       // The row log-sum-exp of the forward scores: one more forward pass.
       a.lse = base + g.off_lse;

@@ -101,6 +101,7 @@ struct TileArgs {
   int C;          // value columns in this launch
   void *out;      // final output (n_split == 1), already offset to the column chunk
   int64_t ldo;
+  void *lse_out;  // softmax: optional row log-sum-exp [N] of the scores (kept for the backward)
   int64_t *idx;   // top-k indices
   int k;
   int largest;

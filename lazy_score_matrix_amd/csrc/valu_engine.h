@@ -307,6 +307,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
       o[1] = l;
     }
   } else if constexpr (CONS == C_SOFTMAX) {
+    if (fin && a.lse_out) static_cast<T *>(a.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
     if (fin) {
       T *o = static_cast<T *>(a.out) + i * a.ldo;
       const T inv = (l > (T)0) ? (T)1 / l : (T)0;

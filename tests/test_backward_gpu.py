@@ -176,3 +176,24 @@ def test_backward_matrix_cores_infonce(n):
                       same=True)
     G = r.standard_normal((n, 1)).astype(np.float32)
     check_backward(e, oe, "logsumexp", G, exclude_self=True, want=("X", "Y"), what="infonce bwd n=%d" % n)
+
+
+@pytest.mark.parametrize("D", [16, 5])
+def test_backward_with_saved_lse(D):
+    """The backward given the forward's saved row log-sum-exp equals the one
+    that recomputes it (and the oracle), on the matrix-core (D = 16) and the
+    vector (D = 5) backward."""
+    r = np.random.default_rng(3800 + D)
+    n, m = 260, 700
+    X = r.standard_normal((n, D)).astype(np.float32)
+    Y = r.standard_normal((m, D)).astype(np.float32)
+    V = r.standard_normal((m, 10)).astype(np.float32)
+    G = r.standard_normal((n, 10)).astype(np.float32)
+    e, oe = bind_both(X, Y, "linear", 1.0, [("mul", 0.25), ("add_rows", r.standard_normal(n).astype(np.float32))])
+    lse = torch.empty(n, device="cuda")
+    out = e.softmax_matmul(to_dev(V), lse=lse)
+    got = e.backward("softmax_matmul", to_dev(G), V=to_dev(V), out=out, lse=lse, want=("X", "Y", "V"))
+    ref = oracle.backward(oe, "softmax_matmul", G, V)
+    for key, terms in (("X", m), ("Y", n), ("V", n)):
+        ok, ratio = grad_report(got[key], ref["d" + key], np.float32, terms)
+        assert ok, (key, ratio)

@@ -344,3 +344,30 @@ def test_mfma_determinism():
     a = e.softmax_matmul(to_dev(V)).cpu().numpy()
     b = e.softmax_matmul(to_dev(V)).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("metric", ["linear", "sqeuclidean"])
+@pytest.mark.parametrize("D", [3, 32, 64])
+@pytest.mark.parametrize("chain", ["scale", "row_affine", "causal"])
+@pytest.mark.parametrize("M", [333, 5000])
+def test_softmax_keeps_row_logsumexp(dtype, metric, D, chain, M):
+    """softmax@V with its row log-sum-exp (the statistic the backward
+    replays with) equals the oracle's log-sum-exp of the same scores, on
+    both engines, with and without column splits (M = 5000)."""
+    import oracle
+    from parity import assert_values
+    X, Y, r = _data(4200 + D + M, 300, M, D, dtype)
+    V = r.standard_normal((M, 12)).astype(dtype)
+    ops = [("mul", (1.0 / np.sqrt(D)) if metric == "linear" else -0.5 / D)]
+    if chain == "row_affine":
+        ops += [("add_rows", r.standard_normal(300).astype(dtype)), ("weight_rows", (0.5 + r.random(300)).astype(dtype))]
+    elif chain == "causal":
+        ops += [("causal", 40)]
+    e, oe = bind_both(X, Y, metric, 1.0, ops)
+    lse = torch.empty(300, dtype=torch.float32 if dtype == np.float32 else torch.float64, device="cuda")
+    out = e.softmax_matmul(to_dev(V), lse=lse)
+    o, mag = oracle.softmax_matmul(oe, V)
+    assert_values(out.cpu().numpy(), o, mag, dtype, n_terms=M, vmax=float(np.max(np.abs(V))), what="softmax")
+    ol, lmag = oracle.logsumexp(oe)
+    assert_values(lse.cpu().numpy(), ol, lmag, dtype, n_terms=M, what="softmax lse")

@@ -368,7 +368,8 @@ def backward_cpu_leg(c, oe, arrays, outs, budget, threads):
     t0 = time.perf_counter()
     ref = run(rows)
     dt = time.perf_counter() - t0
-    pairs = 2 * len(rows) * oe.M + (oe.N * oe.M if base in ("softmax_matmul", "logsumexp") else 0)
+    kept = c.pairs if c.pairs is not None else oe.N * oe.M  # masked workloads count kept pairs
+    pairs = 2 * len(rows) * kept / oe.N + (kept if base in ("softmax_matmul", "logsumexp") else 0)
     import torch
     sel = torch.as_tensor(rows, device=outs[0].device)
     dtype = np.dtype(oe.np_dtype)

@@ -15,7 +15,9 @@
 // Both use the forward engine's layout: lane l owns the row (column) l % 32
 // and holds 16 scores of the streamed side per 32-wide sub-block, so the same
 // registers are the B operand of the second contraction. Column splits give
-// partial sums that the shared merge kernel adds in split order.
+// partial sums that the shared merge kernel adds in split order. A band
+// limits the streamed range and classifies tiles like the forward (skipped,
+// kept whole, or checked pair by pair, as are row and column masks).
 #include "mfma_engine.h"
 
 namespace pw {
@@ -23,7 +25,7 @@ namespace {
 
 constexpr int kGWaves = 4, kGThreads = 256, kGBN = 64;
 
-template <int CONS, int DP, int CP, int SIDE>
+template <int CONS, int DP, int CP, int SIDE, bool MASKED>
 __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradArgs a) {
   using F = Mfma<float>;
   using acc_t = F::acc_t;
@@ -38,13 +40,63 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
   __shared__ __attribute__((aligned(16))) float sA[BN][DP + KP];   // Y_j (row side), r_i X_i (column side)
   __shared__ __attribute__((aligned(16))) float sB[BN][CPS + KP];  // V_j (row side), G_i (column side)
   __shared__ float sC[BN], sD[BN];                                  // column side: c_i, delta_i or g_i
+  __shared__ int sK[MASKED ? BN : 1];                               // streamed side's row / column mask
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, q = l & 31;
-  const int rb = blockIdx.x % a.n_rb, sp = blockIdx.x / a.n_rb;
+  constexpr int OWN = kGWaves * TM;  // own rows (columns) per block
   const int64_t n_own = SIDE == 0 ? a.N : a.M, n_oth = SIDE == 0 ? a.M : a.N;
-  const int64_t o = (int64_t)rb * (kGWaves * TM) + w * TM + q;
+  const MaskArgs &mk = a.mask;
+  // The streamed range a band leaves to own block b: keys j in [i + lo,
+  // i + hi] of its rows (row side), rows i in [j - hi, j - lo] of its
+  // columns (column side); the start on a tile boundary.
+  auto reach = [&](int b, int64_t *f, int64_t *e) {
+    const int64_t b0 = (int64_t)b * OWN, b1 = min(n_own, b0 + OWN) - 1;
+    int64_t lo = 0, hi = n_oth;
+    if (MASKED && mk.band) {
+      lo = max(lo, SIDE == 0 ? b0 + mk.lo : b0 - mk.hi);
+      hi = min(hi, SIDE == 0 ? b1 + mk.hi + 1 : b1 - mk.lo + 1);
+    }
+    *f = lo / BN * BN;
+    *e = hi;
+  };
+  // Paired launches (a band): a workgroup takes own blocks r and
+  // n_rb - 1 - r and an equal run of their tiles, as the forward does.
+  const bool paired = MASKED && a.rb_pairs;
+  const int slots = paired ? a.rb_pairs : a.n_rb;
+  const int rb_first = blockIdx.x % slots, sp = blockIdx.x / slots;
+  const int npass = MASKED ? ((paired && a.n_rb - 1 - rb_first != rb_first) ? 2 : 1) : 1;
+  int64_t pf[2] = {0, 0}, pe[2] = {0, 0}, pt[2] = {0, 0}, v0 = 0, v1 = 0;
+  if (paired) {
+    for (int p = 0; p < npass; ++p) {
+      reach(p ? a.n_rb - 1 - rb_first : rb_first, &pf[p], &pe[p]);
+      pt[p] = pe[p] > pf[p] ? (pe[p] - pf[p] + BN - 1) / BN : 0;
+    }
+    v0 = (pt[0] + pt[1]) * sp / a.n_split;
+    v1 = (pt[0] + pt[1]) * (sp + 1) / a.n_split;
+  }
+  for (int pass = 0; pass < npass; ++pass) {
+  const int rb = pass ? a.n_rb - 1 - rb_first : rb_first;
+  const int64_t own0 = (int64_t)rb * OWN, own1 = min(n_own, own0 + OWN) - 1;
+  const int64_t o = own0 + w * TM + q;
   const bool ov = o < n_own;
-  const int64_t qb = (int64_t)sp * a.split, qe = min(n_oth, qb + a.split);
+  int64_t qb, qe;
+  if (paired) {
+    const int64_t off = pass ? pt[0] : 0;
+    const int64_t t0 = max(v0 - off, (int64_t)0), t1 = min(v1 - off, pt[pass]);
+    qb = pf[pass] + t0 * BN;
+    qe = t1 > t0 ? min(pe[pass], pf[pass] + t1 * BN) : qb;
+  } else {
+    qb = (int64_t)sp * a.split;
+    qe = min(n_oth, qb + a.split);
+    if constexpr (MASKED) {
+      int64_t f, e;
+      reach(rb, &f, &e);
+      if (f > qb) qb += (f - qb) / BN * BN;
+      qe = min(qe, e);
+    }
+  }
+  // Own row (column) dropped by the row (column) mask: no pair contributes.
+  const bool own_keep = ov && (!MASKED || (SIDE == 0 ? (!mk.row || mk.row[o]) : (!mk.col || mk.col[o])));
 
   // ---- own operands
   float pa[DG], pb[SMX ? CG : 1];
@@ -98,6 +150,15 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
 
   for (int64_t q0 = qb; q0 < qe; q0 += BN) {
     const int nb = (int)min((int64_t)BN, qe - q0);
+    // Tile class under the masks (uniform over the workgroup): skipped
+    // tiles are not even staged; boundary tiles check every pair.
+    bool check = false;
+    if (MASKED) {
+      const int64_t s1 = q0 + nb - 1;
+      const int cls = SIDE == 0 ? tile_class(mk, own0, own1, q0, s1, 0, 0) : tile_class(mk, q0, s1, own0, own1, 0, 0);
+      if (cls == TILE_SKIP) continue;
+      check = cls != TILE_FULL || mk.row || mk.col;
+    }
     __syncthreads();
     for (int e = tid; e < BN * DP; e += kGThreads) {
       const int jj = e / DP, d = e % DP;
@@ -126,6 +187,12 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
         sD[jj] = in ? (SMX ? a.delta[t] : a.G[t * a.ldg]) : 0.f;
       }
     }
+    if (MASKED && check) {  // the streamed side's row / column mask
+      for (int jj = tid; jj < BN; jj += kGThreads) {
+        const int64_t t = q0 + jj;
+        sK[MASKED ? jj : 0] = jj < nb && (SIDE == 0 ? (!mk.col || mk.col[t]) : (!mk.row || mk.row[t]));
+      }
+    }
     __syncthreads();
 
 #pragma unroll
@@ -148,8 +215,12 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
 #pragma unroll
       for (int r = 0; r < NREG; ++r) {
         const int key = kb + F::key_of(r, g);
-        bool valid = key < nb;
+        bool valid = key < nb && own_keep;
         if (CONS == C_LOGSUMEXP && a.exclude_self) valid = valid && (q0 + key != o);
+        if (MASKED && check) {
+          const int64_t i = SIDE == 0 ? o : q0 + key, j = SIDE == 0 ? q0 + key : o;
+          valid = valid && sK[MASKED ? key : 0] && pair_kept(mk, i, j, 0, 0);
+        }
         float x = SIDE == 0 ? F::exp2(s[r] - ci) : F::exp2(s[r] * L2E - sC[key]);
         x = valid ? x : 0.f;
         P[r] = x;
@@ -176,31 +247,40 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
       }
     }
   }
-  if (!ov) return;
-  float *dst = a.partial + ((int64_t)sp * n_own + o) * a.W;
+  if (!MASKED && !ov) return;  // one pass only: nothing follows
+  if (ov) {
+    float *dst = a.partial + ((int64_t)sp * n_own + o) * a.W;
 #pragma unroll
-  for (int c = 0; c < ND; ++c)
-#pragma unroll
-    for (int r = 0; r < NREG; ++r) {
-      const int d = c * TM + F::key_of(r, g);
-      if (d < a.D) dst[d] = (SIDE == 0 ? ri : 1.f) * oa[c][r];
-    }
-  if constexpr (SMX && SIDE == 1) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < ND; ++c)
 #pragma unroll
       for (int r = 0; r < NREG; ++r) {
-        const int ch = c * TM + F::key_of(r, g);
-        if (ch < a.C) dst[a.D + ch] = ob[c][r];
+        const int d = c * TM + F::key_of(r, g);
+        if (d < a.D) dst[d] = (SIDE == 0 ? ri : 1.f) * oa[c][r];
       }
+    if constexpr (SMX && SIDE == 1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          const int ch = c * TM + F::key_of(r, g);
+          if (ch < a.C) dst[a.D + ch] = ob[c][r];
+        }
+    }
   }
+  }  // pass
 }
 
 template <int CONS, int DP, int CP>
 hipError_t mfma_grad_side(int side, const MfmaGradArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kGThreads);
-  if (side == 0) hipLaunchKernelGGL((mfma_grad_kernel<CONS, DP, CP, 0>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((mfma_grad_kernel<CONS, DP, CP, 1>), grid, block, 0, s, a);
+  const int slots = (a.mask.any && a.rb_pairs) ? a.rb_pairs : a.n_rb;
+  dim3 grid((unsigned)(slots * a.n_split)), block(kGThreads);
+  if (a.mask.any) {
+    if (side == 0) hipLaunchKernelGGL((mfma_grad_kernel<CONS, DP, CP, 0, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((mfma_grad_kernel<CONS, DP, CP, 1, true>), grid, block, 0, s, a);
+  } else {
+    if (side == 0) hipLaunchKernelGGL((mfma_grad_kernel<CONS, DP, CP, 0, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((mfma_grad_kernel<CONS, DP, CP, 1, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

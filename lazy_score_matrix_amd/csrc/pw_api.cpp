@@ -768,7 +768,7 @@ struct GradPlan {
   int n_rb[2] = {0, 0}, n_split[2] = {1, 1}, W[2] = {0, 0};
   int64_t split[2] = {0, 0};
   // The matrix-core backward (128-row workgroups, two per CU).
-  int m_n_rb[2] = {0, 0}, m_n_split[2] = {1, 1};
+  int m_n_rb[2] = {0, 0}, m_n_split[2] = {1, 1}, m_pairs[2] = {0, 0};
   int64_t m_split[2] = {0, 0};
   size_t off_lse = 0, off_delta = 0, off_invx = 0, off_invy = 0, off_part = 0, off_fwd = 0, off_epi = 0, total = 0;
 };
@@ -797,6 +797,11 @@ GradPlan grad_plan(const pw_expr &e, int consumer, int64_t C) {
     mwant = std::min(mwant, tiles);
     g.m_split[side] = (tiles + mwant - 1) / mwant * kGradCols;
     g.m_n_split[side] = (int)std::max<int64_t>(1, (n_oth + g.m_split[side] - 1) / g.m_split[side]);
+    if (e.band) {  // paired blocks: a pair's band tiles are dealt to the splits
+      g.m_pairs[side] = (g.m_n_rb[side] + 1) / 2;
+      const int64_t pw_ = std::max<int64_t>(1, (2 * kTargetCUs + g.m_pairs[side] - 1) / g.m_pairs[side]);
+      g.m_n_split[side] = (int)std::max<int64_t>(1, std::min<int64_t>(pw_, 2 * tiles / 4));
+    }
     part = std::max(part, (size_t)g.m_n_split[side] * (size_t)n_own * (size_t)g.W[side] * es);
   }
   size_t off = 0;
@@ -827,9 +832,8 @@ int pw_backward_plan_describe(const pw_expr *e, int consumer, int64_t C, int wan
   if (!e || !buf || len == 0 || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
   const GradPlan g = grad_plan(*e, consumer, std::max<int64_t>(C, 1));
   const bool fast = !want_ops && e->stages.size() <= 1 && (e->stages.empty() || e->stages[0].kind == ST_AFFINE);
-  const bool masked = e->row_mask || e->col_mask || e->band || e->grow;
   const bool col_stage = !e->stages.empty() && e->stages[0].col_vec;
-  const bool mfma = e->dtype == PW_F32 && e->metric == PW_LINEAR && fast && !col_stage && !masked && e->D >= 16 &&
+  const bool mfma = e->dtype == PW_F32 && e->metric == PW_LINEAR && fast && !col_stage && !e->grow && e->D >= 16 &&
                     (consumer == PW_C_SOFTMAX_MATMUL || consumer == PW_C_LOGSUMEXP);
   if (consumer == PW_C_TOPK)
     std::snprintf(buf, len, "family=grad_topk dtile=%d", g.dt);
@@ -1011,7 +1015,7 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
 
   // Dot-product scores with one row-only affine stage, float32, no masks:
   // the matrix-core backward (softmax@V and logsumexp).
-  const bool mfma = e->dtype == PW_F32 && e->metric == PW_LINEAR && a.fast && !a.stage.col_vec && !a.mask.any &&
+  const bool mfma = e->dtype == PW_F32 && e->metric == PW_LINEAR && a.fast && !a.stage.col_vec && !a.mask.grow &&
                     e->D >= 16 && (cons == C_SOFTMAX || cons == C_LOGSUMEXP);
   if (mfma) {
     MfmaGradArgs m;
@@ -1036,6 +1040,7 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
     m.r_vec = static_cast<const float *>(a.stage.r_vec);
     m.p_vec = static_cast<const float *>(a.stage.p_vec);
     m.exclude_self = a.exclude_self;
+    m.mask = a.mask;
     m.partial = reinterpret_cast<float *>(base + g.off_part);
     const int dp = e->D <= 16 ? 16 : (e->D <= 32 ? 32 : 64);
     const int cp = C <= 32 ? 32 : 64;
@@ -1046,6 +1051,7 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
       m.n_rb = g.m_n_rb[side];
       m.n_split = g.m_n_split[side];
       m.split = g.m_split[side];
+      m.rb_pairs = g.m_pairs[side];
       m.W = (int)e->D + ((side == 1 && cons == C_SOFTMAX) ? (int)C : 0);
       rc = hip_status(mfma_grad_launch(cons, side, dp, cp, m, s));
       if (rc != PW_OK) break;

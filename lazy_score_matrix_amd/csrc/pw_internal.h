@@ -245,7 +245,9 @@ struct MfmaGradArgs {
   float r_s, p_s;
   const float *r_vec, *p_vec;
   int exclude_self;
+  MaskArgs mask;       // band and row / column masks (no groups on this path)
   int n_rb, n_split;
+  int rb_pairs;        // with a band: workgroups per split, each taking own blocks r, n_rb - 1 - r
   int64_t split;
   float *partial;      // [n_split][own rows][W]: own gradient (D), then dV (C, side 1)
   int W;

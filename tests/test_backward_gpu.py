@@ -197,3 +197,31 @@ def test_backward_with_saved_lse(D):
     for key, terms in (("X", m), ("Y", n), ("V", n)):
         ok, ratio = grad_report(got[key], ref["d" + key], np.float32, terms)
         assert ok, (key, ratio)
+
+
+MASKED_BWD = [(c, D, kind) for c in ("softmax_matmul", "logsumexp") for D in (32, 64)
+              for kind in ("causal", "band", "rows_cols", "causal_rows")]
+
+
+@pytest.mark.parametrize("consumer,D,kind", MASKED_BWD, ids=["%s-D%d-%s" % t for t in MASKED_BWD])
+def test_backward_matrix_cores_masked(consumer, D, kind):
+    """The matrix-core backward under a band and row / column masks:
+    skipped, whole and checked tiles on both sides (N = 400, M = 450)."""
+    r = np.random.default_rng(3900 + D)
+    n, m = 400, 450
+    X = r.standard_normal((n, D)).astype(np.float32)
+    Y = r.standard_normal((m, D)).astype(np.float32)
+    ops = [("mul", 1.0 / np.sqrt(D))]
+    if kind == "causal":
+        ops += [("causal", 0)]
+    elif kind == "band":
+        ops += [("band", (70, 45))]
+    elif kind == "rows_cols":
+        ops += [("mask_rows", r.random(n) < 0.8), ("mask_columns", r.random(m) < 0.7)]
+    else:
+        ops += [("causal", -5), ("mask_rows", r.random(n) < 0.9)]
+    e, oe = bind_both(X, Y, "linear", 1.0, ops)
+    assert e.backward_plan(consumer, 24).startswith("family=mfma_grad")
+    V = r.standard_normal((m, 24)).astype(np.float32) if consumer == "softmax_matmul" else None
+    G = r.standard_normal((n, 24 if V is not None else 1)).astype(np.float32)
+    check_backward(e, oe, consumer, G, V=V, want=("X", "Y", "V"), what="masked mfma bwd %s %s" % (consumer, kind))

@@ -230,6 +230,17 @@ def attention_backward(n: int = 16384, d: int = 64, c: int = 64, seed: int = 101
     return arrays, cases
 
 
+def attention_causal_backward(n: int = 16384, d: int = 64, c: int = 64, seed: int = 1014):
+    """Backward of causal softmax attention, float32 (the arrays of
+    `attention`, dO ~ N(0, 1)); kept pairs n (n + 1) / 2."""
+    arrays, cases = attention_backward(n=n, d=d, c=c, seed=seed)
+    c0 = cases[0]
+    c0.name = "attention_causal_backward"
+    c0.ops = c0.ops + [("causal", 0)]
+    c0.pairs = n * (n + 1) // 2
+    return arrays, cases
+
+
 def kernel_ridge(n: int = 65536, d: int = 16, seed: int = 1012):
     """Kernel ridge regression / GP mean, float32 (Task Map, Kernel ridge row:
     solve(K + a * eye_like(K), Y, method="cg")): x ~ N(0, I) [n, 16], rbf
@@ -269,6 +280,7 @@ WORKLOADS = {
     "attention_packed": (attention_packed, {}, {"n": 900, "min_len": 40, "max_len": 300}),
     "kernel_ridge": (kernel_ridge, {}, {"n": 900}),
     "attention_backward": (attention_backward, {}, {"n": 700}),
+    "attention_causal_backward": (attention_causal_backward, {}, {"n": 700}),
 }
 
 

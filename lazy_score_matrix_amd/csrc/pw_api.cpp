@@ -216,7 +216,9 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       p.vcfg.vtile = valu_vtile(C);
       p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
     } else if (consumer == PW_C_TOPK) {
-      p.vcfg.vtile = k == 1 ? 1 : (k <= 16 ? 16 : 64);
+      // The list is sized to k: its warm-up insertions (and their cost)
+      // scale with its length.
+      p.vcfg.vtile = k == 1 ? 1 : (k <= 8 ? 8 : (k <= 16 ? 16 : 64));
     } else {
       p.vcfg.vtile = 0;
     }

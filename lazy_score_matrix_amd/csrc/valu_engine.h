@@ -134,6 +134,13 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   for (int c = 0; c < ACCN; ++c) acc[c] = 0;
   T mass = 0;
   T m = neg_inf<T>(), l = 0;
+  // Online consumers in float with at most one row-only affine stage run in
+  // base 2 (m is then a base-2 maximum until the end of the sweep).
+  const bool fast2 = (CONS == C_LOGSUMEXP || CONS == C_SOFTMAX) && sizeof(T) == 4 &&
+                     (a.epi.n_stages == 0 ||
+                      (a.epi.n_stages == 1 && a.epi.st[0].kind == ST_AFFINE && !a.epi.st[0].col_vec));
+  const T r2 = (T)kLog2e * (a.epi.n_stages ? re.r[0] : (T)1);
+  const T p2 = (T)kLog2e * (a.epi.n_stages ? re.p[0] : (T)0);
   Key<T> list[KL];
 #pragma unroll
   for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
@@ -182,6 +189,48 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     if (!rv) continue;
 
     if constexpr (CONS == C_LOGSUMEXP || CONS == C_SOFTMAX) {
+      if (fast2) {
+        // float, at most one row-only affine stage: s2 = (r_i log2e) f +
+        // p_i log2e in one FMA, weights 2^(s2 - m2) with the hardware
+        // exponential, and a lazily moved reference m2 (it moves only when a
+        // group's maximum exceeds it by more than 8, so weights stay <= 256).
+        for (int g = 0; g < nb; g += G) {
+          T sv[G];
+          T gm = neg_inf<T>();
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            const int jj = g + u;
+            T s = neg_inf<T>();
+            if (jj < nb) {
+              s = fma(metric(jj), r2, p2);
+              if (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) s = neg_inf<T>();
+              if (check && !kept(jj)) s = neg_inf<T>();
+            }
+            sv[u] = s;
+            gm = max(gm, s);
+          }
+          if (gm > m + (T)8) {
+            const T alpha = __builtin_amdgcn_exp2f(m - gm);
+            l *= alpha;
+            if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+              for (int c = 0; c < ACCN; ++c) acc[c] *= alpha;
+            }
+            m = gm;
+          }
+          const T mu = m == neg_inf<T>() ? (T)0 : m;
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            const T p = __builtin_amdgcn_exp2f(sv[u] - mu);
+            l += p;
+            if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+              for (int c = 0; c < ACCN; ++c) acc[c] = fma(p, sV[g + u][c], acc[c]);
+            }
+          }
+        }
+        continue;
+      }
       for (int g = 0; g < nb; g += G) {
         T sv[G];
         T gm = neg_inf<T>();
@@ -275,6 +324,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     }
   }
   if (!rv) return;
+  if (fast2 && m != neg_inf<T>()) m *= (T)kLn2;  // back to natural units
   if (!rkeep) {  // a masked row: the empty-row result
 #pragma unroll
     for (int c = 0; c < ACCN; ++c) acc[c] = 0;
@@ -358,6 +408,7 @@ hipError_t valu_by_vt(int vt, const TileArgs &a, hipStream_t s) {
     if (vt == 64) return launch_valu_kernel<T, METRIC, CONS, DT, 64>(a, s);
   } else if constexpr (CONS == C_TOPK) {
     if (vt == 1) return launch_valu_kernel<T, METRIC, CONS, DT, 1>(a, s);
+    if (vt == 8) return launch_valu_kernel<T, METRIC, CONS, DT, 8>(a, s);
     if (vt == 16) return launch_valu_kernel<T, METRIC, CONS, DT, 16>(a, s);
     if (vt == 64) return launch_valu_kernel<T, METRIC, CONS, DT, 64>(a, s);
   } else {

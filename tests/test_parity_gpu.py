@@ -131,7 +131,7 @@ def test_exclude_self_aliased_identical_rows():
     assert np.isneginf(out).all()
 
 
-@pytest.mark.parametrize("k", [1, 2, 10, 16, 17, 40, 64])
+@pytest.mark.parametrize("k", [1, 2, 5, 8, 9, 10, 16, 17, 40, 64])
 @pytest.mark.parametrize("largest", [False, True])
 def test_topk_exact_ties(k, largest):
     """Integer grid with duplicated reference rows: every score is exact, so

@@ -85,6 +85,13 @@ def rbf_large(n: int = 65536, seed: int = 1011):
     return arrays, cases[:1]
 
 
+def rbf_small_large(n: int = 65536, seed: int = 1015):
+    """The three calls of ``rbf_small`` (rbf product with the row mass,
+    log-sum-exp of -D/2, top-8 of D) at n = m = 65536, float32: the small
+    configuration's consumers at a size where throughput is measured."""
+    return rbf_small(n=n, seed=seed)
+
+
 def attention(n: int = 16384, m: int | None = None, d: int = 64, c: int = 64, seed: int = 1002):
     """Softmax attention, float32: Q, K, V ~ N(0,1); scores linear(Q,K)/8."""
     m = n if m is None else m
@@ -269,6 +276,7 @@ def resolve(arg, arrays):
 WORKLOADS = {
     "rbf_small": (rbf_small, {}, {"n": 300, "m": 333}),
     "rbf_large": (rbf_large, {}, {"n": 2000}),
+    "rbf_small_large": (rbf_small_large, {}, {"n": 1500}),
     "attention": (attention, {}, {"n": 700, "m": 650}),
     "infonce": (infonce, {}, {"n": 900}),
     "knn": (knn, {}, {"n_query": 500, "n_ref": 4099}),

@@ -166,6 +166,19 @@ __device__ __forceinline__ void key_insert(Key<T> (&l)[L], Key<T> c) {
   }
 }
 
+// A value known to be equal on every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t wave_uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A compile-time flag passed as a value (to generic lambdas).
+template <bool B>
+struct Bool {
+  static constexpr bool value = B;
+};
+
 // ------------------------------------------------------------------ masks
 // Tile classes under the pair masks, for the rows r0..r1 of a row block and
 // the keys j0..j1 of a tile (both inclusive, non-empty).

@@ -5,7 +5,8 @@
 // and the staged column epilogue vectors). Every lane of a wave reads the
 // same LDS address for a column, so the reads are broadcasts. Each score is
 // evaluated in direct form (the sum of squared differences for the distance
-// metrics; the dot product scaled by 1/|x_i| and a staged 1/|y_j| for
+// metrics, so identical points are at distance exactly 0 however far from
+// the origin; the dot product scaled by 1/|x_i| and a staged 1/|y_j| for
 // cosine), run through the epilogue, and folded into the row's reduction:
 //   matmul        acc[c] += s * V[j, c]
 //   displacement  acc[d] += s * y_jd, mass += s; out = acc - x * mass
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   constexpr int VW = HAS_V ? VT : 1;
   constexpr int ACCN = HAS_V ? VT : (CONS == C_DISPLACEMENT ? DT : 1);
   constexpr int KL = (CONS == C_TOPK) ? VT : 1;
-  constexpr int G = 8;  // columns per online-softmax group
+  constexpr int G = 8;  // columns per online-softmax or top-k screening group
   // Three features are padded to four so a column is one aligned LDS read.
   constexpr int DTS = DT == 3 ? 4 : DT;
 
@@ -104,6 +105,10 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   const int64_t gi = (rv && mk.grow) ? mk.grow[i] : 0;
   int64_t jfirst, jlast;
   band_range(mk, rb, r0, r1, jb, je, BN, &jfirst, &jlast);
+  // The column range is the workgroup's: keep it (and so every column
+  // index) in scalar registers.
+  jfirst = wave_uniform(jfirst);
+  jlast = wave_uniform(jlast);
 
   T x[DT];
 #pragma unroll
@@ -141,11 +146,18 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
                       (a.epi.n_stages == 1 && a.epi.st[0].kind == ST_AFFINE && !a.epi.st[0].col_vec));
   const T r2 = (T)kLog2e * (a.epi.n_stages ? re.r[0] : (T)1);
   const T p2 = (T)kLog2e * (a.epi.n_stages ? re.p[0] : (T)0);
-  Key<T> list[KL];
+  T q2 = p2;  // p2 less the base-2 reference (0 until there is one)
+  // Top-k list in the signed orientation (negated for `largest`): values
+  // ascending, equal values in column order, empty slots at +inf with column
+  // ~0; thr is the last value. With k = 1 the best signed value and its
+  // column are kept directly (thr, best_j).
+  T lv[KL];
+  uint32_t lj[KL];
 #pragma unroll
-  for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
-  // Top-k threshold in the signed orientation (negated for `largest`); with
-  // k = 1 the best signed value and its column are kept directly.
+  for (int p = 0; p < KL; ++p) {
+    lv[p] = (T)__builtin_huge_val();
+    lj[p] = ~0u;
+  }
   T thr = __builtin_huge_val();
   uint32_t best_j = ~0u;
 
@@ -187,30 +199,102 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     }
     __syncthreads();
     if (!rv) continue;
-
-    if constexpr (CONS == C_LOGSUMEXP || CONS == C_SOFTMAX) {
-      if (fast2) {
-        // float, at most one row-only affine stage: s2 = (r_i log2e) f +
-        // p_i log2e in one FMA, weights 2^(s2 - m2) with the hardware
-        // exponential, and a lazily moved reference m2 (it moves only when a
-        // group's maximum exceeds it by more than 8, so weights stay <= 256).
-        for (int g = 0; g < nb; g += G) {
+    // A plain tile (full width, nothing masked, no diagonal to drop) runs at
+    // a constant trip count with no per-column conditions; the others take
+    // the same sweep with the conditions in.
+    const bool plain = nb == BN && !check &&
+                       !(CONS == C_LOGSUMEXP && a.exclude_self && j0 <= r1 && j0 + BN > r0);
+    auto sweep = [&](auto plain_tag) {
+      constexpr bool PLAIN = decltype(plain_tag)::value;
+      const int n = PLAIN ? BN : nb;
+      const bool chk = !PLAIN && check;
+      // k = 1: the tile slot of the best column met in this tile (-1: none);
+      // a constant slot number makes the select cheaper than a column index.
+      int bl = -1;
+      // One column at a time: unrolled deeply on plain tiles, where nothing
+      // branches between columns.
+      auto cols = [&](auto body) {
+        if constexpr (PLAIN && HAS_V) {
+#pragma unroll 4
+          for (int jj = 0; jj < BN; ++jj) body(jj);
+        } else if constexpr (PLAIN) {
+#pragma unroll 8
+          for (int jj = 0; jj < BN; ++jj) body(jj);
+        } else {
+          for (int jj = 0; jj < n; ++jj) body(jj);
+        }
+      };
+      if constexpr (CONS == C_LOGSUMEXP || CONS == C_SOFTMAX) {
+        // Pairs that carry no weight: the row's own column under
+        // exclude_self, and masked pairs of a checked tile.
+        auto dropped = [&](int jj) -> bool {
+          if constexpr (PLAIN) return false;
+          return (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) || (chk && !kept(jj));
+        };
+        if (fast2) {
+          // float, at most one row-only affine stage: scores are kept in
+          // base 2 relative to a reference m2, s2 - m2 = (r_i log2e) f +
+          // (p_i log2e - m2) in one FMA, and weighted 2^(s2 - m2) with the
+          // hardware exponential. The reference moves only when a group's
+          // maximum exceeds it by more than 8 (so weights stay <= 256); it
+          // counts as 0 until the first finite score.
+#pragma unroll 1
+          for (int g = 0; g < n; g += G) {
+            T sv[G];
+            T gm = neg_inf<T>();
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+              const int jj = g + u;
+              T s = neg_inf<T>();
+              if (PLAIN || jj < n) {
+                s = fma(metric(jj), r2, q2);
+                if (dropped(jj)) s = neg_inf<T>();
+              }
+              sv[u] = s;
+              gm = max(gm, s);
+            }
+            const bool first = m == neg_inf<T>();
+            if (gm > (first ? neg_inf<T>() : (T)8)) {
+              const T alpha = first ? (T)0 : __builtin_amdgcn_exp2f(-gm);
+              l *= alpha;
+              if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+                for (int c = 0; c < ACCN; ++c) acc[c] *= alpha;
+              }
+              m = (first ? (T)0 : m) + gm;
+              q2 = p2 - m;
+#pragma unroll
+              for (int u = 0; u < G; ++u) sv[u] -= gm;
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+              const T p = __builtin_amdgcn_exp2f(sv[u]);
+              l += p;
+              if constexpr (CONS == C_SOFTMAX) {
+#pragma unroll
+                for (int c = 0; c < ACCN; ++c) acc[c] = fma(p, sV[g + u][c], acc[c]);
+              }
+            }
+          }
+          return;
+        }
+#pragma unroll 1
+        for (int g = 0; g < n; g += G) {
           T sv[G];
           T gm = neg_inf<T>();
 #pragma unroll
           for (int u = 0; u < G; ++u) {
             const int jj = g + u;
             T s = neg_inf<T>();
-            if (jj < nb) {
-              s = fma(metric(jj), r2, p2);
-              if (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) s = neg_inf<T>();
-              if (check && !kept(jj)) s = neg_inf<T>();
+            if (PLAIN || jj < n) {
+              s = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
+              if (dropped(jj)) s = neg_inf<T>();
             }
             sv[u] = s;
             gm = max(gm, s);
           }
-          if (gm > m + (T)8) {
-            const T alpha = __builtin_amdgcn_exp2f(m - gm);
+          if (gm > m) {
+            const T alpha = dexp(m - gm);
             l *= alpha;
             if constexpr (CONS == C_SOFTMAX) {
 #pragma unroll
@@ -218,109 +302,131 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
             }
             m = gm;
           }
-          const T mu = m == neg_inf<T>() ? (T)0 : m;
+          if (m != neg_inf<T>()) {
 #pragma unroll
-          for (int u = 0; u < G; ++u) {
-            const T p = __builtin_amdgcn_exp2f(sv[u] - mu);
-            l += p;
-            if constexpr (CONS == C_SOFTMAX) {
+            for (int u = 0; u < G; ++u) {
+              const T p = dexp(sv[u] - m);
+              l += p;
+              if constexpr (CONS == C_SOFTMAX) {
 #pragma unroll
-              for (int c = 0; c < ACCN; ++c) acc[c] = fma(p, sV[g + u][c], acc[c]);
+                for (int c = 0; c < ACCN; ++c) acc[c] = fma(p, sV[g + u][c], acc[c]);
+              }
             }
           }
         }
-        continue;
-      }
-      for (int g = 0; g < nb; g += G) {
-        T sv[G];
-        T gm = neg_inf<T>();
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-          const int jj = g + u;
-          T s = neg_inf<T>();
-          if (jj < nb) {
-            s = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
-            if (CONS == C_LOGSUMEXP && a.exclude_self && j0 + jj == i) s = neg_inf<T>();
-            if (check && !kept(jj)) s = neg_inf<T>();
-          }
-          sv[u] = s;
-          gm = max(gm, s);
-        }
-        if (gm > m) {
-          const T alpha = dexp(m - gm);
-          l *= alpha;
-          if constexpr (CONS == C_SOFTMAX) {
-#pragma unroll
-            for (int c = 0; c < ACCN; ++c) acc[c] *= alpha;
-          }
-          m = gm;
-        }
-        if (m != neg_inf<T>()) {
-#pragma unroll
-          for (int u = 0; u < G; ++u) {
-            const T p = dexp(sv[u] - m);
-            l += p;
-            if constexpr (CONS == C_SOFTMAX) {
-#pragma unroll
-              for (int c = 0; c < ACCN; ++c) acc[c] = fma(p, sV[g + u][c], acc[c]);
-            }
-          }
-        }
-      }
-    } else {
-      auto fold = [&](int jj, T s) {
-        if constexpr (CONS == C_MATMUL) {
-#pragma unroll
-          for (int c = 0; c < ACCN; ++c) acc[c] = fma(s, sV[jj][c], acc[c]);
-        } else if constexpr (CONS == C_DISPLACEMENT) {
-#pragma unroll
-          for (int d = 0; d < ACCN; ++d) acc[d] = fma(s, sY[jj][d], acc[d]);
-          mass += s;
-        }
-      };
-      // Top-k: columns reach a thread in increasing order, so a candidate
-      // enters only when its signed value is strictly below the threshold.
-      auto fold_topk = [&](int jj, T sv) {
-        if constexpr (KL == 1) {
-          const bool lt = sv < thr;
-          thr = lt ? sv : thr;
-          best_j = lt ? (uint32_t)(j0 + jj) : best_j;
-        } else {
-          if (sv < thr) {
-            key_insert<T, KL>(list, Key<T>::make(a.largest ? -sv : sv, (uint32_t)(j0 + jj), a.largest));
-            thr = key_threshold(list[KL - 1]);
-          }
-        }
-      };
-      // The stage loop runs only when the expression has score arithmetic;
-      // a bare metric takes a loop without it (a uniform branch).
-      // Checked tiles drop masked pairs: no weight in a sum, +inf (never a
-      // candidate) in the signed top-k orientation.
-      if (check) {
-        const T sg = a.largest ? (T)-1 : (T)1;
-        for (int jj = 0; jj < nb; ++jj) {
-          const T sc = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
-          const bool kp = kept(jj);
-          if constexpr (CONS == C_TOPK) fold_topk(jj, kp ? sg * sc : (T)__builtin_huge_val());
-          else fold(jj, kp ? sc : (T)0);
-        }
-      } else if constexpr (CONS == C_TOPK) {
-        if (a.epi.n_stages == 0) {
-          if (a.largest) {
-            for (int jj = 0; jj < nb; ++jj) fold_topk(jj, -metric(jj));
-          } else {
-            for (int jj = 0; jj < nb; ++jj) fold_topk(jj, metric(jj));
-          }
-        } else {
-          const T sg = a.largest ? (T)-1 : (T)1;
-          for (int jj = 0; jj < nb; ++jj) fold_topk(jj, sg * apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj));
-        }
-      } else if (a.epi.n_stages == 0) {
-        for (int jj = 0; jj < nb; ++jj) fold(jj, metric(jj));
       } else {
-        for (int jj = 0; jj < nb; ++jj)
-          fold(jj, apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj));
+        auto fold = [&](int jj, T s) {
+          if constexpr (CONS == C_MATMUL) {
+#pragma unroll
+            for (int c = 0; c < ACCN; ++c) acc[c] = fma(s, sV[jj][c], acc[c]);
+          } else if constexpr (CONS == C_DISPLACEMENT) {
+#pragma unroll
+            for (int d = 0; d < ACCN; ++d) acc[d] = fma(s, sY[jj][d], acc[d]);
+            mass += s;
+          }
+        };
+        // Top-k: columns reach a thread in increasing order, so a candidate
+        // enters only when its signed value is strictly below the threshold.
+        auto fold_topk = [&](int jj, T sv) {
+          if constexpr (KL == 1) {
+            const bool lt = sv < thr;
+            thr = lt ? sv : thr;
+            bl = lt ? jj : bl;
+          } else {
+            if (sv < thr) {
+              // The new column comes after every listed one, so it goes
+              // behind the values it equals: slot p takes slot p - 1 where
+              // the new value lands before that, the new value where it
+              // lands between the two, and otherwise stays.
+              const uint32_t jc = (uint32_t)(j0 + jj);
+              bool below = true;  // sv < lv[KL - 1], as the threshold said
+#pragma unroll
+              for (int p = KL - 1; p > 0; --p) {
+                const bool below_prev = sv < lv[p - 1];
+                lv[p] = below_prev ? lv[p - 1] : (below ? sv : lv[p]);
+                lj[p] = below_prev ? lj[p - 1] : (below ? jc : lj[p]);
+                below = below_prev;
+              }
+              lv[0] = below ? sv : lv[0];
+              lj[0] = below ? jc : lj[0];
+              thr = lv[KL - 1];
+            }
+          }
+        };
+        // With k > 1 and short rows a group of G columns is screened by its
+        // smallest signed value first: most groups hold no candidate once the
+        // list is full. Long rows amortise the per-column test already.
+        auto topk_sweep = [&](auto score) {
+          if constexpr (KL == 1 && PLAIN) {
+            // Groups of G columns with a constant slot inside the group, so
+            // that the select of the best slot takes an inline constant.
+#pragma unroll 1
+            for (int g = 0; g < BN; g += G) {
+              int bu = -1;
+#pragma unroll
+              for (int u = 0; u < G; ++u) {
+                const T sv = score(g + u);
+                const bool lt = sv < thr;
+                thr = lt ? sv : thr;
+                bu = lt ? u : bu;
+              }
+              bl = bu >= 0 ? g + bu : bl;
+            }
+          } else if constexpr (KL == 1 || DT > 4) {
+            cols([&](int jj) { fold_topk(jj, score(jj)); });
+          } else {
+#pragma unroll 1
+            for (int g = 0; g < n; g += G) {
+              T sv[G];
+              T lo = (T)__builtin_huge_val();
+#pragma unroll
+              for (int u = 0; u < G; ++u) {
+                sv[u] = (PLAIN || g + u < n) ? score(g + u) : (T)__builtin_huge_val();
+                lo = min(lo, sv[u]);
+              }
+              if (lo < thr) {
+#pragma unroll
+                for (int u = 0; u < G; ++u) fold_topk(g + u, sv[u]);
+              }
+            }
+          }
+        };
+        // Checked tiles drop masked pairs: no weight in a sum, +inf (never a
+        // candidate) in the signed top-k orientation. The stage loop runs
+        // only when the expression has score arithmetic (a uniform branch).
+        if (chk) {
+          const T sg = a.largest ? (T)-1 : (T)1;
+          for (int jj = 0; jj < n; ++jj) {
+            const T sc = apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj);
+            const bool kp = kept(jj);
+            if constexpr (CONS == C_TOPK) fold_topk(jj, kp ? sg * sc : (T)__builtin_huge_val());
+            else fold(jj, kp ? sc : (T)0);
+          }
+        } else if constexpr (CONS == C_TOPK) {
+          if (a.epi.n_stages == 0) {
+            if (a.largest) topk_sweep([&](int jj) { return -metric(jj); });
+            else topk_sweep([&](int jj) { return metric(jj); });
+          } else {
+            const T sg = a.largest ? (T)-1 : (T)1;
+            topk_sweep([&](int jj) { return sg * apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj); });
+          }
+        } else if (a.epi.n_stages == 0) {
+          cols([&](int jj) { fold(jj, metric(jj)); });
+        } else {
+          cols([&](int jj) { fold(jj, apply_epi<T, BN>(a.epi, re, metric(jj), sQ, sO, jj)); });
+        }
+        if constexpr (CONS == C_TOPK && KL == 1) {
+          if (bl >= 0) best_j = (uint32_t)(j0 + bl);
+        }
       }
+    };
+    // Only narrow rows and value widths take the plain variant: it lets the
+    // compiler hoist a whole group's LDS reads, which wide ones cannot hold.
+    if constexpr (DT <= 4 && VW <= 4) {
+      if (plain) sweep(Bool<true>{});
+      else sweep(Bool<false>{});
+    } else {
+      sweep(Bool<false>{});
     }
   }
   if (!rv) return;
@@ -332,7 +438,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     m = neg_inf<T>();
     l = 0;
 #pragma unroll
-    for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
+    for (int p = 0; p < KL; ++p) lj[p] = ~0u;
     best_j = ~0u;
   }
 
@@ -374,8 +480,13 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     }
   } else if constexpr (CONS == C_TOPK) {
     if constexpr (KL == 1) {
-      if (best_j != ~0u) list[0] = Key<T>::make(a.largest ? -thr : thr, best_j, a.largest);
+      lv[0] = thr;
+      lj[0] = best_j;
     }
+    Key<T> list[KL];
+#pragma unroll
+    for (int p = 0; p < KL; ++p)
+      list[p] = lj[p] == ~0u ? Key<T>::sentinel() : Key<T>::make(a.largest ? -lv[p] : lv[p], lj[p], a.largest);
     if (fin) {
       T *v = static_cast<T *>(a.out) + i * a.k;
       int64_t *ix = a.idx + i * a.k;

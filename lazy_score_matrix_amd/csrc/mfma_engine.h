@@ -254,8 +254,10 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   // with a band) the pair r, n_rb - 1 - r, so the light rows at one end of
   // a causal band and the heavy rows at the other share a workgroup.
   const int rb_slots = (MASKED && a.rb_pairs) ? a.rb_pairs : a.n_rb;
-  const int rb_first = blockIdx.x % rb_slots;
-  const int sp = blockIdx.x / rb_slots;
+  // Block coordinates are wave-uniform: keeping them (and the column range
+  // below) in scalar registers keeps the tile loop's control scalar.
+  const int rb_first = __builtin_amdgcn_readfirstlane(blockIdx.x % rb_slots);
+  const int sp = __builtin_amdgcn_readfirstlane(blockIdx.x / rb_slots);
   const bool paired = MASKED && a.rb_pairs;
   const int npass = (paired && a.n_rb - 1 - rb_first != rb_first) ? 2 : 1;
   // Paired launches deal the pair's tiles (those of the first row block,
@@ -278,7 +280,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   const int rb = pass ? a.n_rb - 1 - rb_first : rb_first;
   const int64_t row0 = (int64_t)rb * BM;
   const int64_t jb = paired ? 0 : (int64_t)sp * a.split_cols;
-  const int64_t je = paired ? a.M : min(a.M, jb + a.split_cols);
+  const int64_t je = wave_uniform(paired ? a.M : min(a.M, jb + a.split_cols));
   const T *__restrict__ Xp = static_cast<const T *>(a.X);
   const T *__restrict__ Yp = static_cast<const T *>(a.Y);
   const MaskArgs &mk = a.mask;
@@ -362,11 +364,16 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 
   // ----------------------------------------------------------- sub-blocks
   // S^T for the TM keys at offset kb of the staged tile, all QB query blocks.
-  auto qk = [&](int kb, acc_t (&s)[QB]) {
+  // A plain search (PL) leaves |x_i|^2 out of the accumulator: it is the
+  // same for every key of the row, so it is added once to the sub-block's
+  // minimum and to each candidate instead of to every score.
+  auto qk = [&](int kb, acc_t (&s)[QB], auto pl) __attribute__((always_inline)) {
+    constexpr bool PL = decltype(pl)::value;
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int r = 0; r < NREG; ++r) s[b][r] = DIST ? nx[b] + sN[kb + F::key_of(r, g)] : (T)0;
+      for (int r = 0; r < NREG; ++r)
+        s[b][r] = DIST ? (PL ? sN[kb + F::key_of(r, g)] : nx[b] + sN[kb + F::key_of(r, g)]) : (T)0;
 #pragma unroll
     for (int st = 0; st < DG; ++st) {
       const T av = sK[kb + q][g * DG + st];
@@ -397,7 +404,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   // Keep bits of every sub-block of a checked tile, formed once when the
   // tile starts (few registers are live there) and read back per sub-block.
   __shared__ uint32_t sKm[MASKED ? SB : 1][QB][MASKED ? NT : 1];
-  auto consume = [&](int kb, int nb, int64_t j0, bool diag, bool check_, acc_t (&s)[QB]) {
+  auto consume = [&](int kb, int nb, int64_t j0, bool diag, bool check_, acc_t (&s)[QB], auto pl) __attribute__((always_inline)) {
+    constexpr bool PL = decltype(pl)::value;
     const bool check = MASKED && check_;
     const bool tail = kb + TM > nb;
     uint32_t km[QB];
@@ -407,12 +415,13 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     }
     if constexpr (CONS == C_TOPK) {
       // Filter a whole sub-block with one wave vote before any insertion.
-      // Plain searches (no epilogue, smallest first, dot product or squared
-      // distance) filter on the raw accumulator: for distances the clamp at
-      // 0 is deferred to the candidates, as max(x, 0) < thr implies x < thr.
-      const bool plain = (METRIC == M_LINEAR || METRIC == M_SQEUCLIDEAN) && !has_epi && !a.largest;
+      // A plain search (no epilogue, smallest first, dot product or squared
+      // distance) filters on the raw accumulator: its minimum plus |x_i|^2
+      // (fl(n + u) is monotone in u, so this is the minimum of the sums) and
+      // the clamp at 0 are applied to candidates only, as max(d, 0) < thr
+      // implies d < thr.
       bool any = false;
-      if (plain) {
+      if constexpr (PL) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
           if (check) {
@@ -423,6 +432,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
           T mn = s[b][0];
 #pragma unroll
           for (int r = 1; r < NREG; ++r) mn = min(mn, s[b][r]);
+          if constexpr (DIST) mn = nx[b] + mn;
           any |= mn < thr[b];
         }
       } else {
@@ -450,10 +460,10 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
           for (int r = 0; r < NREG; ++r) {
             const int key = kb + F::key_of(r, g);
             T x = s[b][r];
-            if (DIST && plain) x = max(x, (T)0);
-            const T sv = a.largest ? -x : x;
+            if (DIST && PL) x = max(nx[b] + x, (T)0);
+            const T sv = (!PL && a.largest) ? -x : x;
             if (key < nb && sv < thr[b]) {
-              key_insert<T, KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), a.largest));
+              key_insert<T, KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), PL ? 0 : a.largest));
               thr[b] = key_threshold(list[b][KLQ - 1]);
             }
           }
@@ -625,6 +635,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       band_range(mk, rb, row0, r1, jb, je, BN, &jfirst, &jlast);
     }
   }
+  jfirst = wave_uniform(jfirst);
+  jlast = wave_uniform(jlast);
   auto tile_cls = [&](int64_t t0) -> int {
     if constexpr (MASKED) return tile_class(mk, row0, r1, t0, min(t0 + BN, je) - 1, rb, t0 / BN);
     return TILE_FULL;
@@ -635,6 +647,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     }
     return t0;
   };
+  constexpr bool PLAIN_OK = CONS == C_TOPK && (METRIC == M_LINEAR || METRIC == M_SQEUCLIDEAN);
+  const bool plain = PLAIN_OK && !has_epi && !a.largest;
   int buf = 0;
   int64_t j0 = next_tile(jfirst);
   if (j0 < jlast) {
@@ -643,46 +657,56 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   }
   __syncthreads();
 
-  while (j0 < jlast) {
-    const int nb = (int)min((int64_t)BN, je - j0);
-    const int64_t jn = next_tile(j0 + BN);
-    const bool next = jn < jlast;
-    if (next) prefetch(jn);
-    sK = sKb[buf];
-    sN = sNb[buf];
-    sV = sVb[buf];
-    sC = sCb[buf];
-    sG = sGb[buf];
-    const bool diag = CONS == C_LOGSUMEXP && a.exclude_self && j0 < row0 + BM && j0 + BN > row0;
-    const bool check = tile_cls(j0) == TILE_CHECK;
+  // Plain searches (see consume) get a tile loop of their own, so their
+  // list registers flow through a single loop.
+  auto tile_loop = [&](auto pl) __attribute__((always_inline)) {
+    while (j0 < jlast) {
+      const int nb = (int)min((int64_t)BN, je - j0);
+      const int64_t jn = next_tile(j0 + BN);
+      const bool next = jn < jlast;
+      if (next) prefetch(jn);
+      sK = sKb[buf];
+      sN = sNb[buf];
+      sV = sVb[buf];
+      sC = sCb[buf];
+      sG = sGb[buf];
+      const bool diag = CONS == C_LOGSUMEXP && a.exclude_self && j0 < row0 + BM && j0 + BN > row0;
+      const bool check = tile_cls(j0) == TILE_CHECK;
 
-    if (MASKED && check) {
+      if (MASKED && check) {
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          uint32_t km[QB];
+          keep_bits(sb * TM, j0, km);
+#pragma unroll
+          for (int b = 0; b < QB; ++b) sKm[MASKED ? sb : 0][b][MASKED ? tid : 0] = km[b];
+        }
+      }
+      acc_t s0[QB], s1[QB];
+      qk(0, s0, pl);
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
-        uint32_t km[QB];
-        keep_bits(sb * TM, j0, km);
-#pragma unroll
-        for (int b = 0; b < QB; ++b) sKm[MASKED ? sb : 0][b][MASKED ? tid : 0] = km[b];
+        if (sb * TM >= nb) break;
+        const bool more = sb + 1 < SB && (sb + 1) * TM < nb;
+        if (sb & 1) {
+          if (more) qk((sb + 1) * TM, s0, pl);
+          consume(sb * TM, nb, j0, diag, check, s1, pl);
+        } else {
+          if (more) qk((sb + 1) * TM, s1, pl);
+          consume(sb * TM, nb, j0, diag, check, s0, pl);
+        }
       }
+      if (next) stage(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      j0 = jn;
     }
-    acc_t s0[QB], s1[QB];
-    qk(0, s0);
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      if (sb * TM >= nb) break;
-      const bool more = sb + 1 < SB && (sb + 1) * TM < nb;
-      if (sb & 1) {
-        if (more) qk((sb + 1) * TM, s0);
-        consume(sb * TM, nb, j0, diag, check, s1);
-      } else {
-        if (more) qk((sb + 1) * TM, s1);
-        consume(sb * TM, nb, j0, diag, check, s0);
-      }
-    }
-    if (next) stage(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    j0 = jn;
+  };
+  if constexpr (PLAIN_OK) {
+    if (plain) tile_loop(Bool<true>());
+    else tile_loop(Bool<false>());
+  } else {
+    tile_loop(Bool<false>());
   }
 
   // Rows dropped by the row mask take the empty-row result.

@@ -166,6 +166,36 @@ __device__ __forceinline__ void key_insert(Key<T> (&l)[L], Key<T> c) {
   }
 }
 
+// Insert `c` into the ascending list l[0..L) when every key already in it
+// has a smaller index (keys reach the list in increasing column order), so
+// that c belongs right after the last key of smaller or equal value: only
+// the values are compared, and each slot takes its left neighbour, c, or
+// itself. The caller has checked that c enters (its value is below the last
+// slot's). Float keys only (value in the high word).
+template <int L>
+__device__ __forceinline__ void key_insert_after(Key<float> (&l)[L], Key<float> c) {
+  const uint32_t cv = (uint32_t)(c.k >> 32);
+  bool lt[L];
+#pragma unroll
+  for (int p = 0; p < L; ++p) lt[p] = cv < (uint32_t)(l[p].k >> 32);
+#pragma unroll
+  for (int p = L - 1; p > 0; --p) l[p].k = lt[p - 1] ? l[p - 1].k : (lt[p] ? c.k : l[p].k);
+  l[0].k = lt[0] ? c.k : l[0].k;
+}
+template <int L>
+__device__ __forceinline__ void key_insert_after(Key<double> (&l)[L], Key<double> c) {
+  if (c < l[L - 1]) {
+#pragma unroll
+    for (int p = 0; p < L; ++p) {
+      bool lt = c < l[p];
+      Key<double> lo = lt ? c : l[p];
+      Key<double> hi = lt ? l[p] : c;
+      l[p] = lo;
+      c = hi;
+    }
+  }
+}
+
 // A value known to be equal on every lane, moved to scalar registers.
 __device__ __forceinline__ int64_t wave_uniform(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);

@@ -337,6 +337,13 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     }
   }
   const T ngl2 = (T)(-a.gamma * kLog2e);
+  // rbf: the accumulator holds u = |y_j|^2 - 2 x_i.y_j and the exponent is
+  // u * c + |x_i|^2 * c, one FMA (c = -gamma log2(e), times 256 for the
+  // double table, whose argument is 256 x).
+  const T rbf_c = TABLE_EXP ? ngl2 * (T)256 : ngl2;
+  T rbf_t[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) rbf_t[b] = rbf_c * nx[b];
 
   acc_t o[QB][NCB];
 #pragma unroll
@@ -373,7 +380,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int r = 0; r < NREG; ++r)
-        s[b][r] = DIST ? (PL ? sN[kb + F::key_of(r, g)] : nx[b] + sN[kb + F::key_of(r, g)]) : (T)0;
+        s[b][r] = DIST ? ((PL || METRIC == M_RBF) ? sN[kb + F::key_of(r, g)] : nx[b] + sN[kb + F::key_of(r, g)])
+                       : (T)0;
 #pragma unroll
     for (int st = 0; st < DG; ++st) {
       const T av = sK[kb + q][g * DG + st];
@@ -404,6 +412,39 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   // Keep bits of every sub-block of a checked tile, formed once when the
   // tile starts (few registers are live there) and read back per sub-block.
   __shared__ uint32_t sKm[MASKED ? SB : 1][QB][MASKED ? NT : 1];
+  // rbf kernel values of a sub-block. The exponent of a pair with x = y
+  // can round slightly above 0, giving a value above 1 by a rounding error
+  // of the distance; it is not clamped. For double the table lookups of all
+  // registers are issued together, then used.
+  auto rbf_values = [&](const acc_t (&s)[QB], T (&v)[QB][NREG]) __attribute__((always_inline)) {
+    if constexpr (TABLE_EXP) {
+      double p[QB][NREG];
+      int n[QB][NREG];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          const double t = fmax(fma(s[b][r], rbf_c, rbf_t[b]), -1073741824.0);
+          const double nd = rint(t);
+          const double f = t - nd;
+          n[b][r] = (int)nd;
+          p[b][r] = f * fma(f, fma(f, fma(f, ec[3], ec[2]), ec[1]), ec[0]);
+        }
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) v[b][r] = sE[n[b][r] & 255];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) v[b][r] = ldexp(fma(v[b][r], p[b][r], v[b][r]), n[b][r] >> 8);
+    } else {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) v[b][r] = F::exp2(fma(s[b][r], rbf_c, rbf_t[b]));
+    }
+  };
   auto consume = [&](int kb, int nb, int64_t j0, bool diag, bool check_, acc_t (&s)[QB], auto pl) __attribute__((always_inline)) {
     constexpr bool PL = decltype(pl)::value;
     const bool check = MASKED && check_;
@@ -436,14 +477,16 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
           any |= mn < thr[b];
         }
       } else {
+        T rv[QB][NREG];
+        if constexpr (METRIC == M_RBF) rbf_values(s, rv);
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
           T mn = __builtin_huge_valf();
 #pragma unroll
           for (int r = 0; r < NREG; ++r) {
             T x = s[b][r];
-            if constexpr (DIST) x = max(x, (T)0);
-            if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
+            if constexpr (METRIC == M_RBF) x = rv[b][r];
+            else if constexpr (DIST) x = max(x, (T)0);
             if constexpr (COS) x = fma(-x * sN[kb + F::key_of(r, g)], nx[b], (T)1);
             x = fma(x, er[b], ep[b]);
             if (check && !((km[b] >> r) & 1u)) x = a.largest ? -__builtin_huge_valf() : __builtin_huge_valf();
@@ -463,7 +506,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
             if (DIST && PL) x = max(nx[b] + x, (T)0);
             const T sv = (!PL && a.largest) ? -x : x;
             if (key < nb && sv < thr[b]) {
-              key_insert<T, KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), PL ? 0 : a.largest));
+              key_insert_after<KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), PL ? 0 : a.largest));
               thr[b] = key_threshold(list[b][KLQ - 1]);
             }
           }
@@ -473,13 +516,14 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 
     // Finished score per register (base 2 for the online consumers).
     T v[QB][NREG];
+    if constexpr (METRIC == M_RBF) rbf_values(s, v);
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
 #pragma unroll
       for (int r = 0; r < NREG; ++r) {
         T x = s[b][r];
-        if constexpr (DIST) x = max(x, (T)0);
-        if constexpr (METRIC == M_RBF) x = ex2(x * ngl2);
+        if constexpr (METRIC == M_RBF) x = v[b][r];
+        else if constexpr (DIST) x = max(x, (T)0);
         if constexpr (COS) x = fma(-x * sN[kb + F::key_of(r, g)], nx[b], (T)1);
         if constexpr (ONLINE && METRIC != M_LINEAR) x = x * er[b];
         v[b][r] = x;

@@ -256,8 +256,14 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   const int rb_slots = (MASKED && a.rb_pairs) ? a.rb_pairs : a.n_rb;
   // Block coordinates are wave-uniform: keeping them (and the column range
   // below) in scalar registers keeps the tile loop's control scalar.
-  const int rb_first = __builtin_amdgcn_readfirstlane(blockIdx.x % rb_slots);
-  const int sp = __builtin_amdgcn_readfirstlane(blockIdx.x / rb_slots);
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+  // Renumbering them XCD-major gives each XCD a contiguous run of blocks,
+  // so the row blocks sharing a column split (and its key tiles) share an
+  // L2.
+  const int nblk = gridDim.x;
+  const int bid = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int rb_first = __builtin_amdgcn_readfirstlane(bid % rb_slots);
+  const int sp = __builtin_amdgcn_readfirstlane(bid / rb_slots);
   const bool paired = MASKED && a.rb_pairs;
   const int npass = (paired && a.n_rb - 1 - rb_first != rb_first) ? 2 : 1;
   // Paired launches deal the pair's tiles (those of the first row block,

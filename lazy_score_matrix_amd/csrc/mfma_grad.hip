@@ -63,7 +63,12 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
   // n_rb - 1 - r and an equal run of their tiles, as the forward does.
   const bool paired = MASKED && a.rb_pairs;
   const int slots = paired ? a.rb_pairs : a.n_rb;
-  const int rb_first = blockIdx.x % slots, sp = blockIdx.x / slots;
+  // XCD-major numbering (workgroups are dealt round-robin to the 8 XCDs) and
+  // block coordinates in scalar registers, as in the forward engine.
+  const int nblk = gridDim.x;
+  const int bid = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int rb_first = __builtin_amdgcn_readfirstlane(bid % slots);
+  const int sp = __builtin_amdgcn_readfirstlane(bid / slots);
   const int npass = MASKED ? ((paired && a.n_rb - 1 - rb_first != rb_first) ? 2 : 1) : 1;
   int64_t pf[2] = {0, 0}, pe[2] = {0, 0}, pt[2] = {0, 0}, v0 = 0, v1 = 0;
   if (paired) {
@@ -148,37 +153,63 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
 #pragma unroll
     for (int r = 0; r < NREG; ++r) ob[c][r] = 0;
 
+  qb = wave_uniform(qb);
+  qe = wave_uniform(qe);
+  // Row side: streamed tiles come through registers, the global reads of the
+  // next tile (16-byte vectors from a uniform base when the tile is full and
+  // aligned) in flight while the current tile is computed from LDS. The
+  // column side holds twice the accumulators and has no registers to spare
+  // for that: it stages each tile element by element.
+  constexpr bool PF = SIDE == 0;
+  TileLoader<float, BN, DP, kGThreads> ldA;
+  TileLoader<float, BN, CPS, kGThreads> ldB;
+  if constexpr (PF) {
+    ldA.init(a.ldy, vec_ok(a.Y, a.ldy, 4), tid);
+    if constexpr (SMX) ldB.init(a.ldv, vec_ok(a.V, a.ldv, 4), tid);
+  }
+  auto fetch = [&](int64_t t0) {
+    if constexpr (PF) {
+      const int nbt = (int)min((int64_t)BN, qe - t0);
+      ldA.load(a.Y, a.ldy, t0, nbt, a.D, tid);
+      if constexpr (SMX) ldB.load(a.V, a.ldv, t0, nbt, a.C, tid);
+    }
+  };
+  if (qb < qe) fetch(qb);
   for (int64_t q0 = qb; q0 < qe; q0 += BN) {
     const int nb = (int)min((int64_t)BN, qe - q0);
+    const bool next = q0 + BN < qe;
     // Tile class under the masks (uniform over the workgroup): skipped
-    // tiles are not even staged; boundary tiles check every pair.
+    // tiles are not staged; boundary tiles check every pair.
     bool check = false;
     if (MASKED) {
       const int64_t s1 = q0 + nb - 1;
       const int cls = SIDE == 0 ? tile_class(mk, own0, own1, q0, s1, 0, 0) : tile_class(mk, q0, s1, own0, own1, 0, 0);
-      if (cls == TILE_SKIP) continue;
+      if (cls == TILE_SKIP) {
+        if (next) fetch(q0 + BN);
+        continue;
+      }
       check = cls != TILE_FULL || mk.row || mk.col;
     }
-    __syncthreads();
-    for (int e = tid; e < BN * DP; e += kGThreads) {
-      const int jj = e / DP, d = e % DP;
-      float v = 0;
-      if (jj < nb && d < a.D) {
-        const int64_t t = q0 + jj;
-        if (SIDE == 0) v = a.Y[t * a.ldy + d];
-        else v = a.X[t * a.ldx + d] * (a.row_vec ? a.r_vec[t] : a.r_s);
-      }
-      sA[jj][d] = v;
-    }
-    if constexpr (SMX) {
-      for (int e = tid; e < BN * CP; e += kGThreads) {
-        const int jj = e / CP, c = e % CP;
+    __syncthreads();  // every wave is done with the previous tile
+    if constexpr (PF) {
+      ldA.store(sA, tid);
+      if constexpr (SMX) ldB.store(sB, tid);
+    } else {
+      for (int e = tid; e < BN * DP; e += kGThreads) {
+        const int jj = e / DP, d = e % DP;
         float v = 0;
-        if (jj < nb && c < a.C) v = SIDE == 0 ? a.V[(q0 + jj) * a.ldv + c] : a.G[(q0 + jj) * a.ldg + c];
-        sB[jj][c] = v;
+        if (jj < nb && d < a.D) {
+          const int64_t t = q0 + jj;
+          v = a.X[t * a.ldx + d] * (a.row_vec ? a.r_vec[t] : a.r_s);
+        }
+        sA[jj][d] = v;
       }
-    }
-    if (SIDE == 1) {
+      if constexpr (SMX) {
+        for (int e = tid; e < BN * CP; e += kGThreads) {
+          const int jj = e / CP, c = e % CP;
+          sB[jj][c] = (jj < nb && c < a.C) ? a.G[(q0 + jj) * a.ldg + c] : 0.f;
+        }
+      }
       for (int jj = tid; jj < BN; jj += kGThreads) {
         const bool in = jj < nb;
         const int64_t t = q0 + jj;
@@ -193,6 +224,7 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
         sK[MASKED ? jj : 0] = jj < nb && (SIDE == 0 ? (!mk.col || mk.col[t]) : (!mk.row || mk.row[t]));
       }
     }
+    if (next) fetch(q0 + BN);
     __syncthreads();
 
 #pragma unroll

@@ -195,19 +195,43 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
       ldA.store(sA, tid);
       if constexpr (SMX) ldB.store(sB, tid);
     } else {
-      for (int e = tid; e < BN * DP; e += kGThreads) {
-        const int jj = e / DP, d = e % DP;
-        float v = 0;
-        if (jj < nb && d < a.D) {
+      // Four consecutive features per thread and step: one 16-byte read
+      // when the rows are aligned and unpadded, else element by element.
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      const bool xv = vec_ok(a.X, a.ldx, 4) && a.D == DP;
+#pragma unroll
+      for (int e = tid; e < BN * DP / 4; e += kGThreads) {
+        const int jj = e / (DP / 4), d = (e % (DP / 4)) * 4;
+        f4 v = {0.f, 0.f, 0.f, 0.f};
+        if (jj < nb) {
           const int64_t t = q0 + jj;
-          v = a.X[t * a.ldx + d] * (a.row_vec ? a.r_vec[t] : a.r_s);
+          const float *src = a.X + t * a.ldx + d;
+          if (xv) {
+            v = *reinterpret_cast<const f4 *>(src);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = d + u < a.D ? src[u] : 0.f;
+          }
+          v *= a.row_vec ? a.r_vec[t] : a.r_s;
         }
-        sA[jj][d] = v;
+        *reinterpret_cast<f4 *>(&sA[jj][d]) = v;
       }
       if constexpr (SMX) {
-        for (int e = tid; e < BN * CP; e += kGThreads) {
-          const int jj = e / CP, c = e % CP;
-          sB[jj][c] = (jj < nb && c < a.C) ? a.G[(q0 + jj) * a.ldg + c] : 0.f;
+        const bool gv = vec_ok(a.G, a.ldg, 4) && a.C == CP;
+#pragma unroll
+        for (int e = tid; e < BN * CP / 4; e += kGThreads) {
+          const int jj = e / (CP / 4), c = (e % (CP / 4)) * 4;
+          f4 v = {0.f, 0.f, 0.f, 0.f};
+          if (jj < nb) {
+            const float *src = a.G + (q0 + jj) * a.ldg + c;
+            if (gv) {
+              v = *reinterpret_cast<const f4 *>(src);
+            } else {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] = c + u < a.C ? src[u] : 0.f;
+            }
+          }
+          *reinterpret_cast<f4 *>(&sB[jj][c]) = v;
         }
       }
       for (int jj = tid; jj < BN; jj += kGThreads) {

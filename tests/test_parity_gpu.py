@@ -323,6 +323,23 @@ def test_mfma_topk_exact_ties(dtype, k):
     check_consumer(e, oe, "topk", k=k, exact=True, what="mfma exact k=%d" % k)
     e, oe = bind_both(X, Y, "linear")
     check_consumer(e, oe, "topk", k=k, largest=True, exact=True, what="mfma exact linear k=%d" % k)
+    # Smallest dot products: the plain search on the raw accumulator.
+    check_consumer(e, oe, "topk", k=k, exact=True, what="mfma exact smallest linear k=%d" % k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("k", [1, 10])
+def test_mfma_topk_far_from_origin(dtype, k):
+    """Clustered points far from the origin: |x|^2 dwarfs the distances, so
+    the plain search's deferred |x_i|^2 and the clamp at 0 are exercised
+    (near-equal values fall under the tolerance rule)."""
+    r = np.random.default_rng(1300 + k)
+    X = (50.0 + r.standard_normal((300, 32))).astype(dtype)
+    Y = (50.0 + r.standard_normal((2000, 32))).astype(dtype)
+    Y[1000:1100] = X[:100]  # exact copies: distance 0 for rows 0..99
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    _assert_family(e, "topk", "mfma", k=k)
+    check_consumer(e, oe, "topk", k=k, what="mfma far topk k=%d" % k)
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])

@@ -24,8 +24,10 @@
 namespace pw {
 
 // neg_gamma = -gamma for double (device exp); -gamma * log2(e) for float
-// (the hardware base-2 exponential).
-template <int METRIC, class T, int DT>
+// (the hardware base-2 exponential). PRE: float rbf with both points
+// pre-scaled by sqrt(gamma log2(e)), so the squared distance is the
+// exponent itself (identical points still give exactly 1).
+template <int METRIC, class T, int DT, bool PRE = false>
 __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gamma) {
   if constexpr (METRIC == M_LINEAR || METRIC == M_COSINE) {
     if constexpr (DT <= 4) {
@@ -66,6 +68,7 @@ __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gam
       d2 = s0 + s1;
     }
     if constexpr (METRIC == M_RBF) {
+      if constexpr (PRE) return __builtin_amdgcn_exp2f(-d2);
       if constexpr (sizeof(T) == 4) return __builtin_amdgcn_exp2f(neg_gamma * d2);
       else return dexp(neg_gamma * d2);
     }
@@ -110,9 +113,14 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   jfirst = wave_uniform(jfirst);
   jlast = wave_uniform(jlast);
 
+  // Float rbf (but displacement, which needs the coordinates themselves)
+  // scales both sides by sqrt(gamma log2(e)) once, which saves the
+  // multiply of every pair's exponent.
+  constexpr bool PRE = METRIC == M_RBF && sizeof(T) == 4 && CONS != C_DISPLACEMENT;
+  const T pre_s = PRE ? (T)sqrt(a.gamma * kLog2e) : (T)1;
   T x[DT];
 #pragma unroll
-  for (int d = 0; d < DT; ++d) x[d] = (rv && d < a.D) ? ldg<T>(a.X, i * a.ldx + d) : (T)0;
+  for (int d = 0; d < DT; ++d) x[d] = (rv && d < a.D) ? ldg<T>(a.X, i * a.ldx + d) * pre_s : (T)0;
   RowEpi<T> re;
   load_row_epi<T>(a.epi, i, rv, re);
   const T neg_gamma = sizeof(T) == 4 ? (T)(-a.gamma * kLog2e) : (T)(-a.gamma);
@@ -129,7 +137,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   auto kept = [&](int jj) -> bool { return sC[jj] && pair_kept(a.mask, i, j0c + jj, gi, sG[jj]); };
   // Score of column slot jj (the metric; cosine scales the dot product).
   auto metric = [&](int jj) -> T {
-    T v = valu_metric<METRIC, T, DT>(x, sY[jj], neg_gamma);
+    T v = valu_metric<METRIC, T, DT, PRE>(x, sY[jj], neg_gamma);
     if constexpr (METRIC == M_COSINE) v = fma(-v * sR[jj], rx, (T)1);
     return v;
   };
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     __syncthreads();
     for (int e = tid; e < BN * DT; e += BM) {
       int jj = e / DT, d = e % DT;
-      sY[jj][d] = (jj < nb && d < a.D) ? ldg<T>(a.Y, (j0 + jj) * a.ldy + d) : (T)0;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<T>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : (T)0;
     }
     if constexpr (HAS_V) {
       for (int e = tid; e < BN * VW; e += BM) {

@@ -302,6 +302,9 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   bool rkeep[QB];    // row survives the row mask
   int64_t gq[QB];    // row group id
   const bool has_epi = a.epi.n_stages == 1;
+  // A single-column product under a pure row scale (s <- r s, as a mean
+  // binds it) scales the finished sum instead of every score.
+  const bool epi_post = NARROW && has_epi && !a.epi.st[0].row_vec && a.epi.st[0].p_scalar == 0.0;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     qi[b] = row0 + (int64_t)(w * QB + b) * TM + q;
@@ -535,7 +538,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         v[b][r] = x;
       }
       if constexpr (!ONLINE) {
-        if (has_epi) {
+        if (has_epi && !epi_post) {
 #pragma unroll
           for (int r = 0; r < NREG; ++r) v[b][r] = fma(v[b][r], er[b], ep[b]);
         }
@@ -819,7 +822,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
           static_cast<T *>(a.lse_out)[i] = lt > (T)0 ? m[b] * (T)kLn2 + ep[b] + F::log(lt) : kNegInf;
       }
     } else if constexpr (NARROW) {
-      const T t = F::gsum((wsum[b][0] + wsum[b][1]) + (wsum[b][2] + wsum[b][3]));
+      T t = F::gsum((wsum[b][0] + wsum[b][1]) + (wsum[b][2] + wsum[b][3]));
+      if (epi_post) t *= er[b];
       if (g == 0 && qv[b]) {
         T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow;
         dst[0] = t;

@@ -391,11 +391,27 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       for (int r = 0; r < NREG; ++r)
         s[b][r] = DIST ? ((PL || METRIC == M_RBF) ? sN[kb + F::key_of(r, g)] : nx[b] + sN[kb + F::key_of(r, g)])
                        : (T)0;
+    if constexpr (DG <= 16) {
+      // A short operand run (at most 16 values) is read whole before the
+      // first MFMA (the scheduling barrier keeps the compiler from sinking
+      // the reads again), so its LDS latency is paid once per sub-block
+      // rather than once per vector read.
+      T av[DG];
 #pragma unroll
-    for (int st = 0; st < DG; ++st) {
-      const T av = sK[kb + q][g * DG + st];
+      for (int st = 0; st < DG; ++st) av[st] = sK[kb + q][g * DG + st];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < QB; ++b) s[b] = F::mma(av, qr[b][st], s[b]);
+      for (int st = 0; st < DG; ++st) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b] = F::mma(av[st], qr[b][st], s[b]);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < DG; ++st) {
+        const T av = sK[kb + q][g * DG + st];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b] = F::mma(av, qr[b][st], s[b]);
+      }
     }
   };
 

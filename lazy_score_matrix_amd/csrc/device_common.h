@@ -171,7 +171,8 @@ __device__ __forceinline__ void key_insert(Key<T> (&l)[L], Key<T> c) {
 // that c belongs right after the last key of smaller or equal value: only
 // the values are compared, and each slot takes its left neighbour, c, or
 // itself. The caller has checked that c enters (its value is below the last
-// slot's). Float keys only (value in the high word).
+// slot's). For float keys the value is the high word; double keys take the
+// full compare-swap pass.
 template <int L>
 __device__ __forceinline__ void key_insert_after(Key<float> (&l)[L], Key<float> c) {
   const uint32_t cv = (uint32_t)(c.k >> 32);

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
   // next tile (16-byte vectors from a uniform base when the tile is full and
   // aligned) in flight while the current tile is computed from LDS. The
   // column side holds twice the accumulators and has no registers to spare
-  // for that: it stages each tile element by element.
+  // for that: it reads each tile between the tile's two barriers, four
+  // features at a time.
   constexpr bool PF = SIDE == 0;
   TileLoader<float, BN, DP, kGThreads> ldA;
   TileLoader<float, BN, CPS, kGThreads> ldB;

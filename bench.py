@@ -34,11 +34,11 @@ import workloads  # noqa: E402
 # Algorithmic flops per pair (FMA = 2; add, mul, max, compare = 1; exp = 1;
 # row norms precomputed; distances through |x|^2 + |y|^2 - 2 x.y).
 PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}
-# Kernels with no contraction run on the vector ALU. This build carries no
-# packed-FP32 instructions, so their ceiling is the plain vector FMA rate:
-# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 TFLOP/s (fp32; the
-# fp64 vector rate is the same).
-ALU_PEAK_TFLOPS = {"f32": 78.6, "f64": 78.6}
+# Kernels with no contraction run on the vector ALU. On gfx950 a plain
+# (unpacked) v_fma_f32 issues every 2 cycles per wave64 (measured), so the
+# fp32 vector FMA peak is 256 CUs x 4 SIMDs x 32 lanes x 2 flop x 2.4 GHz =
+# 157.3 TFLOP/s; fp64 vector FMA runs 16 lanes per cycle: 78.6 TFLOP/s.
+ALU_PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -311,8 +311,8 @@ def main():
         "unit": "TFLOP/s",
         "frac": kernels[dom]["frac"],
         "traffic": recorded_traffic(args.workload),
-        "peak_basis": ("dense %s MFMA (equal to the packed vector rate on gfx950)" % dtype if contraction else
-                       "%s vector FMA without packed instructions: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz" % dtype),
+        "peak_basis": ("dense %s MFMA (equal to the vector FMA rate on gfx950)" % dtype if contraction else
+                       "%s vector FMA: 256 CU x 4 SIMD x %d lanes x 2 flop x 2.4 GHz" % (dtype, 32 if dtype == "f32" else 16)),
         "kernel": kernels[dom]["call"],
         "kernel_avg_ms": kernels[dom]["avg_ms"],
         "kernels": kernels,

@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   constexpr int ACCN = HAS_V ? VT : (CONS == C_DISPLACEMENT ? DT : 1);
   constexpr int KL = (CONS == C_TOPK) ? VT : 1;
   constexpr int G = 8;  // columns per online-softmax or top-k screening group
-  // Three features are padded to four so a column is one aligned LDS read.
-  constexpr int DTS = DT == 3 ? 4 : DT;
+  // Three features are stored unpadded: four consecutive columns are three
+  // 16-byte reads, and every broadcast read costs the LDS its full width.
+  constexpr int DTS = DT;
 
   __shared__ T sY[BN][DTS];
   __shared__ T sV[BN][VW];

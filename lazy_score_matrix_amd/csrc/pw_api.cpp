@@ -215,6 +215,13 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {
       p.vcfg.vtile = valu_vtile(C);
       p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
+      // A plain float product of narrow points and values takes two rows
+      // per thread (one LDS broadcast serves both rows).
+      if (consumer == PW_C_MATMUL && e.dtype == PW_F32 && e.metric != PW_COSINE && e.stages.empty() &&
+          !e.row_mask && !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4 && p.vcfg.vtile == 4) {
+        p.vcfg.rows = 2;
+        p.bm = 2 * kValuBM;
+      }
     } else if (consumer == PW_C_TOPK) {
       // The list is sized to k: its warm-up insertions (and their cost)
       // scale with its length.
@@ -629,9 +636,9 @@ int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf
                   (long long)p.split_cols, (int)e->stages.size(), p.total);
   else
     std::snprintf(buf, len,
-                  "family=valu dtile=%d vtile=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
+                  "family=valu dtile=%d vtile=%d rows=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
                   "workspace=%zu",
-                  p.vcfg.dtile, p.vcfg.vtile, p.bm, p.bn, p.n_rb, p.n_split, (long long)p.split_cols,
+                  p.vcfg.dtile, p.vcfg.vtile, p.vcfg.rows, p.bm, p.bn, p.n_rb, p.n_split, (long long)p.split_cols,
                   (int)e->stages.size(), p.total);
   return PW_OK;
 }

@@ -138,6 +138,7 @@ struct TopkKeyBytes<double> { static constexpr int value = 16; };
 struct ValuConfig {
   int dtile;
   int vtile;
+  int rows = 1;  // rows per thread (2: the blocked float kernel product)
 };
 template <class T, int METRIC>
 hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s);

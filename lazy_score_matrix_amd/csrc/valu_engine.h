@@ -513,6 +513,69 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   }
 }
 
+// The plain float kernel product (no score arithmetic, no masks, D <= 4,
+// C <= 4) with two rows per thread: every broadcast read of a column, which
+// costs the LDS its full width, serves two rows' pairs. Rows i and i + 256
+// of a 512-row block; columns past the tile's end are staged as zeros, so
+// their value rows add nothing.
+template <int METRIC, int DT, int VT>
+__global__ __launch_bounds__(kValuBM) void valu_tile_r2(const TileArgs a) {
+  constexpr int BN = kValuBN, R = 2;
+  __shared__ float sY[BN][DT];
+  __shared__ float sV[BN][VT];
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x % a.n_rb;
+  const int sp = blockIdx.x / a.n_rb;
+  const int64_t jb = wave_uniform((int64_t)sp * a.split_cols);
+  const int64_t je = wave_uniform(min(a.M, jb + a.split_cols));
+  constexpr bool PRE = METRIC == M_RBF;
+  const float pre_s = PRE ? (float)sqrt(a.gamma * kLog2e) : 1.f;
+  const float neg_gamma = (float)(-a.gamma * kLog2e);
+  int64_t i[R];
+  bool rv[R];
+  float x[R][DT], acc[R][VT];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    i[u] = (int64_t)rb * (R * kValuBM) + u * kValuBM + tid;
+    rv[u] = i[u] < a.N;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+#pragma unroll
+    for (int c = 0; c < VT; ++c) acc[u][c] = 0.f;
+  }
+  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+    const int nb = (int)min((int64_t)BN, je - j0);
+    __syncthreads();
+    for (int e = tid; e < BN * DT; e += kValuBM) {
+      const int jj = e / DT, d = e % DT;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+    }
+    for (int e = tid; e < BN * VT; e += kValuBM) {
+      const int jj = e / VT, c = e % VT;
+      sV[jj][c] = (jj < nb && c < a.C) ? ldg<float>(a.V, (j0 + jj) * a.ldv + c) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < BN; ++jj) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const float sc = valu_metric<METRIC, float, DT, PRE>(x[u], sY[jj], neg_gamma);
+#pragma unroll
+        for (int c = 0; c < VT; ++c) acc[u][c] = fma(sc, sV[jj][c], acc[u][c]);
+      }
+    }
+  }
+  const bool fin = a.n_split == 1;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    if (!rv[u]) continue;
+    float *o = fin ? static_cast<float *>(a.out) + i[u] * a.ldo : static_cast<float *>(a.partial) + ((int64_t)sp * a.N + i[u]) * a.C;
+#pragma unroll
+    for (int c = 0; c < VT; ++c)
+      if (c < a.C) o[c] = acc[u][c];
+  }
+}
+
 template <class T, int METRIC, int CONS, int DT, int VT>
 hipError_t launch_valu_kernel(const TileArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
@@ -551,6 +614,16 @@ hipError_t valu_by_consumer(int consumer, int vt, const TileArgs &a, hipStream_t
 
 template <class T, int METRIC>
 hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s) {
+  if constexpr (sizeof(T) == 4 && METRIC != M_COSINE) {
+    if (cfg.rows == 2) {
+      if (consumer != C_MATMUL || cfg.vtile != 4 || (cfg.dtile != 3 && cfg.dtile != 4)) return hipErrorInvalidValue;
+      dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
+      if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2<METRIC, 3, 4>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((valu_tile_r2<METRIC, 4, 4>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (cfg.rows != 1) return hipErrorInvalidValue;
   switch (cfg.dtile) {
     case 3: return valu_by_consumer<T, METRIC, 3>(consumer, cfg.vtile, a, s);
     case 4: return valu_by_consumer<T, METRIC, 4>(consumer, cfg.vtile, a, s);

@@ -226,6 +226,13 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       // The list is sized to k: its warm-up insertions (and their cost)
       // scale with its length.
       p.vcfg.vtile = k == 1 ? 1 : (k <= 8 ? 8 : (k <= 16 ? 16 : 64));
+      // The plain float row minimum of narrow points takes two rows per
+      // thread, as the plain product does.
+      if (k == 1 && e.dtype == PW_F32 && e.metric != PW_COSINE && e.stages.empty() && !e.row_mask &&
+          !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4) {
+        p.vcfg.rows = 2;
+        p.bm = 2 * kValuBM;
+      }
     } else {
       p.vcfg.vtile = 0;
     }

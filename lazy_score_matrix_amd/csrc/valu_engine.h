@@ -576,6 +576,86 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2(const TileArgs a) {
   }
 }
 
+// The plain float row minimum (or maximum) with its column, two rows per
+// thread as in valu_tile_r2. Columns reach a thread in increasing order and
+// a candidate must be strictly better, so the lowest index wins a tie.
+template <int METRIC, int DT, bool LARGEST>
+__device__ __forceinline__ void r2_min_tile(const float (&x)[2][DT], const float (*sY)[DT], int n, float neg_gamma,
+                                            float (&thr)[2], int (&bl)[2]) {
+  constexpr bool PRE = METRIC == M_RBF;
+  auto body = [&](int jj) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float sc = valu_metric<METRIC, float, DT, PRE>(x[u], sY[jj], neg_gamma);
+      const float sv = LARGEST ? -sc : sc;
+      const bool lt = sv < thr[u];
+      thr[u] = lt ? sv : thr[u];
+      bl[u] = lt ? jj : bl[u];
+    }
+  };
+  if (n == kValuBN) {
+#pragma unroll 8
+    for (int jj = 0; jj < kValuBN; ++jj) body(jj);
+  } else {
+    for (int jj = 0; jj < n; ++jj) body(jj);
+  }
+}
+
+template <int METRIC, int DT>
+__global__ __launch_bounds__(kValuBM) void valu_tile_r2_min(const TileArgs a) {
+  constexpr int BN = kValuBN, R = 2;
+  __shared__ float sY[BN][DT];
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x % a.n_rb;
+  const int sp = blockIdx.x / a.n_rb;
+  const int64_t jb = wave_uniform((int64_t)sp * a.split_cols);
+  const int64_t je = wave_uniform(min(a.M, jb + a.split_cols));
+  constexpr bool PRE = METRIC == M_RBF;
+  const float pre_s = PRE ? (float)sqrt(a.gamma * kLog2e) : 1.f;
+  const float neg_gamma = (float)(-a.gamma * kLog2e);
+  int64_t i[R];
+  bool rv[R];
+  float x[R][DT], thr[R];
+  uint32_t bj[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    i[u] = (int64_t)rb * (R * kValuBM) + u * kValuBM + tid;
+    rv[u] = i[u] < a.N;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+    thr[u] = __builtin_huge_valf();
+    bj[u] = ~0u;
+  }
+  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+    const int nb = (int)min((int64_t)BN, je - j0);
+    __syncthreads();
+    for (int e = tid; e < BN * DT; e += kValuBM) {
+      const int jj = e / DT, d = e % DT;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+    }
+    __syncthreads();
+    int bl[R] = {-1, -1};  // tile slot of each row's best column met in this tile
+    if (a.largest) r2_min_tile<METRIC, DT, true>(x, sY, nb, neg_gamma, thr, bl);
+    else r2_min_tile<METRIC, DT, false>(x, sY, nb, neg_gamma, thr, bl);
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      if (bl[u] >= 0) bj[u] = (uint32_t)(j0 + bl[u]);
+  }
+  const bool fin = a.n_split == 1;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    if (!rv[u]) continue;
+    const Key<float> key =
+        bj[u] == ~0u ? Key<float>::sentinel() : Key<float>::make(a.largest ? -thr[u] : thr[u], bj[u], a.largest);
+    if (fin) {
+      static_cast<float *>(a.out)[i[u] * a.k] = key.value(a.largest);
+      a.idx[i[u] * a.k] = key.out_index();
+    } else {
+      key.store(a.partial, ((int64_t)sp * a.N + i[u]) * a.k);
+    }
+  }
+}
+
 template <class T, int METRIC, int CONS, int DT, int VT>
 hipError_t launch_valu_kernel(const TileArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
@@ -616,10 +696,17 @@ template <class T, int METRIC>
 hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s) {
   if constexpr (sizeof(T) == 4 && METRIC != M_COSINE) {
     if (cfg.rows == 2) {
-      if (consumer != C_MATMUL || cfg.vtile != 4 || (cfg.dtile != 3 && cfg.dtile != 4)) return hipErrorInvalidValue;
+      if (cfg.dtile != 3 && cfg.dtile != 4) return hipErrorInvalidValue;
       dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
-      if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2<METRIC, 3, 4>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((valu_tile_r2<METRIC, 4, 4>), grid, block, 0, s, a);
+      if (consumer == C_MATMUL && cfg.vtile == 4) {
+        if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2<METRIC, 3, 4>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((valu_tile_r2<METRIC, 4, 4>), grid, block, 0, s, a);
+      } else if (consumer == C_TOPK && cfg.vtile == 1 && a.k == 1) {
+        if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2_min<METRIC, 3>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((valu_tile_r2_min<METRIC, 4>), grid, block, 0, s, a);
+      } else {
+        return hipErrorInvalidValue;
+      }
       return hipGetLastError();
     }
   }

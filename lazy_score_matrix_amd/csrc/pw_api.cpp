@@ -235,6 +235,15 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       }
     } else {
       p.vcfg.vtile = 0;
+      // The float row log-sum-exp of narrow points under at most one
+      // row-only affine stage takes two rows per thread.
+      const bool row_affine = e.stages.empty() || (e.stages.size() == 1 && e.stages[0].kind == ST_AFFINE &&
+                                                   !e.stages[0].col_vec);
+      if (consumer == PW_C_LOGSUMEXP && e.dtype == PW_F32 && e.metric != PW_COSINE && row_affine && !e.row_mask &&
+          !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4) {
+        p.vcfg.rows = 2;
+        p.bm = 2 * kValuBM;
+      }
     }
   }
   // Column norms: |y_j|^2 for the MFMA engine's distance expansion, 1/|y_j|

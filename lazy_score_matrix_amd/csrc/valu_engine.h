@@ -656,6 +656,117 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_min(const TileArgs a) {
   }
 }
 
+// The float row log-sum-exp of narrow points under at most one row-only
+// affine stage, two rows per thread. Scores are kept in base 2 relative to
+// a reference m (moved only when a group of 8 columns exceeds it by more
+// than 8, so weights stay <= 256), as the one-row engine does. Tiles that
+// meet a row's own column under exclude_self check every pair.
+template <int METRIC, int DT, bool CHECK>
+__device__ __forceinline__ void r2_lse_tile(const float (&x)[2][DT], const float (*sY)[DT], int n, float neg_gamma,
+                                            const float (&r2)[2], const float (&p2)[2], float (&q2)[2],
+                                            float (&m)[2], float (&l)[2], int64_t j0, const int64_t (&i)[2],
+                                            bool excl) {
+  constexpr bool PRE = METRIC == M_RBF;
+  constexpr int G = 8;
+  const int ng = CHECK ? n : kValuBN;
+#pragma unroll 1
+  for (int g = 0; g < ng; g += G) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float sv[G];
+      float gm = -__builtin_huge_valf();
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int jj = g + k;
+        float sc = fma(valu_metric<METRIC, float, DT, PRE>(x[u], sY[jj], neg_gamma), r2[u], q2[u]);
+        if (CHECK && (jj >= n || (excl && j0 + jj == i[u]))) sc = -__builtin_huge_valf();
+        sv[k] = sc;
+        gm = fmaxf(gm, sc);
+      }
+      const bool first = m[u] == -__builtin_huge_valf();
+      if (gm > (first ? -__builtin_huge_valf() : 8.f)) {
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-gm);
+        l[u] *= alpha;
+        m[u] = (first ? 0.f : m[u]) + gm;
+        q2[u] = p2[u] - m[u];
+#pragma unroll
+        for (int k = 0; k < G; ++k) sv[k] -= gm;
+      }
+#pragma unroll
+      for (int k = 0; k < G; ++k) l[u] += __builtin_amdgcn_exp2f(sv[k]);
+    }
+  }
+}
+
+template <int METRIC, int DT>
+__global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
+  constexpr int BN = kValuBN, R = 2;
+  __shared__ float sY[BN][DT];
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x % a.n_rb;
+  const int sp = blockIdx.x / a.n_rb;
+  const int64_t jb = wave_uniform((int64_t)sp * a.split_cols);
+  const int64_t je = wave_uniform(min(a.M, jb + a.split_cols));
+  const int64_t r0 = (int64_t)rb * (R * kValuBM), r1 = min(a.N, r0 + R * kValuBM) - 1;
+  constexpr bool PRE = METRIC == M_RBF;
+  const float pre_s = PRE ? (float)sqrt(a.gamma * kLog2e) : 1.f;
+  const float neg_gamma = (float)(-a.gamma * kLog2e);
+  int64_t i[R];
+  bool rv[R];
+  float x[R][DT], r2[R], p2[R], q2[R], m[R], l[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    i[u] = r0 + u * kValuBM + tid;
+    rv[u] = i[u] < a.N;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+    float r = 1.f, p = 0.f;
+    if (a.epi.n_stages == 1) {
+      const Stage &st = a.epi.st[0];
+      if (st.row_vec) {
+        if (rv[u]) {
+          r = ldg<float>(st.r_vec, i[u]);
+          p = ldg<float>(st.p_vec, i[u]);
+        }
+      } else {
+        r = (float)st.r_scalar;
+        p = (float)st.p_scalar;
+      }
+    }
+    r2[u] = kLog2e_f * r;
+    p2[u] = kLog2e_f * p;
+    q2[u] = p2[u];
+    m[u] = -__builtin_huge_valf();
+    l[u] = 0.f;
+  }
+  const bool excl = a.exclude_self != 0;
+  for (int64_t j0 = jb; j0 < je; j0 += BN) {
+    const int nb = (int)min((int64_t)BN, je - j0);
+    __syncthreads();
+    for (int e = tid; e < BN * DT; e += kValuBM) {
+      const int jj = e / DT, d = e % DT;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+    }
+    __syncthreads();
+    const bool check = nb < BN || (excl && j0 <= r1 && j0 + BN > r0);  // uniform over the workgroup
+    if (check) r2_lse_tile<METRIC, DT, true>(x, sY, nb, neg_gamma, r2, p2, q2, m, l, j0, i, excl);
+    else r2_lse_tile<METRIC, DT, false>(x, sY, nb, neg_gamma, r2, p2, q2, m, l, j0, i, excl);
+  }
+  const bool fin = a.n_split == 1;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    if (!rv[u]) continue;
+    const float mn = m[u] == -__builtin_huge_valf() ? m[u] : m[u] * kLn2_f;  // back to natural units
+    if (fin) {
+      static_cast<float *>(a.out)[i[u]] = l[u] > 0.f ? mn + dlog(l[u]) : -__builtin_huge_valf();
+    } else {
+      float *o = static_cast<float *>(a.partial) + ((int64_t)sp * a.N + i[u]) * 2;
+      o[0] = mn;
+      o[1] = l[u];
+    }
+  }
+}
+
 template <class T, int METRIC, int CONS, int DT, int VT>
 hipError_t launch_valu_kernel(const TileArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
@@ -701,6 +812,9 @@ hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArg
       if (consumer == C_MATMUL && cfg.vtile == 4) {
         if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2<METRIC, 3, 4>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((valu_tile_r2<METRIC, 4, 4>), grid, block, 0, s, a);
+      } else if (consumer == C_LOGSUMEXP) {
+        if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2_lse<METRIC, 3>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((valu_tile_r2_lse<METRIC, 4>), grid, block, 0, s, a);
       } else if (consumer == C_TOPK && cfg.vtile == 1 && a.k == 1) {
         if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2_min<METRIC, 3>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((valu_tile_r2_min<METRIC, 4>), grid, block, 0, s, a);

@@ -22,7 +22,7 @@ import torch
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_forms.json")
-_MATH = {"exp": math.exp, "log": math.log, "__builtins__": {}}
+_MATH = {"exp": math.exp, "log": math.log, "abs": abs, "__builtins__": {}}
 DTYPES = (np.float32, np.float64)
 
 
@@ -800,6 +800,229 @@ def pin_backward_finite_differences():
                     vals.append(float(np.sum(np.asarray(out, np.float64) * Gc)))
                 fd[i, d] = (vals[0] - vals[1]) / (2 * h)
         _close(np.asarray(got["dX"][0], np.float64), fd, rtol=1e-6, atol=1e-7, what="finite differences %s" % consumer)
+
+
+
+# ---------------------------------------------------------------- magnitude pins
+# The oracle's `mag` scales every tolerance of the comparison rule (What to
+# Check, Precision). These pins compare it with values derived by hand from
+# its definition (fixture entries expect_mag), for each metric, each kind of
+# op and each consumer.
+
+def _mags(got, want, what):
+    _close(got, [[_ev(v) for v in row] for row in want] if isinstance(want[0], list) else [_ev(v) for v in want],
+           rtol=1e-13, atol=1e-13, what=what)
+
+
+def pin_mag_metric_closed_forms():
+    c = _golden()["metric_values"]
+    for dt in DTYPES:
+        X, Y = np.array(c["X"], dt), np.array(c["Y"], dt)
+        for metric, rows in c["expect_mag"].items():
+            _, mag = oracle.scores(oracle.Expr(X, Y, metric, gamma=c["gamma"]))
+            _mags(mag, rows, "mag metric %s %s" % (metric, dt.__name__))
+    c = _golden()["grid_distances"]
+    X, Y = np.array(c["X"], np.float32), np.array(c["Y"], np.float32)
+    _, mag = oracle.scores(oracle.Expr(X, Y, "sqeuclidean"))
+    _mags(mag, c["expect_mag"]["sqeuclidean"], "mag grid distances")
+
+
+def pin_mag_op_chain_closed_forms():
+    c = _golden()["op_chain_magnitudes"]
+    for dt in DTYPES:
+        X, Y = np.array(c["X"], dt), np.array(c["Y"], dt)
+        for ch in c["chains"]:
+            ops = [(n, np.array(a, dt) if isinstance(a, list) else a) for n, a in ch["ops"]]
+            out, mag = oracle.scores(oracle.Expr(X, Y, c["metric"], ops=ops))
+            name = "/".join(n for n, _ in ch["ops"])
+            _close(out, [[_ev(ch["expect"])]], rtol=1e-13, atol=1e-13, what="chain %s" % name)
+            _close(mag, [[_ev(ch["expect_mag"])]], rtol=1e-13, atol=1e-13, what="chain mag %s" % name)
+
+
+def pin_mag_consumers_golden():
+    g = _golden()
+    for dt in DTYPES:
+        c = g["grid_kernel_product"]
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], gamma=c["gamma"])
+        _mags(oracle.matmul(e, np.array(c["V"], dt))[1], c["expect_mag"]["matmul"], "mag kernel product")
+        c = g["grid_displacement"]
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], gamma=c["gamma"])
+        _mags(oracle.displacement(e)[1], c["expect_mag"]["displacement"], "mag displacement")
+        c = g["grid_logsumexp"]
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], ops=c["ops"])
+        _mags(oracle.logsumexp(e)[1], c["expect_mag"]["logsumexp"], "mag logsumexp")
+        _mags(oracle.logsumexp(e, exclude_self=True)[1], c["expect_mag"]["logsumexp_exclude_self"],
+              "mag logsumexp exclude_self")
+        c = g["grid_softmax_matmul"]
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), c["metric"], ops=c["ops"])
+        _mags(oracle.softmax_matmul(e, np.array(c["V"], dt))[1], c["expect_mag"]["softmax_matmul"], "mag softmax")
+        c = g["grid_distances"]
+        e = oracle.Expr(np.array(c["X"], dt), np.array(c["Y"], dt), "sqeuclidean")
+        _mags(oracle.topk(e, 3)[2], c["expect_mag"]["topk_smallest_3"], "mag topk")
+
+
+# ---------------------------------------------------------------- comparison-rule pins
+# The rule |g - o| <= rtol max(|o|, mag) (tests/parity.py) must accept what a
+# correct float32 kernel may return -- the same sums rounded to float32 in
+# other orders: blocked online softmax / log-sum-exp, the norm expansion of
+# distances, a row factor applied after the sum -- and must reject the
+# mistakes a tiled kernel can make: one key dropped at a split boundary, the
+# self pair kept, a wrong scale, a swapped tie. Shapes are those of the
+# attention, InfoNCE and Nadaraya-Watson workloads, reduced.
+import parity  # noqa: E402
+
+F32 = torch.float32
+
+
+def _attention_case():
+    r = _rng(500)
+    Q = r.standard_normal((96, 64)).astype(np.float32)
+    K = r.standard_normal((650, 64)).astype(np.float32)
+    V = r.standard_normal((650, 64)).astype(np.float32)
+    return Q, K, V, [("mul", 0.125)]
+
+
+def _infonce_case():
+    r = _rng(501)
+    z = r.standard_normal((700, 64))
+    z = (z / np.linalg.norm(z, axis=1, keepdims=True)).astype(np.float32)
+    b = (math.sqrt(0.1) * r.standard_normal(700)).astype(np.float32)
+    return z, b, [("mul", 1.0 / 0.07), ("add_rows", b)]
+
+
+def _online_softmax_f32(S, V, bn=64):
+    """softmax(S) @ V in float32, column blocks of bn in order, running
+    (max, sum, acc) rescaled at every block."""
+    n = S.shape[0]
+    m = torch.full((n, 1), -float("inf"), dtype=F32)
+    l = torch.zeros((n, 1), dtype=F32)
+    acc = torch.zeros((n, V.shape[1]), dtype=F32)
+    for j in range(0, S.shape[1], bn):
+        s = S[:, j:j + bn]
+        m2 = torch.maximum(m, s.max(1, keepdim=True).values)
+        a = torch.exp(m - m2)
+        p = torch.exp(s - m2)
+        l = l * a + p.sum(1, keepdim=True)
+        acc = acc * a + p @ V[j:j + bn]
+        m = m2
+    return acc / l, m + torch.log(l)
+
+
+def pin_rule_accepts_float32_orders():
+    # Attention: library softmax, and a blocked online softmax.
+    Q, K, V, ops = _attention_case()
+    o, mag = oracle.softmax_matmul(oracle.Expr(Q, K, "linear", ops=ops), V)
+    S = (torch.from_numpy(Q) @ torch.from_numpy(K).T) * 0.125
+    Vt = torch.from_numpy(V)
+    for name, g in (("library", torch.softmax(S, -1) @ Vt), ("online", _online_softmax_f32(S, Vt)[0])):
+        ok, ratio, _ = parity.value_report(g.numpy(), o, mag, np.float32, n_terms=650, vmax=float(np.abs(V).max()))
+        assert ok, "attention %s: float32 result rejected (err/tol %.3g)" % (name, ratio)
+    # InfoNCE: log-sum-exp without the self pair, library and online.
+    z, b, ops = _infonce_case()
+    o, mag = oracle.logsumexp(oracle.Expr(z, z, "linear", ops=ops), exclude_self=True)
+    zt = torch.from_numpy(z)
+    S = (zt @ zt.T) * np.float32(1.0 / 0.07) + torch.from_numpy(b)[:, None]
+    S.fill_diagonal_(-float("inf"))
+    ones = torch.ones((S.shape[0], 1), dtype=F32)
+    for name, g in (("library", torch.logsumexp(S, -1)), ("online", _online_softmax_f32(S, ones)[1][:, 0])):
+        ok, ratio, _ = parity.value_report(g.numpy(), o, mag, np.float32, n_terms=700)
+        assert ok, "infonce %s: float32 result rejected (err/tol %.3g)" % (name, ratio)
+    # Kernel product of rbf scores: direct distances, and the norm expansion
+    # with the row factor 2^(-|x|^2) applied after the column sum.
+    r = _rng(502)
+    X = r.standard_normal((300, 3)).astype(np.float32)
+    Y = r.standard_normal((333, 3)).astype(np.float32)
+    Vk = np.concatenate([r.standard_normal((333, 3)), np.ones((333, 1))], 1).astype(np.float32)
+    o, mag = oracle.matmul(oracle.Expr(X, Y, "rbf", gamma=0.5), Vk)
+    Xt, Yt, Vt = torch.from_numpy(X), torch.from_numpy(Y), torch.from_numpy(Vk)
+    direct = torch.exp(-0.5 * ((Xt[:, None, :] - Yt[None, :, :]) ** 2).sum(-1)) @ Vt
+    sc = np.float32(math.sqrt(0.5 / math.log(2.0)))
+    xs, ys = Xt * sc, Yt * sc
+    t = 2 * (xs @ ys.T) - (ys * ys).sum(1)[None, :]
+    expansion = (torch.exp2(t) @ Vt) * torch.exp2(-(xs * xs).sum(1))[:, None]
+    for name, g in (("direct", direct), ("expansion", expansion)):
+        ok, ratio, _ = parity.value_report(g.numpy(), o, mag, np.float32, n_terms=333, vmax=float(np.abs(Vk).max()))
+        assert ok, "kernel product %s: float32 result rejected (err/tol %.3g)" % (name, ratio)
+
+
+def _rejects(g, o, mag, n_terms, what, vmax=1.0):
+    ok, ratio, _ = parity.value_report(g, o, mag, np.float32, n_terms=n_terms, vmax=vmax)
+    assert not ok, "%s: the comparison rule accepts it (worst err/tol %.3g)" % (what, ratio)
+
+
+def pin_rule_rejects_dropped_key():
+    """The oracle's own result without one key -- the last column of a
+    split, here column 64 and the last column -- fails the rule."""
+    Q, K, V, ops = _attention_case()
+    o, mag = oracle.softmax_matmul(oracle.Expr(Q, K, "linear", ops=ops), V)
+    z, b, zops = _infonce_case()
+    lo, lmag = oracle.logsumexp(oracle.Expr(z, z, "linear", ops=zops), exclude_self=True)
+    r = _rng(503)
+    X = r.standard_normal((200, 3)).astype(np.float32)
+    Vk = np.concatenate([r.standard_normal((333, 3)), np.ones((333, 1))], 1).astype(np.float32)
+    Y = r.standard_normal((333, 3)).astype(np.float32)
+    mo, mmag = oracle.matmul(oracle.Expr(X, Y, "rbf", gamma=0.5), Vk)
+    for drop in (64, -1):
+        keep = np.ones(K.shape[0], bool)
+        keep[drop] = False
+        g, _ = oracle.softmax_matmul(oracle.Expr(Q, K[keep], "linear", ops=ops), V[keep])
+        _rejects(g, o, mag, 650, "attention without key %d" % drop, float(np.abs(V).max()))
+        keep = np.ones(z.shape[0], bool)
+        keep[drop] = False
+        # Column `drop` removed; the self pair of every row stays excluded.
+        S = np.asarray(oracle.scores(oracle.Expr(z, z[keep], "linear", ops=zops))[0], np.float64)
+        rows = np.arange(z.shape[0])
+        cols = np.nonzero(keep)[0]
+        S[rows[:, None] == cols[None, :]] = -np.inf
+        mx = S.max(1)
+        g = mx + np.log(np.exp(S - mx[:, None]).sum(1))
+        _rejects(g, lo, lmag, 700, "infonce without key %d" % drop)
+        keep = np.ones(Y.shape[0], bool)
+        keep[drop] = False
+        g, _ = oracle.matmul(oracle.Expr(X, Y[keep], "rbf", gamma=0.5), Vk[keep])
+        _rejects(g, mo, mmag, 333, "kernel product without key %d" % drop, float(np.abs(Vk).max()))
+
+
+def pin_rule_rejects_kept_self_pair_and_wrong_scale():
+    z, b, ops = _infonce_case()
+    o, mag = oracle.logsumexp(oracle.Expr(z, z, "linear", ops=ops), exclude_self=True)
+    g, _ = oracle.logsumexp(oracle.Expr(z, z, "linear", ops=ops), exclude_self=False)
+    _rejects(g, o, mag, 700, "infonce with the self pair kept")
+    g, _ = oracle.logsumexp(oracle.Expr(z, z, "linear", ops=[("mul", 1.0 / 0.0701), ("add_rows", b)]),
+                            exclude_self=True)
+    _rejects(g, o, mag, 700, "infonce with temperature 0.0701")
+    Q, K, V, aops = _attention_case()
+    o, mag = oracle.softmax_matmul(oracle.Expr(Q, K, "linear", ops=aops), V)
+    g, _ = oracle.softmax_matmul(oracle.Expr(Q, K, "linear", ops=[("mul", 0.1251)]), V)
+    _rejects(g, o, mag, 650, "attention with scale 0.1251", float(np.abs(V).max()))
+
+
+def pin_rule_topk_ties():
+    """Top-k on a grid with exact ties: the float32 norm-expansion search
+    (exact on small integers) passes, exactly and by the tolerance rule;
+    swapping two tied positions, or two separated ones, fails both."""
+    r = _rng(504)
+    X = r.integers(-3, 4, (40, 2)).astype(np.float32)
+    Y = r.integers(-3, 4, (150, 2)).astype(np.float32)
+    k = 6
+    ov, oi, om = oracle.topk(oracle.Expr(X, Y, "sqeuclidean"), k, extra=8)
+    Xt, Yt = torch.from_numpy(X), torch.from_numpy(Y)
+    d = (Xt * Xt).sum(1)[:, None] + (Yt * Yt).sum(1)[None, :] - 2 * (Xt @ Yt.T)
+    gv, gi = torch.sort(d, dim=1, stable=True)
+    gv, gi = gv[:, :k].numpy(), gi[:, :k].numpy()
+    for exact in (True, False):
+        fails = parity.topk_report(gv, gi, ov, oi, om, k, False, np.float32, exact=exact)
+        assert not fails, "float32 expansion search rejected: %s" % fails[:2]
+    ties = [(row, p) for row in range(X.shape[0]) for p in range(k - 1) if ov[row, p] == ov[row, p + 1]]
+    seps = [(row, p) for row in range(X.shape[0]) for p in range(k - 1) if ov[row, p] != ov[row, p + 1]]
+    assert ties and seps, "the grid has both tied and separated neighbours"
+    for row, p in (ties[0], seps[0]):
+        bi, bv = gi.copy(), gv.copy()
+        bi[row, [p, p + 1]] = bi[row, [p + 1, p]]
+        bv[row, [p, p + 1]] = bv[row, [p + 1, p]]
+        for exact in (True, False):
+            assert parity.topk_report(bv, bi, ov, oi, om, k, False, np.float32, exact=exact), \
+                "swapped positions %d/%d of row %d accepted (exact=%s)" % (p, p + 1, row, exact)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -55,6 +55,26 @@ MUTANTS = [
     ("backward_matmul_dv", "gvout[c] += t[n] * g(i, c);", "gvout[c] += g(i, c);"),
     ("backward_topk_position", "if (idx[i * k + p] == j) a += (R)G[i * ldg + p];",
      "if (idx[i * k + p] == j) a += (R)G[i * ldg];"),
+    # Planted mistakes in the error magnitude `mag`, which scales every
+    # tolerance of the comparison rule.
+    ("mag_linear_times_1000", "mu += std::fabs(p);", "mu += 1000 * std::fabs(p);"),
+    ("mag_distance_spread_from_difference", "R w = std::fabs(a) + std::fabs(b);", "R w = std::fabs(a - b);"),
+    ("mag_rbf_without_spread", "mu = s * (1 + (R)e.gamma * spread);", "mu = s;"),
+    ("mag_cosine_constant", "mu = 1 + 3 * adot / den;", "mu = 1;"),
+    ("mag_mul_unscaled", "s = (R)e.op_scalar[k] * s; mu = std::fabs((R)e.op_scalar[k]) * mu;",
+     "s = (R)e.op_scalar[k] * s; mu = mu;"),
+    ("mag_add_ignores_new_score", "case OP_ADD: s = s + (R)e.op_scalar[k]; mu = mu + std::fabs(s);",
+     "case OP_ADD: s = s + (R)e.op_scalar[k]; mu = mu;"),
+    ("mag_exp_drops_one", "R ex = rexp(s); mu = ex * (1 + mu);", "R ex = rexp(s); mu = ex * mu;"),
+    ("mag_weight_columns_unscaled", "s = u * s; mu = std::fabs(u) * mu;", "s = u * s; mu = mu;"),
+    ("mag_matmul_times_1000", "m[c] += (std::fabs(s) + mu) * std::fabs(v);", "m[c] += 1000 * (std::fabs(s) + mu) * std::fabs(v);"),
+    ("mag_displacement_drops_x", "m[d] += (std::fabs(s) + mu) * (std::fabs(yd) + std::fabs(xd));",
+     "m[d] += (std::fabs(s) + mu) * std::fabs(yd);"),
+    ("mag_lse_sum_not_max", "mumax = std::max(mumax, mu[t]);", "mumax = mumax + mu[t];"),
+    ("mag_lse_drops_log", "mag[r] = mumax + rlog(l);", "mag[r] = mumax;"),
+    ("mag_softmax_without_p", "av[c] += p * (1 + mu[t]) * std::fabs(v);", "av[c] += (1 + mu[t]) * std::fabs(v);"),
+    ("mag_softmax_drops_cross_term", "mag[r * C + c] = av[c] + pmu * apv[c];", "mag[r * C + c] = av[c];"),
+    ("mag_topk_of_first_pair", "mag[r * kk + p] = buf[p].mu;", "mag[r * kk + p] = buf[0].mu;"),
 ]
 
 

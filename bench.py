@@ -3,14 +3,21 @@
 A step is one full pass of the hot path over one synthetic workload: the
 consumer call(s) of that workload (epilogue pre-pass, tile kernel, split
 merge), with inputs, outputs and workspace already resident in HBM.
-Default workload: softmax attention, Q, K, V [16384, 64] float32, scores
-Q.K^T / 8 (the attention row of the torchpairwise guide's Task Map).
+
+Headline (the JSON line's value): k-NN retrieval, 65536 queries against
+2^20 references, D = 32, float32, top-10 smallest squared distances (the
+k-NN row of the torchpairwise guide's Task Map), the largest configuration
+that fits one GPU. The same run times every other fused consumer at its
+full size -- softmax attention, the InfoNCE log-sum-exp, the SVGD kernel
+product and displacement (float64) and the narrow rbf kernel product -- and
+reports each in roofline.kernels with its own oracle sample and parity.
 
 Prints ONE JSON line: pair evaluations per second (Gpairs/s), the roofline
-of the dominant kernel, the CPU oracle timed on a bounded row sample on the
-host cores, and the parity of the timed outputs on that sample.
+of the dominant kernel, the CPU oracle timed on bounded row samples on the
+host cores, and the parity of the timed outputs on those samples.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--also NAME,NAME,...] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -134,34 +141,22 @@ def case_operands(c, arrays):
     return X, Y, ops
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="attention", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for cpu_baseline")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device copy (counter calibration)")
-    args = ap.parse_args()
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
+# Workloads timed beside the headline by default: every fused consumer at
+# its full size (attention softmax@V, InfoNCE log-sum-exp, the SVGD product
+# and displacement in float64, the narrow rbf kernel product).
+DEFAULT_ALSO = ("attention", "infonce", "svgd", "rbf_large")
 
+
+def build_calls(name, dev):
+    """Bind every call of a workload on the device, with its outputs and
+    workspace allocated. Returns (arrays, calls, pairs_per_step,
+    solve_infos); calls are (case, expr, fn, outputs, C)."""
     import torch
     import lazy_score_matrix_amd as pw
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    arrays, cases = workloads.make(args.workload)
+    arrays, cases = workloads.make(name)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in arrays.items()}
-
-    calls = []  # (case, expr, run_fn, outputs)
+    calls = []
     pairs_per_step = 0
     solve_infos = []
     for c in cases:
@@ -232,36 +227,115 @@ def main():
         calls.append((c, e, fn, outs, C))
         if c.consumer != "cg_solve":
             pairs_per_step += c.pairs if c.pairs is not None else N * M
+    return arrays, calls, pairs_per_step, solve_infos
 
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        for _, _, fn, _, _ in calls:
-            fn()
-    torch.cuda.synchronize()
 
-    # Timed region: K steps back to back. Per step and call, the library
-    # records a pair of HIP events around its tile-kernel launch on the same
-    # stream (pw_set_tile_events), giving each dominant kernel's own duration.
-    lib = pw.load_library()
-    hip = ctypes.CDLL("libamdhip64.so.7")
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+class _Hip:
+    """HIP events through the runtime's C API: the library records them on
+    the stream it launches on."""
 
-    def new_event():
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
         ev = ctypes.c_void_p()
-        assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
         return ev
 
-    kev = [[(new_event(), new_event()) for _ in calls] for _ in range(args.steps)]
+    def elapsed(self, a, b):
+        f = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def time_calls(calls, steps, warmup, hip, min_warmup_s=0.0):
+    """W untimed steps (more, until min_warmup_s has passed, if given), then
+    exactly K steps between two events on the launch stream, each bracketed
+    by synchronisation. Per step and call, the library records a pair of HIP
+    events around its tile-kernel launch on the same stream
+    (pw_set_tile_events). Returns (ms per step, average tile-kernel ms per
+    call, warm-up steps run)."""
+    import torch
+    import lazy_score_matrix_amd as pw
+
+    lib = pw.load_library()
+    stream = torch.cuda.current_stream()
+    done = 0
+    t0 = time.perf_counter()
+    while done < warmup or (time.perf_counter() - t0 < min_warmup_s and done < 100000):
+        for _, _, fn, _, _ in calls:
+            fn()
+        done += 1
+        if done >= warmup and min_warmup_s > 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    kev = [[(hip.event(), hip.event()) for _ in calls] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for st in range(args.steps):
+    for st in range(steps):
         for ci, (_, _, fn, _, _) in enumerate(calls):
             lib.pw_set_tile_events(kev[st][ci][0], kev[st][ci][1])
             fn()
     lib.pw_set_tile_events(None, None)
     stop.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = start.elapsed_time(stop) / steps
+    kernel_ms = [sum(hip.elapsed(*kev[st][ci]) for st in range(steps)) / steps for ci in range(len(calls))]
+    for row in kev:
+        for a_, b_ in row:
+            hip.destroy(a_)
+            hip.destroy(b_)
+    return ms, kernel_ms, done
+
+
+def dtype_name(e):
+    import torch
+    return "f32" if e.dtype == torch.float32 else "f64"
+
+
+def is_contraction(c, e, C):
+    """Whether a call's tile kernel runs on the matrix cores."""
+    if c.consumer.startswith("backward_"):
+        return e.backward_plan(lib_consumer(c), C).startswith("family=mfma")
+    return e.plan(lib_consumer(c), C, c.k).startswith("family=mfma")
+
+
+def kernel_entries(name, calls, kernel_ms):
+    """One roofline entry per call: its tile kernel's average duration,
+    algorithmic flops and fraction of the peak of the unit it runs on."""
+    out = []
+    for (c, e, _, _, C), kms in zip(calls, kernel_ms):
+        dtype = dtype_name(e)
+        mfma = is_contraction(c, e, C)
+        peak = PEAK_TFLOPS[dtype] if mfma else ALU_PEAK_TFLOPS[dtype]
+        fpp = flops_per_pair(c, e.D, C)
+        pairs = float(c.pairs if c.pairs is not None else e.N * e.M)
+        tf = pairs * fpp / (kms * 1e-3) / 1e12
+        plan = (e.backward_plan(lib_consumer(c), C) if c.consumer.startswith("backward_")
+                else e.plan(lib_consumer(c), C, c.k))
+        out.append({"workload": name, "call": c.name, "dtype": dtype, "bound": "mfma" if mfma else "alu",
+                    "plan": plan, "pairs": int(pairs), "avg_ms": round(kms, 4),
+                    "gpairs_per_s": round(pairs / (kms * 1e-3) / 1e9, 3), "flops_per_pair": fpp,
+                    "tflops": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4)})
+    return out
+
+
+# The workloads timed beside the headline warm up for at least this long
+# (the headline takes exactly --warmup steps): the clock settles over a few
+# hundred milliseconds after a change of load (measured on the narrow rbf
+# product: 0.96 ms per launch after 3 warm-up steps, 0.86 ms after 300).
+ALSO_MIN_WARMUP_S = 0.3
+
+
+def run_workload(name, args, dev, hip, min_warmup_s=0.0):
+    """Time one workload; returns its summary, kernel entries and the state
+    the oracle leg needs."""
+    arrays, calls, pairs_per_step, solve_infos = build_calls(name, dev)
+    ms, kernel_ms, warm = time_calls(calls, args.steps, args.warmup, hip, min_warmup_s)
     solve_summary = None
     if solve_infos:
         # Timed solves: the last args.steps entries of each solve's log.
@@ -271,80 +345,115 @@ def main():
         pairs_per_step += sum(it * e.N * e.M for it, (c, e) in zip(its, cg_calls))
         solve_summary = [{"call": c.name, "iterations_per_solve": it, "info": log[-1]}
                          for it, (c, e), log in zip(its, cg_calls, timed)]
-    gpairs = pairs_per_step / (ms * 1e-3) / 1e9
-    kernel_ms = []
-    for ci in range(len(calls)):
-        tot = 0.0
-        for st in range(args.steps):
-            f = ctypes.c_float()
-            assert hip.hipEventElapsedTime(ctypes.byref(f), kev[st][ci][0], kev[st][ci][1]) == 0
-            tot += f.value
-        kernel_ms.append(tot / args.steps)
-    for row in kev:
-        for a_, b_ in row:
-            hip.hipEventDestroy(a_)
-            hip.hipEventDestroy(b_)
+    e0 = calls[0][1]
+    summary = {
+        "workload": name,
+        "consumers": [c.consumer for c, *_ in calls],
+        "N": int(e0.N), "M": int(e0.M), "D": int(e0.D),
+        "C": [C for *_, C in calls],
+        "dtype": dtype_name(e0),
+        "pairs_per_step": pairs_per_step,
+        "warmup_steps": warm,
+        "ms_per_step": round(ms, 4),
+        "gpairs_per_s": round(pairs_per_step / (ms * 1e-3) / 1e9, 3),
+    }
+    if solve_summary:
+        summary["solves"] = solve_summary
+    return summary, kernel_entries(name, calls, kernel_ms), (arrays, calls)
 
-    dtype = "f32" if calls[0][1].dtype == torch.float32 else "f64"
-    dom0 = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
-    c_, e_, _, _, C_ = calls[dom0]
-    if c_.consumer.startswith("backward_"):
-        contraction = e_.backward_plan(lib_consumer(c_), C_).startswith("family=mfma")
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="knn", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads timed beside the headline (default: every other fused "
+                         "consumer at full size when the headline is knn; 'none' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="target oracle wall time per call for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if args.also is None:
+        also = list(DEFAULT_ALSO) if args.workload == "knn" else []
     else:
-        contraction = e_.plan(lib_consumer(c_), C_, c_.k).startswith("family=mfma")
-    peak = PEAK_TFLOPS[dtype] if contraction else ALU_PEAK_TFLOPS[dtype]
-    kernels = []
-    for (c, e, _, _, C), kms in zip(calls, kernel_ms):
-        fl = float(c.pairs if c.pairs is not None else e.N * e.M) * flops_per_pair(c, e.D, C)
-        tf = fl / (kms * 1e-3) / 1e12
-        plan = (e.backward_plan(lib_consumer(c), C) if c.consumer.startswith("backward_")
-                else e.plan(lib_consumer(c), C, c.k))
-        kernels.append({"call": c.name, "plan": plan, "avg_ms": round(kms, 4),
-                        "flops_per_pair": flops_per_pair(c, e.D, C), "tflops": round(tf, 3),
-                        "frac": round(tf / peak, 4)})
-    dom = max(range(len(calls)), key=lambda ci: kernel_ms[ci])
-    e0 = calls[dom][1]
+        also = [w for w in args.also.split(",") if w and w != "none"]
+    for w in also:
+        if w not in workloads.WORKLOADS:
+            ap.error("unknown workload %r in --also" % w)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = _Hip()
+
+    names = [args.workload] + [w for w in also if w != args.workload]
+    summaries, kernels, cpu_parts, parity = [], [], [], []
+    for wi, name in enumerate(names):
+        summary, kern, (arrays, calls) = run_workload(name, args, dev, hip, ALSO_MIN_WARMUP_S if wi else 0.0)
+        summaries.append(summary)
+        kernels.extend(kern)
+        if not args.no_cpu:
+            cpu, par = cpu_leg(name, calls, arrays, args.cpu_seconds)
+            cpu_parts.append(cpu)
+            parity.extend(par)
+        del calls, arrays
+        torch.cuda.empty_cache()
+
+    head = summaries[0]
+    head_k = [k for k in kernels if k["workload"] == head["workload"]]
+    dom = max(head_k, key=lambda k: k["avg_ms"])
     roofline = {
-        "bound": "mfma" if contraction else "alu",
-        "achieved": kernels[dom]["tflops"],
-        "peak": peak,
+        "bound": dom["bound"],
+        "achieved": dom["tflops"],
+        "peak": dom["peak"],
         "unit": "TFLOP/s",
-        "frac": kernels[dom]["frac"],
-        "traffic": recorded_traffic(args.workload),
-        "peak_basis": ("dense %s MFMA (equal to the vector FMA rate on gfx950)" % dtype if contraction else
-                       "%s vector FMA: 256 CU x 4 SIMD x %d lanes x 2 flop x 2.4 GHz" % (dtype, 32 if dtype == "f32" else 16)),
-        "kernel": kernels[dom]["call"],
-        "kernel_avg_ms": kernels[dom]["avg_ms"],
+        "frac": dom["frac"],
+        "traffic": recorded_traffic(head["workload"]),
+        "peak_basis": ("dense %s MFMA (equal to the vector FMA rate on gfx950)" % dom["dtype"] if dom["bound"] == "mfma"
+                       else "%s vector FMA: 256 CU x 4 SIMD x %d lanes x 2 flop x 2.4 GHz"
+                       % (dom["dtype"], 32 if dom["dtype"] == "f32" else 16)),
+        "kernel": dom["call"],
+        "kernel_avg_ms": dom["avg_ms"],
         "kernels": kernels,
     }
-
+    config = {k: head[k] for k in ("workload", "consumers", "N", "M", "D", "C", "pairs_per_step")}
+    if "solves" in head:
+        config["solves"] = head["solves"]
+    config["also"] = [{k: s_[k] for k in ("workload", "consumers", "N", "M", "D", "dtype", "pairs_per_step",
+                                          "warmup_steps", "ms_per_step", "gpairs_per_s")} for s_ in summaries[1:]]
     result = {
         "metric": "pair evaluations/sec (Gpairs/s) per consumer + % of gfx950 FP32/FP64 peak",
-        "value": round(gpairs, 3),
+        "value": head["gpairs_per_s"],
         "unit": "Gpairs/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {
-            "workload": args.workload,
-            "consumers": [c.consumer for c, *_ in calls],
-            "N": int(e0.N), "M": int(e0.M), "D": int(e0.D),
-            "C": [C for *_, C in calls],
-            "pairs_per_step": pairs_per_step,
-        },
+        "config": config,
         "roofline": roofline,
     }
-    if solve_summary:
-        result["config"]["solves"] = solve_summary
-
-    if not args.no_cpu:
-        result.update(cpu_leg(calls, arrays, args.cpu_seconds))
+    if cpu_parts:
+        cb = dict(cpu_parts[0])
+        cb["workloads"] = cpu_parts
+        result["cpu_baseline"] = cb
+        result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 
@@ -384,16 +493,18 @@ def backward_cpu_leg(c, oe, arrays, outs, budget, threads):
     return pairs, dt, desc, {"call": c.name, "rows": len(rows), "pass": bool(ok), "worst_err_over_tol": worst}
 
 
-def cpu_leg(calls, arrays, seconds):
-    """Time the oracle on a bounded row sample on the host cores, and check
-    the timed GPU outputs against it on the same rows."""
+def cpu_leg(name, calls, arrays, seconds):
+    """Time the oracle on a bounded row sample of one workload on the host
+    cores (about `seconds` per call), and check the timed GPU outputs
+    against it on the same rows. Returns (cpu_baseline entry, parity
+    entries)."""
     import oracle
     from parity import topk_report, value_report
 
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     total_pairs, total_s, rows_desc, parity = 0, 0.0, [], []
-    budget = seconds / len(calls)
+    budget = seconds
     for c, e, _, outs, C in calls:
         X, Y, ops = case_operands(c, arrays)
         oe = oracle.Expr(X, Y, c.metric, gamma=c.gamma, ops=ops)
@@ -457,16 +568,16 @@ def cpu_leg(calls, arrays, seconds):
             ok, ratio, rel = value_report(g, res[0], res[1], dtype, n_terms=oe.M, vmax=vmax)
             parity.append({"call": c.name, "rows": len(rows), "pass": bool(ok), "worst_err_over_tol": ratio,
                            "max_plain_rel_err": rel})
+    for p_ in parity:
+        p_["workload"] = name
     return {
-        "cpu_baseline": {
-            "value": round(total_pairs / total_s / 1e9, 6),
-            "unit": "Gpairs/s",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": "; ".join(rows_desc),
-        },
-        "parity": parity,
-    }
+        "workload": name,
+        "value": round(total_pairs / total_s / 1e9, 6),
+        "unit": "Gpairs/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "; ".join(rows_desc),
+    }, parity
 
 
 if __name__ == "__main__":

@@ -141,8 +141,30 @@ struct pw_expr {
 
 namespace {
 
-constexpr int kTargetCUs = 256;            // MI355X compute units
-constexpr int64_t kTargetWGs = 4 * kTargetCUs;
+// Compute units of the current device (MI355X: 256), read once per device;
+// 256 when no device answers (host-only planning, e.g. workspace sizing on a
+// machine without a GPU), so a plan never depends on a failed query.
+constexpr int kDefaultCUs = 256;
+constexpr int kMaxDevices = 64;
+int target_cus() {
+  static int cached[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      cus = kDefaultCUs;
+    }
+    __atomic_store_n(&cached[dev], cus, __ATOMIC_RELAXED);
+    n = cus;
+  }
+  return n;
+}
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -197,7 +219,8 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     }
   }
   p.off_epi = 0;
-  int64_t target_wgs = kTargetWGs;
+  const int cus = target_cus();
+  int64_t target_wgs = 4 * (int64_t)cus;
   if (mfma_eligible(e, consumer, C)) {
     p.family = 1;
     p.mcfg.dp = e.D <= 16 ? 16 : (e.D <= 32 ? 32 : 64);
@@ -209,18 +232,20 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     p.bm = mfma_bm(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
     p.bn = mfma_bn(e.dtype, consumer, p.mcfg.cp);
     p.chunk = (int)std::min<int64_t>(C, p.mcfg.cp);
-    target_wgs = (int64_t)kTargetCUs * mfma_wgs_per_cu(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
+    target_wgs = (int64_t)cus * mfma_wgs_per_cu(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
   } else {
     p.vcfg.dtile = valu_dtile(e.D);
     if (consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL) {
       p.vcfg.vtile = valu_vtile(C);
       p.chunk = (int)std::min<int64_t>(C, p.vcfg.vtile);
-      // A plain float product of narrow points and values takes two rows
-      // per thread (one LDS broadcast serves both rows).
+      // A plain float product of narrow points and values takes several
+      // rows per thread (one LDS broadcast serves them all) and wide tiles.
       if (consumer == PW_C_MATMUL && e.dtype == PW_F32 && e.metric != PW_COSINE && e.stages.empty() &&
           !e.row_mask && !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4 && p.vcfg.vtile == 4) {
-        p.vcfg.rows = 2;
-        p.bm = 2 * kValuBM;
+        p.vcfg.rows = kProdRows;
+        p.bm = kProdRows * kValuBM;
+        p.bn = kProdBN;
+        target_wgs = (int64_t)kProdWGsPerCU * cus;
       }
     } else if (consumer == PW_C_TOPK) {
       // The list is sized to k: its warm-up insertions (and their cost)
@@ -805,12 +830,13 @@ GradPlan grad_plan(const pw_expr &e, int consumer, int64_t C) {
   g.ct = C <= 16 ? 16 : 64;
   for (const pw_op &o : e.ops) g.n_arith += is_arith_op(o.kind);
   const bool value = consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL;
+  const int cus = target_cus();
   size_t part = 0;
   for (int side = 0; side < 2; ++side) {
     const int64_t n_own = side == 0 ? e.N : e.M, n_oth = side == 0 ? e.M : e.N;
     g.n_rb[side] = (int)std::max<int64_t>(1, (n_own + kGradRows - 1) / kGradRows);
     const int64_t tiles = std::max<int64_t>(1, (n_oth + kGradCols - 1) / kGradCols);
-    int64_t want = std::max<int64_t>(1, (kTargetWGs + g.n_rb[side] - 1) / g.n_rb[side]);
+    int64_t want = std::max<int64_t>(1, (4 * (int64_t)cus + g.n_rb[side] - 1) / g.n_rb[side]);
     want = std::min(want, tiles);
     g.split[side] = (tiles + want - 1) / want * kGradCols;
     g.n_split[side] = (int)std::max<int64_t>(1, (n_oth + g.split[side] - 1) / g.split[side]);
@@ -818,13 +844,13 @@ GradPlan grad_plan(const pw_expr &e, int consumer, int64_t C) {
     part = std::max(part, (size_t)g.n_split[side] * (size_t)n_own * (size_t)g.W[side] * es);
     const int mrows = mfma_grad_rows();
     g.m_n_rb[side] = (int)std::max<int64_t>(1, (n_own + mrows - 1) / mrows);
-    int64_t mwant = std::max<int64_t>(1, (2 * kTargetCUs + g.m_n_rb[side] - 1) / g.m_n_rb[side]);
+    int64_t mwant = std::max<int64_t>(1, (2 * (int64_t)cus + g.m_n_rb[side] - 1) / g.m_n_rb[side]);
     mwant = std::min(mwant, tiles);
     g.m_split[side] = (tiles + mwant - 1) / mwant * kGradCols;
     g.m_n_split[side] = (int)std::max<int64_t>(1, (n_oth + g.m_split[side] - 1) / g.m_split[side]);
     if (e.band) {  // paired blocks: a pair's band tiles are dealt to the splits
       g.m_pairs[side] = (g.m_n_rb[side] + 1) / 2;
-      const int64_t pw_ = std::max<int64_t>(1, (2 * kTargetCUs + g.m_pairs[side] - 1) / g.m_pairs[side]);
+      const int64_t pw_ = std::max<int64_t>(1, (2 * (int64_t)cus + g.m_pairs[side] - 1) / g.m_pairs[side]);
       g.m_n_split[side] = (int)std::max<int64_t>(1, std::min<int64_t>(pw_, 2 * tiles / 4));
     }
     part = std::max(part, (size_t)g.m_n_split[side] * (size_t)n_own * (size_t)g.W[side] * es);

@@ -138,12 +138,22 @@ struct TopkKeyBytes<double> { static constexpr int value = 16; };
 struct ValuConfig {
   int dtile;
   int vtile;
-  int rows = 1;  // rows per thread (2: the blocked float kernel product)
+  int rows = 1;  // rows per thread (kProdRows: the blocked float kernel product; 2: the
+                 // blocked float row minimum and log-sum-exp)
 };
 template <class T, int METRIC>
 hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s);
 constexpr int kValuBM = 256;  // rows per workgroup (one per thread)
 constexpr int kValuBN = 64;   // columns per staged tile
+// The plain float kernel product of narrow points: rows per thread, and
+// columns per staged tile (one per thread).
+constexpr int kProdRows = 4;
+constexpr int kProdBN = kValuBM;
+// Workgroups per compute unit the planner aims the product at: many short
+// workgroups (about 16 per CU, four resident at a time) let the dispatcher
+// even out the CUs' finishing times (measured 0.80 ms against 0.89 ms with
+// four per CU at 65536 x 65536).
+constexpr int kProdWGsPerCU = 16;
 
 // MFMA tile engine: D >= 16, op chains of at most one row-affine stage.
 //   dp: feature tile 16 / 32 / 64; cp: value tile (float 32 / 64, double

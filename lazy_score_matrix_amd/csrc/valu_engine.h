@@ -514,70 +514,177 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
 }
 
 // The plain float kernel product (no score arithmetic, no masks, D <= 4,
-// C <= 4) with two rows per thread: every broadcast read of a column, which
-// costs the LDS its full width, serves two rows' pairs. Rows i and i + 256
-// of a 512-row block; columns past the tile's end are staged as zeros, so
-// their value rows add nothing.
-template <int METRIC, int DT, int VT>
-__global__ __launch_bounds__(kValuBM) void valu_tile_r2(const TileArgs a) {
-  constexpr int BN = kValuBN, R = 2;
-  __shared__ float sY[BN][DT];
-  __shared__ float sV[BN][VT];
+// C <= 4) with R rows per thread: every broadcast read of a column, which
+// costs the LDS its full width, serves R rows' pairs. Thread t owns rows
+// t, t + 256, ... of an R * 256-row block. Column tiles of 256 (one column
+// per thread) are loaded one tile ahead into registers and double-buffered
+// in LDS, one barrier per tile. Columns past the split's end are staged as
+// zeros, so their value rows add nothing.
+//
+// rbf scores are exponentials of base 2 of points pre-scaled by
+// sqrt(gamma log2 e), so exp(-gamma |x - y|^2) = 2^-|x~ - y~|^2. Where every
+// row of a wave and every column of the tile has |x~|^2, |y~|^2 <= 64, the
+// exponent is formed by the norm expansion with the row's own term left
+// out, t = 2 x~.y~ - |y~|^2 (three FMAs from a staged (y~, -|y~|^2)), and
+// the row factor 2^-|x~|^2 multiplies the finished sums; t <= |x~|^2 <= 64,
+// so no term overflows. Elsewhere (points far from the origin, where the
+// expansion would cancel) the pair takes the direct form, its exponent
+// started at the row's deferred |x~|^2 when the wave defers it (else at 0),
+// so identical points still score exactly 1 there.
+constexpr float kExpansionBound = 64.f;
+
+template <int METRIC, int DT, int R>
+__global__ __launch_bounds__(kValuBM) void valu_prod_rn(const TileArgs a) {
+  constexpr int BN = kValuBM;  // columns per tile: one staged per thread
+  static_assert(DT == 3 || DT == 4, "narrow points only");
+  constexpr bool RBF = METRIC == M_RBF;
+  __shared__ float4 sY[2][BN];  // (y0, y1, y2, -|y~|^2) for DT = 3, else (y0..y3)
+  __shared__ float sW[2][DT == 4 ? BN : 1];  // -|y~|^2 for DT = 4
+  __shared__ float4 sV[2][BN];
+  __shared__ int sFar[2];  // tile index whose staging met a column with |y~|^2 > bound
   const int tid = threadIdx.x;
   const int rb = blockIdx.x % a.n_rb;
   const int sp = blockIdx.x / a.n_rb;
   const int64_t jb = wave_uniform((int64_t)sp * a.split_cols);
   const int64_t je = wave_uniform(min(a.M, jb + a.split_cols));
-  constexpr bool PRE = METRIC == M_RBF;
-  const float pre_s = PRE ? (float)sqrt(a.gamma * kLog2e) : 1.f;
-  const float neg_gamma = (float)(-a.gamma * kLog2e);
+  const int n_tiles = (int)((je - jb + BN - 1) / BN);
+  const float pre_s = RBF ? (float)sqrt(a.gamma * kLog2e) : 1.f;
+
+  // Row operand: 2 x~ for rbf (the expansion's factor; x~ = half of it,
+  // exactly), else x itself. One copy keeps the register count at five
+  // waves per SIMD.
   int64_t i[R];
-  bool rv[R];
-  float x[R][DT], acc[R][VT];
+  float xr[R][DT], acc[R][4], x0[R];
+  bool near_all = true;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    i[u] = (int64_t)rb * (R * kValuBM) + u * kValuBM + tid;
-    rv[u] = i[u] < a.N;
+    i[u] = (int64_t)rb * (R * BN) + u * BN + tid;
+    const bool rv = i[u] < a.N;
+    float n2 = 0.f;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+    for (int d = 0; d < DT; ++d) {
+      const float xv = (rv && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+      xr[u][d] = RBF ? 2.f * xv : xv;
+      n2 = fmaf(xv, xv, n2);
+    }
+    x0[u] = n2;  // deferred row term |x~|^2 (rbf)
+    near_all = near_all && n2 <= kExpansionBound;
 #pragma unroll
-    for (int c = 0; c < VT; ++c) acc[u][c] = 0.f;
+    for (int c = 0; c < 4; ++c) acc[u][c] = 0.f;
   }
-  for (int64_t j0 = jb; j0 < je; j0 += BN) {
-    const int nb = (int)min((int64_t)BN, je - j0);
-    __syncthreads();
-    for (int e = tid; e < BN * DT; e += kValuBM) {
-      const int jj = e / DT, d = e % DT;
-      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+  // The wave defers the row factor only if no row can overflow.
+  const bool defer = RBF && __all(near_all);
+  if (!defer) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) x0[u] = 0.f;
+  }
+
+  // Staging registers: this thread's column of the next tile.
+  float ry[DT], rv4[4];
+  auto fetch = [&](int t) {
+    const int64_t j = jb + (int64_t)t * BN + tid;
+    const bool cv = j < je;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) ry[d] = (cv && d < a.D) ? ldg<float>(a.Y, j * a.ldy + d) : 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rv4[c] = (cv && c < a.C) ? ldg<float>(a.V, j * a.ldv + c) : 0.f;
+  };
+  auto stage = [&](int t) {
+    const int b = t & 1;
+    float y[4] = {0.f, 0.f, 0.f, 0.f}, n2 = 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      y[d] = ry[d] * pre_s;
+      n2 = fmaf(y[d], y[d], n2);
     }
-    for (int e = tid; e < BN * VT; e += kValuBM) {
-      const int jj = e / VT, c = e % VT;
-      sV[jj][c] = (jj < nb && c < a.C) ? ldg<float>(a.V, (j0 + jj) * a.ldv + c) : 0.f;
-    }
-    __syncthreads();
+    if constexpr (DT == 3) y[3] = -n2;
+    else sW[b][tid] = -n2;
+    sY[b][tid] = make_float4(y[0], y[1], y[2], y[3]);
+    sV[b][tid] = make_float4(rv4[0], rv4[1], rv4[2], rv4[3]);
+    if (RBF && n2 > kExpansionBound) sFar[b] = t;
+  };
+
+  if (tid < 2) sFar[tid] = -1;
+  __syncthreads();
+  if (n_tiles > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < n_tiles) fetch(t + 1);
+    const float4 *Yb = sY[b];
+    const float4 *Vb = sV[b];
+    if (RBF && defer && sFar[b] != t) {
+      // Norm expansion, row factor deferred.
 #pragma unroll 4
-    for (int jj = 0; jj < BN; ++jj) {
+      for (int jj = 0; jj < BN; ++jj) {
+        const float4 y = Yb[jj];
+        const float4 v = Vb[jj];
+        const float w = DT == 3 ? y.w : sW[b][jj];
 #pragma unroll
-      for (int u = 0; u < R; ++u) {
-        const float sc = valu_metric<METRIC, float, DT, PRE>(x[u], sY[jj], neg_gamma);
+        for (int u = 0; u < R; ++u) {
+          float e = fmaf(xr[u][0], y.x, w);
+          e = fmaf(xr[u][1], y.y, e);
+          e = fmaf(xr[u][2], y.z, e);
+          if constexpr (DT == 4) e = fmaf(xr[u][3], y.w, e);
+          const float k = __builtin_amdgcn_exp2f(e);
+          acc[u][0] = fmaf(k, v.x, acc[u][0]);
+          acc[u][1] = fmaf(k, v.y, acc[u][1]);
+          acc[u][2] = fmaf(k, v.z, acc[u][2]);
+          acc[u][3] = fmaf(k, v.w, acc[u][3]);
+        }
+      }
+    } else {
+      // Direct form.
+#pragma unroll 2
+      for (int jj = 0; jj < BN; ++jj) {
+        const float4 y = Yb[jj];
+        const float4 v = Vb[jj];
+        const float yy[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-        for (int c = 0; c < VT; ++c) acc[u][c] = fma(sc, sV[jj][c], acc[u][c]);
+        for (int u = 0; u < R; ++u) {
+          float sc;
+          if constexpr (METRIC == M_LINEAR) {
+            sc = xr[u][0] * yy[0];
+#pragma unroll
+            for (int d = 1; d < DT; ++d) sc = fmaf(xr[u][d], yy[d], sc);
+          } else {
+            float e = x0[u];
+#pragma unroll
+            for (int d = 0; d < DT; ++d) {
+              const float df = RBF ? fmaf(xr[u][d], 0.5f, -yy[d]) : xr[u][d] - yy[d];
+              e = fmaf(-df, df, e);
+            }
+            sc = RBF ? __builtin_amdgcn_exp2f(e) : -e;
+          }
+          acc[u][0] = fmaf(sc, v.x, acc[u][0]);
+          acc[u][1] = fmaf(sc, v.y, acc[u][1]);
+          acc[u][2] = fmaf(sc, v.z, acc[u][2]);
+          acc[u][3] = fmaf(sc, v.w, acc[u][3]);
+        }
       }
     }
+    if (t + 1 < n_tiles) stage(t + 1);
+    __syncthreads();
   }
   const bool fin = a.n_split == 1;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    if (!rv[u]) continue;
-    float *o = fin ? static_cast<float *>(a.out) + i[u] * a.ldo : static_cast<float *>(a.partial) + ((int64_t)sp * a.N + i[u]) * a.C;
+    if (i[u] >= a.N) continue;
+    const float f = (RBF && defer) ? __builtin_amdgcn_exp2f(-x0[u]) : 1.f;
+    float *o = fin ? static_cast<float *>(a.out) + i[u] * a.ldo
+                   : static_cast<float *>(a.partial) + ((int64_t)sp * a.N + i[u]) * a.C;
 #pragma unroll
-    for (int c = 0; c < VT; ++c)
-      if (c < a.C) o[c] = acc[u][c];
+    for (int c = 0; c < 4; ++c)
+      if (c < a.C) o[c] = acc[u][c] * f;
   }
 }
 
 // The plain float row minimum (or maximum) with its column, two rows per
-// thread as in valu_tile_r2. Columns reach a thread in increasing order and
+// thread (rows i and i + 256 of a 512-row block, 64-column tiles). Columns
+// reach a thread in increasing order and
 // a candidate must be strictly better, so the lowest index wins a tie.
 template <int METRIC, int DT, bool LARGEST>
 __device__ __forceinline__ void r2_min_tile(const float (&x)[2][DT], const float (*sY)[DT], int n, float neg_gamma,
@@ -806,13 +913,17 @@ hipError_t valu_by_consumer(int consumer, int vt, const TileArgs &a, hipStream_t
 template <class T, int METRIC>
 hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArgs &a, hipStream_t s) {
   if constexpr (sizeof(T) == 4 && METRIC != M_COSINE) {
+    if (consumer == C_MATMUL && cfg.rows == kProdRows) {
+      if ((cfg.dtile != 3 && cfg.dtile != 4) || cfg.vtile != 4) return hipErrorInvalidValue;
+      dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
+      if (cfg.dtile == 3) hipLaunchKernelGGL((valu_prod_rn<METRIC, 3, kProdRows>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((valu_prod_rn<METRIC, 4, kProdRows>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
     if (cfg.rows == 2) {
       if (cfg.dtile != 3 && cfg.dtile != 4) return hipErrorInvalidValue;
       dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
-      if (consumer == C_MATMUL && cfg.vtile == 4) {
-        if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2<METRIC, 3, 4>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((valu_tile_r2<METRIC, 4, 4>), grid, block, 0, s, a);
-      } else if (consumer == C_LOGSUMEXP) {
+      if (consumer == C_LOGSUMEXP) {
         if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2_lse<METRIC, 3>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((valu_tile_r2_lse<METRIC, 4>), grid, block, 0, s, a);
       } else if (consumer == C_TOPK && cfg.vtile == 1 && a.k == 1) {

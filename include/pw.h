@@ -46,7 +46,8 @@ typedef enum {
   PW_ERR_INVALID = -1,     /* null pointer, bad enum, bad size or stride, k > M, ... */
   PW_ERR_UNSUPPORTED = -2, /* valid request outside the fused range (D not in 1..64, k > 64, > PW_MAX_OPS ops) */
   PW_ERR_WORKSPACE = -3,   /* workspace missing or smaller than pw_workspace_size reports */
-  PW_ERR_HIP = -4          /* a HIP runtime error was reported while enqueueing */
+  PW_ERR_HIP = -4,         /* a HIP runtime error was reported while enqueueing */
+  PW_ERR_SCRATCH = -5      /* pw_topk_noalloc: the call needs more workspace than its static buffer */
 } pw_status;
 
 typedef enum { PW_F32 = 0, PW_F64 = 1 } pw_dtype;
@@ -202,6 +203,20 @@ int pw_softmax_matmul_lse(const pw_expr *e, const void *V, int64_t C, int64_t ld
  * NaN scores are unsupported. */
 int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices, void *ws, size_t ws_bytes,
             void *stream);
+
+/* Row top-k as pw_topk, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same plan and kernels, with the workspace taken from a
+ * static device buffer of PW_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends. The caller passes inputs
+ * and outputs as for pw_topk; the stream must belong to the current device.
+ * Calls that need more workspace than the buffer holds (pw_workspace_size
+ * of PW_C_TOPK above PW_NOALLOC_SCRATCH_BYTES) return PW_ERR_SCRATCH before
+ * any device work. Every call on one GPU shares that GPU's buffer: calls
+ * that overlap on one GPU (two streams, two host threads) race; calls in
+ * stream order do not. Allocates nothing, ever. */
+#define PW_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pw_topk_noalloc(const pw_expr *e, int k, int largest, void *values, int64_t *indices, void *stream);
 
 /* ------------------------------------------------------------------------
  * Backward by replay (guide, opening section: the consumer's backward

@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpw.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pw.h")
 
-PW_OK, PW_ERR_INVALID, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP = 0, -1, -2, -3, -4
+PW_OK, PW_ERR_INVALID, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP, PW_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 DTYPES = {torch.float32: 0, torch.float64: 1}
 METRICS = {"linear": 0, "sqeuclidean": 1, "rbf": 2, "cosine_distances": 3, "cosine": 3}
 OPS = {"mul": 0, "add": 1, "add_rows": 2, "add_columns": 3, "weight_rows": 4, "weight_columns": 5, "exp": 6,
@@ -99,6 +99,7 @@ def load_library(path: str = LIB_PATH):
         lib.pw_displacement.argtypes = [vp, vp, i64, vp, sz, vp]
         lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
+        lib.pw_topk_noalloc.argtypes = [vp, c_int, c_int, vp, vp, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
         lib.pw_backward_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
         lib.pw_backward_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
@@ -327,6 +328,18 @@ class LazyScores:
         ws, nb = self._ws(workspace, "topk", 0, k)
         check(self._lib.pw_topk(self._h, int(k), int(bool(largest)), values.data_ptr(), indices.data_ptr(),
                                 ws.data_ptr(), nb, _stream(self.device)), "pw_topk")
+        return values, indices
+
+    def topk_noalloc(self, k: int, largest: bool, values: torch.Tensor, indices: torch.Tensor):
+        """topk into the caller's values [N, k] and int64 indices [N, k]
+        through pw_topk_noalloc: no workspace, no allocation (the library's
+        static device buffer serves instead; calls on one GPU must not
+        overlap)."""
+        if values.shape != (self.N, k) or indices.shape != (self.N, k) or not values.is_contiguous() or \
+                not indices.is_contiguous() or values.dtype != self.dtype or indices.dtype != torch.int64:
+            raise ValueError("values and indices must be contiguous [N, k] tensors of the bound dtype and int64")
+        check(self._lib.pw_topk_noalloc(self._h, int(k), int(bool(largest)), values.data_ptr(), indices.data_ptr(),
+                                        _stream(self.device)), "pw_topk_noalloc")
         return values, indices
 
     # -- backward -------------------------------------------------------

@@ -530,6 +530,7 @@ const char *pw_error_string(int code) {
     case PW_ERR_UNSUPPORTED: return "unsupported: outside the fused range";
     case PW_ERR_WORKSPACE: return "workspace missing or too small";
     case PW_ERR_HIP: return "HIP runtime error";
+    case PW_ERR_SCRATCH: return "needs more workspace than the static buffer of pw_topk_noalloc holds";
     default: return "unknown status";
   }
 }

@@ -256,3 +256,50 @@ def test_cg_solve_validation(lib):
     ok, h3 = bind(lib, N=0, M=0, X=0, Y=0)  # empty system: converged, nothing launched
     assert call(handle=h3, B=0, A=0) == pw.PW_OK and info.converged == 1 and info.iterations == 0
     lib.pw_release(h3)
+
+
+def _plan(lib, consumer, C=0, k=0, **kw):
+    rc, h = bind(lib, **kw)
+    assert rc == pw.PW_OK
+    buf = ctypes.create_string_buffer(512)
+    assert lib.pw_plan_describe(h, consumer, C, k, buf, 512) == pw.PW_OK
+    lib.pw_release(h)
+    return dict(t.split("=", 1) for t in buf.value.decode().split() if "=" in t)
+
+
+def test_blocked_vector_kernels_only_where_they_apply(lib):
+    """The several-rows-per-thread vector kernels cover plain float scores of
+    narrow points only: the kernel product (four rows, 256-column tiles),
+    the row log-sum-exp under at most one row-only stage and the row
+    minimum (two rows). Score arithmetic they do not take, masks, cosine
+    and float64 plan one row per thread."""
+    MATMUL, LSE, TOPK = 0, 2, 4
+    N, M = 4100, 3000
+    for metric in (0, 1, 2):
+        p = _plan(lib, MATMUL, 4, N=N, M=M, D=3, metric=metric)
+        assert (p["family"], p["rows"], p["bm"], p["bn"]) == ("valu", "4", "1024", "256"), p
+        assert _plan(lib, LSE, N=N, M=M, D=4, metric=metric)["rows"] == "2"
+        assert _plan(lib, TOPK, 0, 1, N=N, M=M, D=2, metric=metric)["rows"] == "2"
+    mul = [(pw.OPS["mul"], -0.5, None)]
+    addr = [(pw.OPS["mul"], -0.5, None), (pw.OPS["add_rows"], 0.0, FAKE)]
+    addc = [(pw.OPS["add_columns"], 0.0, FAKE)]
+    maskc = [(pw.OPS["mask_columns"], 0.0, FAKE)]
+    causal = [(pw.OPS["band_upper"], 0.0, None)]
+    assert _plan(lib, LSE, N=N, M=M, D=3, ops=mul)["rows"] == "2"
+    assert _plan(lib, LSE, N=N, M=M, D=3, ops=addr)["rows"] == "2"
+    one_row = [
+        _plan(lib, MATMUL, 5, N=N, M=M, D=3),                 # value width above 4
+        _plan(lib, MATMUL, 4, N=N, M=M, D=5),                 # five features
+        _plan(lib, MATMUL, 4, N=N, M=M, D=3, metric=3),       # cosine
+        _plan(lib, MATMUL, 4, N=N, M=M, D=3, dtype=1),        # float64
+        _plan(lib, MATMUL, 4, N=N, M=M, D=3, ops=mul),        # score arithmetic
+        _plan(lib, MATMUL, 4, N=N, M=M, D=3, ops=maskc),      # a column mask
+        _plan(lib, LSE, N=N, M=M, D=3, ops=addc),             # a column stage
+        _plan(lib, LSE, N=N, M=M, D=3, ops=causal),           # a pair mask
+        _plan(lib, LSE, N=N, M=M, D=3, dtype=1),              # float64
+        _plan(lib, TOPK, 0, 2, N=N, M=M, D=3),                # k = 2
+        _plan(lib, TOPK, 0, 1, N=N, M=M, D=3, ops=maskc),     # a column mask
+        _plan(lib, TOPK, 0, 1, N=N, M=M, D=3, metric=3),      # cosine
+    ]
+    for p in one_row:
+        assert p["family"] == "valu" and p["rows"] == "1", p

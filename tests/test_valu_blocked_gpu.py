@@ -1,0 +1,104 @@
+"""The blocked vector kernels against the oracle, each test first asserting
+that the planner picked the kernel it means to cover:
+  * the narrow kernel product (four rows per thread, 256-column tiles; rbf by
+    the norm expansion with the row factor deferred, and its direct-form
+    fallbacks for points far from the origin);
+  * the two-rows row log-sum-exp (no stage, a scalar stage, a row-vector
+    stage; with and without the self pair);
+  * the two-rows row minimum / maximum with exact ties (lowest index wins).
+Sizes span several row blocks (1024 rows for the product, 512 for the
+two-rows kernels) with a ragged last block, and a ragged last column tile.
+"""
+import numpy as np
+import pytest
+
+from gpu_cases import bind_both, check_consumer, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _field(plan, key):
+    for tok in plan.split():
+        k, _, v = tok.partition("=")
+        if k == key:
+            return v
+    raise AssertionError("%s not in plan %r" % (key, plan))
+
+
+PROD = [(m, d, c) for m in ("linear", "sqeuclidean", "rbf") for d in (1, 2, 3, 4) for c in (1, 2, 4)]
+
+
+@pytest.mark.parametrize("metric,D,C", PROD, ids=["%s-D%d-C%d" % p for p in PROD])
+def test_narrow_product(metric, D, C):
+    r = np.random.default_rng(100 + 10 * D + C)
+    X = r.standard_normal((2100, D)).astype(np.float32)
+    Y = r.standard_normal((1333, D)).astype(np.float32)
+    V = r.standard_normal((1333, C)).astype(np.float32)
+    e, oe = bind_both(X, Y, metric, gamma=0.5)
+    plan = e.plan("matmul", C)
+    assert _field(plan, "family") == "valu" and _field(plan, "rows") == "4" and _field(plan, "bn") == "256", plan
+    check_consumer(e, oe, "matmul", V=V, what="narrow product %s D%d C%d" % (metric, D, C))
+
+
+@pytest.mark.parametrize("D", (2, 3, 4))
+def test_narrow_product_rbf_far_points(D):
+    """A row far from the origin keeps its wave in the direct form (row
+    factor not deferred); a far column sends its tile to the direct form
+    with the factor deferred; an exact copy of a far row scores 1."""
+    r = np.random.default_rng(200 + D)
+    X = r.standard_normal((2100, D)).astype(np.float32)
+    Y = r.standard_normal((1333, D)).astype(np.float32)
+    X[5] *= 30.0            # wave 0 of row block 0
+    X[1024 + 300] *= 30.0   # a wave of row block 1
+    Y[300] *= 30.0          # column tile 1
+    Y[1300] = X[5]          # exact copy of a far row, last (ragged) tile
+    V = np.concatenate([r.standard_normal((1333, 3)), np.ones((1333, 1))], 1).astype(np.float32)
+    e, oe = bind_both(X, Y, "rbf", gamma=0.5)
+    assert _field(e.plan("matmul", 4), "rows") == "4"
+    check_consumer(e, oe, "matmul", V=V, what="rbf far points D%d" % D)
+    onehot = np.zeros((1333, 1), np.float32)
+    onehot[1300] = 1.0
+    g = e.matmul(to_dev(onehot)).cpu().numpy()
+    assert g[5, 0] == 1.0, "an exact copy of a far point must score exactly 1 (got %r)" % g[5, 0]
+
+
+LSE_CHAINS = {
+    "none": lambda n, r: [],
+    "mul": lambda n, r: [("mul", -0.5)],
+    "rowvec": lambda n, r: [("mul", -0.5), ("add_rows", r.standard_normal(n).astype(np.float32)),
+                            ("weight_rows", (0.5 + r.random(n)).astype(np.float32))],
+}
+LSE = [(m, d, ch, ex) for m in ("linear", "sqeuclidean", "rbf") for d in (1, 3, 4) for ch in LSE_CHAINS
+       for ex in (False, True)]
+
+
+@pytest.mark.parametrize("metric,D,chain,excl", LSE, ids=["%s-D%d-%s-%s" % (a, b, c, "excl" if x else "all")
+                                                          for a, b, c, x in LSE])
+def test_two_rows_logsumexp(metric, D, chain, excl):
+    r = np.random.default_rng(300 + D)
+    N = 1100
+    M = 1100 if excl else 333
+    X = r.standard_normal((N, D)).astype(np.float32)
+    Y = X if excl else r.standard_normal((M, D)).astype(np.float32)
+    ops = LSE_CHAINS[chain](N, r)
+    e, oe = bind_both(X, Y, metric, gamma=0.5, ops=ops, same=excl)
+    plan = e.plan("logsumexp")
+    assert _field(plan, "family") == "valu" and _field(plan, "rows") == "2", plan
+    check_consumer(e, oe, "logsumexp", exclude_self=excl, what="two-rows lse %s D%d %s" % (metric, D, chain))
+
+
+MINS = [(d, lg) for d in (1, 2, 3, 4) for lg in (False, True)]
+
+
+@pytest.mark.parametrize("D,largest", MINS, ids=["D%d-%s" % (d, "max" if lg else "min") for d, lg in MINS])
+def test_two_rows_min_exact_ties(D, largest):
+    """Integer points: every squared distance is exact and ties abound;
+    the returned index must be the lowest among equal values, bit for bit,
+    on rows of every row block (i and i + 256 of each 512-row block)."""
+    r = np.random.default_rng(400 + D)
+    X = r.integers(-3, 4, (1100, D)).astype(np.float32)
+    Y = r.integers(-3, 4, (333, D)).astype(np.float32)
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    plan = e.plan("topk", 0, 1)
+    assert _field(plan, "family") == "valu" and _field(plan, "rows") == "2", plan
+    check_consumer(e, oe, "topk", k=1, largest=largest, exact=True, what="two-rows min D%d" % D)

@@ -337,9 +337,9 @@ def backward(e: Expr, consumer, G, V=None, exclude_self=False, indices=None, row
     gradients through the selected pairs only), per pair from the chain rule
     (see oracle.cpp). Row-side results (dX, row-op grads) for `rows`,
     column-side results (dY, dV, column-op grads) for `cols` (all by
-    default). Returns a dict of arrays and their absolute-term scales:
-    dX, dY, dV, and "ops": per op its grad (rows or columns, None for a
-    scalar op), each as (value, mag)."""
+    default). Returns a dict of arrays with their first-order error
+    magnitudes (see oracle.cpp): dX, dY, dV, and "ops": per op its grad
+    (rows or columns, None for a scalar op), each as (value, mag)."""
     lib = _load()
     code = CONSUMER_CODES[consumer]
     G = np.ascontiguousarray(np.asarray(G, dtype=e.np_dtype))

@@ -413,8 +413,26 @@ void do_topk(const oracle_expr &ex, int kk, int largest, const int64_t *rows, in
 // Masked and excluded pairs contribute nothing. Row-side outputs (dX, row
 // op vectors) are returned for a list of rows, column-side outputs (dY,
 // dV, column op vectors) for a list of columns; each is computed over all
-// pairs it depends on. `mag` arrays hold the same sums taken over absolute
-// values of every term (the scale of their rounding).
+// pairs it depends on.
+//
+// `mag` arrays hold each gradient's first-order error magnitude, formed as
+// the forward `mag` is: every term contributes its absolute value plus the
+// first-order change it takes under unit roundoff in its inputs, with
+// mu_k the forward magnitude of t_k and lm_i = max_j mu_ij + log(l_i) that
+// of the row's log-sum-exp (the forward log-sum-exp magnitude):
+//   dS magnitude  matmul        sum_c |G_ic V_jc|
+//                 displacement  sum_d |G_id| (|y_jd| + |x_id|)
+//                 logsumexp     |g_i| P (1 + mu + lm_i)
+//                 softmax@V     P ((1 + mu + lm_i) |G_i.V_j - D_i| + sum_c |G_ic V_jc| + dm_i),
+//                               dm_i = sum_j P_ij ((mu_ij + lm_i) |G_i.V_j| + sum_c |G_ic V_jc|)
+//                 top-k         |G| at the selected pairs
+//   direct terms  s G: (|s| + mu)|G|;  P G: P (1 + mu + lm_i) |G|
+//   ops           MUL c: |c| dm; a weight's gradient d t_k: dm |t_k| + |d| mu_k;
+//                 EXP: dm e^t + |d| e^t (1 + mu_k)
+//   metric grad   linear |y| (|x|); sqeuclidean 2 (|x| + |y|);
+//                 rbf 2 gamma (f + mu_f) (|x| + |y|);
+//                 cosine 3 (|y| / (|x||y|) + sum|x y| |x| / (|x|^3 |y|))
+//   and each pair adds dm |df| + |d| (that metric-gradient magnitude).
 template <class T>
 struct Backward {
   using R = RealOf<T>;
@@ -429,6 +447,7 @@ struct Backward {
   const int64_t *idx;
   int k;
   std::vector<R> lse, delta;  // per row, for logsumexp / softmax
+  std::vector<R> lm, dmag;    // their first-order magnitudes
 
   Backward(const oracle_expr &e_, int cons, const T *G_, int64_t ldg_, const T *V_, int64_t C_, int64_t ldv_,
            int excl, const int64_t *idx_, int k_)
@@ -455,11 +474,12 @@ struct Backward {
   // Per-row log-sum-exp and, for softmax, Delta_i = sum_j P_ij G_i.V_j
   // (two passes over the row, as the forward oracle does).
   void row_stats(int64_t i) {
-    R m = -std::numeric_limits<R>::infinity();
+    R m = -std::numeric_limits<R>::infinity(), mumax = 0;
     for (int64_t j = 0; j < ex.M; ++j) {
       if (!kept(i, j)) continue;
       R mu;
       m = std::max(m, E.score(i, j, &mu));
+      mumax = std::max(mumax, mu);
     }
     R l = 0, d = 0;
     if (m != -std::numeric_limits<R>::infinity()) {
@@ -473,40 +493,56 @@ struct Backward {
     }
     lse[i] = l > 0 ? m + rlog(l) : -std::numeric_limits<R>::infinity();
     delta[i] = l > 0 ? d / l : 0;
+    lm[i] = l > 0 ? mumax + rlog(l) : 0;
+    // Magnitude of delta_i = sum_j P_ij G_i.V_j (second pass: needs lm_i).
+    R dm = 0;
+    if (consumer == 3 && l > 0) {
+      for (int64_t j = 0; j < ex.M; ++j) {
+        if (!kept(i, j)) continue;
+        R mu;
+        R p = rexp(E.score(i, j, &mu) - lse[i]);
+        dm += p * ((mu + lm[i]) * std::fabs(gv(i, j)) + gv_abs(i, j));
+      }
+    }
+    dmag[i] = dm;
   }
   void all_row_stats() {
     if (consumer != 2 && consumer != 3) return;
     lse.assign(ex.N, 0);
     delta.assign(ex.N, 0);
+    lm.assign(ex.N, 0);
+    dmag.assign(ex.N, 0);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t i = 0; i < ex.N; ++i) row_stats(i);
   }
 
-  // Forward values t_0..t_n of pair (i, j).
-  void forward(int64_t i, int64_t j, R *t) const {
-    R mu;
+  // Forward values t_0..t_n of pair (i, j) and their magnitudes mu_0..mu_n
+  // (propagated as the forward score's magnitude is).
+  void forward(int64_t i, int64_t j, R *t, R *mu) const {
     // The metric alone: score() with the ops applied is replayed below.
     oracle_expr bare = ex;
     bare.n_ops = 0;
     Expr<T, R> B(bare);
-    t[0] = B.score(i, j, &mu);
+    t[0] = B.score(i, j, &mu[0]);
     for (int op = 0; op < ex.n_ops; ++op) {
-      R x = t[op];
+      R x = t[op], m = mu[op];
       switch (ex.op_kind[op]) {
-        case OP_MUL: x = (R)ex.op_scalar[op] * x; break;
-        case OP_ADD: x = x + (R)ex.op_scalar[op]; break;
-        case OP_ADD_ROWS: x = x + E.vec(op, i); break;
-        case OP_ADD_COLS: x = x + E.vec(op, j); break;
-        case OP_MUL_ROWS: x = E.vec(op, i) * x; break;
-        case OP_MUL_COLS: x = E.vec(op, j) * x; break;
-        case OP_EXP: x = rexp(x); break;
+        case OP_MUL: x = (R)ex.op_scalar[op] * x; m = std::fabs((R)ex.op_scalar[op]) * m; break;
+        case OP_ADD: x = x + (R)ex.op_scalar[op]; m = m + std::fabs(x); break;
+        case OP_ADD_ROWS: x = x + E.vec(op, i); m = m + std::fabs(x); break;
+        case OP_ADD_COLS: x = x + E.vec(op, j); m = m + std::fabs(x); break;
+        case OP_MUL_ROWS: m = std::fabs(E.vec(op, i)) * m; x = E.vec(op, i) * x; break;
+        case OP_MUL_COLS: m = std::fabs(E.vec(op, j)) * m; x = E.vec(op, j) * x; break;
+        case OP_EXP: x = rexp(x); m = x * (1 + m); break;
       }
       t[op + 1] = x;
+      mu[op + 1] = m;
     }
   }
 
-  // Upstream dS of pair (i, j) (and its absolute-term scale), given s.
-  R dS(int64_t i, int64_t j, R s, R *scale) const {
+  // Upstream dS of pair (i, j) and its magnitude, given s and its
+  // magnitude mu.
+  R dS(int64_t i, int64_t j, R s, R mu, R *scale) const {
     switch (consumer) {
       case 0: *scale = gv_abs(i, j); return gv(i, j);
       case 1: {
@@ -521,13 +557,14 @@ struct Backward {
       }
       case 2: {
         R p = rexp(s - lse[i]);
-        *scale = std::fabs((R)G[i * ldg]) * p;
+        *scale = std::fabs((R)G[i * ldg]) * p * (1 + mu + lm[i]);
         return (R)G[i * ldg] * p;
       }
       case 3: {
         R p = rexp(s - lse[i]);
-        *scale = p * (gv_abs(i, j) + std::fabs(delta[i]));
-        return p * (gv(i, j) - delta[i]);
+        R a = gv(i, j) - delta[i];
+        *scale = p * ((1 + mu + lm[i]) * std::fabs(a) + gv_abs(i, j) + dmag[i]);
+        return p * a;
       }
       default: {  // top-k: the selected positions of row i equal to j
         R a = 0;
@@ -539,15 +576,23 @@ struct Backward {
     }
   }
 
-  // df/dx_i (side 0) or df/dy_j (side 1) in out[D], given f = t[0].
-  void metric_grad(int64_t i, int64_t j, R f, int side, R *out) const {
+  // df/dx_i (side 0) or df/dy_j (side 1) in out[D] and its magnitude in
+  // mag[D], given f = t[0] and its magnitude muf.
+  void metric_grad(int64_t i, int64_t j, R f, R muf, int side, R *out, R *mag) const {
     const int64_t D = ex.D;
     if (ex.metric == M_LINEAR) {
-      for (int64_t d = 0; d < D; ++d) out[d] = side == 0 ? E.y(j, d) : E.x(i, d);
+      for (int64_t d = 0; d < D; ++d) {
+        out[d] = side == 0 ? E.y(j, d) : E.x(i, d);
+        mag[d] = std::fabs(out[d]);
+      }
     } else if (ex.metric == M_SQEUCLIDEAN || ex.metric == M_RBF) {
       R c = ex.metric == M_SQEUCLIDEAN ? (R)2 : (R)-2 * (R)ex.gamma * f;
+      R cm = ex.metric == M_SQEUCLIDEAN ? (R)2 : (R)2 * (R)ex.gamma * (f + muf);
       if (side == 1) c = -c;
-      for (int64_t d = 0; d < D; ++d) out[d] = c * (E.x(i, d) - E.y(j, d));
+      for (int64_t d = 0; d < D; ++d) {
+        out[d] = c * (E.x(i, d) - E.y(j, d));
+        mag[d] = cm * (std::fabs(E.x(i, d)) + std::fabs(E.y(j, d)));
+      }
     } else {
       R dot = 0, nx = 0, ny = 0;
       for (int64_t d = 0; d < D; ++d) {
@@ -556,13 +601,19 @@ struct Backward {
         ny += E.y(j, d) * E.y(j, d);
       }
       if (!(nx > 0 && ny > 0)) {
-        for (int64_t d = 0; d < D; ++d) out[d] = 0;
+        for (int64_t d = 0; d < D; ++d) out[d] = mag[d] = 0;
         return;
       }
-      R a = std::sqrt(nx), b = std::sqrt(ny);
+      R a = std::sqrt(nx), b = std::sqrt(ny), adot = 0;
+      for (int64_t d = 0; d < D; ++d) adot += std::fabs(E.x(i, d) * E.y(j, d));
       for (int64_t d = 0; d < D; ++d) {
-        if (side == 0) out[d] = -(E.y(j, d) / (a * b) - dot * E.x(i, d) / (a * a * a * b));
-        else out[d] = -(E.x(i, d) / (a * b) - dot * E.y(j, d) / (b * b * b * a));
+        if (side == 0) {
+          out[d] = -(E.y(j, d) / (a * b) - dot * E.x(i, d) / (a * a * a * b));
+          mag[d] = 3 * (std::fabs(E.y(j, d)) / (a * b) + adot * std::fabs(E.x(i, d)) / (a * a * a * b));
+        } else {
+          out[d] = -(E.x(i, d) / (a * b) - dot * E.y(j, d) / (b * b * b * a));
+          mag[d] = 3 * (std::fabs(E.x(i, d)) / (a * b) + adot * std::fabs(E.y(j, d)) / (b * b * b * a));
+        }
       }
     }
   }
@@ -571,30 +622,30 @@ struct Backward {
   // column j for side 1).
   void pair(int64_t i, int64_t j, int side, R *gx, R *gxm, R *gvout, R *gvm, R *gops, R *gopsm) const {
     if (!kept(i, j)) return;
-    R t[17];
-    forward(i, j, t);
+    R t[17], mu[17];
+    forward(i, j, t, mu);
     const int n = ex.n_ops;
     R sc;
-    R d = dS(i, j, t[n], &sc);
+    R d = dS(i, j, t[n], mu[n], &sc);
     R dm = sc;
     // direct terms
     if (side == 1 && consumer == 0)
       for (int64_t c = 0; c < C; ++c) {
         gvout[c] += t[n] * g(i, c);
-        gvm[c] += std::fabs(t[n] * g(i, c));
+        gvm[c] += (std::fabs(t[n]) + mu[n]) * std::fabs(g(i, c));
       }
     if (side == 1 && consumer == 3) {
       R p = rexp(t[n] - lse[i]);
       for (int64_t c = 0; c < C; ++c) {
         gvout[c] += p * g(i, c);
-        gvm[c] += std::fabs(p * g(i, c));
+        gvm[c] += p * (1 + mu[n] + lm[i]) * std::fabs(g(i, c));
       }
     }
     if (consumer == 1)
       for (int64_t dd = 0; dd < ex.D; ++dd) {
         R w = t[n] * g(i, dd);
         gx[dd] += side == 0 ? -w : w;
-        gxm[dd] += std::fabs(w);
+        gxm[dd] += (std::fabs(t[n]) + mu[n]) * std::fabs(g(i, dd));
       }
     // back through the ops
     for (int op = n - 1; op >= 0; --op) {
@@ -609,23 +660,26 @@ struct Backward {
           if (side == 1) { gops[op] += d; gopsm[op] += dm; }
           break;
         case OP_MUL_ROWS:
-          if (side == 0) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]); }
+          if (side == 0) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]) + std::fabs(d) * mu[op]; }
           d = E.vec(op, i) * d;
           dm = std::fabs(E.vec(op, i)) * dm;
           break;
         case OP_MUL_COLS:
-          if (side == 1) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]); }
+          if (side == 1) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]) + std::fabs(d) * mu[op]; }
           d = E.vec(op, j) * d;
           dm = std::fabs(E.vec(op, j)) * dm;
           break;
-        case OP_EXP: d = d * t[op + 1]; dm = dm * t[op + 1]; break;
+        case OP_EXP:
+          dm = dm * t[op + 1] + std::fabs(d) * t[op + 1] * (1 + mu[op]);
+          d = d * t[op + 1];
+          break;
       }
     }
-    R mg[64];
-    metric_grad(i, j, t[0], side, mg);
+    R mg[64], mgm[64];
+    metric_grad(i, j, t[0], mu[0], side, mg, mgm);
     for (int64_t dd = 0; dd < ex.D; ++dd) {
       gx[dd] += d * mg[dd];
-      gxm[dd] += std::fabs(dm * mg[dd]);
+      gxm[dd] += dm * std::fabs(mg[dd]) + std::fabs(d) * mgm[dd];
     }
   }
 };

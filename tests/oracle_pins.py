@@ -1025,4 +1025,103 @@ def pin_rule_topk_ties():
                 "swapped positions %d/%d of row %d accepted (exact=%s)" % (p, p + 1, row, exact)
 
 
+
+# ---------------------------------------------------------------- gradient magnitude pins
+def pin_backward_mag_golden():
+    """Gradients and their first-order magnitudes on hand-derived cases
+    (fixture backward_magnitudes): log-sum-exp, kernel product, softmax@V
+    and an op chain with a weight and exp."""
+    c = _golden()["backward_magnitudes"]
+
+    def vals(x):
+        return [[_ev(v) for v in row] for row in x] if isinstance(x[0], list) else [[_ev(v) for v in x]]
+
+    for dt in DTYPES:
+        X, Y = np.array(c["X"], dt), np.array(c["Y"], dt)
+        e = oracle.Expr(X, Y, c["metric"])
+        for cons in ("logsumexp", "matmul", "softmax_matmul"):
+            cc = c[cons]
+            V = np.array(cc["V"], dt) if "V" in cc else None
+            r = oracle.backward(e, cons, np.array(cc["G"], dt), V=V)
+            for key in ("dX", "dY", "dV"):
+                if key in cc:
+                    _close(r[key][0], vals(cc[key]), rtol=1e-13, atol=1e-15, what="%s %s" % (cons, key))
+                    _close(r[key][1], vals(cc[key + "_mag"]), rtol=1e-13, atol=1e-15, what="%s %s mag" % (cons, key))
+        ch = c["chain"]
+        ops = [(n, np.array(a, dt) if isinstance(a, list) else a) for n, a in ch["ops"]]
+        e = oracle.Expr(np.array(ch["X"], dt), np.array(ch["Y"], dt), c["metric"], ops=ops)
+        r = oracle.backward(e, "matmul", np.array(ch["G"], dt), V=np.array(ch["V"], dt))
+        _close(r["dX"][0], vals(ch["dX"]), rtol=1e-13, what="chain dX")
+        _close(r["dX"][1], vals(ch["dX_mag"]), rtol=1e-13, what="chain dX mag")
+        _close(r["ops"][0][0], [_ev(v) for v in ch["weight_rows"]], rtol=1e-13, what="chain weight grad")
+        _close(r["ops"][0][1], [_ev(v) for v in ch["weight_rows_mag"]], rtol=1e-13, what="chain weight grad mag")
+
+
+def _attention_grads_f32(Q, K, V, G, scale):
+    """dQ, dK, dV of sum(softmax(Q K^T scale) V * G) by torch autograd in
+    float32 (library matmuls, a differently ordered evaluation)."""
+    Qt = torch.tensor(Q, requires_grad=True)
+    Kt = torch.tensor(K, requires_grad=True)
+    Vt = torch.tensor(V, requires_grad=True)
+    O = torch.softmax((Qt @ Kt.T) * scale, -1) @ Vt
+    return torch.autograd.grad((O * torch.from_numpy(G)).sum(), (Qt, Kt, Vt))
+
+
+def pin_grad_rule_accepts_float32_autograd():
+    """The gradient rule accepts float32 gradients taken by torch autograd
+    of the dense form: attention softmax@V, the InfoNCE log-sum-exp without
+    the self pair, and the rbf kernel product of narrow points."""
+    Q, K, V, ops = _attention_case()
+    G = _rng(510).standard_normal((Q.shape[0], V.shape[1])).astype(np.float32)
+    ref = oracle.backward(oracle.Expr(Q, K, "linear", ops=ops), "softmax_matmul", G, V=V)
+    for name, g in zip(("dX", "dY", "dV"), _attention_grads_f32(Q, K, V, G, 0.125)):
+        ok, ratio, _ = parity.grad_rule(g.numpy(), *ref[name], np.float32)
+        assert ok, "attention %s: float32 autograd rejected (err/tol %.3g)" % (name, ratio)
+    z, b, zops = _infonce_case()
+    g = _rng(511).standard_normal(z.shape[0]).astype(np.float32)
+    ref = oracle.backward(oracle.Expr(z, z, "linear", ops=zops), "logsumexp", g, exclude_self=True)
+    zt = torch.tensor(z, requires_grad=True)
+    S = (zt @ zt.T) * np.float32(1.0 / 0.07) + torch.from_numpy(b)[:, None]
+    S = S.masked_fill(torch.eye(z.shape[0], dtype=torch.bool), -float("inf"))
+    (dz,) = torch.autograd.grad((torch.logsumexp(S, -1) * torch.from_numpy(g)).sum(), zt)
+    # X and Y alias: the set's gradient is the sum of both sides'.
+    ok, ratio, _ = parity.grad_rule(dz.numpy(), ref["dX"][0] + ref["dY"][0], ref["dX"][1] + ref["dY"][1], np.float32)
+    assert ok, "infonce: float32 autograd rejected (err/tol %.3g)" % ratio
+    r = _rng(512)
+    X = r.standard_normal((300, 3)).astype(np.float32)
+    Y = r.standard_normal((333, 3)).astype(np.float32)
+    Vk = np.concatenate([r.standard_normal((333, 3)), np.ones((333, 1))], 1).astype(np.float32)
+    Gk = r.standard_normal((300, 4)).astype(np.float32)
+    ref = oracle.backward(oracle.Expr(X, Y, "rbf", gamma=0.5), "matmul", Gk, V=Vk)
+    Xt, Yt, Vt = (torch.tensor(a, requires_grad=True) for a in (X, Y, Vk))
+    Kt = torch.exp(-0.5 * ((Xt[:, None, :] - Yt[None, :, :]) ** 2).sum(-1))
+    grads = torch.autograd.grad(((Kt @ Vt) * torch.from_numpy(Gk)).sum(), (Xt, Yt, Vt))
+    for name, gg in zip(("dX", "dY", "dV"), grads):
+        ok, ratio, _ = parity.grad_rule(gg.numpy(), *ref[name], np.float32)
+        assert ok, "kernel product %s: float32 autograd rejected (err/tol %.3g)" % (name, ratio)
+
+
+def pin_grad_rule_rejects_dropped_pair_and_kept_self():
+    """The oracle's own gradients with one key dropped (a column mask), or
+    with the self pair kept, fail the gradient rule."""
+    Q, K, V, ops = _attention_case()
+    G = _rng(513).standard_normal((Q.shape[0], V.shape[1])).astype(np.float32)
+    ref = oracle.backward(oracle.Expr(Q, K, "linear", ops=ops), "softmax_matmul", G, V=V)
+    for drop in (64, K.shape[0] - 1):
+        keep = np.ones(K.shape[0], bool)
+        keep[drop] = False
+        got = oracle.backward(oracle.Expr(Q, K, "linear", ops=ops + [("mask_columns", keep)]), "softmax_matmul", G, V=V)
+        for name in ("dX", "dY", "dV"):
+            ok, ratio, _ = parity.grad_rule(got[name][0], *ref[name], np.float32)
+            assert not ok, "attention %s without key %d accepted (err/tol %.3g)" % (name, drop, ratio)
+    z, b, zops = _infonce_case()
+    g = _rng(514).standard_normal(z.shape[0]).astype(np.float32)
+    e = oracle.Expr(z, z, "linear", ops=zops)
+    ref = oracle.backward(e, "logsumexp", g, exclude_self=True)
+    got = oracle.backward(e, "logsumexp", g, exclude_self=False)
+    for name in ("dX", "dY"):
+        ok, ratio, _ = parity.grad_rule(got[name][0], *ref[name], np.float32)
+        assert not ok, "infonce %s with the self pair kept accepted (err/tol %.3g)" % (name, ratio)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

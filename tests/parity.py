@@ -8,6 +8,9 @@ within floating tolerance; mag scales that tolerance to the conditioning of
 each output. atol = n_terms * smallest normal * max|V| only absorbs
 flush-to-zero differences. -inf must match -inf exactly.
 
+Gradients: |g - o| <= rtol * (mag + |o|) with the same rtol, mag the
+oracle's first-order error magnitude of that gradient.
+
 Top-k: indices must be distinct and in range, values sorted with equal
 values in ascending index order, each returned index must carry the value
 the oracle gives it at that position (within tolerance), and wherever the
@@ -49,6 +52,21 @@ def value_report(g, o, mag, dtype, n_terms=1, vmax=1.0):
     ratio = float(np.max(err / tol)) if err.size else 0.0
     rel = float(np.max(err / np.maximum(np.abs(o[fin]), TINY[dtype]))) if err.size else 0.0
     return ratio <= 1.0, ratio, rel
+
+
+def grad_rule(g, o, mag, dtype):
+    """Gradients follow the same rule with the oracle's first-order
+    gradient magnitude: |g - o| <= rtol (mag + |o|). Returns (ok, worst
+    err/tol, worst |g - o| / (mag + |o|))."""
+    dtype = np.dtype(dtype)
+    o = np.asarray(o, np.float64)
+    m = np.asarray(mag, np.float64)
+    g = np.asarray(g, np.float64).reshape(o.shape)
+    if o.size == 0:
+        return True, 0.0, 0.0
+    scale = m + np.abs(o) + 1e-300
+    rel = float(np.max(np.abs(g - o) / scale))
+    return rel <= RTOL[dtype], rel / RTOL[dtype], rel
 
 
 def assert_values(g, o, mag, dtype, n_terms=1, vmax=1.0, what=""):

@@ -3,10 +3,11 @@
 Y, V and every op vector for each consumer, metric and dtype, with masks,
 the excluded self pair and top-k selections; then the autograd integration.
 
-Tolerance (gpu_cases.grad_report): |gpu - oracle| <= rtol * (mag + |oracle|),
-mag the oracle's sum of the absolute terms of the same gradient (their
-rounding scale), rtol 5e-5 (float32) / 1e-11 (float64), widened by
-sqrt(terms / 256) for sums of many pairs."""
+Tolerance (gpu_cases.grad_report), the forward rule: |gpu - oracle| <=
+rtol * (mag + |oracle|), rtol 1e-5 (float32) / 1e-12 (float64), mag the
+oracle's first-order error magnitude of that gradient. Each check prints
+its worst |gpu - oracle| / tol and the relative tolerance it needs
+(`pytest -s` shows them)."""
 import numpy as np
 import pytest
 import torch

@@ -47,9 +47,9 @@ MUTANTS = [
      "if (e.has_lower && j - i > e.lower) return false;"),
     ("group_of_row_index", "e.group_rows[i] != e.group_cols[j]", "e.group_rows[i] != e.group_cols[i % e.M]"),
     ("softmax_v_by_position", "const int64_t j = jx[t];", "const int64_t j = t;"),
-    ("backward_exp_derivative", "case OP_EXP: d = d * t[op + 1];", "case OP_EXP: d = d * t[op];"),
+    ("backward_exp_derivative", "          d = d * t[op + 1];", "          d = d * t[op];"),
     ("backward_weight_rows_grad", "if (side == 0) { gops[op] += d * t[op];", "if (side == 0) { gops[op] += d;"),
-    ("backward_softmax_delta", "return p * (gv(i, j) - delta[i]);", "return p * gv(i, j);"),
+    ("backward_softmax_delta", "R a = gv(i, j) - delta[i];", "R a = gv(i, j);"),
     ("backward_distance_side_sign", "if (side == 1) c = -c;", ""),
     ("backward_displacement_direct", "gx[dd] += side == 0 ? -w : w;", "gx[dd] += w;"),
     ("backward_matmul_dv", "gvout[c] += t[n] * g(i, c);", "gvout[c] += g(i, c);"),
@@ -75,6 +75,19 @@ MUTANTS = [
     ("mag_softmax_without_p", "av[c] += p * (1 + mu[t]) * std::fabs(v);", "av[c] += (1 + mu[t]) * std::fabs(v);"),
     ("mag_softmax_drops_cross_term", "mag[r * C + c] = av[c] + pmu * apv[c];", "mag[r * C + c] = av[c];"),
     ("mag_topk_of_first_pair", "mag[r * kk + p] = buf[p].mu;", "mag[r * kk + p] = buf[0].mu;"),
+    # ... and in the gradients' first-order magnitudes.
+    ("mag_backward_lse_without_mu", "*scale = std::fabs((R)G[i * ldg]) * p * (1 + mu + lm[i]);",
+     "*scale = std::fabs((R)G[i * ldg]) * p;"),
+    ("mag_backward_softmax_without_delta", "+ gv_abs(i, j) + dmag[i]);", "+ gv_abs(i, j));"),
+    ("mag_backward_metric_grad_rounding", "gxm[dd] += dm * std::fabs(mg[dd]) + std::fabs(d) * mgm[dd];",
+     "gxm[dd] += dm * std::fabs(mg[dd]);"),
+    ("mag_backward_weight_rows_without_mu",
+     "if (side == 0) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]) + std::fabs(d) * mu[op]; }",
+     "if (side == 0) { gops[op] += d * t[op]; gopsm[op] += dm * std::fabs(t[op]); }"),
+    ("mag_backward_exp_factor", "dm = dm * t[op + 1] + std::fabs(d) * t[op + 1] * (1 + mu[op]);",
+     "dm = dm * t[op + 1];"),
+    ("mag_backward_matmul_dv_without_mu", "gvm[c] += (std::fabs(t[n]) + mu[n]) * std::fabs(g(i, c));",
+     "gvm[c] += std::fabs(t[n]) * std::fabs(g(i, c));"),
 ]
 
 

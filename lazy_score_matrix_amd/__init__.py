@@ -27,7 +27,8 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpw.so")
+# PW_LIBRARY names another build of libpw (e.g. one with sanitized host code).
+LIB_PATH = os.environ.get("PW_LIBRARY") or os.path.join(_HERE, "libpw.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pw.h")
 
 PW_OK, PW_ERR_INVALID, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP, PW_ERR_SCRATCH = 0, -1, -2, -3, -4, -5

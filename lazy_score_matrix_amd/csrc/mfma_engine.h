@@ -464,10 +464,13 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 #pragma unroll
         for (int r = 0; r < NREG; ++r) v[b][r] = ldexp(fma(v[b][r], p[b][r], v[b][r]), n[b][r] >> 8);
     } else {
+      // The expansion can round a distance below zero (x = y) or, far from
+      // the origin, well below it: the exponent is clamped at 0, so k <= 1
+      // and never overflows (float64's rounding is 2^-52 of |x|^2: no clamp).
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int r = 0; r < NREG; ++r) v[b][r] = F::exp2(fma(s[b][r], rbf_c, rbf_t[b]));
+        for (int r = 0; r < NREG; ++r) v[b][r] = F::exp2(fmin(fma(s[b][r], rbf_c, rbf_t[b]), (T)0));
     }
   };
   auto consume = [&](int kb, int nb, int64_t j0, bool diag, bool check_, acc_t (&s)[QB], auto pl) __attribute__((always_inline)) {

@@ -502,9 +502,9 @@ thread_local hipEvent_t tile_ev_start = nullptr, tile_ev_stop = nullptr;
 // One tile launch plus, when the columns are split, the merge.
 int run_tiles(const pw_expr &e, int consumer, const Plan &p, TileArgs &a, hipStream_t s, bool first = true,
               bool last = true) {
-  if (first && tile_ev_start) hipEventRecord(tile_ev_start, s);
+  if (first && tile_ev_start) (void)hipEventRecord(tile_ev_start, s);
   int rc = hip_status(launch_tile(e, consumer, p, a, s));
-  if (last && tile_ev_stop) hipEventRecord(tile_ev_stop, s);
+  if (last && tile_ev_stop) (void)hipEventRecord(tile_ev_stop, s);
   if (rc == PW_OK && p.n_part > 1) {
     TileArgs m = a;
     m.n_split = p.n_part;
@@ -1098,7 +1098,7 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
     const int cp = C <= 32 ? 32 : 64;
     for (int side = 0; side < 2 && rc == PW_OK; ++side) {
       if (!want_side(side)) continue;
-      if (!started && tile_ev_start) hipEventRecord(tile_ev_start, s);
+      if (!started && tile_ev_start) (void)hipEventRecord(tile_ev_start, s);
       started = true;
       m.n_rb = g.m_n_rb[side];
       m.n_split = g.m_n_split[side];
@@ -1123,13 +1123,13 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
       }
       rc = hip_status(launch_grad_merge(e->dtype, ma, side, side == 0 ? e->N : e->M,
                                         (side == 1 && cons == C_SOFTMAX) ? (int)C : 0, o, s));
-      if (side == last_side && tile_ev_stop) hipEventRecord(tile_ev_stop, s);
+      if (side == last_side && tile_ev_stop) (void)hipEventRecord(tile_ev_stop, s);
     }
     return rc;
   }
   for (int side = 0; side < 2 && rc == PW_OK; ++side) {
     if (!want_side(side)) continue;
-    if (!started && tile_ev_start) hipEventRecord(tile_ev_start, s);
+    if (!started && tile_ev_start) (void)hipEventRecord(tile_ev_start, s);
     started = true;
     a.n_rb = g.n_rb[side];
     a.n_split = g.n_split[side];
@@ -1150,7 +1150,7 @@ int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_g
       if (a.ops[t].where == side + 1) o.dop[t] = out->dops[bound_of[t]];
     rc = hip_status(launch_grad_merge(e->dtype, a, side, side == 0 ? e->N : e->M, (side == 1 && value) ? (int)C : 0,
                                       o, s));
-    if (side == last_side && tile_ev_stop) hipEventRecord(tile_ev_stop, s);
+    if (side == last_side && tile_ev_stop) (void)hipEventRecord(tile_ev_stop, s);
   }
   return rc;
 }

@@ -28,7 +28,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# PW_ORACLE_LIBRARY names a prebuilt oracle (e.g. a sanitized build); build()
+# then leaves it as it is.
+_PREBUILT = os.environ.get("PW_ORACLE_LIBRARY")
+_LIB = _PREBUILT or os.path.join(_HERE, "liboracle.so")
 
 # Score-arithmetic op codes understood by oracle.cpp (its own numbering).
 OPS = {
@@ -56,6 +59,8 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile liboracle.so with g++ (OpenMP, no fast-math). Returns its path."""
+    if _PREBUILT:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-Wall", _SRC, "-o", tmp]

@@ -176,6 +176,30 @@ def test_rbf_self_pairs_are_one():
     assert np.array_equal(g, np.ones((600, 1), np.float32))
 
 
+@pytest.mark.parametrize("D", (16, 32))
+def test_mfma_rbf_kernel_at_most_one(D):
+    """The matrix-core rbf (norm expansion, float32) clamps its exponent at
+    0: every kernel value is finite and <= 1, also for points far from the
+    origin where the expansion cancels; self pairs of ordinary points are
+    1 within the rule's tolerance (|k - 1| <= 1e-5 (1 + gamma sum (|x| +
+    |y|)^2)), and the whole kernel matrix passes the rule."""
+    r = np.random.default_rng(600 + D)
+    n = 300
+    X = r.standard_normal((n, D)).astype(np.float32)
+    X[::17] *= 3e4  # far from the origin: the expansion cancels
+    eye = np.eye(n, dtype=np.float32)
+    e, oe = bind_both(X, X, "rbf", 1.0 / D, same=True)
+    assert e.plan("matmul", 64).startswith("family=mfma"), e.plan("matmul", 64)
+    K = e.matmul(to_dev(eye)).cpu().numpy()
+    assert np.all(np.isfinite(K)) and np.all(K <= 1.0) and np.all(K >= 0.0), (K.max(), K.min())
+    near = np.ones(n, bool)
+    near[::17] = False
+    spread = 4 * np.sum(X.astype(np.float64) ** 2, axis=1)
+    d = np.diag(K)[near]
+    assert np.all(np.abs(d - 1.0) <= 1e-5 * (1 + spread[near] / D)), np.max(np.abs(d - 1.0))
+    check_consumer(e, oe, "matmul", V=eye, what="rbf kernel matrix D%d" % D)
+
+
 def test_softmax_rows_sum_to_one():
     X, Y, r = _data(12, 400, 700, 16, np.float32)
     V = np.ones((700, 1), np.float32)

@@ -145,13 +145,40 @@ typedef enum {
 int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
             const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops);
 
+/* Bind a score over leading batch elements (torchpairwise "Custom
+ * Comparisons / Encoded Feature Reuse" page: one input of batch one against
+ * a batch of B; guide, Task Map, MMD row: one feature set per element).
+ * Element b scores the rows of X + b*sx against those of Y + b*sy with the
+ * same metric and op chain, op t's vector taken at vec + b*op_stride[t];
+ * every consumer then runs all B elements in one launch (the tile grid's
+ * third dimension). Strides count elements of the dtype; 0 shares one
+ * array among all elements (X [1, N, D] against Y [B, M, D] is sx = 0,
+ * sy = M*ldy). Masks are shared by every element: op_stride of a mask or a
+ * scalar op must be 0. Consumers on a batched handle read V at V + b*sv and
+ * write each element's outputs packed one after another: out [B][N][ldo],
+ * log-sum-exp and lse [B][N], top-k values and indices [B][N][k] (indices
+ * within the element). Backward and CG solves take unbatched handles
+ * (PW_ERR_UNSUPPORTED on a batched one).
+ *   batch->B   1..65535 (PW_ERR_UNSUPPORTED above); all strides >= 0 */
+typedef struct {
+  int64_t B;
+  int64_t sx, sy;                 /* X, Y */
+  int64_t sv;                     /* V of the value consumers */
+  int64_t op_stride[PW_MAX_OPS];  /* per op of the list */
+} pw_batch;
+int pw_bind_batched(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
+                    const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops,
+                    const pw_batch *batch);
+
 /* Free a handle (host memory only). NULL is ignored. */
 void pw_release(pw_expr *e);
 
-/* Bytes of device workspace `consumer` needs on this handle: C value
+/* Bytes of device workspace `consumer` needs on this handle (all batch
+ * elements of a batched one): C value
  * columns for PW_C_MATMUL / PW_C_SOFTMAX_MATMUL (ignored otherwise) and k
  * for PW_C_TOPK (ignored otherwise). The size depends on N, M, D, C, k and
- * the op chain, never on N*M (the guide's "tile workspace"); it may be 0. */
+ * the op chain, never on N*M (the guide's introduction: beyond the inputs and outputs, the
+ * streamed path needs only scratch sized by its tiles); it may be 0. */
 int pw_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes);
 
 /* Kernel product (guide, Task Map, "Kernel attention, Nadaraya-Watson" row:

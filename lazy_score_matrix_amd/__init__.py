@@ -54,6 +54,11 @@ class _Op(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("scalar", ctypes.c_double), ("vec", ctypes.c_void_p)]
 
 
+class _Batch(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("sx", ctypes.c_int64), ("sy", ctypes.c_int64), ("sv", ctypes.c_int64),
+                ("op_stride", ctypes.c_int64 * 16)]
+
+
 class _SolveInfo(ctypes.Structure):
     _fields_ = [("converged", ctypes.c_int), ("status", ctypes.c_int), ("iterations", ctypes.c_int),
                 ("max_rel_residual", ctypes.c_double)]
@@ -92,6 +97,8 @@ def load_library(path: str = LIB_PATH):
         lib.pw_bind.argtypes = [ctypes.POINTER(vp), c_int, c_int, ctypes.c_double, vp, i64, i64, vp, i64, i64, i64,
                                 ctypes.POINTER(_Op), c_int]
         lib.pw_release.argtypes = [vp]
+        lib.pw_bind_batched.argtypes = [ctypes.POINTER(vp), c_int, c_int, ctypes.c_double, vp, i64, i64, vp, i64, i64,
+                                        i64, ctypes.POINTER(_Op), c_int, ctypes.POINTER(_Batch)]
         lib.pw_release.restype = None
         lib.pw_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
         lib.pw_matmul.argtypes = [vp, vp, i64, i64, vp, i64, vp, sz, vp]
@@ -588,9 +595,11 @@ class BatchedLazyScores:
     feature set per batch element; the Features page: a [1, N, *] input
     compares against every element of a [B, M, *] input). X is [B or 1,
     N, D], Y is [B or 1, M, D]; op vectors are either shared ([N] / [M]) or
-    per element ([B, N] / [B, M]). Each element binds its own LazyScores
-    and runs the same fused kernels; outputs stack along a leading B axis.
-    Differentiable like LazyScores (the slices carry autograd)."""
+    per element ([B, N] / [B, M]); masks are shared. A forward consumer call
+    binds the whole batch (pw_bind_batched) and runs every element in one
+    launch; outputs stack along a leading B axis. Calls that need autograd,
+    per-element masks or the backward run element by element (each element
+    a LazyScores; the slices carry autograd)."""
 
     def __init__(self, X, Y, metric="linear", gamma=1.0, ops=()):
         if X.dim() != 3 or Y.dim() != 3:
@@ -602,6 +611,7 @@ class BatchedLazyScores:
         self.X, self.Y, self.metric, self.gamma = X, Y, metric, float(gamma)
         self.ops = expand_ops(ops)
         self.N, self.M, self.D = X.shape[1], Y.shape[1], X.shape[2]
+        self.dtype, self.device = X.dtype, X.device
 
     def element(self, b: int) -> LazyScores:
         X = self.X[b if self.X.shape[0] > 1 else 0]
@@ -613,6 +623,83 @@ class BatchedLazyScores:
             ops.append((n, a))
         return LazyScores(X, Y, self.metric, self.gamma, ops)
 
+    # -- one launch for the whole batch ----------------------------------
+    def _stride(self, t, what):
+        """Elements between consecutive batch elements of t [B or 1, ...]
+        (0 for a single shared one); rows of each element must be laid out
+        with unit column stride."""
+        if t.shape[0] == 1:
+            return 0
+        return t.stride(0)
+
+    def _batched_ok(self, V=None):
+        if _needs_grad(self, V):
+            return False
+        for n, a in self.ops:
+            if n in MASK_OPS and torch.is_tensor(a) and a.dim() != 1:
+                return False  # masks are shared by the batch
+        return True
+
+    def _bind(self, V=None):
+        """A pw_expr over the whole batch, and the tensors it borrows."""
+        lib = load_library()
+        X, Y = self.X, self.Y
+        if X.dtype not in DTYPES or Y.dtype != X.dtype or not X.is_cuda or Y.device != X.device:
+            raise ValueError("X and Y must be float32 or float64 tensors on one GPU")
+        ldx, ldy = _rows(X[0], "X"), _rows(Y[0], "Y")
+        bt = _Batch()
+        bt.B = self.B
+        bt.sx, bt.sy = self._stride(X, "X"), self._stride(Y, "Y")
+        bt.sv = 0 if V is None or V.dim() == 2 else self._stride(V, "V")
+        keep = [X, Y]
+        arr = (_Op * max(len(self.ops), 1))()
+        for t, (name, arg) in enumerate(self.ops):
+            arr[t].kind = OPS[name]
+            if name in ("mul", "add", "band_upper", "band_lower"):
+                arr[t].scalar = float(arg)
+            elif name != "exp":
+                n = self.N if name.endswith("_rows") else self.M
+                v = arg
+                per = v.dim() == 2
+                if name in MASK_OPS:
+                    want = (torch.bool, torch.uint8) if name.startswith("mask") else (torch.int64,)
+                else:
+                    want = (self.dtype,)
+                if (v.dtype not in want or v.device != self.device or v.shape[-1] != n or v.stride(-1) != 1
+                        or (per and v.shape[0] not in (1, self.B))):
+                    raise ValueError("%s needs a %s vector of %d elements (or [B, %d]) on %s"
+                                     % (name, " or ".join(str(w) for w in want), n, n, self.device))
+                arr[t].vec = v.data_ptr()
+                bt.op_stride[t] = v.stride(0) if per and v.shape[0] > 1 else 0
+                keep.append(v)
+        h = ctypes.c_void_p()
+        check(lib.pw_bind_batched(ctypes.byref(h), DTYPES[X.dtype], METRICS[self.metric], self.gamma, X.data_ptr(),
+                                  self.N, ldx, Y.data_ptr(), self.M, ldy, self.D, arr, len(self.ops),
+                                  ctypes.byref(bt)), "pw_bind_batched")
+        return _Handle(lib, h, keep)
+
+    def plan(self, consumer: str, C: int = 0, k: int = 0) -> str:
+        """The batched launch plan of a consumer (pw_plan_describe)."""
+        return self._bind().plan(consumer, C, k)
+
+    def _V3(self, V):
+        V3 = V if V.dim() == 3 else V[None]
+        if V3.dtype != self.dtype or V3.device != self.device or V3.shape[1] != self.M or \
+                V3.shape[0] not in (1, self.B):
+            raise ValueError("V must be [B or 1, M, C] (or [M, C]) %s on %s" % (self.dtype, self.device))
+        return V3
+
+    def _value_consumer(self, name, V):
+        V3 = self._V3(V)
+        h = self._bind(V)
+        C = V3.shape[2]
+        out = torch.empty(self.B, self.N, C, dtype=self.dtype, device=self.device)
+        ws, nb = h.workspace(name, C)
+        fn = h.lib.pw_matmul if name == "matmul" else h.lib.pw_softmax_matmul
+        check(fn(h.h, V3.data_ptr(), C, _rows(V3[0], "V"), out.data_ptr(), C, ws.data_ptr(), nb,
+                 _stream(self.device)), "pw_" + name)
+        return out
+
     def _each(self, fn):
         outs = [fn(self.element(b)) for b in range(self.B)]
         if isinstance(outs[0], tuple):
@@ -623,36 +710,95 @@ class BatchedLazyScores:
         return V[b if V.shape[0] > 1 else 0] if V.dim() == 3 else V
 
     def matmul(self, V, mask=None):
-        return torch.stack([self.element(b).matmul(self._V(V, b), mask=mask) for b in range(self.B)])
+        if mask is not None:
+            return self.masked(mask).matmul(V)
+        if self._batched_ok(V):
+            return self._value_consumer("matmul", V)
+        return torch.stack([self.element(b).matmul(self._V(V, b)) for b in range(self.B)])
 
     __matmul__ = matmul
 
     def softmax_matmul(self, V, mask=None):
-        return torch.stack([self.element(b).softmax_matmul(self._V(V, b), mask=mask) for b in range(self.B)])
+        if mask is not None:
+            return self.masked(mask).softmax_matmul(V)
+        if self._batched_ok(V):
+            return self._value_consumer("softmax_matmul", V)
+        return torch.stack([self.element(b).softmax_matmul(self._V(V, b)) for b in range(self.B)])
 
     def displacement(self, mask=None):
-        return self._each(lambda e: e.displacement(mask=mask))
+        if mask is not None:
+            return self.masked(mask).displacement()
+        if not self._batched_ok():
+            return self._each(lambda e: e.displacement())
+        h = self._bind()
+        out = torch.empty(self.B, self.N, self.D, dtype=self.dtype, device=self.device)
+        ws, nb = h.workspace("displacement")
+        check(h.lib.pw_displacement(h.h, out.data_ptr(), self.D, ws.data_ptr(), nb, _stream(self.device)),
+              "pw_displacement")
+        return out
 
     def logsumexp(self, exclude_self=False, mask=None):
-        return self._each(lambda e: e.logsumexp(exclude_self, mask=mask))
+        if mask is not None:
+            return self.masked(mask).logsumexp(exclude_self)
+        if not self._batched_ok():
+            return self._each(lambda e: e.logsumexp(exclude_self))
+        h = self._bind()
+        out = torch.empty(self.B, self.N, dtype=self.dtype, device=self.device)
+        ws, nb = h.workspace("logsumexp")
+        check(h.lib.pw_logsumexp(h.h, int(bool(exclude_self)), out.data_ptr(), ws.data_ptr(), nb,
+                                 _stream(self.device)), "pw_logsumexp")
+        return out
 
     def topk(self, k, largest=False, mask=None):
-        return self._each(lambda e: e.topk(k, largest, mask=mask))
+        if mask is not None:
+            return self.masked(mask).topk(k, largest)
+        if not self._batched_ok():
+            return self._each(lambda e: e.topk(k, largest))
+        h = self._bind()
+        vals = torch.empty(self.B, self.N, k, dtype=self.dtype, device=self.device)
+        idx = torch.empty(self.B, self.N, k, dtype=torch.int64, device=self.device)
+        ws, nb = h.workspace("topk", 0, k)
+        check(h.lib.pw_topk(h.h, int(k), int(bool(largest)), vals.data_ptr(), idx.data_ptr(), ws.data_ptr(), nb,
+                            _stream(self.device)), "pw_topk")
+        return vals, idx
 
     def min(self, dim=-1):
-        return self._each(lambda e: e.min(dim))
+        if dim in (-2, 1):
+            return self.T.min(-1)
+        v, i = self.topk(1)
+        return v[..., 0], i[..., 0]
 
     def max(self, dim=-1):
-        return self._each(lambda e: e.max(dim))
+        if dim in (-2, 1):
+            return self.T.max(-1)
+        v, i = self.topk(1, largest=True)
+        return v[..., 0], i[..., 0]
 
     def argmin(self, dim=-1):
-        return self._each(lambda e: e.argmin(dim))
+        return self.min(dim)[1]
 
     def sum(self, dim=-1):
-        return self._each(lambda e: e.sum(dim))
+        """Sum over `dim`: the product with a column of ones."""
+        if dim in (-2, 1):
+            return self.T.sum(-1)
+        ones = torch.ones(self.M, 1, dtype=self.dtype, device=self.device)
+        return self.matmul(ones)[..., 0]
 
     def mean(self, dim=-1):
-        return self._each(lambda e: e.mean(dim))
+        """Mean over `dim`: the scores scaled by 1/M in the same product; with
+        masks, the sum divided by each row's kept count (a second product of
+        the masks with unit scores; the division is the host's)."""
+        if dim in (-2, 1):
+            return self.T.mean(-1)
+        if self.M == 0:
+            return torch.full((self.B, self.N), float("nan"), dtype=self.dtype, device=self.device)
+        masks = [(n, a) for n, a in self.ops if n in MASK_OPS]
+        if masks:
+            ones = BatchedLazyScores(self.X, self.Y, "linear", 1.0, [("mul", 0.0), ("add", 1.0)] + masks)
+            return self.sum(-1) / ones.sum(-1)
+        scaled = BatchedLazyScores(self.X, self.Y, self.metric, self.gamma,
+                                   list(self.ops) + [("mul", 1.0 / self.M)])
+        return scaled.sum(-1)
 
     def masked(self, mask):
         mask = [mask] if isinstance(mask, tuple) else list(mask)
@@ -662,6 +808,32 @@ class BatchedLazyScores:
     def T(self):
         ops = [(_SWAP.get(n, n), a) for n, a in self.ops]
         return BatchedLazyScores(self.Y, self.X, self.metric, self.gamma, ops)
+
+
+class _Handle:
+    """A bound pw_expr that owns its handle and keeps the tensors it
+    borrows alive."""
+
+    def __init__(self, lib, h, keep):
+        self.lib, self.h, self._keep = lib, h, keep
+        self.device = keep[0].device
+
+    def __del__(self):
+        if self.h is not None and self.h.value:
+            self.lib.pw_release(self.h)
+            self.h = None
+
+    def plan(self, consumer, C=0, k=0):
+        buf = ctypes.create_string_buffer(512)
+        check(self.lib.pw_plan_describe(self.h, CONSUMERS[consumer], int(C), int(k), buf, 512), "pw_plan_describe")
+        return buf.value.decode()
+
+    def workspace(self, consumer, C=0, k=0):
+        n = ctypes.c_size_t()
+        check(self.lib.pw_workspace_size(self.h, CONSUMERS[consumer], int(C), int(k), ctypes.byref(n)),
+              "pw_workspace_size")
+        ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=self.device)
+        return ws, n.value
 
 
 def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()):

@@ -31,9 +31,11 @@ FLAGS = [
 
 
 # Device code: NaN scores are unsupported (include/pw.h), so kernels are built
-# without NaN semantics and without IEEE mode; min/max then need no operand
-# canonicalisation. Host validation (pw_api.cpp) keeps full NaN handling.
-KERNEL_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+# without NaN semantics; min/max then need no operand canonicalisation. IEEE
+# mode stays on: a kernel built without it cannot inline the device library
+# (work-item ids, float64 exp/log), and every kernel would call those out of
+# line. Host validation (pw_api.cpp) keeps full NaN handling.
+KERNEL_FLAGS = ["-fno-honor-nans"]
 
 
 def sources():

@@ -8,6 +8,7 @@ namespace pw {
 // Epilogue vectors: every program of the batch evaluated per element in
 // double, rounded once to the dtype.
 // ---------------------------------------------------------------------------
+// Program blockIdx.y of the batch, for batch element blockIdx.z.
 template <class T>
 __global__ __launch_bounds__(256) void vec_prog_kernel(const VecProgBatch b) {
   const int pi = blockIdx.y;
@@ -15,6 +16,7 @@ __global__ __launch_bounds__(256) void vec_prog_kernel(const VecProgBatch b) {
   const VecProg &p = b.p[pi];
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= p.len) return;
+  const int64_t z = blockIdx.z;
   double v = 0.0;
   for (int k = 0; k < p.n; ++k) {
     const VecInstr &in = p.ins[k];
@@ -22,18 +24,18 @@ __global__ __launch_bounds__(256) void vec_prog_kernel(const VecProgBatch b) {
       case VO_SET: v = in.c; break;
       case VO_MULC: v *= in.c; break;
       case VO_ADDC: v += in.c; break;
-      case VO_MULV: v *= (double)ldg<T>(in.v, e); break;
-      case VO_ADDV: v += (double)ldg<T>(in.v, e); break;
+      case VO_MULV: v *= (double)ldg<T>(batch_ptr(in.v, in.bstride, z), e); break;
+      case VO_ADDV: v += (double)ldg<T>(batch_ptr(in.v, in.bstride, z), e); break;
     }
   }
-  static_cast<T *>(p.out)[e] = (T)v;
+  static_cast<T *>(batch_ptr(p.out, p.out_bstride, z))[e] = (T)v;
 }
 
-hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s) {
+hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, int64_t n_batch, hipStream_t s) {
   int64_t len = 0;
   for (int i = 0; i < b.n_progs; ++i) len = b.p[i].len > len ? b.p[i].len : len;
   if (len == 0 || b.n_progs == 0) return hipSuccess;
-  dim3 grid((unsigned)((len + 255) / 256), (unsigned)b.n_progs), block(256);
+  dim3 grid((unsigned)((len + 255) / 256), (unsigned)b.n_progs, (unsigned)n_batch), block(256);
   if (dtype == 0) hipLaunchKernelGGL(vec_prog_kernel<float>, grid, block, 0, s, b);
   else hipLaunchKernelGGL(vec_prog_kernel<double>, grid, block, 0, s, b);
   return hipGetLastError();
@@ -145,8 +147,11 @@ hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, in
 // partial sums are folded with lane exchanges inside the group.
 // ---------------------------------------------------------------------------
 template <class T, int L>
-__global__ __launch_bounds__(256) void row_norms_kernel(const T *__restrict__ X, int64_t n, int64_t ld, int D,
-                                                        T *__restrict__ out, bool inverse) {
+__global__ __launch_bounds__(256) void row_norms_kernel(const T *__restrict__ X_in, int64_t n, int64_t ld, int D,
+                                                        T *__restrict__ out_in, bool inverse, int64_t x_bstride,
+                                                        int64_t out_bstride) {
+  const T *__restrict__ X = static_cast<const T *>(batch_ptr(X_in, x_bstride, blockIdx.y));
+  T *__restrict__ out = static_cast<T *>(batch_ptr(out_in, out_bstride, blockIdx.y));
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = t / L;
   const int lane = (int)(t % L);
@@ -163,20 +168,23 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const T *__restrict__ X,
 }
 
 template <class T>
-static hipError_t row_norms_t(const T *X, int64_t n, int64_t ld, int D, T *out, hipStream_t s, bool inv) {
+static hipError_t row_norms_t(const T *X, int64_t n, int64_t ld, int D, T *out, hipStream_t s, bool inv, int64_t nb,
+                              int64_t xs, int64_t os) {
   dim3 block(256);
-  auto grid = [&](int L) { return dim3((unsigned)((n * L + 255) / 256)); };
-  if (D <= 4) hipLaunchKernelGGL((row_norms_kernel<T, 4>), grid(4), block, 0, s, X, n, ld, D, out, inv);
-  else if (D <= 8) hipLaunchKernelGGL((row_norms_kernel<T, 8>), grid(8), block, 0, s, X, n, ld, D, out, inv);
-  else hipLaunchKernelGGL((row_norms_kernel<T, 16>), grid(16), block, 0, s, X, n, ld, D, out, inv);
+  auto grid = [&](int L) { return dim3((unsigned)((n * L + 255) / 256), (unsigned)nb); };
+  if (D <= 4) hipLaunchKernelGGL((row_norms_kernel<T, 4>), grid(4), block, 0, s, X, n, ld, D, out, inv, xs, os);
+  else if (D <= 8) hipLaunchKernelGGL((row_norms_kernel<T, 8>), grid(8), block, 0, s, X, n, ld, D, out, inv, xs, os);
+  else hipLaunchKernelGGL((row_norms_kernel<T, 16>), grid(16), block, 0, s, X, n, ld, D, out, inv, xs, os);
   return hipGetLastError();
 }
 
 hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s,
-                            bool inverse) {
-  if (n == 0) return hipSuccess;
-  if (dtype == 0) return row_norms_t<float>((const float *)X, n, ld, D, (float *)out, s, inverse);
-  return row_norms_t<double>((const double *)X, n, ld, D, (double *)out, s, inverse);
+                            bool inverse, int64_t n_batch, int64_t x_bstride, int64_t out_bstride) {
+  if (n == 0 || n_batch == 0) return hipSuccess;
+  if (dtype == 0)
+    return row_norms_t<float>((const float *)X, n, ld, D, (float *)out, s, inverse, n_batch, x_bstride, out_bstride);
+  return row_norms_t<double>((const double *)X, n, ld, D, (double *)out, s, inverse, n_batch, x_bstride,
+                             out_bstride);
 }
 
 // ---------------------------------------------------------------------------
@@ -185,22 +193,24 @@ hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int
 // ---------------------------------------------------------------------------
 template <class T>
 __global__ __launch_bounds__(256) void merge_sum_kernel(const TileArgs a, int W) {
+  const BatchPtrs bp = batch_ptrs(a);
   // matmul (W = C) and displacement (W = D): plain sums of the partials.
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= a.N * W) return;
   const int64_t i = t / W;
   const int c = (int)(t % W);
-  const T *part = static_cast<const T *>(a.partial);
+  const T *part = static_cast<const T *>(bp.partial);
   T s = 0;
   for (int sp = 0; sp < a.n_split; ++sp) s += part[((int64_t)sp * a.N + i) * W + c];
-  static_cast<T *>(a.out)[i * a.ldo + c] = s;
+  static_cast<T *>(bp.out)[i * a.ldo + c] = s;
 }
 
 template <class T>
 __global__ __launch_bounds__(256) void merge_lse_kernel(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= a.N) return;
-  const T *part = static_cast<const T *>(a.partial);
+  const T *part = static_cast<const T *>(bp.partial);
   T m = neg_inf<T>();
   for (int sp = 0; sp < a.n_split; ++sp) m = max(m, part[((int64_t)sp * a.N + i) * 2]);
   T l = 0;
@@ -210,17 +220,18 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const TileArgs a) {
       if (q[1] > (T)0) l += q[1] * dexp(q[0] - m);
     }
   }
-  static_cast<T *>(a.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
+  static_cast<T *>(bp.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
 }
 
 template <class T>
 __global__ __launch_bounds__(256) void merge_softmax_kernel(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= a.N * a.C) return;
   const int64_t i = t / a.C;
   const int c = (int)(t % a.C);
   const int64_t W = a.C + 2;
-  const T *part = static_cast<const T *>(a.partial);
+  const T *part = static_cast<const T *>(bp.partial);
   T m = neg_inf<T>();
   for (int sp = 0; sp < a.n_split; ++sp) m = max(m, part[((int64_t)sp * a.N + i) * W]);
   T l = 0, acc = 0;
@@ -234,13 +245,14 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const TileArgs a) {
       }
     }
   }
-  static_cast<T *>(a.out)[i * a.ldo + c] = (l > (T)0) ? acc / l : (T)0;
+  static_cast<T *>(bp.out)[i * a.ldo + c] = (l > (T)0) ? acc / l : (T)0;
   // The split maxima carry the row offset, so m + log l is the row's lse.
-  if (c == 0 && a.lse_out) static_cast<T *>(a.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
+  if (c == 0 && bp.lse_out) static_cast<T *>(bp.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
 }
 
 template <class T, int KL>
 __global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= a.N) return;
   Key<T> list[KL];
@@ -248,10 +260,10 @@ __global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
   for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
   for (int sp = 0; sp < a.n_split; ++sp) {
     const int64_t base = ((int64_t)sp * a.N + i) * a.k;
-    for (int p = 0; p < a.k; ++p) key_insert<T, KL>(list, Key<T>::load(a.partial, base + p));
+    for (int p = 0; p < a.k; ++p) key_insert<T, KL>(list, Key<T>::load(bp.partial, base + p));
   }
-  T *v = static_cast<T *>(a.out) + i * a.k;
-  int64_t *ix = a.idx + i * a.k;
+  T *v = static_cast<T *>(bp.out) + i * a.k;
+  int64_t *ix = bp.idx + i * a.k;
 #pragma unroll
   for (int p = 0; p < KL; ++p)
     if (p < a.k) {
@@ -263,7 +275,7 @@ __global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
 template <class T>
 static hipError_t merge_t(int consumer, const TileArgs &a, hipStream_t s) {
   dim3 block(256);
-  auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
+  auto blocks = [&](int64_t n) { return dim3((unsigned)((n + 255) / 256), 1, (unsigned)a.bat.n); };
   if (a.N == 0) return hipSuccess;
   switch (consumer) {
     case C_MATMUL:

@@ -36,16 +36,17 @@ struct RowEpi {
   T p[kMaxStages];
 };
 
+// zb: byte offset of the batch element's epilogue vectors.
 template <class T>
-__device__ __forceinline__ void load_row_epi(const Epi &e, int64_t i, bool valid, RowEpi<T> &re) {
+__device__ __forceinline__ void load_row_epi(const Epi &e, int64_t i, bool valid, RowEpi<T> &re, int64_t zb) {
 #pragma unroll
   for (int s = 0; s < kMaxStages; ++s) {
     T r = (T)1, p = (T)0;
     if (s < e.n_stages && e.st[s].kind == ST_AFFINE) {
       if (e.st[s].row_vec) {
         if (valid) {
-          r = ldg<T>(e.st[s].r_vec, i);
-          p = ldg<T>(e.st[s].p_vec, i);
+          r = ldg<T>(static_cast<const char *>(e.st[s].r_vec) + zb, i);
+          p = ldg<T>(static_cast<const char *>(e.st[s].p_vec) + zb, i);
         }
       } else {
         r = (T)e.st[s].r_scalar;
@@ -195,6 +196,41 @@ __device__ __forceinline__ void key_insert_after(Key<double> (&l)[L], Key<double
       c = hi;
     }
   }
+}
+
+// The arrays of batch element blockIdx.z, each offset by its batch stride
+// (element 0, and every unbatched launch, see them as given). Kernels read
+// their arrays through these; the epilogue's stage vectors are offset where
+// they are read (epi_vec).
+// (The host gives an absent array, a null pointer, stride 0.)
+__device__ __forceinline__ const void *batch_ptr(const void *p, int64_t stride, int64_t z) {
+  return static_cast<const char *>(p) + stride * z;
+}
+__device__ __forceinline__ void *batch_ptr(void *p, int64_t stride, int64_t z) {
+  return static_cast<char *>(p) + stride * z;
+}
+struct BatchPtrs {
+  const void *X, *Y, *V, *ny;
+  void *out, *lse_out, *partial;
+  int64_t *idx;
+};
+__device__ __forceinline__ BatchPtrs batch_ptrs(const TileArgs &a) {
+  const int64_t z = blockIdx.z;
+  BatchPtrs b;
+  b.X = batch_ptr(a.X, a.bat.x, z);
+  b.Y = batch_ptr(a.Y, a.bat.y, z);
+  b.V = batch_ptr(a.V, a.bat.v, z);
+  b.ny = batch_ptr(a.ny, a.bat.ny, z);
+  b.out = batch_ptr(a.out, a.bat.out, z);
+  b.lse_out = batch_ptr(a.lse_out, a.bat.lse, z);
+  b.partial = batch_ptr(a.partial, a.bat.part, z);
+  b.idx = static_cast<int64_t *>(batch_ptr(static_cast<void *>(a.idx), a.bat.idx, z));
+  return b;
+}
+// Byte offset of this batch element's epilogue vectors, and one of them.
+__device__ __forceinline__ int64_t epi_shift(const TileArgs &a) { return a.bat.epi * (int64_t)blockIdx.z; }
+__device__ __forceinline__ const void *epi_vec(const TileArgs &a, const void *v) {
+  return static_cast<const char *>(v) + epi_shift(a);
 }
 
 // A value known to be equal on every lane, moved to scalar registers.

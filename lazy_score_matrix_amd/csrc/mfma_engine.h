@@ -193,6 +193,7 @@ struct MfmaShape {
 template <class T, int METRIC, int CONS, int DP, int CP, int KL, bool MASKED>
 __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
                              (mfma_wgs_per_cu(sizeof(T) == 4 ? 0 : 1, CONS, DP, CP, KL))) void mfma_tile(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   using F = Mfma<T>;
   using acc_t = typename F::acc_t;
   constexpr int TM = F::TM, G = F::G, NREG = F::NREG;
@@ -287,8 +288,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   const int64_t row0 = (int64_t)rb * BM;
   const int64_t jb = paired ? 0 : (int64_t)sp * a.split_cols;
   const int64_t je = wave_uniform(paired ? a.M : min(a.M, jb + a.split_cols));
-  const T *__restrict__ Xp = static_cast<const T *>(a.X);
-  const T *__restrict__ Yp = static_cast<const T *>(a.Y);
+  const T *__restrict__ Xp = static_cast<const T *>(bp.X);
+  const T *__restrict__ Yp = static_cast<const T *>(bp.Y);
   const MaskArgs &mk = a.mask;
   const bool keyflags = MASKED && (mk.col || mk.grow);  // per-key mask data is staged
   const int64_t r1 = min(a.N, row0 + BM) - 1;
@@ -326,8 +327,8 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       const Stage &st = a.epi.st[0];
       if (st.row_vec) {
         if (qv[b]) {
-          r = ldg<T>(st.r_vec, qi[b]);
-          p = ldg<T>(st.p_vec, qi[b]);
+          r = ldg<T>(epi_vec(a, st.r_vec), qi[b]);
+          p = ldg<T>(epi_vec(a, st.p_vec), qi[b]);
         }
       } else {
         r = (T)st.r_scalar;
@@ -665,16 +666,16 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   T nyv = 0, vcol = 0;
   int ckv = 0;
   int64_t gkv = 0;
-  const bool kvec = vec_ok(a.Y, a.ldy, 16 / (int)sizeof(T));
-  const bool vvec = VTILE && vec_ok(a.V, a.ldv, 16 / (int)sizeof(T));
+  const bool kvec = vec_ok(bp.Y, a.ldy, 16 / (int)sizeof(T));
+  const bool vvec = VTILE && vec_ok(bp.V, a.ldv, 16 / (int)sizeof(T));
   ldK.init(a.ldy, kvec, tid);
   if constexpr (VTILE) ldV.init(a.ldv, vvec, tid);
   auto prefetch = [&](int64_t t0) {
     const int nbt = (int)min((int64_t)BN, je - t0);
     ldK.load(Yp, a.ldy, t0, nbt, a.D, tid);
-    if constexpr (VTILE) ldV.load(static_cast<const T *>(a.V), a.ldv, t0, nbt, a.C, tid);
-    if constexpr (NARROW) vcol = (tid < nbt) ? ldg<T>(a.V, (t0 + tid) * a.ldv) : (T)0;
-    if constexpr (NEEDN) nyv = (tid < nbt) ? ldg<T>(a.ny, t0 + tid) : (T)0;
+    if constexpr (VTILE) ldV.load(static_cast<const T *>(bp.V), a.ldv, t0, nbt, a.C, tid);
+    if constexpr (NARROW) vcol = (tid < nbt) ? ldg<T>(bp.V, (t0 + tid) * a.ldv) : (T)0;
+    if constexpr (NEEDN) nyv = (tid < nbt) ? ldg<T>(bp.ny, t0 + tid) : (T)0;
     if (keyflags) {
       ckv = (tid < nbt && (!mk.col || mk.col[t0 + tid])) ? 1 : 0;
       gkv = (tid < nbt && mk.grow) ? mk.gcol[t0 + tid] : 0;
@@ -810,9 +811,9 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       if (g == 0 && qv[b]) {
         const T mnat = m[b] * (T)kLn2 + ep[b];
         if (fin) {
-          static_cast<T *>(a.out)[i] = lt > (T)0 ? mnat + F::log(lt) : kNegInf;
+          static_cast<T *>(bp.out)[i] = lt > (T)0 ? mnat + F::log(lt) : kNegInf;
         } else {
-          T *pp = static_cast<T *>(a.partial) + prow * 2;
+          T *pp = static_cast<T *>(bp.partial) + prow * 2;
           pp[0] = lt > (T)0 ? mnat : kNegInf;
           pp[1] = lt;
         }
@@ -821,7 +822,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       const T lt = F::gsum(lsum[b]);
       if (qv[b]) {
         const T inv = lt > (T)0 ? (T)1 / lt : (T)0;
-        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * (a.C + 2) + 2;
+        T *dst = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow * (a.C + 2) + 2;
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -833,23 +834,23 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         // row's log-sum-exp: it rides on the partial maximum (the merge's
         // rescale is unchanged by a common shift).
         if (!fin && g == 0) {
-          T *pp = static_cast<T *>(a.partial) + prow * (a.C + 2);
+          T *pp = static_cast<T *>(bp.partial) + prow * (a.C + 2);
           pp[0] = lt > (T)0 ? m[b] * (T)kLn2 + ep[b] : kNegInf;
           pp[1] = lt;
         }
-        if (fin && g == 0 && a.lse_out)
-          static_cast<T *>(a.lse_out)[i] = lt > (T)0 ? m[b] * (T)kLn2 + ep[b] + F::log(lt) : kNegInf;
+        if (fin && g == 0 && bp.lse_out)
+          static_cast<T *>(bp.lse_out)[i] = lt > (T)0 ? m[b] * (T)kLn2 + ep[b] + F::log(lt) : kNegInf;
       }
     } else if constexpr (NARROW) {
       T t = F::gsum((wsum[b][0] + wsum[b][1]) + (wsum[b][2] + wsum[b][3]));
       if (epi_post) t *= er[b];
       if (g == 0 && qv[b]) {
-        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow;
+        T *dst = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow;
         dst[0] = t;
       }
     } else if constexpr (CONS == C_MATMUL) {
       if (qv[b]) {
-        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.C;
+        T *dst = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow * a.C;
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -861,7 +862,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     } else if constexpr (CONS == C_DISPLACEMENT) {
       const T mt = F::gsum(mass[b]);
       if (qv[b]) {
-        T *dst = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.D;
+        T *dst = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow * a.D;
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -878,7 +879,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         const int64_t prow_g = ((int64_t)sp * G + g) * a.N + i;
 #pragma unroll
         for (int p = 0; p < KLQ; ++p)
-          if (p >= off) list[b][p].store(a.partial, prow_g * a.k + (p - off));
+          if (p >= off) list[b][p].store(bp.partial, prow_g * a.k + (p - off));
       }
     }
   }
@@ -890,7 +891,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 template <class T, int METRIC, int CONS, int DP, int CP, int KL>
 hipError_t launch_mfma_kernel(const TileArgs &a, hipStream_t s) {
   const int slots = (a.mask.any && a.rb_pairs) ? a.rb_pairs : a.n_rb;
-  dim3 grid((unsigned)(slots * a.n_split)), block(MfmaShape<T, CONS, DP, CP, KL>::NT);
+  dim3 grid((unsigned)(slots * a.n_split), 1, (unsigned)a.bat.n), block(MfmaShape<T, CONS, DP, CP, KL>::NT);
   if (a.mask.any) hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((mfma_tile<T, METRIC, CONS, DP, CP, KL, false>), grid, block, 0, s, a);
   return hipGetLastError();

@@ -38,12 +38,13 @@ struct Prog {
     ins.push_back(VecInstr{VO_ADDC, c, nullptr});
     if (!vec) cval += c;
   }
-  void mulv(const void *v) {
-    ins.push_back(VecInstr{VO_MULV, 0.0, v});
+  // bs: bytes between the vectors of consecutive batch elements (0: shared).
+  void mulv(const void *v, int64_t bs) {
+    ins.push_back(VecInstr{VO_MULV, 0.0, v, bs});
     vec = true;
   }
-  void addv(const void *v) {
-    ins.push_back(VecInstr{VO_ADDV, 0.0, v});
+  void addv(const void *v, int64_t bs) {
+    ins.push_back(VecInstr{VO_ADDV, 0.0, v, bs});
     vec = true;
   }
   bool is_const(double c) const { return !vec && cval == c; }
@@ -85,7 +86,7 @@ struct StageBuilder {
     out.push_back(s);
     start();
   }
-  void op(const pw_op &o) {
+  void op(const pw_op &o, int64_t bs) {
     switch (o.kind) {
       case PW_OP_EXP: {
         close();
@@ -100,12 +101,12 @@ struct StageBuilder {
         bc.mulc(o.scalar);
         break;
       case PW_OP_ADD: br.addc(o.scalar); break;
-      case PW_OP_ADD_ROWS: br.addv(o.vec); break;
-      case PW_OP_ADD_COLUMNS: bc.addv(o.vec); break;
+      case PW_OP_ADD_ROWS: br.addv(o.vec, bs); break;
+      case PW_OP_ADD_COLUMNS: bc.addv(o.vec, bs); break;
       case PW_OP_WEIGHT_ROWS:
         if (bc.vec) close();  // w_i * o_j is not separable: new stage
-        ar.mulv(o.vec);
-        br.mulv(o.vec);
+        ar.mulv(o.vec, bs);
+        br.mulv(o.vec, bs);
         break;
       case PW_OP_WEIGHT_COLUMNS:
         if (br.vec) close();  // u_j * p_i is not separable: new stage
@@ -113,8 +114,8 @@ struct StageBuilder {
           bc.addc(br.cval);
           br.set(0.0);
         }
-        ac.mulv(o.vec);
-        bc.mulv(o.vec);
+        ac.mulv(o.vec, bs);
+        bc.mulv(o.vec, bs);
         break;
     }
   }
@@ -137,6 +138,9 @@ struct pw_expr {
   bool band = false;
   int64_t lo = -kBandNone, hi = kBandNone;
   const int64_t *grow = nullptr, *gcol = nullptr;
+  // Batch (pw_bind_batched): B elements; element b reads X + b * sx, Y +
+  // b * sy, V + b * sv and each op vector + b * its stride (elements).
+  int64_t B = 1, sx = 0, sy = 0, sv = 0;
 };
 
 namespace {
@@ -185,6 +189,9 @@ struct Plan {
   bool col_norms = false;
   size_t off_epi = 0, off_ny = 0, off_part = 0, part_bytes = 0, total = 0;
   std::vector<size_t> stage_off;  // per stage: offset of its vectors
+  // Batched expressions: bytes between consecutive elements' epilogue
+  // vectors, column norms and partials (0: shared).
+  size_t epi_stride = 0, ny_stride = 0, part_stride = 0;
 };
 
 int valu_dtile(int64_t D) { return D <= 3 ? 3 : (D <= 4 ? 4 : (D <= 16 ? 16 : 64)); }
@@ -219,6 +226,10 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     }
   }
   p.off_epi = 0;
+  if (e.B > 1) {  // one set of epilogue vectors per batch element
+    p.epi_stride = align_up(off);
+    off = p.epi_stride * (size_t)e.B;
+  }
   const int cus = target_cus();
   int64_t target_wgs = 4 * (int64_t)cus;
   if (mfma_eligible(e, consumer, C)) {
@@ -275,7 +286,11 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   // for cosine on either engine.
   p.col_norms = (p.family == 1 && e.metric != PW_LINEAR) || e.metric == PW_COSINE;
   p.off_ny = off;
-  if (p.col_norms) off += align_up((size_t)e.M * es);
+  if (p.col_norms) {
+    const size_t one = align_up((size_t)e.M * es);
+    if (e.B > 1 && e.sy != 0) p.ny_stride = one;  // per element, unless Y is shared
+    off += e.B > 1 && e.sy != 0 ? one * (size_t)e.B : one;
+  }
   // Tile grid: enough workgroups to fill the chip, splitting the columns
   // when there are too few row blocks.
   p.n_rb = (int)((e.N + p.bm - 1) / p.bm);
@@ -319,6 +334,10 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       case PW_C_TOPK: per_row = (size_t)k * (e.dtype == PW_F32 ? 8 : 16); break;
     }
     p.part_bytes = align_up((size_t)p.n_part * (size_t)e.N * per_row);
+    if (e.B > 1) {
+      p.part_stride = p.part_bytes;
+      p.part_bytes *= (size_t)e.B;
+    }
   }
   p.total = p.off_part + p.part_bytes;
   if (p.total) p.total += kAlign;  // room to align the caller's pointer
@@ -355,9 +374,10 @@ int prepare_epilogue(const pw_expr &e, const Plan &p, char *base, Epi *epi, hipS
     vp.n = (int)pr.ins.size();
     vp.len = len;
     vp.out = out;
+    vp.out_bstride = (int64_t)p.epi_stride;
     for (size_t t = 0; t < pr.ins.size(); ++t) vp.ins[t] = pr.ins[t];
     if (batch.n_progs == kProgsPerLaunch) {
-      int rc = hip_status(launch_vec_progs(e.dtype, batch, s));
+      int rc = hip_status(launch_vec_progs(e.dtype, batch, e.B, s));
       std::memset(&batch, 0, sizeof(batch));
       return rc;
     }
@@ -390,7 +410,7 @@ int prepare_epilogue(const pw_expr &e, const Plan &p, char *base, Epi *epi, hipS
     }
     if (rc != PW_OK) return rc;
   }
-  if (batch.n_progs) return hip_status(launch_vec_progs(e.dtype, batch, s));
+  if (batch.n_progs) return hip_status(launch_vec_progs(e.dtype, batch, e.B, s));
   return PW_OK;
 }
 
@@ -411,6 +431,13 @@ TileArgs base_args(const pw_expr &e, const Plan &p, char *base) {
   a.split_cols = p.split_cols;
   a.partial = p.n_part > 1 ? base + p.off_part : nullptr;
   a.ny = p.col_norms ? base + p.off_ny : nullptr;
+  const int64_t es = (int64_t)esize(e.dtype);
+  a.bat.n = e.B;
+  a.bat.x = e.sx * es;
+  a.bat.y = e.sy * es;
+  a.bat.part = (int64_t)p.part_stride;
+  a.bat.ny = (int64_t)p.ny_stride;
+  a.bat.epi = (int64_t)p.epi_stride;
   // Taylor coefficients of e^(a f) - 1, a = ln2/256, for the double exp2.
   const long double ak = logl(2.0L) / 256.0L;
   long double c = 1.0L;
@@ -457,8 +484,10 @@ hipError_t launch_tile(const pw_expr &e, int consumer, const Plan &p, const Tile
 // Column norms |y_j|^2 for the MFMA engine's distance expansion.
 int prepare_norms(const pw_expr &e, const Plan &p, const TileArgs &a, hipStream_t s) {
   if (!p.col_norms) return PW_OK;
-  return hip_status(
-      launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s, e.metric == PW_COSINE));
+  const bool per = e.B > 1 && e.sy != 0;
+  return hip_status(launch_row_norms(e.dtype, e.Y, e.M, e.ldy, (int)e.D, const_cast<void *>(a.ny), s,
+                                     e.metric == PW_COSINE, per ? e.B : 1, per ? a.bat.y : 0,
+                                     (int64_t)p.ny_stride));
 }
 
 // Mask arguments, and the group ranges per row block and key tile.
@@ -535,10 +564,23 @@ const char *pw_error_string(int code) {
   }
 }
 
-int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
-            const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops) {
+static int bind_impl(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
+                     const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops,
+                     const pw_batch *batch) {
   if (!out) return PW_ERR_INVALID;
   *out = nullptr;
+  const int64_t *op_bstride = batch ? batch->op_stride : nullptr;
+  if (batch) {
+    if (batch->B < 1 || batch->sx < 0 || batch->sy < 0 || batch->sv < 0) return PW_ERR_INVALID;
+    if (batch->B > kMaxBatch) return PW_ERR_UNSUPPORTED;
+    for (int t = 0; t < n_ops && t < PW_MAX_OPS; ++t) {
+      if (op_bstride[t] < 0) return PW_ERR_INVALID;
+      const int k = ops ? ops[t].kind : -1;
+      const bool vec = k == PW_OP_ADD_ROWS || k == PW_OP_ADD_COLUMNS || k == PW_OP_WEIGHT_ROWS ||
+                       k == PW_OP_WEIGHT_COLUMNS;
+      if (!vec && op_bstride[t] != 0) return PW_ERR_UNSUPPORTED;  // masks are shared by the batch
+    }
+  }
   if (dtype != PW_F32 && dtype != PW_F64) return PW_ERR_INVALID;
   if (metric < PW_LINEAR || metric > PW_COSINE) return PW_ERR_INVALID;
   if (metric == PW_RBF && !(std::isfinite(gamma) && gamma >= 0.0)) return PW_ERR_INVALID;
@@ -624,15 +666,33 @@ int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, i
   e->hi = std::max(std::min(e->hi, kBandNone), -kBandNone);
   e->lo = std::max(std::min(e->lo, kBandNone), -kBandNone);
   StageBuilder b;
-  for (const pw_op &o : e->ops) b.op(o);
+  for (size_t t = 0; t < e->ops.size(); ++t) b.op(e->ops[t], op_bstride ? op_bstride[t] * (int64_t)es : 0);
   b.close();
   e->stages = b.out;
   if (e->stages.size() > (size_t)kMaxStages) {
     delete e;
     return PW_ERR_UNSUPPORTED;
   }
+  if (batch) {
+    e->B = batch->B;
+    e->sx = batch->sx;
+    e->sy = batch->sy;
+    e->sv = batch->sv;
+  }
   *out = e;
   return PW_OK;
+}
+
+int pw_bind(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
+            const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops) {
+  return bind_impl(out, dtype, metric, gamma, X, N, ldx, Y, M, ldy, D, ops, n_ops, nullptr);
+}
+
+int pw_bind_batched(pw_expr **out, int dtype, int metric, double gamma, const void *X, int64_t N, int64_t ldx,
+                    const void *Y, int64_t M, int64_t ldy, int64_t D, const pw_op *ops, int n_ops,
+                    const pw_batch *batch) {
+  if (!batch) return PW_ERR_INVALID;
+  return bind_impl(out, dtype, metric, gamma, X, N, ldx, Y, M, ldy, D, ops, n_ops, batch);
 }
 
 void pw_release(pw_expr *e) { delete e; }
@@ -673,15 +733,15 @@ int pw_plan_describe(const pw_expr *e, int consumer, int64_t C, int k, char *buf
   if (p.family == 1)
     std::snprintf(buf, len,
                   "family=mfma dp=%d cp=%d kl=%d bm=%d bn=%d row_blocks=%d row_block_pairs=%d splits=%d partials=%d "
-                  "split_cols=%lld stages=%d workspace=%zu",
+                  "split_cols=%lld stages=%d batch=%lld workspace=%zu",
                   p.mcfg.dp, p.mcfg.cp, p.mcfg.kl, p.bm, p.bn, p.n_rb, p.rb_pairs, p.n_split, p.n_part,
-                  (long long)p.split_cols, (int)e->stages.size(), p.total);
+                  (long long)p.split_cols, (int)e->stages.size(), (long long)e->B, p.total);
   else
     std::snprintf(buf, len,
                   "family=valu dtile=%d vtile=%d rows=%d bm=%d bn=%d row_blocks=%d splits=%d split_cols=%lld stages=%d "
-                  "workspace=%zu",
+                  "batch=%lld workspace=%zu",
                   p.vcfg.dtile, p.vcfg.vtile, p.vcfg.rows, p.bm, p.bn, p.n_rb, p.n_split, (long long)p.split_cols,
-                  (int)e->stages.size(), p.total);
+                  (int)e->stages.size(), (long long)e->B, p.total);
   return PW_OK;
 }
 
@@ -697,9 +757,9 @@ static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t
   if (lse_out && !aligned(lse_out, es)) return PW_ERR_INVALID;
   if (e->N == 0) return PW_OK;
   hipStream_t s = (hipStream_t)stream;
-  if (e->M == 0) {
-    rc = hip_status(launch_fill(e->dtype, out, e->N, C, ldo, 0.0, s));
-    if (rc == PW_OK && lse_out) rc = hip_status(launch_fill(e->dtype, lse_out, e->N, 1, 1, -HUGE_VAL, s));
+  if (e->M == 0) {  // batched outputs are packed: B * N rows
+    rc = hip_status(launch_fill(e->dtype, out, e->B * e->N, C, ldo, 0.0, s));
+    if (rc == PW_OK && lse_out) rc = hip_status(launch_fill(e->dtype, lse_out, e->B * e->N, 1, 1, -HUGE_VAL, s));
     return rc;
   }
   Plan p = make_plan(*e, consumer, C, 0);
@@ -712,6 +772,9 @@ static int value_consumer(const pw_expr *e, int consumer, const void *V, int64_t
   a.ldv = ldv;
   a.ldo = ldo;
   a.lse_out = consumer == PW_C_SOFTMAX_MATMUL ? lse_out : nullptr;
+  a.bat.out = e->N * ldo * (int64_t)es;
+  a.bat.lse = a.lse_out ? e->N * (int64_t)es : 0;
+  a.bat.v = e->sv * (int64_t)es;
   const int cons = consumer == PW_C_MATMUL ? C_MATMUL : C_SOFTMAX;
   for (int64_t c0 = 0; c0 < C && rc == PW_OK; c0 += p.chunk) {
     a.C = (int)std::min<int64_t>(p.chunk, C - c0);
@@ -744,7 +807,7 @@ int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t w
   if (ldo < e->D || (e->N > 0 && !out) || !aligned(out, esize(e->dtype))) return PW_ERR_INVALID;
   if (e->N == 0) return PW_OK;
   hipStream_t s = (hipStream_t)stream;
-  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->N, e->D, ldo, 0.0, s));
+  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->B * e->N, e->D, ldo, 0.0, s));
   Plan p = make_plan(*e, PW_C_DISPLACEMENT, 0, 0);
   char *base;
   rc = check_ws(p, ws, ws_bytes, &base);
@@ -754,6 +817,7 @@ int pw_displacement(const pw_expr *e, void *out, int64_t ldo, void *ws, size_t w
   if (rc != PW_OK) return rc;
   a.out = out;
   a.ldo = ldo;
+  a.bat.out = e->N * ldo * (int64_t)esize(e->dtype);
   return run_tiles(*e, C_DISPLACEMENT, p, a, s);
 }
 
@@ -764,7 +828,7 @@ int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t
   if ((e->N > 0 && !out) || !aligned(out, esize(e->dtype))) return PW_ERR_INVALID;
   if (e->N == 0) return PW_OK;
   hipStream_t s = (hipStream_t)stream;
-  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->N, 1, 1, -HUGE_VAL, s));
+  if (e->M == 0) return hip_status(launch_fill(e->dtype, out, e->B * e->N, 1, 1, -HUGE_VAL, s));
   Plan p = make_plan(*e, PW_C_LOGSUMEXP, 0, 0);
   char *base;
   rc = check_ws(p, ws, ws_bytes, &base);
@@ -774,6 +838,7 @@ int pw_logsumexp(const pw_expr *e, int exclude_self, void *out, void *ws, size_t
   if (rc != PW_OK) return rc;
   a.out = out;
   a.exclude_self = exclude_self;
+  a.bat.out = e->N * (int64_t)esize(e->dtype);
   return run_tiles(*e, C_LOGSUMEXP, p, a, s);
 }
 
@@ -796,6 +861,8 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
   a.idx = indices;
   a.k = k;
   a.largest = largest;
+  a.bat.out = e->N * k * (int64_t)esize(e->dtype);
+  a.bat.idx = e->N * k * (int64_t)sizeof(int64_t);
   return run_tiles(*e, C_TOPK, p, a, s);
 }
 
@@ -882,6 +949,7 @@ extern "C" {
 
 int pw_backward_plan_describe(const pw_expr *e, int consumer, int64_t C, int want_ops, char *buf, size_t len) {
   if (!e || !buf || len == 0 || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
+  if (e->B > 1) return PW_ERR_UNSUPPORTED;  // the backward runs per batch element
   const GradPlan g = grad_plan(*e, consumer, std::max<int64_t>(C, 1));
   const bool fast = !want_ops && e->stages.size() <= 1 && (e->stages.empty() || e->stages[0].kind == ST_AFFINE);
   const bool col_stage = !e->stages.empty() && e->stages[0].col_vec;
@@ -901,6 +969,7 @@ int pw_backward_plan_describe(const pw_expr *e, int consumer, int64_t C, int wan
 int pw_backward_workspace_size(const pw_expr *e, int consumer, int64_t C, int k, size_t *bytes) {
   (void)k;
   if (!e || !bytes || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
+  if (e->B > 1) return PW_ERR_UNSUPPORTED;
   *bytes = grad_plan(*e, consumer, std::max<int64_t>(C, 1)).total;
   return PW_OK;
 }
@@ -908,6 +977,7 @@ int pw_backward_workspace_size(const pw_expr *e, int consumer, int64_t C, int k,
 int pw_backward(const pw_expr *e, int consumer, const pw_grad_in *in, const pw_grad_out *out, void *ws,
                 size_t ws_bytes, void *stream) {
   if (!e || !in || !out || consumer < PW_C_MATMUL || consumer > PW_C_TOPK) return PW_ERR_INVALID;
+  if (e->B > 1) return PW_ERR_UNSUPPORTED;
   const size_t es = esize(e->dtype);
   const bool value = consumer == PW_C_MATMUL || consumer == PW_C_SOFTMAX_MATMUL;
   const int64_t C = value ? in->C : 0;
@@ -1193,6 +1263,7 @@ extern "C" {
 
 int pw_cg_workspace_size(const pw_expr *e, int64_t C, size_t *bytes) {
   if (!e || !bytes || C < 1) return PW_ERR_INVALID;
+  if (e->B > 1) return PW_ERR_UNSUPPORTED;  // one system per solve
   *bytes = cg_layout(*e, C).total;
   return PW_OK;
 }
@@ -1201,6 +1272,7 @@ int pw_cg_solve(const pw_expr *e, double shift, const void *B, int64_t C, int64_
                 int max_iter, double rtol, int check_every, void *ws, size_t ws_bytes, void *stream,
                 pw_solve_info *info) {
   if (!e || !info || e->N != e->M || C < 1 || ldb < C || lda < C) return PW_ERR_INVALID;
+  if (e->B > 1) return PW_ERR_UNSUPPORTED;
   if (!(std::isfinite(shift) && shift > 0) || !(std::isfinite(rtol) && rtol >= 0)) return PW_ERR_INVALID;
   if (max_iter < 1 || check_every < 1) return PW_ERR_INVALID;
   const size_t es = esize(e->dtype);

@@ -46,12 +46,14 @@ constexpr int kMaxVecInstr = 12;
 struct VecInstr {
   int op;
   double c;
-  const void *v;  // dtype vector for VO_MULV / VO_ADDV
+  const void *v;    // dtype vector for VO_MULV / VO_ADDV
+  int64_t bstride;  // bytes between the vectors of consecutive batch elements (0: shared)
 };
 struct VecProg {
   int n;
   int64_t len;
-  void *out;  // dtype vector of `len` elements
+  void *out;            // dtype vector of `len` elements
+  int64_t out_bstride;  // bytes between consecutive batch elements' outputs
   VecInstr ins[kMaxVecInstr];
 };
 constexpr int kProgsPerLaunch = 6;
@@ -88,6 +90,16 @@ struct MaskArgs {
 };
 constexpr int64_t kBandNone = (int64_t)1 << 62;
 
+// Batched launches: the grid's z index is the batch element, and each array
+// below is offset by z times its stride in bytes (0: one array serves every
+// element; an absent array, a null pointer, always has stride 0). Masks and
+// their tables are shared by every element.
+struct BatchArgs {
+  int64_t n;  // batch elements (1: an unbatched call)
+  int64_t x, y, v, out, idx, lse, part, ny, epi;
+};
+constexpr int64_t kMaxBatch = 65535;  // the grid's z extent
+
 struct TileArgs {
   const void *X;
   int64_t ldx;
@@ -117,6 +129,7 @@ struct TileArgs {
   double exp2_c[4];      // (ln2/256)^k / k!, k = 1..4, for the table-driven double exp2
   Epi epi;
   MaskArgs mask;
+  BatchArgs bat;
 };
 
 // Top-k partial key layouts in the workspace.
@@ -293,7 +306,7 @@ hipError_t launch_cg_scalars(int phase, const double *part, int nblk, int C, CgS
                              hipStream_t s);
 
 // Auxiliary kernels.
-hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, hipStream_t s);
+hipError_t launch_vec_progs(int dtype, const VecProgBatch &b, int64_t n_batch, hipStream_t s);
 // Per block of `block` entries of g[0..n): min and max, written as pairs.
 hipError_t launch_group_ranges(const int64_t *g, int64_t n, int block, int64_t *out, hipStream_t s);
 // Per row block of bm rows: the column span [first, end) of the key tiles of
@@ -302,8 +315,11 @@ hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, in
                              hipStream_t s);
 hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);
 // Row norms |x_i|^2, or with `inverse` 1/|x_i| (0 for a zero row).
+// With n_batch > 1, element b reads X + b * x_bstride and writes out +
+// b * out_bstride (bytes).
 hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int D, void *out, hipStream_t s,
-                            bool inverse = false);
+                            bool inverse = false, int64_t n_batch = 1, int64_t x_bstride = 0,
+                            int64_t out_bstride = 0);
 hipError_t launch_merge(int dtype, int consumer, const TileArgs &a, hipStream_t s);
 
 }  // namespace pw

@@ -78,6 +78,7 @@ __device__ __forceinline__ T valu_metric(const T (&x)[DT], const T *y, T neg_gam
 
 template <class T, int METRIC, int CONS, int DT, int VT>
 __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   constexpr int BM = kValuBM, BN = kValuBN;
   constexpr bool HAS_V = (CONS == C_MATMUL || CONS == C_SOFTMAX);
   constexpr int VW = HAS_V ? VT : 1;
@@ -121,9 +122,9 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   const T pre_s = PRE ? (T)sqrt(a.gamma * kLog2e) : (T)1;
   T x[DT];
 #pragma unroll
-  for (int d = 0; d < DT; ++d) x[d] = (rv && d < a.D) ? ldg<T>(a.X, i * a.ldx + d) * pre_s : (T)0;
+  for (int d = 0; d < DT; ++d) x[d] = (rv && d < a.D) ? ldg<T>(bp.X, i * a.ldx + d) * pre_s : (T)0;
   RowEpi<T> re;
-  load_row_epi<T>(a.epi, i, rv, re);
+  load_row_epi<T>(a.epi, i, rv, re, epi_shift(a));
   const T neg_gamma = sizeof(T) == 4 ? (T)(-a.gamma * kLog2e) : (T)(-a.gamma);
   T rx = 0;  // 1/|x_i| for cosine (0 for a zero row)
   if constexpr (METRIC == M_COSINE) {
@@ -179,16 +180,16 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     __syncthreads();
     for (int e = tid; e < BN * DT; e += BM) {
       int jj = e / DT, d = e % DT;
-      sY[jj][d] = (jj < nb && d < a.D) ? ldg<T>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : (T)0;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<T>(bp.Y, (j0 + jj) * a.ldy + d) * pre_s : (T)0;
     }
     if constexpr (HAS_V) {
       for (int e = tid; e < BN * VW; e += BM) {
         int jj = e / VW, c = e % VW;
-        sV[jj][c] = (jj < nb && c < a.C) ? ldg<T>(a.V, (j0 + jj) * a.ldv + c) : (T)0;
+        sV[jj][c] = (jj < nb && c < a.C) ? ldg<T>(bp.V, (j0 + jj) * a.ldv + c) : (T)0;
       }
     }
     if constexpr (METRIC == M_COSINE) {
-      for (int e = tid; e < BN; e += BM) sR[e] = e < nb ? ldg<T>(a.ny, j0 + e) : (T)0;
+      for (int e = tid; e < BN; e += BM) sR[e] = e < nb ? ldg<T>(bp.ny, j0 + e) : (T)0;
     }
     if (check) {
       for (int e = tid; e < BN; e += BM) {
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
         int st = e / BN, jj = e % BN;
         if (st < a.epi.n_stages && a.epi.st[st].col_vec) {
           bool ok = jj < nb;
-          sQ[st][jj] = ok ? ldg<T>(a.epi.st[st].q_vec, j0 + jj) : (T)1;
-          sO[st][jj] = ok ? ldg<T>(a.epi.st[st].o_vec, j0 + jj) : (T)0;
+          sQ[st][jj] = ok ? ldg<T>(epi_vec(a, a.epi.st[st].q_vec), j0 + jj) : (T)1;
+          sO[st][jj] = ok ? ldg<T>(epi_vec(a, a.epi.st[st].o_vec), j0 + jj) : (T)0;
         }
       }
     }
@@ -454,33 +455,33 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   const bool fin = a.n_split == 1;
   const int64_t prow = (int64_t)sp * a.N + i;  // partial row
   if constexpr (CONS == C_MATMUL) {
-    T *o = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.C;
+    T *o = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow * a.C;
 #pragma unroll
     for (int c = 0; c < ACCN; ++c)
       if (c < a.C) o[c] = acc[c];
   } else if constexpr (CONS == C_DISPLACEMENT) {
-    T *o = fin ? static_cast<T *>(a.out) + i * a.ldo : static_cast<T *>(a.partial) + prow * a.D;
+    T *o = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow * a.D;
 #pragma unroll
     for (int d = 0; d < ACCN; ++d)
       if (d < a.D) o[d] = acc[d] - x[d] * mass;
   } else if constexpr (CONS == C_LOGSUMEXP) {
     if (fin) {
-      static_cast<T *>(a.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
+      static_cast<T *>(bp.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
     } else {
-      T *o = static_cast<T *>(a.partial) + prow * 2;
+      T *o = static_cast<T *>(bp.partial) + prow * 2;
       o[0] = m;
       o[1] = l;
     }
   } else if constexpr (CONS == C_SOFTMAX) {
-    if (fin && a.lse_out) static_cast<T *>(a.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
+    if (fin && bp.lse_out) static_cast<T *>(bp.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
     if (fin) {
-      T *o = static_cast<T *>(a.out) + i * a.ldo;
+      T *o = static_cast<T *>(bp.out) + i * a.ldo;
       const T inv = (l > (T)0) ? (T)1 / l : (T)0;
 #pragma unroll
       for (int c = 0; c < ACCN; ++c)
         if (c < a.C) o[c] = acc[c] * inv;
     } else {
-      T *o = static_cast<T *>(a.partial) + prow * (a.C + 2);
+      T *o = static_cast<T *>(bp.partial) + prow * (a.C + 2);
       o[0] = m;
       o[1] = l;
 #pragma unroll
@@ -497,8 +498,8 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     for (int p = 0; p < KL; ++p)
       list[p] = lj[p] == ~0u ? Key<T>::sentinel() : Key<T>::make(a.largest ? -lv[p] : lv[p], lj[p], a.largest);
     if (fin) {
-      T *v = static_cast<T *>(a.out) + i * a.k;
-      int64_t *ix = a.idx + i * a.k;
+      T *v = static_cast<T *>(bp.out) + i * a.k;
+      int64_t *ix = bp.idx + i * a.k;
 #pragma unroll
       for (int p = 0; p < KL; ++p)
         if (p < a.k) {
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
     } else {
 #pragma unroll
       for (int p = 0; p < KL; ++p)
-        if (p < a.k) list[p].store(a.partial, prow * a.k + p);
+        if (p < a.k) list[p].store(bp.partial, prow * a.k + p);
     }
   }
 }
@@ -533,8 +534,13 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
 // so identical points still score exactly 1 there.
 constexpr float kExpansionBound = 64.f;
 
+// Waves per SIMD each product kernel is held to: what its registers allow,
+// so that the scheduler does not trade occupancy for a deeper schedule.
+constexpr int prod_waves(int metric, int dt) { return metric == M_RBF ? (dt == 3 ? 5 : 4) : (dt == 3 ? 8 : 7); }
+
 template <int METRIC, int DT, int R>
-__global__ __launch_bounds__(kValuBM) void valu_prod_rn(const TileArgs a) {
+__global__ __launch_bounds__(kValuBM) __attribute__((amdgpu_waves_per_eu(prod_waves(METRIC, DT)))) void valu_prod_rn(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   constexpr int BN = kValuBM;  // columns per tile: one staged per thread
   static_assert(DT == 3 || DT == 4, "narrow points only");
   constexpr bool RBF = METRIC == M_RBF;
@@ -551,8 +557,8 @@ __global__ __launch_bounds__(kValuBM) void valu_prod_rn(const TileArgs a) {
   const float pre_s = RBF ? (float)sqrt(a.gamma * kLog2e) : 1.f;
 
   // Row operand: 2 x~ for rbf (the expansion's factor; x~ = half of it,
-  // exactly), else x itself. One copy keeps the register count at five
-  // waves per SIMD.
+  // exactly), else x itself. One copy keeps the rbf kernel within five waves
+  // per SIMD for three features (four for four).
   int64_t i[R];
   float xr[R][DT], acc[R][4], x0[R];
   bool near_all = true;
@@ -563,7 +569,7 @@ __global__ __launch_bounds__(kValuBM) void valu_prod_rn(const TileArgs a) {
     float n2 = 0.f;
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const float xv = (rv && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+      const float xv = (rv && d < a.D) ? ldg<float>(bp.X, i[u] * a.ldx + d) * pre_s : 0.f;
       xr[u][d] = RBF ? 2.f * xv : xv;
       n2 = fmaf(xv, xv, n2);
     }
@@ -585,9 +591,9 @@ __global__ __launch_bounds__(kValuBM) void valu_prod_rn(const TileArgs a) {
     const int64_t j = jb + (int64_t)t * BN + tid;
     const bool cv = j < je;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) ry[d] = (cv && d < a.D) ? ldg<float>(a.Y, j * a.ldy + d) : 0.f;
+    for (int d = 0; d < DT; ++d) ry[d] = (cv && d < a.D) ? ldg<float>(bp.Y, j * a.ldy + d) : 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) rv4[c] = (cv && c < a.C) ? ldg<float>(a.V, j * a.ldv + c) : 0.f;
+    for (int c = 0; c < 4; ++c) rv4[c] = (cv && c < a.C) ? ldg<float>(bp.V, j * a.ldv + c) : 0.f;
   };
   auto stage = [&](int t) {
     const int b = t & 1;
@@ -674,8 +680,8 @@ __global__ __launch_bounds__(kValuBM) void valu_prod_rn(const TileArgs a) {
   for (int u = 0; u < R; ++u) {
     if (i[u] >= a.N) continue;
     const float f = (RBF && defer) ? __builtin_amdgcn_exp2f(-x0[u]) : 1.f;
-    float *o = fin ? static_cast<float *>(a.out) + i[u] * a.ldo
-                   : static_cast<float *>(a.partial) + ((int64_t)sp * a.N + i[u]) * a.C;
+    float *o = fin ? static_cast<float *>(bp.out) + i[u] * a.ldo
+                   : static_cast<float *>(bp.partial) + ((int64_t)sp * a.N + i[u]) * a.C;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       if (c < a.C) o[c] = acc[u][c] * f;
@@ -709,7 +715,8 @@ __device__ __forceinline__ void r2_min_tile(const float (&x)[2][DT], const float
 }
 
 template <int METRIC, int DT>
-__global__ __launch_bounds__(kValuBM) void valu_tile_r2_min(const TileArgs a) {
+__global__ __launch_bounds__(kValuBM) __attribute__((amdgpu_waves_per_eu(8))) void valu_tile_r2_min(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   constexpr int BN = kValuBN, R = 2;
   __shared__ float sY[BN][DT];
   const int tid = threadIdx.x;
@@ -729,7 +736,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_min(const TileArgs a) {
     i[u] = (int64_t)rb * (R * kValuBM) + u * kValuBM + tid;
     rv[u] = i[u] < a.N;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(bp.X, i[u] * a.ldx + d) * pre_s : 0.f;
     thr[u] = __builtin_huge_valf();
     bj[u] = ~0u;
   }
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_min(const TileArgs a) {
     __syncthreads();
     for (int e = tid; e < BN * DT; e += kValuBM) {
       const int jj = e / DT, d = e % DT;
-      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(bp.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
     }
     __syncthreads();
     int bl[R] = {-1, -1};  // tile slot of each row's best column met in this tile
@@ -755,10 +762,10 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_min(const TileArgs a) {
     const Key<float> key =
         bj[u] == ~0u ? Key<float>::sentinel() : Key<float>::make(a.largest ? -thr[u] : thr[u], bj[u], a.largest);
     if (fin) {
-      static_cast<float *>(a.out)[i[u] * a.k] = key.value(a.largest);
-      a.idx[i[u] * a.k] = key.out_index();
+      static_cast<float *>(bp.out)[i[u] * a.k] = key.value(a.largest);
+      bp.idx[i[u] * a.k] = key.out_index();
     } else {
-      key.store(a.partial, ((int64_t)sp * a.N + i[u]) * a.k);
+      key.store(bp.partial, ((int64_t)sp * a.N + i[u]) * a.k);
     }
   }
 }
@@ -807,6 +814,7 @@ __device__ __forceinline__ void r2_lse_tile(const float (&x)[2][DT], const float
 
 template <int METRIC, int DT>
 __global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
+  const BatchPtrs bp = batch_ptrs(a);
   constexpr int BN = kValuBN, R = 2;
   __shared__ float sY[BN][DT];
   const int tid = threadIdx.x;
@@ -826,14 +834,14 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
     i[u] = r0 + u * kValuBM + tid;
     rv[u] = i[u] < a.N;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(a.X, i[u] * a.ldx + d) * pre_s : 0.f;
+    for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(bp.X, i[u] * a.ldx + d) * pre_s : 0.f;
     float r = 1.f, p = 0.f;
     if (a.epi.n_stages == 1) {
       const Stage &st = a.epi.st[0];
       if (st.row_vec) {
         if (rv[u]) {
-          r = ldg<float>(st.r_vec, i[u]);
-          p = ldg<float>(st.p_vec, i[u]);
+          r = ldg<float>(epi_vec(a, st.r_vec), i[u]);
+          p = ldg<float>(epi_vec(a, st.p_vec), i[u]);
         }
       } else {
         r = (float)st.r_scalar;
@@ -852,7 +860,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
     __syncthreads();
     for (int e = tid; e < BN * DT; e += kValuBM) {
       const int jj = e / DT, d = e % DT;
-      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(a.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(bp.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
     }
     __syncthreads();
     const bool check = nb < BN || (excl && j0 <= r1 && j0 + BN > r0);  // uniform over the workgroup
@@ -865,9 +873,9 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
     if (!rv[u]) continue;
     const float mn = m[u] == -__builtin_huge_valf() ? m[u] : m[u] * kLn2_f;  // back to natural units
     if (fin) {
-      static_cast<float *>(a.out)[i[u]] = l[u] > 0.f ? mn + dlog(l[u]) : -__builtin_huge_valf();
+      static_cast<float *>(bp.out)[i[u]] = l[u] > 0.f ? mn + dlog(l[u]) : -__builtin_huge_valf();
     } else {
-      float *o = static_cast<float *>(a.partial) + ((int64_t)sp * a.N + i[u]) * 2;
+      float *o = static_cast<float *>(bp.partial) + ((int64_t)sp * a.N + i[u]) * 2;
       o[0] = mn;
       o[1] = l[u];
     }
@@ -876,7 +884,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
 
 template <class T, int METRIC, int CONS, int DT, int VT>
 hipError_t launch_valu_kernel(const TileArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
+  dim3 grid((unsigned)(a.n_rb * a.n_split), 1, (unsigned)a.bat.n), block(kValuBM);
   hipLaunchKernelGGL((valu_tile<T, METRIC, CONS, DT, VT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
@@ -915,14 +923,14 @@ hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArg
   if constexpr (sizeof(T) == 4 && METRIC != M_COSINE) {
     if (consumer == C_MATMUL && cfg.rows == kProdRows) {
       if ((cfg.dtile != 3 && cfg.dtile != 4) || cfg.vtile != 4) return hipErrorInvalidValue;
-      dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
+      dim3 grid((unsigned)(a.n_rb * a.n_split), 1, (unsigned)a.bat.n), block(kValuBM);
       if (cfg.dtile == 3) hipLaunchKernelGGL((valu_prod_rn<METRIC, 3, kProdRows>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((valu_prod_rn<METRIC, 4, kProdRows>), grid, block, 0, s, a);
       return hipGetLastError();
     }
     if (cfg.rows == 2) {
       if (cfg.dtile != 3 && cfg.dtile != 4) return hipErrorInvalidValue;
-      dim3 grid((unsigned)(a.n_rb * a.n_split)), block(kValuBM);
+      dim3 grid((unsigned)(a.n_rb * a.n_split), 1, (unsigned)a.bat.n), block(kValuBM);
       if (consumer == C_LOGSUMEXP) {
         if (cfg.dtile == 3) hipLaunchKernelGGL((valu_tile_r2_lse<METRIC, 3>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((valu_tile_r2_lse<METRIC, 4>), grid, block, 0, s, a);

@@ -99,7 +99,7 @@ def ws_size(lib, h, consumer, C=0, k=0):
 
 def test_workspace_size_bounded(lib):
     """The workspace never grows with N*M: at fixed N it is constant in M
-    (the guide's 'tile workspace'), and it scales with N (C + k)."""
+    (the guide's introduction bounds scratch by the tiles), and it scales with N (C + k)."""
     for cons, C, k in ((0, 4, 0), (1, 0, 0), (2, 0, 0), (3, 64, 0), (4, 0, 10)):
         sizes = []
         for M in (4096, 65536, 1 << 20, 1 << 24):
@@ -303,3 +303,57 @@ def test_blocked_vector_kernels_only_where_they_apply(lib):
     ]
     for p in one_row:
         assert p["family"] == "valu" and p["rows"] == "1", p
+
+
+def _bind_batched(lib, B=5, sx=0, sy=12 * 4, sv=0, N=10, M=12, D=4, ops=(), op_stride=(), metric=1):
+    h = ctypes.c_void_p()
+    arr = (pw._Op * max(len(ops), 1))()
+    for t, (kind, scalar, vec) in enumerate(ops):
+        arr[t].kind, arr[t].scalar, arr[t].vec = kind, scalar, vec
+    bt = pw._Batch()
+    bt.B, bt.sx, bt.sy, bt.sv = B, sx, sy, sv
+    for t, s in enumerate(op_stride):
+        bt.op_stride[t] = s
+    rc = lib.pw_bind_batched(ctypes.byref(h), 0, metric, 1.0, FAKE, N, D, FAKE, M, D, D, arr, len(ops),
+                             ctypes.byref(bt))
+    return rc, h
+
+
+def test_bind_batched_validation(lib):
+    """A batch of B elements: strides >= 0, B in 1..65535, masks and scalar
+    ops shared (stride 0); the plan reports the batch, the workspace holds
+    one set of partials per element and never grows with N*M; backward and
+    CG take unbatched handles only."""
+    rc, h = _bind_batched(lib)
+    assert rc == pw.PW_OK and h.value
+    buf = ctypes.create_string_buffer(512)
+    assert lib.pw_plan_describe(h, 0, 4, 0, buf, 512) == pw.PW_OK and b"batch=5" in buf.value
+    n5 = ctypes.c_size_t()
+    assert lib.pw_workspace_size(h, 4, 0, 3, ctypes.byref(n5)) == pw.PW_OK
+    gin, gout = pw._GradIn(), pw._GradOut()
+    assert lib.pw_backward(h, 0, ctypes.byref(gin), ctypes.byref(gout), FAKE, 1 << 20, None) == pw.PW_ERR_UNSUPPORTED
+    nb = ctypes.c_size_t()
+    assert lib.pw_backward_workspace_size(h, 0, 4, 0, ctypes.byref(nb)) == pw.PW_ERR_UNSUPPORTED
+    assert lib.pw_cg_workspace_size(h, 1, ctypes.byref(nb)) == pw.PW_ERR_UNSUPPORTED
+    lib.pw_release(h)
+    # Per-element partials: a wide split plan at B = 1 and B = 7.
+    sizes = []
+    for B in (1, 7):
+        rc, h = _bind_batched(lib, B=B, N=300, M=200000, D=32)
+        n = ctypes.c_size_t()
+        assert rc == pw.PW_OK and lib.pw_workspace_size(h, 4, 0, 10, ctypes.byref(n)) == pw.PW_OK
+        sizes.append(n.value)
+        lib.pw_release(h)
+    assert sizes[1] > 6 * (sizes[0] - 4096) and sizes[1] < 300 * 200000, sizes
+    assert _bind_batched(lib, B=0)[0] == pw.PW_ERR_INVALID
+    assert _bind_batched(lib, B=65536)[0] == pw.PW_ERR_UNSUPPORTED
+    assert _bind_batched(lib, sx=-1)[0] == pw.PW_ERR_INVALID
+    assert _bind_batched(lib, sv=-4)[0] == pw.PW_ERR_INVALID
+    addr = [(pw.OPS["add_rows"], 0.0, FAKE)]
+    assert _bind_batched(lib, ops=addr, op_stride=(10,))[0] == pw.PW_OK
+    assert _bind_batched(lib, ops=addr, op_stride=(-10,))[0] == pw.PW_ERR_INVALID
+    maskc = [(pw.OPS["mask_columns"], 0.0, FAKE)]
+    assert _bind_batched(lib, ops=maskc, op_stride=(12,))[0] == pw.PW_ERR_UNSUPPORTED
+    assert _bind_batched(lib, ops=[(pw.OPS["mul"], 2.0, None)], op_stride=(3,))[0] == pw.PW_ERR_UNSUPPORTED
+    assert lib.pw_bind_batched(ctypes.byref(ctypes.c_void_p()), 0, 1, 1.0, FAKE, 10, 4, FAKE, 12, 4, 4,
+                               (pw._Op * 1)(), 0, None) == pw.PW_ERR_INVALID

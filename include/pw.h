@@ -245,6 +245,25 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
 #define PW_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int pw_topk_noalloc(const pw_expr *e, int k, int largest, void *values, int64_t *indices, void *stream);
 
+/* Row mean over the kept pairs (Features page, Native Deployment: the mean
+ * reduction over the last dim; guide, Score Expressions: masks decide which
+ * pairs a row reduces over):
+ *   out[i] = (sum of s_ij over kept j) / (number of kept j),
+ * NaN for a row with no kept pair (every row when M == 0). The sums are the
+ * kernel product with a column of ones; with masks in the op list, the
+ * counts are a second product that scores each kept pair 1 (exact for
+ * counts up to 2^24 in float32); a small kernel divides.
+ *   out         [N] device vector of the bound dtype ([B][N] on a batched
+ *               handle)
+ *   inv_counts  optional [N] device vector (NULL to skip): 1 / (number of
+ *               kept j), 0 for a row with none; the same for every batch
+ *               element. With an appended weight_rows op of this vector, the
+ *               kernel product with ones is the mean again, and pw_backward
+ *               of that product is the mean's backward.
+ * Workspace: pw_mean_workspace_size bytes, caller-owned. */
+int pw_mean_workspace_size(const pw_expr *e, size_t *bytes);
+int pw_mean(const pw_expr *e, void *out, void *inv_counts, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Backward by replay (guide, opening section: the consumer's backward
  * re-evaluates the pairs instead of keeping the [N, M] matrix; "What to

@@ -108,6 +108,8 @@ def load_library(path: str = LIB_PATH):
         lib.pw_logsumexp.argtypes = [vp, c_int, vp, vp, sz, vp]
         lib.pw_topk.argtypes = [vp, c_int, c_int, vp, vp, vp, sz, vp]
         lib.pw_topk_noalloc.argtypes = [vp, c_int, c_int, vp, vp, vp]
+        lib.pw_mean_workspace_size.argtypes = [vp, ctypes.POINTER(sz)]
+        lib.pw_mean.argtypes = [vp, vp, vp, vp, sz, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
         lib.pw_backward_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
         lib.pw_backward_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
@@ -494,20 +496,27 @@ class LazyScores:
         ones = torch.ones(self.M, 1, dtype=self.dtype, device=self.device)
         return self.matmul(ones)[:, 0]
 
-    def mean(self, dim: int = -1) -> torch.Tensor:
-        """Mean over `dim` (Features page, Native Deployment: reduce("mean",
-        -1)): the sum of the scores scaled by 1/count, as one more op."""
+    def mean(self, dim: int = -1, inv_counts=None) -> torch.Tensor:
+        """Mean over `dim` of the kept pairs (Features page, Native
+        Deployment: reduce("mean", -1)); NaN for a row with none (pw_mean).
+        With `inv_counts` (an [N] tensor) each row's 1 / kept count is
+        written too. Under autograd the value still comes from pw_mean, and
+        the backward replays the sum product weighted by those inverse
+        counts."""
         if dim in (-2, 0):
-            return self.T.mean(-1)
-        if self.M == 0:
-            return torch.full((self.N,), float("nan"), dtype=self.dtype, device=self.device)
-        masks = [(n, a) for n, a in self.ops if n in MASK_OPS]
-        if masks:
-            # Divide by each row's kept count: a second product whose score is 1.
-            ones = LazyScores(self.X, self.Y, "linear", 1.0, [("mul", 0.0), ("add", 1.0)] + masks)
-            return self.sum(-1) / ones.sum(-1)
-        scaled = LazyScores(self.X, self.Y, self.metric, self.gamma, list(self.ops) + [("mul", 1.0 / self.M)])
-        return scaled.sum(-1)
+            return self.T.mean(-1, inv_counts)
+        if inv_counts is None and _needs_grad(self):
+            return _replay(self, "mean")
+        out = torch.empty(self.N, dtype=self.dtype, device=self.device)
+        if inv_counts is not None and (inv_counts.dtype != self.dtype or inv_counts.device != self.device
+                                       or inv_counts.numel() != self.N or not inv_counts.is_contiguous()):
+            raise ValueError("inv_counts must be a contiguous [N] %s tensor on %s" % (self.dtype, self.device))
+        n = ctypes.c_size_t()
+        check(self._lib.pw_mean_workspace_size(self._h, ctypes.byref(n)), "pw_mean_workspace_size")
+        ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=self.device)
+        check(self._lib.pw_mean(self._h, out.data_ptr(), None if inv_counts is None else inv_counts.data_ptr(),
+                                ws.data_ptr(), n.value, _stream(self.device)), "pw_mean")
+        return out
 
 
 from . import masks  # noqa: E402  (pair-mask helpers)
@@ -540,6 +549,10 @@ class _Replay(torch.autograd.Function):
         elif consumer == "logsumexp":
             out = e.logsumexp(kw.get("exclude_self", False))
             outs = (out,)
+        elif consumer == "mean":
+            V = torch.empty(e.N, dtype=e.dtype, device=e.device)  # the rows' inverse kept counts
+            out = e.mean(-1, inv_counts=V)
+            outs = (out,)
         else:
             vals, idx = e.topk(kw["k"], kw.get("largest", False))
             ctx.mark_non_differentiable(idx)
@@ -549,6 +562,14 @@ class _Replay(torch.autograd.Function):
         ctx.save_for_backward(X, Y, V if V is not None else torch.empty(0), out, outs[-1], lse, *tensors)
         ctx.has_v = V is not None
         return outs if len(outs) > 1 else outs[0]
+
+    @staticmethod
+    def _mean_backward(ctx, e, G, inv, want):
+        """The mean is the sum product of the scores weighted by the rows'
+        inverse kept counts: replay that product's backward."""
+        we = LazyScores(e.X, e.Y, e.metric, e.gamma, list(e.ops) + [("weight_rows", inv)])
+        ones = torch.ones(e.M, 1, dtype=e.dtype, device=e.device)
+        return we.backward("matmul", G.reshape(-1, 1).contiguous(), V=ones, want=tuple(want))
 
     @staticmethod
     def backward(ctx, *grads):
@@ -564,11 +585,15 @@ class _Replay(torch.autograd.Function):
             want.append("X")
         if ctx.needs_input_grad[2]:
             want.append("Y")
-        if ctx.needs_input_grad[3]:
+        if ctx.needs_input_grad[3] and consumer != "mean":
             want.append("V")
-        r = e.backward(consumer, G, V=V, out=out if consumer in ("softmax_matmul", "logsumexp") else None,
-                       indices=last if consumer == "topk" else None, exclude_self=kw.get("exclude_self", False),
-                       want=tuple(want), lse=lse if consumer == "softmax_matmul" else None)
+        if consumer == "mean":
+            r = _Replay._mean_backward(ctx, e, G, V, want)
+            r = dict(r, V=None)
+        else:
+            r = e.backward(consumer, G, V=V, out=out if consumer in ("softmax_matmul", "logsumexp") else None,
+                           indices=last if consumer == "topk" else None, exclude_self=kw.get("exclude_self", False),
+                           want=tuple(want), lse=lse if consumer == "softmax_matmul" else None)
         op_grads = []
         for t, (n, a, is_t) in enumerate(ops_spec):
             if is_t:
@@ -785,20 +810,20 @@ class BatchedLazyScores:
         return self.matmul(ones)[..., 0]
 
     def mean(self, dim=-1):
-        """Mean over `dim`: the scores scaled by 1/M in the same product; with
-        masks, the sum divided by each row's kept count (a second product of
-        the masks with unit scores; the division is the host's)."""
+        """Mean over `dim` of the kept pairs, NaN for a row with none: one
+        pw_mean call for the whole batch (element by element under autograd
+        or with per-element masks)."""
         if dim in (-2, 1):
             return self.T.mean(-1)
-        if self.M == 0:
-            return torch.full((self.B, self.N), float("nan"), dtype=self.dtype, device=self.device)
-        masks = [(n, a) for n, a in self.ops if n in MASK_OPS]
-        if masks:
-            ones = BatchedLazyScores(self.X, self.Y, "linear", 1.0, [("mul", 0.0), ("add", 1.0)] + masks)
-            return self.sum(-1) / ones.sum(-1)
-        scaled = BatchedLazyScores(self.X, self.Y, self.metric, self.gamma,
-                                   list(self.ops) + [("mul", 1.0 / self.M)])
-        return scaled.sum(-1)
+        if not self._batched_ok():
+            return self._each(lambda e: e.mean(-1))
+        h = self._bind()
+        out = torch.empty(self.B, self.N, dtype=self.dtype, device=self.device)
+        n = ctypes.c_size_t()
+        check(h.lib.pw_mean_workspace_size(h.h, ctypes.byref(n)), "pw_mean_workspace_size")
+        ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=self.device)
+        check(h.lib.pw_mean(h.h, out.data_ptr(), None, ws.data_ptr(), n.value, _stream(self.device)), "pw_mean")
+        return out
 
     def masked(self, mask):
         mask = [mask] if isinstance(mask, tuple) else list(mask)

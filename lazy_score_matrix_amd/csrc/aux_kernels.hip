@@ -61,6 +61,57 @@ hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// Row means from row sums: out[b][i] = out[b][i] / c_i with c_i the kept
+// count of row i (cnt[i], or M for every row when cnt is null); a row with
+// c_i = 0 gets a quiet NaN. inv (optional) receives 1 / c_i, or 0 for an
+// empty row, from batch element 0's threads. Device code is built without
+// NaN semantics, so the NaN is chosen and stored as an integer bit pattern,
+// out of the reach of float folding.
+// ---------------------------------------------------------------------------
+template <class T>
+struct Bits;
+template <>
+struct Bits<float> {
+  using U = uint32_t;
+  static constexpr U kQuietNan = 0x7fc00000u;
+};
+template <>
+struct Bits<double> {
+  using U = uint64_t;
+  static constexpr U kQuietNan = 0x7ff8000000000000ull;
+};
+
+template <class T>
+__global__ __launch_bounds__(256) void mean_finish_kernel(T *out, int64_t N, int64_t total, const T *cnt, T M,
+                                                          T *inv) {
+  using U = typename Bits<T>::U;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t i = t % N;
+  const T c = cnt ? cnt[i] : M;
+  const bool kept = c > (T)0;
+  const T q = out[t] / c;
+  U b;
+  __builtin_memcpy(&b, &q, sizeof b);
+  reinterpret_cast<U *>(out)[t] = kept ? b : Bits<T>::kQuietNan;
+  if (inv && t < N) inv[t] = kept ? (T)1 / c : (T)0;
+}
+
+hipError_t launch_mean_finish(int dtype, void *out, int64_t N, int64_t B, const void *cnt, int64_t M, void *inv,
+                              hipStream_t s) {
+  const int64_t n = N * B;
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(mean_finish_kernel<float>, grid, block, 0, s, (float *)out, N, n, (const float *)cnt,
+                       (float)M, (float *)inv);
+  else
+    hipLaunchKernelGGL(mean_finish_kernel<double>, grid, block, 0, s, (double *)out, N, n, (const double *)cnt,
+                       (double)M, (double *)inv);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Group ranges for the same_group mask: min and max id of each block of
 // `block` consecutive entries (a row block, or a key tile), so the tile
 // kernels can skip pairs of blocks whose ranges are disjoint. One wave per

@@ -868,6 +868,104 @@ int pw_topk(const pw_expr *e, int k, int largest, void *values, int64_t *indices
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// Row means: the kernel product with a column of ones, divided by each
+// row's kept count. Without masks the count is M. With masks it is a second
+// product over the same masks whose every pair scores 1: the linear metric
+// of one-feature points that are all 1, so no input value can overflow it.
+// ---------------------------------------------------------------------------
+namespace {
+
+bool is_mask_op(int kind) {
+  return kind == PW_OP_MASK_ROWS || kind == PW_OP_MASK_COLUMNS || kind == PW_OP_GROUP_ROWS ||
+         kind == PW_OP_GROUP_COLUMNS || kind == PW_OP_BAND_UPPER || kind == PW_OP_BAND_LOWER;
+}
+
+struct ExprHolder {
+  pw_expr *e = nullptr;
+  ~ExprHolder() { delete e; }
+};
+
+// The unit-score count expression of e over `ones` (>= max(N, M) entries),
+// or none when e has no masks. Unbatched: masks are shared by the batch.
+int count_expr(const pw_expr &e, const void *ones, ExprHolder *out) {
+  std::vector<pw_op> masks;
+  for (const pw_op &o : e.ops)
+    if (is_mask_op(o.kind)) masks.push_back(o);
+  if (masks.empty()) return PW_OK;
+  return bind_impl(&out->e, e.dtype, PW_LINEAR, 1.0, ones, e.N, 1, ones, e.M, 1, 1, masks.data(), (int)masks.size(),
+                   nullptr);
+}
+
+// Workspace of a mean: ones [max(N, M)], counts [N], then the products'
+// workspace (the larger of the two).
+struct MeanLayout {
+  size_t cnt = 0, prod = 0, prod_bytes = 0, total = 0;
+};
+
+MeanLayout mean_layout(const pw_expr &e, const pw_expr *ce) {
+  MeanLayout L;
+  const size_t es = esize(e.dtype);
+  size_t off = align_up((size_t)std::max(e.N, e.M) * es);
+  L.cnt = off;
+  off += align_up((size_t)e.N * es);
+  L.prod = off;
+  L.prod_bytes = make_plan(e, PW_C_MATMUL, 1, 0).total;
+  if (ce) L.prod_bytes = std::max(L.prod_bytes, make_plan(*ce, PW_C_MATMUL, 1, 0).total);
+  L.total = off + L.prod_bytes + kAlign;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pw_mean_workspace_size(const pw_expr *e, size_t *bytes) {
+  if (!e || !bytes) return PW_ERR_INVALID;
+  *bytes = 0;
+  if (e->N == 0 || e->M == 0) return PW_OK;
+  ExprHolder ce;
+  // Only sizes matter here: any aligned non-null pointer stands for the ones.
+  int rc = count_expr(*e, reinterpret_cast<const void *>(kAlign), &ce);
+  if (rc != PW_OK) return rc;
+  *bytes = mean_layout(*e, ce.e).total;
+  return PW_OK;
+}
+
+int pw_mean(const pw_expr *e, void *out, void *inv_counts, void *ws, size_t ws_bytes, void *stream) {
+  if (!e) return PW_ERR_INVALID;
+  const size_t es = esize(e->dtype);
+  if ((e->N > 0 && !out) || !aligned(out, es) || !aligned(inv_counts, es)) return PW_ERR_INVALID;
+  if (e->N == 0) return PW_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (e->M == 0) {  // no kept pair anywhere: NaN means, zero inverse counts
+    int rc = hip_status(launch_fill(e->dtype, out, e->B * e->N, 1, 1, 0.0, s));
+    if (rc == PW_OK) rc = hip_status(launch_mean_finish(e->dtype, out, e->N, e->B, nullptr, 0, inv_counts, s));
+    return rc;
+  }
+  ExprHolder ce;
+  int rc = count_expr(*e, reinterpret_cast<const void *>(kAlign), &ce);
+  if (rc != PW_OK) return rc;
+  const MeanLayout L = mean_layout(*e, ce.e);
+  if (!ws || ws_bytes < L.total) return PW_ERR_WORKSPACE;
+  char *base = reinterpret_cast<char *>(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+  void *ones = base, *cnt = base + L.cnt;
+  rc = hip_status(launch_fill(e->dtype, ones, std::max(e->N, e->M), 1, 1, 1.0, s));
+  pw_expr sums = *e;
+  sums.sv = 0;  // the column of ones is shared by the batch
+  if (rc == PW_OK) rc = value_consumer(&sums, PW_C_MATMUL, ones, 1, 1, out, 1, base + L.prod, L.prod_bytes, stream);
+  if (rc == PW_OK && ce.e) {
+    ce.e->X = ones;
+    ce.e->Y = ones;
+    rc = value_consumer(ce.e, PW_C_MATMUL, ones, 1, 1, cnt, 1, base + L.prod, L.prod_bytes, stream);
+  }
+  if (rc == PW_OK)
+    rc = hip_status(launch_mean_finish(e->dtype, out, e->N, e->B, ce.e ? cnt : nullptr, e->M, inv_counts, s));
+  return rc;
+}
+
+}  // extern "C"
+
 // ------------------------------------------------------------------ backward
 
 namespace {

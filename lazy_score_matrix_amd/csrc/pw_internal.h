@@ -314,6 +314,10 @@ hipError_t launch_group_ranges(const int64_t *g, int64_t n, int block, int64_t *
 hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, int bn, int n_rb, int64_t *out,
                              hipStream_t s);
 hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);
+// out[b][i] /= kept count of row i (cnt[i], or M when cnt is null); NaN for a
+// row with none; inv[i] = 1 / count (0 for none) when inv is not null.
+hipError_t launch_mean_finish(int dtype, void *out, int64_t N, int64_t B, const void *cnt, int64_t M, void *inv,
+                              hipStream_t s);
 // Row norms |x_i|^2, or with `inverse` 1/|x_i| (0 for a zero row).
 // With n_batch > 1, element b reads X + b * x_bstride and writes out +
 // b * out_bstride (bytes).

@@ -357,3 +357,35 @@ def test_bind_batched_validation(lib):
     assert _bind_batched(lib, ops=[(pw.OPS["mul"], 2.0, None)], op_stride=(3,))[0] == pw.PW_ERR_UNSUPPORTED
     assert lib.pw_bind_batched(ctypes.byref(ctypes.c_void_p()), 0, 1, 1.0, FAKE, 10, 4, FAKE, 12, 4, 4,
                                (pw._Op * 1)(), 0, None) == pw.PW_ERR_INVALID
+
+
+def test_mean_validation_and_workspace(lib):
+    """pw_mean: a null handle or an unaligned output is rejected, no rows is
+    a no-op, and the workspace (a column of ones, the counts and the larger
+    product workspace) grows with N + M, never with N*M; masks add the
+    count product's needs, never more than one more product."""
+    n = ctypes.c_size_t()
+    assert lib.pw_mean_workspace_size(None, ctypes.byref(n)) == pw.PW_ERR_INVALID
+    assert lib.pw_mean(None, FAKE, None, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    rc, h = bind(lib, N=0, X=0, M=12)
+    assert rc == 0 and lib.pw_mean(h, 0, None, 0, 0, None) == pw.PW_OK
+    assert lib.pw_mean_workspace_size(h, ctypes.byref(n)) == pw.PW_OK and n.value == 0
+    lib.pw_release(h)
+    rc, h = bind(lib, N=100, M=120)
+    assert lib.pw_mean(h, FAKE + 2, None, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    assert lib.pw_mean(h, FAKE, FAKE + 2, FAKE, 1 << 20, None) == pw.PW_ERR_INVALID
+    lib.pw_release(h)
+    sizes = {}
+    for M in (4096, 8192):
+        for masked in (False, True):
+            ops = [(pw.OPS["mask_columns"], 0.0, FAKE)] if masked else []
+            rc, h = bind(lib, N=2048, M=M, D=8, ops=ops)
+            assert rc == 0 and lib.pw_mean_workspace_size(h, ctypes.byref(n)) == pw.PW_OK
+            prod = ctypes.c_size_t()
+            assert lib.pw_workspace_size(h, 0, 1, 0, ctypes.byref(prod)) == pw.PW_OK
+            assert n.value >= prod.value + 4 * (M + 2048)
+            if not masked:
+                assert n.value <= prod.value + 4 * (M + 2048) + 3 * 256
+            sizes[M, masked] = n.value
+            lib.pw_release(h)
+    assert all(v < 2048 * M for (M, _), v in sizes.items())

@@ -6,6 +6,7 @@ every class (skipped, checked pair by pair, kept whole)."""
 import numpy as np
 import pytest
 
+import oracle
 from gpu_cases import bind_both, check_consumer
 
 pytestmark = pytest.mark.gpu
@@ -160,3 +161,112 @@ def test_mean_with_mask_counts_kept():
     want = np.asarray(o[:, 0], np.float64) / keep.sum()
     assert np.allclose(got, want, rtol=1e-12, atol=0)
     assert torch.is_tensor(e.mean())
+
+
+def _kept(ops, n, m):
+    """The kept-pair matrix of an op list, written out from the mask
+    definitions (guide, Score Expressions and Task Map, Attention row)."""
+    K = np.ones((n, m), bool)
+    i, j = np.arange(n)[:, None], np.arange(m)[None, :]
+    for name, a in ops:
+        if name == "mask_rows":
+            K &= np.asarray(a, bool)[:, None]
+        elif name == "mask_columns":
+            K &= np.asarray(a, bool)[None, :]
+        elif name == "causal":
+            K &= (j - i) <= a
+        elif name == "band":
+            K &= ((i - j) <= a[0]) & ((j - i) <= a[1])
+        elif name == "same_group":
+            K &= np.asarray(a[0])[:, None] == np.asarray(a[1])[None, :]
+    return K
+
+
+def _mean_reference(oe, ops, n, m):
+    o, mag = oracle.matmul(oe, np.ones((m, 1), dtype=oe.np_dtype))
+    cnt = _kept(ops, n, m).sum(1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want = np.where(cnt > 0, np.asarray(o[:, 0], np.float64) / np.maximum(cnt, 1), np.nan)
+    return want, np.asarray(mag[:, 0], np.float64) / np.maximum(cnt, 1), cnt
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("kind", KINDS + ("empty_band",))
+def test_mean_masked_in_library(kind, dtype):
+    """pw_mean: sums over the kept pairs divided by the kept count, NaN for
+    a row with none, and the inverse counts (0 for none) it reports."""
+    import torch
+    from parity import assert_values
+    X, Y, r = _data(2200, 300, 333, 5, dtype)
+    ops = [("band", (-200, 10 ** 9))] if kind == "empty_band" else _masks(kind, 300, 333, r)
+    e, oe = bind_both(X, Y, "rbf", gamma=0.2, ops=ops)
+    inv = torch.empty(300, dtype=e.dtype, device=e.device)
+    got = e.mean(-1, inv_counts=inv).cpu().numpy().astype(np.float64)
+    want, mag, cnt = _mean_reference(oe, ops, 300, 333)
+    empty = cnt == 0
+    if kind in ("rows", "empty_band"):
+        assert empty.any()
+    assert np.all(np.isnan(got[empty])), "rows with no kept pair must be NaN"
+    if (~empty).any():
+        assert_values(got[~empty][:, None], want[~empty][:, None], mag[~empty][:, None], dtype, n_terms=333,
+                      what="mean %s" % kind)
+    one = np.asarray(1, dtype)
+    want_inv = np.where(cnt > 0, one / np.maximum(cnt, 1).astype(dtype), 0).astype(dtype)
+    assert np.array_equal(inv.cpu().numpy(), want_inv)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+def test_mean_batched_one_call(dtype):
+    """A batched handle's mean: one pw_mean call for every element, each
+    against the oracle, masks shared, per-element row offsets."""
+    import torch
+    import lazy_score_matrix_amd as pw
+    from gpu_cases import to_dev
+    from parity import assert_values
+    r = np.random.default_rng(2300)
+    B, n, m, d = 3, 150, 170, 4
+    X = r.standard_normal((B, n, d)).astype(dtype)
+    Y = r.standard_normal((1, m, d)).astype(dtype)
+    a = r.standard_normal((B, n)).astype(dtype)
+    gr = np.sort(r.integers(0, 5, n)).astype(np.int64)
+    gc = np.sort(r.integers(0, 5, m)).astype(np.int64)
+    ops = [("add_rows", to_dev(a)), ("same_group", (to_dev(gr), to_dev(gc))), ("causal", 20)]
+    e = pw.lazy(to_dev(X), to_dev(Y), "sqeuclidean", ops=ops)
+    assert "batch=3" in e.plan("matmul", C=1)
+    got = e.mean(-1).cpu().numpy().astype(np.float64)
+    host_ops = [("same_group", (gr, gc)), ("causal", 20)]
+    for b in range(B):
+        oe = oracle.Expr(X[b], Y[0], "sqeuclidean", ops=[("add_rows", a[b])] + host_ops)
+        want, mag, cnt = _mean_reference(oe, host_ops, n, m)
+        empty = cnt == 0
+        assert np.all(np.isnan(got[b][empty]))
+        assert_values(got[b][~empty][:, None], want[~empty][:, None], mag[~empty][:, None], dtype, n_terms=m,
+                      what="batched mean element %d" % b)
+    assert torch.is_tensor(e.mean(-1))
+
+
+def test_mean_autograd_replays_weighted_sum():
+    """Gradients of sum(mean * G): the sum product's backward with G scaled
+    by each row's inverse kept count (the derivative of a sum over a fixed
+    kept set divided by its size)."""
+    import torch
+    import lazy_score_matrix_amd as pw
+    from gpu_cases import grad_report, to_dev
+    r = np.random.default_rng(2400)
+    X = r.standard_normal((120, 6))
+    Y = r.standard_normal((140, 6))
+    keep = r.random(140) < 0.6
+    rows = r.random(120) < 0.9
+    ops = [("mask_columns", keep), ("mask_rows", rows)]
+    Xt, Yt = to_dev(X).requires_grad_(True), to_dev(Y).requires_grad_(True)
+    e = pw.lazy(Xt, Yt, "rbf", gamma=0.3, ops=[("mask_columns", to_dev(keep)), ("mask_rows", to_dev(rows))])
+    out = e.mean(-1)
+    cnt = _kept(ops, 120, 140).sum(1)
+    assert np.all(np.isnan(out.detach().cpu().numpy()[cnt == 0]))
+    G = torch.randn(120, dtype=torch.float64, device=out.device)
+    dX, dY = torch.autograd.grad((torch.nan_to_num(out) * G).sum(), [Xt, Yt])
+    Gs = np.where(cnt > 0, G.cpu().numpy() / np.maximum(cnt, 1), 0.0)
+    ref = oracle.backward(oracle.Expr(X, Y, "rbf", 0.3, ops), "matmul", Gs[:, None], np.ones((140, 1)))
+    for g, rv, what in ((dX, ref["dX"], "dX"), (dY, ref["dY"], "dY")):
+        ok, ratio = grad_report(g, rv, np.float64, 140)
+        assert ok, "%s: worst |gpu - oracle| / tol = %.3g" % (what, ratio)

@@ -272,13 +272,22 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     } else {
       p.vcfg.vtile = 0;
       // The float row log-sum-exp of narrow points under at most one
-      // row-only affine stage takes two rows per thread.
+      // row-only affine stage takes several rows per thread.
       const bool row_affine = e.stages.empty() || (e.stages.size() == 1 && e.stages[0].kind == ST_AFFINE &&
                                                    !e.stages[0].col_vec);
       if (consumer == PW_C_LOGSUMEXP && e.dtype == PW_F32 && e.metric != PW_COSINE && row_affine && !e.row_mask &&
           !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4) {
-        p.vcfg.rows = 2;
-        p.bm = 2 * kValuBM;
+        if (e.metric == PW_RBF) {
+          p.vcfg.rows = 2;
+          p.bm = 2 * kValuBM;
+        } else {
+          // Dot products and squared distances: four rows per thread, the
+          // product's wide tiles and many short workgroups.
+          p.vcfg.rows = kProdRows;
+          p.bm = kProdRows * kValuBM;
+          p.bn = kProdBN;
+          target_wgs = (int64_t)kProdWGsPerCU * cus;
+        }
       }
     }
   }

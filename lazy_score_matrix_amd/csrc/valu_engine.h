@@ -882,6 +882,169 @@ __global__ __launch_bounds__(kValuBM) void valu_tile_r2_lse(const TileArgs a) {
   }
 }
 
+// The float row log-sum-exp of narrow points, linear or squared euclidean,
+// under at most one row-only affine stage s = r_i f + p_i: four rows per
+// thread and 256-column tiles loaded one tile ahead, as the product above.
+// In base 2 and relative to the row's reference m,
+//   s2 - m = C_i + B_i |y|^2 + A_i . y,
+// with B_i = r_i log2 e, A_i = -2 B_i x_i and C_i = B_i |x_i|^2 + p_i log2 e
+// - m for the squared distance (its norm expansion: four FMAs a pair at
+// three features), and A_i = B_i x_i, C_i = p_i log2 e - m, no |y|^2 term,
+// for the dot product. The reference moves only when a group of 8 columns
+// exceeds it by more than 8 (weights stay <= 256) and counts as 0 until the
+// first finite score, as in the one-row engine. The ragged last tile and
+// tiles that meet a row's own column under exclude_self check every pair.
+
+template <int METRIC, int DT, int R>
+__global__ __launch_bounds__(kValuBM) void valu_lse_rn(const TileArgs a) {
+  static_assert(METRIC == M_LINEAR || METRIC == M_SQEUCLIDEAN, "dot product or squared distance");
+  static_assert(DT == 3 || DT == 4, "narrow points only");
+  const BatchPtrs bp = batch_ptrs(a);
+  constexpr int BN = kValuBM, G = 4;
+  constexpr bool SQ = METRIC == M_SQEUCLIDEAN;
+  __shared__ float4 sY[2][BN];                // (y0, y1, y2, |y|^2) for DT = 3, else (y0..y3)
+  __shared__ float sW[2][DT == 4 ? BN : 1];   // |y|^2 for DT = 4
+  const int tid = threadIdx.x;
+  const int rb = blockIdx.x % a.n_rb;
+  const int sp = blockIdx.x / a.n_rb;
+  const int64_t jb = wave_uniform((int64_t)sp * a.split_cols);
+  const int64_t je = wave_uniform(min(a.M, jb + a.split_cols));
+  const int n_tiles = (int)((je - jb + BN - 1) / BN);
+  const int64_t r0 = (int64_t)rb * (R * BN), r1 = min(a.N, r0 + R * BN) - 1;
+
+  float A[R][DT], B[R], P[R], C[R], m[R], l[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int64_t i = r0 + u * BN + tid;
+    const bool rv = i < a.N;
+    float r = 1.f, p = 0.f;
+    if (a.epi.n_stages == 1) {
+      const Stage &st = a.epi.st[0];
+      if (st.row_vec) {
+        if (rv) {
+          r = ldg<float>(epi_vec(a, st.r_vec), i);
+          p = ldg<float>(epi_vec(a, st.p_vec), i);
+        }
+      } else {
+        r = (float)st.r_scalar;
+        p = (float)st.p_scalar;
+      }
+    }
+    if (!rv) r = 0.f;  // rows past the end score 0 everywhere
+    B[u] = kLog2e_f * r;
+    float n2 = 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      const float xv = (rv && d < a.D) ? ldg<float>(bp.X, i * a.ldx + d) : 0.f;
+      A[u][d] = (SQ ? -2.f * B[u] : B[u]) * xv;
+      n2 = fmaf(xv, xv, n2);
+    }
+    P[u] = SQ ? fmaf(B[u], n2, kLog2e_f * p) : kLog2e_f * p;
+    C[u] = P[u];
+    m[u] = -__builtin_huge_valf();
+    l[u] = 0.f;
+  }
+
+  float ry[DT];
+  auto fetch = [&](int t) {
+    const int64_t j = jb + (int64_t)t * BN + tid;
+    const bool cv = j < je;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) ry[d] = (cv && d < a.D) ? ldg<float>(bp.Y, j * a.ldy + d) : 0.f;
+  };
+  auto stage = [&](int t) {
+    const int b = t & 1;
+    float y[4] = {0.f, 0.f, 0.f, 0.f}, n2 = 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      y[d] = ry[d];
+      n2 = fmaf(y[d], y[d], n2);
+    }
+    if constexpr (DT == 3) y[3] = n2;
+    else sW[b][tid] = n2;
+    sY[b][tid] = make_float4(y[0], y[1], y[2], y[3]);
+  };
+
+  // One tile of columns j0 + [0, n) from buffer b.
+  auto sweep = [&](auto check_tag, int b, int64_t j0, int n) {
+    constexpr bool CHECK = decltype(check_tag)::value;
+    const float4 *Yb = sY[b];
+    const bool excl = a.exclude_self != 0;
+    int own[R];  // the row's own column as a tile slot (outside [0, BN) if not here)
+#pragma unroll
+    for (int u = 0; u < R; ++u) own[u] = (int)(r0 + u * BN + tid - j0);
+#pragma unroll 1
+    for (int g = 0; g < BN; g += G) {
+      if (CHECK && g >= n) break;
+      float4 y[G];
+      float w[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        y[k] = Yb[g + k];
+        w[k] = DT == 3 ? y[k].w : sW[b][g + k];
+      }
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        float sv[G];
+        float gm = -__builtin_huge_valf();
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          float e = SQ ? fmaf(B[u], w[k], C[u]) : C[u];
+          e = fmaf(A[u][0], y[k].x, e);
+          e = fmaf(A[u][1], y[k].y, e);
+          e = fmaf(A[u][2], y[k].z, e);
+          if constexpr (DT == 4) e = fmaf(A[u][3], y[k].w, e);
+          if (CHECK && (g + k >= n || (excl && g + k == own[u]))) e = -__builtin_huge_valf();
+          sv[k] = e;
+          gm = fmaxf(gm, e);
+        }
+        const bool first = m[u] == -__builtin_huge_valf();
+        if (gm > (first ? -__builtin_huge_valf() : 8.f)) {
+          const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-gm);
+          l[u] *= alpha;
+          m[u] = (first ? 0.f : m[u]) + gm;
+          C[u] = P[u] - m[u];
+#pragma unroll
+          for (int k = 0; k < G; ++k) sv[k] -= gm;
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) l[u] += __builtin_amdgcn_exp2f(sv[k]);
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < n_tiles) fetch(t + 1);
+    const int64_t j0 = jb + (int64_t)t * BN;
+    const int nb = (int)min((int64_t)BN, je - j0);
+    const bool check = nb < BN || (a.exclude_self && j0 <= r1 && j0 + BN > r0);  // uniform
+    if (check) sweep(Bool<true>{}, b, j0, nb);
+    else sweep(Bool<false>{}, b, j0, nb);
+    if (t + 1 < n_tiles) stage(t + 1);
+    __syncthreads();
+  }
+  const bool fin = a.n_split == 1;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int64_t i = r0 + u * BN + tid;
+    if (i >= a.N) continue;
+    const float mn = m[u] == -__builtin_huge_valf() ? m[u] : m[u] * kLn2_f;  // back to natural units
+    if (fin) {
+      static_cast<float *>(bp.out)[i] = l[u] > 0.f ? mn + dlog(l[u]) : -__builtin_huge_valf();
+    } else {
+      float *o = static_cast<float *>(bp.partial) + ((int64_t)sp * a.N + i) * 2;
+      o[0] = mn;
+      o[1] = l[u];
+    }
+  }
+}
+
 template <class T, int METRIC, int CONS, int DT, int VT>
 hipError_t launch_valu_kernel(const TileArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.n_rb * a.n_split), 1, (unsigned)a.bat.n), block(kValuBM);
@@ -927,6 +1090,15 @@ hipError_t valu_launch_metric(int consumer, const ValuConfig &cfg, const TileArg
       if (cfg.dtile == 3) hipLaunchKernelGGL((valu_prod_rn<METRIC, 3, kProdRows>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((valu_prod_rn<METRIC, 4, kProdRows>), grid, block, 0, s, a);
       return hipGetLastError();
+    }
+    if constexpr (METRIC != M_RBF) {
+      if (consumer == C_LOGSUMEXP && cfg.rows == kProdRows) {
+        if (cfg.dtile != 3 && cfg.dtile != 4) return hipErrorInvalidValue;
+        dim3 grid((unsigned)(a.n_rb * a.n_split), 1, (unsigned)a.bat.n), block(kValuBM);
+        if (cfg.dtile == 3) hipLaunchKernelGGL((valu_lse_rn<METRIC, 3, kProdRows>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((valu_lse_rn<METRIC, 4, kProdRows>), grid, block, 0, s, a);
+        return hipGetLastError();
+      }
     }
     if (cfg.rows == 2) {
       if (cfg.dtile != 3 && cfg.dtile != 4) return hipErrorInvalidValue;

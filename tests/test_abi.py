@@ -269,24 +269,32 @@ def _plan(lib, consumer, C=0, k=0, **kw):
 
 def test_blocked_vector_kernels_only_where_they_apply(lib):
     """The several-rows-per-thread vector kernels cover plain float scores of
-    narrow points only: the kernel product (four rows, 256-column tiles),
-    the row log-sum-exp under at most one row-only stage and the row
-    minimum (two rows). Score arithmetic they do not take, masks, cosine
-    and float64 plan one row per thread."""
+    narrow points only: the kernel product and the row log-sum-exp of dot
+    products and squared distances under at most one row-only stage (four
+    rows, 256-column tiles), the rbf log-sum-exp and the row minimum (two
+    rows). Score arithmetic they do not take, masks, cosine and float64
+    plan one row per thread."""
     MATMUL, LSE, TOPK = 0, 2, 4
     N, M = 4100, 3000
+    four = ("valu", "4", "1024", "256")
     for metric in (0, 1, 2):
         p = _plan(lib, MATMUL, 4, N=N, M=M, D=3, metric=metric)
-        assert (p["family"], p["rows"], p["bm"], p["bn"]) == ("valu", "4", "1024", "256"), p
-        assert _plan(lib, LSE, N=N, M=M, D=4, metric=metric)["rows"] == "2"
+        assert (p["family"], p["rows"], p["bm"], p["bn"]) == four, p
+        p = _plan(lib, LSE, N=N, M=M, D=4, metric=metric)
+        if metric == 2:
+            assert p["rows"] == "2", p
+        else:
+            assert (p["family"], p["rows"], p["bm"], p["bn"]) == four, p
         assert _plan(lib, TOPK, 0, 1, N=N, M=M, D=2, metric=metric)["rows"] == "2"
     mul = [(pw.OPS["mul"], -0.5, None)]
     addr = [(pw.OPS["mul"], -0.5, None), (pw.OPS["add_rows"], 0.0, FAKE)]
     addc = [(pw.OPS["add_columns"], 0.0, FAKE)]
     maskc = [(pw.OPS["mask_columns"], 0.0, FAKE)]
     causal = [(pw.OPS["band_upper"], 0.0, None)]
-    assert _plan(lib, LSE, N=N, M=M, D=3, ops=mul)["rows"] == "2"
-    assert _plan(lib, LSE, N=N, M=M, D=3, ops=addr)["rows"] == "2"
+    for metric in (0, 1):
+        assert _plan(lib, LSE, N=N, M=M, D=3, ops=mul, metric=metric)["rows"] == "4"
+        assert _plan(lib, LSE, N=N, M=M, D=3, ops=addr, metric=metric)["rows"] == "4"
+    assert _plan(lib, LSE, N=N, M=M, D=3, ops=addr, metric=2)["rows"] == "2"
     one_row = [
         _plan(lib, MATMUL, 5, N=N, M=M, D=3),                 # value width above 4
         _plan(lib, MATMUL, 4, N=N, M=M, D=5),                 # five features

@@ -3,11 +3,15 @@ that the planner picked the kernel it means to cover:
   * the narrow kernel product (four rows per thread, 256-column tiles; rbf by
     the norm expansion with the row factor deferred, and its direct-form
     fallbacks for points far from the origin);
-  * the two-rows row log-sum-exp (no stage, a scalar stage, a row-vector
-    stage; with and without the self pair);
+  * the row log-sum-exp (four rows per thread and 256-column tiles for dot
+    products and squared distances, by the norm expansion; two rows for
+    rbf) with no stage, a scalar stage (gentle and steep, positive scales
+    moving the reference often), a row-vector stage, with and without the
+    self pair;
   * the two-rows row minimum / maximum with exact ties (lowest index wins).
-Sizes span several row blocks (1024 rows for the product, 512 for the
-two-rows kernels) with a ragged last block, and a ragged last column tile.
+Sizes span several row blocks (1024 rows for the four-rows kernels, 512 for
+the two-rows kernels) with a ragged last block, and a ragged last column
+tile.
 """
 import numpy as np
 import pytest
@@ -65,6 +69,7 @@ def test_narrow_product_rbf_far_points(D):
 LSE_CHAINS = {
     "none": lambda n, r: [],
     "mul": lambda n, r: [("mul", -0.5)],
+    "steep": lambda n, r: [("mul", 6.0)],
     "rowvec": lambda n, r: [("mul", -0.5), ("add_rows", r.standard_normal(n).astype(np.float32)),
                             ("weight_rows", (0.5 + r.random(n)).astype(np.float32))],
 }
@@ -74,17 +79,18 @@ LSE = [(m, d, ch, ex) for m in ("linear", "sqeuclidean", "rbf") for d in (1, 3, 
 
 @pytest.mark.parametrize("metric,D,chain,excl", LSE, ids=["%s-D%d-%s-%s" % (a, b, c, "excl" if x else "all")
                                                           for a, b, c, x in LSE])
-def test_two_rows_logsumexp(metric, D, chain, excl):
+def test_blocked_logsumexp(metric, D, chain, excl):
     r = np.random.default_rng(300 + D)
-    N = 1100
-    M = 1100 if excl else 333
+    N = 2100
+    M = 2100 if excl else 1333
     X = r.standard_normal((N, D)).astype(np.float32)
     Y = X if excl else r.standard_normal((M, D)).astype(np.float32)
     ops = LSE_CHAINS[chain](N, r)
     e, oe = bind_both(X, Y, metric, gamma=0.5, ops=ops, same=excl)
     plan = e.plan("logsumexp")
-    assert _field(plan, "family") == "valu" and _field(plan, "rows") == "2", plan
-    check_consumer(e, oe, "logsumexp", exclude_self=excl, what="two-rows lse %s D%d %s" % (metric, D, chain))
+    rows = "2" if metric == "rbf" else "4"
+    assert _field(plan, "family") == "valu" and _field(plan, "rows") == rows, plan
+    check_consumer(e, oe, "logsumexp", exclude_self=excl, what="blocked lse %s D%d %s" % (metric, D, chain))
 
 
 MINS = [(d, lg) for d in (1, 2, 3, 4) for lg in (False, True)]
@@ -102,3 +108,21 @@ def test_two_rows_min_exact_ties(D, largest):
     plan = e.plan("topk", 0, 1)
     assert _field(plan, "family") == "valu" and _field(plan, "rows") == "2", plan
     check_consumer(e, oe, "topk", k=1, largest=largest, exact=True, what="two-rows min D%d" % D)
+
+
+@pytest.mark.parametrize("metric", ("linear", "sqeuclidean"))
+def test_blocked_logsumexp_far_points(metric):
+    """Points far from the origin: the norm expansion cancels more there,
+    within the error magnitude the comparison rule allows; very far ones
+    keep their wave (row) or tile (column) on the path that tracks maxima."""
+    r = np.random.default_rng(330)
+    X = r.standard_normal((2100, 3)).astype(np.float32)
+    Y = r.standard_normal((1333, 3)).astype(np.float32)
+    X[5] *= 30.0
+    Y[300] *= 30.0
+    Y[1300] = X[5]
+    X[1500] *= 1000.0   # a row whose wave keeps tracking maxima
+    Y[700] *= 1000.0    # a column whose tile does
+    e, oe = bind_both(X, Y, metric, ops=[("mul", -0.5)])
+    assert _field(e.plan("logsumexp"), "rows") == "4"
+    check_consumer(e, oe, "logsumexp", what="blocked lse far points %s" % metric)

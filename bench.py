@@ -50,10 +50,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_digest():
-    """Digest of the HIP/C++ sources of libpw; a counter reading taken on
-    other sources no longer describes the kernel."""
+    """Digest of the HIP/C++ sources of libpw and of its build script (the
+    compiler flags); a counter reading taken on other sources or flags no
+    longer describes the kernel."""
     h = hashlib.sha1()
-    for f in sorted(glob.glob(os.path.join(ROOT, "lazy_score_matrix_amd", "csrc", "*"))):
+    files = glob.glob(os.path.join(ROOT, "lazy_score_matrix_amd", "csrc", "*"))
+    files.append(os.path.join(ROOT, "lazy_score_matrix_amd", "build.py"))
+    for f in sorted(files):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]

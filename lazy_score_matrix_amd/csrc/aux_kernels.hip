@@ -301,6 +301,32 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const TileArgs a) {
   if (c == 0 && bp.lse_out) static_cast<T *>(bp.lse_out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
 }
 
+// Keep in `a` the KL smallest keys of two ascending lists a and b, ascending:
+// min(a[p], b[KL-1-p]) is a bitonic sequence holding them, and log2(KL)
+// half-cleaner stages sort it.
+template <class T, int KL>
+__device__ __forceinline__ void keep_smallest(Key<T> (&a)[KL], const Key<T> (&b)[KL]) {
+#pragma unroll
+  for (int p = 0; p < KL; ++p) a[p] = b[KL - 1 - p] < a[p] ? b[KL - 1 - p] : a[p];
+#pragma unroll
+  for (int j = KL / 2; j > 0; j >>= 1) {
+#pragma unroll
+    for (int p = 0; p < KL; ++p) {
+      if ((p & j) == 0) {
+        const bool sw = a[p + j] < a[p];
+        const Key<T> lo = sw ? a[p + j] : a[p];
+        const Key<T> hi = sw ? a[p] : a[p + j];
+        a[p] = lo;
+        a[p + j] = hi;
+      }
+    }
+  }
+}
+
+// Each split left an ascending list of k keys per row. Lists of up to 16
+// merge pairwise (keep_smallest), the next split's keys loaded before the
+// current one is merged, so one row's loads are in flight together; longer
+// lists take the keys one by one into a sorted list.
 template <class T, int KL>
 __global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
   const BatchPtrs bp = batch_ptrs(a);
@@ -309,9 +335,26 @@ __global__ __launch_bounds__(256) void merge_topk_kernel(const TileArgs a) {
   Key<T> list[KL];
 #pragma unroll
   for (int p = 0; p < KL; ++p) list[p] = Key<T>::sentinel();
-  for (int sp = 0; sp < a.n_split; ++sp) {
-    const int64_t base = ((int64_t)sp * a.N + i) * a.k;
-    for (int p = 0; p < a.k; ++p) key_insert<T, KL>(list, Key<T>::load(bp.partial, base + p));
+  if constexpr (KL <= 16) {
+    Key<T> next[KL];
+    auto load = [&](int sp) {
+      const int64_t base = ((int64_t)sp * a.N + i) * a.k;
+#pragma unroll
+      for (int p = 0; p < KL; ++p) next[p] = p < a.k ? Key<T>::load(bp.partial, base + p) : Key<T>::sentinel();
+    };
+    load(0);
+    for (int sp = 0; sp < a.n_split; ++sp) {
+      Key<T> cur[KL];
+#pragma unroll
+      for (int p = 0; p < KL; ++p) cur[p] = next[p];
+      if (sp + 1 < a.n_split) load(sp + 1);
+      keep_smallest<T, KL>(list, cur);
+    }
+  } else {
+    for (int sp = 0; sp < a.n_split; ++sp) {
+      const int64_t base = ((int64_t)sp * a.N + i) * a.k;
+      for (int p = 0; p < a.k; ++p) key_insert<T, KL>(list, Key<T>::load(bp.partial, base + p));
+    }
   }
   T *v = static_cast<T *>(bp.out) + i * a.k;
   int64_t *ix = bp.idx + i * a.k;
@@ -342,7 +385,8 @@ static hipError_t merge_t(int consumer, const TileArgs &a, hipStream_t s) {
       hipLaunchKernelGGL(merge_softmax_kernel<T>, blocks(a.N * a.C), block, 0, s, a);
       break;
     case C_TOPK:
-      if (a.k <= 16) hipLaunchKernelGGL((merge_topk_kernel<T, 16>), blocks(a.N), block, 0, s, a);
+      if (a.k <= 8) hipLaunchKernelGGL((merge_topk_kernel<T, 8>), blocks(a.N), block, 0, s, a);
+      else if (a.k <= 16) hipLaunchKernelGGL((merge_topk_kernel<T, 16>), blocks(a.N), block, 0, s, a);
       else hipLaunchKernelGGL((merge_topk_kernel<T, 64>), blocks(a.N), block, 0, s, a);
       break;
     default:

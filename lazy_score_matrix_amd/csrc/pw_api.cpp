@@ -232,6 +232,11 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   }
   const int cus = target_cus();
   int64_t target_wgs = 4 * (int64_t)cus;
+  // The four-rows vector kernels (1024-row blocks, 256-column tiles) only
+  // where their grid can still give every CU a workgroup; smaller problems
+  // keep the finer-grained kernels.
+  const bool four_rows_fill =
+      ((e.N + kProdRows * kValuBM - 1) / (kProdRows * kValuBM)) * ((e.M + kProdBN - 1) / kProdBN) >= cus;
   if (mfma_eligible(e, consumer, C)) {
     p.family = 1;
     p.mcfg.dp = e.D <= 16 ? 16 : (e.D <= 32 ? 32 : 64);
@@ -252,7 +257,8 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
       // A plain float product of narrow points and values takes several
       // rows per thread (one LDS broadcast serves them all) and wide tiles.
       if (consumer == PW_C_MATMUL && e.dtype == PW_F32 && e.metric != PW_COSINE && e.stages.empty() &&
-          !e.row_mask && !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4 && p.vcfg.vtile == 4) {
+          !e.row_mask && !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4 && p.vcfg.vtile == 4 &&
+          four_rows_fill) {
         p.vcfg.rows = kProdRows;
         p.bm = kProdRows * kValuBM;
         p.bn = kProdBN;
@@ -277,7 +283,7 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
                                                    !e.stages[0].col_vec);
       if (consumer == PW_C_LOGSUMEXP && e.dtype == PW_F32 && e.metric != PW_COSINE && row_affine && !e.row_mask &&
           !e.col_mask && !e.band && !e.grow && p.vcfg.dtile <= 4) {
-        if (e.metric == PW_RBF) {
+        if (e.metric == PW_RBF || !four_rows_fill) {
           p.vcfg.rows = 2;
           p.bm = 2 * kValuBM;
         } else {

@@ -271,12 +271,16 @@ def test_blocked_vector_kernels_only_where_they_apply(lib):
     """The several-rows-per-thread vector kernels cover plain float scores of
     narrow points only: the kernel product and the row log-sum-exp of dot
     products and squared distances under at most one row-only stage (four
-    rows, 256-column tiles), the rbf log-sum-exp and the row minimum (two
-    rows). Score arithmetic they do not take, masks, cosine and float64
+    rows, 256-column tiles, where that grid fills the chip), the rbf (or
+    smaller) log-sum-exp and the row minimum (two rows). Score arithmetic they do not take, masks, cosine and float64
     plan one row per thread."""
     MATMUL, LSE, TOPK = 0, 2, 4
-    N, M = 4100, 3000
+    N, M = 4100, 200000
     four = ("valu", "4", "1024", "256")
+    # Too small a grid for 1024-row blocks: the finer kernels.
+    for metric in (0, 1, 2):
+        assert _plan(lib, MATMUL, 4, N=1024, M=1024, D=3, metric=metric)["rows"] == "1"
+        assert _plan(lib, LSE, N=1024, M=1024, D=3, metric=metric)["rows"] == "2"
     for metric in (0, 1, 2):
         p = _plan(lib, MATMUL, 4, N=N, M=M, D=3, metric=metric)
         assert (p["family"], p["rows"], p["bm"], p["bn"]) == four, p

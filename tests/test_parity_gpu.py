@@ -48,6 +48,25 @@ def test_grid_ragged(dtype, metric, consumer, D):
     check_consumer(e, oe, consumer, V=V, k=10, exclude_self=True, what=consumer)
 
 
+SPLIT_GRID = [(dt, m, c, d) for dt in DTYPES for m in METRICS for c in CONSUMERS for d in (3, 5)]
+
+
+@pytest.mark.parametrize("dtype,metric,consumer,D", SPLIT_GRID,
+                         ids=["%s-%s-%s-D%d" % (np.dtype(a).name, b, c, d) for a, b, c, d in SPLIT_GRID])
+def test_vector_engine_column_splits(dtype, metric, consumer, D):
+    """Vector-engine split partials and their merges on every consumer:
+    N = 300, M = 2500 (many column splits, a ragged last tile)."""
+    X, Y, r = _data(17 + D, 300, 2500, D, dtype)
+    V = r.standard_normal((2500, 5)).astype(dtype)
+    ops = _linear_scale(metric, D)
+    if metric == "sqeuclidean" and consumer in ("logsumexp", "softmax_matmul"):
+        ops = [("mul", -0.5)]
+    e, oe = bind_both(X, Y, metric, _gamma(metric, D), ops)
+    plan = e.plan(consumer, 5 if consumer in ("matmul", "softmax_matmul") else 0, 10 if consumer == "topk" else 0)
+    assert "family=valu" in plan and "splits=1 " not in plan, plan
+    check_consumer(e, oe, consumer, V=V, k=10, exclude_self=True, what=consumer)
+
+
 @pytest.mark.parametrize("D", [1, 2, 4, 5, 15, 16, 17, 31, 32, 63, 64])
 def test_feature_dims(D):
     X, Y, r = _data(100 + D, 70, 130, D, np.float32)

@@ -419,3 +419,49 @@ def svgd_direction(x, score, gamma, rows=None):
     phi = (km - 2 * g * kd) / n
     mag = (km_mag + 2 * g * kd_mag) / n
     return phi, mag
+
+
+def mmd2(X, Y, metric="rbf", gamma=1.0, unbiased=True):
+    """Squared maximum mean discrepancy between point clouds X [n, D] and
+    Y [m, D] under the kernel k = the bound score (Task Map, MMD row:
+    mmd_statistics, unbiased by default; one feature set is one cloud), from
+    the dense oracle scores:
+      unbiased: sum_{i != i'} k(x_i, x_i') / (n (n - 1))
+                + sum_{j != j'} k(y_j, y_j') / (m (m - 1))
+                - 2 sum_{i, j} k(x_i, y_j) / (n m)
+      biased:   every pair, diagonals included, over n^2 and m^2.
+    Batched clouds X [B, n, D] with Y [B or 1, m, D] give one value per
+    element. Returns (value, mag): mag sums the three terms' magnitudes
+    (|k| plus its first-order error magnitude, over the same pairs and
+    weights), so that cancellation between the terms keeps a tolerance."""
+    X = np.asarray(X)
+    Y = np.asarray(Y)
+    if X.ndim == 3:
+        Yb = Y if Y.ndim == 3 else Y[None]
+        outs = [mmd2(X[b], Yb[b if Yb.shape[0] > 1 else 0], metric, gamma, unbiased) for b in range(X.shape[0])]
+        return np.array([o[0] for o in outs]), np.array([o[1] for o in outs])
+    n, m = X.shape[0], Y.shape[0]
+    if unbiased and (n < 2 or m < 2):
+        raise ValueError("the unbiased statistic needs at least two points per cloud")
+
+    def term(A, B, same):
+        e = Expr(A, B, metric, gamma=gamma)
+        k, mk = scores(e)
+        real = k.dtype
+        k = np.asarray(k, real)
+        a = np.abs(k) + np.asarray(mk, real)
+        if same and unbiased:
+            keep = ~np.eye(k.shape[0], dtype=bool)
+            return k[keep].sum(), a[keep].sum(), real
+        return k.sum(), a.sum(), real
+
+    sxx, axx, real = term(X, X, True)
+    syy, ayy, _ = term(Y, Y, True)
+    sxy, axy, _ = term(X, Y, False)
+    one = real.type(1)
+    cx = one / (n * (n - 1)) if unbiased else one / (n * n)
+    cy = one / (m * (m - 1)) if unbiased else one / (m * m)
+    cxy = one / (n * m)
+    value = cx * sxx + cy * syy - 2 * cxy * sxy
+    mag = cx * axx + cy * ayy + 2 * cxy * axy
+    return value, mag

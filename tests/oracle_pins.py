@@ -631,6 +631,53 @@ def pin_solve_shift_only():
     _close(A, B / 4.0, rtol=1e-14, atol=1e-15, what="shift only")
 
 
+# ---------------------------------------------------------------- MMD
+def pin_mmd_two_points_closed_form():
+    """Two one-point-apart clouds with a hand-derived statistic (fixture
+    mmd_two_points), unbiased and biased."""
+    c = _golden()["mmd_two_points"]
+    X, Y = np.array(c["X"]), np.array(c["Y"])
+    v, _ = oracle.mmd2(X, Y, "rbf", c["gamma"], unbiased=True)
+    _close(v, _ev(c["expect_unbiased"]), rtol=1e-14, atol=1e-15, what="mmd unbiased")
+    v, _ = oracle.mmd2(X, Y, "rbf", c["gamma"], unbiased=False)
+    _close(v, _ev(c["expect_biased"]), rtol=1e-14, atol=1e-15, what="mmd biased")
+
+
+def pin_mmd_linear_kernel_means():
+    """With the linear kernel the sums reduce to vector sums:
+    sum_{i != i'} x_i.x_i' = |sum x|^2 - sum |x_i|^2, sum_{i,j} x_i.y_j =
+    (sum x).(sum y); the biased statistic is |mean x - mean y|^2."""
+    r = _rng(130)
+    X, Y = r.standard_normal((7, 3)), r.standard_normal((5, 3))
+    sx, sy = X.sum(0), Y.sum(0)
+    n, m = 7, 5
+    want_u = ((sx @ sx - (X * X).sum()) / (n * (n - 1)) + (sy @ sy - (Y * Y).sum()) / (m * (m - 1))
+              - 2 * (sx @ sy) / (n * m))
+    v, _ = oracle.mmd2(X, Y, "linear", unbiased=True)
+    _close(v, want_u, rtol=1e-12, atol=1e-14, what="linear mmd unbiased")
+    dm = X.mean(0) - Y.mean(0)
+    v, _ = oracle.mmd2(X, Y, "linear", unbiased=False)
+    _close(v, dm @ dm, rtol=1e-12, atol=1e-14, what="linear mmd biased")
+
+
+def pin_mmd_symmetric_and_batched():
+    """MMD(X, Y) = MMD(Y, X); a batch of clouds gives each element's value,
+    a cloud shared by the batch ([1, m, D]) included; the magnitude bounds
+    the sum of the terms' absolute values."""
+    r = _rng(131)
+    X, Y = r.standard_normal((3, 6, 2)), r.standard_normal((3, 4, 2))
+    for unb in (True, False):
+        a, ma = oracle.mmd2(X[0], Y[0], "rbf", 0.4, unb)
+        b, _ = oracle.mmd2(Y[0], X[0], "rbf", 0.4, unb)
+        _close(a, b, rtol=1e-14, atol=1e-15, what="symmetry")
+        assert ma >= abs(a)
+        vb, _ = oracle.mmd2(X, Y, "rbf", 0.4, unb)
+        for k in range(3):
+            _close(vb[k], oracle.mmd2(X[k], Y[k], "rbf", 0.4, unb)[0], rtol=1e-15, atol=0, what="batch")
+        vs, _ = oracle.mmd2(X, Y[:1], "rbf", 0.4, unb)
+        _close(vs[2], oracle.mmd2(X[2], Y[0], "rbf", 0.4, unb)[0], rtol=1e-15, atol=0, what="shared cloud")
+
+
 # ---------------------------------------------------------------- backward
 def _autograd_reference(X, Y, metric, gamma, ops, consumer, G, V=None, exclude_self=False, masks=(), indices=None):
     """Gradients of sum(out * G) by torch autograd on the dense float64

@@ -6,6 +6,7 @@ a temporary library. Every pin of oracle_pins.py is run against it; the test
 passes only if some pin fails. Mutations keep every access in bounds.
 """
 import concurrent.futures as cf
+import inspect
 import os
 import subprocess
 
@@ -123,4 +124,37 @@ def test_planted_mistake_is_caught(name, mutant_libs):
                 caught.append(pin.__name__)
     finally:
         oracle._lib = prev
+    assert caught, "no pin catches the planted mistake %s" % name
+
+
+# Planted mistakes in the oracle's Python-level MMD (a composition of the
+# dense oracle scores), applied to its source text and run in the oracle
+# module's namespace.
+PY_MUTANTS = [
+    ("mmd_keeps_diagonal", "keep = ~np.eye(k.shape[0], dtype=bool)", "keep = np.ones_like(k, dtype=bool)"),
+    ("mmd_unbiased_over_n_squared", "cx = one / (n * (n - 1)) if unbiased else one / (n * n)",
+     "cx = one / (n * n)"),
+    ("mmd_cross_term_once", "value = cx * sxx + cy * syy - 2 * cxy * sxy", "value = cx * sxx + cy * syy - cxy * sxy"),
+    ("mmd_y_within_from_x", "syy, ayy, _ = term(Y, Y, True)", "syy, ayy, _ = term(X, X, True)"),
+]
+
+
+@pytest.mark.parametrize("name", [m[0] for m in PY_MUTANTS])
+def test_planted_python_mistake_is_caught(name):
+    _, old, new = next(m for m in PY_MUTANTS if m[0] == name)
+    src = inspect.getsource(oracle.mmd2)
+    assert src.count(old) == 1, "mutation %s does not match exactly once" % name
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), "<mutant %s>" % name, "exec"), ns)
+    keep = oracle.mmd2
+    oracle.mmd2 = ns["mmd2"]
+    caught = []
+    try:
+        for pin in ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(pin.__name__)
+    finally:
+        oracle.mmd2 = keep
     assert caught, "no pin catches the planted mistake %s" % name

@@ -264,6 +264,30 @@ int pw_topk_noalloc(const pw_expr *e, int k, int largest, void *values, int64_t 
 int pw_mean_workspace_size(const pw_expr *e, size_t *bytes);
 int pw_mean(const pw_expr *e, void *out, void *inv_counts, void *ws, size_t ws_bytes, void *stream);
 
+/* Squared maximum mean discrepancy between point clouds (guide, Task Map,
+ * MMD row: mmd_statistics of [B, n, D] and [B, m, D] clouds, one feature set
+ * per cloud, unbiased by default), under the kernel k given by `metric` and
+ * `gamma` (any built-in metric; all are symmetric):
+ *   unbiased: sum_{i != i'} k(x_i, x_i') / (n (n-1))
+ *             + sum_{j != j'} k(y_j, y_j') / (m (m-1)) - 2 sum_{i,j} k(x_i, y_j) / (n m)
+ *   biased:   the within-cloud sums over all pairs, over n^2 and m^2.
+ * The three sums are kernel products with a column of ones; a within-cloud
+ * sum of the unbiased statistic takes the strict upper triangle (a band
+ * mask: half the pairs) and doubles it. One kernel per batch element adds
+ * the row sums in double and forms the statistic.
+ *   X     element b's cloud at X + b*sx ([n, ldx] row-major, dtype); sx = 0
+ *         shares one cloud across the batch; likewise Y, m, ldy, sy
+ *   B     1..65535 batch elements; n, m >= 2 (unbiased) or >= 1 (biased);
+ *         D 1..PW_MAX_D
+ *   out   [B] device vector of the dtype
+ * Workspace: pw_mmd2_workspace_size bytes, caller-owned. Errors as pw_bind
+ * (PW_ERR_INVALID / PW_ERR_UNSUPPORTED) before any device work. */
+int pw_mmd2_workspace_size(int dtype, int metric, double gamma, int64_t n, int64_t m, int64_t D, int64_t B,
+                           size_t *bytes);
+int pw_mmd2(int dtype, int metric, double gamma, const void *X, int64_t n, int64_t ldx, int64_t sx, const void *Y,
+            int64_t m, int64_t ldy, int64_t sy, int64_t D, int64_t B, int unbiased, void *out, void *ws,
+            size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Backward by replay (guide, opening section: the consumer's backward
  * re-evaluates the pairs instead of keeping the [N, M] matrix; "What to

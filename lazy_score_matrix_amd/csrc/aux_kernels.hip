@@ -112,6 +112,50 @@ hipError_t launch_mean_finish(int dtype, void *out, int64_t N, int64_t B, const 
 }
 
 // ---------------------------------------------------------------------------
+// Squared MMD from three row-sum vectors, one workgroup per batch element:
+// each thread adds a strided share of every vector in double, then a fixed
+// LDS tree adds the threads' shares.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void mmd_finish_kernel(const T *rxx, const T *ryy, const T *rxy, int64_t n,
+                                                         int64_t m, double cx, double cy, double cxy, T *out) {
+  __shared__ double part[3][256];
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  double sx = 0.0, sy = 0.0, sxy = 0.0;
+  for (int64_t i = tid; i < n; i += 256) {
+    sx += (double)rxx[b * n + i];
+    sxy += (double)rxy[b * n + i];
+  }
+  for (int64_t j = tid; j < m; j += 256) sy += (double)ryy[b * m + j];
+  part[0][tid] = sx;
+  part[1][tid] = sy;
+  part[2][tid] = sxy;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) part[q][tid] += part[q][tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) out[b] = (T)(cx * part[0][0] + cy * part[1][0] - cxy * part[2][0]);
+}
+
+hipError_t launch_mmd_finish(int dtype, const void *rxx, const void *ryy, const void *rxy, int64_t n, int64_t m,
+                             int64_t B, double cx, double cy, double cxy, void *out, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid((unsigned)B), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(mmd_finish_kernel<float>, grid, block, 0, s, (const float *)rxx, (const float *)ryy,
+                       (const float *)rxy, n, m, cx, cy, cxy, (float *)out);
+  else
+    hipLaunchKernelGGL(mmd_finish_kernel<double>, grid, block, 0, s, (const double *)rxx, (const double *)ryy,
+                       (const double *)rxy, n, m, cx, cy, cxy, (double *)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Group ranges for the same_group mask: min and max id of each block of
 // `block` consecutive entries (a row block, or a key tile), so the tile
 // kernels can skip pairs of blocks whose ranges are disjoint. One wave per

@@ -1458,3 +1458,113 @@ int pw_cg_solve(const pw_expr *e, double shift, const void *B, int64_t C, int64_
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// Squared MMD: three batched kernel products with a column of ones (within
+// X, within Y, across). The unbiased statistic's within-cloud sums take the
+// strict upper triangle (band mask: keep j >= i + 1) and count it twice; all
+// built-in metrics are symmetric. One finishing kernel per batch element.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct MmdExprs {
+  ExprHolder xx, yy, xy;
+};
+
+int mmd_bind(int dtype, int metric, double gamma, const void *X, int64_t n, int64_t ldx, int64_t sx, const void *Y,
+             int64_t m, int64_t ldy, int64_t sy, int64_t D, int64_t B, bool unbiased, MmdExprs *ex) {
+  pw_op upper{};
+  upper.kind = PW_OP_BAND_LOWER;  // i - j <= -1
+  upper.scalar = -1.0;
+  const int n_ops = unbiased ? 1 : 0;
+  pw_batch bx{}, by{}, bxy{};
+  bx.B = by.B = bxy.B = B;
+  bx.sx = bx.sy = sx;
+  by.sx = by.sy = sy;
+  bxy.sx = sx;
+  bxy.sy = sy;
+  int rc = bind_impl(&ex->xx.e, dtype, metric, gamma, X, n, ldx, X, n, ldx, D, &upper, n_ops, &bx);
+  if (rc == PW_OK) rc = bind_impl(&ex->yy.e, dtype, metric, gamma, Y, m, ldy, Y, m, ldy, D, &upper, n_ops, &by);
+  if (rc == PW_OK) rc = bind_impl(&ex->xy.e, dtype, metric, gamma, X, n, ldx, Y, m, ldy, D, nullptr, 0, &bxy);
+  return rc;
+}
+
+// Workspace: ones [max(n, m)], row sums rxx [B][n], ryy [B][m], rxy [B][n],
+// then the largest of the three products' workspaces.
+struct MmdLayout {
+  size_t rxx = 0, ryy = 0, rxy = 0, prod = 0, prod_bytes = 0, total = 0;
+};
+
+MmdLayout mmd_layout(const MmdExprs &ex) {
+  MmdLayout L;
+  const pw_expr &x = *ex.xx.e;
+  const size_t es = esize(x.dtype), n = (size_t)x.N, m = (size_t)ex.yy.e->N, B = (size_t)x.B;
+  size_t off = align_up(std::max(n, m) * es);
+  L.rxx = off;
+  off += align_up(B * n * es);
+  L.ryy = off;
+  off += align_up(B * m * es);
+  L.rxy = off;
+  off += align_up(B * n * es);
+  L.prod = off;
+  for (const pw_expr *e : {ex.xx.e, ex.yy.e, ex.xy.e})
+    L.prod_bytes = std::max(L.prod_bytes, make_plan(*e, PW_C_MATMUL, 1, 0).total);
+  L.total = off + L.prod_bytes + kAlign;
+  return L;
+}
+
+int mmd_check_sizes(int64_t n, int64_t m, int64_t B, int unbiased) {
+  if (unbiased != 0 && unbiased != 1) return PW_ERR_INVALID;
+  if (B < 1 || n < (unbiased ? 2 : 1) || m < (unbiased ? 2 : 1)) return PW_ERR_INVALID;
+  return PW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pw_mmd2_workspace_size(int dtype, int metric, double gamma, int64_t n, int64_t m, int64_t D, int64_t B,
+                           size_t *bytes) {
+  if (!bytes) return PW_ERR_INVALID;
+  *bytes = 0;
+  int rc = mmd_check_sizes(n, m, B, 0);
+  if (rc != PW_OK) return rc;
+  // Sizes only: aligned stand-in pointers, and per-element clouds (the
+  // larger workspace of the two stride cases).
+  const void *fake = reinterpret_cast<const void *>(kAlign);
+  MmdExprs ex;
+  rc = mmd_bind(dtype, metric, gamma, fake, n, D, 1, fake, m, D, 1, D, B, true, &ex);
+  if (rc != PW_OK) return rc;
+  MmdExprs exb;
+  rc = mmd_bind(dtype, metric, gamma, fake, n, D, 1, fake, m, D, 1, D, B, false, &exb);
+  if (rc != PW_OK) return rc;
+  *bytes = std::max(mmd_layout(ex).total, mmd_layout(exb).total);
+  return PW_OK;
+}
+
+int pw_mmd2(int dtype, int metric, double gamma, const void *X, int64_t n, int64_t ldx, int64_t sx, const void *Y,
+            int64_t m, int64_t ldy, int64_t sy, int64_t D, int64_t B, int unbiased, void *out, void *ws,
+            size_t ws_bytes, void *stream) {
+  int rc = mmd_check_sizes(n, m, B, unbiased);
+  if (rc != PW_OK) return rc;
+  if (dtype != PW_F32 && dtype != PW_F64) return PW_ERR_INVALID;
+  if (!out || !aligned(out, esize(dtype))) return PW_ERR_INVALID;
+  MmdExprs ex;
+  rc = mmd_bind(dtype, metric, gamma, X, n, ldx, sx, Y, m, ldy, sy, D, B, unbiased != 0, &ex);
+  if (rc != PW_OK) return rc;
+  const MmdLayout L = mmd_layout(ex);
+  if (!ws || ws_bytes < L.total) return PW_ERR_WORKSPACE;
+  char *base = reinterpret_cast<char *>(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+  hipStream_t s = (hipStream_t)stream;
+  void *ones = base, *rxx = base + L.rxx, *ryy = base + L.ryy, *rxy = base + L.rxy;
+  rc = hip_status(launch_fill(dtype, ones, std::max(n, m), 1, 1, 1.0, s));
+  if (rc == PW_OK) rc = value_consumer(ex.xx.e, PW_C_MATMUL, ones, 1, 1, rxx, 1, base + L.prod, L.prod_bytes, stream);
+  if (rc == PW_OK) rc = value_consumer(ex.yy.e, PW_C_MATMUL, ones, 1, 1, ryy, 1, base + L.prod, L.prod_bytes, stream);
+  if (rc == PW_OK) rc = value_consumer(ex.xy.e, PW_C_MATMUL, ones, 1, 1, rxy, 1, base + L.prod, L.prod_bytes, stream);
+  if (rc != PW_OK) return rc;
+  const double dn = (double)n, dm = (double)m;
+  const double cx = unbiased ? 2.0 / (dn * (dn - 1.0)) : 1.0 / (dn * dn);
+  const double cy = unbiased ? 2.0 / (dm * (dm - 1.0)) : 1.0 / (dm * dm);
+  return hip_status(launch_mmd_finish(dtype, rxx, ryy, rxy, n, m, B, cx, cy, 2.0 / (dn * dm), out, s));
+}
+
+}  // extern "C"

@@ -318,6 +318,11 @@ hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t
 // row with none; inv[i] = 1 / count (0 for none) when inv is not null.
 hipError_t launch_mean_finish(int dtype, void *out, int64_t N, int64_t B, const void *cnt, int64_t M, void *inv,
                               hipStream_t s);
+// Per batch element b: the squared MMD from the kernel products' row sums
+// rxx [B][n], ryy [B][m], rxy [B][n]: cx * sum rxx + cy * sum ryy - cxy * sum
+// rxy, the sums in double in a fixed order; out [B].
+hipError_t launch_mmd_finish(int dtype, const void *rxx, const void *ryy, const void *rxy, int64_t n, int64_t m,
+                             int64_t B, double cx, double cy, double cxy, void *out, hipStream_t s);
 // Row norms |x_i|^2, or with `inverse` 1/|x_i| (0 for a zero row).
 // With n_batch > 1, element b reads X + b * x_bstride and writes out +
 // b * out_bstride (bytes).

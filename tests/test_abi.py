@@ -401,3 +401,33 @@ def test_mean_validation_and_workspace(lib):
             sizes[M, masked] = n.value
             lib.pw_release(h)
     assert all(v < 2048 * M for (M, _), v in sizes.items())
+
+
+def test_mmd_validation_and_workspace(lib):
+    """pw_mmd2: the unbiased statistic needs two points per cloud, the
+    biased one one; B in 1..65535; flags 0/1; every check precedes device
+    work. The workspace holds three row-sum vectors per batch element and
+    never grows with n*m."""
+    n = ctypes.c_size_t()
+    assert lib.pw_mmd2_workspace_size(0, 2, 1.0, 100, 80, 3, 2, None) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_workspace_size(0, 2, 1.0, 0, 80, 3, 2, ctypes.byref(n)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_workspace_size(0, 2, 1.0, 100, 80, 3, 0, ctypes.byref(n)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_workspace_size(0, 2, 1.0, 100, 80, 3, 65536, ctypes.byref(n)) == pw.PW_ERR_UNSUPPORTED
+    assert lib.pw_mmd2_workspace_size(0, 2, 1.0, 100, 80, 65, 2, ctypes.byref(n)) == pw.PW_ERR_UNSUPPORTED
+    args = lambda **kw: [kw.get(k, v) for k, v in (("dtype", 0), ("metric", 2), ("gamma", 1.0), ("X", FAKE), ("n", 100),
+                         ("ldx", 3), ("sx", 300), ("Y", FAKE), ("m", 80), ("ldy", 3), ("sy", 240), ("D", 3), ("B", 2),
+                         ("unbiased", 1), ("out", FAKE), ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
+    assert lib.pw_mmd2(*args(n=1)) == pw.PW_ERR_INVALID          # unbiased needs two points
+    assert lib.pw_mmd2(*args(unbiased=2)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2(*args(out=FAKE + 2)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2(*args(out=0)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2(*args(sx=-1)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2(*args(ldx=2)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2(*args(metric=7)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2(*args(ws=0)) == pw.PW_ERR_WORKSPACE
+    sizes = []
+    for m in (4096, 16384):
+        assert lib.pw_mmd2_workspace_size(0, 2, 1.0, 2048, m, 3, 2, ctypes.byref(n)) == pw.PW_OK
+        sizes.append(n.value)
+        assert n.value >= 4 * (2 * (2048 + m + 2048))
+        assert n.value < 2048 * m

@@ -465,3 +465,46 @@ def mmd2(X, Y, metric="rbf", gamma=1.0, unbiased=True):
     value = cx * sxx + cy * syy - 2 * cxy * sxy
     mag = cx * axx + cy * ayy + 2 * cxy * axy
     return value, mag
+
+
+def mmd2_grad(X, Y, metric="rbf", gamma=1.0, unbiased=True, G=1.0):
+    """Gradients of G * mmd2(X, Y) with respect to both clouds: each of the
+    statistic's three sums is the kernel product of its pairs with a column
+    of ones, so its gradient is that product's chain-rule backward (row and
+    column sides) with the sum's coefficient as upstream gradient; distinct
+    pairs of one cloud are its two strict triangles (band masks j > i and
+    j < i). Batched clouds ([B, n, D] with Y [B or 1, m, D], G [B]) give
+    per-element gradients; a cloud shared by the batch gets their sum.
+    Returns ((dX, dX_mag), (dY, dY_mag)), each mag summing its pieces'."""
+    X = np.asarray(X)
+    Y = np.asarray(Y)
+    if X.ndim == 3:
+        Yb = Y if Y.ndim == 3 else Y[None]
+        Gb = np.broadcast_to(np.asarray(G, np.float64), (X.shape[0],))
+        parts = [mmd2_grad(X[b], Yb[b if Yb.shape[0] > 1 else 0], metric, gamma, unbiased, Gb[b])
+                 for b in range(X.shape[0])]
+        dX = np.stack([p[0][0] for p in parts]), np.stack([p[0][1] for p in parts])
+        dY = np.stack([p[1][0] for p in parts]), np.stack([p[1][1] for p in parts])
+        if Yb.shape[0] == 1 and X.shape[0] > 1:
+            dY = dY[0].sum(0, keepdims=True), dY[1].sum(0, keepdims=True)
+        return dX, dY
+    n, m = X.shape[0], Y.shape[0]
+    g = float(G)
+
+    def pieces(A, B, ops, coef):
+        e = Expr(A, B, metric, gamma=gamma, ops=ops)
+        r = backward(e, "matmul", np.full((A.shape[0], 1), coef), np.ones((B.shape[0], 1)))
+        return r["dX"], r["dY"]
+
+    def within(A, k):
+        if unbiased:
+            c = g / (k * (k - 1))
+            parts = pieces(A, A, [("band", (-1, 10 ** 9))], c) + pieces(A, A, [("band", (10 ** 9, -1))], c)
+        else:
+            parts = pieces(A, A, [], g / (k * k))
+        return sum(p[0] for p in parts), sum(p[1] for p in parts)
+
+    wx, wxm = within(X, n)
+    wy, wym = within(Y, m)
+    cx_, cy_ = pieces(X, Y, [], -2.0 * g / (n * m))
+    return (wx + cx_[0], wxm + cx_[1]), (wy + cy_[0], wym + cy_[1])

@@ -678,6 +678,60 @@ def pin_mmd_symmetric_and_batched():
         _close(vs[2], oracle.mmd2(X[2], Y[0], "rbf", 0.4, unb)[0], rtol=1e-15, atol=0, what="shared cloud")
 
 
+def _mmd2_torch(X, Y, metric, gamma, unbiased):
+    """The statistic written out densely in torch float64 (squared
+    distances as sums of squared differences, so that autograd is defined
+    at coincident points)."""
+    def k(A, B):
+        if metric == "linear":
+            return A @ B.T
+        d2 = ((A[:, None, :] - B[None, :, :]) ** 2).sum(-1)
+        return torch.exp(-gamma * d2) if metric == "rbf" else d2
+    n, m = X.shape[0], Y.shape[0]
+    kxx, kyy, kxy = k(X, X), k(Y, Y), k(X, Y)
+    if unbiased:
+        kxx = kxx * (1 - torch.eye(n, dtype=X.dtype))
+        kyy = kyy * (1 - torch.eye(m, dtype=X.dtype))
+        return kxx.sum() / (n * (n - 1)) + kyy.sum() / (m * (m - 1)) - 2 * kxy.sum() / (n * m)
+    return kxx.sum() / (n * n) + kyy.sum() / (m * m) - 2 * kxy.sum() / (n * m)
+
+
+def pin_mmd_value_and_gradient_vs_torch():
+    """mmd2 and mmd2_grad against torch autograd of the dense statistic
+    (float64), for the rbf, linear and squared-distance kernels, unbiased
+    and biased, with a scaled upstream gradient."""
+    r = _rng(132)
+    X, Y = r.standard_normal((6, 3)), 0.5 + r.standard_normal((5, 3))
+    for metric in ("rbf", "linear", "sqeuclidean"):
+        for unb in (True, False):
+            Xt = torch.tensor(X, requires_grad=True)
+            Yt = torch.tensor(Y, requires_grad=True)
+            v = _mmd2_torch(Xt, Yt, metric, 0.3, unb)
+            gx, gy = torch.autograd.grad(1.7 * v, [Xt, Yt])
+            ov, _ = oracle.mmd2(X, Y, metric, 0.3, unb)
+            _close(ov, v.item(), rtol=1e-12, atol=1e-13, what="mmd %s value" % metric)
+            (dx, dxm), (dy, dym) = oracle.mmd2_grad(X, Y, metric, 0.3, unb, 1.7)
+            _close(dx, gx.numpy(), rtol=1e-11, atol=1e-12, what="mmd %s dX" % metric)
+            _close(dy, gy.numpy(), rtol=1e-11, atol=1e-12, what="mmd %s dY" % metric)
+            assert np.all(np.asarray(dxm) >= np.abs(np.asarray(dx)) * (1 - 1e-12))
+
+
+def pin_mmd_gradient_batched_and_shared():
+    """Batched gradients equal the per-element ones; a cloud shared by the
+    batch gets the sum of the elements' gradients."""
+    r = _rng(133)
+    X, Y = r.standard_normal((3, 5, 2)), r.standard_normal((1, 4, 2))
+    G = np.array([0.5, -1.0, 2.0])
+    (dX, _), (dY, _) = oracle.mmd2_grad(X, Y, "rbf", 0.6, True, G)
+    assert dX.shape == (3, 5, 2) and dY.shape == (1, 4, 2)
+    want_y = 0
+    for b in range(3):
+        (dx, _), (dy, _) = oracle.mmd2_grad(X[b], Y[0], "rbf", 0.6, True, G[b])
+        _close(dX[b], dx, rtol=1e-15, atol=0, what="batched dX")
+        want_y = want_y + np.asarray(dy, np.float64)
+    _close(dY[0], want_y, rtol=1e-13, atol=1e-15, what="shared dY")
+
+
 # ---------------------------------------------------------------- backward
 def _autograd_reference(X, Y, metric, gamma, ops, consumer, G, V=None, exclude_self=False, masks=(), indices=None):
     """Gradients of sum(out * G) by torch autograd on the dense float64

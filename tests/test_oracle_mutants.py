@@ -131,23 +131,33 @@ def test_planted_mistake_is_caught(name, mutant_libs):
 # dense oracle scores), applied to its source text and run in the oracle
 # module's namespace.
 PY_MUTANTS = [
-    ("mmd_keeps_diagonal", "keep = ~np.eye(k.shape[0], dtype=bool)", "keep = np.ones_like(k, dtype=bool)"),
-    ("mmd_unbiased_over_n_squared", "cx = one / (n * (n - 1)) if unbiased else one / (n * n)",
+    ("mmd_keeps_diagonal", "mmd2", "keep = ~np.eye(k.shape[0], dtype=bool)", "keep = np.ones_like(k, dtype=bool)"),
+    ("mmd_unbiased_over_n_squared", "mmd2", "cx = one / (n * (n - 1)) if unbiased else one / (n * n)",
      "cx = one / (n * n)"),
-    ("mmd_cross_term_once", "value = cx * sxx + cy * syy - 2 * cxy * sxy", "value = cx * sxx + cy * syy - cxy * sxy"),
-    ("mmd_y_within_from_x", "syy, ayy, _ = term(Y, Y, True)", "syy, ayy, _ = term(X, X, True)"),
+    ("mmd_cross_term_once", "mmd2", "value = cx * sxx + cy * syy - 2 * cxy * sxy",
+     "value = cx * sxx + cy * syy - cxy * sxy"),
+    ("mmd_y_within_from_x", "mmd2", "syy, ayy, _ = term(Y, Y, True)", "syy, ayy, _ = term(X, X, True)"),
+    ("mmd_grad_one_triangle", "mmd2_grad",
+     "parts = pieces(A, A, [(\"band\", (-1, 10 ** 9))], c) + pieces(A, A, [(\"band\", (10 ** 9, -1))], c)",
+     "parts = pieces(A, A, [(\"band\", (-1, 10 ** 9))], c)"),
+    ("mmd_grad_row_side_only", "mmd2_grad", "return sum(p[0] for p in parts), sum(p[1] for p in parts)",
+     "return sum(p[0] for p in parts[::2]), sum(p[1] for p in parts[::2])"),
+    ("mmd_grad_cross_sign", "mmd2_grad", "cx_, cy_ = pieces(X, Y, [], -2.0 * g / (n * m))",
+     "cx_, cy_ = pieces(X, Y, [], 2.0 * g / (n * m))"),
+    ("mmd_grad_shared_cloud_not_summed", "mmd2_grad", "dY = dY[0].sum(0, keepdims=True), dY[1].sum(0, keepdims=True)",
+     "dY = dY[0][:1], dY[1][:1]"),
 ]
 
 
 @pytest.mark.parametrize("name", [m[0] for m in PY_MUTANTS])
 def test_planted_python_mistake_is_caught(name):
-    _, old, new = next(m for m in PY_MUTANTS if m[0] == name)
-    src = inspect.getsource(oracle.mmd2)
+    _, fn, old, new = next(m for m in PY_MUTANTS if m[0] == name)
+    src = inspect.getsource(getattr(oracle, fn))
     assert src.count(old) == 1, "mutation %s does not match exactly once" % name
     ns = dict(vars(oracle))
     exec(compile(src.replace(old, new), "<mutant %s>" % name, "exec"), ns)
-    keep = oracle.mmd2
-    oracle.mmd2 = ns["mmd2"]
+    keep = getattr(oracle, fn)
+    setattr(oracle, fn, ns[fn])
     caught = []
     try:
         for pin in ALL_PINS:
@@ -156,5 +166,5 @@ def test_planted_python_mistake_is_caught(name):
             except AssertionError:
                 caught.append(pin.__name__)
     finally:
-        oracle.mmd2 = keep
+        setattr(oracle, fn, keep)
     assert caught, "no pin catches the planted mistake %s" % name

@@ -110,6 +110,8 @@ def flops_per_pair(case, D, C):
         return body + 1 + 2  # the 1/M scale, then a product with a ones column
     if case.consumer == "cg_solve":
         return body + 2 * C  # one kernel product per iteration
+    if case.consumer == "mmd":
+        return body + 2  # each of its products sums the scores against a ones column
     if case.consumer == "backward_softmax_matmul":
         # Both sides replay the pair: metric and ops, the upstream dot
         # product (2C) and exp, the gradient sums (2D); the column side
@@ -128,7 +130,7 @@ def lib_consumer(c):
     as its forward consumer)."""
     if c.consumer.startswith("backward_"):
         return c.consumer[len("backward_"):]
-    return "matmul" if c.consumer in ("mean", "cg_solve") else c.consumer
+    return "matmul" if c.consumer in ("mean", "cg_solve", "mmd") else c.consumer
 
 
 def case_operands(c, arrays):
@@ -167,7 +169,7 @@ def build_calls(name, dev):
         e = pw.lazy(X, Y, c.metric, gamma=c.gamma, ops=ops)
         N, D = X.shape
         M = Y.shape[0]
-        C = t[c.v].shape[1] if c.v else (1 if c.consumer == "mean" else 0)
+        C = t[c.v].shape[1] if c.v else (1 if c.consumer in ("mean", "mmd") else 0)
         if c.consumer == "backward_softmax_matmul":
             # One step is the backward given dO and the forward output (the
             # forward itself runs once, before the timed region).
@@ -196,6 +198,21 @@ def build_calls(name, dev):
                   log.append(e.solve(B, p["shift"], rtol=p["rtol"], max_iter=p["max_iter"], out=A,
                                      workspace=ws)[1]))
             outs = (A,)
+        elif c.consumer == "mmd":
+            # One step is the whole statistic (pw_mmd2: three products with
+            # ones and the finishing kernel). Its tile events keep the last
+            # product's launch: the cross-cloud one, N * M pairs.
+            lib = pw.load_library()
+            dt, mt = pw.DTYPES[X.dtype], pw.METRICS[c.metric]
+            n_ws = ctypes.c_size_t()
+            pw.check(lib.pw_mmd2_workspace_size(dt, mt, c.gamma, N, M, D, 1, ctypes.byref(n_ws)))
+            ws = torch.empty(n_ws.value, dtype=torch.uint8, device=dev)
+            out = torch.empty(1, dtype=X.dtype, device=dev)
+            unb = int(c.params.get("unbiased", True))
+            fn = (lambda X=X, Y=Y, out=out, ws=ws, dt=dt, mt=mt, g=c.gamma, unb=unb, N=N, M=M, D=D, lib=lib:
+                  pw.check(lib.pw_mmd2(dt, mt, g, X.data_ptr(), N, D, 0, Y.data_ptr(), M, D, 0, D, 1, unb,
+                                       out.data_ptr(), ws.data_ptr(), ws.numel(), pw._stream(X.device)), "pw_mmd2"))
+            outs = (out,)
         elif c.consumer == "mean":
             # The row mean: the scores scaled by 1/M (an extra op bound
             # above) times a ones column, as LazyScores.mean computes it.
@@ -316,7 +333,8 @@ def kernel_entries(name, calls, kernel_ms):
         mfma = is_contraction(c, e, C)
         peak = PEAK_TFLOPS[dtype] if mfma else ALU_PEAK_TFLOPS[dtype]
         fpp = flops_per_pair(c, e.D, C)
-        pairs = float(c.pairs if c.pairs is not None else e.N * e.M)
+        # An MMD step's timed tile kernel is its cross-cloud product.
+        pairs = float(e.N * e.M if c.consumer == "mmd" or c.pairs is None else c.pairs)
         tf = pairs * fpp / (kms * 1e-3) / 1e12
         plan = (e.backward_plan(lib_consumer(c), C) if c.consumer.startswith("backward_")
                 else e.plan(lib_consumer(c), C, c.k))
@@ -496,6 +514,36 @@ def backward_cpu_leg(c, oe, arrays, outs, budget, threads):
     return pairs, dt, desc, {"call": c.name, "rows": len(rows), "pass": bool(ok), "worst_err_over_tol": worst}
 
 
+def mmd_cpu_leg(c, X, Y, seconds, threads):
+    """The oracle's statistic on the first s points of each cloud, s sized
+    to the time budget (the statistic has no row sample), and the GPU's
+    pw_mmd2 on the same sub-clouds against it."""
+    import torch
+    import oracle
+    import lazy_score_matrix_amd as pw
+    from parity import value_report
+
+    unb = c.params.get("unbiased", True)
+    s = 256
+    t0 = time.perf_counter()
+    oracle.mmd2(X[:s], Y[:s], c.metric, c.gamma, unb)
+    tp = max(time.perf_counter() - t0, 1e-6)
+    s = int(min(X.shape[0], Y.shape[0], 4096, s * max(1.0, (seconds / tp) ** 0.5)))
+    t0 = time.perf_counter()
+    o, mag = oracle.mmd2(X[:s], Y[:s], c.metric, c.gamma, unb)
+    dt = time.perf_counter() - t0
+    pairs = s * (s - 1) + s * s  # the within-cloud sums (distinct pairs) and the cross sum
+    dev = torch.device("cuda:0")
+    g = pw.mmd_statistics(torch.from_numpy(np.ascontiguousarray(X[:s])).to(dev),
+                          torch.from_numpy(np.ascontiguousarray(Y[:s])).to(dev), c.metric, c.gamma, unb)
+    ok, ratio, rel = value_report(np.atleast_1d(g.cpu().numpy()), np.atleast_1d(o), np.atleast_1d(mag),
+                                  np.dtype(X.dtype), n_terms=s * s)
+    desc = ("%s: the oracle's statistic on the first %d points of each cloud (its dense scores), and pw_mmd2 "
+            "on the same sub-clouds checked against it" % (c.name, s))
+    return pairs, dt, desc, {"call": c.name, "points": s, "pass": bool(ok), "worst_err_over_tol": ratio,
+                             "max_plain_rel_err": rel}
+
+
 def cpu_leg(name, calls, arrays, seconds):
     """Time the oracle on a bounded row sample of one workload on the host
     cores (about `seconds` per call), and check the timed GPU outputs
@@ -517,6 +565,13 @@ def cpu_leg(name, calls, arrays, seconds):
             # iteration: timed as S @ A on the sampled rows, which is also
             # the true residual's product for the parity check.
             A_gpu = outs[0].cpu().numpy()
+        if c.consumer == "mmd":
+            total_pairs_m, dt_m, desc_m, par_m = mmd_cpu_leg(c, X, Y, budget, threads)
+            total_pairs += total_pairs_m
+            total_s += dt_m
+            rows_desc.append(desc_m)
+            parity.append(par_m)
+            continue
         if c.consumer.startswith("backward_"):
             total_pairs_b, dt_b, desc_b, par_b = backward_cpu_leg(c, oe, arrays, outs, budget, threads)
             total_pairs += total_pairs_b

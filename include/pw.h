@@ -288,6 +288,26 @@ int pw_mmd2(int dtype, int metric, double gamma, const void *X, int64_t n, int64
             int64_t m, int64_t ldy, int64_t sy, int64_t D, int64_t B, int unbiased, void *out, void *ws,
             size_t ws_bytes, void *stream);
 
+/* Gradients of sum_b G[b] * MMD2_b (the statistics of pw_mmd2 with the same
+ * arguments) with respect to both clouds (Task Map: every row has
+ * first-order gradients; guide, opening section: a backward replays the
+ * pairs). Each of the three sums is a kernel product with ones, so its
+ * gradient is pw_backward of that product (row and column sides) with a
+ * column of ones as upstream gradient; a kernel then adds the sides with
+ * the statistic's coefficients, scaled by G[b]. Batch elements run one after
+ * another (the backward takes unbatched products).
+ *   G     [B] device vector (dtype): upstream gradient of each statistic
+ *   dX    [B][n][lddx] (sx > 0), or [n][lddx] (sx == 0: the gradient of the
+ *         shared cloud, summed over the batch), or NULL if not wanted;
+ *         lddx >= D; dY, lddy likewise for Y. Outputs are overwritten.
+ * Workspace: pw_mmd2_backward_workspace_size bytes. Errors as pw_mmd2. */
+int pw_mmd2_backward_workspace_size(int dtype, int metric, double gamma, int64_t n, int64_t m, int64_t D,
+                                    size_t *bytes);
+int pw_mmd2_backward(int dtype, int metric, double gamma, const void *X, int64_t n, int64_t ldx, int64_t sx,
+                     const void *Y, int64_t m, int64_t ldy, int64_t sy, int64_t D, int64_t B, int unbiased,
+                     const void *G, void *dX, int64_t lddx, void *dY, int64_t lddy, void *ws, size_t ws_bytes,
+                     void *stream);
+
 /* ------------------------------------------------------------------------
  * Backward by replay (guide, opening section: the consumer's backward
  * re-evaluates the pairs instead of keeping the [N, M] matrix; "What to

@@ -113,6 +113,10 @@ def load_library(path: str = LIB_PATH):
         lib.pw_mmd2_workspace_size.argtypes = [c_int, c_int, ctypes.c_double, i64, i64, i64, i64, ctypes.POINTER(sz)]
         lib.pw_mmd2.argtypes = [c_int, c_int, ctypes.c_double, vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, c_int,
                                 vp, vp, sz, vp]
+        lib.pw_mmd2_backward_workspace_size.argtypes = [c_int, c_int, ctypes.c_double, i64, i64, i64,
+                                                        ctypes.POINTER(sz)]
+        lib.pw_mmd2_backward.argtypes = [c_int, c_int, ctypes.c_double, vp, i64, i64, i64, vp, i64, i64, i64, i64,
+                                         i64, c_int, vp, vp, i64, vp, i64, vp, sz, vp]
         lib.pw_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
         lib.pw_backward_workspace_size.argtypes = [vp, c_int, i64, c_int, ctypes.POINTER(sz)]
         lib.pw_backward_plan_describe.argtypes = [vp, c_int, i64, c_int, ctypes.c_char_p, sz]
@@ -873,39 +877,71 @@ def lazy(X, Y=None, metric: str = "linear", gamma: float = 1.0, ops=()):
     return LazyScores(X, Y, metric, gamma, ops)
 
 
-def mmd_statistics(X: torch.Tensor, Y: torch.Tensor, kernel: str = "rbf", gamma: float = 1.0,
-                   unbiased: bool = True) -> torch.Tensor:
-    """Squared maximum mean discrepancy between point clouds (Task Map, MMD
-    row: mmd_statistics(X[None], Y[None], kernel="rbf", gamma=g), unbiased by
-    default; one feature set is one cloud): X [B, n, D] (or [n, D]) against
-    Y [B or 1, m, D] (or [m, D]); returns [B] (a scalar for 2-D inputs).
-    pw_mmd2 does every step on the device."""
-    lib = load_library()
-    vec = X.dim() == 2 and Y.dim() == 2
-    X3 = X[None] if X.dim() == 2 else X
-    Y3 = Y[None] if Y.dim() == 2 else Y
+def _mmd_args(X3, Y3, kernel):
     if X3.dim() != 3 or Y3.dim() != 3 or X3.shape[2] != Y3.shape[2]:
         raise ValueError("clouds must be [B, n, D] and [B or 1, m, D]")
     if X3.dtype not in DTYPES or Y3.dtype != X3.dtype or not X3.is_cuda or Y3.device != X3.device:
         raise ValueError("X and Y must be float32 or float64 tensors on one GPU")
     if kernel not in METRICS:
         raise ValueError("unknown kernel %r" % kernel)
-    if torch.is_grad_enabled() and (X3.requires_grad or Y3.requires_grad):
-        raise NotImplementedError("mmd_statistics has no backward here")
     B = max(X3.shape[0], Y3.shape[0])
     if X3.shape[0] not in (1, B) or Y3.shape[0] not in (1, B):
         raise ValueError("batch sizes %d and %d do not broadcast" % (X3.shape[0], Y3.shape[0]))
-    n, m, D = X3.shape[1], Y3.shape[1], X3.shape[2]
     sx = 0 if X3.shape[0] == 1 else X3.stride(0)
     sy = 0 if Y3.shape[0] == 1 else Y3.stride(0)
-    dt, mt = DTYPES[X3.dtype], METRICS[kernel]
-    nb = ctypes.c_size_t()
-    check(lib.pw_mmd2_workspace_size(dt, mt, float(gamma), n, m, D, B, ctypes.byref(nb)), "pw_mmd2_workspace_size")
-    ws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=X3.device)
-    out = torch.empty(B, dtype=X3.dtype, device=X3.device)
-    check(lib.pw_mmd2(dt, mt, float(gamma), X3.data_ptr(), n, _rows(X3[0], "X"), sx, Y3.data_ptr(), m,
-                      _rows(Y3[0], "Y"), sy, D, B, int(bool(unbiased)), out.data_ptr(), ws.data_ptr(), nb.value,
-                      _stream(X3.device)), "pw_mmd2")
+    return B, X3.shape[1], Y3.shape[1], X3.shape[2], sx, sy, DTYPES[X3.dtype], METRICS[kernel]
+
+
+class _Mmd(torch.autograd.Function):
+    """pw_mmd2 forward; pw_mmd2_backward for the clouds' gradients."""
+
+    @staticmethod
+    def forward(ctx, X3, Y3, kernel, gamma, unbiased):
+        lib = load_library()
+        B, n, m, D, sx, sy, dt, mt = _mmd_args(X3, Y3, kernel)
+        nb = ctypes.c_size_t()
+        check(lib.pw_mmd2_workspace_size(dt, mt, float(gamma), n, m, D, B, ctypes.byref(nb)), "pw_mmd2_workspace_size")
+        ws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=X3.device)
+        out = torch.empty(B, dtype=X3.dtype, device=X3.device)
+        check(lib.pw_mmd2(dt, mt, float(gamma), X3.data_ptr(), n, _rows(X3[0], "X"), sx, Y3.data_ptr(), m,
+                          _rows(Y3[0], "Y"), sy, D, B, int(bool(unbiased)), out.data_ptr(), ws.data_ptr(), nb.value,
+                          _stream(X3.device)), "pw_mmd2")
+        ctx.save_for_backward(X3, Y3)
+        ctx.args = (kernel, float(gamma), bool(unbiased))
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        lib = load_library()
+        X3, Y3 = ctx.saved_tensors
+        kernel, gamma, unbiased = ctx.args
+        B, n, m, D, sx, sy, dt, mt = _mmd_args(X3, Y3, kernel)
+        G = g.to(X3.dtype).contiguous()
+        dX = torch.empty(X3.shape[0], n, D, dtype=X3.dtype, device=X3.device) if ctx.needs_input_grad[0] else None
+        dY = torch.empty(Y3.shape[0], m, D, dtype=X3.dtype, device=X3.device) if ctx.needs_input_grad[1] else None
+        nb = ctypes.c_size_t()
+        check(lib.pw_mmd2_backward_workspace_size(dt, mt, gamma, n, m, D, ctypes.byref(nb)),
+              "pw_mmd2_backward_workspace_size")
+        ws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=X3.device)
+        check(lib.pw_mmd2_backward(dt, mt, gamma, X3.data_ptr(), n, _rows(X3[0], "X"), sx, Y3.data_ptr(), m,
+                                   _rows(Y3[0], "Y"), sy, D, B, int(unbiased), G.data_ptr(),
+                                   None if dX is None else dX.data_ptr(), D, None if dY is None else dY.data_ptr(),
+                                   D, ws.data_ptr(), nb.value, _stream(X3.device)), "pw_mmd2_backward")
+        return dX, dY, None, None, None
+
+
+def mmd_statistics(X: torch.Tensor, Y: torch.Tensor, kernel: str = "rbf", gamma: float = 1.0,
+                   unbiased: bool = True) -> torch.Tensor:
+    """Squared maximum mean discrepancy between point clouds (Task Map, MMD
+    row: mmd_statistics(X[None], Y[None], kernel="rbf", gamma=g), unbiased by
+    default; one feature set is one cloud): X [B, n, D] (or [n, D]) against
+    Y [B or 1, m, D] (or [m, D]); returns [B] (a scalar for 2-D inputs).
+    pw_mmd2 does every step on the device, and pw_mmd2_backward gives the
+    clouds' gradients under autograd."""
+    vec = X.dim() == 2 and Y.dim() == 2
+    X3 = X[None] if X.dim() == 2 else X
+    Y3 = Y[None] if Y.dim() == 2 else Y
+    out = _Mmd.apply(X3, Y3, kernel, gamma, unbiased)
     return out[0] if vec else out
 
 

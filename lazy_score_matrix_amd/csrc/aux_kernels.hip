@@ -156,6 +156,40 @@ hipError_t launch_mmd_finish(int dtype, const void *rxx, const void *ryy, const 
 }
 
 // ---------------------------------------------------------------------------
+// MMD gradient of one cloud for batch element b: the two sides of its
+// within-cloud product (a, a2) and its side of the cross product (c),
+// combined with the statistic's coefficients and scaled by G[b]; written,
+// or added for a cloud shared by the batch.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void mmd_grad_combine_kernel(const T *a, const T *a2, const T *c, int64_t rows,
+                                                               int64_t D, const T *G, int64_t b, double c1, double c2,
+                                                               T *out, int64_t ldo, int accumulate) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * D) return;
+  const int64_t i = t / D, d = t % D;
+  const double v = (double)G[b] * (c1 * ((double)a[t] + (double)a2[t]) - c2 * (double)c[t]);
+  T *o = out + i * ldo + d;
+  *o = accumulate ? (T)((double)*o + v) : (T)v;
+}
+
+hipError_t launch_mmd_grad_combine(int dtype, const void *a, const void *a2, const void *c, int64_t rows, int64_t D,
+                                   const void *G, int64_t b, double c1, double c2, void *out, int64_t ldo,
+                                   bool accumulate, hipStream_t s) {
+  const int64_t n = rows * D;
+  if (n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(mmd_grad_combine_kernel<float>, grid, block, 0, s, (const float *)a, (const float *)a2,
+                       (const float *)c, rows, D, (const float *)G, b, c1, c2, (float *)out, ldo, (int)accumulate);
+  else
+    hipLaunchKernelGGL(mmd_grad_combine_kernel<double>, grid, block, 0, s, (const double *)a, (const double *)a2,
+                       (const double *)c, rows, D, (const double *)G, b, c1, c2, (double *)out, ldo,
+                       (int)accumulate);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Group ranges for the same_group mask: min and max id of each block of
 // `block` consecutive entries (a row block, or a key tile), so the tile
 // kernels can skip pairs of blocks whose ranges are disjoint. One wave per

@@ -1568,3 +1568,138 @@ int pw_mmd2(int dtype, int metric, double gamma, const void *X, int64_t n, int64
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// MMD backward: per batch element, pw_backward of the three products with
+// ones (the unbiased within-cloud ones over the strict upper triangle, whose
+// two sides are the two members of each distinct pair), then one combining
+// kernel per cloud.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Workspace: ones [max(n, m)], six gradient blocks (within X: rows and
+// columns [n][D]; within Y: [m][D] twice; across: X side [n][D], Y side
+// [m][D]), then the largest pw_backward workspace of the three products.
+struct MmdGradLayout {
+  size_t t[6] = {0, 0, 0, 0, 0, 0}, bwd = 0, bwd_bytes = 0, total = 0;
+};
+
+MmdGradLayout mmd_grad_layout(const MmdExprs &ex) {
+  MmdGradLayout L;
+  const pw_expr &x = *ex.xx.e;
+  const size_t es = esize(x.dtype), n = (size_t)x.N, m = (size_t)ex.yy.e->N, D = (size_t)x.D;
+  size_t off = align_up(std::max(n, m) * es);
+  const size_t rows[6] = {n, n, m, m, n, m};
+  for (int q = 0; q < 6; ++q) {
+    L.t[q] = off;
+    off += align_up(rows[q] * D * es);
+  }
+  L.bwd = off;
+  for (const pw_expr *e : {ex.xx.e, ex.yy.e, ex.xy.e})
+    L.bwd_bytes = std::max(L.bwd_bytes, grad_plan(*e, PW_C_MATMUL, 1).total);
+  L.total = off + L.bwd_bytes + kAlign;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pw_mmd2_backward_workspace_size(int dtype, int metric, double gamma, int64_t n, int64_t m, int64_t D,
+                                    size_t *bytes) {
+  if (!bytes) return PW_ERR_INVALID;
+  *bytes = 0;
+  int rc = mmd_check_sizes(n, m, 1, 0);
+  if (rc != PW_OK) return rc;
+  const void *fake = reinterpret_cast<const void *>(kAlign);
+  size_t most = 0;
+  for (bool unbiased : {true, false}) {
+    MmdExprs ex;
+    rc = mmd_bind(dtype, metric, gamma, fake, n, D, 0, fake, m, D, 0, D, 1, unbiased, &ex);
+    if (rc != PW_OK) return rc;
+    most = std::max(most, mmd_grad_layout(ex).total);
+  }
+  *bytes = most;
+  return PW_OK;
+}
+
+int pw_mmd2_backward(int dtype, int metric, double gamma, const void *X, int64_t n, int64_t ldx, int64_t sx,
+                     const void *Y, int64_t m, int64_t ldy, int64_t sy, int64_t D, int64_t B, int unbiased,
+                     const void *G, void *dX, int64_t lddx, void *dY, int64_t lddy, void *ws, size_t ws_bytes,
+                     void *stream) {
+  int rc = mmd_check_sizes(n, m, B, unbiased);
+  if (rc != PW_OK) return rc;
+  if (dtype != PW_F32 && dtype != PW_F64) return PW_ERR_INVALID;
+  const size_t es = esize(dtype);
+  if (sx < 0 || sy < 0) return PW_ERR_INVALID;
+  if (!G || !aligned(G, es)) return PW_ERR_INVALID;
+  if ((dX && (lddx < D || !aligned(dX, es))) || (dY && (lddy < D || !aligned(dY, es)))) return PW_ERR_INVALID;
+  // Validate every argument (and size the work) on element 0 before any
+  // device work.
+  MmdExprs ex0;
+  rc = mmd_bind(dtype, metric, gamma, X, n, ldx, 0, Y, m, ldy, 0, D, 1, unbiased != 0, &ex0);
+  if (rc != PW_OK) return rc;
+  const MmdGradLayout L = mmd_grad_layout(ex0);
+  if (!ws || ws_bytes < L.total) return PW_ERR_WORKSPACE;
+  if (!dX && !dY) return PW_OK;
+  char *base = reinterpret_cast<char *>(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+  hipStream_t s = (hipStream_t)stream;
+  void *ones = base;
+  void *t[6];
+  for (int q = 0; q < 6; ++q) t[q] = base + L.t[q];
+  rc = hip_status(launch_fill(dtype, ones, std::max(n, m), 1, 1, 1.0, s));
+  const double dn = (double)n, dm = (double)m;
+  const double cx = unbiased ? 2.0 / (dn * (dn - 1.0)) : 1.0 / (dn * dn);
+  const double cy = unbiased ? 2.0 / (dm * (dm - 1.0)) : 1.0 / (dm * dm);
+  const double cxy = 2.0 / (dn * dm);
+  pw_grad_in in{};
+  in.G = ones;
+  in.ldg = 1;
+  in.V = ones;
+  in.C = 1;
+  in.ldv = 1;
+  for (int64_t b = 0; b < B && rc == PW_OK; ++b) {
+    const char *Xb = static_cast<const char *>(X) + b * sx * (int64_t)es;
+    const char *Yb = static_cast<const char *>(Y) + b * sy * (int64_t)es;
+    MmdExprs ex;
+    rc = mmd_bind(dtype, metric, gamma, Xb, n, ldx, 0, Yb, m, ldy, 0, D, 1, unbiased != 0, &ex);
+    if (rc != PW_OK) break;
+    pw_grad_out o{};
+    if (dX) {
+      o.dX = t[0];
+      o.lddx = D;
+      o.dY = t[1];
+      o.lddy = D;
+      rc = pw_backward(ex.xx.e, PW_C_MATMUL, &in, &o, base + L.bwd, L.bwd_bytes, stream);
+    }
+    if (rc == PW_OK && dY) {
+      o.dX = t[2];
+      o.lddx = D;
+      o.dY = t[3];
+      o.lddy = D;
+      rc = pw_backward(ex.yy.e, PW_C_MATMUL, &in, &o, base + L.bwd, L.bwd_bytes, stream);
+    }
+    if (rc == PW_OK) {
+      o.dX = dX ? t[4] : nullptr;
+      o.lddx = D;
+      o.dY = dY ? t[5] : nullptr;
+      o.lddy = D;
+      rc = pw_backward(ex.xy.e, PW_C_MATMUL, &in, &o, base + L.bwd, L.bwd_bytes, stream);
+    }
+    if (rc == PW_OK && dX) {
+      const bool shared = sx == 0;
+      char *out = static_cast<char *>(dX) + (shared ? 0 : b * n * lddx * (int64_t)es);
+      rc = hip_status(launch_mmd_grad_combine(dtype, t[0], t[1], t[4], n, D, G, b, cx, cxy, out, lddx,
+                                              shared && b > 0, s));
+    }
+    if (rc == PW_OK && dY) {
+      const bool shared = sy == 0;
+      char *out = static_cast<char *>(dY) + (shared ? 0 : b * m * lddy * (int64_t)es);
+      rc = hip_status(launch_mmd_grad_combine(dtype, t[2], t[3], t[5], m, D, G, b, cy, cxy, out, lddy,
+                                              shared && b > 0, s));
+    }
+  }
+  return rc;
+}
+
+}  // extern "C"

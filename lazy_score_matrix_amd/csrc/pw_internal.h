@@ -323,6 +323,11 @@ hipError_t launch_mean_finish(int dtype, void *out, int64_t N, int64_t B, const 
 // rxy, the sums in double in a fixed order; out [B].
 hipError_t launch_mmd_finish(int dtype, const void *rxx, const void *ryy, const void *rxy, int64_t n, int64_t m,
                              int64_t B, double cx, double cy, double cxy, void *out, hipStream_t s);
+// out[i][d] (= or +=) G[b] * (c1 * (a + a2)[i][d] - c2 * c[i][d]) over a [rows][D]
+// gradient block; a, a2, c dense [rows][D], out [rows][ldo].
+hipError_t launch_mmd_grad_combine(int dtype, const void *a, const void *a2, const void *c, int64_t rows, int64_t D,
+                                   const void *G, int64_t b, double c1, double c2, void *out, int64_t ldo,
+                                   bool accumulate, hipStream_t s);
 // Row norms |x_i|^2, or with `inverse` 1/|x_i| (0 for a zero row).
 // With n_batch > 1, element b reads X + b * x_bstride and writes out +
 // b * out_bstride (bytes).

@@ -492,9 +492,11 @@ def mmd2_grad(X, Y, metric="rbf", gamma=1.0, unbiased=True, G=1.0):
     g = float(G)
 
     def pieces(A, B, ops, coef):
+        # The backward of the product with unit upstream gradients, scaled.
         e = Expr(A, B, metric, gamma=gamma, ops=ops)
-        r = backward(e, "matmul", np.full((A.shape[0], 1), coef), np.ones((B.shape[0], 1)))
-        return r["dX"], r["dY"]
+        r = backward(e, "matmul", np.ones((A.shape[0], 1), e.np_dtype), np.ones((B.shape[0], 1), e.np_dtype))
+        c = e.real(coef)
+        return (r["dX"][0] * c, r["dX"][1] * abs(c)), (r["dY"][0] * c, r["dY"][1] * abs(c))
 
     def within(A, k):
         if unbiased:

@@ -147,6 +147,20 @@ def check_consumer(e, oe, consumer, V=None, exclude_self=False, k=0, largest=Fal
                                    rows=rows, cols=None if rows is None else p.get("cols", rows), report=report,
                                    what=what)
         return (ok, ratio) if report else (ratio, 0.0)
+    if consumer == "mmd":
+        # One statistic for the whole pair of clouds: the oracle's, from
+        # its dense scores (row samples do not apply).
+        import lazy_score_matrix_amd as pw
+        from parity import value_report
+        unbiased = dict(params or {}).get("unbiased", True)
+        g = pw.mmd_statistics(e.X, e.Y, e.metric, e.gamma, unbiased).cpu().numpy()
+        o, mag = oracle.mmd2(oe.X, oe.Y, oe.metric, oe.gamma, unbiased)
+        ok, ratio, rel = value_report(np.atleast_1d(g), np.atleast_1d(o), np.atleast_1d(mag), dtype,
+                                      n_terms=oe.N * oe.M)
+        if report:
+            return ok, ratio
+        assert ok, (what, "worst err/tol", ratio)
+        return ratio, rel
     if consumer == "cg_solve":
         p = dict(params or {})
         A, info = e.solve(to_dev(V), p["shift"], rtol=p["rtol"], max_iter=p.get("max_iter", 1000))

@@ -431,3 +431,24 @@ def test_mmd_validation_and_workspace(lib):
         sizes.append(n.value)
         assert n.value >= 4 * (2 * (2048 + m + 2048))
         assert n.value < 2048 * m
+
+
+def test_mmd_backward_validation(lib):
+    """pw_mmd2_backward rejects what pw_mmd2 rejects, and a missing G or an
+    output stride below D, before any device work; asking for neither
+    gradient is a no-op."""
+    n = ctypes.c_size_t()
+    assert lib.pw_mmd2_backward_workspace_size(0, 2, 1.0, 100, 80, 3, ctypes.byref(n)) == pw.PW_OK and n.value > 0
+    assert lib.pw_mmd2_backward_workspace_size(0, 2, 1.0, 100, 80, 3, None) == pw.PW_ERR_INVALID
+    args = lambda **kw: [kw.get(k, v) for k, v in (("dtype", 0), ("metric", 2), ("gamma", 1.0), ("X", FAKE), ("n", 100),
+                         ("ldx", 3), ("sx", 300), ("Y", FAKE), ("m", 80), ("ldy", 3), ("sy", 240), ("D", 3), ("B", 2),
+                         ("unbiased", 1), ("G", FAKE), ("dX", FAKE), ("lddx", 3), ("dY", FAKE), ("lddy", 3),
+                         ("ws", FAKE), ("wsb", 1 << 30), ("s", None))]
+    assert lib.pw_mmd2_backward(*args(n=1)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_backward(*args(G=0)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_backward(*args(lddx=2)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_backward(*args(lddy=2)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_backward(*args(sy=-1)) == pw.PW_ERR_INVALID
+    assert lib.pw_mmd2_backward(*args(D=65, ldx=65, ldy=65, lddx=65, lddy=65)) == pw.PW_ERR_UNSUPPORTED
+    assert lib.pw_mmd2_backward(*args(ws=0)) == pw.PW_ERR_WORKSPACE
+    assert lib.pw_mmd2_backward(*args(dX=0, dY=0)) == pw.PW_OK

@@ -72,3 +72,45 @@ def test_mmd_large_clouds():
     got = pw.mmd_statistics(to_dev(X), to_dev(Y), "rbf", 1.0 / 32).cpu().numpy()
     want, mag = oracle.mmd2(X, Y, "rbf", 1.0 / 32)
     assert_values(got, want, mag, np.float32, n_terms=4000 * 3500, what="large mmd")
+
+
+GRAD = [(k, d, dt, u) for k in ("rbf", "linear", "sqeuclidean") for d in (3, 20)
+        for dt in (np.float32, np.float64) for u in (True, False)]
+
+
+@pytest.mark.parametrize("kernel,D,dtype,unbiased", GRAD,
+                         ids=["%s-D%d-%s-%s" % (k, d, np.dtype(t).name, "u" if u else "b") for k, d, t, u in GRAD])
+def test_mmd_gradients_against_oracle(kernel, D, dtype, unbiased):
+    """Autograd through mmd_statistics (pw_mmd2_backward) against the
+    oracle's chain-rule gradient, per batch element and for a cloud shared
+    by the batch (its gradient summed over the elements)."""
+    import lazy_score_matrix_amd as pw
+    from parity import grad_rule
+    r = np.random.default_rng(700 + D)
+    X = r.standard_normal((2, 130, D)).astype(dtype)
+    Y = (0.2 + r.standard_normal((1, 110, D))).astype(dtype)
+    G = np.array([0.7, -1.3])
+    g = 0.5 / D
+    Xt, Yt = to_dev(X).requires_grad_(True), to_dev(Y).requires_grad_(True)
+    out = pw.mmd_statistics(Xt, Yt, kernel, g, unbiased)
+    dX, dY = torch.autograd.grad((out * torch.as_tensor(G, dtype=out.dtype, device=out.device)).sum(), [Xt, Yt])
+    (ox, oxm), (oy, oym) = oracle.mmd2_grad(X, Y, kernel, g, unbiased, G)
+    for got, want, mag, what in ((dX, ox, oxm, "dX"), (dY, oy, oym, "dY")):
+        ok, ratio, rel = grad_rule(got.detach().cpu().numpy(), want, mag, dtype)
+        print("GRAD mmd %s D%d %s %s worst_err_over_tol=%.3g" % (kernel, D, np.dtype(dtype).name, what, ratio))
+        assert ok, "%s: worst |gpu - oracle| / tol = %.3g" % (what, ratio)
+
+
+def test_mmd_gradient_of_plain_inputs():
+    """2-D clouds under autograd: gradients keep the inputs' shapes."""
+    import lazy_score_matrix_amd as pw
+    from parity import grad_rule
+    r = np.random.default_rng(710)
+    X, Y = r.standard_normal((90, 4)), r.standard_normal((70, 4))
+    Xt, Yt = to_dev(X).requires_grad_(True), to_dev(Y).requires_grad_(True)
+    out = pw.mmd_statistics(Xt, Yt, "rbf", 0.4)
+    out.backward()
+    (ox, oxm), (oy, oym) = oracle.mmd2_grad(X, Y, "rbf", 0.4, True, 1.0)
+    assert Xt.grad.shape == Xt.shape and Yt.grad.shape == Yt.shape
+    assert grad_rule(Xt.grad.cpu().numpy(), ox, oxm, np.float64)[0]
+    assert grad_rule(Yt.grad.cpu().numpy(), oy, oym, np.float64)[0]

@@ -31,7 +31,7 @@ def test_full_size_workload(name):
 
 
 def _plan_args(c, V):
-    if c.consumer in ("mean", "cg_solve"):
+    if c.consumer in ("mean", "cg_solve", "mmd"):
         return "matmul", 1, 0
     if c.consumer.startswith("backward_"):
         return c.consumer[len("backward_"):], V.shape[1] if V is not None else 0, c.k

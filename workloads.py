@@ -41,7 +41,7 @@ def _randn(g, *shape):
 class Case:
     """One consumer call on a workload."""
     name: str
-    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk | mean | cg_solve
+    consumer: str            # matmul | displacement | logsumexp | softmax_matmul | topk | mean | cg_solve | mmd
     #                          | backward_<consumer>
     x: str                   # array used as X
     y: str                   # array used as Y
@@ -54,7 +54,7 @@ class Case:
     largest: bool = False
     transpose: bool = False  # reduce over rows instead (the transposed score)
     pairs: int | None = None  # pairs the masks keep (None: all N * M)
-    params: dict = field(default_factory=dict)  # consumer settings (cg_solve: shift, rtol, max_iter)
+    params: dict = field(default_factory=dict)  # consumer settings (cg_solve: shift, rtol, max_iter; mmd: unbiased)
 
 
 def rbf_small(n: int = 1024, m: int | None = None, d: int = 3, seed: int = 1001):
@@ -263,6 +263,22 @@ def kernel_ridge(n: int = 65536, d: int = 16, seed: int = 1012):
     return arrays, cases
 
 
+def mmd(n: int = 16384, m: int | None = None, d: int = 16, seed: int = 1016):
+    """Two-sample test statistic, float32 (Task Map, MMD row:
+    mmd_statistics(X[None], Y[None], kernel="rbf", gamma=g), unbiased by
+    default): X ~ N(0, I) [n, 16] and Y ~ N(0.1, I) [m, 16], one cloud each;
+    rbf gamma = 1/32. Its pairs are the n(n-1)/2 + m(m-1)/2 distinct
+    within-cloud pairs and the n m cross pairs."""
+    m = n if m is None else m
+    g = _gen(seed)
+    X = _randn(g, n, d)
+    Y = 0.1 + _randn(g, m, d)
+    arrays = {"X": X.to(torch.float32).numpy(), "Y": Y.to(torch.float32).numpy()}
+    pairs = n * (n - 1) // 2 + m * (m - 1) // 2 + n * m
+    cases = [Case("mmd", "mmd", "X", "Y", "rbf", gamma=1.0 / 32, pairs=pairs, params={"unbiased": True})]
+    return arrays, cases
+
+
 def resolve(arg, arrays):
     """An op argument with array names replaced by the arrays."""
     if isinstance(arg, str):
@@ -289,6 +305,7 @@ WORKLOADS = {
     "kernel_ridge": (kernel_ridge, {}, {"n": 900}),
     "attention_backward": (attention_backward, {}, {"n": 700}),
     "attention_causal_backward": (attention_causal_backward, {}, {"n": 700}),
+    "mmd": (mmd, {}, {"n": 600, "m": 500}),
 }
 
 

@@ -270,6 +270,57 @@ hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, in
 }
 
 // ---------------------------------------------------------------------------
+// Pair order of a masked launch: each row block's tile count as the paired
+// launch deals it (band and span reach), sorted heaviest first with one
+// workgroup's bitonic network in LDS (keys (~count, index), so ties keep
+// index order and the order is deterministic). Pairing the i-th heaviest
+// with the i-th lightest evens out pair totals that a sawtooth of packed
+// sequences leaves uneven when blocks pair by index.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pair_order_kernel(const MaskArgs m, int64_t N, int64_t M, int bm, int bn,
+                                                         int n_rb, int P, int *__restrict__ order) {
+  __shared__ unsigned long long key[kMaxOrderedBlocks];
+  for (int r = threadIdx.x; r < P; r += 256) {
+    unsigned long long k = ~0ull;
+    if (r < n_rb) {
+      const int64_t r0 = (int64_t)r * bm, r1 = min(N, r0 + bm) - 1;
+      int64_t f, l;
+      band_range(m, r, r0, r1, 0, M, bn, &f, &l);
+      const int64_t t = l > f ? (l - f + bn - 1) / bn : 0;
+      k = ((unsigned long long)(0xffffffffu - (uint32_t)min(t, (int64_t)0xffffffff)) << 32) | (uint32_t)r;
+    }
+    key[r] = k;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < P; i += 256) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const unsigned long long a = key[i], b = key[j];
+          if (up ? (b < a) : (a < b)) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = threadIdx.x; r < n_rb; r += 256) order[r] = (int)(uint32_t)key[r];
+}
+
+hipError_t launch_pair_order(const MaskArgs &m, int64_t N, int64_t M, int bm, int bn, int n_rb, int *order,
+                             hipStream_t s) {
+  if (n_rb <= 0 || n_rb > kMaxOrderedBlocks) return hipErrorInvalidValue;
+  int P = 1;
+  while (P < n_rb) P <<= 1;
+  hipLaunchKernelGGL(pair_order_kernel, dim3(1), dim3(256), 0, s, m, N, M, bm, bn, n_rb, P, order);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Row norms |x_i|^2 for the kernels that evaluate distances through the
 // expansion |x|^2 + |y|^2 - 2 x.y. L consecutive lanes share a row and read
 // consecutive features, so a wave reads whole rows contiguously; the L

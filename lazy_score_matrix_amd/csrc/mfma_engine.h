@@ -263,19 +263,24 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   // L2.
   const int nblk = gridDim.x;
   const int bid = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int rb_first = __builtin_amdgcn_readfirstlane(bid % rb_slots);
+  const int slot = __builtin_amdgcn_readfirstlane(bid % rb_slots);
   const int sp = __builtin_amdgcn_readfirstlane(bid / rb_slots);
   const bool paired = MASKED && a.rb_pairs;
-  const int npass = (paired && a.n_rb - 1 - rb_first != rb_first) ? 2 : 1;
+  // The slot's row blocks: by index, or by the pair order (heaviest with
+  // lightest) when the launch has one.
+  const int rb_first = (paired && a.rb_order) ? __builtin_amdgcn_readfirstlane(a.rb_order[slot]) : slot;
+  const int rb_second = paired ? ((a.rb_order) ? __builtin_amdgcn_readfirstlane(a.rb_order[a.n_rb - 1 - slot])
+                                               : a.n_rb - 1 - slot)
+                               : slot;
+  const int npass = (paired && rb_second != rb_first) ? 2 : 1;
   // Paired launches deal the pair's tiles (those of the first row block,
   // then those of the second, each within its band reach) out to the
   // splits in equal runs, so every workgroup gets the same number of tiles.
   int64_t pf[2] = {0, 0}, pl[2] = {0, 0}, pt[2] = {0, 0}, v0 = 0, v1 = 0;
   if (paired) {
     for (int p = 0; p < npass; ++p) {
-      const int64_t q0 = (int64_t)(p ? a.n_rb - 1 - rb_first : rb_first) * BM;
-      band_range(a.mask, p ? a.n_rb - 1 - rb_first : rb_first, q0, min(a.N, q0 + BM) - 1, 0, a.M, BN, &pf[p],
-                 &pl[p]);
+      const int64_t q0 = (int64_t)(p ? rb_second : rb_first) * BM;
+      band_range(a.mask, p ? rb_second : rb_first, q0, min(a.N, q0 + BM) - 1, 0, a.M, BN, &pf[p], &pl[p]);
       pt[p] = pl[p] > pf[p] ? (pl[p] - pf[p] + BN - 1) / BN : 0;
     }
     const int64_t tt = pt[0] + pt[1];
@@ -284,7 +289,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   }
   for (int pass = 0; pass < npass; ++pass) {
   if (pass) __syncthreads();  // the previous row block's last LDS reads
-  const int rb = pass ? a.n_rb - 1 - rb_first : rb_first;
+  const int rb = pass ? rb_second : rb_first;
   const int64_t row0 = (int64_t)rb * BM;
   const int64_t jb = paired ? 0 : (int64_t)sp * a.split_cols;
   const int64_t je = wave_uniform(paired ? a.M : min(a.M, jb + a.split_cols));

@@ -180,6 +180,8 @@ struct Plan {
   MfmaConfig mcfg{16, 32, 16};
   int bm = kValuBM, bn = kValuBN;
   int rb_pairs = 0;
+  bool order = false;  // pair the row blocks by their dealt tiles (heaviest with lightest)
+  size_t off_order = 0;
   size_t off_grp = 0;  // group ranges: rows [n_rb][2], then key tiles [ceil(M / bn)][2]
   size_t off_span = 0;  // kept-tile spans per row block [n_rb][2]
   int n_rb = 0, n_split = 1;
@@ -333,6 +335,13 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
   if (e.grow) {
     p.off_span = off;
     off += align_up((size_t)p.n_rb * 2 * sizeof(int64_t));
+  }
+  // With groups the blocks' tile counts follow the groups (a sawtooth for
+  // packed sequences): pair them by count, not by index.
+  p.order = p.rb_pairs && e.grow && p.n_rb <= kMaxOrderedBlocks;
+  if (p.order) {
+    p.off_order = off;
+    off += align_up((size_t)p.n_rb * sizeof(int));
   }
   // Partials: one per column split, and for MFMA top-k one per split and
   // lane group.
@@ -528,6 +537,11 @@ int prepare_masks(const pw_expr &e, const Plan &p, char *base, TileArgs &a, hipS
     int64_t *span = reinterpret_cast<int64_t *>(base + p.off_span);
     rc = hip_status(launch_tile_spans(m, e.N, e.M, p.bm, p.bn, p.n_rb, span, s));
     m.span = span;  // the spans pass itself runs without them
+  }
+  if (rc == PW_OK && p.order) {
+    int *order = reinterpret_cast<int *>(base + p.off_order);
+    rc = hip_status(launch_pair_order(m, e.N, e.M, p.bm, p.bn, p.n_rb, order, s));
+    a.rb_order = order;
   }
   return rc;
 }

@@ -121,6 +121,9 @@ struct TileArgs {
   int n_rb;              // row blocks
   int rb_pairs;          // MFMA masked launches: workgroups per split that each take
                          // row blocks r and n_rb - 1 - r (0: one row block each)
+  const int *rb_order;   // with rb_pairs: row blocks by kept tiles, heaviest first, so
+                         // pair slot r takes rb_order[r] and rb_order[n_rb - 1 - r]
+                         // (null: by index)
   int n_split;           // column splits
   int64_t split_cols;    // columns per split (multiple of the tile width)
   void *partial;         // workspace partials when n_split > 1
@@ -312,6 +315,11 @@ hipError_t launch_group_ranges(const int64_t *g, int64_t n, int block, int64_t *
 // Per row block of bm rows: the column span [first, end) of the key tiles of
 // bn columns that the pair masks do not skip ([0, 0) when none).
 hipError_t launch_tile_spans(const MaskArgs &m, int64_t N, int64_t M, int bm, int bn, int n_rb, int64_t *out,
+                             hipStream_t s);
+// Row blocks ordered by the key tiles a paired launch deals them (their band
+// and span reach), heaviest first, ties by index; n_rb <= kMaxOrderedBlocks.
+constexpr int kMaxOrderedBlocks = 4096;
+hipError_t launch_pair_order(const MaskArgs &m, int64_t N, int64_t M, int bm, int bn, int n_rb, int *order,
                              hipStream_t s);
 hipError_t launch_fill(int dtype, void *out, int64_t rows, int64_t cols, int64_t ld, double value, hipStream_t s);
 // out[b][i] /= kept count of row i (cnt[i], or M when cnt is null); NaN for a

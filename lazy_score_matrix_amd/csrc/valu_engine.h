@@ -170,6 +170,47 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
   }
   T thr = __builtin_huge_val();
   uint32_t best_j = ~0u;
+  // k > 1: candidates below the threshold (as it stood when they were met)
+  // are queued in LDS, one column of slots per lane, and the whole wave
+  // inserts them together once some lane's queue could overflow, and at the
+  // end. An insertion then runs once per queued candidate of the wave's
+  // fullest lane, instead of once for every column at which any lane had a
+  // candidate. A candidate enters only if still below the threshold when
+  // its turn comes; queues keep column order, so ties still go to the
+  // lower index.
+  constexpr bool QUEUE = CONS == C_TOPK && KL > 1;
+  constexpr int QCAP = QUEUE ? (sizeof(T) == 4 ? 16 : 12) : 1;
+  static_assert(!QUEUE || QCAP >= G, "a group's candidates must fit a drained queue");
+  __shared__ T sQv[QCAP][BM];
+  __shared__ uint32_t sQj[QCAP][BM];
+  int qn = 0;
+  auto list_insert = [&](T sv, uint32_t jc) {
+    // The new column comes after every listed one, so it goes behind the
+    // values it equals: slot p takes slot p - 1 where the new value lands
+    // before that, the new value where it lands between the two, and
+    // otherwise stays.
+    bool below = true;  // sv < lv[KL - 1], as the caller checked
+#pragma unroll
+    for (int p = KL - 1; p > 0; --p) {
+      const bool below_prev = sv < lv[p - 1];
+      lv[p] = below_prev ? lv[p - 1] : (below ? sv : lv[p]);
+      lj[p] = below_prev ? lj[p - 1] : (below ? jc : lj[p]);
+      below = below_prev;
+    }
+    lv[0] = below ? sv : lv[0];
+    lj[0] = below ? jc : lj[0];
+    thr = lv[KL - 1];
+  };
+  // Wave-uniform: every lane inserts its queued candidates in order.
+  auto drain = [&]() {
+    for (int q = 0; __any(q < qn); ++q) {
+      if (q < qn) {
+        const T v = sQv[q][tid];
+        if (v < thr) list_insert(v, sQj[q][tid]);
+      }
+    }
+    qn = 0;
+  };
 
   for (int64_t j0 = jfirst; j0 < jlast; j0 += BN) {
     const int nb = (int)min((int64_t)BN, je - j0);
@@ -343,23 +384,33 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
             thr = lt ? sv : thr;
             bl = lt ? jj : bl;
           } else {
-            if (sv < thr) {
-              // The new column comes after every listed one, so it goes
-              // behind the values it equals: slot p takes slot p - 1 where
-              // the new value lands before that, the new value where it
-              // lands between the two, and otherwise stays.
-              const uint32_t jc = (uint32_t)(j0 + jj);
-              bool below = true;  // sv < lv[KL - 1], as the threshold said
-#pragma unroll
-              for (int p = KL - 1; p > 0; --p) {
-                const bool below_prev = sv < lv[p - 1];
-                lv[p] = below_prev ? lv[p - 1] : (below ? sv : lv[p]);
-                lj[p] = below_prev ? lj[p - 1] : (below ? jc : lj[p]);
-                below = below_prev;
+            // One column: drain first if some lane's queue is full.
+            const bool hit = sv < thr;
+            if (__any(hit)) {
+              if (__any(qn == QCAP)) drain();
+              if (hit && sv < thr) {
+                sQv[qn][tid] = sv;
+                sQj[qn][tid] = (uint32_t)(j0 + jj);
+                ++qn;
               }
-              lv[0] = below ? sv : lv[0];
-              lj[0] = below ? jc : lj[0];
-              thr = lv[KL - 1];
+            }
+          }
+        };
+        // A group of G columns whose smallest value is below the threshold:
+        // drain first if some lane could not queue the whole group.
+        auto fold_group = [&](int g, const T (&sv)[G], T lo) {
+          const bool hit = lo < thr;
+          if (__any(hit)) {
+            if (__any(qn > QCAP - G)) drain();
+            if (hit) {
+#pragma unroll
+              for (int u = 0; u < G; ++u) {
+                if (sv[u] < thr) {
+                  sQv[qn][tid] = sv[u];
+                  sQj[qn][tid] = (uint32_t)(j0 + g + u);
+                  ++qn;
+                }
+              }
             }
           }
         };
@@ -394,10 +445,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
                 sv[u] = (PLAIN || g + u < n) ? score(g + u) : (T)__builtin_huge_val();
                 lo = min(lo, sv[u]);
               }
-              if (lo < thr) {
-#pragma unroll
-                for (int u = 0; u < G; ++u) fold_topk(g + u, sv[u]);
-              }
+              fold_group(g, sv, lo);
             }
           }
         };
@@ -439,6 +487,7 @@ __global__ __launch_bounds__(kValuBM) void valu_tile(const TileArgs a) {
       sweep(Bool<false>{});
     }
   }
+  if constexpr (QUEUE) drain();
   if (!rv) return;
   if (fast2 && m != neg_inf<T>()) m *= (T)kLn2;  // back to natural units
   if (!rkeep) {  // a masked row: the empty-row result

@@ -402,7 +402,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     if args.also is None:

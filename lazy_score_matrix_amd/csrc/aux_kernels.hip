@@ -112,40 +112,67 @@ hipError_t launch_mean_finish(int dtype, void *out, int64_t N, int64_t B, const 
 }
 
 // ---------------------------------------------------------------------------
-// Squared MMD from three row-sum vectors, one workgroup per batch element:
-// each thread adds a strided share of every vector in double, then a fixed
-// LDS tree adds the threads' shares.
+// Squared MMD from three row-sum vectors, one workgroup of 1024 threads per
+// batch element: each thread keeps four independent double sums per vector
+// (so four loads per vector are in flight, not one), the wave adds its lanes
+// by butterfly, and the first wave adds the 16 waves' shares. The order is
+// fixed for a given size, so the result is reproducible.
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(256) void mmd_finish_kernel(const T *rxx, const T *ryy, const T *rxy, int64_t n,
-                                                         int64_t m, double cx, double cy, double cxy, T *out) {
-  __shared__ double part[3][256];
-  const int64_t b = blockIdx.x;
-  const int tid = threadIdx.x;
-  double sx = 0.0, sy = 0.0, sxy = 0.0;
-  for (int64_t i = tid; i < n; i += 256) {
-    sx += (double)rxx[b * n + i];
-    sxy += (double)rxy[b * n + i];
-  }
-  for (int64_t j = tid; j < m; j += 256) sy += (double)ryy[b * m + j];
-  part[0][tid] = sx;
-  part[1][tid] = sy;
-  part[2][tid] = sxy;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) {
+constexpr int kMmdFinishThreads = 1024;
+
+__device__ inline double wave_sum_f64(double v) {
 #pragma unroll
-      for (int q = 0; q < 3; ++q) part[q][tid] += part[q][tid + w];
-    }
-    __syncthreads();
+  for (int sh = 32; sh >= 1; sh >>= 1) v += __shfl_xor(v, sh, 64);
+  return v;
+}
+
+template <class T>
+__device__ inline double strided_sum(const T *p, int64_t n, int tid) {
+  constexpr int S = kMmdFinishThreads;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int64_t i = tid;
+  for (; i + 3 * S < n; i += 4 * S) {
+    s0 += (double)p[i];
+    s1 += (double)p[i + S];
+    s2 += (double)p[i + 2 * S];
+    s3 += (double)p[i + 3 * S];
   }
-  if (tid == 0) out[b] = (T)(cx * part[0][0] + cy * part[1][0] - cxy * part[2][0]);
+  for (; i < n; i += S) s0 += (double)p[i];
+  return (s0 + s1) + (s2 + s3);
+}
+
+template <class T>
+__global__ __launch_bounds__(kMmdFinishThreads) void mmd_finish_kernel(const T *rxx, const T *ryy, const T *rxy,
+                                                                       int64_t n, int64_t m, double cx, double cy,
+                                                                       double cxy, T *out) {
+  constexpr int W = kMmdFinishThreads / 64;
+  __shared__ double part[3][W];
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double sx = wave_sum_f64(strided_sum(rxx + b * n, n, tid));
+  double sxy = wave_sum_f64(strided_sum(rxy + b * n, n, tid));
+  double sy = wave_sum_f64(strided_sum(ryy + b * m, m, tid));
+  if (lane == 0) {
+    part[0][wave] = sx;
+    part[1][wave] = sy;
+    part[2][wave] = sxy;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    sx = lane < W ? part[0][lane] : 0.0;
+    sy = lane < W ? part[1][lane] : 0.0;
+    sxy = lane < W ? part[2][lane] : 0.0;
+    sx = wave_sum_f64(sx);
+    sy = wave_sum_f64(sy);
+    sxy = wave_sum_f64(sxy);
+    if (lane == 0) out[b] = (T)(cx * sx + cy * sy - cxy * sxy);
+  }
 }
 
 hipError_t launch_mmd_finish(int dtype, const void *rxx, const void *ryy, const void *rxy, int64_t n, int64_t m,
                              int64_t B, double cx, double cy, double cxy, void *out, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  dim3 grid((unsigned)B), block(256);
+  dim3 grid((unsigned)B), block(kMmdFinishThreads);
   if (dtype == 0)
     hipLaunchKernelGGL(mmd_finish_kernel<float>, grid, block, 0, s, (const float *)rxx, (const float *)ryy,
                        (const float *)rxy, n, m, cx, cy, cxy, (float *)out);

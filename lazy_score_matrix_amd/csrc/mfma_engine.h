@@ -371,6 +371,23 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   T wsum[QB][4];  // NARROW: four partial sums per row
   Key<T> list[QB][KLQ];
   T thr[QB];
+  // Float top-k queues each lane's candidates (keys below the threshold as
+  // it stood when they were met) in LDS and inserts them wave-wide later, so
+  // one insertion serves every lane that has a candidate rather than one
+  // lane at a time. Queues are per lane and in column order, and a queued
+  // key enters only if still below the list's last value, so the result is
+  // the same as inserting at once. The capacity is what the LDS left at this
+  // kernel's occupancy allows; without room for a sub-block's candidates
+  // and four more the kernel inserts at once.
+  constexpr int kLdsPerCu = 160 * 1024;
+  constexpr int LDS_USED = (int)sizeof(T) * (2 * BN * (DP + KPAD) + 2 * BN + 2 * (HAS_V ? BN : 1) * VW) +
+                           (4 + 8) * 2 * MBN + (TABLE_EXP ? 2048 : 8) + 4 * (MASKED ? SB * QB * NT : 1);
+  constexpr int QROOM = (kLdsPerCu / mfma_wgs_per_cu(sizeof(T) == 4 ? 0 : 1, CONS, DP, CP, KL) - LDS_USED - 1024) /
+                        (NT * 8);
+  constexpr int QCAP = QROOM < 32 ? QROOM : 32;
+  constexpr bool QUEUE = CONS == C_TOPK && sizeof(T) == 4 && QB == 1 && QCAP >= NREG + 4;
+  __shared__ uint64_t sQ[QUEUE ? QCAP : 1][QUEUE ? NT : 1];
+  int qn = 0;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     thr[b] = __builtin_huge_valf();
@@ -479,6 +496,22 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         for (int r = 0; r < NREG; ++r) v[b][r] = F::exp2(fmin(fma(s[b][r], rbf_c, rbf_t[b]), (T)0));
     }
   };
+  // Insert every lane's queued candidates, oldest first; the trip count is
+  // the longest queue of the wave.
+  auto drain = [&]() __attribute__((always_inline)) {
+    if constexpr (QUEUE) {
+      for (int t = 0; __any(t < qn); ++t) {
+        if (t < qn) {
+          const Key<T> c{sQ[t][tid]};
+          if ((uint32_t)(c.k >> 32) < (uint32_t)(list[0][KLQ - 1].k >> 32)) {
+            key_insert_after<KLQ>(list[0], c);
+            thr[0] = key_threshold(list[0][KLQ - 1]);
+          }
+        }
+      }
+      qn = 0;
+    }
+  };
   auto consume = [&](int kb, int nb, int64_t j0, bool diag, bool check_, acc_t (&s)[QB], auto pl) __attribute__((always_inline)) {
     constexpr bool PL = decltype(pl)::value;
     const bool check = MASKED && check_;
@@ -531,19 +564,44 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         }
       }
       if (__any(any)) {
+        if constexpr (QUEUE) {
+          // A lane with a candidate may queue up to NREG keys: make room.
+          if (__any(any && qn > QCAP - NREG)) drain();
+          // A plain search compares n + u before the clamp at 0 (a clamped
+          // value below the threshold implies it); the queued key carries
+          // the clamped value, and the drain compares that. Only a ragged
+          // sub-block checks the column range.
+          auto push = [&](auto ragged) __attribute__((always_inline)) {
 #pragma unroll
-        for (int b = 0; b < QB; ++b)
-#pragma unroll
-          for (int r = 0; r < NREG; ++r) {
-            const int key = kb + F::key_of(r, g);
-            T x = s[b][r];
-            if (DIST && PL) x = max(nx[b] + x, (T)0);
-            const T sv = (!PL && a.largest) ? -x : x;
-            if (key < nb && sv < thr[b]) {
-              key_insert_after<KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), PL ? 0 : a.largest));
-              thr[b] = key_threshold(list[b][KLQ - 1]);
+            for (int r = 0; r < NREG; ++r) {
+              const int key = kb + F::key_of(r, g);
+              T x = s[0][r];
+              if (DIST && PL) x = nx[0] + x;
+              const T sv = (!PL && a.largest) ? -x : x;
+              if ((!decltype(ragged)::value || key < nb) && sv < thr[0]) {
+                if (DIST && PL) x = max(x, (T)0);
+                sQ[qn][tid] = Key<T>::make(x, (uint32_t)(j0 + key), PL ? 0 : a.largest).k;
+                ++qn;
+              }
             }
-          }
+          };
+          if (tail) push(Bool<true>());
+          else push(Bool<false>());
+        } else {
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int r = 0; r < NREG; ++r) {
+              const int key = kb + F::key_of(r, g);
+              T x = s[b][r];
+              if (DIST && PL) x = max(nx[b] + x, (T)0);
+              const T sv = (!PL && a.largest) ? -x : x;
+              if (key < nb && sv < thr[b]) {
+                key_insert_after<KLQ>(list[b], Key<T>::make(x, (uint32_t)(j0 + key), PL ? 0 : a.largest));
+                thr[b] = key_threshold(list[b][KLQ - 1]);
+              }
+            }
+        }
       }
       return;
     }
@@ -786,6 +844,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   } else {
     tile_loop(Bool<false>());
   }
+  drain();
 
   // Rows dropped by the row mask take the empty-row result.
 #pragma unroll

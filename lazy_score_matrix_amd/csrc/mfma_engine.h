@@ -497,12 +497,15 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
     }
   };
   // Insert every lane's queued candidates, oldest first; the trip count is
-  // the longest queue of the wave.
+  // the longest queue of the wave. Each entry is read from LDS one step
+  // ahead, so the read's latency overlaps the previous insertion.
   auto drain = [&]() __attribute__((always_inline)) {
     if constexpr (QUEUE) {
+      uint64_t nk = sQ[0][tid];
       for (int t = 0; __any(t < qn); ++t) {
+        const Key<T> c{nk};
+        if (t + 1 < QCAP) nk = sQ[t + 1][tid];
         if (t < qn) {
-          const Key<T> c{sQ[t][tid]};
           if ((uint32_t)(c.k >> 32) < (uint32_t)(list[0][KLQ - 1].k >> 32)) {
             key_insert_after<KLQ>(list[0], c);
             thr[0] = key_threshold(list[0][KLQ - 1]);

@@ -201,7 +201,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   constexpr int QB = Shape::QB;
   constexpr int BM = Shape::BM;
   constexpr int NT = Shape::NT;
-  constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS, CP);
+  constexpr int BN = mfma_bn(sizeof(T) == 4 ? 0 : 1, CONS, CP, DP);
   constexpr int SB = BN / TM;
   constexpr int DG = DP / G;
   constexpr bool DIST = METRIC == M_SQEUCLIDEAN || METRIC == M_RBF;  // norm expansion

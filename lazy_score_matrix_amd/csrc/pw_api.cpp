@@ -248,7 +248,7 @@ Plan make_plan(const pw_expr &e, int consumer, int64_t C, int k) {
     else p.mcfg.cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
     p.mcfg.kl = consumer == PW_C_TOPK ? (k <= 16 ? 16 : 64) : 1;
     p.bm = mfma_bm(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
-    p.bn = mfma_bn(e.dtype, consumer, p.mcfg.cp);
+    p.bn = mfma_bn(e.dtype, consumer, p.mcfg.cp, p.mcfg.dp);
     p.chunk = (int)std::min<int64_t>(C, p.mcfg.cp);
     target_wgs = (int64_t)cus * mfma_wgs_per_cu(e.dtype, consumer, p.mcfg.dp, p.mcfg.cp, p.mcfg.kl);
   } else {

@@ -198,9 +198,13 @@ constexpr int mfma_bm(int dtype, int consumer, int dp, int cp, int kl) {
 }
 // Keys per staged tile: float 128 (4 sub-blocks of 32) except for the value
 // consumers with a V tile (cp > 1), whose prefetched tile needs the
-// registers (64); double 64.
-constexpr int mfma_bn(int dtype, int consumer, int cp) {
-  return (dtype == 0 && ((consumer != C_MATMUL && consumer != C_SOFTMAX) || cp == 1)) ? 128 : 64;
+// registers, and top-k with more than 32 features, whose candidate queue
+// needs the LDS (64); double 64.
+constexpr int mfma_bn(int dtype, int consumer, int cp, int dp) {
+  return (dtype == 0 && ((consumer != C_MATMUL && consumer != C_SOFTMAX) || cp == 1) &&
+          !(consumer == C_TOPK && dp > 32))
+             ? 128
+             : 64;
 }
 // Lane groups per query in the MFMA layouts (float 2, double 4); each keeps
 // its own top-k list, written as a separate partial.

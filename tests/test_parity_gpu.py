@@ -386,6 +386,52 @@ def test_mfma_topk_far_from_origin(dtype, k):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("k", [10, 16, 40])
+def test_mfma_topk_every_key_enters(dtype, D, k):
+    """References on a ray with norms falling by index: every key is closer
+    to every query (and has a larger dot product) than all keys before it,
+    so each one enters every list and the float engine's candidate queues
+    run full at every sub-block. The k last references win, in reverse
+    order."""
+    r = np.random.default_rng(1400 + D + k)
+    X = (0.05 * r.standard_normal((300, D))).astype(dtype)
+    u = r.standard_normal(D)
+    u /= np.linalg.norm(u)
+    M = 1700
+    Y = ((1000.0 - 0.5 * np.arange(M))[:, None] * u[None, :]).astype(dtype)
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    _assert_family(e, "topk", "mfma", k=k)
+    check_consumer(e, oe, "topk", k=k, what="every key enters, sqeuclidean k=%d" % k)
+    # Dot products rising with the index: queries along u, norms rising.
+    Xu = (u[None, :] + 0.05 * r.standard_normal((300, D))).astype(dtype)
+    Yu = ((100.0 + 0.5 * np.arange(M))[:, None] * u[None, :]).astype(dtype)
+    e, oe = bind_both(Xu, Yu, "linear")
+    check_consumer(e, oe, "topk", k=k, largest=True, what="every key enters, largest linear k=%d" % k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
+@pytest.mark.parametrize("D", [3, 8])
+@pytest.mark.parametrize("k", [2, 8, 16, 40])
+def test_valu_topk_every_key_enters(dtype, D, k):
+    """The vector engine under the same order: every key enters every list,
+    so each thread's queue fills at every group of columns."""
+    r = np.random.default_rng(1500 + D + k)
+    u = r.standard_normal(D)
+    u /= np.linalg.norm(u)
+    M = 1700
+    X = (0.05 * r.standard_normal((300, D))).astype(dtype)
+    Y = ((1000.0 - 0.5 * np.arange(M))[:, None] * u[None, :]).astype(dtype)
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    _assert_family(e, "topk", "valu", k=k)
+    check_consumer(e, oe, "topk", k=k, what="vector engine, every key enters, k=%d" % k)
+    Xu = (u[None, :] + 0.05 * r.standard_normal((300, D))).astype(dtype)
+    Yu = ((100.0 + 0.5 * np.arange(M))[:, None] * u[None, :]).astype(dtype)
+    e, oe = bind_both(Xu, Yu, "linear")
+    check_consumer(e, oe, "topk", k=k, largest=True, what="vector engine, every key enters, largest k=%d" % k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "f64"])
 @pytest.mark.parametrize("N", [129, 300, 1000])
 def test_mfma_exclude_self(dtype, N):
     X, _, r = _data(1300 + N, N, 1, 64, dtype)

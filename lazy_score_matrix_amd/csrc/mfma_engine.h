@@ -127,26 +127,28 @@ struct TileLoader {
   static constexpr int VPR = COLS / VEC;  // vectors per row
   static constexpr int NV = (ROWS * VPR + NT - 1) / NT;
   typedef T vec_t __attribute__((ext_vector_type(VEC)));
+  // Slot v of a thread is row tid / VPR + v * (NT / VPR), column
+  // (tid % VPR) * VEC: one offset per thread and a uniform step, so the
+  // slots need no address register each.
+  static_assert(NT % VPR == 0, "a thread's slots are whole rows apart");
+  static constexpr int RSTEP = NT / VPR;
   vec_t buf[NV];
-  uint32_t off[NV];  // element offset of each slot inside a full tile
-  bool fast;         // offsets fit 32 bits and rows are vector aligned
+  uint32_t off0;  // element offset of the thread's first slot inside a full tile
+  bool fast;      // offsets fit 32 bits and rows are vector aligned
 
   __device__ __forceinline__ void init(int64_t ld, bool vec_ok, int tid) {
     fast = vec_ok && (int64_t)ROWS * ld < (int64_t)1 << 31;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int idx = tid + v * NT;
-      off[v] = (uint32_t)((idx / VPR) * ld + (idx % VPR) * VEC);
-    }
+    off0 = (uint32_t)((tid / VPR) * ld + (tid % VPR) * VEC);
   }
   __device__ __forceinline__ void load(const T *__restrict__ src, int64_t ld, int64_t row0, int nrows, int ncols,
                                        int tid) {
     if (fast && nrows == ROWS && ncols == COLS) {
-      const T *__restrict__ base = src + row0 * ld;
+      const T *__restrict__ base = src + row0 * ld + off0;
+      const uint32_t step = (uint32_t)(RSTEP * ld);
 #pragma unroll
       for (int v = 0; v < NV; ++v)
         if (ROWS * VPR % NT == 0 || tid + v * NT < ROWS * VPR)
-          buf[v] = *reinterpret_cast<const vec_t *>(base + off[v]);
+          buf[v] = *reinterpret_cast<const vec_t *>(base + v * step);
       return;
     }
 #pragma unroll
@@ -162,13 +164,11 @@ struct TileLoader {
   }
   template <int LD>
   __device__ __forceinline__ void store(T (*dst)[LD], int tid) const {
+    T *p = &dst[tid / VPR][(tid % VPR) * VEC];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int idx = tid + v * NT;
-      if (ROWS * VPR % NT == 0 || idx < ROWS * VPR) {
-        const int r = idx / VPR, c = (idx % VPR) * VEC;
-        *reinterpret_cast<vec_t *>(&dst[r][c]) = buf[v];
-      }
+      if (ROWS * VPR % NT == 0 || tid + v * NT < ROWS * VPR)
+        *reinterpret_cast<vec_t *>(p + v * RSTEP * LD) = buf[v];
     }
   }
 };

@@ -629,17 +629,20 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
           for (int r = 0; r < NREG; ++r) v[b][r] = fma(v[b][r], er[b], ep[b]);
         }
       }
-      if (tail) {
+      // The masks below apply to a few sub-blocks only (ragged, diagonal,
+      // checked): marked unlikely, so they stay behind uniform branches
+      // rather than becoming a select on every register of every sub-block.
+      if (__builtin_expect(tail, 0)) {
 #pragma unroll
         for (int r = 0; r < NREG; ++r)
           if (kb + F::key_of(r, g) >= nb) v[b][r] = ONLINE ? kNegInf : (T)0;
       }
-      if (CONS == C_LOGSUMEXP && diag) {
+      if (__builtin_expect(CONS == C_LOGSUMEXP && diag, 0)) {
 #pragma unroll
         for (int r = 0; r < NREG; ++r)
           if (j0 + kb + F::key_of(r, g) == qi[b]) v[b][r] = kNegInf;
       }
-      if (check) {
+      if (__builtin_expect(check, 0)) {
 #pragma unroll
         for (int r = 0; r < NREG; ++r)
           if (!((km[b] >> r) & 1u)) v[b][r] = ONLINE ? kNegInf : (T)0;

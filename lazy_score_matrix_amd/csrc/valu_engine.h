@@ -763,11 +763,42 @@ __device__ __forceinline__ void r2_min_tile(const float (&x)[2][DT], const float
   }
 }
 
+// Three-feature squared distances by the norm expansion with the row's own
+// term left out: a staged column holds (y, |y|^2), a row holds -2x, and
+// three FMAs give u = |y|^2 - 2 x.y. fl(|x|^2 + u) is monotone in u, so the
+// row's extreme u, plus |x|^2 and clamped at 0, is its extreme distance;
+// a tie the final rounding creates is within the pair's rounding error.
+template <bool LARGEST>
+__device__ __forceinline__ void r2_min_tile_exp(const float (&xm)[2][3], const float (*sY)[4], int n,
+                                                float (&thr)[2], int (&bl)[2]) {
+  auto body = [&](int jj) {
+    const float4 y = *reinterpret_cast<const float4 *>(sY[jj]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float sc = fma(xm[u][0], y.x, fma(xm[u][1], y.y, fma(xm[u][2], y.z, y.w)));
+      const float sv = LARGEST ? -sc : sc;
+      const bool lt = sv < thr[u];
+      thr[u] = lt ? sv : thr[u];
+      bl[u] = lt ? jj : bl[u];
+    }
+  };
+  if (n == kValuBN) {
+#pragma unroll 8
+    for (int jj = 0; jj < kValuBN; ++jj) body(jj);
+  } else {
+    for (int jj = 0; jj < n; ++jj) body(jj);
+  }
+}
+
 template <int METRIC, int DT>
 __global__ __launch_bounds__(kValuBM) __attribute__((amdgpu_waves_per_eu(8))) void valu_tile_r2_min(const TileArgs a) {
   const BatchPtrs bp = batch_ptrs(a);
   constexpr int BN = kValuBN, R = 2;
-  __shared__ float sY[BN][DT];
+  // Three-feature squared distances take the expansion (columns staged with
+  // their norms); other shapes and metrics are evaluated directly.
+  constexpr bool EXP = METRIC == M_SQEUCLIDEAN && DT == 3;
+  constexpr int SW = EXP ? 4 : DT;
+  __shared__ __attribute__((aligned(16))) float sY[BN][SW];
   const int tid = threadIdx.x;
   const int rb = blockIdx.x % a.n_rb;
   const int sp = blockIdx.x / a.n_rb;
@@ -778,7 +809,7 @@ __global__ __launch_bounds__(kValuBM) __attribute__((amdgpu_waves_per_eu(8))) vo
   const float neg_gamma = (float)(-a.gamma * kLog2e);
   int64_t i[R];
   bool rv[R];
-  float x[R][DT], thr[R];
+  float x[R][DT], thr[R], nx[R];
   uint32_t bj[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) {
@@ -788,18 +819,39 @@ __global__ __launch_bounds__(kValuBM) __attribute__((amdgpu_waves_per_eu(8))) vo
     for (int d = 0; d < DT; ++d) x[u][d] = (rv[u] && d < a.D) ? ldg<float>(bp.X, i[u] * a.ldx + d) * pre_s : 0.f;
     thr[u] = __builtin_huge_valf();
     bj[u] = ~0u;
+    nx[u] = 0.f;
+    if constexpr (EXP) {
+      nx[u] = fma(x[u][0], x[u][0], fma(x[u][1], x[u][1], x[u][2] * x[u][2]));
+#pragma unroll
+      for (int d = 0; d < DT; ++d) x[u][d] *= -2.f;
+    }
   }
   for (int64_t j0 = jb; j0 < je; j0 += BN) {
     const int nb = (int)min((int64_t)BN, je - j0);
     __syncthreads();
-    for (int e = tid; e < BN * DT; e += kValuBM) {
-      const int jj = e / DT, d = e % DT;
-      sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(bp.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+    if constexpr (EXP) {
+      if (tid < BN) {
+        float y[3];
+#pragma unroll
+        for (int d = 0; d < 3; ++d) y[d] = (tid < nb && d < a.D) ? ldg<float>(bp.Y, (j0 + tid) * a.ldy + d) : 0.f;
+        *reinterpret_cast<float4 *>(sY[tid]) =
+            make_float4(y[0], y[1], y[2], fma(y[0], y[0], fma(y[1], y[1], y[2] * y[2])));
+      }
+    } else {
+      for (int e = tid; e < BN * DT; e += kValuBM) {
+        const int jj = e / DT, d = e % DT;
+        sY[jj][d] = (jj < nb && d < a.D) ? ldg<float>(bp.Y, (j0 + jj) * a.ldy + d) * pre_s : 0.f;
+      }
     }
     __syncthreads();
     int bl[R] = {-1, -1};  // tile slot of each row's best column met in this tile
-    if (a.largest) r2_min_tile<METRIC, DT, true>(x, sY, nb, neg_gamma, thr, bl);
-    else r2_min_tile<METRIC, DT, false>(x, sY, nb, neg_gamma, thr, bl);
+    if constexpr (EXP) {
+      if (a.largest) r2_min_tile_exp<true>(x, sY, nb, thr, bl);
+      else r2_min_tile_exp<false>(x, sY, nb, thr, bl);
+    } else {
+      if (a.largest) r2_min_tile<METRIC, DT, true>(x, sY, nb, neg_gamma, thr, bl);
+      else r2_min_tile<METRIC, DT, false>(x, sY, nb, neg_gamma, thr, bl);
+    }
 #pragma unroll
     for (int u = 0; u < R; ++u)
       if (bl[u] >= 0) bj[u] = (uint32_t)(j0 + bl[u]);
@@ -808,8 +860,9 @@ __global__ __launch_bounds__(kValuBM) __attribute__((amdgpu_waves_per_eu(8))) vo
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     if (!rv[u]) continue;
-    const Key<float> key =
-        bj[u] == ~0u ? Key<float>::sentinel() : Key<float>::make(a.largest ? -thr[u] : thr[u], bj[u], a.largest);
+    float best = a.largest ? -thr[u] : thr[u];
+    if constexpr (EXP) best = max(nx[u] + best, 0.f);
+    const Key<float> key = bj[u] == ~0u ? Key<float>::sentinel() : Key<float>::make(best, bj[u], a.largest);
     if (fin) {
       static_cast<float *>(bp.out)[i[u] * a.k] = key.value(a.largest);
       bp.idx[i[u] * a.k] = key.out_index();

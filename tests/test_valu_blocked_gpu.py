@@ -127,6 +127,22 @@ def test_two_rows_min_exact_ties(D, largest):
     check_consumer(e, oe, "topk", k=1, largest=largest, exact=True, what="two-rows min D%d" % D)
 
 
+@pytest.mark.parametrize("largest", (False, True), ids=("min", "max"))
+def test_two_rows_min_far_points(largest):
+    """Three-feature minima by the norm expansion on clustered points far
+    from the origin (|x|^2 near 7500 against distances near 1), with exact
+    copies among the columns (distance 0): values within the rule's
+    error magnitude, indices wherever the oracle's values are separated."""
+    r = np.random.default_rng(410)
+    X = (50.0 + r.standard_normal((1100, 3))).astype(np.float32)
+    Y = (50.0 + r.standard_normal((1333, 3))).astype(np.float32)
+    Y[600:700] = X[:100]
+    e, oe = bind_both(X, Y, "sqeuclidean")
+    plan = e.plan("topk", 0, 1)
+    assert _field(plan, "family") == "valu" and _field(plan, "rows") == "2", plan
+    check_consumer(e, oe, "topk", k=1, largest=largest, what="two-rows far min")
+
+
 @pytest.mark.parametrize("metric", ("linear", "sqeuclidean"))
 def test_blocked_logsumexp_far_points(metric):
     """Points far from the origin: the norm expansion cancels more there,

@@ -398,6 +398,12 @@ hipError_t launch_row_norms(int dtype, const void *X, int64_t n, int64_t ld, int
 // Merge of n_split column-split partials, always in split order 0..S-1 so
 // results are deterministic for a fixed plan.
 // ---------------------------------------------------------------------------
+// The split merges read the partials kMergeBatch splits at a time, every
+// load of a batch issued before any is used (a plain loop waits on each load
+// in turn); the arithmetic and its order are a plain loop's: the maximum
+// first, then the sums in split order.
+constexpr int kMergeBatch = 8;
+
 template <class T>
 __global__ __launch_bounds__(256) void merge_sum_kernel(const TileArgs a, int W) {
   const BatchPtrs bp = batch_ptrs(a);
@@ -406,9 +412,16 @@ __global__ __launch_bounds__(256) void merge_sum_kernel(const TileArgs a, int W)
   if (t >= a.N * W) return;
   const int64_t i = t / W;
   const int c = (int)(t % W);
-  const T *part = static_cast<const T *>(bp.partial);
+  const T *part = static_cast<const T *>(bp.partial) + i * W + c;
+  const int64_t stride = a.N * W;
   T s = 0;
-  for (int sp = 0; sp < a.n_split; ++sp) s += part[((int64_t)sp * a.N + i) * W + c];
+  for (int s0 = 0; s0 < a.n_split; s0 += kMergeBatch) {
+    T v[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = s0 + u < a.n_split ? part[(s0 + u) * stride] : (T)0;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) s += v[u];
+  }
   static_cast<T *>(bp.out)[i * a.ldo + c] = s;
 }
 
@@ -417,14 +430,29 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const TileArgs a) {
   const BatchPtrs bp = batch_ptrs(a);
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= a.N) return;
-  const T *part = static_cast<const T *>(bp.partial);
+  const T *part = static_cast<const T *>(bp.partial) + i * 2;
+  const int64_t stride = a.N * 2;
+  const int n = a.n_split;
   T m = neg_inf<T>();
-  for (int sp = 0; sp < a.n_split; ++sp) m = max(m, part[((int64_t)sp * a.N + i) * 2]);
+  for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+    T v[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = s0 + u < n ? part[(s0 + u) * stride] : neg_inf<T>();
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) m = max(m, v[u]);
+  }
   T l = 0;
   if (m != neg_inf<T>()) {
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      const T *q = part + ((int64_t)sp * a.N + i) * 2;
-      if (q[1] > (T)0) l += q[1] * dexp(q[0] - m);
+    for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+      T qm[kMergeBatch], ql[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        qm[u] = s0 + u < n ? part[(s0 + u) * stride] : (T)0;
+        ql[u] = s0 + u < n ? part[(s0 + u) * stride + 1] : (T)0;
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u)
+        if (ql[u] > (T)0) l += ql[u] * dexp(qm[u] - m);
     }
   }
   static_cast<T *>(bp.out)[i] = (l > (T)0) ? m + dlog(l) : neg_inf<T>();
@@ -438,17 +466,35 @@ __global__ __launch_bounds__(256) void merge_softmax_kernel(const TileArgs a) {
   const int64_t i = t / a.C;
   const int c = (int)(t % a.C);
   const int64_t W = a.C + 2;
-  const T *part = static_cast<const T *>(bp.partial);
+  const T *part = static_cast<const T *>(bp.partial) + i * W;
+  const int64_t stride = a.N * W;
+  const int n = a.n_split;
   T m = neg_inf<T>();
-  for (int sp = 0; sp < a.n_split; ++sp) m = max(m, part[((int64_t)sp * a.N + i) * W]);
+  for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+    T v[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = s0 + u < n ? part[(s0 + u) * stride] : neg_inf<T>();
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) m = max(m, v[u]);
+  }
   T l = 0, acc = 0;
   if (m != neg_inf<T>()) {
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      const T *q = part + ((int64_t)sp * a.N + i) * W;
-      if (q[1] > (T)0) {
-        const T f = dexp(q[0] - m);
-        l += q[1] * f;
-        acc += q[2 + c] * f;
+    for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+      T qm[kMergeBatch], ql[kMergeBatch], qo[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const T *q = part + (s0 + u) * stride;
+        qm[u] = s0 + u < n ? q[0] : (T)0;
+        ql[u] = s0 + u < n ? q[1] : (T)0;
+        qo[u] = s0 + u < n ? q[2 + c] : (T)0;
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (ql[u] > (T)0) {
+          const T f = dexp(qm[u] - m);
+          l += ql[u] * f;
+          acc += qo[u] * f;
+        }
       }
     }
   }

@@ -488,12 +488,16 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
         for (int r = 0; r < NREG; ++r) v[b][r] = ldexp(fma(v[b][r], p[b][r], v[b][r]), n[b][r] >> 8);
     } else {
       // The expansion can round a distance below zero (x = y) or, far from
-      // the origin, well below it: the exponent is clamped at 0, so k <= 1
-      // and never overflows (float64's rounding is 2^-52 of |x|^2: no clamp).
+      // the origin, well below it: the value is clamped to [0, 1], so k <= 1
+      // (an overflow to +inf clamps to 1 as well). The clamp is the exp
+      // instruction's own output clamp, which the median of (k, 0, 1)
+      // compiles to: no instruction of its own. float64's rounding is 2^-52
+      // of |x|^2: no clamp.
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int r = 0; r < NREG; ++r) v[b][r] = F::exp2(fmin(fma(s[b][r], rbf_c, rbf_t[b]), (T)0));
+        for (int r = 0; r < NREG; ++r)
+          v[b][r] = __builtin_amdgcn_fmed3f(F::exp2(fma(s[b][r], rbf_c, rbf_t[b])), 0.f, 1.f);
     }
   };
   // Insert every lane's queued candidates, oldest first; the trip count is

@@ -272,18 +272,35 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
 #pragma unroll
       for (int r = 0; r < NREG; ++r) {
         const int key = kb + F::key_of(r, g);
-        bool valid = key < nb && own_keep;
-        if (CONS == C_LOGSUMEXP && a.exclude_self) valid = valid && (q0 + key != o);
-        if (MASKED && check) {
-          const int64_t i = SIDE == 0 ? o : q0 + key, j = SIDE == 0 ? q0 + key : o;
-          valid = valid && sK[MASKED ? key : 0] && pair_kept(mk, i, j, 0, 0);
+        P[r] = SIDE == 0 ? F::exp2(s[r] - ci) : F::exp2(s[r] * L2E - sC[key]);
+      }
+      // Pairs are dropped only in ragged sub-blocks, sub-blocks that may
+      // hold the own point itself (exclude_self) and checked tiles: a branch
+      // marked unlikely keeps that test off every other sub-block (left to
+      // itself the compiler turns it into a select on every register). An
+      // own row (column) dropped by its mask is zeroed at the store instead:
+      // a lane's dS only ever reaches its own outputs.
+      const bool ragged = kb + TM > nb;
+      const bool self = CONS == C_LOGSUMEXP && a.exclude_self && q0 + kb <= own1 && q0 + kb + TM > own0;
+      if (__builtin_expect(ragged || self || (MASKED && check), 0)) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) {
+          const int key = kb + F::key_of(r, g);
+          bool valid = key < nb;
+          if (CONS == C_LOGSUMEXP && a.exclude_self) valid = valid && (q0 + key != o);
+          if (MASKED && check) {
+            const int64_t i = SIDE == 0 ? o : q0 + key, j = SIDE == 0 ? q0 + key : o;
+            valid = valid && sK[MASKED ? key : 0] && pair_kept(mk, i, j, 0, 0);
+          }
+          P[r] = valid ? P[r] : 0.f;
         }
-        float x = SIDE == 0 ? F::exp2(s[r] - ci) : F::exp2(s[r] * L2E - sC[key]);
-        x = valid ? x : 0.f;
-        P[r] = x;
+      }
+#pragma unroll
+      for (int r = 0; r < NREG; ++r) {
+        const int key = kb + F::key_of(r, g);
         const float dr = SIDE == 0 ? di : sD[key];
-        if constexpr (SMX) dS[r] = x * (dp[r] - dr);
-        else dS[r] = x * dr;
+        if constexpr (SMX) dS[r] = P[r] * (dp[r] - dr);
+        else dS[r] = P[r] * dr;
       }
       // Own-point gradient: sum over the streamed side of dS times its point.
 #pragma unroll
@@ -312,7 +329,7 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
 #pragma unroll
       for (int r = 0; r < NREG; ++r) {
         const int d = c * TM + F::key_of(r, g);
-        if (d < a.D) dst[d] = (SIDE == 0 ? ri : 1.f) * oa[c][r];
+        if (d < a.D) dst[d] = own_keep ? (SIDE == 0 ? ri : 1.f) * oa[c][r] : 0.f;
       }
     if constexpr (SMX && SIDE == 1) {
 #pragma unroll
@@ -320,7 +337,7 @@ __global__ __launch_bounds__(kGThreads, 2) void mfma_grad_kernel(const MfmaGradA
 #pragma unroll
         for (int r = 0; r < NREG; ++r) {
           const int ch = c * TM + F::key_of(r, g);
-          if (ch < a.C) dst[a.D + ch] = ob[c][r];
+          if (ch < a.C) dst[a.D + ch] = own_keep ? ob[c][r] : 0.f;
         }
     }
   }

@@ -299,6 +299,13 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
   const bool keyflags = MASKED && (mk.col || mk.grow);  // per-key mask data is staged
   const int64_t r1 = min(a.N, row0 + BM) - 1;
 
+  // A paired pass whose run of tiles is empty reads no row operands; its
+  // partial is the empty one.
+  bool empty = false;
+  if (paired) {
+    const int64_t off = pass ? pt[0] : 0;
+    empty = min(v1 - off, pt[pass]) <= max(v0 - off, (int64_t)0);
+  }
   // ------------------------------------------------------------ row state
   int64_t qi[QB];
   bool qv[QB];
@@ -321,7 +328,7 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
 #pragma unroll
     for (int s = 0; s < DG; ++s) {
       const int d = g * DG + s;
-      T v = (qv[b] && d < a.D) ? Xp[qi[b] * a.ldx + d] : (T)0;
+      T v = (qv[b] && !empty && d < a.D) ? Xp[qi[b] * a.ldx + d] : (T)0;
       part = fma(v, v, part);
       qr[b][s] = DIST ? (T)-2 * v : v;
     }
@@ -903,13 +910,17 @@ __global__ __launch_bounds__((MfmaShape<T, CONS, DP, CP, KL>::NT),
       if (qv[b]) {
         const T inv = lt > (T)0 ? (T)1 / lt : (T)0;
         T *dst = fin ? static_cast<T *>(bp.out) + i * a.ldo : static_cast<T *>(bp.partial) + prow * (a.C + 2) + 2;
+        // A partial with no weight (l = 0) is skipped by the merge: its
+        // values are not written.
+        if (fin || lt > (T)0) {
 #pragma unroll
-        for (int c = 0; c < NCB; ++c)
+          for (int c = 0; c < NCB; ++c)
 #pragma unroll
-          for (int r = 0; r < NREG; ++r) {
-            const int ch = c * TM + F::key_of(r, g);
-            if (ch < a.C) dst[ch] = fin ? o[b][c][r] * inv : o[b][c][r];
-          }
+            for (int r = 0; r < NREG; ++r) {
+              const int ch = c * TM + F::key_of(r, g);
+              if (ch < a.C) dst[ch] = fin ? o[b][c][r] * inv : o[b][c][r];
+            }
+        }
         // The row offset p_i drops out of the softmax but belongs to the
         // row's log-sum-exp: it rides on the partial maximum (the merge's
         // rescale is unchanged by a common shift).

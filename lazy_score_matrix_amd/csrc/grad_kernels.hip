@@ -69,8 +69,19 @@ __global__ __launch_bounds__(256) void grad_merge_kernel(const T *__restrict__ p
   if (e >= n_own * W) return;
   const int64_t r = e / W;
   const int w = (int)(e % W);
+  // Eight splits' partials at a time, every load of a batch issued before
+  // any is used; the sum keeps split order.
+  constexpr int NB = 8;
+  const T *src = part + r * W + w;
+  const int64_t stride = n_own * W;
   T acc = 0;
-  for (int sp = 0; sp < n_split; ++sp) acc += part[((int64_t)sp * n_own + r) * W + w];
+  for (int s0 = 0; s0 < n_split; s0 += NB) {
+    T v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = s0 + u < n_split ? src[(s0 + u) * stride] : (T)0;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) acc += v[u];
+  }
   if (w < D) {
     if (o.own) static_cast<T *>(o.own)[r * o.ld_own + w] = acc;
   } else if (w < D + C1) {
